@@ -1,0 +1,205 @@
+"""Plain CPU reference ("oracle") for token-sparse GQA decode attention with
+proposal-refined cross-layer index sharing, as "Prism Attention:
+Proposal-Refined Index Sharing Mechanism for Efficient LLMs Inference"
+(arXiv 2610.22985) describes it.
+
+TEST INFRASTRUCTURE.  This module is slow on purpose and exists only to check
+the GPU library.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import it.  It shares no code with the HIP
+library and imports nothing from it.
+
+Everything is float64 numpy.  bf16 inputs are widened exactly.  Readings taken
+where the paper is silent (all also listed in the design notes):
+  * scoring uses the bf16 keys themselves, not the paper's INT2 codes;
+  * GQA: query head j belongs to KV head j // G (consecutive blocks);
+  * TopK ties go to the lower token position; the selected set is returned as
+    ascending positions (the paper treats it as a set);
+  * refined layers use a positional window: the candidate pool is the union of
+    [i - w, i + w], clipped to [0, L), over the anchor layer's top-kappa set
+    (the paper's own pool is the anchor's top-(rho*kappa), Eq. 4);
+  * a refined layer always expands the nearest preceding anchor's set;
+  * SparseAttn is softmax attention with scale 1/sqrt(D) unless given.
+
+Parity pins: every function below is pinned by tests (brute force on tiny
+inputs, closed forms, invariants, a library routine for dense attention, and a
+hand-worked example).  The chained multi-layer step is a composition of the
+pinned parts and is otherwise "parity unpinned": the paper prints no numeric
+end-to-end example.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# bf16 and the paged cache
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """A bf16 value is the upper 16 bits of a binary32 word; widening is exact."""
+    w = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return w.view(np.float32).astype(np.float64)
+
+
+def cache_rows(pages, block_table_row, kv_head: int, positions, page_size: int) -> np.ndarray:
+    """Rows of the paged cache (the historical keys or values of Section 4.1)
+    for one sequence and KV head, at the given token positions: float64 [n, D].
+
+    pages: uint16 [num_pages, Hkv, page_size, D]; logical page p of the
+    sequence lives at physical page block_table_row[p].
+    """
+    pos = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(block_table_row, dtype=np.int64)[pos // page_size]
+    return bf16_to_f64(pages[phys, kv_head, pos % page_size, :])
+
+
+# ---------------------------------------------------------------------------
+# Section 4.1 / 4.2: relevance, TopK, the candidate pool
+# ---------------------------------------------------------------------------
+
+def relevance(q_group: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Eq. 9 (used as phi in Eq. 1 and Eq. 5): the score of token i is the
+    largest inner product <q_j, k_i> over the query heads j of the KV head's
+    group.  q_group: [G, D]; keys: [n, D]; returns [n]."""
+    dots = keys @ q_group.T          # [n, G]
+    return dots.max(axis=1)
+
+
+def top_kappa(scores: np.ndarray, kappa: int, positions: np.ndarray) -> np.ndarray:
+    """Eq. 2 / Eq. 6: positions of the kappa largest scores.  A full stable sort
+    on (-score, position): equal scores go to the lower position.  Returned
+    ascending (set semantics)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    positions = np.asarray(positions, dtype=np.int64)
+    if not 1 <= kappa <= scores.shape[0]:
+        raise ValueError("need 1 <= kappa <= number of candidates")
+    order = np.lexsort((positions, -scores))
+    return np.sort(positions[order[:kappa]])
+
+
+def window_pool(anchor_positions, w: int, length: int) -> np.ndarray:
+    """Candidate pool of a refined layer: every position within +-w of a token
+    the anchor layer selected, clipped to [0, length), each position once.
+    (The paper motivates refinement by salient tokens shifting to the
+    neighbourhood of the previously selected ones; the positional window is
+    this library's concrete pool rule.)  Returned ascending."""
+    mask = np.zeros(length, dtype=bool)
+    for i in np.asarray(anchor_positions, dtype=np.int64):
+        lo = max(0, int(i) - w)
+        hi = min(length - 1, int(i) + w)
+        mask[lo: hi + 1] = True
+    return np.flatnonzero(mask).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 1, SparseAttn
+# ---------------------------------------------------------------------------
+
+def attention_weights(q_group: np.ndarray, keys: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax over the selected tokens of z_i = scale * <q_j, k_i>, per query
+    head j: [G, n].  The largest logit is subtracted first (exact in real
+    arithmetic, keeps exp in range)."""
+    z = (q_group @ keys.T) * scale
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def sparse_attention(q_group: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                     scale: float) -> np.ndarray:
+    """SparseAttn of Algorithm 1: attention of each query head over the selected
+    tokens only.  keys/values: [n, D] rows of the selected tokens; [G, D] out."""
+    return attention_weights(q_group, keys, scale) @ values
+
+
+def default_scale(head_dim: int) -> float:
+    return 1.0 / math.sqrt(head_dim)
+
+
+# ---------------------------------------------------------------------------
+# One layer and one decode step over the paged cache
+# ---------------------------------------------------------------------------
+
+def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size):
+    """Proposal (anchor) layer, Alg. 1 lines 4-7 with bf16 keys: score every
+    cached token, keep the exact top-kappa.  Returns (selected, scores)."""
+    pos = np.arange(length, dtype=np.int64)
+    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pos, page_size))
+    return top_kappa(s, kappa, pos), s
+
+
+def refined_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size,
+                   anchor_positions, w):
+    """Refined layer, Eqs. 5-6 and Alg. 1 lines 8-10: re-score only inside the
+    pool built from the anchor's set, keep the top-kappa there.
+    Returns (selected, pool, scores over the pool)."""
+    pool = window_pool(anchor_positions, w, length)
+    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pool, page_size))
+    return top_kappa(s, kappa, pool), pool, s
+
+
+def attend(q_group, k_pages, v_pages, block_table_row, kv_head, selected, page_size, scale):
+    keys = cache_rows(k_pages, block_table_row, kv_head, selected, page_size)
+    vals = cache_rows(v_pages, block_table_row, kv_head, selected, page_size)
+    return sparse_attention(q_group, keys, vals, scale)
+
+
+def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_kv_heads,
+                 kappa, anchor_stride, window, page_size, anchor_state=None, scale=None,
+                 problems=None):
+    """One layer of Algorithm 1 for every (sequence, KV head).
+
+    q_bits: uint16 [B, Hq, D].  anchor_state: int64 [B, Hkv, kappa], the most
+    recent anchor layer's sets (required for a refined layer).
+    problems: optional list of (b, g) to restrict the work to (others are left
+    as -1 / NaN).
+
+    Returns dict(selected [B,Hkv,kappa] int64, out [B,Hq,D] float64,
+    anchor_state, pools {(b,g): pool}, scores {(b,g): scores over the pool}).
+    """
+    B, Hq, D = q_bits.shape
+    G = Hq // num_kv_heads
+    if scale is None or scale == 0:
+        scale = default_scale(D)
+    q = bf16_to_f64(q_bits)
+    is_anchor = layer % anchor_stride == 0
+    if not is_anchor and anchor_state is None:
+        raise ValueError("a refined layer needs the preceding anchor's sets")
+    sel = np.full((B, num_kv_heads, kappa), -1, dtype=np.int64)
+    out = np.full((B, Hq, D), np.nan)
+    pools, scores = {}, {}
+    todo = problems if problems is not None else [(b, g) for b in range(B)
+                                                  for g in range(num_kv_heads)]
+    for b, g in todo:
+        qg = q[b, g * G:(g + 1) * G]
+        L = int(seq_lens[b])
+        if is_anchor:
+            t, s = anchor_select(qg, k_pages, block_table[b], g, L, kappa, page_size)
+            pools[(b, g)] = np.arange(L, dtype=np.int64)
+        else:
+            t, pool, s = refined_select(qg, k_pages, block_table[b], g, L, kappa, page_size,
+                                        anchor_state[b, g], window)
+            pools[(b, g)] = pool
+        scores[(b, g)] = s
+        sel[b, g] = t
+        out[b, g * G:(g + 1) * G] = attend(qg, k_pages, v_pages, block_table[b], g, t,
+                                           page_size, scale)
+    new_state = sel.copy() if is_anchor else anchor_state
+    return dict(selected=sel, out=out, anchor_state=new_state, pools=pools, scores=scores)
+
+
+def decode_step(layers, block_table, seq_lens, *, num_kv_heads, kappa, anchor_stride, window,
+                page_size, scale=None):
+    """Algorithm 1 over layers 0..N-1 in order; `layers` yields
+    (q_bits, k_pages, v_pages) per layer.  Layer 0 must be an anchor."""
+    state = None
+    results = []
+    for l, (q_bits, kp, vp) in enumerate(layers):
+        r = decode_layer(l, q_bits, kp, vp, block_table, seq_lens, num_kv_heads=num_kv_heads,
+                         kappa=kappa, anchor_stride=anchor_stride, window=window,
+                         page_size=page_size, anchor_state=state, scale=scale)
+        state = r["anchor_state"]
+        results.append(r)
+    return results

@@ -1,0 +1,277 @@
+"""Checks that pin the CPU oracle to facts fixed independently of it: brute
+force on tiny inputs, closed forms, invariants, a library routine for dense
+attention and a hand-worked example (tests/golden/hand_example.json).
+
+Each check takes the implementation under test as a namespace, so the same
+checks run against the oracle (they must pass) and against deliberately broken
+copies of it (each must be caught by at least one check).
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+_GOLDEN_PATH = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+with open(_GOLDEN_PATH) as _f:
+    GOLDEN = json.load(_f)
+
+
+def _arr(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# --------------------------------------------------------------------- bf16
+def pin_bf16_decode(impl):
+    cases = {0x3F80: 1.0, 0xBF80: -1.0, 0x4000: 2.0, 0xC040: -3.0, 0x3F00: 0.5, 0x0000: 0.0,
+             0x7F7F: 3.3895313892515355e38, 0x0001: 2.0 ** -133, 0x0080: 2.0 ** -126,
+             0x3FC0: 1.5, 0x3F81: 1.0 + 2.0 ** -7, 0x4248: 50.0}
+    got = impl.bf16_to_f64(np.array(list(cases), dtype=np.uint16))
+    assert np.array_equal(got, np.array(list(cases.values()))), got
+    neg0 = impl.bf16_to_f64(np.array([0x8000], dtype=np.uint16))
+    assert neg0[0] == 0.0 and math.copysign(1.0, neg0[0]) < 0
+
+
+# ---------------------------------------------------------------- relevance
+def pin_relevance_bruteforce(impl, seed=11):
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        G, D, n = int(rng.integers(1, 6)), int(rng.integers(1, 9)), int(rng.integers(1, 12))
+        q = rng.integers(-9, 10, size=(G, D))
+        k = rng.integers(-9, 10, size=(n, D))
+        want = []
+        for i in range(n):
+            dots = [sum(int(q[j, t]) * int(k[i, t]) for t in range(D)) for j in range(G)]
+            want.append(max(dots))
+        got = impl.relevance(_arr(q), _arr(k))
+        assert got.shape == (n,) and np.array_equal(got, _arr(want)), (got, want)
+    for _ in range(20):   # real-valued: compare with exactly rounded sums
+        G, D, n = int(rng.integers(1, 5)), 16, int(rng.integers(1, 8))
+        q, k = rng.standard_normal((G, D)), rng.standard_normal((n, D))
+        want = [max(math.fsum(q[j, t] * k[i, t] for t in range(D)) for j in range(G))
+                for i in range(n)]
+        np.testing.assert_allclose(impl.relevance(q, k), want, rtol=1e-12, atol=1e-12)
+
+
+def pin_relevance_hand(impl):
+    q = _arr(GOLDEN["q_group"])
+    for part in ("anchor", "refined"):
+        got = impl.relevance(q, _arr(GOLDEN[part]["keys"]))
+        assert np.array_equal(got, _arr(GOLDEN[part]["scores"])), (part, got)
+
+
+# --------------------------------------------------------------------- TopK
+def _brute_topk(scores, kappa, pos):
+    """Among all kappa-subsets, the largest score sum; among those, the
+    lexicographically smallest ascending position tuple (= lower position wins
+    ties at the threshold)."""
+    best = None
+    for comb in itertools.combinations(range(len(scores)), kappa):
+        key = (-sum(scores[c] for c in comb), sorted(int(pos[c]) for c in comb))
+        if best is None or key < best:
+            best = key
+    return best[1]
+
+
+def pin_topk_exhaustive(impl, seed=12):
+    rng = np.random.default_rng(seed)
+    for _ in range(120):
+        n = int(rng.integers(1, 9))
+        scores = rng.integers(-2, 3, size=n)            # heavy ties
+        pos = rng.permutation(40)[:n]                   # arbitrary distinct labels
+        for kappa in range(1, n + 1):
+            got = impl.top_kappa(_arr(scores), kappa, pos)
+            assert list(map(int, got)) == _brute_topk(list(map(int, scores)), kappa, pos), \
+                (scores, pos, kappa, got)
+
+
+def pin_topk_invariants(impl, seed=13):
+    rng = np.random.default_rng(seed)
+    for _ in range(40):
+        n = int(rng.integers(2, 300))
+        s = np.round(rng.standard_normal(n), 1)          # ties at 0.1 resolution
+        pos = np.sort(rng.choice(10 * n, size=n, replace=False))
+        kappa = int(rng.integers(1, n + 1))
+        t = np.asarray(impl.top_kappa(s, kappa, pos))
+        assert t.shape == (kappa,)
+        assert np.all(np.diff(t) > 0), "ascending, no duplicates"
+        assert np.isin(t, pos).all()
+        sel = np.isin(pos, t)
+        if kappa < n:
+            lo, hi = s[sel].min(), s[~sel].max()
+            assert lo >= hi
+            if lo == hi:   # equal scores at the threshold: lower positions win
+                assert pos[sel & (s == lo)].max() < pos[~sel & (s == hi)].min()
+
+
+def pin_topk_hand(impl):
+    s = _arr(GOLDEN["anchor"]["scores"])
+    pos = np.arange(len(s))
+    for k, want in GOLDEN["anchor"]["topk"].items():
+        assert list(map(int, impl.top_kappa(s, int(k), pos))) == want, k
+
+
+# --------------------------------------------------------------------- pool
+def pin_pool_bruteforce(impl, seed=14):
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        L = int(rng.integers(1, 50))
+        kappa = int(rng.integers(1, L + 1))
+        A = np.sort(rng.choice(L, size=kappa, replace=False))
+        for w in (0, 1, 2, 3, 7, L - 1, L + 5):
+            want = sorted({t for i in A for t in range(i - w, i + w + 1) if 0 <= t < L})
+            got = impl.window_pool(A, w, L)
+            assert list(map(int, got)) == want, (L, A, w)
+            assert len(got) <= min(L, kappa * (2 * w + 1))
+            assert np.isin(A, got).all()
+            if w >= L - 1:
+                assert list(map(int, got)) == list(range(L))
+            if w == 0:
+                assert list(map(int, got)) == list(map(int, A))
+
+
+def pin_pool_hand(impl):
+    A = GOLDEN["anchor"]["topk"]["3"]
+    for w, want in GOLDEN["pool_of_anchor_top3"].items():
+        if w == "derivation":
+            continue
+        assert list(map(int, impl.window_pool(np.array(A), int(w), 8))) == want, w
+
+
+# --------------------------------------------------------------- refinement
+def _tiny_paged(rows_per_layer, page_size=2, hkv=1, seed=0):
+    """Pack per-layer key rows [L, D] (float, exactly bf16-representable) into a
+    paged cache with a shuffled block table.  Returns (pages list, block_table)."""
+    rng = np.random.default_rng(seed)
+    L, D = np.asarray(rows_per_layer[0]).shape
+    npg = (L + page_size - 1) // page_size
+    perm = rng.permutation(npg + 3)[:npg]
+    out = []
+    for rows in rows_per_layer:
+        bits = (np.asarray(rows, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        pages = np.zeros((npg + 3, hkv, page_size, D), dtype=np.uint16)
+        for p in range(npg):
+            chunk = bits[p * page_size:(p + 1) * page_size]
+            pages[perm[p], 0, :len(chunk)] = chunk
+        out.append(pages)
+    return out, perm.astype(np.int32)
+
+
+def pin_refine_hand(impl):
+    q = _arr(GOLDEN["q_group"])
+    (pa, pr), bt = _tiny_paged([GOLDEN["anchor"]["keys"], GOLDEN["refined"]["keys"]])
+    A, s = impl.anchor_select(q, pa, bt, 0, 8, 3, 2)
+    assert list(map(int, A)) == GOLDEN["anchor"]["topk"]["3"]
+    assert np.array_equal(s, _arr(GOLDEN["anchor"]["scores"]))
+    for w, want in GOLDEN["refined"]["refined_top3"].items():
+        t, pool, _ = impl.refined_select(q, pr, bt, 0, 8, 3, 2, A, int(w))
+        assert list(map(int, t)) == want, w
+    ex, _ = impl.anchor_select(q, pr, bt, 0, 8, 3, 2)
+    assert list(map(int, ex)) == GOLDEN["refined"]["exact_top3"]
+
+
+def pin_refine_limits(impl, seed=15):
+    """w >= L-1 makes refinement the exact TopK; w = 0 reproduces static reuse
+    (Eq. 3) whenever the pool is exactly the anchor set."""
+    rng = np.random.default_rng(seed)
+    for _ in range(25):
+        L, D, G = int(rng.integers(4, 60)), 4, int(rng.integers(1, 4))
+        kappa = int(rng.integers(1, L + 1))
+        ra = np.round(rng.standard_normal((L, D)) * 4) / 4
+        rr = np.round(rng.standard_normal((L, D)) * 4) / 4
+        (pa, pr), bt = _tiny_paged([ra, rr], page_size=4, seed=int(rng.integers(1000)))
+        q = np.round(rng.standard_normal((G, D)) * 4) / 4
+        A, _ = impl.anchor_select(q, pa, bt, 0, L, kappa, 4)
+        exact, _ = impl.anchor_select(q, pr, bt, 0, L, kappa, 4)
+        t_full, _, _ = impl.refined_select(q, pr, bt, 0, L, kappa, 4, A, L - 1)
+        assert np.array_equal(t_full, exact)
+        t0, pool0, _ = impl.refined_select(q, pr, bt, 0, L, kappa, 4, A, 0)
+        assert np.array_equal(t0, A) and np.array_equal(pool0, A)
+
+
+# ---------------------------------------------------------------- attention
+def pin_attention_dense_library(impl, seed=16):
+    """kappa = L: sparse attention over every token equals dense attention, here
+    PyTorch's scaled_dot_product_attention in float64 on the CPU."""
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(seed)
+    for _ in range(10):
+        G, D, n = int(rng.integers(1, 9)), int(rng.choice([8, 64, 128])), int(rng.integers(1, 300))
+        qg, k, v = (rng.standard_normal((G, D)), rng.standard_normal((n, D)),
+                    rng.standard_normal((n, D)))
+        scale = 1.0 / math.sqrt(D)
+        tq = torch.tensor(qg)[None, :, None, :]
+        tk = torch.tensor(k)[None, None].expand(1, G, n, D)
+        tv = torch.tensor(v)[None, None].expand(1, G, n, D)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0, :, 0, :].numpy()
+        np.testing.assert_allclose(impl.sparse_attention(qg, k, v, scale), ref,
+                                   rtol=1e-10, atol=1e-12)
+
+
+def pin_attention_closed_forms(impl, seed=17):
+    rng = np.random.default_rng(seed)
+    for _ in range(20):
+        G, D = int(rng.integers(1, 5)), int(rng.integers(1, 17))
+        qg = rng.standard_normal((G, D)) * 3
+        k1, v1 = rng.standard_normal((1, D)), rng.standard_normal((1, D))
+        # one token: the output is that token's value row for every head
+        assert np.allclose(impl.sparse_attention(qg, k1, v1, 0.3), np.repeat(v1, G, 0),
+                           rtol=0, atol=1e-15)
+        # two tokens: weights are the logistic function of the logit difference
+        k2, v2 = rng.standard_normal((2, D)), rng.standard_normal((2, D))
+        sc = float(rng.uniform(0.05, 1.0))
+        dz = sc * (qg @ k2[0] - qg @ k2[1])
+        w0 = 1.0 / (1.0 + np.exp(-dz))
+        want = w0[:, None] * v2[0] + (1 - w0)[:, None] * v2[1]
+        np.testing.assert_allclose(impl.sparse_attention(qg, k2, v2, sc), want, rtol=1e-12,
+                                   atol=1e-13)
+        # weights are a distribution; output does not depend on token order
+        n = int(rng.integers(2, 50))
+        k, v = rng.standard_normal((n, D)), rng.standard_normal((n, D))
+        wts = impl.attention_weights(qg, k, sc)
+        assert wts.shape == (G, n) and np.all(wts >= 0)
+        np.testing.assert_allclose(wts.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+        perm = rng.permutation(n)
+        np.testing.assert_allclose(impl.sparse_attention(qg, k[perm], v[perm], sc),
+                                   impl.sparse_attention(qg, k, v, sc), rtol=1e-12, atol=1e-13)
+
+
+def pin_attention_hand(impl):
+    a = GOLDEN["attention"]
+    scale = math.log(3.0) / 2.0
+    q, k, v = _arr(a["q_group"]), _arr(a["keys"]), _arr(a["values"])
+    np.testing.assert_allclose(impl.attention_weights(q, k, scale), a["weights"], rtol=1e-14)
+    np.testing.assert_allclose(impl.sparse_attention(q, k, v, scale), a["out"], rtol=1e-14)
+
+
+# ------------------------------------------------------------- paged cache
+def pin_cache_rows(impl):
+    """The paged gather returns exactly the rows the generator produced for
+    that (sequence, KV head) before paging."""
+    import synth
+    wl = synth.scaled(synth.BATCHED_16, name="paging-pin", wid=901, batch=3, num_q_heads=4,
+                      num_kv_heads=2, len_range=(128, 640), num_layers=1)
+    li = synth.layer_inputs(wl, 0, threads=1)
+    pg = synth.paging(wl)
+    rng = np.random.default_rng(18)
+    for b in range(wl.batch):
+        L = int(pg.seq_lens[b])
+        for g in range(wl.num_kv_heads):
+            kb, vb = synth.kv_head(wl, 0, b, g, L, li.q)
+            pos = rng.choice(L, size=min(L, 50), replace=False)
+            want_k = synth.bf16_bits_to_f32(kb[pos]).astype(np.float64)
+            want_v = synth.bf16_bits_to_f32(vb[pos]).astype(np.float64)
+            assert np.array_equal(impl.cache_rows(li.k_pages, pg.block_table[b], g, pos,
+                                                  wl.page_size), want_k)
+            assert np.array_equal(impl.cache_rows(li.v_pages, pg.block_table[b], g, pos,
+                                                  wl.page_size), want_v)
+
+
+ALL_PINS = [pin_bf16_decode, pin_relevance_bruteforce, pin_relevance_hand, pin_topk_exhaustive,
+            pin_topk_invariants, pin_topk_hand, pin_pool_bruteforce, pin_pool_hand,
+            pin_refine_hand, pin_refine_limits, pin_attention_dense_library,
+            pin_attention_closed_forms, pin_attention_hand, pin_cache_rows]

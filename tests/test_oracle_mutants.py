@@ -1,0 +1,119 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and check that
+the pins catch every one: a pin set that a dropped term, a wrong sign or index
+or a transposed operand slips through would not be pinning anything."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import prism_oracle as po
+from tests import pins
+
+
+def _compose(ns):
+    """anchor/refined selection built from the namespace's own parts, so a
+    mutated part shows through them."""
+    def anchor_select(q, kp, bt, g, L, kappa, ps):
+        pos = np.arange(L, dtype=np.int64)
+        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pos, ps))
+        return ns.top_kappa(s, kappa, pos), s
+
+    def refined_select(q, kp, bt, g, L, kappa, ps, A, w):
+        pool = ns.window_pool(A, w, L)
+        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pool, ps))
+        return ns.top_kappa(s, kappa, pool), pool, s
+
+    ns.anchor_select, ns.refined_select = anchor_select, refined_select
+    return ns
+
+
+def _impl(**over):
+    ns = types.SimpleNamespace(**{n: getattr(oracle, n) for n in oracle.__all__})
+    for k, v in over.items():
+        setattr(ns, k, v)
+    return _compose(ns)
+
+
+def _topk_with(sort_keys):
+    def f(scores, kappa, positions):
+        scores, positions = np.asarray(scores, float), np.asarray(positions, np.int64)
+        order = np.lexsort(sort_keys(scores, positions))
+        return np.sort(positions[order[:kappa]])
+    return f
+
+
+def _pool_with(lo_fn, hi_fn, incl=1):
+    def f(A, w, L):
+        m = np.zeros(L, bool)
+        for i in np.asarray(A, np.int64):
+            m[max(0, lo_fn(int(i), w)): min(L - 1, hi_fn(int(i), w)) + incl] = True
+        return np.flatnonzero(m)
+    return f
+
+
+def _attn_weights_with(transform):
+    def f(q, k, scale):
+        return transform(q, k, scale)
+    return f
+
+
+def _softmax_rows(z):
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    return p / p.sum(axis=1, keepdims=True)
+
+
+def _attn_pair(weights):
+    return dict(attention_weights=weights,
+                sparse_attention=lambda q, k, v, s: weights(q, k, s) @ v)
+
+
+MUTANTS = {
+    "bf16 widened by 15 bits": dict(
+        bf16_to_f64=lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15)
+        .view(np.float32).astype(float)),
+    "group mean instead of max": dict(relevance=lambda q, k: (k @ q.T).mean(axis=1)),
+    "group sum instead of max": dict(relevance=lambda q, k: (k @ q.T).sum(axis=1)),
+    "group min instead of max": dict(relevance=lambda q, k: (k @ q.T).min(axis=1)),
+    "first head only": dict(relevance=lambda q, k: k @ q[0]),
+    "negated score": dict(relevance=lambda q, k: -(k @ q.T).max(axis=1)),
+    "ties to the higher position": dict(top_kappa=_topk_with(lambda s, p: (-p, -s))),
+    "smallest instead of largest": dict(top_kappa=_topk_with(lambda s, p: (p, s))),
+    "kappa-1 kept": dict(top_kappa=lambda s, k, p: oracle.top_kappa(s, k, p)[:-1]),
+    "output in score order": dict(
+        top_kappa=lambda s, k, p: np.asarray(p)[np.lexsort((np.asarray(p), -np.asarray(s)))[:k]]),
+    "window w-1": dict(window_pool=_pool_with(lambda i, w: i - w + 1, lambda i, w: i + w - 1)),
+    "window half open": dict(window_pool=_pool_with(lambda i, w: i - w, lambda i, w: i + w, 0)),
+    "window left side only": dict(window_pool=_pool_with(lambda i, w: i - w, lambda i, w: i)),
+    "window right side only": dict(window_pool=_pool_with(lambda i, w: i, lambda i, w: i + w)),
+    "attention without scale": _attn_pair(lambda q, k, s: _softmax_rows(q @ k.T)),
+    "attention scale squared": _attn_pair(lambda q, k, s: _softmax_rows(q @ k.T * s * s)),
+    "softmax over heads": _attn_pair(lambda q, k, s: _softmax_rows((q @ k.T * s).T).T),
+    "logits with a negated key": _attn_pair(lambda q, k, s: _softmax_rows(-(q @ k.T) * s)),
+    "logical page ignores block table": dict(
+        cache_rows=lambda pages, bt, g, pos, ps: po.bf16_to_f64(
+            pages[np.asarray(pos) // ps, g, np.asarray(pos) % ps, :])),
+    "row index off by one": dict(
+        cache_rows=lambda pages, bt, g, pos, ps: po.bf16_to_f64(
+            pages[np.asarray(bt)[np.asarray(pos) // ps], g, (np.asarray(pos) + 1) % ps, :])),
+}
+
+
+def test_unmutated_composition_passes():
+    impl = _impl()
+    for pin in pins.ALL_PINS:
+        pin(impl)
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name):
+    impl = _impl(**MUTANTS[name])
+    caught = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(impl)
+        except Exception as e:   # an assertion or a crash both expose the mutant
+            caught.append((pin.__name__, type(e).__name__))
+            break
+    assert caught, f"mutant '{name}' passed every pin"
