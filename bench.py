@@ -1,0 +1,345 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of token-sparse GQA attention with proposal-refined
+cross-layer index sharing on one MI355X.
+
+A step is one decode step's attention path over every layer of the workload:
+prism_decode_layer(l) for l = 0..N-1 (anchor layers: relevance of the whole
+cache, exact top-kappa, SparseAttn; refined layers: window pool, re-score,
+top-kappa, SparseAttn).  Inputs are seeded synthetic tensors of the workload's
+shapes, resident in HBM before timing starts.
+
+Prints ONE JSON line (rank 0).  Per-kernel durations come from HIP events the
+kernel dispatches record themselves (prism_profile_events), over the same
+timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor, as_completed
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SRC = os.path.join(ROOT, "token_sparse_attention_gqa_amd", "csrc", "prism_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for raw events."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        out = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(h.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(e)
+
+
+def launches_per_step(wl):
+    na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
+    nr = wl.num_layers - na
+    return {"anchor_score": na, "hist_reset": na, "pool_plan": nr, "pool_score": nr,
+            "select": wl.num_layers, "attention": wl.num_layers, "combine": wl.num_layers}
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_for(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source and this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    e = t.get("kernels", {}).get(kernel)
+    if not e or e.get("workload") != workload:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, host, seconds):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: one
+    anchor layer and one refined layer for as many (sequence, KV head) problems
+    as fit in about `seconds`, extrapolated to a whole decode step."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    pg = synth.paging(wl)
+    G = wl.group
+    la, lr = 0, 1
+    qa, qr = oracle.bf16_to_f64(host[la].q), oracle.bf16_to_f64(host[lr].q)
+    probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    ta, tr, done = [], [], 0
+    t_start = time.perf_counter()
+    for b, g in probs:
+        L = int(pg.seq_lens[b])
+        t0 = time.perf_counter()
+        A, _ = oracle.anchor_select(qa[b, g * G:(g + 1) * G], host[la].k_pages,
+                                    pg.block_table[b], g, L, wl.kappa, wl.page_size)
+        oracle.attend(qa[b, g * G:(g + 1) * G], host[la].k_pages, host[la].v_pages,
+                      pg.block_table[b], g, A, wl.page_size, oracle.default_scale(wl.head_dim))
+        t1 = time.perf_counter()
+        T, _, _ = oracle.refined_select(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
+                                        pg.block_table[b], g, L, wl.kappa, wl.page_size, A,
+                                        wl.window)
+        oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
+                      pg.block_table[b], g, T, wl.page_size, oracle.default_scale(wl.head_dim))
+        t2 = time.perf_counter()
+        ta.append(t1 - t0)
+        tr.append(t2 - t1)
+        done += 1
+        if time.perf_counter() - t_start > seconds:
+            break
+    n_anchor = launches_per_step(wl)["anchor_score"]
+    n_ref = wl.num_layers - n_anchor
+    P = len(probs)
+    step_s = P * (n_anchor * float(np.mean(ta)) + n_ref * float(np.mean(tr)))
+    return {"value": wl.batch / step_s, "unit": "tokens/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"oracle (numpy float64) on layer {la} (anchor) and layer {lr} (refined) "
+                       f"for {done} of {P} (sequence, KV head) problems "
+                       f"({time.perf_counter() - t_start:.1f} s); per-problem times "
+                       f"extrapolated to {n_anchor} anchor + {n_ref} refined layers x {P} problems"),
+            "ms_per_step": step_s * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3-8b-128k-planted")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the CPU-oracle baseline sample (0 skips it)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured as one HIP graph")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested)", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import token_sparse_attention_gqa_amd as tsa
+
+    wl = synth.BY_NAME[args.workload]
+    pg = synth.paging(wl)
+    dev = torch.device("cuda:0")
+    tsa.lib()
+    hip = Hip()
+
+    # ---- inputs, resident in HBM ------------------------------------------------
+    t0 = time.perf_counter()
+    log(f"[bench] generating {wl.num_layers} layers of {wl.name} "
+        f"(B={wl.batch}, L={int(pg.seq_lens.max())}, {wl.num_q_heads}q/{wl.num_kv_heads}kv)")
+    bt = torch.from_numpy(pg.block_table).to(dev)
+    sl = torch.from_numpy(pg.seq_lens).to(dev)
+    L_max, L_min = int(pg.seq_lens.max()), int(pg.seq_lens.min())
+    q_dev, kv_dev, host_keep = {}, {}, {}
+    keep_host = {0, 1} if args.cpu_seconds > 0 else set()
+    nthreads = synth.default_threads()
+    with ThreadPoolExecutor(nthreads) as ex:
+        futs = {ex.submit(synth.layer_inputs, wl, l, 1): l for l in range(wl.num_layers)}
+        for n_done, f in enumerate(as_completed(futs), 1):
+            l = futs[f]
+            li = f.result()
+            q_dev[l] = torch.from_numpy(li.q.view(np.int16)).to(dev)
+            k = torch.from_numpy(li.k_pages.view(np.int16)).to(dev)
+            v = torch.from_numpy(li.v_pages.view(np.int16)).to(dev)
+            kv_dev[l] = tsa.KVCache(k, v, bt, sl, max_seq_len=L_max, min_seq_len=L_min)
+            if l in keep_host:
+                host_keep[l] = li
+            del li
+            log(f"[bench] layer {l} resident ({n_done}/{wl.num_layers}, "
+                f"{time.perf_counter() - t0:.1f} s)")
+    torch.cuda.synchronize()
+
+    p = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window)
+    ws = torch.empty(tsa.prism_workspace_size(kv_dev[0], p), dtype=torch.uint8, device=dev)
+    anchor = torch.zeros((wl.batch, wl.num_kv_heads, wl.kappa), dtype=torch.int32, device=dev)
+    outs = torch.zeros((wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
+                       device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(wl.num_layers):
+            tsa.prism_decode_layer(l, kv_dev[l], q_dev[l], p, anchor, None, outs[l], ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # ---- timed region: per-kernel events recorded by the dispatches --------------
+    per_step = launches_per_step(wl)
+    rings = {}
+    for kind, n in per_step.items():
+        cnt = n * args.steps
+        rings[kind] = (hip.events(cnt), hip.events(cnt))
+        tsa.prism_profile_events(kind, rings[kind][0], rings[kind][1])
+    e_start, e_stop = hip.events(1)[0], hip.events(1)[0]
+    rt = hip.rt
+    rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    rt.hipEventRecord(e_start, ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(args.steps):
+        step()
+    rt.hipEventRecord(e_stop, ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall1 = time.perf_counter()
+    ms_total = hip.elapsed_ms(e_start, e_stop)
+    ms_per_step = ms_total / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step "
+        f"(wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
+
+    kernels = {}
+    for kind, (starts, stops) in rings.items():
+        n = tsa.prism_profile_launches(kind)
+        assert n == per_step[kind] * args.steps, (kind, n)
+        durs = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
+        kernels[kind] = {"launches_per_step": per_step[kind],
+                         "avg_us": 1e3 * float(np.mean(durs)) if durs else 0.0,
+                         "us_per_step": 1e3 * float(np.sum(durs)) / args.steps}
+        tsa.prism_profile_events(kind, [], [])
+        hip.destroy(starts + stops)
+
+    # ---- algorithmic bytes ----------------------------------------------------------
+    D2 = wl.head_dim * 2
+    anchor_bytes = int(pg.seq_lens.astype(np.int64).sum()) * wl.num_kv_heads * D2
+    attn_bytes = wl.batch * wl.num_kv_heads * wl.kappa * 2 * D2
+    # pool sizes of the refined layers of this step (untimed pass, same inputs)
+    pool_len = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=dev)
+    tmp_idx = torch.zeros_like(anchor)
+    pool_bytes = []
+    for l in range(wl.num_layers):
+        if wl.is_anchor(l):
+            tsa.prism_score_topk(kv_dev[l], q_dev[l], p, anchor, None, ws)
+        else:
+            tsa.prism_refine_topk(kv_dev[l], q_dev[l], p, anchor, tmp_idx, None, pool_len, None, ws)
+            pool_bytes.append(int(pool_len.sum().item()) * D2)
+    n_anchor = per_step["anchor_score"]
+    step_bytes = n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
+    algo = {"anchor_score": anchor_bytes,
+            "pool_score": (sum(pool_bytes) / len(pool_bytes)) if pool_bytes else 0,
+            "attention": attn_bytes}
+    for kind, k in kernels.items():
+        if kind in algo and k["avg_us"] > 0:
+            k["algorithmic_bytes_per_launch"] = algo[kind]
+            k["GBps"] = algo[kind] / (k["avg_us"] * 1e-6) / 1e9
+
+    dominant = max((k for k in kernels if k in algo), key=lambda k: kernels[k]["us_per_step"])
+    dk = kernels[dominant]
+    achieved = dk["GBps"]
+    roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic_for(dominant, wl.name),
+                "algorithmic_bytes_per_launch": int(algo[dominant]),
+                "avg_launch_us": round(dk["avg_us"], 3)}
+
+    result = {
+        "metric": "sparse decode-attn tokens/sec + % HBM roofline at 128K, kappa=2048 (1 GPU)",
+        "value": round(wl.batch * 1e3 / ms_per_step, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; paged bf16 K/V with RoPE, planted sinks and drifting clusters)"
+                if wl.planted else "synthetic (seeded; paged bf16 K/V with RoPE)",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": L_max,
+                   "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
+                   "head_dim": wl.head_dim, "layers": wl.num_layers,
+                   "anchor_stride": wl.anchor_stride, "kappa": wl.kappa, "window": wl.window,
+                   "page_size": wl.page_size},
+        "roofline": roofline,
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_algorithmic_bytes": int(step_bytes),
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                        for kk, vv in v.items()} for k, v in kernels.items()},
+    }
+
+    if args.graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            s = torch.cuda.current_stream()
+            rt.hipEventRecord(e_start, ctypes.c_void_p(s.cuda_stream))
+            for _ in range(args.steps):
+                g.replay()
+            rt.hipEventRecord(e_stop, ctypes.c_void_p(s.cuda_stream))
+            torch.cuda.synchronize()
+            gms = hip.elapsed_ms(e_start, e_stop) / args.steps
+            result["graph"] = {"ms_per_step": round(gms, 5),
+                               "tokens_per_s": round(wl.batch * 1e3 / gms, 2)}
+            log(f"[bench] graph replay: {gms:.4f} ms/step")
+        except Exception as exc:  # report, keep the eager result
+            result["graph"] = {"error": str(exc)[:200]}
+
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cb = cpu_baseline(wl, host_keep, args.cpu_seconds)
+        result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                  for k, v in cb.items()}
+    else:
+        result["cpu_baseline"] = None
+    hip.destroy([e_start, e_stop])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,218 @@
+/*
+ * prism.h -- C ABI of the MI355X (gfx950) library for token-sparse GQA decode
+ * attention with proposal-refined cross-layer index sharing.
+ *
+ * The operations follow "Prism Attention: Proposal-Refined Index Sharing
+ * Mechanism for Efficient LLMs Inference" (arXiv 2610.22985):
+ *   - relevance of a cached token to the step's query: Eq. 1 with phi given by
+ *     Eq. 9, the maximum over the KV head's group of query heads of <q_j, k_i>
+ *     (computed here on the bf16 keys themselves);
+ *   - exact top-kappa selection: Eq. 2 (anchor / proposal layers);
+ *   - refinement inside a candidate pool: Eqs. 5-6 (refined layers), where the
+ *     pool is the union of [i - w, i + w] (clipped to the sequence) over the
+ *     anchor layer's selected positions i;
+ *   - SparseAttn of Algorithm 1: softmax attention of every query head over
+ *     its KV head's selected tokens only.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer unless marked host.  The
+ *     caller owns every buffer; the library allocates nothing and keeps no
+ *     state between calls.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
+ *     and return without synchronising.  Arguments are validated on the host
+ *     before anything is enqueued; an invalid call enqueues nothing.
+ *   - bf16 values are passed as their 16-bit patterns (uint16_t).
+ *   - Selected index sets are token positions in ascending order, without
+ *     duplicates; ties in relevance go to the lower position.
+ *   - No exception or abort crosses the ABI; failures return a negative
+ *     prism_status and prism_last_error() describes the most recent one on
+ *     the calling thread.
+ *   - Supported shapes: head_dim 128, page_size 64, group size
+ *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, 1 <= kappa <= 8192,
+ *     max_seq_len <= 524288.  Anything else returns PRISM_ERR_UNSUPPORTED.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PRISM_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PRISM_API __attribute__((visibility("default")))
+#else
+#define PRISM_API
+#endif
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_INVALID_ARG = -1, /* null pointer, inconsistent sizes, kappa out of range ... */
+  PRISM_ERR_UNSUPPORTED = -2, /* valid but outside the supported shapes listed above     */
+  PRISM_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or smaller than required  */
+  PRISM_ERR_HIP = -4          /* no usable GPU, or a HIP call / kernel launch failed     */
+} prism_status;
+
+/*
+ * Paged KV cache of ONE layer (the historical keys K and values of Section
+ * 4.1).  Layout, all row-major:
+ *   k_pages, v_pages : bf16 [num_pages][num_kv_heads][page_size][head_dim],
+ *                      16-byte aligned; token t of sequence b, KV head g is
+ *                      row (t % page_size) of physical page
+ *                      block_table[b][t / page_size], head g.
+ *   block_table      : int32 [batch][max_pages_per_seq]; only the first
+ *                      ceil(seq_lens[b] / page_size) entries of a row are read;
+ *                      entries are physical page ids in [0, num_pages).
+ *   seq_lens         : int32 [batch]; tokens 0 .. seq_lens[b]-1 are attendable
+ *                      (the current token is already in the cache).
+ * Host integers: min_seq_len <= seq_lens[b] <= max_seq_len must hold for all b
+ * and max_seq_len <= max_pages_per_seq * page_size.  The library cannot check
+ * the device arrays; kernels clamp every length and position so that
+ * inconsistent contents give wrong results, never out-of-bounds accesses.
+ */
+typedef struct {
+  const uint16_t* k_pages;
+  const uint16_t* v_pages;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t num_pages;          /* physical pages in k_pages / v_pages */
+  int32_t max_pages_per_seq;
+  int32_t max_seq_len;
+  int32_t min_seq_len;
+} prism_kv_cache;
+
+/*
+ * kappa          sparse budget per KV head (Eq. 2); 1 <= kappa <= min_seq_len.
+ * anchor_stride  layer l is an anchor (proposal) layer iff l % anchor_stride == 0;
+ *                every other layer is refined against the nearest preceding
+ *                anchor (the association f of Section 4.1).  >= 1.
+ * window         w >= 0 of the refinement pool [i - w, i + w].
+ * softmax_scale  logit scale of SparseAttn; 0 selects 1/sqrt(head_dim).
+ * Query head j belongs to KV head j / G.
+ */
+typedef struct {
+  int32_t num_q_heads;
+  int32_t kappa;
+  int32_t anchor_stride;
+  int32_t window;
+  float softmax_scale;
+} prism_params;
+
+/* Bytes of device workspace every compute entry point needs for these shapes
+ * (0 when the arguments are invalid).  The workspace must be 256-byte aligned;
+ * its contents need no initialisation and are scratch between calls.  Calls
+ * that run concurrently must not share a workspace. */
+PRISM_API size_t prism_workspace_size(const prism_kv_cache* kv, const prism_params* params);
+
+/*
+ * Anchor (proposal) layer selection: Eq. 9 relevance of EVERY cached token,
+ * then the exact top-kappa of Eq. 2, per (sequence, KV head).
+ *   q          bf16 [batch][num_q_heads][head_dim], 16-byte aligned.
+ *   idx_out    int32 [batch][num_kv_heads][kappa]: ascending positions.
+ *   scores_out optional (NULL to skip), float [batch][num_kv_heads][max_seq_len]:
+ *              the fp32 relevance of every token (entries past seq_lens[b]
+ *              are unspecified).  For checking only; costs an extra copy.
+ */
+PRISM_API prism_status prism_score_topk(const prism_kv_cache* kv, const uint16_t* q,
+                              const prism_params* params, int32_t* idx_out, float* scores_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Refined layer selection (Eqs. 5-6): build the pool from the anchor's set,
+ * score only the pool's tokens (Eq. 9), keep the top-kappa.
+ *   anchor_idx    int32 [batch][num_kv_heads][kappa]: the anchor layer's sets,
+ *                 ascending (as prism_score_topk writes them).
+ *   idx_out       int32 [batch][num_kv_heads][kappa]: ascending positions.
+ *   pool_out      optional int32 [batch][num_kv_heads][max_seq_len]: the pool's
+ *                 positions, ascending, first pool_len_out[b][g] entries valid.
+ *   pool_len_out  optional int32 [batch][num_kv_heads].
+ *   pool_scores_out optional float [batch][num_kv_heads][max_seq_len]: fp32
+ *                 relevance of pool entry e (same order as pool_out).
+ */
+PRISM_API prism_status prism_refine_topk(const prism_kv_cache* kv, const uint16_t* q,
+                               const prism_params* params, const int32_t* anchor_idx,
+                               int32_t* idx_out, int32_t* pool_out, int32_t* pool_len_out,
+                               float* pool_scores_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * SparseAttn (Algorithm 1): for every query head j of KV head g,
+ *   out[b][j] = sum_{i in idx[b][g]} softmax_i(scale * <q_j, k_i>) * v_i,
+ * accumulated in fp32 with an online softmax over splits of the set.
+ *   idx   int32 [batch][num_kv_heads][kappa]; entries < 0 are ignored.
+ *   out   float [batch][num_q_heads][head_dim].
+ */
+PRISM_API prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_t* q,
+                               const prism_params* params, const int32_t* idx, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One layer of Algorithm 1.  If layer % anchor_stride == 0 the layer is an
+ * anchor: select as prism_score_topk and store the set in anchor_idx.
+ * Otherwise it is refined against anchor_idx (which must hold the nearest
+ * preceding anchor's set: calling a refined layer first is the caller's error)
+ * as prism_refine_topk.  Then SparseAttn over the layer's set into out.
+ *   anchor_idx     int32 [batch][num_kv_heads][kappa], state carried between
+ *                  the layers of one decode step (written by anchors, read by
+ *                  refined layers).
+ *   layer_idx_out  optional int32 [batch][num_kv_heads][kappa]: this layer's set.
+ *   out            float [batch][num_q_heads][head_dim].
+ */
+PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const uint16_t* q,
+                                const prism_params* params, int32_t* anchor_idx,
+                                int32_t* layer_idx_out, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Optional instrumentation for benchmarks.  Kernel kinds launched by the calls
+ * above: */
+typedef enum {
+  PRISM_KERNEL_ANCHOR_SCORE = 0, /* relevance of every cached token (anchor layers)  */
+  PRISM_KERNEL_POOL_SCORE = 1,   /* relevance of a refined layer's pool             */
+  PRISM_KERNEL_SELECT = 2,       /* top-kappa selection                             */
+  PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the selected set      */
+  PRISM_KERNEL_COMBINE = 4,      /* merge of the attention splits                   */
+  PRISM_KERNEL_POOL_PLAN = 5,    /* refined-layer pool construction                 */
+  PRISM_KERNEL_HIST_RESET = 6,   /* histogram reset before anchor scoring           */
+  PRISM_KERNEL_KINDS = 7
+} prism_kernel_kind;
+
+/*
+ * Registers a ring of `count` (start, stop) hipEvent_t pairs for one kernel
+ * kind: every later launch of that kind takes the next pair, round robin, and
+ * the events are recorded by the dispatch itself at the kernel's start and end
+ * on the stream it runs on (hipEventElapsedTime of a pair = that launch's
+ * duration).  count 0 (or NULL arrays) switches the kind back to plain
+ * launches.  The arrays are copied; the events stay owned by the caller and
+ * must outlive their use.  Process-wide setting, not thread-safe: meant for a
+ * single benchmarking thread.  Returns PRISM_ERR_INVALID_ARG for a bad kind
+ * or a negative count.
+ */
+PRISM_API prism_status prism_profile_events(int32_t kind, void* const* start_events,
+                                            void* const* stop_events, int32_t count);
+
+/* Launches of `kind` that took an event pair since its ring was registered. */
+PRISM_API int64_t prism_profile_launches(int32_t kind);
+
+/* Static description of a status code. */
+PRISM_API const char* prism_status_string(prism_status status);
+
+/* Message of the most recent failure on the calling thread ("" if none). */
+PRISM_API const char* prism_last_error(void);
+
+/* PRISM_ABI_VERSION of the built library. */
+PRISM_API int32_t prism_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

@@ -63,6 +63,9 @@ class Paging:
 
 
 def seq_lens(wl: Workload) -> np.ndarray:
+    if wl.lengths is not None:
+        assert len(wl.lengths) == wl.batch
+        return np.array(wl.lengths, dtype=np.int32)
     if wl.context is not None:
         return np.full(wl.batch, wl.context, dtype=np.int32)
     lo, hi = wl.len_range

@@ -28,6 +28,7 @@ class Workload:
     rope_base: float
     context: Optional[int] = None               # fixed context length for every sequence
     len_range: Optional[Tuple[int, int]] = None  # else lengths drawn uniformly in this range
+    lengths: Optional[Tuple[int, ...]] = None    # else these exact lengths (one per sequence)
     planted: bool = False         # sink tokens + query-aligned drifting clusters
     n_sinks: int = 4
     sink_scale: float = 4.0

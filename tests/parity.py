@@ -1,0 +1,129 @@
+"""Helpers of the GPU parity tests: upload seeded inputs, call the HIP library
+through its C ABI binding, and compare with the CPU oracle.
+
+Comparison rules:
+  * index sets: valid (kappa ascending distinct positions inside the pool) and
+    identical to the oracle's whenever the oracle's kappa-th and (kappa+1)-th
+    scores differ by more than 1e-3 relative; otherwise the overlap is at
+    least 0.999.  In every case each element in which the sets differ must sit
+    within 1e-4 (relative) of the oracle's threshold score: a difference is
+    only allowed where fp32 accumulation can reorder a near-tie.
+  * attention outputs: max-abs error <= 2e-3 and relative L2 error <= 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import token_sparse_attention_gqa_amd as tsa
+
+GAP_RULE = 1e-3
+OVERLAP_MIN = 0.999
+ATTN_MAX_ABS = 2e-3
+ATTN_REL_L2 = 1e-3
+NEAR_TIE = 1e-4
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda")
+
+
+class Setup:
+    """Seeded inputs of some layers of a workload, resident on the device."""
+
+    def __init__(self, wl: synth.Workload, layers):
+        self.wl = wl
+        self.pg = synth.paging(wl)
+        self.bt = dev(self.pg.block_table)
+        self.sl = dev(self.pg.seq_lens)
+        self.host = {}
+        self.q, self.kv = {}, {}
+        for l in layers:
+            li = synth.layer_inputs(wl, l)
+            self.host[l] = li
+            self.q[l] = dev(li.q)
+            self.kv[l] = tsa.KVCache(dev(li.k_pages), dev(li.v_pages), self.bt, self.sl,
+                                     max_seq_len=int(self.pg.seq_lens.max()),
+                                     min_seq_len=int(self.pg.seq_lens.min()))
+        self.params = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window)
+        first = next(iter(self.kv.values()))
+        self.ws = torch.empty(tsa.prism_workspace_size(first, self.params), dtype=torch.uint8,
+                              device="cuda")
+
+    @property
+    def P(self):
+        return self.wl.batch * self.wl.num_kv_heads
+
+    def idx_buf(self):
+        return torch.full((self.wl.batch, self.wl.num_kv_heads, self.wl.kappa), -7,
+                          dtype=torch.int32, device="cuda")
+
+    def out_buf(self):
+        return torch.full((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim), float("nan"),
+                          dtype=torch.float32, device="cuda")
+
+    # --- oracle views -------------------------------------------------------
+    def q_group(self, l, b, g):
+        G = self.wl.group
+        return oracle.bf16_to_f64(self.host[l].q[b, g * G:(g + 1) * G])
+
+    def oracle_anchor(self, l, b, g):
+        li = self.host[l]
+        return oracle.anchor_select(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
+                                    int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size)
+
+    def oracle_refine(self, l, b, g, anchor):
+        li = self.host[l]
+        return oracle.refined_select(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
+                                     int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size,
+                                     np.asarray(anchor, np.int64), self.wl.window)
+
+    def oracle_attend(self, l, b, g, sel):
+        li = self.host[l]
+        return oracle.attend(self.q_group(l, b, g), li.k_pages, li.v_pages, self.pg.block_table[b],
+                             g, np.asarray(sel, np.int64), self.wl.page_size,
+                             oracle.default_scale(self.wl.head_dim))
+
+
+def check_set(gpu_sel, want, scores, pool, kappa, where=""):
+    """Returns 'exact' or 'near-tie' (raises AssertionError otherwise)."""
+    gpu_sel = np.asarray(gpu_sel, dtype=np.int64)
+    want = np.asarray(want, dtype=np.int64)
+    pool = np.asarray(pool, dtype=np.int64)
+    assert gpu_sel.shape == (kappa,), f"{where}: shape {gpu_sel.shape}"
+    assert np.all(np.diff(gpu_sel) > 0), f"{where}: not ascending/distinct"
+    assert np.isin(gpu_sel, pool).all(), f"{where}: positions outside the pool"
+    if np.array_equal(gpu_sel, want):
+        return "exact"
+    assert len(pool) > kappa, f"{where}: pool of size kappa must be selected whole"
+    s = np.asarray(scores, dtype=np.float64)
+    srt = np.sort(s)[::-1]
+    sk, sk1 = srt[kappa - 1], srt[kappa]
+    gap = (sk - sk1) / abs(sk) if sk != 0 else np.inf
+    missing = np.setdiff1d(want, gpu_sel)
+    extra = np.setdiff1d(gpu_sel, want)
+    pos_score = dict(zip(pool.tolist(), s.tolist()))
+    assert gap <= GAP_RULE, (f"{where}: sets differ ({len(missing)} missing) although the "
+                             f"kappa-th gap is {gap:.3g} > {GAP_RULE}")
+    overlap = 1.0 - len(missing) / kappa
+    assert overlap >= OVERLAP_MIN, f"{where}: overlap {overlap:.5f} < {OVERLAP_MIN}"
+    for e in np.concatenate([missing, extra]):
+        assert abs(pos_score[int(e)] - sk) <= NEAR_TIE * max(abs(sk), 1e-30), \
+            f"{where}: differing position {e} is not a near-tie ({pos_score[int(e)]} vs {sk})"
+    return "near-tie"
+
+
+def check_attn(gpu_out, want, where=""):
+    gpu_out = np.asarray(gpu_out, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert np.all(np.isfinite(gpu_out)), f"{where}: non-finite output"
+    err = np.abs(gpu_out - want).max()
+    rel = np.linalg.norm(gpu_out - want) / max(np.linalg.norm(want), 1e-30)
+    assert err <= ATTN_MAX_ABS and rel <= ATTN_REL_L2, \
+        f"{where}: max-abs {err:.3g} (<= {ATTN_MAX_ABS}), rel-L2 {rel:.3g} (<= {ATTN_REL_L2})"
+    return err, rel

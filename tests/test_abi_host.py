@@ -1,0 +1,143 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid calls on the host before touching any
+device (fake, never dereferenced addresses are used)."""
+import ctypes
+
+import pytest
+
+import token_sparse_attention_gqa_amd as tsa
+from token_sparse_attention_gqa_amd import _lib as L
+
+FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation first
+
+
+def _kv(**over):
+    d = dict(k_pages=FAKE, v_pages=FAKE, block_table=FAKE, seq_lens=FAKE, batch=2,
+             num_kv_heads=8, head_dim=128, page_size=64, num_pages=1024, max_pages_per_seq=512,
+             max_seq_len=32768, min_seq_len=4096)
+    d.update(over)
+    return L.KVCacheStruct(*[d[n] for n, _ in L.KVCacheStruct._fields_])
+
+
+def _params(**over):
+    d = dict(num_q_heads=32, kappa=2048, anchor_stride=8, window=32, softmax_scale=0.0)
+    d.update(over)
+    return L.ParamsStruct(*[d[n] for n, _ in L.ParamsStruct._fields_])
+
+
+def _call(fn, kv, p, ws=FAKE, nbytes=1 << 40, **extra):
+    lib = tsa.lib()
+    kvp = ctypes.byref(kv) if kv is not None else None
+    pp = ctypes.byref(p) if p is not None else None
+    if fn == "score":
+        return lib.prism_score_topk(kvp, FAKE, pp, FAKE, None, ws, nbytes, None)
+    if fn == "refine":
+        return lib.prism_refine_topk(kvp, FAKE, pp, FAKE, FAKE, None, None, None, ws, nbytes, None)
+    if fn == "attn":
+        return lib.prism_sparse_attn(kvp, FAKE, pp, FAKE, FAKE, ws, nbytes, None)
+    if fn == "layer":
+        return lib.prism_decode_layer(extra.get("layer", 0), kvp, FAKE, pp, FAKE, None, FAKE, ws,
+                                      nbytes, None)
+    raise ValueError(fn)
+
+
+def test_library_exports_every_declared_function():
+    declared = tsa.declared_functions()
+    assert set(declared) == {"prism_workspace_size", "prism_score_topk", "prism_refine_topk",
+                             "prism_sparse_attn", "prism_decode_layer", "prism_status_string",
+                             "prism_last_error", "prism_abi_version", "prism_profile_events",
+                             "prism_profile_launches"}
+    lib = tsa.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert tsa.prism_abi_version() == 1
+    for s in (0, -1, -2, -3, -4):
+        assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
+    assert tsa.prism_status_string(-99) == "unknown status"
+
+
+def test_workspace_size():
+    lib = tsa.lib()
+    n = lib.prism_workspace_size(ctypes.byref(_kv()), ctypes.byref(_params()))
+    assert n > 2 * 16 * 32768 * 4            # scores + pool lists of 16 problems at least
+    assert n % 256 == 0
+    assert lib.prism_workspace_size(ctypes.byref(_kv()), ctypes.byref(_params(kappa=0))) == 0
+    bigger = lib.prism_workspace_size(ctypes.byref(_kv(max_seq_len=65536, max_pages_per_seq=1024)),
+                                      ctypes.byref(_params()))
+    assert bigger > n
+
+
+CASES = [
+    ("null kv", dict(kv=None), L.PRISM_ERR_INVALID_ARG),
+    ("null k_pages", dict(kv=_kv(k_pages=None)), L.PRISM_ERR_INVALID_ARG),
+    ("null seq_lens", dict(kv=_kv(seq_lens=None)), L.PRISM_ERR_INVALID_ARG),
+    ("batch 0", dict(kv=_kv(batch=0)), L.PRISM_ERR_INVALID_ARG),
+    ("hq not multiple of hkv", dict(p=_params(num_q_heads=30)), L.PRISM_ERR_INVALID_ARG),
+    ("group 3", dict(kv=_kv(num_kv_heads=2), p=_params(num_q_heads=6)), L.PRISM_ERR_UNSUPPORTED),
+    ("group 32", dict(kv=_kv(num_kv_heads=1)), L.PRISM_ERR_UNSUPPORTED),
+    ("head_dim 64", dict(kv=_kv(head_dim=64)), L.PRISM_ERR_UNSUPPORTED),
+    ("page 32", dict(kv=_kv(page_size=32)), L.PRISM_ERR_UNSUPPORTED),
+    ("no pages", dict(kv=_kv(num_pages=0)), L.PRISM_ERR_INVALID_ARG),
+    ("min > max", dict(kv=_kv(min_seq_len=40000)), L.PRISM_ERR_INVALID_ARG),
+    ("max beyond pages", dict(kv=_kv(max_pages_per_seq=100)), L.PRISM_ERR_INVALID_ARG),
+    ("max_seq_len too big", dict(kv=_kv(max_seq_len=1 << 20, max_pages_per_seq=1 << 14)),
+     L.PRISM_ERR_UNSUPPORTED),
+    ("kappa 0", dict(p=_params(kappa=0)), L.PRISM_ERR_INVALID_ARG),
+    ("kappa > min_seq_len", dict(p=_params(kappa=4097)), L.PRISM_ERR_INVALID_ARG),
+    ("kappa above 8192", dict(kv=_kv(min_seq_len=20000), p=_params(kappa=9000)),
+     L.PRISM_ERR_UNSUPPORTED),
+    ("negative window", dict(p=_params(window=-1)), L.PRISM_ERR_INVALID_ARG),
+    ("stride 0", dict(p=_params(anchor_stride=0)), L.PRISM_ERR_INVALID_ARG),
+    ("nan scale", dict(p=_params(softmax_scale=float("nan"))), L.PRISM_ERR_INVALID_ARG),
+    ("misaligned k", dict(kv=_kv(k_pages=FAKE + 2)), L.PRISM_ERR_INVALID_ARG),
+    ("null workspace", dict(ws=None), L.PRISM_ERR_WORKSPACE),
+    ("misaligned workspace", dict(ws=FAKE + 16), L.PRISM_ERR_WORKSPACE),
+    ("small workspace", dict(nbytes=1024), L.PRISM_ERR_WORKSPACE),
+]
+
+
+@pytest.mark.parametrize("fn", ["score", "refine", "attn", "layer"])
+@pytest.mark.parametrize("name,args,want", CASES, ids=[c[0] for c in CASES])
+def test_invalid_calls_rejected_on_host(fn, name, args, want):
+    kv = args.get("kv", _kv()) if "kv" in args else _kv()
+    p = args.get("p", _params())
+    st = _call(fn, kv, p, ws=args.get("ws", FAKE), nbytes=args.get("nbytes", 1 << 40))
+    assert st == want, (fn, name, st, tsa.prism_last_error())
+    assert tsa.prism_last_error()
+
+
+def test_negative_layer_rejected():
+    assert _call("layer", _kv(), _params(), layer=-1) == L.PRISM_ERR_INVALID_ARG
+
+
+def test_null_outputs_rejected():
+    lib = tsa.lib()
+    kv, p = _kv(), _params()
+    assert lib.prism_score_topk(ctypes.byref(kv), FAKE, ctypes.byref(p), None, None, FAKE, 1 << 40,
+                                None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_sparse_attn(ctypes.byref(kv), FAKE, ctypes.byref(p), FAKE, None, FAKE,
+                                 1 << 40, None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_score_topk(ctypes.byref(kv), None, ctypes.byref(p), FAKE, None, FAKE, 1 << 40,
+                                None) == L.PRISM_ERR_INVALID_ARG
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
+    for fn in ("score", "refine", "attn", "layer"):
+        st = _call(fn, _kv(), _params())
+        assert st == L.PRISM_ERR_HIP, (fn, st)
+        assert "device" in tsa.prism_last_error().lower()
+
+
+def test_profile_hook_argument_checks():
+    lib = tsa.lib()
+    assert lib.prism_profile_events(99, None, None, 0) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_profile_events(0, None, None, -1) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_profile_events(0, None, None, 0) == L.PRISM_OK
+    assert lib.prism_profile_launches(0) == 0
+    assert lib.prism_profile_launches(42) == -1

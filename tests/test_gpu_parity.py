@@ -1,0 +1,282 @@
+"""HIP path against the CPU oracle, element by element, through the C ABI.
+
+Small cases span several workgroup tiles and ragged tails; the full-size cases
+run every workload at its real shape through prism_decode_layer (the launch
+path the benchmark times) and check sampled (sequence, KV head) problems."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_sparse_attention_gqa_amd as tsa
+from tests.parity import Setup, check_attn, check_set, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    tsa.lib()   # the HIP library must be built; no fallback exists
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _small(G, lengths, kappa, window=16, hkv=2, wid=100, planted=False, layers=2, stride=2,
+           context=None):
+    return synth.scaled(synth.TINY_4K, name=f"small-g{G}", wid=wid, batch=len(lengths),
+                        num_q_heads=G * hkv, num_kv_heads=hkv, kappa=kappa, window=window,
+                        context=context, lengths=None if context else tuple(lengths),
+                        planted=planted, num_layers=layers, anchor_stride=stride)
+
+
+def _anchor_gpu(st, l, scores=False):
+    idx = st.idx_buf()
+    sc = (torch.full((st.wl.batch, st.wl.num_kv_heads, st.kv[l].struct.max_seq_len), float("nan"),
+                     device="cuda") if scores else None)
+    tsa.prism_score_topk(st.kv[l], st.q[l], st.params, idx, sc, st.ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), (sc.cpu().numpy() if scores else None)
+
+
+# --------------------------------------------------------------------------- anchor
+def test_anchor_scores_and_sets_tiny():
+    st = Setup(synth.TINY_4K, [0])
+    idx, sc = _anchor_gpu(st, 0, scores=True)
+    for b in range(1):
+        for g in range(2):
+            want, s = st.oracle_anchor(0, b, g)
+            np.testing.assert_allclose(sc[b, g, :4096], s, rtol=1e-5, atol=1e-3)
+            assert check_set(idx[b, g], want, s, np.arange(4096), 256, f"b{b}g{g}") == "exact"
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("kappa", [1, 97, 130])
+def test_anchor_ragged_groups(G, kappa):
+    lengths = (1000, 4097, 130, 2113)
+    st = Setup(_small(G, lengths, kappa, wid=110 + G), [0])
+    idx, sc = _anchor_gpu(st, 0, scores=True)
+    for b, L in enumerate(lengths):
+        for g in range(2):
+            want, s = st.oracle_anchor(0, b, g)
+            np.testing.assert_allclose(sc[b, g, :L], s, rtol=1e-5, atol=1e-3)
+            check_set(idx[b, g], want, s, np.arange(L), kappa, f"G{G} k{kappa} b{b} g{g}")
+
+
+def _hand_cache(rows_by_head, lengths):
+    """Identity-paged cache from explicit bf16 rows [Hkv][L][128] (same L per head)."""
+    hkv = len(rows_by_head)
+    L = max(lengths)
+    npg = (L + 63) // 64
+    B = len(lengths)
+    kp = np.zeros((npg * B, hkv, 64, 128), np.uint16)
+    for b in range(B):
+        for h in range(hkv):
+            r = np.zeros((npg * 64, 128), np.uint16)
+            r[:L] = rows_by_head[h][:L]
+            kp[b * npg:(b + 1) * npg, h] = r.reshape(npg, 64, 128)
+    bt = np.arange(npg * B, dtype=np.int32).reshape(B, npg)
+    return kp, bt
+
+
+def test_exact_ties_go_to_lowest_position():
+    """Equal scores in any precision (identical key rows): the lowest positions win."""
+    rng = np.random.default_rng(7)
+    L, kappa, G = 700, 50, 4
+    base = synth.f32_to_bf16_bits(rng.standard_normal((L, 128)).astype(np.float32))
+    tie = synth.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+    rows0 = np.repeat(tie[None], L, 0)                    # head 0: every row equal
+    rows1 = base.copy()                                   # head 1: 80 copies of one strong row
+    q = synth.f32_to_bf16_bits(rng.standard_normal((1, 2 * G, 128)).astype(np.float32))
+    qf = synth.bf16_bits_to_f32(q[0, G:2 * G]).astype(np.float64)
+    strong = synth.f32_to_bf16_bits((3 * qf[0] / np.linalg.norm(qf[0]) * 11.3).astype(np.float32))
+    dup_pos = np.sort(rng.choice(L, 80, replace=False))
+    rows1[dup_pos] = strong
+    kp, bt = _hand_cache([rows0, rows1], [L])
+    kv = tsa.KVCache(dev(kp), dev(kp), dev(bt), dev(np.array([L], np.int32)), max_seq_len=L,
+                     min_seq_len=L)
+    p = tsa.params(2 * G, kappa)
+    ws = torch.empty(tsa.prism_workspace_size(kv, p), dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((1, 2, kappa), dtype=torch.int32, device="cuda")
+    tsa.prism_score_topk(kv, dev(q), p, idx, None, ws)
+    got = idx.cpu().numpy()
+    assert list(got[0, 0]) == list(range(kappa))
+    assert list(got[0, 1]) == list(dup_pos[:kappa])
+
+
+# --------------------------------------------------------------------------- refine
+def test_refine_stage_isolated_tiny():
+    st = Setup(synth.TINY_4K, [0, 1])
+    A = np.stack([st.oracle_anchor(0, 0, g)[0] for g in range(2)])[None].astype(np.int32)
+    P = 2
+    idx, pool = st.idx_buf(), torch.full((1, 2, 4096), -5, dtype=torch.int32, device="cuda")
+    plen = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    psc = torch.zeros((1, 2, 4096), dtype=torch.float32, device="cuda")
+    tsa.prism_refine_topk(st.kv[1], st.q[1], st.params, dev(A), idx, pool, plen, psc, st.ws)
+    idx, pool, plen, psc = (t.cpu().numpy() for t in (idx, pool, plen, psc))
+    for g in range(P):
+        want, wpool, s = st.oracle_refine(1, 0, g, A[0, g])
+        n = int(plen[0, g])
+        assert n == len(wpool) and np.array_equal(pool[0, g, :n], wpool)   # bit-exact pool
+        np.testing.assert_allclose(psc[0, g, :n], s, rtol=1e-5, atol=1e-3)
+        check_set(idx[0, g], want, s, wpool, 256, f"refine g{g}")
+
+
+@pytest.mark.parametrize("window", [0, 1, 5, 33])
+def test_refine_pools_and_sets_ragged(window):
+    lengths = (1000, 4097, 300, 2113)
+    wl = _small(4, lengths, 97, window=window, wid=130 + window)
+    st = Setup(wl, [0, 1])
+    A_gpu, _ = _anchor_gpu(st, 0)
+    idx = st.idx_buf()
+    pool = torch.full((4, 2, 4097), -5, dtype=torch.int32, device="cuda")
+    plen = torch.zeros((4, 2), dtype=torch.int32, device="cuda")
+    psc = torch.zeros((4, 2, 4097), dtype=torch.float32, device="cuda")
+    tsa.prism_refine_topk(st.kv[1], st.q[1], st.params, dev(A_gpu), idx, pool, plen, psc, st.ws)
+    idx, pool, plen, psc = (t.cpu().numpy() for t in (idx, pool, plen, psc))
+    for b, L in enumerate(lengths):
+        for g in range(2):
+            want, wpool, s = st.oracle_refine(1, b, g, A_gpu[b, g])
+            n = int(plen[b, g])
+            assert n == len(wpool) and np.array_equal(pool[b, g, :n], wpool), (b, g)
+            np.testing.assert_allclose(psc[b, g, :n], s, rtol=1e-5, atol=1e-3)
+            check_set(idx[b, g], want, s, wpool, 97, f"w{window} b{b} g{g}")
+            if window == 0:
+                assert np.array_equal(idx[b, g], A_gpu[b, g])        # static reuse (Eq. 3)
+
+
+def test_refine_full_window_is_exact_topk():
+    lengths = (1000, 1500)
+    wl = _small(4, lengths, 64, window=5000, wid=140)
+    st = Setup(wl, [0, 1])
+    A_gpu, _ = _anchor_gpu(st, 0)
+    exact, _ = _anchor_gpu(st, 1)
+    idx = st.idx_buf()
+    tsa.prism_refine_topk(st.kv[1], st.q[1], st.params, dev(A_gpu), idx, workspace=st.ws)
+    assert np.array_equal(idx.cpu().numpy(), exact)
+
+
+# ------------------------------------------------------------------------ attention
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("kappa", [1, 100, 300])
+def test_attention_on_identical_sets(G, kappa):
+    lengths = (300, 1000, 4097)
+    st = Setup(_small(G, lengths, kappa, wid=150 + G), [0])
+    sets = np.zeros((3, 2, kappa), np.int32)
+    for b in range(3):
+        for g in range(2):
+            sets[b, g] = st.oracle_anchor(0, b, g)[0]
+    out = st.out_buf()
+    tsa.prism_sparse_attn(st.kv[0], st.q[0], st.params, dev(sets), out, st.ws)
+    out = out.cpu().numpy()
+    for b in range(3):
+        for g in range(2):
+            check_attn(out[b, g * G:(g + 1) * G], st.oracle_attend(0, b, g, sets[b, g]),
+                       f"G{G} k{kappa} b{b} g{g}")
+
+
+def test_attention_dense_and_ignored_entries():
+    """kappa = L is dense attention; negative entries of the set are skipped."""
+    L = 300
+    st = Setup(_small(4, (L, L), L, wid=160), [0])
+    full = np.tile(np.arange(L, dtype=np.int32), (2, 2, 1))
+    out = st.out_buf()
+    tsa.prism_sparse_attn(st.kv[0], st.q[0], st.params, dev(full), out, st.ws)
+    o = out.cpu().numpy()
+    for b in range(2):
+        for g in range(2):
+            check_attn(o[b, 4 * g:4 * g + 4], st.oracle_attend(0, b, g, np.arange(L)), "dense")
+    holes = full.copy()
+    holes[:, :, ::3] = -1
+    tsa.prism_sparse_attn(st.kv[0], st.q[0], st.params, dev(holes), out, st.ws)
+    o = out.cpu().numpy()
+    keep = np.array([i for i in range(L) if i % 3])
+    for b in range(2):
+        for g in range(2):
+            check_attn(o[b, 4 * g:4 * g + 4], st.oracle_attend(0, b, g, keep), "holes")
+
+
+# ---------------------------------------------------------------------- decode chain
+def _run_chain(st, layers, problems, label):
+    """prism_decode_layer over `layers` in order; each layer checked against the
+    oracle applied to the GPU's own anchor sets (chained) for the sampled problems."""
+    wl = st.wl
+    anchor = st.idx_buf()
+    layer_idx = st.idx_buf()
+    out = st.out_buf()
+    stats = {"exact": 0, "near-tie": 0}
+    A_gpu = None
+    for l in layers:
+        say(f"[{label}] layer {l} ({'anchor' if wl.is_anchor(l) else 'refined'})")
+        tsa.prism_decode_layer(l, st.kv[l], st.q[l], st.params, anchor, layer_idx, out, st.ws)
+        torch.cuda.synchronize()
+        sel = layer_idx.cpu().numpy()
+        o = out.cpu().numpy()
+        if wl.is_anchor(l):
+            A_gpu = anchor.cpu().numpy()
+            assert np.array_equal(A_gpu, sel)
+        for b, g in problems:
+            if wl.is_anchor(l):
+                want, s = st.oracle_anchor(l, b, g)
+                pool = np.arange(int(st.pg.seq_lens[b]))
+            else:
+                want, pool, s = st.oracle_refine(l, b, g, A_gpu[b, g])
+            stats[check_set(sel[b, g], want, s, pool, wl.kappa, f"{label} l{l} b{b} g{g}")] += 1
+            G = wl.group
+            check_attn(o[b, g * G:(g + 1) * G], st.oracle_attend(l, b, g, sel[b, g]),
+                       f"{label} l{l} b{b} g{g}")
+    say(f"[{label}] sets: {stats}")
+    return stats
+
+
+def test_decode_chain_tiny():
+    st = Setup(synth.TINY_4K, [0, 1])
+    s = _run_chain(st, [0, 1], [(0, 0), (0, 1)], "tiny")
+    assert s["exact"] == 4
+
+
+def test_decode_chain_planted_small():
+    wl = synth.scaled(synth.LLAMA_128K_PLANTED, name="planted-16k", wid=170, context=16384,
+                      kappa=512, n_clusters=16, num_layers=8, anchor_stride=4)
+    st = Setup(wl, range(8))
+    _run_chain(st, range(8), [(0, g) for g in range(8)], "planted-16k")
+
+
+def test_determinism():
+    st = Setup(synth.TINY_4K, [0, 1])
+    res = []
+    for _ in range(2):
+        anchor, li, out = st.idx_buf(), st.idx_buf(), st.out_buf()
+        for l in (0, 1):
+            tsa.prism_decode_layer(l, st.kv[l], st.q[l], st.params, anchor, li, out, st.ws)
+        torch.cuda.synchronize()
+        res.append((li.cpu().numpy(), out.cpu().numpy().view(np.uint32)))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+# ---------------------------------------------------------------------- full sizes
+FULL = [
+    (synth.LLAMA_32K, [0, 1, 7], None),
+    (synth.LLAMA_128K_PLANTED, [0, 1, 7], None),
+    (synth.BATCHED_16, [0, 1, 3], 6),
+    (synth.LONG_4x128K, [0, 1, 7], 5),
+]
+
+
+@pytest.mark.parametrize("wl,layers,nsample", FULL, ids=[f[0].name for f in FULL])
+def test_full_size_sampled(wl, layers, nsample):
+    say(f"[full] {wl.name}: generating layers {layers}")
+    st = Setup(wl, layers)
+    probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    if nsample is not None:
+        rng = np.random.default_rng(wl.wid)
+        probs = [probs[i] for i in sorted(rng.choice(len(probs), nsample, replace=False))]
+    _run_chain(st, layers, probs, wl.name)

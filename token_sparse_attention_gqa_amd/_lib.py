@@ -1,0 +1,250 @@
+"""ctypes binding of libprism.so: argument marshalling only.  Every computation
+happens in the HIP library; there is no fallback path.  Tensor arguments are
+PyTorch device tensors (PyTorch is used for device memory and streams); bf16
+arrays may be given as torch.bfloat16, torch.int16 or torch.uint16 tensors
+holding the bit patterns."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libprism.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "prism.h")
+
+PRISM_OK, PRISM_ERR_INVALID_ARG, PRISM_ERR_UNSUPPORTED, PRISM_ERR_WORKSPACE, PRISM_ERR_HIP = \
+    0, -1, -2, -3, -4
+
+
+class PrismError(RuntimeError):
+    def __init__(self, status: int, fn: str, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+class KVCacheStruct(ctypes.Structure):
+    _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("min_seq_len", ctypes.c_int32)]
+
+
+class ParamsStruct(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("kappa", ctypes.c_int32),
+                ("anchor_stride", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "prism_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(KVCacheStruct),
+                                               ctypes.POINTER(ParamsStruct)]),
+    "prism_score_topk": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), _P,
+                                        ctypes.POINTER(ParamsStruct), _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "prism_refine_topk": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), _P,
+                                         ctypes.POINTER(ParamsStruct), _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "prism_sparse_attn": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), _P,
+                                         ctypes.POINTER(ParamsStruct), _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "prism_decode_layer": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
+                                          ctypes.POINTER(ParamsStruct), _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
+    "prism_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "prism_last_error": (ctypes.c_char_p, []),
+    "prism_abi_version": (ctypes.c_int32, []),
+    "prism_profile_events": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
+    "prism_profile_launches": (ctypes.c_int64, [ctypes.c_int32]),
+}
+
+# prism_kernel_kind
+KERNEL_KINDS = {"anchor_score": 0, "pool_score": 1, "select": 2, "attention": 3, "combine": 4,
+                "pool_plan": 5, "hist_reset": 6}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(token_sparse_attention_gqa_amd.build.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/prism.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^PRISM_API\s+[\w\s\*]+?\b(prism_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, fn: str):
+    if status != PRISM_OK:
+        msg = lib().prism_last_error().decode(errors="replace")
+        raise PrismError(status, fn, msg)
+
+
+# ---------------------------------------------------------------------------
+# Marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t, name, *, itemsize=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if isinstance(t, int):          # raw device address
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if itemsize is not None and t.element_size() != itemsize:
+        raise ValueError(f"{name} must have {itemsize}-byte elements")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class KVCache:
+    """One layer's paged cache: keeps the tensors alive and the C struct."""
+
+    def __init__(self, k_pages, v_pages, block_table, seq_lens, *, max_seq_len, min_seq_len,
+                 head_dim=None, page_size=None):
+        self.tensors = (k_pages, v_pages, block_table, seq_lens)
+        num_pages, hkv, ps, d = k_pages.shape
+        if tuple(v_pages.shape) != tuple(k_pages.shape):
+            raise ValueError("k_pages and v_pages must have the same shape")
+        batch, max_pages = block_table.shape
+        self.struct = KVCacheStruct(
+            _ptr(k_pages, "k_pages", itemsize=2), _ptr(v_pages, "v_pages", itemsize=2),
+            _ptr(block_table, "block_table", itemsize=4), _ptr(seq_lens, "seq_lens", itemsize=4),
+            batch, hkv, head_dim if head_dim is not None else d,
+            page_size if page_size is not None else ps, num_pages, max_pages, int(max_seq_len),
+            int(min_seq_len))
+
+    def with_layer(self, k_pages, v_pages) -> "KVCache":
+        """Same sequences and block table, another layer's K/V arrays."""
+        bt, sl = self.tensors[2], self.tensors[3]
+        s = self.struct
+        return KVCache(k_pages, v_pages, bt, sl, max_seq_len=s.max_seq_len,
+                       min_seq_len=s.min_seq_len, head_dim=s.head_dim, page_size=s.page_size)
+
+
+def params(num_q_heads, kappa, anchor_stride=1, window=0, softmax_scale=0.0) -> ParamsStruct:
+    return ParamsStruct(int(num_q_heads), int(kappa), int(anchor_stride), int(window),
+                        float(softmax_scale))
+
+
+def _ws(workspace):
+    if workspace is None:
+        return None, 0
+    if isinstance(workspace, tuple):
+        return workspace
+    return _ptr(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
+# ---------------------------------------------------------------------------
+# The C entry points, same names
+# ---------------------------------------------------------------------------
+
+def prism_workspace_size(kv: KVCache, p: ParamsStruct) -> int:
+    return int(lib().prism_workspace_size(ctypes.byref(kv.struct), ctypes.byref(p)))
+
+
+def prism_score_topk(kv, q, p, idx_out, scores_out=None, workspace=None, stream=None):
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_score_topk(ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2),
+                                  ctypes.byref(p), _ptr(idx_out, "idx_out", itemsize=4),
+                                  _ptr(scores_out, "scores_out", itemsize=4, optional=True),
+                                  ws, nbytes, _stream(stream)), "prism_score_topk")
+
+
+def prism_refine_topk(kv, q, p, anchor_idx, idx_out, pool_out=None, pool_len_out=None,
+                      pool_scores_out=None, workspace=None, stream=None):
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_refine_topk(
+        ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2), ctypes.byref(p),
+        _ptr(anchor_idx, "anchor_idx", itemsize=4), _ptr(idx_out, "idx_out", itemsize=4),
+        _ptr(pool_out, "pool_out", itemsize=4, optional=True),
+        _ptr(pool_len_out, "pool_len_out", itemsize=4, optional=True),
+        _ptr(pool_scores_out, "pool_scores_out", itemsize=4, optional=True),
+        ws, nbytes, _stream(stream)), "prism_refine_topk")
+
+
+def prism_sparse_attn(kv, q, p, idx, out, workspace=None, stream=None):
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_sparse_attn(ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2),
+                                   ctypes.byref(p), _ptr(idx, "idx", itemsize=4),
+                                   _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
+           "prism_sparse_attn")
+
+
+def prism_decode_layer(layer, kv, q, p, anchor_idx, layer_idx_out, out, workspace=None,
+                       stream=None):
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_decode_layer(int(layer), ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2),
+                                    ctypes.byref(p), _ptr(anchor_idx, "anchor_idx", itemsize=4),
+                                    _ptr(layer_idx_out, "layer_idx_out", itemsize=4,
+                                         optional=True),
+                                    _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
+           "prism_decode_layer")
+
+
+def prism_status_string(status: int) -> str:
+    return lib().prism_status_string(int(status)).decode()
+
+
+def prism_last_error() -> str:
+    return lib().prism_last_error().decode(errors="replace")
+
+
+def prism_abi_version() -> int:
+    return int(lib().prism_abi_version())
+
+
+def prism_profile_events(kind, start_events, stop_events):
+    """start_events / stop_events: lists of torch.cuda.Event (timing enabled) or
+    raw hipEvent_t handles; empty lists switch profiling of that kind off."""
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    n = len(start_events)
+    if len(stop_events) != n:
+        raise ValueError("need as many stop events as start events")
+
+    def handle(e):
+        if isinstance(e, int):
+            return e
+        if e.cuda_event == 0:        # torch creates the event lazily on first record
+            e.record()
+        return e.cuda_event
+
+    arr_t = ctypes.c_void_p * max(n, 1)
+    starts = arr_t(*[handle(e) for e in start_events])
+    stops = arr_t(*[handle(e) for e in stop_events])
+    _check(lib().prism_profile_events(k, starts if n else None, stops if n else None, n),
+           "prism_profile_events")
+
+
+def prism_profile_launches(kind) -> int:
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    return int(lib().prism_profile_launches(k))

@@ -1,0 +1,269 @@
+// Host side of the C ABI declared in include/prism.h: argument validation,
+// workspace carving and the order in which kernels are enqueued.
+#include "prism.h"
+#include "prism_internal.hpp"
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+using prism::Geometry;
+using prism::Workspace;
+
+thread_local std::string g_last_error;
+
+prism_status fail(prism_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Validates the cache description and parameters and fills the geometry.
+prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* g) {
+  if (!kv || !p) return fail(PRISM_ERR_INVALID_ARG, "kv cache and params must not be NULL");
+  if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_lens)
+    return fail(PRISM_ERR_INVALID_ARG, "k_pages, v_pages, block_table and seq_lens must not be NULL");
+  if (kv->batch < 1 || kv->num_kv_heads < 1 || p->num_q_heads < 1)
+    return fail(PRISM_ERR_INVALID_ARG, "batch, num_kv_heads and num_q_heads must be >= 1");
+  if (p->num_q_heads % kv->num_kv_heads != 0)
+    return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = p->num_q_heads / kv->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PRISM_ERR_UNSUPPORTED, "group size num_q_heads/num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (kv->head_dim != prism::kHeadDim) return fail(PRISM_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (kv->page_size != prism::kPageSize) return fail(PRISM_ERR_UNSUPPORTED, "page_size must be 64");
+  if (kv->num_pages < 1 || kv->max_pages_per_seq < 1)
+    return fail(PRISM_ERR_INVALID_ARG, "num_pages and max_pages_per_seq must be >= 1");
+  if (kv->max_seq_len < 1 || kv->min_seq_len < 1 || kv->min_seq_len > kv->max_seq_len)
+    return fail(PRISM_ERR_INVALID_ARG, "need 1 <= min_seq_len <= max_seq_len");
+  if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages_per_seq * kv->page_size)
+    return fail(PRISM_ERR_INVALID_ARG, "max_seq_len exceeds max_pages_per_seq * page_size");
+  if (kv->max_seq_len > prism::kMaxSeqLen)
+    return fail(PRISM_ERR_UNSUPPORTED, "max_seq_len above 524288");
+  if ((int64_t)kv->batch * kv->num_kv_heads > (1 << 22) ||
+      (int64_t)kv->batch * p->num_q_heads > (1 << 24))
+    return fail(PRISM_ERR_UNSUPPORTED, "batch * heads too large");
+  if (p->kappa < 1 || p->kappa > kv->min_seq_len)
+    return fail(PRISM_ERR_INVALID_ARG, "need 1 <= kappa <= min_seq_len");
+  if (p->kappa > prism::kMaxKappa) return fail(PRISM_ERR_UNSUPPORTED, "kappa above 8192");
+  if (p->window < 0) return fail(PRISM_ERR_INVALID_ARG, "window must be >= 0");
+  if (p->anchor_stride < 1) return fail(PRISM_ERR_INVALID_ARG, "anchor_stride must be >= 1");
+  if (!std::isfinite(p->softmax_scale))
+    return fail(PRISM_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(kv->k_pages, 16) || !aligned(kv->v_pages, 16))
+    return fail(PRISM_ERR_INVALID_ARG, "k_pages and v_pages must be 16-byte aligned");
+  if (!aligned(kv->block_table, 4) || !aligned(kv->seq_lens, 4))
+    return fail(PRISM_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
+
+  g->k_pages = kv->k_pages;
+  g->v_pages = kv->v_pages;
+  g->block_table = kv->block_table;
+  g->seq_lens = kv->seq_lens;
+  g->batch = kv->batch;
+  g->hkv = kv->num_kv_heads;
+  g->hq = p->num_q_heads;
+  g->group = G;
+  g->num_pages = kv->num_pages;
+  g->max_pages = kv->max_pages_per_seq;
+  g->max_seq_len = kv->max_seq_len;
+  g->n_cap = (kv->max_seq_len + 63) / 64 * 64;
+  g->kappa = p->kappa;
+  g->window = p->window;
+  g->splits = (p->kappa + prism::kAttnSplit - 1) / prism::kAttnSplit;
+  g->page_stride = (size_t)kv->num_kv_heads * prism::kPageSize * prism::kHeadDim;
+  return PRISM_OK;
+}
+
+prism_status check_q(const uint16_t* q) {
+  if (!q) return fail(PRISM_ERR_INVALID_ARG, "q must not be NULL");
+  if (!aligned(q, 16)) return fail(PRISM_ERR_INVALID_ARG, "q must be 16-byte aligned");
+  return PRISM_OK;
+}
+
+prism_status check_ws(const Geometry& g, void* ws, size_t bytes) {
+  const size_t need = prism::workspace_bytes(g);
+  if (!ws) return fail(PRISM_ERR_WORKSPACE, "workspace must not be NULL");
+  if (!aligned(ws, 256)) return fail(PRISM_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < need)
+    return fail(PRISM_ERR_WORKSPACE, "workspace too small: need " + std::to_string(need) +
+                                         " bytes, got " + std::to_string(bytes));
+  return PRISM_OK;
+}
+
+// A usable device must be current; also clears any stale runtime error so that
+// launch errors reported afterwards are this call's own.
+prism_status check_device() {
+  int n = 0;
+  hipError_t e = hipGetDeviceCount(&n);
+  if (e != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return fail(PRISM_ERR_HIP, std::string("no HIP device available: ") +
+                                   (e != hipSuccess ? hipGetErrorString(e) : "device count is 0"));
+  }
+  (void)hipGetLastError();
+  return PRISM_OK;
+}
+
+prism_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PRISM_OK;
+  return fail(PRISM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+float resolve_scale(const prism_params* p) {
+  return p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)prism::kHeadDim);
+}
+
+#define PRISM_TRY(expr)                 \
+  do {                                  \
+    const prism_status _s = (expr);     \
+    if (_s != PRISM_OK) return _s;      \
+  } while (0)
+
+prism_status run_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
+                        int32_t* out2, hipStream_t s) {
+  PRISM_TRY(hip_check(prism::launch_zero_hist(g, w, s), "histogram reset launch"));
+  PRISM_TRY(hip_check(prism::launch_score(g, w, q, false, s), "scoring launch"));
+  PRISM_TRY(hip_check(prism::launch_select(g, w, false, out, out2, s), "select launch"));
+  return PRISM_OK;
+}
+
+prism_status run_refine(const Geometry& g, const Workspace& w, const uint16_t* q,
+                        const int32_t* anchor, int32_t* out, hipStream_t s) {
+  PRISM_TRY(hip_check(prism::launch_pool_plan(g, w, anchor, s), "pool plan launch"));
+  PRISM_TRY(hip_check(prism::launch_score(g, w, q, true, s), "pool scoring launch"));
+  PRISM_TRY(hip_check(prism::launch_select(g, w, true, out, nullptr, s), "select launch"));
+  return PRISM_OK;
+}
+
+prism_status copy_rows(void* dst, size_t dst_row, const void* src, size_t src_row, size_t row,
+                       size_t rows, hipStream_t s, const char* what) {
+  return hip_check(hipMemcpy2DAsync(dst, dst_row, src, src_row, row, rows,
+                                    hipMemcpyDeviceToDevice, s),
+                   what);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t prism_workspace_size(const prism_kv_cache* kv, const prism_params* params) {
+  Geometry g;
+  if (resolve(kv, params, &g) != PRISM_OK) return 0;
+  return prism::workspace_bytes(g);
+}
+
+prism_status prism_score_topk(const prism_kv_cache* kv, const uint16_t* q,
+                              const prism_params* params, int32_t* idx_out, float* scores_out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (!idx_out) return fail(PRISM_ERR_INVALID_ARG, "idx_out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace w = prism::carve_workspace(workspace, g);
+  PRISM_TRY(run_anchor(g, w, q, idx_out, nullptr, s));
+  if (scores_out)
+    PRISM_TRY(copy_rows(scores_out, (size_t)g.max_seq_len * 4, w.scores, (size_t)g.n_cap * 4,
+                        (size_t)g.max_seq_len * 4, (size_t)g.problems(), s, "scores copy"));
+  return PRISM_OK;
+}
+
+prism_status prism_refine_topk(const prism_kv_cache* kv, const uint16_t* q,
+                               const prism_params* params, const int32_t* anchor_idx,
+                               int32_t* idx_out, int32_t* pool_out, int32_t* pool_len_out,
+                               float* pool_scores_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (!anchor_idx || !idx_out)
+    return fail(PRISM_ERR_INVALID_ARG, "anchor_idx and idx_out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace w = prism::carve_workspace(workspace, g);
+  PRISM_TRY(run_refine(g, w, q, anchor_idx, idx_out, s));
+  const size_t rowb = (size_t)g.max_seq_len * 4, caprow = (size_t)g.n_cap * 4;
+  if (pool_out)
+    PRISM_TRY(copy_rows(pool_out, rowb, w.pool_pos, caprow, rowb, g.problems(), s, "pool copy"));
+  if (pool_scores_out)
+    PRISM_TRY(copy_rows(pool_scores_out, rowb, w.scores, caprow, rowb, g.problems(), s,
+                        "pool scores copy"));
+  if (pool_len_out)
+    PRISM_TRY(hip_check(hipMemcpyAsync(pool_len_out, w.pool_len, (size_t)g.problems() * 4,
+                                       hipMemcpyDeviceToDevice, s),
+                        "pool length copy"));
+  return PRISM_OK;
+}
+
+prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_t* q,
+                               const prism_params* params, const int32_t* idx, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (!idx || !out) return fail(PRISM_ERR_INVALID_ARG, "idx and out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace w = prism::carve_workspace(workspace, g);
+  return hip_check(prism::launch_attention(g, w, q, idx, resolve_scale(params), out, s),
+                   "attention launch");
+}
+
+prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const uint16_t* q,
+                                const prism_params* params, int32_t* anchor_idx,
+                                int32_t* layer_idx_out, float* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (layer < 0) return fail(PRISM_ERR_INVALID_ARG, "layer must be >= 0");
+  if (!anchor_idx || !out) return fail(PRISM_ERR_INVALID_ARG, "anchor_idx and out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace w = prism::carve_workspace(workspace, g);
+  const int32_t* sel;
+  if (layer % params->anchor_stride == 0) {
+    PRISM_TRY(run_anchor(g, w, q, anchor_idx, layer_idx_out, s));
+    sel = anchor_idx;
+  } else {
+    int32_t* dst = layer_idx_out ? layer_idx_out : w.idx_tmp;
+    PRISM_TRY(run_refine(g, w, q, anchor_idx, dst, s));
+    sel = dst;
+  }
+  return hip_check(prism::launch_attention(g, w, q, sel, resolve_scale(params), out, s),
+                   "attention launch");
+}
+
+prism_status prism_profile_events(int32_t kind, void* const* start_events,
+                                  void* const* stop_events, int32_t count) {
+  if (!prism::set_profile_events(kind, start_events, stop_events, count))
+    return fail(PRISM_ERR_INVALID_ARG, "bad kernel kind or negative count");
+  return PRISM_OK;
+}
+
+int64_t prism_profile_launches(int32_t kind) { return prism::profile_launches(kind); }
+
+const char* prism_status_string(prism_status status) {
+  switch (status) {
+    case PRISM_OK: return "ok";
+    case PRISM_ERR_INVALID_ARG: return "invalid argument";
+    case PRISM_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case PRISM_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PRISM_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* prism_last_error(void) { return g_last_error.c_str(); }
+
+int32_t prism_abi_version(void) { return PRISM_ABI_VERSION; }
+
+}  // extern "C"
