@@ -68,8 +68,8 @@ class Hip:
 def launches_per_step(wl):
     na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     nr = wl.num_layers - na
-    return {"anchor_score": na, "hist_reset": na, "pool_plan": nr, "pool_score": nr,
-            "select": wl.num_layers, "attention": wl.num_layers, "combine": wl.num_layers}
+    return {"anchor_score": na, "refine_score": nr, "select": wl.num_layers,
+            "attention": wl.num_layers}
 
 
 def kernel_source_hash():
@@ -207,8 +207,9 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step():
+        s = torch.cuda.current_stream()   # the capture stream while a graph is recorded
         for l in range(wl.num_layers):
-            tsa.prism_decode_layer(l, kv_dev[l], q_dev[l], p, anchor, None, outs[l], ws, stream)
+            tsa.prism_decode_layer(l, kv_dev[l], q_dev[l], p, anchor, None, outs[l], ws, s)
 
     for _ in range(args.warmup):
         step()
@@ -267,7 +268,7 @@ def main():
     n_anchor = per_step["anchor_score"]
     step_bytes = n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
     algo = {"anchor_score": anchor_bytes,
-            "pool_score": (sum(pool_bytes) / len(pool_bytes)) if pool_bytes else 0,
+            "refine_score": (sum(pool_bytes) / len(pool_bytes)) if pool_bytes else 0,
             "attention": attn_bytes}
     for kind, k in kernels.items():
         if kind in algo and k["avg_us"] > 0:

@@ -29,7 +29,7 @@
  *     the calling thread.
  *   - Supported shapes: head_dim 128, page_size 64, group size
  *     G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, 1 <= kappa <= 8192,
- *     max_seq_len <= 524288.  Anything else returns PRISM_ERR_UNSUPPORTED.
+ *     max_seq_len <= 262144.  Anything else returns PRISM_ERR_UNSUPPORTED.
  */
 #ifndef PRISM_H
 #define PRISM_H
@@ -108,8 +108,12 @@ typedef struct {
 
 /* Bytes of device workspace every compute entry point needs for these shapes
  * (0 when the arguments are invalid).  The workspace must be 256-byte aligned;
- * its contents need no initialisation and are scratch between calls.  Calls
- * that run concurrently must not share a workspace. */
+ * its contents need no initialisation.  Besides scratch it carries one piece
+ * of state: the refinement pool that the latest anchor-layer selection
+ * (prism_score_topk, or prism_decode_layer at an anchor layer) derived from
+ * the set it wrote, which prism_decode_layer's refined layers re-score (the
+ * candidate cache of Algorithm 1).  Calls that run concurrently must not share
+ * a workspace. */
 PRISM_API size_t prism_workspace_size(const prism_kv_cache* kv, const prism_params* params);
 
 /*
@@ -156,10 +160,13 @@ PRISM_API prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_
 
 /*
  * One layer of Algorithm 1.  If layer % anchor_stride == 0 the layer is an
- * anchor: select as prism_score_topk and store the set in anchor_idx.
- * Otherwise it is refined against anchor_idx (which must hold the nearest
- * preceding anchor's set: calling a refined layer first is the caller's error)
- * as prism_refine_topk.  Then SparseAttn over the layer's set into out.
+ * anchor: select as prism_score_topk, store the set in anchor_idx and its
+ * refinement pool in the workspace.  Otherwise the layer is refined as
+ * prism_refine_topk would refine it against anchor_idx, re-scoring the pool
+ * the nearest preceding anchor layer left in the same workspace: the layers
+ * of one decode step share anchor_idx and the workspace, and calling a refined
+ * layer before any anchor layer is the caller's error.  Then SparseAttn over
+ * the layer's set into out.
  *   anchor_idx     int32 [batch][num_kv_heads][kappa], state carried between
  *                  the layers of one decode step (written by anchors, read by
  *                  refined layers).
@@ -175,14 +182,12 @@ PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* k
  * Optional instrumentation for benchmarks.  Kernel kinds launched by the calls
  * above: */
 typedef enum {
-  PRISM_KERNEL_ANCHOR_SCORE = 0, /* relevance of every cached token (anchor layers)  */
-  PRISM_KERNEL_POOL_SCORE = 1,   /* relevance of a refined layer's pool             */
-  PRISM_KERNEL_SELECT = 2,       /* top-kappa selection                             */
-  PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the selected set      */
-  PRISM_KERNEL_COMBINE = 4,      /* merge of the attention splits                   */
-  PRISM_KERNEL_POOL_PLAN = 5,    /* refined-layer pool construction                 */
-  PRISM_KERNEL_HIST_RESET = 6,   /* histogram reset before anchor scoring           */
-  PRISM_KERNEL_KINDS = 7
+  PRISM_KERNEL_ANCHOR_SCORE = 0, /* anchor layer: relevance of every cached token        */
+  PRISM_KERNEL_REFINE_SCORE = 1, /* refined layer: relevance of the pool                 */
+  PRISM_KERNEL_SELECT = 2,       /* top-kappa of every (sequence, KV head) list          */
+  PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the set + merge of splits  */
+  PRISM_KERNEL_POOL_BUILD = 4,   /* pool of an anchor set given to prism_refine_topk     */
+  PRISM_KERNEL_KINDS = 5
 } prism_kernel_kind;
 
 /*

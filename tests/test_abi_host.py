@@ -141,3 +141,4 @@ def test_profile_hook_argument_checks():
     assert lib.prism_profile_events(0, None, None, 0) == L.PRISM_OK
     assert lib.prism_profile_launches(0) == 0
     assert lib.prism_profile_launches(42) == -1
+    assert lib.prism_profile_launches(3) == 0

@@ -63,8 +63,8 @@ _SIGS = {
 }
 
 # prism_kernel_kind
-KERNEL_KINDS = {"anchor_score": 0, "pool_score": 1, "select": 2, "attention": 3, "combine": 4,
-                "pool_plan": 5, "hist_reset": 6}
+KERNEL_KINDS = {"anchor_score": 0, "refine_score": 1, "select": 2, "attention": 3,
+                "pool_build": 4}
 
 _lib = None
 

@@ -42,7 +42,7 @@ prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* 
   if ((int64_t)kv->max_seq_len > (int64_t)kv->max_pages_per_seq * kv->page_size)
     return fail(PRISM_ERR_INVALID_ARG, "max_seq_len exceeds max_pages_per_seq * page_size");
   if (kv->max_seq_len > prism::kMaxSeqLen)
-    return fail(PRISM_ERR_UNSUPPORTED, "max_seq_len above 524288");
+    return fail(PRISM_ERR_UNSUPPORTED, "max_seq_len above 262144");
   if ((int64_t)kv->batch * kv->num_kv_heads > (1 << 22) ||
       (int64_t)kv->batch * p->num_q_heads > (1 << 24))
     return fail(PRISM_ERR_UNSUPPORTED, "batch * heads too large");
@@ -124,18 +124,7 @@ float resolve_scale(const prism_params* p) {
 
 prism_status run_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                         int32_t* out2, hipStream_t s) {
-  PRISM_TRY(hip_check(prism::launch_zero_hist(g, w, s), "histogram reset launch"));
-  PRISM_TRY(hip_check(prism::launch_score(g, w, q, false, s), "scoring launch"));
-  PRISM_TRY(hip_check(prism::launch_select(g, w, false, out, out2, s), "select launch"));
-  return PRISM_OK;
-}
-
-prism_status run_refine(const Geometry& g, const Workspace& w, const uint16_t* q,
-                        const int32_t* anchor, int32_t* out, hipStream_t s) {
-  PRISM_TRY(hip_check(prism::launch_pool_plan(g, w, anchor, s), "pool plan launch"));
-  PRISM_TRY(hip_check(prism::launch_score(g, w, q, true, s), "pool scoring launch"));
-  PRISM_TRY(hip_check(prism::launch_select(g, w, true, out, nullptr, s), "select launch"));
-  return PRISM_OK;
+  return hip_check(prism::launch_anchor(g, w, q, out, out2, s), "anchor selection launch");
 }
 
 prism_status copy_rows(void* dst, size_t dst_row, const void* src, size_t src_row, size_t row,
@@ -187,7 +176,8 @@ prism_status prism_refine_topk(const prism_kv_cache* kv, const uint16_t* q,
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  PRISM_TRY(run_refine(g, w, q, anchor_idx, idx_out, s));
+  PRISM_TRY(hip_check(prism::launch_pool_build(g, w, anchor_idx, s), "pool build launch"));
+  PRISM_TRY(hip_check(prism::launch_refine(g, w, q, idx_out, s), "refined selection launch"));
   const size_t rowb = (size_t)g.max_seq_len * 4, caprow = (size_t)g.n_cap * 4;
   if (pool_out)
     PRISM_TRY(copy_rows(pool_out, rowb, w.pool_pos, caprow, rowb, g.problems(), s, "pool copy"));
@@ -212,7 +202,8 @@ prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_t* q,
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  return hip_check(prism::launch_attention(g, w, q, idx, resolve_scale(params), out, s),
+  PRISM_TRY(hip_check(prism::launch_zero_counters(g, w, s), "counter reset launch"));
+  return hip_check(prism::launch_attention(g, w, q, idx, false, resolve_scale(params), out, s),
                    "attention launch");
 }
 
@@ -229,16 +220,13 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  const int32_t* sel;
   if (layer % params->anchor_stride == 0) {
     PRISM_TRY(run_anchor(g, w, q, anchor_idx, layer_idx_out, s));
-    sel = anchor_idx;
   } else {
     int32_t* dst = layer_idx_out ? layer_idx_out : w.idx_tmp;
-    PRISM_TRY(run_refine(g, w, q, anchor_idx, dst, s));
-    sel = dst;
+    PRISM_TRY(hip_check(prism::launch_refine(g, w, q, dst, s), "refined selection launch"));
   }
-  return hip_check(prism::launch_attention(g, w, q, sel, resolve_scale(params), out, s),
+  return hip_check(prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params), out, s),
                    "attention launch");
 }
 

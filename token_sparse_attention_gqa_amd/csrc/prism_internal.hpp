@@ -8,15 +8,17 @@
 
 namespace prism {
 
-constexpr int kHeadDim = 128;       // elements per K/V row
-constexpr int kPageSize = 64;       // tokens per page
-constexpr int kHistBits = 12;       // leading key bits histogrammed by the scoring kernel
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kScoreChunk = 1024;   // list entries scored by one workgroup
-constexpr int kAttnSplit = 64;      // selected tokens attended by one workgroup
-constexpr int kSelectCap = 4096;    // threshold-bin candidates the select kernel holds in LDS
+constexpr int kHeadDim = 128;         // elements per K/V row
+constexpr int kPageSize = 64;         // tokens per page
+constexpr int kSelThreads = 1024;     // threads of a selection workgroup
+constexpr int kScoreThreads = 256;    // threads of a relevance workgroup
+constexpr int kAnchorEntries = 1024;  // cached tokens scored by one anchor-layer workgroup
+constexpr int kPoolEntries = 512;     // pool entries scored by one refined-layer workgroup
+constexpr int kAttnSplit = 64;        // selected tokens attended by one workgroup
+constexpr int kAttnThreads = 256;
 constexpr int kMaxKappa = 8192;
-constexpr int kMaxSeqLen = 524288;
+constexpr int kMaxSeqLen = 262144;
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;  // row id of an empty selection slot
 
 // Shapes of one call, resolved and validated on the host.
 struct Geometry {
@@ -36,23 +38,25 @@ struct Geometry {
   int window;
   int splits;       // attention splits per problem
   size_t page_stride;  // elements per physical page: hkv * page * head_dim
-  int problems() const { return batch * hkv; }
+  __host__ __device__ int problems() const { return batch * hkv; }
 };
 
-// Carved workspace regions (device pointers).
+// Carved workspace regions (device pointers).  A row id r addresses the K/V
+// row at element offset r * head_dim of a layer's page array.
 struct Workspace {
-  uint32_t* hist;     // [P][kHistBins]
-  float* scores;      // [P][n_cap] relevance in list order
-  int32_t* pool_pos;  // [P][n_cap] positions of a refined layer's pool
-  int32_t* pool_len;  // [P]
-  int32_t* idx_tmp;   // [P][kappa]
-  float* part_o;      // [P][splits][G][head_dim]
-  float* part_ml;     // [P][splits][G][2]  (running max, sum of exponentials)
+  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernel
+  float* scores;          // [P][n_cap] relevance in list order
+  int32_t* pool_pos;      // [P][n_cap] refinement pool: positions, ascending
+  uint32_t* pool_row;     // [P][n_cap] refinement pool: row ids
+  int32_t* pool_len;      // [P]
+  uint32_t* sel_row;      // [P][kappa] row ids of the latest selection
+  int32_t* idx_tmp;       // [P][kappa]
+  float* part_o;          // [P][splits][G][head_dim]
+  float* part_ml;         // [P][splits][G][2]  (max logit, sum of exponentials)
 };
 
 // Kernel kinds, numbered as prism_kernel_kind in prism.h.
-enum KernelKind { kAnchorScore = 0, kPoolScore, kSelect, kAttention, kCombine, kPoolPlan,
-                  kHistReset, kKernelKinds };
+enum KernelKind { kAnchorScore = 0, kRefineScore, kSelect, kAttention, kPoolBuild, kKernelKinds };
 
 // Benchmark instrumentation: per kind, a ring of (start, stop) events that the
 // dispatch of each launch records.
@@ -62,14 +66,23 @@ int64_t profile_launches(int kind);
 size_t workspace_bytes(const Geometry& g);
 Workspace carve_workspace(void* base, const Geometry& g);
 
-hipError_t launch_zero_hist(const Geometry& g, const Workspace& w, hipStream_t s);
-hipError_t launch_pool_plan(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
-                            hipStream_t s);
-hipError_t launch_score(const Geometry& g, const Workspace& w, const uint16_t* q, bool pool,
-                        hipStream_t s);
-hipError_t launch_select(const Geometry& g, const Workspace& w, bool pool, int32_t* out,
+// Anchor layer: relevance of every cached token, top-kappa into out (and out2),
+// the selection's row ids, and the refinement pool of the selected set.
+hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s);
+// Refinement pool of an anchor set given in device memory.
+hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
+                             hipStream_t s);
+// Refined layer over the workspace's pool: relevance of the pool, top-kappa
+// into out, and the selection's row ids.
+hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
+                         hipStream_t s);
+// Zeroes the attention arrival counters (before a standalone attention call).
+hipError_t launch_zero_counters(const Geometry& g, const Workspace& w, hipStream_t s);
+// SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with
+// use_sel_rows, over the row ids the latest selection left in the workspace.
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
-                            const int32_t* idx, float scale, float* out, hipStream_t s);
+                            const int32_t* idx, bool use_sel_rows, float scale, float* out,
+                            hipStream_t s);
 
 }  // namespace prism

@@ -1,17 +1,19 @@
 // HIP kernels for gfx950 (CDNA4): token-sparse GQA decode attention with
 // proposal-refined cross-layer index sharing ("Prism Attention", arXiv
-// 2610.22985).
+// 2610.22985).  Three kernels per layer:
 //
-//   score_kernel      relevance (Eq. 9 / Eq. 1) of every entry of a token list
-//                     (all cached tokens at an anchor layer, the refinement pool
-//                     at a refined layer) with one MFMA per 16 tokens x 32 dims,
-//                     plus a 4096-bin histogram of the scores' leading bits.
-//   pool_plan_kernel  the refined layer's pool: union of [i-w, i+w] over the
-//                     anchor's ascending set, as disjoint runs, flattened.
-//   select_kernel     exact top-kappa (Eq. 2 / Eq. 6) by radix select on
-//                     order-preserving 32-bit keys; lower position wins ties.
-//   attn_kernel       SparseAttn of Algorithm 1 over one split of the set,
-//   combine_kernel    and the fixed-order merge of the splits.
+//   score_anchor_kernel / score_pool_kernel
+//       relevance (Eq. 9 / Eq. 1) of every cached token at an anchor layer, or
+//       of the refinement pool at a refined layer (Eq. 5), one MFMA per 16
+//       tokens x 32 dimensions;
+//   select_kernel
+//       the exact top-kappa (Eq. 2 / Eq. 6) of each (sequence, KV head) list,
+//       the row ids of the selected tokens, and at an anchor layer the pool
+//       that the following refined layers re-score (the candidate cache that
+//       proposal layers populate in Algorithm 1);
+//   attn_kernel
+//       SparseAttn of Algorithm 1 over one split of the selected set; the last
+//       split of each (sequence, KV head) merges all splits in split order.
 #include "prism_internal.hpp"
 
 #include <hip/hip_ext.h>
@@ -26,7 +28,12 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSelThreads = 1024;
+constexpr int NT = kSelThreads;
+constexpr int kSmall = 8192;    // lists up to this length are selected entirely in LDS
+constexpr int kSample = 8192;   // most entries of a longer list sampled to bracket the kappa-th key
+constexpr int kCand = 4096;     // bracketed candidates held in LDS
+constexpr int kPassUnroll = 8;  // 16-byte loads in flight per thread in the list pass
+constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the pool build
 
 // Monotone map of a float to uint32: a > b  <=>  key(a) > key(b); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -41,23 +48,82 @@ __device__ __forceinline__ int seq_len_of(const Geometry& g, int b) {
   return clampi(g.seq_lens[b], 0, g.max_seq_len);
 }
 
-// Element offset of token `pos` of sequence b, KV head h in the paged cache.
-__device__ __forceinline__ size_t row_offset(const Geometry& g, int b, int h, int pos) {
-  int page = g.block_table[(size_t)b * g.max_pages + (pos >> 6)];
-  page = clampi(page, 0, g.num_pages - 1);
-  return (size_t)page * g.page_stride + ((size_t)h * kPageSize + (pos & (kPageSize - 1))) * kHeadDim;
+__device__ __forceinline__ int phys_page(const Geometry& g, int b, int logical) {
+  return clampi(g.block_table[(size_t)b * g.max_pages + logical], 0, g.num_pages - 1);
+}
+
+// Row id of token `pos` of sequence b, KV head h: its row in the page array.
+__device__ __forceinline__ uint32_t row_id_of_page(const Geometry& g, int page, int h, int pos) {
+  return (uint32_t)page * (uint32_t)(g.hkv * kPageSize) + (uint32_t)(h * kPageSize) +
+         (uint32_t)(pos & (kPageSize - 1));
+}
+__device__ __forceinline__ uint32_t row_id(const Geometry& g, int b, int h, int pos) {
+  return row_id_of_page(g, phys_page(g, b, pos >> 6), h, pos);
+}
+
+// Workgroup -> (problem, index within problem).  Dispatch places workgroup i
+// on XCD i % 8; when the problem count allows, all workgroups of a problem
+// land on one XCD so that its scores stay in that XCD's L2.
+__device__ __forceinline__ void map_block(int bid, int P, int W, int* p, int* w) {
+  if ((P & 7) == 0) {
+    const int x = bid & 7, s = bid >> 3;
+    *p = x + 8 * (s / W);
+    *w = s % W;
+  } else {
+    *p = bid / W;
+    *w = bid % W;
+  }
+}
+
+// Attention partials handed from one workgroup to another within a launch are
+// written and read with device-scope accesses (sc1: written through to, and
+// read from, the device coherence point), so no cache-wide L2 writeback or
+// invalidate is needed.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrival counter of the workgroups of one problem: zero when the launch
+// starts (zeroed by an earlier kernel of the same call) and reset to zero by
+// the last arrival.  Every wave first waits for its own device-scope stores to
+// complete; one fetch-add per workgroup.  True in every thread of the last one.
+__device__ bool publish_and_arrive(uint32_t* ctr, uint32_t total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old =
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (old + 1u == total) ? 1 : 0;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+__device__ __forceinline__ void ticket_reset(uint32_t* ctr) {
+  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Orders this workgroup's global stores and L2 atomics before its later
+// cache-bypassing loads (used inside one workgroup only).
+__device__ __forceinline__ void wg_global_sync() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 // MFMA A-operand fragment of the group's query heads.  Lane l holds head
 // (l % 16) (zero when >= G) and, for step s, the 16-byte chunk g4 + 4s of the
-// head dimension, g4 = l / 16.  The key fragments use the same chunk order, so
-// the four steps together contract over all 128 dimensions.
+// head dimension, g4 = l / 16.  Key fragments use the same chunk order, so the
+// four steps together contract over all 128 dimensions.
 template <int G>
 __device__ __forceinline__ void load_q_frag(const uint16_t* q, const Geometry& g, int b, int kvh,
                                             int lane, u32x4 (&qf)[4]) {
   const int j = lane & 15, g4 = lane >> 4;
   if (j < G) {
-    const u32x4* qrow = reinterpret_cast<const u32x4*>(q + ((size_t)b * g.hq + kvh * G + j) * kHeadDim);
+    const u32x4* qrow =
+        reinterpret_cast<const u32x4*>(q + ((size_t)b * g.hq + kvh * G + j) * kHeadDim);
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[s] = qrow[g4 + 4 * s];
   } else {
@@ -73,7 +139,8 @@ __device__ __forceinline__ f32x4 qk_tile(const u32x4 (&qf)[4], const u32x4 (&kf)
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qf[s]),
-                                                  __builtin_bit_cast(bf16x8, kf[s]), acc, 0, 0, 0);
+                                                  __builtin_bit_cast(bf16x8, kf[s]), acc, 0, 0,
+                                                  0);
   return acc;
 }
 
@@ -99,23 +166,29 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
   return v;
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
+}
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(v, d);
+    const int o = __shfl_up(v, d);
     if (lane >= d) v += o;
   }
   return v;
 }
 
-// Exclusive prefix sum over the NT threads of the block; *total gets the sum.
-// tmp: at least NT/64 + 1 ints of LDS.  Contains barriers: call uniformly.
-template <int NT>
+// Exclusive prefix sum over the T threads of the block; *total gets the sum.
+// tmp: at least T/64 + 1 ints of LDS.  Contains barriers: call uniformly.
+template <int T>
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
-  constexpr int NW = NT / 64;
+  constexpr int NW = T / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int inc = wave_incl_scan(v);
+  __syncthreads();
   if (lane == 63) tmp[w] = inc;
   __syncthreads();
   if (w == 0) {
@@ -127,394 +200,655 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   __syncthreads();
   const int r = tmp[w] + inc - v;
   *total = tmp[NW];
-  __syncthreads();
   return r;
 }
 
-// ---------------------------------------------------------------------------
-// Histogram reset (anchor layers; the pool plan resets it for refined layers)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void zero_hist_kernel(uint32_t* hist) {
-  uint32_t* h = hist + (size_t)blockIdx.x * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0u;
-}
+struct Bin {
+  int bin, above, count;
+};
 
-// ---------------------------------------------------------------------------
-// Refined-layer pool.  With the anchor set ascending and every window of equal
-// width, the union of [a_k - w, a_k + w] is the disjoint union over k of
-// [max(lo_k, hi_{k-1} + 1), hi_k]: run k only adds what run k-1 did not cover.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void pool_plan_kernel(Geometry g, Workspace ws,
-                                                        const int32_t* __restrict__ anchor) {
-  extern __shared__ int32_t plan[];  // run start [kappa], then run offset [kappa]
-  __shared__ int tmp[8];
-  const int p = blockIdx.x, b = p / g.hkv, t = threadIdx.x;
-  const int K = g.kappa;
-  int32_t* st = plan;
-  int32_t* off = plan + K;
-  const int L = seq_len_of(g, b);
-  const int w = g.window < L ? g.window : L;
-
-  uint32_t* h = ws.hist + (size_t)p * kHistBins;
-  for (int i = t; i < kHistBins; i += 256) h[i] = 0u;
-
-  const int32_t* a = anchor + (size_t)p * K;
-  const int per = (K + 255) / 256;
-  const int k0 = min(K, t * per), k1 = min(K, k0 + per);
+// One wave: in a histogram of NB bins, the bin holding the need-th largest
+// element (1-based, counting down from the top bin), the count of higher bins
+// and the bin's own count; bin = -1 if the histogram holds fewer than need.
+// Lane l owns NB/64 consecutive bins; their sums (read in a rotated order that
+// keeps the lanes on distinct LDS banks) are scanned across the wave, then the
+// owning lane's bins are scanned across the wave, one bin per lane.  Result is
+// uniform over the wave.
+template <int NB>
+__device__ Bin wave_find_bin(const uint32_t* h, int need) {
+  constexpr int R = NB / 64;
+  const int lane = threadIdx.x & 63;
+  const int top = NB - 1 - R * lane;
   int sum = 0;
-  for (int k = k0; k < k1; ++k) {
-    const int ai = a[k];
-    int s0 = 0, len = 0;
-    if (ai >= 0 && ai < L) {
-      const int lo = max(ai - w, 0), hi = min(ai + w, L - 1);
-      int prev_hi = -1;
-      if (k > 0) {
-        const int ap = a[k - 1];
-        if (ap >= 0 && ap < L) prev_hi = min(ap + w, L - 1);
-      }
-      s0 = max(lo, prev_hi + 1);
-      len = max(0, hi - s0 + 1);
-    }
-    st[k] = s0;
-    off[k] = len;
-    sum += len;
-  }
-  int total;
-  int ex = block_excl_scan<256>(sum, tmp, &total);
-  for (int k = k0; k < k1; ++k) {
-    const int len = off[k];
-    off[k] = ex;
-    ex += len;
-  }
-  const int n = min(total, g.n_cap);
-  if (t == 0) ws.pool_len[p] = n;
-  __syncthreads();
-  int32_t* out = ws.pool_pos + (size_t)p * g.n_cap;
-  for (int e = t; e < n; e += 256) {
-    int lo = 0, hi = K - 1;  // largest k with off[k] <= e
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (off[mid] <= e) lo = mid; else hi = mid - 1;
-    }
-    out[e] = st[lo] + (e - off[lo]);
-  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) sum += (int)h[top - ((r + lane) & (R - 1))];
+  const int incl = wave_incl_scan(sum);
+  const int excl = incl - sum;
+  const unsigned long long hit = __ballot(excl < need && incl >= need);
+  if (!hit) return Bin{-1, 0, 0};
+  const int src = __ffsll((unsigned long long)hit) - 1;
+  const int base = __shfl(excl, src);
+  const int src_top = NB - 1 - R * src;
+  const int c = lane < R ? (int)h[src_top - lane] : 0;
+  const int inc2 = wave_incl_scan(c) + base;
+  const unsigned long long hit2 = __ballot(lane < R && inc2 >= need);
+  const int k = __ffsll((unsigned long long)hit2) - 1;
+  return Bin{src_top - k, __shfl(inc2 - c, k), __shfl(c, k)};
 }
 
 // ---------------------------------------------------------------------------
-// Relevance of a token list (Eq. 9).  One workgroup scores kScoreChunk list
-// entries of one (sequence, KV head); each wave takes 256 of them as 16 tiles of
-// 16 tokens.  Per tile every lane issues four 16-byte loads (the 64-byte
-// quarter-rows of 16 consecutive tokens) and the wave issues four MFMAs.
+// Relevance
 // ---------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void score_kernel(Geometry g, Workspace ws,
-                                                    const uint16_t* __restrict__ q, int chunks,
-                                                    int pool) {
-  __shared__ uint32_t lhist[kHistBins];
-  const int p = blockIdx.x / chunks;
-  const int chunk = blockIdx.x - p * chunks;
-  const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int L = seq_len_of(g, b);
-  const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : L;
-  const int begin = chunk * kScoreChunk;
-  if (L <= 0 || begin >= n) return;  // uniform over the workgroup
-  const int end = min(n, begin + kScoreChunk);
 
-  for (int i = threadIdx.x; i < kHistBins; i += 256) lhist[i] = 0u;
+// Anchor layer: workgroup w of problem p scores tokens [w * kAnchorEntries, +kAnchorEntries)
+// of the cache; each wave takes 256 consecutive tokens = 4 whole pages.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g, Workspace ws,
+                                                                     const uint16_t* __restrict__ q,
+                                                                     int wgs) {
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int n = seq_len_of(g, b);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
+  const int wbase = w * kAnchorEntries + wave * 256;
+  if (wbase >= n) return;
   u32x4 qf[4];
   load_q_frag<G>(q, g, b, kvh, lane, qf);
-  __syncthreads();
-
-  const int32_t* plist = ws.pool_pos + (size_t)p * g.n_cap;
-  float* out = ws.scores + (size_t)p * g.n_cap;
-  const int wbegin = begin + wave * (kScoreChunk / 4);
-#pragma unroll 1
-  for (int t0 = 0; t0 < 16; t0 += 4) {
-    u32x4 kf[4][4];
-    int e[4];
+  float* sc = ws.scores + (size_t)p * g.n_cap;
+  const int last_page = (n - 1) >> 6;
+  const size_t head = (size_t)kvh * kPageSize * kHeadDim;
+  size_t page_off[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      e[u] = wbegin + (t0 + u) * 16 + j;
-      const int es = min(e[u], end - 1);
-      const int pos = clampi(pool ? plist[es] : es, 0, L - 1);
-      const u32x4* row = reinterpret_cast<const u32x4*>(g.k_pages + row_offset(g, b, kvh, pos));
+  for (int r = 0; r < 4; ++r)
+    page_off[r] = (size_t)phys_page(g, b, min((wbase >> 6) + r, last_page)) * g.page_stride + head;
+  // One page (4 tiles of 16 tokens) per step, double-buffered: the next page's
+  // 16 loads are issued before the current page's MFMAs (the scheduling
+  // barriers keep the compiler from interleaving them back into a few loads
+  // in flight).  Addresses stay offsets from the kernel-argument base so the
+  // loads remain global loads.
+  u32x4 kb[2][4][4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) kf[u][s] = __builtin_nontemporal_load(row + g4 + 4 * s);
-    }
+  for (int r = 0; r < 5; ++r) {
+    if (r < 4) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
-      if (g4 == 0 && e[u] < end) {
-        out[e[u]] = m;
-        atomicAdd(&lhist[order_key(m) >> (32 - kHistBits)], 1u);
+      for (int u = 0; u < 4; ++u) {
+        const u32x4* row = reinterpret_cast<const u32x4*>(
+            g.k_pages + page_off[r] + (size_t)((u * 16 + j) * kHeadDim));
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          kb[r & 1][u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
       }
     }
-  }
-  __syncthreads();
-  uint32_t* gh = ws.hist + (size_t)p * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += 256) {
-    const uint32_t c = lhist[i];
-    if (c) atomicAdd(gh + i, c);
+    __builtin_amdgcn_sched_barrier(0);
+    if (r > 0) {
+      const int rp = r - 1;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float m = group_max<G>(qk_tile(qf, kb[rp & 1][u]), g4);
+        const int e = wbase + rp * 64 + u * 16 + j;
+        if (g4 == 0 && e < n) sc[e] = m;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// In a histogram of NB bins, the bin holding the need-th largest element
-// (1-based, counting down from the top bin).  res = {bin, count strictly above,
-// count in bin}; res[0] stays -1 if the histogram holds fewer than need.
+// Refined layer: workgroup w of problem p scores pool entries
+// [w * kPoolEntries, +kPoolEntries) from the pool's row ids; each wave 8 tiles.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, Workspace ws,
+                                                                   const uint16_t* __restrict__ q,
+                                                                   int wgs) {
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int wbase = w * kPoolEntries + wave * (kPoolEntries / 4);
+  if (wbase >= n) return;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  u32x4 qf[4];
+  load_q_frag<G>(q, g, b, kvh, lane, qf);
+  const uint32_t* prow = ws.pool_row + (size_t)p * g.n_cap;
+  float* sc = ws.scores + (size_t)p * g.n_cap;
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  constexpr int kTiles = kPoolEntries / 4 / 16;  // 8
+  uint32_t rid[kTiles];
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) rid[u] = prow[min(wbase + u * 16 + j, n - 1)];
+  u32x4 kf[kTiles][4];
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    const u32x4* row =
+        reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) kf[u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < kTiles; ++u) {
+    const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
+    const int e = wbase + u * 16 + j;
+    if (g4 == 0 && e < n) sc[e] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection
+// ---------------------------------------------------------------------------
+constexpr int kMaxPages = kMaxSeqLen / kPageSize;
+
+struct SelectSmem {
+  int32_t bt[kMaxPages];              // the sequence's block table row (physical pages)
+  uint32_t bitmap[kMaxSeqLen / 32];   // selection marks in list order
+  uint32_t hist[4096 + 1024 + 1024];  // three histogram levels
+  uint32_t cbuf[2 * kCand];           // list keys / sample keys / candidate keys and indices
+  int32_t apos[kMaxKappa];            // the emitted set, for the pool build
+  int tmp[NT / 64 + 1];
+  int res[9];
+  int cnt[2];
+};
+
+struct SelList {
+  const float* sc;       // relevance in list order
+  const int32_t* plist;  // list index -> position (null: identity)
+  const uint32_t* prow;  // list index -> row id (null: from the block table)
+  int n, K, b, kvh;
+  int32_t* o1;
+  int32_t* o2;
+  uint32_t* srow;
+};
+
+__device__ __forceinline__ void emit_entry(const Geometry& g, const SelList& c, int e, int o,
+                                           SelectSmem& sm) {
+  const int pos = c.plist ? c.plist[e] : e;
+  const uint32_t row = c.prow ? c.prow[e] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
+  c.o1[o] = pos;
+  if (c.o2) c.o2[o] = pos;
+  c.srow[o] = row;
+  sm.apos[o] = pos;
+}
+
+__device__ __forceinline__ void emit_empty(const SelList& c, int o, SelectSmem& sm) {
+  c.o1[o] = -1;
+  if (c.o2) c.o2[o] = -1;
+  c.srow[o] = kNoRow;
+  sm.apos[o] = -1;
+}
+
+// Wave 0 finds a bin and publishes it in sm.res[slot..slot+2]; all threads
+// read it after the barrier.
 template <int NB>
-__device__ void find_bin(const uint32_t* h, int need, int* res, int* tmp) {
-  constexpr int R = NB / kSelThreads;
-  const int t = threadIdx.x;
-  if (t == 0) res[0] = -1;
-  int c[R];
-  int sum = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    c[r] = (int)h[NB - 1 - (R * t + r)];
-    sum += c[r];
-  }
-  int total;
-  const int excl = block_excl_scan<kSelThreads>(sum, tmp, &total);
-  if (excl < need && excl + sum >= need) {
-    int acc = excl;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      if (acc + c[r] >= need) {
-        res[0] = NB - 1 - (R * t + r);
-        res[1] = acc;
-        res[2] = c[r];
-        break;
-      }
-      acc += c[r];
+__device__ Bin find_publish(const uint32_t* h, int need, SelectSmem& sm, int slot) {
+  if (threadIdx.x < 64) {
+    const Bin r = wave_find_bin<NB>(h, need);
+    if (threadIdx.x == 0) {
+      sm.res[slot] = r.bin;
+      sm.res[slot + 1] = r.above;
+      sm.res[slot + 2] = r.count;
     }
   }
   __syncthreads();
+  return Bin{sm.res[slot], sm.res[slot + 1], sm.res[slot + 2]};
 }
 
-// ---------------------------------------------------------------------------
-// Exact top-kappa of one (sequence, KV head) list.  The scoring kernel's
-// histogram gives the bin of the kappa-th largest key; one pass over the list
-// marks every entry of a higher bin in an LDS bitmap and gathers the threshold
-// bin into LDS; two 10-bit radix levels there give the exact kappa-th key T.
-// Entries equal to T are taken lowest list index first (list order is position
-// order).  The bitmap, read in order, gives ascending positions.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kSelThreads) void select_kernel(Geometry g, Workspace ws, int pool,
-                                                             int32_t* __restrict__ out,
-                                                             int32_t* __restrict__ out2) {
-  extern __shared__ uint32_t bitmap[];
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t ckey[kSelectCap];
-  __shared__ int32_t cidx[kSelectCap];
-  __shared__ int tmp[kSelThreads / 64 + 1];
-  __shared__ int res[4];
-  __shared__ int ccount;
-
-  const int p = blockIdx.x, b = p / g.hkv, t = threadIdx.x;
-  const int K = g.kappa;
-  const int L = seq_len_of(g, b);
-  const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : L;
-  int32_t* o1 = out + (size_t)p * K;
-  int32_t* o2 = out2 ? out2 + (size_t)p * K : nullptr;
-  const int32_t* plist = ws.pool_pos + (size_t)p * g.n_cap;
-
-  if (n <= K) {  // everything is selected (n == kappa for consistent inputs)
-    for (int e = t; e < K; e += kSelThreads) {
-      const int v = e < n ? (pool ? plist[e] : e) : -1;
-      o1[e] = v;
-      if (o2) o2[e] = v;
-    }
-    return;
-  }
-
-  const float* sc = ws.scores + (size_t)p * g.n_cap;
-  const int words = (n + 31) >> 5;
-  for (int i = t; i < words; i += kSelThreads) bitmap[i] = 0u;
-  for (int i = t; i < kHistBins; i += kSelThreads) h[i] = ws.hist[(size_t)p * kHistBins + i];
-  if (t == 0) ccount = 0;
-  __syncthreads();
-
-  find_bin<kHistBins>(h, K, res, tmp);
-  const int tbin = res[0], need1 = K - res[1], inbin = res[2];
-  if (tbin < 0) {  // histogram inconsistent with the list: only on corrupted workspace
-    for (int e = t; e < K; e += kSelThreads) {
-      o1[e] = -1;
-      if (o2) o2[e] = -1;
-    }
-    return;
-  }
-  const bool fast = inbin <= kSelectCap;
-
-  // Pass 1: lanes hold 4 consecutive entries, 8 lanes one 32-bit bitmap word.
-  for (int base = 0; base < n; base += 4 * kSelThreads) {
-    const int e0 = base + 4 * t;
-    u32x4 raw = {0u, 0u, 0u, 0u};
-    if (e0 < n) raw = *reinterpret_cast<const u32x4*>(sc + e0);
-    uint32_t nib = 0u;
+// Lists of at most kSmall entries: all keys in registers / LDS histograms.
+// Thread t holds entries 8t .. 8t+7, so per-thread counts scanned in thread
+// order give ascending output positions directly.
+__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  const int t = threadIdx.x;
+  uint32_t* h1 = sm.hist;
+  uint32_t* h2 = sm.hist + 4096;
+  uint32_t* h3 = sm.hist + 5120;
+  for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+  const int e0 = 8 * t;
+  uint32_t key[8];
+  {
+    const int ea = e0 < c.n ? e0 : 0;  // entries past n are loaded but not used
+    const u32x4 r0 = *reinterpret_cast<const u32x4*>(c.sc + ea);
+    const u32x4 r1 = *reinterpret_cast<const u32x4*>(c.sc + ea + 4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int e = e0 + c;
-      if (e < n) {
-        const uint32_t key = order_key(__uint_as_float(raw[c]));
-        const int bin = (int)(key >> (32 - kHistBits));
-        if (bin > tbin) {
-          nib |= 1u << c;
-        } else if (bin == tbin && fast) {
-          const int slot = atomicAdd(&ccount, 1);
-          if (slot < kSelectCap) {
-            ckey[slot] = key;
-            cidx[slot] = e;
-          }
-        }
-      }
-    }
-    uint32_t word = nib << (4 * (t & 7));
-    word |= __shfl_xor(word, 1);
-    word |= __shfl_xor(word, 2);
-    word |= __shfl_xor(word, 4);
-    if ((t & 7) == 0 && e0 < n) bitmap[e0 >> 5] = word;
-  }
-  __syncthreads();
-
-  uint32_t T;
-  int need_eq, count_eq;
-  if (fast) {
-    const int nc = min(ccount, kSelectCap);
-    for (int i = t; i < 1024; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
-    for (int c = t; c < nc; c += kSelThreads) atomicAdd(&h[(ckey[c] >> 10) & 1023u], 1u);
-    __syncthreads();
-    find_bin<1024>(h, need1, res, tmp);
-    const uint32_t dA = (uint32_t)res[0];
-    const int need2 = need1 - res[1];
-    for (int i = t; i < 1024; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
-    for (int c = t; c < nc; c += kSelThreads)
-      if (((ckey[c] >> 10) & 1023u) == dA) atomicAdd(&h[ckey[c] & 1023u], 1u);
-    __syncthreads();
-    find_bin<1024>(h, need2, res, tmp);
-    T = ((uint32_t)tbin << 20) | (dA << 10) | (uint32_t)res[0];
-    need_eq = need2 - res[1];
-    count_eq = res[2];
-    for (int c = t; c < nc; c += kSelThreads) {
-      const uint32_t key = ckey[c];
-      const int e = cidx[c];
-      bool take = key > T;
-      if (key == T) {
-        if (count_eq == need_eq) {
-          take = true;
-        } else {  // rank among equal keys by list index
-          int rank = 0;
-          for (int c2 = 0; c2 < nc; ++c2) rank += (ckey[c2] == T && cidx[c2] < e) ? 1 : 0;
-          take = rank < need_eq;
-        }
-      }
-      if (take) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-    }
-  } else {
-    // Threshold bin too large for LDS: resolve the low 20 bits over the list.
-    for (int i = t; i < 1024; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
-    for (int e = t; e < n; e += kSelThreads) {
-      const uint32_t key = order_key(sc[e]);
-      if ((int)(key >> 20) == tbin) atomicAdd(&h[(key >> 10) & 1023u], 1u);
-    }
-    __syncthreads();
-    find_bin<1024>(h, need1, res, tmp);
-    const uint32_t prefix = ((uint32_t)tbin << 10) | (uint32_t)res[0];
-    const int need2 = need1 - res[1];
-    for (int i = t; i < 1024; i += kSelThreads) h[i] = 0u;
-    __syncthreads();
-    for (int e = t; e < n; e += kSelThreads) {
-      const uint32_t key = order_key(sc[e]);
-      if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
-    }
-    __syncthreads();
-    find_bin<1024>(h, need2, res, tmp);
-    T = (prefix << 10) | (uint32_t)res[0];
-    need_eq = need2 - res[1];
-    count_eq = res[2];
-    int run = 0;  // equal keys seen in earlier chunks
-    for (int base = 0; base < n; base += kSelThreads) {
-      const int e = base + t;
-      const bool valid = e < n;
-      const uint32_t key = valid ? order_key(sc[e]) : 0u;
-      const bool gt = valid && key > T && (int)(key >> 20) == tbin;
-      const bool eq = valid && key == T;
-      int tot;
-      const int r = block_excl_scan<kSelThreads>(eq ? 1 : 0, tmp, &tot);
-      if (gt || (eq && run + r < need_eq)) atomicOr(&bitmap[e >> 5], 1u << (e & 31));
-      run += tot;
+    for (int i = 0; i < 4; ++i) {
+      key[i] = order_key(__uint_as_float(r0[i]));
+      key[i + 4] = order_key(__uint_as_float(r1[i]));
     }
   }
-  (void)count_eq;
+  const int nv = clampi(c.n - e0, 0, 8);  // valid entries of this thread
   __syncthreads();
-
-  // Emission in bitmap order = ascending position.
-  const int wpt = (words + kSelThreads - 1) / kSelThreads;
-  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(bitmap[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < nv) atomicAdd(&h1[key[i] >> 20], 1u);
+  __syncthreads();
+  const Bin a = find_publish<4096>(h1, c.K, sm, 0);
+  const int need2 = c.K - a.above;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < nv && (int)(key[i] >> 20) == a.bin) atomicAdd(&h2[(key[i] >> 10) & 1023u], 1u);
+  __syncthreads();
+  const Bin bb = find_publish<1024>(h2, need2, sm, 3);
+  const int need3 = need2 - bb.above;
+  const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < nv && (key[i] >> 10) == pre) atomicAdd(&h3[key[i] & 1023u], 1u);
+  __syncthreads();
+  const Bin cc = find_publish<1024>(h3, need3, sm, 6);
+  const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
+  const int need_eq = need3 - cc.above;
+  uint32_t take = 0u;
+  if (cc.count == need_eq) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nv && key[i] >= T) take |= 1u << i;
+  } else {  // more entries equal T than needed: the lowest list indices win
+    int my_eq = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (i < nv && key[i] == T) ++my_eq;
+    int tot;
+    int r = block_excl_scan<NT>(my_eq, sm.tmp, &tot);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nv && key[i] > T) take |= 1u << i;
+      if (i < nv && key[i] == T) {
+        if (r < need_eq) take |= 1u << i;
+        ++r;
+      }
+    }
+  }
   int total;
-  int o = block_excl_scan<kSelThreads>(cnt, tmp, &total);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t m = bitmap[i];
-    while (m) {
-      const int e = i * 32 + (__ffs(m) - 1);
-      m &= m - 1u;
-      if (o < K) {
-        const int v = pool ? plist[e] : e;
-        o1[o] = v;
-        if (o2) o2[o] = v;
-      }
+  int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (take & (1u << i)) {
+      if (o < c.K) emit_entry(g, c, e0 + i, o, sm);
       ++o;
     }
   }
-  for (int e = total + t; e < K; e += kSelThreads) {
-    o1[e] = -1;
-    if (o2) o2[e] = -1;
+  for (int o2 = total + t; o2 < c.K; o2 += NT) emit_empty(c, o2, sm);
+}
+
+// Longer lists.  A strided sample of at most kSample keys brackets the K-th
+// largest key by 22-bit prefixes [lo22, hi22] (+-4 sigma of the sample count
+// plus slack).  One pass over the list marks entries above the bracket in the
+// bitmap and gathers the bracket into LDS, where three radix levels find the
+// exact K-th key T.  If the bracket misses or overflows, the exact radix runs
+// over the whole list instead.  The bitmap, read in order, gives ascending
+// positions; entries equal to T are taken lowest list index first.
+__device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int n = c.n, K = c.K;
+  uint32_t* h1 = sm.hist;
+  uint32_t* h2 = sm.hist + 4096;
+  uint32_t* h3 = sm.hist + 5120;
+  uint32_t* const ckey = sm.cbuf;
+  int32_t* const cidx = reinterpret_cast<int32_t*>(sm.cbuf + kCand);
+
+  const int S = (n + kSample - 1) / kSample;
+  const int ns = (n + S - 1) / S;
+  const float ks = (float)K * (float)ns / (float)n;
+  const int d = (int)ceilf(4.f * sqrtf(ks * (1.f - ks / (float)ns))) + 16;
+  const int r_hi = (int)floorf(ks) - d, r_lo = (int)ceilf(ks) + d;
+
+  for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+  {
+    uint32_t key[kSample / NT];
+#pragma unroll
+    for (int u = 0; u < kSample / NT; ++u) {
+      const int i = u * NT + t;
+      key[u] = order_key(c.sc[(size_t)(i < ns ? i : 0) * S]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kSample / NT; ++u) {
+      const int i = u * NT + t;
+      if (i < ns) {
+        sm.cbuf[i] = key[u];
+        atomicAdd(&h1[key[u] >> 20], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  if (t < 64) {
+    const Bin bh = r_hi >= 1 ? wave_find_bin<4096>(h1, r_hi) : Bin{-1, 0, 0};
+    const Bin bl = r_lo <= ns ? wave_find_bin<4096>(h1, r_lo) : Bin{-1, 0, 0};
+    if (t == 0) {
+      sm.res[0] = bh.bin;
+      sm.res[1] = bh.above;
+      sm.res[3] = bl.bin;
+      sm.res[4] = bl.above;
+    }
+  }
+  __syncthreads();
+  const int bh = sm.res[0], bh_above = sm.res[1], bl = sm.res[3], bl_above = sm.res[4];
+  for (int i = t; i < ns; i += NT) {
+    const uint32_t key = sm.cbuf[i];
+    const int top = (int)(key >> 20);
+    if (top == bh) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
+    if (top == bl) atomicAdd(&h3[(key >> 10) & 1023u], 1u);
+  }
+  __syncthreads();
+  if (t < 64) {
+    uint32_t hi22 = 0x3FFFFFu, lo22 = 0u;
+    if (bh >= 0) hi22 = ((uint32_t)bh << 10) | (uint32_t)max(wave_find_bin<1024>(h2, r_hi - bh_above).bin, 0);
+    if (bl >= 0) lo22 = ((uint32_t)bl << 10) | (uint32_t)max(wave_find_bin<1024>(h3, r_lo - bl_above).bin, 0);
+    if (t == 0) {
+      sm.res[6] = (int)hi22;
+      sm.res[7] = (int)lo22;
+      sm.cnt[0] = 0;
+      sm.cnt[1] = 0;
+    }
+  }
+  __syncthreads();
+  const uint32_t hi22 = (uint32_t)sm.res[6], lo22 = (uint32_t)sm.res[7];
+  for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;  // for the candidate radix
+
+  // --- one pass over the list: lanes hold 4 consecutive entries, 8 lanes one
+  //     32-bit bitmap word -------------------------------------------------------
+  int above = 0;
+  for (int base = 0; base < n; base += 4 * NT * kPassUnroll) {
+    u32x4 raw[kPassUnroll];
+#pragma unroll
+    for (int u = 0; u < kPassUnroll; ++u) {
+      const int e0 = base + u * 4 * NT + 4 * t;
+      raw[u] = *reinterpret_cast<const u32x4*>(c.sc + (e0 < n ? e0 : 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kPassUnroll; ++u) {
+      const int e0 = base + u * 4 * NT + 4 * t;
+      uint32_t nib = 0u;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int e = e0 + q4;
+        if (e < n) {
+          const uint32_t key = order_key(__uint_as_float(raw[u][q4]));
+          const uint32_t k22 = key >> 10;
+          if (k22 > hi22) {
+            nib |= 1u << q4;
+            ++above;
+          } else if (k22 >= lo22) {
+            const int slot = atomicAdd(&sm.cnt[0], 1);
+            if (slot < kCand) {
+              ckey[slot] = key;
+              cidx[slot] = e;
+            }
+          }
+        }
+      }
+      uint32_t word = nib << (4 * (t & 7));
+      word |= __shfl_xor(word, 1);
+      word |= __shfl_xor(word, 2);
+      word |= __shfl_xor(word, 4);
+      if ((t & 7) == 0 && e0 < n) sm.bitmap[e0 >> 5] = word;
+    }
+  }
+  above = wave_sum_i(above);
+  if (lane == 0) atomicAdd(&sm.cnt[1], above);
+  __syncthreads();
+  const int ncand = sm.cnt[0];
+  const int need = K - sm.cnt[1];
+
+  if (need >= 1 && need <= ncand && ncand <= kCand) {
+    for (int i = t; i < ncand; i += NT) atomicAdd(&h1[ckey[i] >> 20], 1u);
+    __syncthreads();
+    const Bin a = find_publish<4096>(h1, need, sm, 0);
+    for (int i = t; i < ncand; i += NT)
+      if ((int)(ckey[i] >> 20) == a.bin) atomicAdd(&h2[(ckey[i] >> 10) & 1023u], 1u);
+    __syncthreads();
+    const Bin bb = find_publish<1024>(h2, need - a.above, sm, 3);
+    const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+    for (int i = t; i < ncand; i += NT)
+      if ((ckey[i] >> 10) == pre) atomicAdd(&h3[ckey[i] & 1023u], 1u);
+    __syncthreads();
+    const Bin cc = find_publish<1024>(h3, need - a.above - bb.above, sm, 6);
+    const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
+    const int need_eq = need - a.above - bb.above - cc.above;
+    for (int i = t; i < ncand; i += NT) {
+      const uint32_t key = ckey[i];
+      const int e = cidx[i];
+      bool take = key > T;
+      if (key == T) {
+        if (cc.count == need_eq) {
+          take = true;
+        } else {  // rank among equal keys by list index
+          int rank = 0;
+          for (int i2 = 0; i2 < ncand; ++i2) rank += (ckey[i2] == T && cidx[i2] < e) ? 1 : 0;
+          take = rank < need_eq;
+        }
+      }
+      if (take) atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
+    }
+  } else {
+    // exact radix over the whole list
+    for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
+    __syncthreads();
+    const Bin a = find_publish<4096>(h1, K, sm, 0);
+    for (int e = t; e < n; e += NT) {
+      const uint32_t key = order_key(c.sc[e]);
+      if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
+    }
+    __syncthreads();
+    const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
+    const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+    for (int e = t; e < n; e += NT) {
+      const uint32_t key = order_key(c.sc[e]);
+      if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
+    }
+    __syncthreads();
+    const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
+    const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
+    const int need_eq = K - a.above - bb.above - cc.above;
+    int run = 0;  // equal keys in earlier chunks
+    for (int base = 0; base < n; base += NT) {
+      const int e = base + t;
+      const bool valid = e < n;
+      const uint32_t key = valid ? order_key(c.sc[e]) : 0u;
+      const bool eq = valid && key == T;
+      int tot;
+      const int r = block_excl_scan<NT>(eq ? 1 : 0, sm.tmp, &tot);
+      const bool take = valid && (key > T || (eq && run + r < need_eq));
+      const unsigned long long m = __ballot(take);
+      if (lane == 0 && e < n) sm.bitmap[e >> 5] = (uint32_t)m;
+      if (lane == 32 && e < n) sm.bitmap[e >> 5] = (uint32_t)(m >> 32);
+      run += tot;
+    }
+  }
+  __syncthreads();
+
+  // --- emission in bitmap order = ascending position ---------------------------
+  const int words = (n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
+  int total;
+  int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t m = sm.bitmap[i];
+    while (m) {
+      const int e = i * 32 + (__ffs(m) - 1);
+      m &= m - 1u;
+      if (o < K) emit_entry(g, c, e, o, sm);
+      ++o;
+    }
+  }
+  for (int o2 = total + t; o2 < K; o2 += NT) emit_empty(c, o2, sm);
+}
+
+// Refinement pool of one (sequence, KV head) from its ascending anchor set:
+// the union of [a_k - w, a_k + w] clipped to [0, L) is the disjoint union over
+// k of [max(lo_k, hi_{k-1} + 1), hi_k] (all windows have one width, so run k
+// adds exactly what run k-1 did not cover).  Run lengths are scanned for their
+// offsets (kept in LDS), then each wave writes whole runs, 64 entries per
+// store.  anchor_at(k) gives entry k; bt is the sequence's block table in LDS.
+template <typename AnchorAt>
+__device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L,
+                           AnchorAt anchor_at, const int32_t* bt, int* tmp) {
+  const int K = g.kappa, t = threadIdx.x;
+  const int win = min(g.window, L);
+  const int per = (K + NT - 1) / NT;
+  const int j0 = min(K, t * per), j1 = min(K, j0 + per);
+  int starts[kPoolPer], lens[kPoolPer];
+  int sum = 0;
+  int prev = j0 > 0 ? anchor_at(j0 - 1) : -1;
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    const int k = j0 + i;
+    starts[i] = 0;
+    lens[i] = 0;
+    if (k < j1) {
+      const int ai = anchor_at(k);
+      if (ai >= 0 && ai < L) {
+        const int lo = max(ai - win, 0), hi = min(ai + win, L - 1);
+        const int prev_hi = (prev >= 0 && prev < L) ? min(prev + win, L - 1) : -1;
+        starts[i] = max(lo, prev_hi + 1);
+        lens[i] = max(0, hi - starts[i] + 1);
+      }
+      prev = ai;
+    }
+    sum += lens[i];
+  }
+  int total;
+  int e = block_excl_scan<NT>(sum, tmp, &total);
+  const int n = min(total, g.n_cap);
+  if (t == 0) ws.pool_len[p] = n;
+  int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
+  uint32_t* pr = ws.pool_row + (size_t)p * g.n_cap;
+#pragma unroll
+  for (int i = 0; i < kPoolPer; ++i) {
+    // a run's rows are consecutive within a page: one block-table read per page
+    int pos = starts[i];
+    const int run_end = e + lens[i];
+    for (int w = e; w < min(n, run_end);) {
+      const int chunk = min(min(n, run_end) - w, kPageSize - (pos & (kPageSize - 1)));
+      const uint32_t r0 = row_id_of_page(g, bt[pos >> 6], kvh, pos);
+      for (int x = 0; x < chunk; ++x) {
+        pp[w + x] = pos + x;
+        pr[w + x] = r0 + (uint32_t)x;
+      }
+      w += chunk;
+      pos += chunk;
+    }
+    e = run_end;
   }
 }
 
+// Loads the block table row of sequence b (its first ceil(L/64) entries,
+// clamped to physical pages) into LDS.
+__device__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
+  const int np = (L + kPageSize - 1) / kPageSize;
+  for (int i = threadIdx.x; i < np; i += NT) bt[i] = phys_page(g, b, i);
+}
+
+// Top-kappa of one (sequence, KV head) per workgroup; zeroes the problem's
+// attention arrival counter; at an anchor layer also builds the pool.
+template <bool POOL>
+__global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
+                                                    int32_t* __restrict__ out,
+                                                    int32_t* __restrict__ out2) {
+  __shared__ SelectSmem sm;
+  const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
+  const int L = seq_len_of(g, b);
+  const int K = g.kappa;
+  if (threadIdx.x == 0) ws.ticket_attn[p] = 0u;
+  if (!POOL) {
+    load_bt(g, b, L, sm.bt);
+    __syncthreads();
+  }
+  SelList c;
+  c.sc = ws.scores + (size_t)p * g.n_cap;
+  c.plist = POOL ? ws.pool_pos + (size_t)p * g.n_cap : nullptr;
+  c.prow = POOL ? ws.pool_row + (size_t)p * g.n_cap : nullptr;
+  c.n = POOL ? clampi(ws.pool_len[p], 0, g.n_cap) : L;
+  c.K = K;
+  c.b = b;
+  c.kvh = kvh;
+  c.o1 = out + (size_t)p * K;
+  c.o2 = out2 ? out2 + (size_t)p * K : nullptr;
+  c.srow = ws.sel_row + (size_t)p * K;
+  if (c.n <= K) {
+    for (int e = threadIdx.x; e < K; e += NT) {
+      if (e < c.n) emit_entry(g, c, e, e, sm);
+      else emit_empty(c, e, sm);
+    }
+  } else if (c.n <= kSmall) {
+    select_small(g, c, sm);
+  } else {
+    select_large(g, c, sm);
+  }
+  if (!POOL) {
+    __syncthreads();
+    build_pool(g, ws, p, kvh, L, [&](int k) { return sm.apos[k]; }, sm.bt, sm.tmp);
+  }
+}
+
+// Pool of an anchor set given in device memory (one workgroup per problem).
+__global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws,
+                                                        const int32_t* __restrict__ anchor) {
+  __shared__ int32_t bt[kMaxPages];
+  __shared__ int tmp[NT / 64 + 1];
+  const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
+  const int L = seq_len_of(g, b);
+  const int32_t* a = anchor + (size_t)p * g.kappa;
+  load_bt(g, b, L, bt);
+  __syncthreads();
+  build_pool(g, ws, p, kvh, L, [&](int k) { return a[k]; }, bt, tmp);
+}
+
+__global__ void zero_counters_kernel(uint32_t* c, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
-// SparseAttn over one split of kAttnSplit selected tokens of one (sequence,
-// KV head), all G query heads.  Logits by MFMA as in scoring; the split's
-// softmax statistics (max, sum of exponentials) and unnormalised output are
-// written for the combine kernel.
+// SparseAttn over one split of kAttnSplit selected tokens of one (sequence, KV
+// head), all G query heads: logits by MFMA as in scoring; the split's softmax
+// statistics (max logit, sum of exponentials) and unnormalised output go to the
+// workspace; the last split to finish merges all splits in split order.
 // ---------------------------------------------------------------------------
-template <int G>
-__global__ __launch_bounds__(256) void attn_kernel(Geometry g, Workspace ws,
-                                                   const uint16_t* __restrict__ q,
-                                                   const int32_t* __restrict__ idx, float scale) {
+template <int G, bool ROWS>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspace ws,
+                                                            const uint16_t* __restrict__ q,
+                                                            const int32_t* __restrict__ idx,
+                                                            float scale,
+                                                            float* __restrict__ out) {
   __shared__ float lg[G][kAttnSplit];
   __shared__ float red[4][G][kHeadDim];
   __shared__ float sm[G], sl[G];
+  __shared__ int last;
   const int splits = g.splits;
-  const int p = blockIdx.x / splits, s = blockIdx.x - p * splits;
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int L = seq_len_of(g, b);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane & 15, g4 = lane >> 4;
 
-  const int t = s * kAttnSplit + wave * 16 + j;
-  int pos = t < g.kappa ? idx[(size_t)p * g.kappa + t] : -1;
-  const bool valid = pos >= 0 && pos < L;
-  if (!valid) pos = 0;
-  const size_t roff = row_offset(g, b, kvh, pos);
+  const int ti = s * kAttnSplit + wave * 16 + j;
+  bool valid;
+  uint32_t row;
+  if (ROWS) {
+    row = ti < g.kappa ? ws.sel_row[(size_t)p * g.kappa + ti] : kNoRow;
+    const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+    valid = row <= max_row;
+    if (!valid) row = 0u;
+  } else {
+    const int L = seq_len_of(g, b);
+    const int pos = ti < g.kappa ? idx[(size_t)p * g.kappa + ti] : -1;
+    valid = pos >= 0 && pos < L;
+    row = row_id(g, b, kvh, valid ? pos : 0);
+  }
+  const size_t roff = (size_t)row * kHeadDim;
 
   u32x4 kf[4];
   const u32x4* krow = reinterpret_cast<const u32x4*>(g.k_pages + roff);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) kf[s4] = krow[g4 + 4 * s4];
   uint32_t vv[16];
-  const uint32_t lo = (uint32_t)roff, hi = (uint32_t)(roff >> 32);
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    const size_t o = (size_t)(uint32_t)__shfl((int)lo, jj) |
-                     ((size_t)(uint32_t)__shfl((int)hi, jj) << 32);
-    vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + o)[lane];
+    const uint32_t rj = (uint32_t)__shfl((int)row, jj);
+    vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
   }
   u32x4 qf[4];
   load_q_frag<G>(q, g, b, kvh, lane, qf);
@@ -559,68 +893,102 @@ __global__ __launch_bounds__(256) void attn_kernel(Geometry g, Workspace ws,
   }
   __syncthreads();
   float* po = ws.part_o + ((size_t)p * splits + s) * G * kHeadDim;
-  for (int o = threadIdx.x; o < G * kHeadDim; o += 256) {
+  for (int o = t; o < G * kHeadDim; o += kAttnThreads) {
     const int i = o / kHeadDim, d = o - i * kHeadDim;
-    po[o] = (red[0][i][d] + red[1][i][d]) + (red[2][i][d] + red[3][i][d]);
+    st_dev(po + o, (red[0][i][d] + red[1][i][d]) + (red[2][i][d] + red[3][i][d]));
   }
-  if (threadIdx.x < G) {
-    float* pm = ws.part_ml + (((size_t)p * splits + s) * G + threadIdx.x) * 2;
-    pm[0] = sm[threadIdx.x];
-    pm[1] = sl[threadIdx.x];
+  if (t < G) {
+    float* pm = ws.part_ml + (((size_t)p * splits + s) * G + t) * 2;
+    st_dev(pm, sm[t]);
+    st_dev(pm + 1, sl[t]);
   }
-}
 
-// Merge of the splits in split order (deterministic, no float atomics).
-template <int G>
-__global__ __launch_bounds__(kHeadDim) void combine_kernel(Geometry g, Workspace ws, float* out) {
-  const int bq = blockIdx.x, b = bq / g.hq, h = bq - b * g.hq;
-  const int kvh = h / G, i = h - kvh * G;
-  const int p = b * g.hkv + kvh, d = threadIdx.x, splits = g.splits;
+  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, &last)) return;
+
+  // Merge: the splits' (max, sum) pairs go to LDS, then each output element
+  // reads its per-split partial values (independent device-scope loads).
   const float* pml = ws.part_ml + (size_t)p * splits * G * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[(s * G + i) * 2]);
-  float lsum = 0.f, o = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < splits; ++s) {
-      const float ms = pml[(s * G + i) * 2];
-      if (ms == -INFINITY) continue;
-      const float f = __expf(ms - M);
-      lsum += pml[(s * G + i) * 2 + 1] * f;
-      o += ws.part_o[(((size_t)p * splits + s) * G + i) * kHeadDim + d] * f;
+  const float* pob = ws.part_o + (size_t)p * splits * G * kHeadDim;
+  float* ml = &red[0][0][0];  // 2 * G * splits <= 4 * G * kHeadDim floats
+  for (int i = t; i < 2 * G * splits; i += kAttnThreads) ml[i] = ld_dev(pml + i);
+  __syncthreads();
+  for (int o = t; o < G * kHeadDim; o += kAttnThreads) {
+    const int i = o / kHeadDim, d = o - i * kHeadDim;
+    float M = -INFINITY;
+    for (int x = 0; x < splits; ++x) M = fmaxf(M, ml[(x * G + i) * 2]);
+    float lsum = 0.f, acc2 = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 16
+      for (int x = 0; x < splits; ++x) {
+        const float mx = ml[(x * G + i) * 2];
+        const float f = (mx == -INFINITY) ? 0.f : __expf(mx - M);
+        lsum += ml[(x * G + i) * 2 + 1] * f;
+        acc2 += ld_dev(pob + ((size_t)x * G + i) * kHeadDim + d) * f;
+      }
     }
+    out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = lsum > 0.f ? acc2 / lsum : 0.f;
   }
-  out[((size_t)b * g.hq + h) * kHeadDim + d] = lsum > 0.f ? o / lsum : 0.f;
+  if (t == 0) ticket_reset(&ws.ticket_attn[p]);
 }
 
-size_t select_lds_bytes(const Geometry& g) { return (size_t)(g.n_cap / 32) * sizeof(uint32_t); }
-
-}  // namespace
-
 // ---------------------------------------------------------------------------
-// Host-side launchers
+// Host side
 // ---------------------------------------------------------------------------
-namespace {
-
 struct ProfileRing {
   std::vector<hipEvent_t> starts, stops;
   int64_t launches = 0;
 };
 ProfileRing g_profile[kKernelKinds];
 
-// Launches `kernel`; if the kind has an event ring, the dispatch records the
+// Launches `kernel`; if its kind has an event ring, the dispatch records the
 // ring's next pair at kernel start and end.
 template <typename... KArgs, typename... Args>
-void launch(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+void launch(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s,
             Args... args) {
   ProfileRing& r = g_profile[kind];
   if (!r.starts.empty()) {
     const size_t i = (size_t)(r.launches++ % (int64_t)r.starts.size());
-    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, s, r.starts[i], r.stops[i], 0,
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, r.starts[i], r.stops[i], 0,
                           static_cast<KArgs>(args)...);
   } else {
-    hipLaunchKernelGGL(kernel, grid, block, lds, s, static_cast<KArgs>(args)...);
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, static_cast<KArgs>(args)...);
   }
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int G>
+void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+                           hipStream_t s) {
+  const int wgs = (g.n_cap + kAnchorEntries - 1) / kAnchorEntries;
+  launch(kAnchorScore, score_anchor_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
+         g, w, q, wgs);
+}
+
+template <int G>
+void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+                         hipStream_t s) {
+  const int wgs = (g.n_cap + kPoolEntries - 1) / kPoolEntries;
+  launch(kRefineScore, score_pool_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s, g,
+         w, q, wgs);
+}
+
+template <int G, bool ROWS>
+void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+                        const int32_t* idx, float scale, float* out, hipStream_t s) {
+  launch(kAttention, attn_kernel<G, ROWS>, dim3(g.problems() * g.splits), dim3(kAttnThreads), s,
+         g, w, q, idx, scale, out);
+}
+
+#define PRISM_BY_GROUP(FN, ...)                      \
+  switch (g.group) {                                 \
+    case 1: FN<1>(__VA_ARGS__); break;               \
+    case 2: FN<2>(__VA_ARGS__); break;               \
+    case 4: FN<4>(__VA_ARGS__); break;               \
+    case 8: FN<8>(__VA_ARGS__); break;               \
+    case 16: FN<16>(__VA_ARGS__); break;             \
+    default: return hipErrorInvalidValue;            \
+  }
 
 }  // namespace
 
@@ -643,18 +1011,18 @@ int64_t profile_launches(int kind) {
   return g_profile[kind].launches;
 }
 
-static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
-  o += align256(P * kHistBins * 4);
-  o += align256(P * (size_t)g.n_cap * 4);
-  o += align256(P * (size_t)g.n_cap * 4);
-  o += align256(P * 4);
-  o += align256(P * (size_t)g.kappa * 4);
-  o += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);
-  o += align256(P * (size_t)g.splits * g.group * 2 * 4);
+  o += align256(P * 4);                                          // ticket_attn
+  o += align256(P * (size_t)g.n_cap * 4);                        // scores
+  o += align256(P * (size_t)g.n_cap * 4);                        // pool_pos
+  o += align256(P * (size_t)g.n_cap * 4);                        // pool_row
+  o += align256(P * 4);                                          // pool_len
+  o += align256(P * (size_t)g.kappa * 4);                        // sel_row
+  o += align256(P * (size_t)g.kappa * 4);                        // idx_tmp
+  o += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);  // part_o
+  o += align256(P * (size_t)g.splits * g.group * 2 * 4);         // part_ml
   return o;
 }
 
@@ -662,14 +1030,18 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   const size_t P = (size_t)g.problems();
   char* c = static_cast<char*>(base);
   Workspace w;
-  w.hist = reinterpret_cast<uint32_t*>(c);
-  c += align256(P * kHistBins * 4);
+  w.ticket_attn = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * 4);
   w.scores = reinterpret_cast<float*>(c);
   c += align256(P * (size_t)g.n_cap * 4);
   w.pool_pos = reinterpret_cast<int32_t*>(c);
   c += align256(P * (size_t)g.n_cap * 4);
+  w.pool_row = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * (size_t)g.n_cap * 4);
   w.pool_len = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4);
+  w.sel_row = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * (size_t)g.kappa * 4);
   w.idx_tmp = reinterpret_cast<int32_t*>(c);
   c += align256(P * (size_t)g.kappa * 4);
   w.part_o = reinterpret_cast<float*>(c);
@@ -678,78 +1050,58 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   return w;
 }
 
-hipError_t launch_zero_hist(const Geometry& g, const Workspace& w, hipStream_t s) {
-  launch(kHistReset, zero_hist_kernel, dim3(g.problems()), dim3(256), 0, s, w.hist);
-  return hipGetLastError();
-}
-
-hipError_t launch_pool_plan(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
-                            hipStream_t s) {
-  const size_t lds = (size_t)2 * g.kappa * sizeof(int32_t);
-  static bool attr_done = false;
-  if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(pool_plan_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((size_t)2 * kMaxKappa * sizeof(int32_t)));
-    attr_done = true;
-  }
-  launch(kPoolPlan, pool_plan_kernel, dim3(g.problems()), dim3(256), lds, s, g, w, anchor_idx);
-  return hipGetLastError();
-}
-
-template <int G>
-static void launch_score_g(const Geometry& g, const Workspace& w, const uint16_t* q, bool pool,
-                           hipStream_t s) {
-  const int chunks = (g.n_cap + kScoreChunk - 1) / kScoreChunk;
-  launch(pool ? kPoolScore : kAnchorScore, score_kernel<G>, dim3(g.problems() * chunks), dim3(256),
-         0, s, g, w, q, chunks, pool ? 1 : 0);
-}
-
-hipError_t launch_score(const Geometry& g, const Workspace& w, const uint16_t* q, bool pool,
-                        hipStream_t s) {
-  switch (g.group) {
-    case 1: launch_score_g<1>(g, w, q, pool, s); break;
-    case 2: launch_score_g<2>(g, w, q, pool, s); break;
-    case 4: launch_score_g<4>(g, w, q, pool, s); break;
-    case 8: launch_score_g<8>(g, w, q, pool, s); break;
-    case 16: launch_score_g<16>(g, w, q, pool, s); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_select(const Geometry& g, const Workspace& w, bool pool, int32_t* out,
+hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const size_t lds = select_lds_bytes(g);
-  static bool attr_done = false;
-  if (!attr_done) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)((size_t)kMaxSeqLen / 32 * sizeof(uint32_t)));
-    attr_done = true;
-  }
-  launch(kSelect, select_kernel, dim3(g.problems()), dim3(kSelThreads), lds, s, g, w, pool ? 1 : 0,
-         out, out2);
+  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
   return hipGetLastError();
 }
 
-template <int G>
-static void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q,
-                               const int32_t* idx, float scale, float* out, hipStream_t s) {
-  launch(kAttention, attn_kernel<G>, dim3(g.problems() * g.splits), dim3(256), 0, s, g, w, q, idx,
-         scale);
-  launch(kCombine, combine_kernel<G>, dim3(g.batch * g.hq), dim3(kHeadDim), 0, s, g, w, out);
+hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
+                             hipStream_t s) {
+  launch(kPoolBuild, pool_build_kernel, dim3(g.problems()), dim3(NT), s, g, w, anchor_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
+                         hipStream_t s) {
+  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w, out,
+         static_cast<int32_t*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_counters(const Geometry& g, const Workspace& w, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3((g.problems() + 255) / 256), dim3(256), 0, s,
+                     w.ticket_attn, g.problems());
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
-                            const int32_t* idx, float scale, float* out, hipStream_t s) {
-  switch (g.group) {
-    case 1: launch_attention_g<1>(g, w, q, idx, scale, out, s); break;
-    case 2: launch_attention_g<2>(g, w, q, idx, scale, out, s); break;
-    case 4: launch_attention_g<4>(g, w, q, idx, scale, out, s); break;
-    case 8: launch_attention_g<8>(g, w, q, idx, scale, out, s); break;
-    case 16: launch_attention_g<16>(g, w, q, idx, scale, out, s); break;
-    default: return hipErrorInvalidValue;
+                            const int32_t* idx, bool use_sel_rows, float scale, float* out,
+                            hipStream_t s) {
+  if (use_sel_rows) {
+    switch (g.group) {
+      case 1: launch_attention_g<1, true>(g, w, q, idx, scale, out, s); break;
+      case 2: launch_attention_g<2, true>(g, w, q, idx, scale, out, s); break;
+      case 4: launch_attention_g<4, true>(g, w, q, idx, scale, out, s); break;
+      case 8: launch_attention_g<8, true>(g, w, q, idx, scale, out, s); break;
+      case 16: launch_attention_g<16, true>(g, w, q, idx, scale, out, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (g.group) {
+      case 1: launch_attention_g<1, false>(g, w, q, idx, scale, out, s); break;
+      case 2: launch_attention_g<2, false>(g, w, q, idx, scale, out, s); break;
+      case 4: launch_attention_g<4, false>(g, w, q, idx, scale, out, s); break;
+      case 8: launch_attention_g<8, false>(g, w, q, idx, scale, out, s); break;
+      case 16: launch_attention_g<16, false>(g, w, q, idx, scale, out, s); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
