@@ -154,6 +154,9 @@ def main():
                     help="budget of the CPU-oracle baseline sample (0 skips it)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured as one HIP graph")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times and "
+                         "exit: the known-size reference for hardware byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -163,6 +166,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe > 0:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
 
     import synth
     import token_sparse_attention_gqa_amd as tsa
