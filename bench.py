@@ -66,10 +66,12 @@ class Hip:
 
 
 def launches_per_step(wl):
+    import synth
     na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     nr = wl.num_layers - na
+    L = int(synth.paging(wl).seq_lens.max())
     return {"anchor_score": na, "refine_score": nr, "select": wl.num_layers,
-            "attention": wl.num_layers}
+            "attention": wl.num_layers, "classify": na if (L > 8192 and L > wl.kappa) else 0}
 
 
 def kernel_source_hash():

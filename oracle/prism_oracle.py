@@ -123,7 +123,7 @@ def default_scale(head_dim: int) -> float:
 # ---------------------------------------------------------------------------
 
 def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size):
-    """Proposal (anchor) layer, Alg. 1 lines 4-7 with bf16 keys: score every
+    """Proposal (anchor) layer of Algorithm 1, with bf16 keys: score every
     cached token, keep the exact top-kappa.  Returns (selected, scores)."""
     pos = np.arange(length, dtype=np.int64)
     s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pos, page_size))
@@ -132,7 +132,7 @@ def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, pag
 
 def refined_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size,
                    anchor_positions, w):
-    """Refined layer, Eqs. 5-6 and Alg. 1 lines 8-10: re-score only inside the
+    """Refined layer of Algorithm 1 (Eqs. 5-6): re-score only inside the
     pool built from the anchor's set, keep the top-kappa there.
     Returns (selected, pool, scores over the pool)."""
     pool = window_pool(anchor_positions, w, length)

@@ -112,6 +112,33 @@ def test_exact_ties_go_to_lowest_position():
     assert list(got[0, 1]) == list(dup_pos[:kappa])
 
 
+@pytest.mark.parametrize("L,kappa", [(3000, 100), (20000, 1000)])
+def test_concentrated_scores_and_long_ties(L, kappa):
+    """Head 0: every row equal (one score repeated L times).  Head 1: one key
+    row scaled by 2^16, so every other score sits inside one 1/4096 slice of
+    the score range.  Lists below and above 8192 entries."""
+    rng = np.random.default_rng(8)
+    G = 4
+    base = rng.standard_normal((L, 128)).astype(np.float32)
+    tie = synth.f32_to_bf16_bits(rng.standard_normal(128).astype(np.float32))
+    rows0 = np.repeat(tie[None], L, 0)
+    base[L // 3] *= 65536.0
+    rows1 = synth.f32_to_bf16_bits(base)
+    q = synth.f32_to_bf16_bits(rng.standard_normal((1, 2 * G, 128)).astype(np.float32))
+    kp, bt = _hand_cache([rows0, rows1], [L])
+    kv = tsa.KVCache(dev(kp), dev(kp), dev(bt), dev(np.array([L], np.int32)), max_seq_len=L,
+                     min_seq_len=L)
+    p = tsa.params(2 * G, kappa)
+    ws = torch.empty(tsa.prism_workspace_size(kv, p), dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((1, 2, kappa), dtype=torch.int32, device="cuda")
+    tsa.prism_score_topk(kv, dev(q), p, idx, None, ws)
+    got = idx.cpu().numpy()
+    assert list(got[0, 0]) == list(range(kappa))
+    qf = oracle.bf16_to_f64(q[0, G:2 * G])
+    want, s = oracle.anchor_select(qf, kp, bt[0], 1, L, kappa, 64)
+    check_set(got[0, 1], want, s, np.arange(L), kappa, f"outlier L{L}")
+
+
 # --------------------------------------------------------------------------- refine
 def test_refine_stage_isolated_tiny():
     st = Setup(synth.TINY_4K, [0, 1])

@@ -18,6 +18,8 @@ constexpr int kAttnSplit = 64;        // selected tokens attended by one workgro
 constexpr int kAttnThreads = 256;
 constexpr int kMaxKappa = 8192;
 constexpr int kMaxSeqLen = 262144;
+constexpr int kCoarseBins = 4096;   // anchor-layer score histogram: top 12 bits of the order key
+constexpr int kMaxCand = 4096;      // threshold-bin entries an anchor selection ranks exactly
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;  // row id of an empty selection slot
 
 // Shapes of one call, resolved and validated on the host.
@@ -44,6 +46,12 @@ struct Geometry {
 // Carved workspace regions (device pointers).  A row id r addresses the K/V
 // row at element offset r * head_dim of a layer's page array.
 struct Workspace {
+  uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram; followed by
+  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered (zeroed together with ghist)
+  int32_t* sel_meta;      // [P][4] threshold bin, entries above it, entries in it
+  uint32_t* cand_key;     // [P][kMaxCand] order keys of the threshold-bin entries
+  int32_t* cand_idx;      // [P][kMaxCand] their list indices
+  uint32_t* gbits;        // [P][n_cap / 32] marks of the entries above the threshold bin
   uint32_t* ticket_attn;  // [P] arrival counters of the attention kernel
   float* scores;          // [P][n_cap] relevance in list order
   int32_t* pool_pos;      // [P][n_cap] refinement pool: positions, ascending
@@ -56,7 +64,15 @@ struct Workspace {
 };
 
 // Kernel kinds, numbered as prism_kernel_kind in prism.h.
-enum KernelKind { kAnchorScore = 0, kRefineScore, kSelect, kAttention, kPoolBuild, kKernelKinds };
+enum KernelKind {
+  kAnchorScore = 0,
+  kRefineScore,
+  kSelect,
+  kAttention,
+  kPoolBuild,
+  kClassify,
+  kKernelKinds
+};
 
 // Benchmark instrumentation: per kind, a ring of (start, stop) events that the
 // dispatch of each launch records.

@@ -32,8 +32,12 @@ constexpr int NT = kSelThreads;
 constexpr int kSmall = 8192;    // lists up to this length are selected entirely in LDS
 constexpr int kSample = 8192;   // most entries of a longer list sampled to bracket the kappa-th key
 constexpr int kCand = 4096;     // bracketed candidates held in LDS
-constexpr int kPassUnroll = 8;  // 16-byte loads in flight per thread in the list pass
+constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the list pass
 constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the pool build
+constexpr int kClsThreads = 256;
+constexpr int kClsEntries = 8192;         // anchor-list entries classified by one workgroup
+static_assert(kMaxCand <= kCand, "candidates of the threshold bin fit the LDS candidate buffer");
+static_assert(kMaxKappa <= 2 * kCand, "pool-build run offsets fit the LDS candidate buffer");
 
 // Monotone map of a float to uint32: a > b  <=>  key(a) > key(b); -0 == +0.
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -156,51 +160,73 @@ __device__ __forceinline__ float group_max(const f32x4& acc, int g4) {
   return m;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d));
+// Lane movement inside a wave by DPP (GCN/CDNA controls): row_shr:n moves
+// lane i - n of the same 16-lane row to lane i; row_bcast:15 sends lane 15 of
+// each row to the next row, row_bcast:31 lane 31 to rows 2 and 3; quad_perm
+// permutes inside groups of four lanes.  Lanes with no source (or a row left
+// out by the row mask) get `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+
+// Inclusive scan of an associative op over the wave (ident: its identity);
+// lane 63 ends with the result over all 64 lanes.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t ident, Op op) {
+  v = op(v, dpp<kRowShr1, 0xf>(ident, v));
+  v = op(v, dpp<kRowShr2, 0xf>(ident, v));
+  v = op(v, dpp<kRowShr4, 0xf>(ident, v));
+  v = op(v, dpp<kRowShr8, 0xf>(ident, v));
+  v = op(v, dpp<kRowBcast15, 0xa>(ident, v));
+  v = op(v, dpp<kRowBcast31, 0xc>(ident, v));
   return v;
+}
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  const uint32_t r = wave_scan(__float_as_uint(v), __float_as_uint(-INFINITY), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  });
+  return __uint_as_float(lane63(r));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
-}
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
-  return v;
+  const uint32_t r = wave_scan(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float(lane63(r));
 }
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(v, d);
-    if (lane >= d) v += o;
-  }
-  return v;
+  return (int)wave_scan((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ int wave_sum_i(int v) { return (int)lane63((uint32_t)wave_incl_scan(v)); }
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  return lane63(wave_scan(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); }));
+}
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  return lane63(wave_scan(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }));
 }
 
 // Exclusive prefix sum over the T threads of the block; *total gets the sum.
-// tmp: at least T/64 + 1 ints of LDS.  Contains barriers: call uniformly.
+// tmp: at least T/64 ints of LDS.  Contains barriers: call uniformly.
 template <int T>
 __device__ int block_excl_scan(int v, int* tmp, int* total) {
   constexpr int NW = T / 64;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int inc = wave_incl_scan(v);
-  __syncthreads();
+  __syncthreads();  // earlier readers of tmp are done
   if (lane == 63) tmp[w] = inc;
   __syncthreads();
-  if (w == 0) {
-    const int x = lane < NW ? tmp[lane] : 0;
-    const int xi = wave_incl_scan(x);
-    if (lane < NW) tmp[lane] = xi - x;
-    if (lane == NW - 1) tmp[NW] = xi;
-  }
-  __syncthreads();
-  const int r = tmp[w] + inc - v;
-  *total = tmp[NW];
-  return r;
+  const int x = lane < NW ? tmp[lane] : 0;
+  const int xi = wave_incl_scan(x);
+  *total = __builtin_amdgcn_readlane(xi, NW - 1);
+  return __builtin_amdgcn_readlane(xi - x, w) + inc - v;
 }
 
 struct Bin {
@@ -227,13 +253,13 @@ __device__ Bin wave_find_bin(const uint32_t* h, int need) {
   const unsigned long long hit = __ballot(excl < need && incl >= need);
   if (!hit) return Bin{-1, 0, 0};
   const int src = __ffsll((unsigned long long)hit) - 1;
-  const int base = __shfl(excl, src);
+  const int base = __builtin_amdgcn_readlane(excl, src);
   const int src_top = NB - 1 - R * src;
   const int c = lane < R ? (int)h[src_top - lane] : 0;
   const int inc2 = wave_incl_scan(c) + base;
   const unsigned long long hit2 = __ballot(lane < R && inc2 >= need);
   const int k = __ffsll((unsigned long long)hit2) - 1;
-  return Bin{src_top - k, __shfl(inc2 - c, k), __shfl(c, k)};
+  return Bin{src_top - k, __builtin_amdgcn_readlane(inc2 - c, k), __builtin_amdgcn_readlane(c, k)};
 }
 
 // ---------------------------------------------------------------------------
@@ -241,57 +267,74 @@ __device__ Bin wave_find_bin(const uint32_t* h, int need) {
 // ---------------------------------------------------------------------------
 
 // Anchor layer: workgroup w of problem p scores tokens [w * kAnchorEntries, +kAnchorEntries)
-// of the cache; each wave takes 256 consecutive tokens = 4 whole pages.
+// of the cache; each wave takes 256 consecutive tokens = 4 whole pages.  The
+// workgroup also counts its scores by coarse bin (top 12 bits of the order
+// key) in LDS and adds the counts to the problem's histogram in the workspace,
+// which the selection uses to find the bin holding the kappa-th score.
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g, Workspace ws,
                                                                      const uint16_t* __restrict__ q,
                                                                      int wgs) {
+  __shared__ uint32_t lh[kCoarseBins];
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
+  if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
   const int wbase = w * kAnchorEntries + wave * 256;
-  if (wbase >= n) return;
-  u32x4 qf[4];
-  load_q_frag<G>(q, g, b, kvh, lane, qf);
-  float* sc = ws.scores + (size_t)p * g.n_cap;
-  const int last_page = (n - 1) >> 6;
-  const size_t head = (size_t)kvh * kPageSize * kHeadDim;
-  size_t page_off[4];
+  for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
+  __syncthreads();
+  if (wbase < n) {
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    float* sc = ws.scores + (size_t)p * g.n_cap;
+    const int last_page = (n - 1) >> 6;
+    const size_t head = (size_t)kvh * kPageSize * kHeadDim;
+    size_t page_off[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-    page_off[r] = (size_t)phys_page(g, b, min((wbase >> 6) + r, last_page)) * g.page_stride + head;
-  // One page (4 tiles of 16 tokens) per step, double-buffered: the next page's
-  // 16 loads are issued before the current page's MFMAs (the scheduling
-  // barriers keep the compiler from interleaving them back into a few loads
-  // in flight).  Addresses stay offsets from the kernel-argument base so the
-  // loads remain global loads.
-  u32x4 kb[2][4][4];
+    for (int r = 0; r < 4; ++r)
+      page_off[r] = (size_t)phys_page(g, b, min((wbase >> 6) + r, last_page)) * g.page_stride + head;
+    // One page (4 tiles of 16 tokens) per step, double-buffered: the next page's
+    // 16 loads are issued before the current page's MFMAs (the scheduling
+    // barriers keep the compiler from interleaving them back into a few loads
+    // in flight).  Addresses stay offsets from the kernel-argument base so the
+    // loads remain global loads.
+    u32x4 kb[2][4][4];
 #pragma unroll
-  for (int r = 0; r < 5; ++r) {
-    if (r < 4) {
+    for (int r = 0; r < 5; ++r) {
+      if (r < 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x4* row = reinterpret_cast<const u32x4*>(
-            g.k_pages + page_off[r] + (size_t)((u * 16 + j) * kHeadDim));
+        for (int u = 0; u < 4; ++u) {
+          const u32x4* row = reinterpret_cast<const u32x4*>(
+              g.k_pages + page_off[r] + (size_t)((u * 16 + j) * kHeadDim));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
-          kb[r & 1][u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+          for (int s4 = 0; s4 < 4; ++s4)
+            kb[r & 1][u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+        }
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (r > 0) {
-      const int rp = r - 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (r > 0) {
+        const int rp = r - 1;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float m = group_max<G>(qk_tile(qf, kb[rp & 1][u]), g4);
-        const int e = wbase + rp * 64 + u * 16 + j;
-        if (g4 == 0 && e < n) sc[e] = m;
+        for (int u = 0; u < 4; ++u) {
+          const float m = group_max<G>(qk_tile(qf, kb[rp & 1][u]), g4);
+          const int e = wbase + rp * 64 + u * 16 + j;
+          if (g4 == 0 && e < n) {
+            sc[e] = m;
+            atomicAdd(&lh[order_key(m) >> 20], 1u);
+          }
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();
+  uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
+  for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) {
+    const uint32_t c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
   }
 }
 
@@ -340,12 +383,16 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
 // ---------------------------------------------------------------------------
 constexpr int kMaxPages = kMaxSeqLen / kPageSize;
 
+constexpr int kPairMax = 256;  // bucket entries ranked against each other directly
+
 struct SelectSmem {
   int32_t bt[kMaxPages];              // the sequence's block table row (physical pages)
   uint32_t bitmap[kMaxSeqLen / 32];   // selection marks in list order
-  uint32_t hist[4096 + 1024 + 1024];  // three histogram levels
+  uint32_t hist[4096 + 1024 + 1024];  // bucket histogram / three radix levels
   uint32_t cbuf[2 * kCand];           // list keys / sample keys / candidate keys and indices
   int32_t apos[kMaxKappa];            // the emitted set, for the pool build
+  uint32_t pair[kPairMax];            // keys of the threshold bucket
+  uint32_t ured[32];                  // per-wave minima and maxima
   int tmp[NT / 64 + 1];
   int res[9];
   int cnt[2];
@@ -361,14 +408,19 @@ struct SelList {
   uint32_t* srow;
 };
 
-__device__ __forceinline__ void emit_entry(const Geometry& g, const SelList& c, int e, int o,
-                                           SelectSmem& sm) {
-  const int pos = c.plist ? c.plist[e] : e;
-  const uint32_t row = c.prow ? c.prow[e] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
+__device__ __forceinline__ void emit_at(const Geometry& g, const SelList& c, int pos, uint32_t row,
+                                        int o, SelectSmem& sm) {
   c.o1[o] = pos;
   if (c.o2) c.o2[o] = pos;
   c.srow[o] = row;
   sm.apos[o] = pos;
+}
+
+__device__ __forceinline__ void emit_entry(const Geometry& g, const SelList& c, int e, int o,
+                                           SelectSmem& sm) {
+  const int pos = c.plist ? c.plist[e] : e;
+  const uint32_t row = c.prow ? c.prow[e] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
+  emit_at(g, c, pos, row, o, sm);
 }
 
 __device__ __forceinline__ void emit_empty(const SelList& c, int o, SelectSmem& sm) {
@@ -394,66 +446,227 @@ __device__ Bin find_publish(const uint32_t* h, int need, SelectSmem& sm, int slo
   return Bin{sm.res[slot], sm.res[slot + 1], sm.res[slot + 2]};
 }
 
-// Lists of at most kSmall entries: all keys in registers / LDS histograms.
-// Thread t holds entries 8t .. 8t+7, so per-thread counts scanned in thread
-// order give ascending output positions directly.
-__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
+// The bin of a 4096-bin histogram holding the need-th largest entry (counted
+// down from the top bin), with the count of higher bins and its own count;
+// bin = -1 if the histogram holds fewer than need.  Thread t owns bins
+// 4092 - 4t .. 4095 - 4t, so an exclusive scan in thread order counts from the
+// top.  Uniform over the block; contains barriers.
+__device__ Bin block_find_top(const uint32_t* h, int need, SelectSmem& sm) {
+  static_assert(NT * 4 == 4096, "four bins per thread");
   const int t = threadIdx.x;
+  const u32x4 c4 = *reinterpret_cast<const u32x4*>(h + 4092 - 4 * t);
+  const int sum = (int)(c4[0] + c4[1] + c4[2] + c4[3]);
+  if (t == 0) {
+    sm.res[3] = -1;
+    sm.res[4] = 0;
+    sm.res[5] = 0;
+  }
+  int tot;
+  const int above = block_excl_scan<NT>(sum, sm.tmp, &tot);
+  if (above < need && need <= above + sum) {
+    int a = above, k = 3, cnt = (int)c4[3];
+    if (need > a + (int)c4[3]) {
+      a += (int)c4[3];
+      k = 2;
+      cnt = (int)c4[2];
+      if (need > a + (int)c4[2]) {
+        a += (int)c4[2];
+        k = 1;
+        cnt = (int)c4[1];
+        if (need > a + (int)c4[1]) {
+          a += (int)c4[1];
+          k = 0;
+          cnt = (int)c4[0];
+        }
+      }
+    }
+    sm.res[3] = 4092 - 4 * t + k;
+    sm.res[4] = a;
+    sm.res[5] = cnt;
+  }
+  __syncthreads();
+  return Bin{sm.res[3], sm.res[4], sm.res[5]};
+}
+
+// The float whose order_key is k (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Threshold of a selection: T is the need-th largest key; need_eq entries
+// equal to T are taken (lowest list index first) out of eq_total equal to T.
+struct Thresh {
+  uint32_t T;
+  int need_eq, eq_total;
+};
+
+// The need-th largest of the keys the block holds in registers: thread t
+// holds key[0 .. nv) (nv <= R); 1 <= need <= total count.
+//
+// Scores are binned into 4096 equal-width buckets between the smallest and
+// the largest score.  The map score -> bucket is monotone (each rounding step
+// of (s - lo) * (4096 / range) is), so a higher bucket holds only higher
+// scores.  The bucket holding the need-th largest is found from the top; if it
+// holds at most kPairMax entries they are ranked against each other (four
+// threads per entry).  A larger bucket (scores concentrated far inside their
+// range), a zero range or a non-finite range falls back to an exact
+// 12/10/10-bit radix over the keys.
+template <int R>
+__device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, SelectSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (i < nv) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+    }
+  }
+  kmin = wave_min_u(kmin);
+  kmax = wave_max_u(kmax);
+  if (lane == 0) {
+    sm.ured[wave] = kmin;
+    sm.ured[16 + wave] = kmax;
+  }
+  for (int i = t; i < 4096; i += NT) sm.hist[i] = 0u;
+  if (t == 0) sm.cnt[0] = 0;
+  __syncthreads();
+  kmin = wave_min_u(lane < NT / 64 ? sm.ured[lane] : 0xFFFFFFFFu);
+  kmax = wave_max_u(lane < NT / 64 ? sm.ured[16 + lane] : 0u);
+  const float lo = key_value(kmin);
+  const float range = key_value(kmax) - lo;
+  const float inv = 4096.f / range;
+  if (range > 0.f && range <= 3.0e38f && inv <= 3.0e38f) {
+    int bk[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      bk[i] = i < nv ? clampi((int)((key_value(key[i]) - lo) * inv), 0, 4095) : -1;
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+      if (bk[i] >= 0) atomicAdd(&sm.hist[bk[i]], 1u);
+    __syncthreads();
+    const Bin B = block_find_top(sm.hist, need, sm);
+    if (B.bin >= 0 && B.count <= kPairMax) {
+      // gather the bucket's keys: one LDS atomic per wave
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < R; ++i) cnt += bk[i] == B.bin ? 1 : 0;
+      const int inc = wave_incl_scan(cnt);
+      const int wtot = (int)lane63((uint32_t)inc);
+      if (wtot) {
+        int off = 0;
+        if (lane == 0) off = atomicAdd(&sm.cnt[0], wtot);
+        int slot = __builtin_amdgcn_readfirstlane(off) + inc - cnt;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          if (bk[i] == B.bin) {
+            if (slot < kPairMax) sm.pair[slot] = key[i];
+            ++slot;
+          }
+        }
+      }
+      __syncthreads();
+      const int pc = min(B.count, kPairMax);
+      const int need_b = need - B.above;
+      const int x = t >> 2, part = t & 3;
+      int gt = 0, ge = 0;
+      uint32_t kx = 0u;
+      if (x < pc) {
+        kx = sm.pair[x];
+        for (int y = part; y < pc; y += 4) {
+          const uint32_t ky = sm.pair[y];
+          gt += ky > kx ? 1 : 0;
+          ge += ky >= kx ? 1 : 0;
+        }
+      }
+      gt += (int)dpp<kQuadXor1, 0xf>(0u, (uint32_t)gt);
+      ge += (int)dpp<kQuadXor1, 0xf>(0u, (uint32_t)ge);
+      gt += (int)dpp<kQuadXor2, 0xf>(0u, (uint32_t)gt);
+      ge += (int)dpp<kQuadXor2, 0xf>(0u, (uint32_t)ge);
+      if (x < pc && part == 0 && gt < need_b && need_b <= ge) {
+        sm.res[0] = (int)kx;  // every thread that writes writes the same values
+        sm.res[1] = need_b - gt;
+        sm.res[2] = ge - gt;
+      }
+      __syncthreads();
+      return Thresh{(uint32_t)sm.res[0], sm.res[1], sm.res[2]};
+    }
+  }
+  // exact radix over the keys
   uint32_t* h1 = sm.hist;
   uint32_t* h2 = sm.hist + 4096;
   uint32_t* h3 = sm.hist + 5120;
+  __syncthreads();
   for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nv) atomicAdd(&h1[key[i] >> 20], 1u);
+  __syncthreads();
+  const Bin a = find_publish<4096>(h1, need, sm, 0);
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nv && (int)(key[i] >> 20) == a.bin) atomicAdd(&h2[(key[i] >> 10) & 1023u], 1u);
+  __syncthreads();
+  const Bin bb = find_publish<1024>(h2, need - a.above, sm, 3);
+  const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+    if (i < nv && (key[i] >> 10) == pre) atomicAdd(&h3[key[i] & 1023u], 1u);
+  __syncthreads();
+  const Bin cc = find_publish<1024>(h3, need - a.above - bb.above, sm, 6);
+  return Thresh{(pre << 10) | (uint32_t)cc.bin, need - a.above - bb.above - cc.above, cc.count};
+}
+
+// Lists of at most kSmall entries.  Thread t holds entries 8t .. 8t+7 (keys,
+// and for a pool their positions and row ids, all loaded up front), so counts
+// scanned in thread order give ascending output positions directly.
+__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  const int t = threadIdx.x;
   const int e0 = 8 * t;
+  const int nv = clampi(c.n - e0, 0, 8);  // valid entries of this thread
+  const int ea = e0 < c.n ? e0 : 0;       // entries past n are loaded but not used
   uint32_t key[8];
+  int32_t pl[8];
+  uint32_t pr[8];
   {
-    const int ea = e0 < c.n ? e0 : 0;  // entries past n are loaded but not used
     const u32x4 r0 = *reinterpret_cast<const u32x4*>(c.sc + ea);
     const u32x4 r1 = *reinterpret_cast<const u32x4*>(c.sc + ea + 4);
+    u32x4 p0 = {0u, 0u, 0u, 0u}, p1 = p0, w0 = p0, w1 = p0;
+    if (c.plist) {
+      p0 = *reinterpret_cast<const u32x4*>(c.plist + ea);
+      p1 = *reinterpret_cast<const u32x4*>(c.plist + ea + 4);
+      w0 = *reinterpret_cast<const u32x4*>(c.prow + ea);
+      w1 = *reinterpret_cast<const u32x4*>(c.prow + ea + 4);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       key[i] = order_key(__uint_as_float(r0[i]));
       key[i + 4] = order_key(__uint_as_float(r1[i]));
+      pl[i] = (int32_t)p0[i];
+      pl[i + 4] = (int32_t)p1[i];
+      pr[i] = w0[i];
+      pr[i + 4] = w1[i];
     }
   }
-  const int nv = clampi(c.n - e0, 0, 8);  // valid entries of this thread
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i < nv) atomicAdd(&h1[key[i] >> 20], 1u);
-  __syncthreads();
-  const Bin a = find_publish<4096>(h1, c.K, sm, 0);
-  const int need2 = c.K - a.above;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i < nv && (int)(key[i] >> 20) == a.bin) atomicAdd(&h2[(key[i] >> 10) & 1023u], 1u);
-  __syncthreads();
-  const Bin bb = find_publish<1024>(h2, need2, sm, 3);
-  const int need3 = need2 - bb.above;
-  const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    if (i < nv && (key[i] >> 10) == pre) atomicAdd(&h3[key[i] & 1023u], 1u);
-  __syncthreads();
-  const Bin cc = find_publish<1024>(h3, need3, sm, 6);
-  const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
-  const int need_eq = need3 - cc.above;
+  const Thresh th = find_threshold<8>(key, nv, c.K, sm);
   uint32_t take = 0u;
-  if (cc.count == need_eq) {
+  if (th.eq_total == th.need_eq) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i < nv && key[i] >= T) take |= 1u << i;
+      if (i < nv && key[i] >= th.T) take |= 1u << i;
   } else {  // more entries equal T than needed: the lowest list indices win
     int my_eq = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (i < nv && key[i] == T) ++my_eq;
+      if (i < nv && key[i] == th.T) ++my_eq;
     int tot;
     int r = block_excl_scan<NT>(my_eq, sm.tmp, &tot);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < nv && key[i] > T) take |= 1u << i;
-      if (i < nv && key[i] == T) {
-        if (r < need_eq) take |= 1u << i;
+      if (i < nv && key[i] > th.T) take |= 1u << i;
+      if (i < nv && key[i] == th.T) {
+        if (r < th.need_eq) take |= 1u << i;
         ++r;
       }
     }
@@ -463,7 +676,34 @@ __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     if (take & (1u << i)) {
-      if (o < c.K) emit_entry(g, c, e0 + i, o, sm);
+      if (o < c.K) {
+        const int pos = c.plist ? pl[i] : e0 + i;
+        const uint32_t row = c.prow ? pr[i] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
+        emit_at(g, c, pos, row, o, sm);
+      }
+      ++o;
+    }
+  }
+  for (int o2 = total + t; o2 < c.K; o2 += NT) emit_empty(c, o2, sm);
+}
+
+// Emission of the entries marked in the LDS bitmap, in list order (ascending
+// positions): per-thread runs of words, counts scanned in thread order.
+__device__ void emit_bitmap(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  const int t = threadIdx.x;
+  const int words = (c.n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
+  int total;
+  int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  for (int i = w0; i < w1; ++i) {
+    uint32_t m = sm.bitmap[i];
+    while (m) {
+      const int e = i * 32 + (__ffs(m) - 1);
+      m &= m - 1u;
+      if (o < c.K) emit_entry(g, c, e, o, sm);
       ++o;
     }
   }
@@ -471,12 +711,12 @@ __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm
 }
 
 // Longer lists.  A strided sample of at most kSample keys brackets the K-th
-// largest key by 22-bit prefixes [lo22, hi22] (+-4 sigma of the sample count
-// plus slack).  One pass over the list marks entries above the bracket in the
-// bitmap and gathers the bracket into LDS, where three radix levels find the
-// exact K-th key T.  If the bracket misses or overflows, the exact radix runs
-// over the whole list instead.  The bitmap, read in order, gives ascending
-// positions; entries equal to T are taken lowest list index first.
+// largest key between two sample order statistics [klo, khi] (+-4 sigma of the
+// sample count plus slack).  One pass over the list marks entries above khi
+// in the bitmap and gathers the entries inside the bracket into LDS, where
+// the exact K-th key T is found.  If the bracket misses or overflows, an exact
+// radix runs over the whole list instead.  The bitmap, read in order, gives
+// ascending positions; entries equal to T are taken lowest list index first.
 __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
   const int t = threadIdx.x, lane = t & 63;
   const int n = c.n, K = c.K;
@@ -492,62 +732,30 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
   const int d = (int)ceilf(4.f * sqrtf(ks * (1.f - ks / (float)ns))) + 16;
   const int r_hi = (int)floorf(ks) - d, r_lo = (int)ceilf(ks) + d;
 
-  for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+  uint32_t khi = 0xFFFFFFFFu, klo = 0u;
   {
-    uint32_t key[kSample / NT];
+    constexpr int RS = kSample / NT;
+    uint32_t key[RS];
 #pragma unroll
-    for (int u = 0; u < kSample / NT; ++u) {
+    for (int u = 0; u < RS; ++u) {
       const int i = u * NT + t;
       key[u] = order_key(c.sc[(size_t)(i < ns ? i : 0) * S]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < kSample / NT; ++u) {
-      const int i = u * NT + t;
-      if (i < ns) {
-        sm.cbuf[i] = key[u];
-        atomicAdd(&h1[key[u] >> 20], 1u);
-      }
-    }
+    const int nvs = clampi((ns - t + NT - 1) / NT, 0, RS);  // sample u*NT + t exists iff u < nvs
+    if (r_hi >= 1) khi = find_threshold<RS>(key, nvs, r_hi, sm).T;
+    if (r_lo <= ns) klo = find_threshold<RS>(key, nvs, r_lo, sm).T;
+  }
+  if (t == 0) {
+    sm.cnt[0] = 0;
+    sm.cnt[1] = 0;
   }
   __syncthreads();
-  if (t < 64) {
-    const Bin bh = r_hi >= 1 ? wave_find_bin<4096>(h1, r_hi) : Bin{-1, 0, 0};
-    const Bin bl = r_lo <= ns ? wave_find_bin<4096>(h1, r_lo) : Bin{-1, 0, 0};
-    if (t == 0) {
-      sm.res[0] = bh.bin;
-      sm.res[1] = bh.above;
-      sm.res[3] = bl.bin;
-      sm.res[4] = bl.above;
-    }
-  }
-  __syncthreads();
-  const int bh = sm.res[0], bh_above = sm.res[1], bl = sm.res[3], bl_above = sm.res[4];
-  for (int i = t; i < ns; i += NT) {
-    const uint32_t key = sm.cbuf[i];
-    const int top = (int)(key >> 20);
-    if (top == bh) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
-    if (top == bl) atomicAdd(&h3[(key >> 10) & 1023u], 1u);
-  }
-  __syncthreads();
-  if (t < 64) {
-    uint32_t hi22 = 0x3FFFFFu, lo22 = 0u;
-    if (bh >= 0) hi22 = ((uint32_t)bh << 10) | (uint32_t)max(wave_find_bin<1024>(h2, r_hi - bh_above).bin, 0);
-    if (bl >= 0) lo22 = ((uint32_t)bl << 10) | (uint32_t)max(wave_find_bin<1024>(h3, r_lo - bl_above).bin, 0);
-    if (t == 0) {
-      sm.res[6] = (int)hi22;
-      sm.res[7] = (int)lo22;
-      sm.cnt[0] = 0;
-      sm.cnt[1] = 0;
-    }
-  }
-  __syncthreads();
-  const uint32_t hi22 = (uint32_t)sm.res[6], lo22 = (uint32_t)sm.res[7];
-  for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;  // for the candidate radix
 
-  // --- one pass over the list: lanes hold 4 consecutive entries, 8 lanes one
-  //     32-bit bitmap word -------------------------------------------------------
-  int above = 0;
+  // --- one pass over the list: lanes hold 4 consecutive entries; the bitmap
+  //     words of a wave's 256 entries are built from ballots, and bracket
+  //     entries are appended with one LDS atomic per wave and round ----------------
+  int above = 0;  // uniform over the wave
+  const int wave = t >> 6;
   for (int base = 0; base < n; base += 4 * NT * kPassUnroll) {
     u32x4 raw[kPassUnroll];
 #pragma unroll
@@ -555,73 +763,90 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
       const int e0 = base + u * 4 * NT + 4 * t;
       raw[u] = *reinterpret_cast<const u32x4*>(c.sc + (e0 < n ? e0 : 0));
     }
+    uint32_t cand = 0u;  // bit 4u + q4: entry inside the bracket
 #pragma unroll
     for (int u = 0; u < kPassUnroll; ++u) {
       const int e0 = base + u * 4 * NT + 4 * t;
-      uint32_t nib = 0u;
+      unsigned long long mh[4];
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int e = e0 + q4;
-        if (e < n) {
-          const uint32_t key = order_key(__uint_as_float(raw[u][q4]));
-          const uint32_t k22 = key >> 10;
-          if (k22 > hi22) {
-            nib |= 1u << q4;
-            ++above;
-          } else if (k22 >= lo22) {
-            const int slot = atomicAdd(&sm.cnt[0], 1);
+        const uint32_t key = order_key(__uint_as_float(raw[u][q4]));
+        const bool ok = e0 + q4 < n;
+        const bool hi = ok && key > khi;
+        cand |= (ok && !hi && key >= klo) ? 1u << (4 * u + q4) : 0u;
+        mh[q4] = __ballot(hi);
+        above += __popcll(mh[q4]);
+      }
+      // word k of the wave's 256 entries holds lanes 8k .. 8k+7: bit 4i + q4 is
+      // bit 8k + i of mask q4
+      const int first = base + u * 4 * NT + 256 * wave + 32 * lane;
+      if (lane < 8 && first < n) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint32_t x = (uint32_t)(mh[q4] >> (8 * lane)) & 0xFFu;
+          x = (x | (x << 12)) & 0x000F000Fu;
+          x = (x | (x << 6)) & 0x03030303u;
+          x = (x | (x << 3)) & 0x11111111u;
+          word |= x << q4;
+        }
+        sm.bitmap[first >> 5] = word;
+      }
+    }
+    const int cnt = __popc(cand);
+    const int inc = wave_incl_scan(cnt);
+    const int wtot = (int)lane63((uint32_t)inc);
+    if (wtot) {
+      int off = 0;
+      if (lane == 0) off = atomicAdd(&sm.cnt[0], wtot);
+      int slot = __builtin_amdgcn_readfirstlane(off) + inc - cnt;
+#pragma unroll
+      for (int u = 0; u < kPassUnroll; ++u) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          if (cand & (1u << (4 * u + q4))) {
             if (slot < kCand) {
-              ckey[slot] = key;
-              cidx[slot] = e;
+              ckey[slot] = order_key(__uint_as_float(raw[u][q4]));
+              cidx[slot] = base + u * 4 * NT + 4 * t + q4;
             }
+            ++slot;
           }
         }
       }
-      uint32_t word = nib << (4 * (t & 7));
-      word |= __shfl_xor(word, 1);
-      word |= __shfl_xor(word, 2);
-      word |= __shfl_xor(word, 4);
-      if ((t & 7) == 0 && e0 < n) sm.bitmap[e0 >> 5] = word;
     }
   }
-  above = wave_sum_i(above);
   if (lane == 0) atomicAdd(&sm.cnt[1], above);
   __syncthreads();
   const int ncand = sm.cnt[0];
   const int need = K - sm.cnt[1];
+  __syncthreads();  // every thread has read the counters before they are reused
 
   if (need >= 1 && need <= ncand && ncand <= kCand) {
-    for (int i = t; i < ncand; i += NT) atomicAdd(&h1[ckey[i] >> 20], 1u);
-    __syncthreads();
-    const Bin a = find_publish<4096>(h1, need, sm, 0);
-    for (int i = t; i < ncand; i += NT)
-      if ((int)(ckey[i] >> 20) == a.bin) atomicAdd(&h2[(ckey[i] >> 10) & 1023u], 1u);
-    __syncthreads();
-    const Bin bb = find_publish<1024>(h2, need - a.above, sm, 3);
-    const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
-    for (int i = t; i < ncand; i += NT)
-      if ((ckey[i] >> 10) == pre) atomicAdd(&h3[ckey[i] & 1023u], 1u);
-    __syncthreads();
-    const Bin cc = find_publish<1024>(h3, need - a.above - bb.above, sm, 6);
-    const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
-    const int need_eq = need - a.above - bb.above - cc.above;
+    constexpr int RC = kCand / NT;
+    uint32_t ck[RC];
+#pragma unroll
+    for (int u = 0; u < RC; ++u) ck[u] = ckey[min(u * NT + t, kCand - 1)];
+    const int nvc = clampi((ncand - t + NT - 1) / NT, 0, RC);
+    const Thresh th = find_threshold<RC>(ck, nvc, need, sm);
     for (int i = t; i < ncand; i += NT) {
       const uint32_t key = ckey[i];
       const int e = cidx[i];
-      bool take = key > T;
-      if (key == T) {
-        if (cc.count == need_eq) {
+      bool take = key > th.T;
+      if (key == th.T) {
+        if (th.eq_total == th.need_eq) {
           take = true;
         } else {  // rank among equal keys by list index
           int rank = 0;
-          for (int i2 = 0; i2 < ncand; ++i2) rank += (ckey[i2] == T && cidx[i2] < e) ? 1 : 0;
-          take = rank < need_eq;
+          for (int i2 = 0; i2 < ncand; ++i2) rank += (ckey[i2] == th.T && cidx[i2] < e) ? 1 : 0;
+          take = rank < th.need_eq;
         }
       }
       if (take) atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
     }
   } else {
     // exact radix over the whole list
+    for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+    __syncthreads();
     for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
     __syncthreads();
     const Bin a = find_publish<4096>(h1, K, sm, 0);
@@ -656,82 +881,175 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
     }
   }
   __syncthreads();
+  emit_bitmap(g, c, sm);
+}
 
-  // --- emission in bitmap order = ascending position ---------------------------
+// Anchor lists longer than kSmall, after the classify kernel: the entries
+// above the threshold bin are marked in the workspace bitmap, and the bin's own
+// entries (the candidates) are listed with their keys.  The candidates are
+// ranked here; if the bin held more than kMaxCand of them, an exact radix over
+// the whole list runs instead.
+__device__ void select_classified(const Geometry& g, const Workspace& ws, int p, const SelList& c,
+                                  SelectSmem& sm) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int n = c.n, K = c.K;
   const int words = (n + 31) >> 5;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
-  int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
-  int total;
-  int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t m = sm.bitmap[i];
-    while (m) {
-      const int e = i * 32 + (__ffs(m) - 1);
-      m &= m - 1u;
-      if (o < K) emit_entry(g, c, e, o, sm);
-      ++o;
+  const uint32_t* gb = ws.gbits + (size_t)p * (g.n_cap >> 5);
+  for (int i = t; i < words; i += NT) sm.bitmap[i] = gb[i];
+  const int above = ws.sel_meta[4 * p + 1];
+  const int ncand = (int)ws.cand_cnt[p];
+  const int need = K - above;
+  uint32_t* const ckey = sm.cbuf;
+  int32_t* const cidx = reinterpret_cast<int32_t*>(sm.cbuf + kCand);
+  if (need >= 1 && need <= ncand && ncand <= kMaxCand) {
+    constexpr int RC = kMaxCand / NT;
+    uint32_t ck[RC];
+    int32_t ci[RC];
+    const uint32_t* gk = ws.cand_key + (size_t)p * kMaxCand;
+    const int32_t* gi = ws.cand_idx + (size_t)p * kMaxCand;
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      const int i = u * NT + t;
+      ck[u] = gk[i];
+      ci[u] = gi[i];
+      ckey[i] = ck[u];
+      cidx[i] = ci[u];
+    }
+    const int nvc = clampi((ncand - t + NT - 1) / NT, 0, RC);
+    const Thresh th = find_threshold<RC>(ck, nvc, need, sm);  // its barriers order the LDS writes
+#pragma unroll
+    for (int u = 0; u < RC; ++u) {
+      if (u < nvc) {
+        const int e = clampi(ci[u], 0, n - 1);
+        bool take = ck[u] > th.T;
+        if (ck[u] == th.T) {
+          if (th.eq_total == th.need_eq) {
+            take = true;
+          } else {  // rank among equal keys by list index
+            int rank = 0;
+            for (int i2 = 0; i2 < ncand; ++i2) rank += (ckey[i2] == th.T && cidx[i2] < ci[u]) ? 1 : 0;
+            take = rank < th.need_eq;
+          }
+        }
+        if (take) atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
+      }
+    }
+  } else {
+    // exact radix over the whole list
+    uint32_t* h1 = sm.hist;
+    uint32_t* h2 = sm.hist + 4096;
+    uint32_t* h3 = sm.hist + 5120;
+    for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+    __syncthreads();
+    for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
+    __syncthreads();
+    const Bin a = find_publish<4096>(h1, K, sm, 0);
+    for (int e = t; e < n; e += NT) {
+      const uint32_t key = order_key(c.sc[e]);
+      if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
+    }
+    __syncthreads();
+    const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
+    const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+    for (int e = t; e < n; e += NT) {
+      const uint32_t key = order_key(c.sc[e]);
+      if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
+    }
+    __syncthreads();
+    const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
+    const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
+    const int need_eq = K - a.above - bb.above - cc.above;
+    int run = 0;  // equal keys in earlier chunks
+    for (int base = 0; base < n; base += NT) {
+      const int e = base + t;
+      const bool valid = e < n;
+      const uint32_t key = valid ? order_key(c.sc[e]) : 0u;
+      const bool eq = valid && key == T;
+      int tot;
+      const int r = block_excl_scan<NT>(eq ? 1 : 0, sm.tmp, &tot);
+      const bool take = valid && (key > T || (eq && run + r < need_eq));
+      const unsigned long long m = __ballot(take);
+      if (lane == 0 && e < n) sm.bitmap[e >> 5] = (uint32_t)m;
+      if (lane == 32 && e < n) sm.bitmap[e >> 5] = (uint32_t)(m >> 32);
+      run += tot;
     }
   }
-  for (int o2 = total + t; o2 < K; o2 += NT) emit_empty(c, o2, sm);
+  __syncthreads();
+  emit_bitmap(g, c, sm);
 }
 
 // Refinement pool of one (sequence, KV head) from its ascending anchor set:
 // the union of [a_k - w, a_k + w] clipped to [0, L) is the disjoint union over
-// k of [max(lo_k, hi_{k-1} + 1), hi_k] (all windows have one width, so run k
-// adds exactly what run k-1 did not cover).  Run lengths are scanned for their
-// offsets (kept in LDS), then each wave writes whole runs, 64 entries per
-// store.  anchor_at(k) gives entry k; bt is the sequence's block table in LDS.
-template <typename AnchorAt>
+// k of the runs [max(lo_k, hi_{k-1} + 1), hi_k] (all windows have one width, so
+// run k adds exactly what run k-1 did not cover).  Run lengths are scanned
+// into offsets (kept in LDS); then each thread fills 8 consecutive pool
+// entries per round: a binary search over the offsets finds the run of the
+// first one, and positions and row ids leave as 32-byte stores.  sm.apos holds
+// the anchor set, sm.bt the sequence's block table.
 __device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L,
-                           AnchorAt anchor_at, const int32_t* bt, int* tmp) {
+                           SelectSmem& sm) {
   const int K = g.kappa, t = threadIdx.x;
   const int win = min(g.window, L);
+  int32_t* const off = reinterpret_cast<int32_t*>(sm.cbuf);  // [K] run offsets
+  auto run_of = [&](int k, int* start) -> int {                // length and start of run k
+    const int ai = sm.apos[k];
+    *start = 0;
+    if (ai < 0 || ai >= L) return 0;
+    const int prev = k > 0 ? sm.apos[k - 1] : -1;
+    const int lo = max(ai - win, 0), hi = min(ai + win, L - 1);
+    const int prev_hi = (prev >= 0 && prev < L) ? min(prev + win, L - 1) : -1;
+    *start = max(lo, prev_hi + 1);
+    return max(0, hi - *start + 1);
+  };
   const int per = (K + NT - 1) / NT;
   const int j0 = min(K, t * per), j1 = min(K, j0 + per);
-  int starts[kPoolPer], lens[kPoolPer];
+  int lens[kPoolPer];
   int sum = 0;
-  int prev = j0 > 0 ? anchor_at(j0 - 1) : -1;
 #pragma unroll
   for (int i = 0; i < kPoolPer; ++i) {
-    const int k = j0 + i;
-    starts[i] = 0;
-    lens[i] = 0;
-    if (k < j1) {
-      const int ai = anchor_at(k);
-      if (ai >= 0 && ai < L) {
-        const int lo = max(ai - win, 0), hi = min(ai + win, L - 1);
-        const int prev_hi = (prev >= 0 && prev < L) ? min(prev + win, L - 1) : -1;
-        starts[i] = max(lo, prev_hi + 1);
-        lens[i] = max(0, hi - starts[i] + 1);
-      }
-      prev = ai;
-    }
+    int st;
+    lens[i] = j0 + i < j1 ? run_of(j0 + i, &st) : 0;
     sum += lens[i];
   }
   int total;
-  int e = block_excl_scan<NT>(sum, tmp, &total);
-  const int n = min(total, g.n_cap);
-  if (t == 0) ws.pool_len[p] = n;
-  int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
-  uint32_t* pr = ws.pool_row + (size_t)p * g.n_cap;
+  int e = block_excl_scan<NT>(sum, sm.tmp, &total);
 #pragma unroll
   for (int i = 0; i < kPoolPer; ++i) {
-    // a run's rows are consecutive within a page: one block-table read per page
-    int pos = starts[i];
-    const int run_end = e + lens[i];
-    for (int w = e; w < min(n, run_end);) {
-      const int chunk = min(min(n, run_end) - w, kPageSize - (pos & (kPageSize - 1)));
-      const uint32_t r0 = row_id_of_page(g, bt[pos >> 6], kvh, pos);
-      for (int x = 0; x < chunk; ++x) {
-        pp[w + x] = pos + x;
-        pr[w + x] = r0 + (uint32_t)x;
-      }
-      w += chunk;
-      pos += chunk;
+    if (j0 + i < j1) off[j0 + i] = e;
+    e += lens[i];
+  }
+  const int n = min(total, g.n_cap);
+  if (t == 0) ws.pool_len[p] = n;
+  __syncthreads();
+  int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
+  uint32_t* pr = ws.pool_row + (size_t)p * g.n_cap;
+  for (int o0 = 8 * t; o0 < n; o0 += 8 * NT) {
+    int lo = 0, hi = K - 1;  // the last run k with off[k] <= o0 (it is not empty)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= o0) lo = mid;
+      else hi = mid - 1;
     }
-    e = run_end;
+    int k = lo, st;
+    run_of(k, &st);
+    u32x4 pv[2], rv[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int o = o0 + i;
+      uint32_t ps = 0u, rw = 0u;
+      if (o < n) {
+        while (k + 1 < K && off[k + 1] <= o) run_of(++k, &st);
+        ps = (uint32_t)(st + (o - off[k]));
+        rw = row_id_of_page(g, sm.bt[ps >> 6], kvh, (int)ps);
+      }
+      pv[i >> 2][i & 3] = ps;
+      rv[i >> 2][i & 3] = rw;
+    }
+    // n_cap is a multiple of 64, so the 8 entries stay inside the problem's row
+    *reinterpret_cast<u32x4*>(pp + o0) = pv[0];
+    *reinterpret_cast<u32x4*>(pp + o0 + 4) = pv[1];
+    *reinterpret_cast<u32x4*>(pr + o0) = rv[0];
+    *reinterpret_cast<u32x4*>(pr + o0 + 4) = rv[1];
   }
 }
 
@@ -775,26 +1093,154 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
     }
   } else if (c.n <= kSmall) {
     select_small(g, c, sm);
+  } else if (!POOL) {
+    select_classified(g, ws, p, c, sm);
   } else {
     select_large(g, c, sm);
   }
   if (!POOL) {
     __syncthreads();
-    build_pool(g, ws, p, kvh, L, [&](int k) { return sm.apos[k]; }, sm.bt, sm.tmp);
+    build_pool(g, ws, p, kvh, L, sm);
   }
 }
 
 // Pool of an anchor set given in device memory (one workgroup per problem).
 __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws,
                                                         const int32_t* __restrict__ anchor) {
-  __shared__ int32_t bt[kMaxPages];
-  __shared__ int tmp[NT / 64 + 1];
+  __shared__ SelectSmem sm;
   const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
   const int32_t* a = anchor + (size_t)p * g.kappa;
-  load_bt(g, b, L, bt);
+  load_bt(g, b, L, sm.bt);
+  for (int k = threadIdx.x; k < g.kappa; k += NT) sm.apos[k] = a[k];
   __syncthreads();
-  build_pool(g, ws, p, kvh, L, [&](int k) { return a[k]; }, bt, tmp);
+  build_pool(g, ws, p, kvh, L, sm);
+}
+
+// Anchor lists longer than kSmall: workgroup w of problem p takes list entries
+// [w * kClsEntries, +kClsEntries).  From the problem's coarse histogram it
+// finds the bin holding the kappa-th score (every workgroup finds the same
+// bin; workgroup 0 records it with the count of entries above it and in it),
+// marks its entries above that bin in the workspace bitmap and appends the
+// bin's own entries, with their keys, to the problem's candidate list.
+__global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs) {
+  __shared__ int tmp[kClsThreads / 64];
+  __shared__ int res[3];
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int b = p / g.hkv;
+  const int n = seq_len_of(g, b);
+  const int base = w * kClsEntries;
+  if (n <= kSmall || n <= g.kappa || base >= n) return;  // uniform over the workgroup
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float* sc = ws.scores + (size_t)p * g.n_cap;
+  constexpr int U = kClsEntries / (4 * kClsThreads);
+  u32x4 raw[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e0 = base + u * 4 * kClsThreads + 4 * t;
+    raw[u] = *reinterpret_cast<const u32x4*>(sc + (e0 < n ? e0 : 0));
+  }
+  // thread t holds bins 4080 - 16t .. 4095 - 16t; scanned in thread order the
+  // counts run down from the top bin
+  constexpr int BPT = kCoarseBins / kClsThreads;  // 16
+  const uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins + kCoarseBins - BPT * (t + 1);
+  u32x4 h[BPT / 4];
+#pragma unroll
+  for (int k = 0; k < BPT / 4; ++k) h[k] = reinterpret_cast<const u32x4*>(gh)[k];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < BPT / 4; ++k) sum += (int)(h[k][0] + h[k][1] + h[k][2] + h[k][3]);
+  if (t == 0) {
+    res[0] = -1;
+    res[1] = 0;
+    res[2] = 0;
+  }
+  int tot;
+  const int above_t = block_excl_scan<kClsThreads>(sum, tmp, &tot);
+  const int need = g.kappa;
+  if (above_t < need && need <= above_t + sum) {
+    int a = above_t, bin = -1, cnt = 0;
+#pragma unroll
+    for (int k = BPT / 4 - 1; k >= 0; --k) {
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        const int hc = (int)h[k][q];
+        if (bin < 0) {
+          if (need <= a + hc) {
+            bin = kCoarseBins - BPT * (t + 1) + 4 * k + q;
+            cnt = hc;
+          } else {
+            a += hc;
+          }
+        }
+      }
+    }
+    res[0] = bin;
+    res[1] = a;
+    res[2] = cnt;
+  }
+  __syncthreads();
+  const int bstar = res[0];
+  if (w == 0 && t == 0) {
+    ws.sel_meta[4 * p] = bstar;
+    ws.sel_meta[4 * p + 1] = res[1];
+    ws.sel_meta[4 * p + 2] = res[2];
+  }
+  if (bstar < 0) return;  // the histogram disagrees with the list: the selection falls back
+
+  uint32_t* gb = ws.gbits + (size_t)p * (g.n_cap >> 5);
+  uint32_t cand = 0u;  // bit 4u + q4: entry in the threshold bin
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int e0 = base + u * 4 * kClsThreads + 4 * t;
+    unsigned long long mh[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int bin = (int)(order_key(__uint_as_float(raw[u][q4])) >> 20);
+      const bool ok = e0 + q4 < n;
+      cand |= (ok && bin == bstar) ? 1u << (4 * u + q4) : 0u;
+      mh[q4] = __ballot(ok && bin > bstar);
+    }
+    // word k of the wave's 256 entries holds lanes 8k .. 8k+7: bit 4i + q4 is
+    // bit 8k + i of mask q4
+    const int first = base + u * 4 * kClsThreads + 256 * wave + 32 * lane;
+    if (lane < 8 && first < n) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        uint32_t x = (uint32_t)(mh[q4] >> (8 * lane)) & 0xFFu;
+        x = (x | (x << 12)) & 0x000F000Fu;
+        x = (x | (x << 6)) & 0x03030303u;
+        x = (x | (x << 3)) & 0x11111111u;
+        word |= x << q4;
+      }
+      gb[first >> 5] = word;
+    }
+  }
+  const int cnt = __popc(cand);
+  const int inc = wave_incl_scan(cnt);
+  const int wtot = (int)lane63((uint32_t)inc);
+  if (wtot) {
+    int off = 0;
+    if (lane == 0) off = (int)atomicAdd(&ws.cand_cnt[p], (uint32_t)wtot);
+    int slot = __builtin_amdgcn_readfirstlane(off) + inc - cnt;
+    uint32_t* ck = ws.cand_key + (size_t)p * kMaxCand;
+    int32_t* ci = ws.cand_idx + (size_t)p * kMaxCand;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        if (cand & (1u << (4 * u + q4))) {
+          if (slot < kMaxCand) {
+            ck[slot] = order_key(__uint_as_float(raw[u][q4]));
+            ci[slot] = base + u * 4 * kClsThreads + 4 * t + q4;
+          }
+          ++slot;
+        }
+      }
+    }
+  }
 }
 
 __global__ void zero_counters_kernel(uint32_t* c, int n) {
@@ -847,7 +1293,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
   uint32_t vv[16];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    const uint32_t rj = (uint32_t)__shfl((int)row, jj);
+    const uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)row, jj);
     vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
   }
   u32x4 qf[4];
@@ -1011,9 +1457,15 @@ int64_t profile_launches(int kind) {
   return g_profile[kind].launches;
 }
 
+// Workspace regions in carve order: {bytes, alignment padding applied}.
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
+  o += align256(P * (kCoarseBins + 1) * 4);                      // ghist, cand_cnt
+  o += align256(P * 4 * 4);                                      // sel_meta
+  o += align256(P * (size_t)kMaxCand * 4);                       // cand_key
+  o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx
+  o += align256(P * (size_t)(g.n_cap / 32) * 4);                 // gbits
   o += align256(P * 4);                                          // ticket_attn
   o += align256(P * (size_t)g.n_cap * 4);                        // scores
   o += align256(P * (size_t)g.n_cap * 4);                        // pool_pos
@@ -1030,6 +1482,17 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   const size_t P = (size_t)g.problems();
   char* c = static_cast<char*>(base);
   Workspace w;
+  w.ghist = reinterpret_cast<uint32_t*>(c);
+  w.cand_cnt = w.ghist + P * kCoarseBins;
+  c += align256(P * (kCoarseBins + 1) * 4);
+  w.sel_meta = reinterpret_cast<int32_t*>(c);
+  c += align256(P * 4 * 4);
+  w.cand_key = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * (size_t)kMaxCand * 4);
+  w.cand_idx = reinterpret_cast<int32_t*>(c);
+  c += align256(P * (size_t)kMaxCand * 4);
+  w.gbits = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * (size_t)(g.n_cap / 32) * 4);
   w.ticket_attn = reinterpret_cast<uint32_t*>(c);
   c += align256(P * 4);
   w.scores = reinterpret_cast<float*>(c);
@@ -1050,11 +1513,25 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   return w;
 }
 
+// Anchor layer: zero the coarse histogram and candidate counters, score every
+// cached token (filling the histogram), classify lists longer than kSmall
+// over many workgroups, then select per problem (and build the pool).
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  const int nz = g.problems() * (kCoarseBins + 1);
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
+                     w.ghist, nz);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
+    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
   return hipGetLastError();
 }
