@@ -8,9 +8,13 @@ cache, exact top-kappa, SparseAttn; refined layers: window pool, re-score,
 top-kappa, SparseAttn).  Inputs are seeded synthetic tensors of the workload's
 shapes, resident in HBM before timing starts.
 
-Prints ONE JSON line (rank 0).  Per-kernel durations come from HIP events the
-kernel dispatches record themselves (prism_profile_events), over the same
-timed steps.
+Two timed regions of K steps each, after W warm-up steps:
+  1. the step captured once as a HIP graph and replayed K times: `value` and
+     `ms_per_step` (with --eager, or if capture fails, region 2 is reported);
+  2. the same steps launched eagerly from the host, each kernel's start and end
+     recorded by its own dispatch (prism_profile_events): the per-kernel
+     durations, the roofline of the dominant kernel and `eager_ms_per_step`.
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -154,8 +158,9 @@ def main():
     ap.add_argument("--workload", default="llama3-8b-128k-planted")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample (0 skips it)")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the step captured as one HIP graph")
+    ap.add_argument("--eager", action="store_true",
+                    help="report eager launches only (no HIP graph capture of the step)")
+    ap.add_argument("--graph", action="store_true", help=argparse.SUPPRESS)  # the default
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and "
                          "exit: the known-size reference for hardware byte counters")
@@ -221,27 +226,61 @@ def main():
                        device=dev)
     stream = torch.cuda.current_stream()
 
+    # raw addresses, resolved once: the per-layer call is then one C call
+    ws_arg = (ws.data_ptr(), ws.numel())
+    layer_args = [(kv_dev[l], q_dev[l].data_ptr(), outs[l].data_ptr())
+                  for l in range(wl.num_layers)]
+    anchor_ptr = anchor.data_ptr()
+
     def step():
-        s = torch.cuda.current_stream()   # the capture stream while a graph is recorded
-        for l in range(wl.num_layers):
-            tsa.prism_decode_layer(l, kv_dev[l], q_dev[l], p, anchor, None, outs[l], ws, s)
+        s = torch.cuda.current_stream().cuda_stream  # the capture stream while recording
+        for l, (kv, qp, op) in enumerate(layer_args):
+            tsa.prism_decode_layer(l, kv, qp, p, anchor_ptr, None, op, ws_arg, s)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
+    rt = hip.rt
+    rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    e_start, e_stop = hip.events(1)[0], hip.events(1)[0]
 
-    # ---- timed region: per-kernel events recorded by the dispatches --------------
+    # ---- timed region 1 (the reported value): the step captured once as a HIP
+    #      graph, replayed K times ----------------------------------------------------
+    graph_ms, graph_err = None, None
+    if not args.eager:
+        try:
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step()
+            for _ in range(max(1, args.warmup)):
+                gr.replay()
+            torch.cuda.synchronize()
+            gs = torch.cuda.current_stream()
+            wall0 = time.perf_counter()
+            rt.hipEventRecord(e_start, ctypes.c_void_p(gs.cuda_stream))
+            for _ in range(args.steps):
+                gr.replay()
+            rt.hipEventRecord(e_stop, ctypes.c_void_p(gs.cuda_stream))
+            torch.cuda.synchronize()
+            wall1 = time.perf_counter()
+            graph_ms = hip.elapsed_ms(e_start, e_stop) / args.steps
+            log(f"[bench] graph replay, {args.steps} steps: {graph_ms:.4f} ms/step "
+                f"(wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
+            del gr
+        except Exception as exc:  # report it and fall back to eager launches
+            graph_err = str(exc)[:200]
+            log(f"[bench] graph capture failed ({graph_err}); reporting eager launches")
+            torch.cuda.synchronize()
+
+    # ---- timed region 2: eager launches, every kernel's start and end recorded
+    #      by its dispatch (per-kernel durations and the roofline) -------------------
     per_step = launches_per_step(wl)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
         rings[kind] = (hip.events(cnt), hip.events(cnt))
         tsa.prism_profile_events(kind, rings[kind][0], rings[kind][1])
-    e_start, e_stop = hip.events(1)[0], hip.events(1)[0]
-    rt = hip.rt
-    rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     rt.hipEventRecord(e_start, ctypes.c_void_p(stream.cuda_stream))
@@ -250,10 +289,10 @@ def main():
     rt.hipEventRecord(e_stop, ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     wall1 = time.perf_counter()
-    ms_total = hip.elapsed_ms(e_start, e_stop)
-    ms_per_step = ms_total / args.steps
-    log(f"[bench] timed {args.steps} steps: {ms_per_step:.4f} ms/step "
-        f"(wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
+    eager_ms = hip.elapsed_ms(e_start, e_stop) / args.steps
+    log(f"[bench] eager launches with per-kernel events, {args.steps} steps: {eager_ms:.4f} "
+        f"ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
 
     kernels = {}
     for kind, (starts, stops) in rings.items():
@@ -325,26 +364,10 @@ def main():
                         for kk, vv in v.items()} for k, v in kernels.items()},
     }
 
-    if args.graph:
-        try:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step()
-            for _ in range(3):
-                g.replay()
-            torch.cuda.synchronize()
-            s = torch.cuda.current_stream()
-            rt.hipEventRecord(e_start, ctypes.c_void_p(s.cuda_stream))
-            for _ in range(args.steps):
-                g.replay()
-            rt.hipEventRecord(e_stop, ctypes.c_void_p(s.cuda_stream))
-            torch.cuda.synchronize()
-            gms = hip.elapsed_ms(e_start, e_stop) / args.steps
-            result["graph"] = {"ms_per_step": round(gms, 5),
-                               "tokens_per_s": round(wl.batch * 1e3 / gms, 2)}
-            log(f"[bench] graph replay: {gms:.4f} ms/step")
-        except Exception as exc:  # report, keep the eager result
-            result["graph"] = {"error": str(exc)[:200]}
+    result["launch"] = "hip_graph_replay" if graph_ms is not None else "eager"
+    result["eager_ms_per_step"] = round(eager_ms, 5)
+    if graph_err:
+        result["graph_error"] = graph_err
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

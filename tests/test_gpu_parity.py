@@ -277,6 +277,19 @@ def test_decode_chain_planted_small():
     _run_chain(st, range(8), [(0, g) for g in range(8)], "planted-16k")
 
 
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_decode_chain_groups_mixed_pools(G):
+    """Ragged batch whose refined pools fall on both sides of 8192 entries
+    (the 9000-token sequence's pool exceeds it, the others stay below), for
+    group sizes whose refined layers select inside the attention kernel
+    (G <= 8) or in the selection kernel (G = 16)."""
+    wl = synth.scaled(synth.TINY_4K, name=f"chain-g{G}", wid=180 + G, num_q_heads=2 * G,
+                      num_kv_heads=2, batch=3, context=None, lengths=(4096, 1500, 9000),
+                      kappa=300, window=40, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3))
+    _run_chain(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"chain-g{G}")
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []

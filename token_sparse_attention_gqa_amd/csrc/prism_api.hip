@@ -222,12 +222,13 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   const Workspace w = prism::carve_workspace(workspace, g);
   if (layer % params->anchor_stride == 0) {
     PRISM_TRY(run_anchor(g, w, q, anchor_idx, layer_idx_out, s));
-  } else {
-    int32_t* dst = layer_idx_out ? layer_idx_out : w.idx_tmp;
-    PRISM_TRY(hip_check(prism::launch_refine(g, w, q, dst, s), "refined selection launch"));
+    return hip_check(
+        prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params), out, s),
+        "attention launch");
   }
-  return hip_check(prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params), out, s),
-                   "attention launch");
+  return hip_check(
+      prism::launch_refine_attend(g, w, q, resolve_scale(params), layer_idx_out, out, s),
+      "refined layer launch");
 }
 
 prism_status prism_profile_events(int32_t kind, void* const* start_events,

@@ -93,6 +93,11 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
 // into out, and the selection's row ids.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          hipStream_t s);
+// Refined layer of a decode step: pool scoring, then selection and SparseAttn
+// (pools of at most 8192 entries are selected inside the attention kernel).
+// layer_idx (nullable) receives the layer's set.
+hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, int32_t* layer_idx, float* out, hipStream_t s);
 // Zeroes the attention arrival counters (before a standalone attention call).
 hipError_t launch_zero_counters(const Geometry& g, const Workspace& w, hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with

@@ -36,6 +36,7 @@ constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the lis
 constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the pool build
 constexpr int kClsThreads = 256;
 constexpr int kClsEntries = 8192;         // anchor-list entries classified by one workgroup
+constexpr int kFusedSplit = 128;          // selected tokens attended by one fused refined workgroup
 static_assert(kMaxCand <= kCand, "candidates of the threshold bin fit the LDS candidate buffer");
 static_assert(kMaxKappa <= 2 * kCand, "pool-build run offsets fit the LDS candidate buffer");
 
@@ -432,8 +433,8 @@ __device__ __forceinline__ void emit_empty(const SelList& c, int o, SelectSmem& 
 
 // Wave 0 finds a bin and publishes it in sm.res[slot..slot+2]; all threads
 // read it after the barrier.
-template <int NB>
-__device__ Bin find_publish(const uint32_t* h, int need, SelectSmem& sm, int slot) {
+template <int NB, typename Sm>
+__device__ Bin find_publish(const uint32_t* h, int need, Sm& sm, int slot) {
   if (threadIdx.x < 64) {
     const Bin r = wave_find_bin<NB>(h, need);
     if (threadIdx.x == 0) {
@@ -451,7 +452,8 @@ __device__ Bin find_publish(const uint32_t* h, int need, SelectSmem& sm, int slo
 // bin = -1 if the histogram holds fewer than need.  Thread t owns bins
 // 4092 - 4t .. 4095 - 4t, so an exclusive scan in thread order counts from the
 // top.  Uniform over the block; contains barriers.
-__device__ Bin block_find_top(const uint32_t* h, int need, SelectSmem& sm) {
+template <typename Sm>
+__device__ Bin block_find_top(const uint32_t* h, int need, Sm& sm) {
   static_assert(NT * 4 == 4096, "four bins per thread");
   const int t = threadIdx.x;
   const u32x4 c4 = *reinterpret_cast<const u32x4*>(h + 4092 - 4 * t);
@@ -511,8 +513,8 @@ struct Thresh {
 // threads per entry).  A larger bucket (scores concentrated far inside their
 // range), a zero range or a non-finite range falls back to an exact
 // 12/10/10-bit radix over the keys.
-template <int R>
-__device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, SelectSmem& sm) {
+template <int R, typename Sm>
+__device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm& sm) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -1062,15 +1064,18 @@ __device__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
 
 // Top-kappa of one (sequence, KV head) per workgroup; zeroes the problem's
 // attention arrival counter; at an anchor layer also builds the pool.
+// With skip_small (refined layers of a decode step), pools of at most kSmall
+// entries are left to refine_attn_kernel, which selects them itself.
 template <bool POOL>
 __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
                                                     int32_t* __restrict__ out,
-                                                    int32_t* __restrict__ out2) {
+                                                    int32_t* __restrict__ out2, int skip_small) {
   __shared__ SelectSmem sm;
   const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
   const int K = g.kappa;
   if (threadIdx.x == 0) ws.ticket_attn[p] = 0u;
+  if (POOL && skip_small && clampi(ws.pool_len[p], 0, g.n_cap) <= kSmall) return;
   if (!POOL) {
     load_bt(g, b, L, sm.bt);
     __syncthreads();
@@ -1249,19 +1254,207 @@ __global__ void zero_counters_kernel(uint32_t* c, int n) {
 
 // ---------------------------------------------------------------------------
 // SparseAttn over one split of kAttnSplit selected tokens of one (sequence, KV
-// head), all G query heads: logits by MFMA as in scoring; the split's softmax
-// statistics (max logit, sum of exponentials) and unnormalised output go to the
-// workspace; the last split to finish merges all splits in split order.
+// head), all G query heads.  Each wave takes 16 tokens: logits by MFMA as in
+// scoring (lane j + 16 i4 holds token j for heads 4 i4 .. 4 i4 + 3), softmax
+// statistics over the wave's tokens inside 16-lane rows, the probabilities
+// through the wave's own LDS rows into the V accumulation (two dimensions per
+// lane).  One barrier combines the four waves into the split's statistics
+// (max logit, sum of exponentials) and unnormalised output, which go to the
+// workspace with device-scope stores; the last split to finish merges all
+// splits in split order, loading its share of every split's partials in one
+// batch.
 // ---------------------------------------------------------------------------
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __uint_as_float(dpp<kRowRor8, 0xf>(0u, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kRowRor4, 0xf>(0u, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kRowRor2, 0xf>(0u, __float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp<kRowRor1, 0xf>(0u, __float_as_uint(v))));
+  return v;
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __uint_as_float(dpp<kRowRor8, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowRor4, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowRor2, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kRowRor1, 0xf>(0u, __float_as_uint(v)));
+  return v;
+}
+
+static_assert(kAttnSplit == 64 && kAttnThreads == 256, "one 16-token tile per wave");
+constexpr int kMergeBatch = 32;  // splits whose partials one merge round loads at once
+static_assert(3 * (kMaxKappa / kAttnSplit) + 1 <= 4 * kHeadDim, "merge tables fit the wave outputs");
+
+template <int G>
+constexpr int prob_stride() { return G < 4 ? 4 : G; }
+
+// One wave's share of SparseAttn: 16 tokens (row ids; `valid` false masks a
+// token).  Leaves the wave's softmax statistics for heads 4 g4 + r in m[r],
+// l[r] (lanes 16 g4 .. 16 g4 + 15 agree) and the unnormalised output of every
+// head for dimensions 2 lane, 2 lane + 1 in o0, o1.  pw: the wave's own
+// [16][prob_stride<G>] rows of LDS.
+template <int G>
+__device__ __forceinline__ void wave_attend(const Geometry& g, const uint16_t* q, int b, int kvh,
+                                            uint32_t row, bool valid, float scale, float* pw,
+                                            float (&m)[4], float (&l)[4], float (&o0)[G],
+                                            float (&o1)[G]) {
+  constexpr int GP = prob_stride<G>();
+  const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+  u32x4 kf[4];
+  const u32x4* krow = reinterpret_cast<const u32x4*>(g.k_pages + (size_t)row * kHeadDim);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) kf[s4] = krow[g4 + 4 * s4];
+  uint32_t vv[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)row, jj);
+    vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
+  }
+  u32x4 qf[4];
+  load_q_frag<G>(q, g, b, kvh, lane, qf);
+  const f32x4 acc = qk_tile(qf, kf);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float z = valid ? acc[r] * scale : -INFINITY;
+    m[r] = row16_max(z);
+    const float e = (z == -INFINITY) ? 0.f : __expf(z - m[r]);
+    l[r] = row16_sum(e);
+    if (4 * g4 + r < G) pw[j * GP + 4 * g4 + r] = e;
+  }
+  // pw rows are written and read by this wave only: LDS keeps a wave's
+  // accesses in order; this keeps the compiler from reordering them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < G; ++i) o0[i] = o1[i] = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const float v0 = __uint_as_float(vv[jj] << 16);
+    const float v1 = __uint_as_float(vv[jj] & 0xffff0000u);
+#pragma unroll
+    for (int i4 = 0; i4 < GP / 4; ++i4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&pw[jj * GP + 4 * i4]);
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * i4 + r < G) {
+          o0[4 * i4 + r] += wv[r] * v0;
+          o1[4 * i4 + r] += wv[r] * v1;
+        }
+      }
+    }
+  }
+}
+
+// The block's split of SparseAttn from its NW waves' results (wo, wml, filled
+// and synchronised by the caller): rescaled to a common maximum and stored to
+// the workspace with device-scope stores; then the last split of the problem
+// to arrive merges all splits in split order into out.  Each merging thread
+// owns outputs t + T k; the first batch of their partials is loaded together
+// with the splits' (max, sum) pairs; wave w then finds, for heads w, w + NW,
+// ..., the maximum over splits (one split per lane), every split's weight
+// exp(m - M) and the weighted sum of the splits' sums.
+template <int G, int NW, int T>
+__device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int s, int splits,
+                             int b, int kvh, float (*wo)[G][kHeadDim], float (*wml)[G][2],
+                             int* last, float* out) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  float* po = ws.part_o + ((size_t)p * splits + s) * G * kHeadDim;
+  float* pm = ws.part_ml + ((size_t)p * splits + s) * G * 2;
+  for (int o = t; o < G * kHeadDim; o += T) {
+    const int i = o / kHeadDim, d = o - i * kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wml[w][i][0]);
+    float a = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = wml[w][i][0];
+        const float f = (mw == -INFINITY) ? 0.f : __expf(mw - M);
+        a += wo[w][i][d] * f;
+        L += wml[w][i][1] * f;
+      }
+    }
+    st_dev(po + o, a);
+    if (d == 0) {
+      st_dev(pm + 2 * i, M);
+      st_dev(pm + 2 * i + 1, L);
+    }
+  }
+
+  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, last)) return;
+
+  constexpr int NO = (G * kHeadDim + T - 1) / T;
+  const float* pml = ws.part_ml + (size_t)p * splits * G * 2;
+  const float* pob = ws.part_o + (size_t)p * splits * G * kHeadDim;
+  float* mls = &wo[0][0][0];          // [splits][G][2]
+  float* wgt = mls + 2 * G * splits;  // [G][splits]
+  float* lsum = wgt + G * splits;     // [G]
+  // unconditional loads (indices clamped into the partials; surplus values
+  // get no weight) keep the batch free of branches
+  float pv[NO][kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int o = min(t + T * k, G * kHeadDim - 1);
+#pragma unroll
+    for (int x = 0; x < kMergeBatch; ++x)
+      pv[k][x] = ld_dev(pob + (size_t)min(x, splits - 1) * G * kHeadDim + o);
+  }
+  for (int i = t; i < 2 * G * splits; i += T) mls[i] = ld_dev(pml + i);
+  __syncthreads();
+  for (int i = wave; i < G; i += T / 64) {
+    float M = -INFINITY;
+    for (int x = lane; x < splits; x += 64) M = fmaxf(M, mls[(x * G + i) * 2]);
+    M = wave_max(M);
+    float ls = 0.f;
+    for (int x = lane; x < splits; x += 64) {
+      const float mx = mls[(x * G + i) * 2];
+      const float f = (mx == -INFINITY) ? 0.f : __expf(mx - M);
+      wgt[i * splits + x] = f;
+      ls += mls[(x * G + i) * 2 + 1] * f;
+    }
+    ls = wave_sum(ls);
+    if (lane == 0) lsum[i] = ls;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < NO; ++k) {
+    const int o = t + T * k;
+    if (o >= G * kHeadDim) break;
+    const int i = o / kHeadDim, d = o - i * kHeadDim;
+    const float* wi = wgt + i * splits;
+    float a = 0.f;
+    for (int x0 = 0; x0 < splits; x0 += kMergeBatch) {
+      if (x0 > 0) {
+#pragma unroll
+        for (int x = 0; x < kMergeBatch; ++x)
+          pv[k][x] = ld_dev(pob + (size_t)min(x0 + x, splits - 1) * G * kHeadDim + o);
+      }
+#pragma unroll
+      for (int x = 0; x < kMergeBatch; ++x)
+        if (x0 + x < splits) a += pv[k][x] * wi[x0 + x];
+    }
+    const float L = lsum[i];
+    out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = L > 0.f ? a / L : 0.f;
+  }
+  if (t == 0) ticket_reset(&ws.ticket_attn[p]);
+}
+
+// SparseAttn over a given set (positions in idx) or over the row ids the
+// latest selection left in the workspace (ROWS): kAttnSplit tokens per
+// workgroup, 16 per wave.
 template <int G, bool ROWS>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspace ws,
                                                             const uint16_t* __restrict__ q,
                                                             const int32_t* __restrict__ idx,
                                                             float scale,
                                                             float* __restrict__ out) {
-  __shared__ float lg[G][kAttnSplit];
-  __shared__ float red[4][G][kHeadDim];
-  __shared__ float sm[G], sl[G];
+  constexpr int NW = kAttnThreads / 64;
+  __shared__ float wo[NW][G][kHeadDim];
+  __shared__ float wml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
   __shared__ int last;
   const int splits = g.splits;
   int p, s;
@@ -1284,97 +1477,164 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
     valid = pos >= 0 && pos < L;
     row = row_id(g, b, kvh, valid ? pos : 0);
   }
-  const size_t roff = (size_t)row * kHeadDim;
-
-  u32x4 kf[4];
-  const u32x4* krow = reinterpret_cast<const u32x4*>(g.k_pages + roff);
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) kf[s4] = krow[g4 + 4 * s4];
-  uint32_t vv[16];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)row, jj);
-    vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
-  }
-  u32x4 qf[4];
-  load_q_frag<G>(q, g, b, kvh, lane, qf);
-
-  const f32x4 acc = qk_tile(qf, kf);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = 4 * g4 + r;
-    if (i < G) lg[i][wave * 16 + j] = valid ? acc[r] * scale : -INFINITY;
-  }
-  __syncthreads();
-  for (int i = wave; i < G; i += 4) {
-    const float z = lg[i][lane];
-    const float m = wave_max(z);
-    const float e = (z == -INFINITY) ? 0.f : __expf(z - m);
-    const float l = wave_sum(e);
-    lg[i][lane] = e;
-    if (lane == 0) {
-      sm[i] = m;
-      sl[i] = l;
-    }
-  }
-  __syncthreads();
-  float o0[G], o1[G];
-#pragma unroll
-  for (int i = 0; i < G; ++i) o0[i] = o1[i] = 0.f;
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const float v0 = __uint_as_float(vv[jj] << 16);
-    const float v1 = __uint_as_float(vv[jj] & 0xffff0000u);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const float pw = lg[i][wave * 16 + jj];
-      o0[i] += pw * v0;
-      o1[i] += pw * v1;
-    }
-  }
+  float m[4], l[4], o0[G], o1[G];
+  wave_attend<G>(g, q, b, kvh, row, valid, scale, pw[wave], m, l, o0, o1);
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    red[wave][i][2 * lane] = o0[i];
-    red[wave][i][2 * lane + 1] = o1[i];
+    wo[wave][i][2 * lane] = o0[i];
+    wo[wave][i][2 * lane + 1] = o1[i];
   }
-  __syncthreads();
-  float* po = ws.part_o + ((size_t)p * splits + s) * G * kHeadDim;
-  for (int o = t; o < G * kHeadDim; o += kAttnThreads) {
-    const int i = o / kHeadDim, d = o - i * kHeadDim;
-    st_dev(po + o, (red[0][i][d] + red[1][i][d]) + (red[2][i][d] + red[3][i][d]));
-  }
-  if (t < G) {
-    float* pm = ws.part_ml + (((size_t)p * splits + s) * G + t) * 2;
-    st_dev(pm, sm[t]);
-    st_dev(pm + 1, sl[t]);
-  }
-
-  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, &last)) return;
-
-  // Merge: the splits' (max, sum) pairs go to LDS, then each output element
-  // reads its per-split partial values (independent device-scope loads).
-  const float* pml = ws.part_ml + (size_t)p * splits * G * 2;
-  const float* pob = ws.part_o + (size_t)p * splits * G * kHeadDim;
-  float* ml = &red[0][0][0];  // 2 * G * splits <= 4 * G * kHeadDim floats
-  for (int i = t; i < 2 * G * splits; i += kAttnThreads) ml[i] = ld_dev(pml + i);
-  __syncthreads();
-  for (int o = t; o < G * kHeadDim; o += kAttnThreads) {
-    const int i = o / kHeadDim, d = o - i * kHeadDim;
-    float M = -INFINITY;
-    for (int x = 0; x < splits; ++x) M = fmaxf(M, ml[(x * G + i) * 2]);
-    float lsum = 0.f, acc2 = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 16
-      for (int x = 0; x < splits; ++x) {
-        const float mx = ml[(x * G + i) * 2];
-        const float f = (mx == -INFINITY) ? 0.f : __expf(mx - M);
-        lsum += ml[(x * G + i) * 2 + 1] * f;
-        acc2 += ld_dev(pob + ((size_t)x * G + i) * kHeadDim + d) * f;
+  if (j == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * g4 + r < G) {
+        wml[wave][4 * g4 + r][0] = m[r];
+        wml[wave][4 * g4 + r][1] = l[r];
       }
     }
-    out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = lsum > 0.f ? acc2 / lsum : 0.f;
   }
-  if (t == 0) ticket_reset(&ws.ticket_attn[p]);
+  __syncthreads();
+  finish_split<G, NW, kAttnThreads>(g, ws, p, s, splits, b, kvh, wo, wml, &last, out);
+}
+
+// Refined layer, pools of at most kSmall entries: the selection and SparseAttn
+// in one kernel.  Workgroup s of problem p selects the pool's top-kappa itself
+// (every split's workgroup reaches the same set: same keys, same order) and
+// attends its ranks [s * kFusedSplit, +kFusedSplit) of the ascending set, 16
+// per wave; layer_idx, if given, receives those ranks' positions.  Pools longer
+// than kSmall were selected by select_kernel, whose row ids it reads instead.
+template <int G>
+struct FusedSmem {
+  uint32_t hist[4096 + 1024 + 1024];
+  uint32_t pair[kPairMax];
+  uint32_t ured[32];
+  int tmp[NT / 64 + 1];
+  int res[9];
+  int cnt[2];
+  uint32_t srow[kFusedSplit];
+  float wo[NT / 64][G][kHeadDim];
+  float wml[NT / 64][G][2];
+  float pw[NT / 64][16 * prob_stride<G>()] __attribute__((aligned(16)));
+  int last;
+};
+
+template <int G>
+__global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
+                                                         const uint16_t* __restrict__ q,
+                                                         float scale, float* __restrict__ out,
+                                                         int32_t* __restrict__ layer_idx) {
+  constexpr int NW = kFusedSplit / 16;  // waves that attend, 16 tokens each
+  static_assert(NW >= 1 && NW <= NT / 64, "attending waves fit the workgroup");
+  static_assert(3 * (kMaxKappa / kFusedSplit) + 1 <= NW * kHeadDim, "merge tables fit");
+  __shared__ FusedSmem<G> sm;
+  const int K = g.kappa;
+  const int splits = (K + kFusedSplit - 1) / kFusedSplit;
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+  const int r0 = s * kFusedSplit;  // first rank of this split
+  const int myr = r0 + wave * 16 + j;
+  uint32_t row = 0u;
+  bool valid = false;
+  if (n <= kSmall) {  // uniform over the workgroup
+    const int e0 = 8 * t;
+    const int nv = clampi(n - e0, 0, 8);
+    const int ea = e0 < n ? e0 : 0;
+    const size_t base = (size_t)p * g.n_cap + ea;
+    const u32x4 r0k = *reinterpret_cast<const u32x4*>(ws.scores + base);
+    const u32x4 r1k = *reinterpret_cast<const u32x4*>(ws.scores + base + 4);
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(ws.pool_row + base);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(ws.pool_row + base + 4);
+    u32x4 p0 = {0u, 0u, 0u, 0u}, p1 = p0;
+    if (layer_idx) {
+      p0 = *reinterpret_cast<const u32x4*>(ws.pool_pos + base);
+      p1 = *reinterpret_cast<const u32x4*>(ws.pool_pos + base + 4);
+    }
+    uint32_t key[8], pr[8];
+    int32_t pl[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      key[i] = order_key(__uint_as_float(r0k[i]));
+      key[i + 4] = order_key(__uint_as_float(r1k[i]));
+      pr[i] = w0[i];
+      pr[i + 4] = w1[i];
+      pl[i] = (int32_t)p0[i];
+      pl[i + 4] = (int32_t)p1[i];
+    }
+    uint32_t take = 0u;
+    if (n <= K) {
+      take = nv >= 8 ? 0xFFu : ((1u << nv) - 1u);
+    } else {
+      const Thresh th = find_threshold<8>(key, nv, K, sm);
+      if (th.eq_total == th.need_eq) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nv && key[i] >= th.T) take |= 1u << i;
+      } else {  // more entries equal T than needed: the lowest list indices win
+        int my_eq = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < nv && key[i] == th.T) ++my_eq;
+        int tot;
+        int r = block_excl_scan<NT>(my_eq, sm.tmp, &tot);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          if (i < nv && key[i] > th.T) take |= 1u << i;
+          if (i < nv && key[i] == th.T) {
+            if (r < th.need_eq) take |= 1u << i;
+            ++r;
+          }
+        }
+      }
+    }
+    int total;
+    int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
+    const int rend = min(K, r0 + kFusedSplit);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (take & (1u << i)) {
+        if (o >= r0 && o < rend) {
+          sm.srow[o - r0] = pr[i];
+          if (layer_idx) layer_idx[(size_t)p * K + o] = pl[i];
+        }
+        ++o;
+      }
+    }
+    if (layer_idx)
+      for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
+    __syncthreads();
+    valid = myr < min(total, K);
+    row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
+  } else {
+    row = myr < K && wave < NW ? ws.sel_row[(size_t)p * K + myr] : kNoRow;
+  }
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  valid = row <= max_row && myr < K && (n > kSmall || valid);
+  if (!valid) row = 0u;
+
+  if (wave < NW) {  // uniform over the wave
+    float m[4], l[4], o0[G], o1[G];
+    wave_attend<G>(g, q, b, kvh, row, valid, scale, sm.pw[wave], m, l, o0, o1);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      sm.wo[wave][i][2 * lane] = o0[i];
+      sm.wo[wave][i][2 * lane + 1] = o1[i];
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g4 + r < G) {
+          sm.wml[wave][4 * g4 + r][0] = m[r];
+          sm.wml[wave][4 * g4 + r][1] = l[r];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out);
 }
 
 // ---------------------------------------------------------------------------
@@ -1532,7 +1792,7 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
+  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2, 0);
   return hipGetLastError();
 }
 
@@ -1548,7 +1808,39 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w, out,
-         static_cast<int32_t*>(nullptr));
+         static_cast<int32_t*>(nullptr), 0);
+  return hipGetLastError();
+}
+
+template <int G>
+void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
+                          float* out, int32_t* layer_idx, hipStream_t s) {
+  const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
+  launch(kAttention, refine_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
+         scale, out, layer_idx);
+}
+
+hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, int32_t* layer_idx, float* out, hipStream_t s) {
+  if (g.group > 8) {  // the fused kernel's LDS holds up to 8 heads: select, then attend
+    hipError_t e = launch_refine(g, w, q, layer_idx ? layer_idx : w.idx_tmp, s);
+    if (e != hipSuccess) return e;
+    return launch_attention(g, w, q, nullptr, true, scale, out, s);
+  }
+  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w,
+         layer_idx ? layer_idx : w.idx_tmp, static_cast<int32_t*>(nullptr), 1);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (g.group) {
+    case 1: launch_refine_attn_g<1>(g, w, q, scale, out, layer_idx, s); break;
+    case 2: launch_refine_attn_g<2>(g, w, q, scale, out, layer_idx, s); break;
+    case 4: launch_refine_attn_g<4>(g, w, q, scale, out, layer_idx, s); break;
+    case 8: launch_refine_attn_g<8>(g, w, q, scale, out, layer_idx, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
