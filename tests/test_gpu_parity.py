@@ -116,7 +116,7 @@ def test_exact_ties_go_to_lowest_position():
 def test_concentrated_scores_and_long_ties(L, kappa):
     """Head 0: every row equal (one score repeated L times).  Head 1: one key
     row scaled by 2^16, so every other score sits inside one 1/4096 slice of
-    the score range.  Lists below and above 8192 entries."""
+    the score range.  Lists below and above 16384 entries."""
     rng = np.random.default_rng(8)
     G = 4
     base = rng.standard_normal((L, 128)).astype(np.float32)
@@ -279,13 +279,13 @@ def test_decode_chain_planted_small():
 
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_decode_chain_groups_mixed_pools(G):
-    """Ragged batch whose refined pools fall on both sides of 8192 entries
-    (the 9000-token sequence's pool exceeds it, the others stay below), for
+    """Ragged batch whose refined pools fall on both sides of 16384 entries
+    (the 20000-token sequence's pool exceeds it, the others stay below), for
     group sizes whose refined layers select inside the attention kernel
     (G <= 8) or in the selection kernel (G = 16)."""
     wl = synth.scaled(synth.TINY_4K, name=f"chain-g{G}", wid=180 + G, num_q_heads=2 * G,
-                      num_kv_heads=2, batch=3, context=None, lengths=(4096, 1500, 9000),
-                      kappa=300, window=40, num_layers=3, anchor_stride=3)
+                      num_kv_heads=2, batch=3, context=None, lengths=(4096, 1500, 20000),
+                      kappa=300, window=100, num_layers=3, anchor_stride=3)
     st = Setup(wl, range(3))
     _run_chain(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"chain-g{G}")
 

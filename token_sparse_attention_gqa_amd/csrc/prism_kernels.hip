@@ -29,7 +29,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = kSelThreads;
-constexpr int kSmall = 8192;    // lists up to this length are selected entirely in LDS
+constexpr int kSmall = 16384;   // lists up to this length are selected with every key in registers
+constexpr int kSmallPer = kSmall / kSelThreads;  // 16 consecutive entries per thread
 constexpr int kSample = 8192;   // most entries of a longer list sampled to bracket the kappa-th key
 constexpr int kCand = 4096;     // bracketed candidates held in LDS
 constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the list pass
@@ -620,52 +621,29 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
   return Thresh{(pre << 10) | (uint32_t)cc.bin, need - a.above - bb.above - cc.above, cc.count};
 }
 
-// Lists of at most kSmall entries.  Thread t holds entries 8t .. 8t+7 (keys,
-// and for a pool their positions and row ids, all loaded up front), so counts
-// scanned in thread order give ascending output positions directly.
-__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
-  const int t = threadIdx.x;
-  const int e0 = 8 * t;
-  const int nv = clampi(c.n - e0, 0, 8);  // valid entries of this thread
-  const int ea = e0 < c.n ? e0 : 0;       // entries past n are loaded but not used
-  uint32_t key[8];
-  int32_t pl[8];
-  uint32_t pr[8];
-  {
-    const u32x4 r0 = *reinterpret_cast<const u32x4*>(c.sc + ea);
-    const u32x4 r1 = *reinterpret_cast<const u32x4*>(c.sc + ea + 4);
-    u32x4 p0 = {0u, 0u, 0u, 0u}, p1 = p0, w0 = p0, w1 = p0;
-    if (c.plist) {
-      p0 = *reinterpret_cast<const u32x4*>(c.plist + ea);
-      p1 = *reinterpret_cast<const u32x4*>(c.plist + ea + 4);
-      w0 = *reinterpret_cast<const u32x4*>(c.prow + ea);
-      w1 = *reinterpret_cast<const u32x4*>(c.prow + ea + 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      key[i] = order_key(__uint_as_float(r0[i]));
-      key[i + 4] = order_key(__uint_as_float(r1[i]));
-      pl[i] = (int32_t)p0[i];
-      pl[i + 4] = (int32_t)p1[i];
-      pr[i] = w0[i];
-      pr[i + 4] = w1[i];
-    }
-  }
-  const Thresh th = find_threshold<8>(key, nv, c.K, sm);
+// Which of a thread's R consecutive list entries (keys in registers, valid
+// for i < nv) belong to the top-K of the n-entry list: bit i of the result.
+// Ties at the threshold go to the lowest list indices (thread order is list
+// order).  Contains barriers: call uniformly.
+template <int R, typename Sm>
+__device__ uint32_t top_k_mask(const uint32_t (&key)[R], int nv, int n, int K, Sm& sm) {
+  static_assert(R <= 32, "one mask bit per entry");
+  if (n <= K) return nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+  const Thresh th = find_threshold<R>(key, nv, K, sm);
   uint32_t take = 0u;
   if (th.eq_total == th.need_eq) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < R; ++i)
       if (i < nv && key[i] >= th.T) take |= 1u << i;
   } else {  // more entries equal T than needed: the lowest list indices win
     int my_eq = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < R; ++i)
       if (i < nv && key[i] == th.T) ++my_eq;
     int tot;
     int r = block_excl_scan<NT>(my_eq, sm.tmp, &tot);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
       if (i < nv && key[i] > th.T) take |= 1u << i;
       if (i < nv && key[i] == th.T) {
         if (r < th.need_eq) take |= 1u << i;
@@ -673,13 +651,46 @@ __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm
       }
     }
   }
+  return take;
+}
+
+// Loads R consecutive 32-bit entries starting at e0 (a multiple of R below the
+// row's capacity, a multiple of 64) as R / 4 vector loads.
+template <int R, typename T>
+__device__ __forceinline__ void load_run(const T* base, int e0, uint32_t (&v)[R]) {
+#pragma unroll
+  for (int k = 0; k < R / 4; ++k) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(base + e0 + 4 * k);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[4 * k + i] = x[i];
+  }
+}
+
+// Lists of at most kSmall entries.  Thread t holds entries R t .. R t + R - 1
+// (keys, and for a pool their positions and row ids, all loaded up front), so
+// counts scanned in thread order give ascending output positions directly.
+__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  constexpr int R = kSmallPer;
+  const int t = threadIdx.x;
+  const int e0 = R * t;
+  const int nv = clampi(c.n - e0, 0, R);  // valid entries of this thread
+  const int ea = e0 < c.n ? e0 : 0;       // entries past n are loaded but not used
+  uint32_t key[R], pl[R], pr[R];
+  load_run<R>(c.sc, ea, key);
+  if (c.plist) {
+    load_run<R>(c.plist, ea, pl);
+    load_run<R>(c.prow, ea, pr);
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+  const uint32_t take = top_k_mask<R>(key, nv, c.n, c.K, sm);
   int total;
   int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < R; ++i) {
     if (take & (1u << i)) {
       if (o < c.K) {
-        const int pos = c.plist ? pl[i] : e0 + i;
+        const int pos = c.plist ? (int)pl[i] : e0 + i;
         const uint32_t row = c.prow ? pr[i] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
         emit_at(g, c, pos, row, o, sm);
       }
@@ -1540,65 +1551,27 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
   uint32_t row = 0u;
   bool valid = false;
   if (n <= kSmall) {  // uniform over the workgroup
-    const int e0 = 8 * t;
-    const int nv = clampi(n - e0, 0, 8);
+    constexpr int R = kSmallPer;
+    const int e0 = R * t;
+    const int nv = clampi(n - e0, 0, R);
     const int ea = e0 < n ? e0 : 0;
-    const size_t base = (size_t)p * g.n_cap + ea;
-    const u32x4 r0k = *reinterpret_cast<const u32x4*>(ws.scores + base);
-    const u32x4 r1k = *reinterpret_cast<const u32x4*>(ws.scores + base + 4);
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(ws.pool_row + base);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(ws.pool_row + base + 4);
-    u32x4 p0 = {0u, 0u, 0u, 0u}, p1 = p0;
-    if (layer_idx) {
-      p0 = *reinterpret_cast<const u32x4*>(ws.pool_pos + base);
-      p1 = *reinterpret_cast<const u32x4*>(ws.pool_pos + base + 4);
-    }
-    uint32_t key[8], pr[8];
-    int32_t pl[8];
+    const size_t base = (size_t)p * g.n_cap;
+    uint32_t key[R], pr[R], pl[R];
+    load_run<R>(ws.scores + base, ea, key);
+    load_run<R>(ws.pool_row + base, ea, pr);
+    if (layer_idx) load_run<R>(ws.pool_pos + base, ea, pl);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      key[i] = order_key(__uint_as_float(r0k[i]));
-      key[i + 4] = order_key(__uint_as_float(r1k[i]));
-      pr[i] = w0[i];
-      pr[i + 4] = w1[i];
-      pl[i] = (int32_t)p0[i];
-      pl[i + 4] = (int32_t)p1[i];
-    }
-    uint32_t take = 0u;
-    if (n <= K) {
-      take = nv >= 8 ? 0xFFu : ((1u << nv) - 1u);
-    } else {
-      const Thresh th = find_threshold<8>(key, nv, K, sm);
-      if (th.eq_total == th.need_eq) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < nv && key[i] >= th.T) take |= 1u << i;
-      } else {  // more entries equal T than needed: the lowest list indices win
-        int my_eq = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < nv && key[i] == th.T) ++my_eq;
-        int tot;
-        int r = block_excl_scan<NT>(my_eq, sm.tmp, &tot);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (i < nv && key[i] > th.T) take |= 1u << i;
-          if (i < nv && key[i] == th.T) {
-            if (r < th.need_eq) take |= 1u << i;
-            ++r;
-          }
-        }
-      }
-    }
+    for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+    const uint32_t take = top_k_mask<R>(key, nv, n, K, sm);
     int total;
     int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
     const int rend = min(K, r0 + kFusedSplit);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < R; ++i) {
       if (take & (1u << i)) {
         if (o >= r0 && o < rend) {
           sm.srow[o - r0] = pr[i];
-          if (layer_idx) layer_idx[(size_t)p * K + o] = pl[i];
+          if (layer_idx) layer_idx[(size_t)p * K + o] = (int32_t)pl[i];
         }
         ++o;
       }
