@@ -669,8 +669,8 @@ __device__ __forceinline__ void load_run(const T* base, int e0, uint32_t (&v)[R]
 // Lists of at most kSmall entries.  Thread t holds entries R t .. R t + R - 1
 // (keys, and for a pool their positions and row ids, all loaded up front), so
 // counts scanned in thread order give ascending output positions directly.
+template <int R>
 __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
-  constexpr int R = kSmallPer;
   const int t = threadIdx.x;
   const int e0 = R * t;
   const int nv = clampi(c.n - e0, 0, R);  // valid entries of this thread
@@ -1107,8 +1107,10 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
       if (e < c.n) emit_entry(g, c, e, e, sm);
       else emit_empty(c, e, sm);
     }
+  } else if (c.n <= kSmall / 2) {
+    select_small<kSmallPer / 2>(g, c, sm);
   } else if (c.n <= kSmall) {
-    select_small(g, c, sm);
+    select_small<kSmallPer>(g, c, sm);
   } else if (!POOL) {
     select_classified(g, ws, p, c, sm);
   } else {
@@ -1529,6 +1531,44 @@ struct FusedSmem {
   int last;
 };
 
+// The selection step of refine_attn_kernel: every thread holds R consecutive
+// pool entries (R n_threads >= n); the block finds the pool's top-kappa and
+// keeps the row ids of ranks [r0, r0 + kFusedSplit) in sm.srow (and writes
+// their positions to layer_idx).  Returns the size of the selected set.
+template <int R, typename Sm>
+__device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p, int n, int r0,
+                                  int32_t* layer_idx, Sm& sm) {
+  const int t = threadIdx.x, K = g.kappa;
+  const int e0 = R * t;
+  const int nv = clampi(n - e0, 0, R);
+  const int ea = e0 < n ? e0 : 0;
+  const size_t base = (size_t)p * g.n_cap;
+  uint32_t key[R], pr[R], pl[R];
+  load_run<R>(ws.scores + base, ea, key);
+  load_run<R>(ws.pool_row + base, ea, pr);
+  if (layer_idx) load_run<R>(ws.pool_pos + base, ea, pl);
+#pragma unroll
+  for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+  const uint32_t take = top_k_mask<R>(key, nv, n, K, sm);
+  int total;
+  int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
+  const int rend = min(K, r0 + kFusedSplit);
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (take & (1u << i)) {
+      if (o >= r0 && o < rend) {
+        sm.srow[o - r0] = pr[i];
+        if (layer_idx) layer_idx[(size_t)p * K + o] = (int32_t)pl[i];
+      }
+      ++o;
+    }
+  }
+  if (layer_idx)
+    for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
+  __syncthreads();
+  return total;
+}
+
 template <int G>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
@@ -1551,34 +1591,11 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
   uint32_t row = 0u;
   bool valid = false;
   if (n <= kSmall) {  // uniform over the workgroup
-    constexpr int R = kSmallPer;
-    const int e0 = R * t;
-    const int nv = clampi(n - e0, 0, R);
-    const int ea = e0 < n ? e0 : 0;
-    const size_t base = (size_t)p * g.n_cap;
-    uint32_t key[R], pr[R], pl[R];
-    load_run<R>(ws.scores + base, ea, key);
-    load_run<R>(ws.pool_row + base, ea, pr);
-    if (layer_idx) load_run<R>(ws.pool_pos + base, ea, pl);
-#pragma unroll
-    for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
-    const uint32_t take = top_k_mask<R>(key, nv, n, K, sm);
     int total;
-    int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
-    const int rend = min(K, r0 + kFusedSplit);
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      if (take & (1u << i)) {
-        if (o >= r0 && o < rend) {
-          sm.srow[o - r0] = pr[i];
-          if (layer_idx) layer_idx[(size_t)p * K + o] = (int32_t)pl[i];
-        }
-        ++o;
-      }
-    }
-    if (layer_idx)
-      for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
-    __syncthreads();
+    if (n <= kSmall / 2)
+      total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, layer_idx, sm);
+    else
+      total = fused_select_slice<kSmallPer>(g, ws, p, n, r0, layer_idx, sm);
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   } else {
