@@ -348,6 +348,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
                                                                    int wgs) {
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
@@ -730,7 +731,8 @@ __device__ void emit_bitmap(const Geometry& g, const SelList& c, SelectSmem& sm)
 // the exact K-th key T is found.  If the bracket misses or overflows, an exact
 // radix runs over the whole list instead.  The bitmap, read in order, gives
 // ascending positions; entries equal to T are taken lowest list index first.
-__device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
+template <typename Sm>
+__device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) {
   const int t = threadIdx.x, lane = t & 63;
   const int n = c.n, K = c.K;
   uint32_t* h1 = sm.hist;
@@ -894,6 +896,10 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
     }
   }
   __syncthreads();
+}
+
+__device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  select_large_marks(g, c, sm);
   emit_bitmap(g, c, sm);
 }
 
@@ -1075,18 +1081,15 @@ __device__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
 
 // Top-kappa of one (sequence, KV head) per workgroup; zeroes the problem's
 // attention arrival counter; at an anchor layer also builds the pool.
-// With skip_small (refined layers of a decode step), pools of at most kSmall
-// entries are left to refine_attn_kernel, which selects them itself.
 template <bool POOL>
 __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
                                                     int32_t* __restrict__ out,
-                                                    int32_t* __restrict__ out2, int skip_small) {
+                                                    int32_t* __restrict__ out2) {
   __shared__ SelectSmem sm;
   const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
   const int K = g.kappa;
   if (threadIdx.x == 0) ws.ticket_attn[p] = 0u;
-  if (POOL && skip_small && clampi(ws.pool_len[p], 0, g.n_cap) <= kSmall) return;
   if (!POOL) {
     load_bt(g, b, L, sm.bt);
     __syncthreads();
@@ -1510,12 +1513,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
   finish_split<G, NW, kAttnThreads>(g, ws, p, s, splits, b, kvh, wo, wml, &last, out);
 }
 
-// Refined layer, pools of at most kSmall entries: the selection and SparseAttn
-// in one kernel.  Workgroup s of problem p selects the pool's top-kappa itself
-// (every split's workgroup reaches the same set: same keys, same order) and
-// attends its ranks [s * kFusedSplit, +kFusedSplit) of the ascending set, 16
-// per wave; layer_idx, if given, receives those ranks' positions.  Pools longer
-// than kSmall were selected by select_kernel, whose row ids it reads instead.
+// Refined layer of a decode step: the selection and SparseAttn in one kernel.
+// Workgroup s of problem p selects the pool's top-kappa itself (every split's
+// workgroup reaches the same set: same keys, same order) and attends its ranks
+// [s * kFusedSplit, +kFusedSplit) of the ascending set, 16 per wave;
+// layer_idx, if given, receives those ranks' positions.  Pools of at most
+// kSmall entries are selected in registers, longer ones by the sampled
+// bracket and one pass over the pool (marks in an LDS bitmap).
 template <int G>
 struct FusedSmem {
   uint32_t hist[4096 + 1024 + 1024];
@@ -1524,10 +1528,12 @@ struct FusedSmem {
   int tmp[NT / 64 + 1];
   int res[9];
   int cnt[2];
+  uint32_t bitmap[kMaxSeqLen / 32];  // pools longer than kSmall: selection marks
+  uint32_t cbuf[2 * kCand];
   uint32_t srow[kFusedSplit];
-  float wo[NT / 64][G][kHeadDim];
-  float wml[NT / 64][G][2];
-  float pw[NT / 64][16 * prob_stride<G>()] __attribute__((aligned(16)));
+  float wo[kFusedSplit / 16][G][kHeadDim];
+  float wml[kFusedSplit / 16][G][2];
+  float pw[kFusedSplit / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
   int last;
 };
 
@@ -1569,6 +1575,40 @@ __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p,
   return total;
 }
 
+// Ranks [r0, r0 + kFusedSplit) of the entries marked in sm.bitmap (marks in
+// list order, so ranks are ascending positions): their row ids go to sm.srow
+// and their positions to layer_idx.  Returns the number of marked entries.
+template <typename Sm>
+__device__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_idx, Sm& sm) {
+  const int t = threadIdx.x, K = c.K;
+  const int words = (c.n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
+  int total;
+  int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  const int rend = min(K, r0 + kFusedSplit);
+  if (o < rend && o + cnt > r0) {
+    for (int i = w0; i < w1 && o < rend; ++i) {
+      uint32_t m = sm.bitmap[i];
+      while (m && o < rend) {
+        const int e = i * 32 + (__ffs(m) - 1);
+        m &= m - 1u;
+        if (o >= r0) {
+          sm.srow[o - r0] = c.prow[e];
+          if (layer_idx) layer_idx[(size_t)p * K + o] = c.plist[e];
+        }
+        ++o;
+      }
+    }
+  }
+  if (layer_idx)
+    for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
+  __syncthreads();
+  return total;
+}
+
 template <int G>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
@@ -1599,10 +1639,23 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   } else {
-    row = myr < K && wave < NW ? ws.sel_row[(size_t)p * K + myr] : kNoRow;
+    SelList c;
+    c.sc = ws.scores + (size_t)p * g.n_cap;
+    c.plist = ws.pool_pos + (size_t)p * g.n_cap;
+    c.prow = ws.pool_row + (size_t)p * g.n_cap;
+    c.n = n;
+    c.K = K;
+    c.b = b;
+    c.kvh = kvh;
+    c.o1 = c.o2 = nullptr;
+    c.srow = nullptr;
+    select_large_marks(g, c, sm);
+    const int total = slice_from_marks(c, p, r0, layer_idx, sm);
+    valid = myr < min(total, K);
+    row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   }
   const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
-  valid = row <= max_row && myr < K && (n > kSmall || valid);
+  valid = valid && row <= max_row;
   if (!valid) row = 0u;
 
   if (wave < NW) {  // uniform over the wave
@@ -1782,7 +1835,7 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2, 0);
+  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
   return hipGetLastError();
 }
 
@@ -1798,7 +1851,7 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w, out,
-         static_cast<int32_t*>(nullptr), 0);
+         static_cast<int32_t*>(nullptr));
   return hipGetLastError();
 }
 
@@ -1819,10 +1872,6 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
   }
   PRISM_BY_GROUP(launch_pool_score_g, g, w, q, s);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w,
-         layer_idx ? layer_idx : w.idx_tmp, static_cast<int32_t*>(nullptr), 1);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g.group) {
     case 1: launch_refine_attn_g<1>(g, w, q, scale, out, layer_idx, s); break;
