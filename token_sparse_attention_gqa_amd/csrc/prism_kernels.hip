@@ -50,6 +50,15 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Workgroup barrier for LDS communication only: waits for the workgroup's LDS
+// accesses, not for its global loads and stores still in flight (the
+// compiler's __syncthreads waits for every memory access of the workgroup).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ int seq_len_of(const Geometry& g, int b) {
   return clampi(g.seq_lens[b], 0, g.max_seq_len);
 }
@@ -104,7 +113,7 @@ __device__ bool publish_and_arrive(uint32_t* ctr, uint32_t total, int* flag) {
         __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *flag = (old + 1u == total) ? 1 : 0;
   }
-  __syncthreads();
+  lds_barrier();
   return *flag != 0;
 }
 
@@ -116,7 +125,7 @@ __device__ __forceinline__ void ticket_reset(uint32_t* ctr) {
 // cache-bypassing loads (used inside one workgroup only).
 __device__ __forceinline__ void wg_global_sync() {
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  lds_barrier();
 }
 
 // MFMA A-operand fragment of the group's query heads.  Lane l holds head
@@ -222,9 +231,9 @@ __device__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int inc = wave_incl_scan(v);
-  __syncthreads();  // earlier readers of tmp are done
+  lds_barrier();  // earlier readers of tmp are done
   if (lane == 63) tmp[w] = inc;
-  __syncthreads();
+  lds_barrier();
   const int x = lane < NW ? tmp[lane] : 0;
   const int xi = wave_incl_scan(x);
   *total = __builtin_amdgcn_readlane(xi, NW - 1);
@@ -287,7 +296,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
   const int j = lane & 15, g4 = lane >> 4;
   const int wbase = w * kAnchorEntries + wave * 256;
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   if (wbase < n) {
     u32x4 qf[4];
     load_q_frag<G>(q, g, b, kvh, lane, qf);
@@ -332,7 +341,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) {
     const uint32_t c = lh[i];
@@ -445,7 +454,7 @@ __device__ Bin find_publish(const uint32_t* h, int need, Sm& sm, int slot) {
       sm.res[slot + 2] = r.count;
     }
   }
-  __syncthreads();
+  lds_barrier();
   return Bin{sm.res[slot], sm.res[slot + 1], sm.res[slot + 2]};
 }
 
@@ -488,7 +497,7 @@ __device__ Bin block_find_top(const uint32_t* h, int need, Sm& sm) {
     sm.res[4] = a;
     sm.res[5] = cnt;
   }
-  __syncthreads();
+  lds_barrier();
   return Bin{sm.res[3], sm.res[4], sm.res[5]};
 }
 
@@ -534,7 +543,7 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
   }
   for (int i = t; i < 4096; i += NT) sm.hist[i] = 0u;
   if (t == 0) sm.cnt[0] = 0;
-  __syncthreads();
+  lds_barrier();
   kmin = wave_min_u(lane < NT / 64 ? sm.ured[lane] : 0xFFFFFFFFu);
   kmax = wave_max_u(lane < NT / 64 ? sm.ured[16 + lane] : 0u);
   const float lo = key_value(kmin);
@@ -548,7 +557,7 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
 #pragma unroll
     for (int i = 0; i < R; ++i)
       if (bk[i] >= 0) atomicAdd(&sm.hist[bk[i]], 1u);
-    __syncthreads();
+    lds_barrier();
     const Bin B = block_find_top(sm.hist, need, sm);
     if (B.bin >= 0 && B.count <= kPairMax) {
       // gather the bucket's keys: one LDS atomic per wave
@@ -569,7 +578,7 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       const int pc = min(B.count, kPairMax);
       const int need_b = need - B.above;
       const int x = t >> 2, part = t & 3;
@@ -592,7 +601,7 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
         sm.res[1] = need_b - gt;
         sm.res[2] = ge - gt;
       }
-      __syncthreads();
+      lds_barrier();
       return Thresh{(uint32_t)sm.res[0], sm.res[1], sm.res[2]};
     }
   }
@@ -600,24 +609,24 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
   uint32_t* h1 = sm.hist;
   uint32_t* h2 = sm.hist + 4096;
   uint32_t* h3 = sm.hist + 5120;
-  __syncthreads();
+  lds_barrier();
   for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < R; ++i)
     if (i < nv) atomicAdd(&h1[key[i] >> 20], 1u);
-  __syncthreads();
+  lds_barrier();
   const Bin a = find_publish<4096>(h1, need, sm, 0);
 #pragma unroll
   for (int i = 0; i < R; ++i)
     if (i < nv && (int)(key[i] >> 20) == a.bin) atomicAdd(&h2[(key[i] >> 10) & 1023u], 1u);
-  __syncthreads();
+  lds_barrier();
   const Bin bb = find_publish<1024>(h2, need - a.above, sm, 3);
   const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
 #pragma unroll
   for (int i = 0; i < R; ++i)
     if (i < nv && (key[i] >> 10) == pre) atomicAdd(&h3[key[i] & 1023u], 1u);
-  __syncthreads();
+  lds_barrier();
   const Bin cc = find_publish<1024>(h3, need - a.above - bb.above, sm, 6);
   return Thresh{(pre << 10) | (uint32_t)cc.bin, need - a.above - bb.above - cc.above, cc.count};
 }
@@ -764,7 +773,7 @@ __device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) 
     sm.cnt[0] = 0;
     sm.cnt[1] = 0;
   }
-  __syncthreads();
+  lds_barrier();
 
   // --- one pass over the list: lanes hold 4 consecutive entries; the bitmap
   //     words of a wave's 256 entries are built from ballots, and bracket
@@ -831,10 +840,10 @@ __device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) 
     }
   }
   if (lane == 0) atomicAdd(&sm.cnt[1], above);
-  __syncthreads();
+  lds_barrier();
   const int ncand = sm.cnt[0];
   const int need = K - sm.cnt[1];
-  __syncthreads();  // every thread has read the counters before they are reused
+  lds_barrier();  // every thread has read the counters before they are reused
 
   if (need >= 1 && need <= ncand && ncand <= kCand) {
     constexpr int RC = kCand / NT;
@@ -861,22 +870,22 @@ __device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) 
   } else {
     // exact radix over the whole list
     for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
-    __syncthreads();
+    lds_barrier();
     const Bin a = find_publish<4096>(h1, K, sm, 0);
     for (int e = t; e < n; e += NT) {
       const uint32_t key = order_key(c.sc[e]);
       if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
     const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
     for (int e = t; e < n; e += NT) {
       const uint32_t key = order_key(c.sc[e]);
       if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
     const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
     const int need_eq = K - a.above - bb.above - cc.above;
@@ -895,7 +904,7 @@ __device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) 
       run += tot;
     }
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
@@ -959,22 +968,22 @@ __device__ void select_classified(const Geometry& g, const Workspace& ws, int p,
     uint32_t* h2 = sm.hist + 4096;
     uint32_t* h3 = sm.hist + 5120;
     for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
-    __syncthreads();
+    lds_barrier();
     for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
-    __syncthreads();
+    lds_barrier();
     const Bin a = find_publish<4096>(h1, K, sm, 0);
     for (int e = t; e < n; e += NT) {
       const uint32_t key = order_key(c.sc[e]);
       if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
     const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
     for (int e = t; e < n; e += NT) {
       const uint32_t key = order_key(c.sc[e]);
       if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
     }
-    __syncthreads();
+    lds_barrier();
     const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
     const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
     const int need_eq = K - a.above - bb.above - cc.above;
@@ -993,7 +1002,7 @@ __device__ void select_classified(const Geometry& g, const Workspace& ws, int p,
       run += tot;
     }
   }
-  __syncthreads();
+  lds_barrier();
   emit_bitmap(g, c, sm);
 }
 
@@ -1039,7 +1048,7 @@ __device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kv
   }
   const int n = min(total, g.n_cap);
   if (t == 0) ws.pool_len[p] = n;
-  __syncthreads();
+  lds_barrier();
   int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
   uint32_t* pr = ws.pool_row + (size_t)p * g.n_cap;
   for (int o0 = 8 * t; o0 < n; o0 += 8 * NT) {
@@ -1092,7 +1101,7 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
   if (threadIdx.x == 0) ws.ticket_attn[p] = 0u;
   if (!POOL) {
     load_bt(g, b, L, sm.bt);
-    __syncthreads();
+    lds_barrier();
   }
   SelList c;
   c.sc = ws.scores + (size_t)p * g.n_cap;
@@ -1120,7 +1129,7 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
     select_large(g, c, sm);
   }
   if (!POOL) {
-    __syncthreads();
+    lds_barrier();
     build_pool(g, ws, p, kvh, L, sm);
   }
 }
@@ -1134,7 +1143,7 @@ __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws
   const int32_t* a = anchor + (size_t)p * g.kappa;
   load_bt(g, b, L, sm.bt);
   for (int k = threadIdx.x; k < g.kappa; k += NT) sm.apos[k] = a[k];
-  __syncthreads();
+  lds_barrier();
   build_pool(g, ws, p, kvh, L, sm);
 }
 
@@ -1201,7 +1210,7 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
     res[1] = a;
     res[2] = cnt;
   }
-  __syncthreads();
+  lds_barrier();
   const int bstar = res[0];
   if (w == 0 && t == 0) {
     ws.sel_meta[4 * p] = bstar;
@@ -1419,7 +1428,7 @@ __device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int 
       pv[k][x] = ld_dev(pob + (size_t)min(x, splits - 1) * G * kHeadDim + o);
   }
   for (int i = t; i < 2 * G * splits; i += T) mls[i] = ld_dev(pml + i);
-  __syncthreads();
+  lds_barrier();
   for (int i = wave; i < G; i += T / 64) {
     float M = -INFINITY;
     for (int x = lane; x < splits; x += 64) M = fmaxf(M, mls[(x * G + i) * 2]);
@@ -1434,7 +1443,7 @@ __device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int 
     ls = wave_sum(ls);
     if (lane == 0) lsum[i] = ls;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int k = 0; k < NO; ++k) {
     const int o = t + T * k;
@@ -1509,7 +1518,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   finish_split<G, NW, kAttnThreads>(g, ws, p, s, splits, b, kvh, wo, wml, &last, out);
 }
 
@@ -1571,7 +1580,7 @@ __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p,
   }
   if (layer_idx)
     for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
-  __syncthreads();
+  lds_barrier();
   return total;
 }
 
@@ -1605,7 +1614,7 @@ __device__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_
   }
   if (layer_idx)
     for (int o2 = max(total, r0) + t; o2 < rend; o2 += NT) layer_idx[(size_t)p * K + o2] = -1;
-  __syncthreads();
+  lds_barrier();
   return total;
 }
 
@@ -1676,7 +1685,7 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out);
 }
 
