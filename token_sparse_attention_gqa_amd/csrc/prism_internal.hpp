@@ -13,7 +13,7 @@ constexpr int kPageSize = 64;         // tokens per page
 constexpr int kSelThreads = 1024;     // threads of a selection workgroup
 constexpr int kScoreThreads = 256;    // threads of a relevance workgroup
 constexpr int kAnchorEntries = 1024;  // cached tokens scored by one anchor-layer workgroup
-constexpr int kPoolEntries = 512;     // pool entries scored by one refined-layer workgroup
+constexpr int kPoolEntries = 256;     // pool entries scored by one refined-layer workgroup
 constexpr int kAttnSplit = 64;        // selected tokens attended by one workgroup
 constexpr int kAttnThreads = 256;
 constexpr int kMaxKappa = 8192;
