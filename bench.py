@@ -74,9 +74,9 @@ def launches_per_step(wl):
     na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     nr = wl.num_layers - na
     L = int(synth.paging(wl).seq_lens.max())
-    # refined layers with G <= 8 select inside the attention kernel
+    # with G <= 8 every layer selects inside its attention kernel
     return {"anchor_score": na, "refine_score": nr,
-            "select": na + (nr if wl.group > 8 else 0), "attention": wl.num_layers,
+            "select": wl.num_layers if wl.group > 8 else 0, "attention": wl.num_layers,
             "classify": na if (L > 16384 and L > wl.kappa) else 0}
 
 

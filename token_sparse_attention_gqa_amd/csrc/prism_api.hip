@@ -220,12 +220,10 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  if (layer % params->anchor_stride == 0) {
-    PRISM_TRY(run_anchor(g, w, q, anchor_idx, layer_idx_out, s));
-    return hip_check(
-        prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params), out, s),
-        "attention launch");
-  }
+  if (layer % params->anchor_stride == 0)
+    return hip_check(prism::launch_anchor_attend(g, w, q, resolve_scale(params), anchor_idx,
+                                                 layer_idx_out, out, s),
+                     "anchor layer launch");
   return hip_check(
       prism::launch_refine_attend(g, w, q, resolve_scale(params), layer_idx_out, out, s),
       "refined layer launch");

@@ -47,12 +47,13 @@ struct Geometry {
 // row at element offset r * head_dim of a layer's page array.
 struct Workspace {
   uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram; followed by
-  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered (zeroed together with ghist)
+  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered, and
+  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernels (all three zeroed
+                          //     together at the start of an anchor layer)
   int32_t* sel_meta;      // [P][4] threshold bin, entries above it, entries in it
   uint32_t* cand_key;     // [P][kMaxCand] order keys of the threshold-bin entries
   int32_t* cand_idx;      // [P][kMaxCand] their list indices
   uint32_t* gbits;        // [P][n_cap / 32] marks of the entries above the threshold bin
-  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernel
   float* scores;          // [P][n_cap] relevance in list order
   int32_t* pool_pos;      // [P][n_cap] refinement pool: positions, ascending
   uint32_t* pool_row;     // [P][n_cap] refinement pool: row ids
@@ -93,6 +94,11 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
 // into out, and the selection's row ids.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          hipStream_t s);
+// Anchor layer of a decode step: scoring, selection, the refinement pool and
+// SparseAttn.  anchor_idx receives the set (and layer_idx, if not null).
+hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, int32_t* anchor_idx, int32_t* layer_idx, float* out,
+                                hipStream_t s);
 // Refined layer of a decode step: pool scoring, then selection and SparseAttn
 // (pools of at most 8192 entries are selected inside the attention kernel).
 // layer_idx (nullable) receives the layer's set.

@@ -37,7 +37,8 @@ constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the lis
 constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the pool build
 constexpr int kClsThreads = 256;
 constexpr int kClsEntries = 8192;         // anchor-list entries classified by one workgroup
-constexpr int kFusedSplit = 128;          // selected tokens attended by one fused refined workgroup
+constexpr int kFusedSplit = 128;          // selected tokens attended by one fused workgroup
+constexpr int kFusedAnchorLen = 6144 * 32;  // contexts whose nonzero mark words fit sm.hist
 static_assert(kMaxCand <= kCand, "candidates of the threshold bin fit the LDS candidate buffer");
 static_assert(kMaxKappa <= 2 * kCand, "pool-build run offsets fit the LDS candidate buffer");
 
@@ -917,8 +918,9 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
 // entries (the candidates) are listed with their keys.  The candidates are
 // ranked here; if the bin held more than kMaxCand of them, an exact radix over
 // the whole list runs instead.
-__device__ void select_classified(const Geometry& g, const Workspace& ws, int p, const SelList& c,
-                                  SelectSmem& sm) {
+template <typename Sm>
+__device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, const SelList& c,
+                                 Sm& sm) {
   const int t = threadIdx.x, lane = t & 63;
   const int n = c.n, K = c.K;
   const int words = (n + 31) >> 5;
@@ -1003,6 +1005,11 @@ __device__ void select_classified(const Geometry& g, const Workspace& ws, int p,
     }
   }
   lds_barrier();
+}
+
+__device__ void select_classified(const Geometry& g, const Workspace& ws, int p, const SelList& c,
+                                  SelectSmem& sm) {
+  classified_marks(g, ws, p, c, sm);
   emit_bitmap(g, c, sm);
 }
 
@@ -1690,6 +1697,235 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 }
 
 // ---------------------------------------------------------------------------
+// Anchor layer of a decode step: the selection, the refinement pool and
+// SparseAttn in one kernel (after scoring and, for contexts longer than
+// kSmall, classification).  Every split's workgroup rebuilds the selection as
+// a bitmap over the cache (same inputs, same set), takes the marked entries'
+// ranks, predecessors and run offsets from block scans, writes its rank slice
+// of the anchor set and of the pool, and attends that slice (16 tokens per
+// wave); the last split to finish merges all splits.
+// ---------------------------------------------------------------------------
+template <int G>
+struct AnchorSmem {
+  int32_t bt[kMaxPages];
+  uint32_t bitmap[kMaxSeqLen / 32];
+  uint32_t cbuf[2 * kCand];
+  uint32_t hist[4096 + 1024 + 1024];
+  uint32_t pair[kPairMax];
+  uint32_t ured[32];
+  int tmp[NT / 64 + 1];
+  int res[9];
+  int cnt[2];
+  uint32_t srow[kFusedSplit];
+  int32_t spos[kFusedSplit];  // the split's anchors: positions and pool-run starts
+  int32_t sst[kFusedSplit];
+  float wo[kFusedSplit / 16][G][kHeadDim];
+  float wml[kFusedSplit / 16][G][2];
+  float pw[kFusedSplit / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
+  int last;
+};
+
+// Marks of a list of at most kSmall entries from the keys in registers.
+template <int R, typename Sm>
+__device__ void small_marks(const float* sc, int n, int K, Sm& sm) {
+  const int t = threadIdx.x;
+  const int words = (n + 31) >> 5;
+  for (int i = t; i < words; i += NT) sm.bitmap[i] = 0u;
+  const int e0 = R * t;
+  const int nv = clampi(n - e0, 0, R);
+  uint32_t key[R];
+  load_run<R>(sc, e0 < n ? e0 : 0, key);
+#pragma unroll
+  for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+  const uint32_t take = top_k_mask<R>(key, nv, n, K, sm);  // its barriers order the zeroing
+  if (take) atomicOr(&sm.bitmap[e0 >> 5], take << (e0 & 31));
+  lds_barrier();
+}
+
+template <int G>
+__global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace ws,
+                                                         const uint16_t* __restrict__ q,
+                                                         float scale, float* __restrict__ out,
+                                                         int32_t* __restrict__ anchor_idx,
+                                                         int32_t* __restrict__ layer_idx) {
+  constexpr int NW = kFusedSplit / 16;
+  static_assert(3 * (kMaxKappa / kFusedSplit) + 1 <= NW * kHeadDim, "merge tables fit");
+  __shared__ AnchorSmem<G> sm;
+  const int K = g.kappa;
+  const int splits = (K + kFusedSplit - 1) / kFusedSplit;
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane & 15, g4 = lane >> 4;
+  const int n = seq_len_of(g, b);
+  const int r0 = s * kFusedSplit;
+  load_bt(g, b, n, sm.bt);
+
+  // the selection as marks over the list
+  if (n <= K) {
+    for (int i = t; i < ((n + 31) >> 5); i += NT)
+      sm.bitmap[i] = (32 * i + 32 <= n) ? 0xFFFFFFFFu : ((1u << (n & 31)) - 1u);
+    lds_barrier();
+  } else if (n <= kSmall / 2) {
+    small_marks<kSmallPer / 2>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
+  } else if (n <= kSmall) {
+    small_marks<kSmallPer>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
+  } else {
+    SelList c;
+    c.sc = ws.scores + (size_t)p * g.n_cap;
+    c.plist = nullptr;
+    c.prow = nullptr;
+    c.n = n;
+    c.K = K;
+    c.b = b;
+    c.kvh = kvh;
+    c.o1 = c.o2 = nullptr;
+    c.srow = nullptr;
+    classified_marks(g, ws, p, c, sm);
+  }
+
+  // --- the anchor set from the marks ----------------------------------------
+  // 1. the nonzero words in order, each with the rank of its first mark, as a
+  //    list in sm.hist (word index << 14 | rank, ranks clamped to 16383)
+  const int words = (n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0, nz = 0;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    cnt += __popc(m);
+    nz += m ? 1 : 0;
+  }
+  int total, nz_total;
+  int rank = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  int slot = block_excl_scan<NT>(nz, sm.tmp, &nz_total);
+  uint32_t* const wl = sm.hist;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    if (m) {
+      wl[slot++] = ((uint32_t)i << 14) | (uint32_t)min(rank, 16383);
+      rank += __popc(m);
+    }
+  }
+  lds_barrier();
+  // 2. one lane per bit of two listed words at a time: the mark's rank,
+  //    position and predecessor give its pool run; run lengths go to lens[rank]
+  //    and the slice's anchors (position, run start) to spos / sst
+  const int kt = min(total, K);  // anchors
+  const int rend = min(K, r0 + kFusedSplit);
+  int32_t* const lens = reinterpret_cast<int32_t*>(sm.cbuf);  // [K]: run lengths, then offsets
+  const int win = min(g.window, n);
+  for (int x = 2 * wave; x < nz_total; x += 2 * (NT / 64)) {
+    const int idx = x + (lane >> 5), bit = lane & 31;
+    if (idx < nz_total) {
+      const uint32_t e = wl[idx];
+      const int wi = (int)(e >> 14), base = (int)(e & 16383u);
+      const uint32_t m = sm.bitmap[wi];
+      if ((m >> bit) & 1u) {
+        const uint32_t below = m & ((1u << bit) - 1u);
+        const int r = base + __popc(below);
+        int pv = -1;
+        if (below) {
+          pv = wi * 32 + 31 - __clz(below);
+        } else if (idx > 0) {
+          const int wp = (int)(wl[idx - 1] >> 14);
+          pv = wp * 32 + 31 - __clz(sm.bitmap[wp]);
+        }
+        const int a = wi * 32 + bit;
+        const int lo = max(a - win, 0), hi = min(a + win, n - 1);
+        const int phi = pv >= 0 ? min(pv + win, n - 1) : -1;
+        const int st = max(lo, phi + 1);
+        if (r < kt) lens[r] = max(0, hi - st + 1);
+        if (r >= r0 && r < rend) {
+          sm.spos[r - r0] = a;
+          sm.sst[r - r0] = st;
+        }
+      }
+    }
+  }
+  lds_barrier();
+  // 3. run offsets in rank order
+  const int per = (K + NT - 1) / NT;
+  const int k0 = min(kt, t * per), k1 = min(kt, k0 + per);
+  int sum = 0;
+  for (int k = k0; k < k1; ++k) sum += lens[k];
+  int pool_n;
+  int off = block_excl_scan<NT>(sum, sm.tmp, &pool_n);
+  for (int k = k0; k < k1; ++k) {
+    const int l = lens[k];
+    lens[k] = off;
+    off += l;
+  }
+  lds_barrier();
+  // 4. this split's ranks: row ids for the attention below, the anchor set
+  for (int k = t; k < rend - r0; k += NT) {
+    const int r = r0 + k;
+    int a = -1;
+    if (r < kt) {
+      a = sm.spos[k];
+      sm.srow[k] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
+    }
+    if (anchor_idx) anchor_idx[(size_t)p * K + r] = a;
+    if (layer_idx) layer_idx[(size_t)p * K + r] = a;
+  }
+  // 5. this split's part of the pool: 8 consecutive entries per thread, the run
+  //    of the first found by binary search over the slice's offsets
+  int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
+  uint32_t* prw = ws.pool_row + (size_t)p * g.n_cap;
+  if (r0 < kt) {
+    const int re = min(rend, kt);
+    const int ob = lens[r0];
+    const int oe = min(re < kt ? lens[re] : pool_n, g.n_cap);
+    for (int o = ob + 8 * t; o < oe; o += 8 * NT) {
+      int lo = r0, hi = re - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (lens[mid] <= o) lo = mid;
+        else hi = mid - 1;
+      }
+      int k = lo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int oi = o + i;
+        if (oi < oe) {
+          while (k + 1 < re && lens[k + 1] <= oi) ++k;
+          const int ps = sm.sst[k - r0] + (oi - lens[k]);
+          pp[oi] = ps;
+          prw[oi] = row_id_of_page(g, sm.bt[ps >> 6], kvh, ps);
+        }
+      }
+    }
+  }
+  if (s == 0 && t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
+  lds_barrier();
+
+  const int myr = r0 + wave * 16 + j;
+  bool valid = wave < NW && myr < min(total, K);
+  uint32_t row = valid ? sm.srow[wave * 16 + j] : 0u;
+  if (wave < NW) {  // uniform over the wave
+    float m[4], l[4], o0v[G], o1v[G];
+    wave_attend<G>(g, q, b, kvh, row, valid, scale, sm.pw[wave], m, l, o0v, o1v);
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      sm.wo[wave][i][2 * lane] = o0v[i];
+      sm.wo[wave][i][2 * lane + 1] = o1v[i];
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * g4 + r < G) {
+          sm.wml[wave][4 * g4 + r][0] = m[r];
+          sm.wml[wave][4 * g4 + r][1] = l[r];
+        }
+      }
+    }
+  }
+  lds_barrier();
+  finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 struct ProfileRing {
@@ -1773,12 +2009,11 @@ int64_t profile_launches(int kind) {
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
-  o += align256(P * (kCoarseBins + 1) * 4);                      // ghist, cand_cnt
+  o += align256(P * (kCoarseBins + 2) * 4);                      // ghist, cand_cnt, ticket_attn
   o += align256(P * 4 * 4);                                      // sel_meta
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_key
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx
   o += align256(P * (size_t)(g.n_cap / 32) * 4);                 // gbits
-  o += align256(P * 4);                                          // ticket_attn
   o += align256(P * (size_t)g.n_cap * 4);                        // scores
   o += align256(P * (size_t)g.n_cap * 4);                        // pool_pos
   o += align256(P * (size_t)g.n_cap * 4);                        // pool_row
@@ -1796,7 +2031,8 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   Workspace w;
   w.ghist = reinterpret_cast<uint32_t*>(c);
   w.cand_cnt = w.ghist + P * kCoarseBins;
-  c += align256(P * (kCoarseBins + 1) * 4);
+  w.ticket_attn = w.cand_cnt + P;
+  c += align256(P * (kCoarseBins + 2) * 4);
   w.sel_meta = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4 * 4);
   w.cand_key = reinterpret_cast<uint32_t*>(c);
@@ -1805,8 +2041,6 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   c += align256(P * (size_t)kMaxCand * 4);
   w.gbits = reinterpret_cast<uint32_t*>(c);
   c += align256(P * (size_t)(g.n_cap / 32) * 4);
-  w.ticket_attn = reinterpret_cast<uint32_t*>(c);
-  c += align256(P * 4);
   w.scores = reinterpret_cast<float*>(c);
   c += align256(P * (size_t)g.n_cap * 4);
   w.pool_pos = reinterpret_cast<int32_t*>(c);
@@ -1830,7 +2064,7 @@ Workspace carve_workspace(void* base, const Geometry& g) {
 // over many workgroups, then select per problem (and build the pool).
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 1);
+  const int nz = g.problems() * (kCoarseBins + 2);
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -1845,6 +2079,48 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
     if (e != hipSuccess) return e;
   }
   launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
+  return hipGetLastError();
+}
+
+template <int G>
+void launch_anchor_attn_g(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
+                          float* out, int32_t* anchor_idx, int32_t* layer_idx, hipStream_t s) {
+  const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
+  launch(kAttention, anchor_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
+         scale, out, anchor_idx, layer_idx);
+}
+
+hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, int32_t* anchor_idx, int32_t* layer_idx, float* out,
+                                hipStream_t s) {
+  // the fused kernel's LDS holds up to 8 heads and lists up to kFusedAnchorLen
+  // nonzero mark words; otherwise select, then attend
+  if (g.group > 8 || g.max_seq_len > kFusedAnchorLen) {
+    hipError_t e = launch_anchor(g, w, q, anchor_idx, layer_idx, s);
+    if (e != hipSuccess) return e;
+    return launch_attention(g, w, q, nullptr, true, scale, out, s);
+  }
+  const int nz = g.problems() * (kCoarseBins + 2);  // histogram, candidate and arrival counters
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
+                     w.ghist, nz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
+    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (g.group) {
+    case 1: launch_anchor_attn_g<1>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
+    case 2: launch_anchor_attn_g<2>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
+    case 4: launch_anchor_attn_g<4>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
+    case 8: launch_anchor_attn_g<8>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
