@@ -290,6 +290,20 @@ def test_decode_chain_groups_mixed_pools(G):
     _run_chain(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"chain-g{G}")
 
 
+@pytest.mark.parametrize("fill", [0x00, 0xAB, 0xFF])
+def test_decode_from_leftover_workspace(fill):
+    """A workspace holding arbitrary bytes (as after other use): the counters in
+    it are not trusted, results match the oracle, and a second decode step on
+    the same workspace matches again."""
+    wl = synth.scaled(synth.LLAMA_128K_PLANTED, name="leftover-ws", wid=190, context=40960,
+                      kappa=512, n_clusters=16, num_layers=3, anchor_stride=2)
+    st = Setup(wl, range(3))
+    st.ws.fill_(fill)
+    probs = [(0, g) for g in range(wl.num_kv_heads)]
+    for rep in range(2):
+        _run_chain(st, range(3), probs, f"leftover-ws {fill:#x} step {rep}")
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []

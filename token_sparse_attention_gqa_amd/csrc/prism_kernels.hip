@@ -292,6 +292,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
+  if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = lane & 15, g4 = lane >> 4;
@@ -913,6 +914,14 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
   emit_bitmap(g, c, sm);
 }
 
+// Leaves the problem's coarse histogram and candidate counter zero for the
+// next anchor layer (called by one workgroup once nothing reads them).
+__device__ void reset_selection_counters(const Workspace& ws, int p) {
+  uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
+  for (int i = threadIdx.x; i < kCoarseBins; i += blockDim.x) gh[i] = 0u;
+  if (threadIdx.x == 0) ws.cand_cnt[p] = 0u;
+}
+
 // Anchor lists longer than kSmall, after the classify kernel: the entries
 // above the threshold bin are marked in the workspace bitmap, and the bin's own
 // entries (the candidates) are listed with their keys.  The candidates are
@@ -925,13 +934,23 @@ __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, 
   const int n = c.n, K = c.K;
   const int words = (n + 31) >> 5;
   const uint32_t* gb = ws.gbits + (size_t)p * (g.n_cap >> 5);
-  for (int i = t; i < words; i += NT) sm.bitmap[i] = gb[i];
+  int marks = 0;
+  for (int i = t; i < words; i += NT) {
+    const uint32_t m = gb[i];
+    sm.bitmap[i] = m;
+    marks += __popc(m);
+  }
+  block_excl_scan<NT>(marks, sm.tmp, &marks);
   const int above = ws.sel_meta[4 * p + 1];
+  const int in_bin = ws.sel_meta[4 * p + 2];
   const int ncand = (int)ws.cand_cnt[p];
   const int need = K - above;
   uint32_t* const ckey = sm.cbuf;
   int32_t* const cidx = reinterpret_cast<int32_t*>(sm.cbuf + kCand);
-  if (need >= 1 && need <= ncand && ncand <= kMaxCand) {
+  // the classify pass must agree with itself: as many marks as entries above the
+  // threshold bin and as many candidates as entries in it (a histogram left
+  // over from an earlier call, e.g. in a fresh workspace, fails this)
+  if (marks == above && ncand == in_bin && need >= 1 && need <= ncand && ncand <= kMaxCand) {
     constexpr int RC = kMaxCand / NT;
     uint32_t ck[RC];
     int32_t ci[RC];
@@ -1138,6 +1157,7 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
   if (!POOL) {
     lds_barrier();
     build_pool(g, ws, p, kvh, L, sm);
+    reset_selection_counters(ws, p);
   }
 }
 
@@ -1259,9 +1279,11 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
   const int inc = wave_incl_scan(cnt);
   const int wtot = (int)lane63((uint32_t)inc);
   if (wtot) {
-    int off = 0;
-    if (lane == 0) off = (int)atomicAdd(&ws.cand_cnt[p], (uint32_t)wtot);
-    int slot = __builtin_amdgcn_readfirstlane(off) + inc - cnt;
+    uint32_t off = 0u;
+    if (lane == 0) off = atomicAdd(&ws.cand_cnt[p], (uint32_t)wtot);
+    // unsigned: a counter left over in the workspace gives slots past the end
+    // (nothing is written; the selection's consistency check rejects the pass)
+    uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)off) + (uint32_t)(inc - cnt);
     uint32_t* ck = ws.cand_key + (size_t)p * kMaxCand;
     int32_t* ci = ws.cand_idx + (size_t)p * kMaxCand;
 #pragma unroll
@@ -1269,7 +1291,7 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         if (cand & (1u << (4 * u + q4))) {
-          if (slot < kMaxCand) {
+          if (slot < (uint32_t)kMaxCand) {
             ck[slot] = order_key(__uint_as_float(raw[u][q4]));
             ci[slot] = base + u * 4 * kClsThreads + 4 * t + q4;
           }
@@ -1388,7 +1410,7 @@ __device__ __forceinline__ void wave_attend(const Geometry& g, const uint16_t* q
 // ..., the maximum over splits (one split per lane), every split's weight
 // exp(m - M) and the weighted sum of the splits' sums.
 template <int G, int NW, int T>
-__device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int s, int splits,
+__device__ bool finish_split(const Geometry& g, const Workspace& ws, int p, int s, int splits,
                              int b, int kvh, float (*wo)[G][kHeadDim], float (*wml)[G][2],
                              int* last, float* out) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -1416,7 +1438,7 @@ __device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int 
     }
   }
 
-  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, last)) return;
+  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, last)) return false;
 
   constexpr int NO = (G * kHeadDim + T - 1) / T;
   const float* pml = ws.part_ml + (size_t)p * splits * G * 2;
@@ -1472,6 +1494,7 @@ __device__ void finish_split(const Geometry& g, const Workspace& ws, int p, int 
     out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = L > 0.f ? a / L : 0.f;
   }
   if (t == 0) ticket_reset(&ws.ticket_attn[p]);
+  return true;
 }
 
 // SparseAttn over a given set (positions in idx) or over the row ids the
@@ -1922,7 +1945,8 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
     }
   }
   lds_barrier();
-  finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out);
+  if (finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out))
+    reset_selection_counters(ws, p);  // every split has read them
 }
 
 // ---------------------------------------------------------------------------
@@ -2100,13 +2124,11 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
     if (e != hipSuccess) return e;
     return launch_attention(g, w, q, nullptr, true, scale, out, s);
   }
-  const int nz = g.problems() * (kCoarseBins + 2);  // histogram, candidate and arrival counters
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
-                     w.ghist, nz);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // The histogram and candidate counter are zero from the previous anchor
+  // layer (the selection checks its own consistency, so a fresh workspace only
+  // takes the exact fallback once); anchor scoring zeroes the arrival counter.
   PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
