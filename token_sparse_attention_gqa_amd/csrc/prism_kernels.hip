@@ -184,6 +184,7 @@ __device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
 constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;             // lane 7 - i of each 8-lane half row
 
 // Inclusive scan of an associative op over the wave (ident: its identity);
 // lane 63 ends with the result over all 64 lanes.
@@ -278,11 +279,35 @@ __device__ Bin wave_find_bin(const uint32_t* h, int need) {
 // Relevance
 // ---------------------------------------------------------------------------
 
+// Sum over each group of 8 lanes (lanes 8k .. 8k + 7); every lane of the group
+// receives the same value.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += __uint_as_float(dpp<kRowHalfMirror, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadXor2, 0xf>(0u, __float_as_uint(v)));
+  v += __uint_as_float(dpp<kQuadXor1, 0xf>(0u, __float_as_uint(v)));
+  return v;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
 // Anchor layer: workgroup w of problem p scores tokens [w * kAnchorEntries, +kAnchorEntries)
 // of the cache; each wave takes 256 consecutive tokens = 4 whole pages.  The
 // workgroup also counts its scores by coarse bin (top 12 bits of the order
 // key) in LDS and adds the counts to the problem's histogram in the workspace,
 // which the selection uses to find the bin holding the kappa-th score.
+//
+// Groups of up to 8 query heads score on the VALU: 8 lanes share a key row,
+// each lane taking the 16-byte chunks `part` and `part + 8`, so one load
+// instruction of the wave reads 8 rows x 128 contiguous bytes (whole cache
+// lines; operand fragments for the matrix cores would read 16 rows x 64 bytes
+// per instruction, which streams from HBM measurably slower).  Each lane forms
+// bf16 pair products with the group's query chunks (v_dot2), the 8 lanes of a
+// row sum their partials, and the maximum over the heads is the relevance.
+// Larger groups use the matrix cores (four MFMAs per 16 tokens).
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g, Workspace ws,
                                                                      const uint16_t* __restrict__ q,
@@ -295,13 +320,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
   if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15, g4 = lane >> 4;
   const int wbase = w * kAnchorEntries + wave * 256;
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
   lds_barrier();
   if (wbase < n) {
-    u32x4 qf[4];
-    load_q_frag<G>(q, g, b, kvh, lane, qf);
     float* sc = ws.scores + (size_t)p * g.n_cap;
     const int last_page = (n - 1) >> 6;
     const size_t head = (size_t)kvh * kPageSize * kHeadDim;
@@ -309,38 +331,96 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       page_off[r] = (size_t)phys_page(g, b, min((wbase >> 6) + r, last_page)) * g.page_stride + head;
-    // One page (4 tiles of 16 tokens) per step, double-buffered: the next page's
-    // 16 loads are issued before the current page's MFMAs (the scheduling
-    // barriers keep the compiler from interleaving them back into a few loads
-    // in flight).  Addresses stay offsets from the kernel-argument base so the
-    // loads remain global loads.
-    u32x4 kb[2][4][4];
+    if constexpr (G <= 8) {
+      const int part = lane & 7, rs = lane >> 3;
+      uint32_t qv[G][8];  // head h: chunk `part` in [0, 4), chunk `part + 8` in [4, 8)
 #pragma unroll
-    for (int r = 0; r < 5; ++r) {
-      if (r < 4) {
+      for (int h = 0; h < G; ++h) {
+        const u32x4* qrow =
+            reinterpret_cast<const u32x4*>(q + ((size_t)b * g.hq + kvh * G + h) * kHeadDim);
+        const u32x4 x0 = qrow[part], x1 = qrow[part + 8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const u32x4* row = reinterpret_cast<const u32x4*>(
-              g.k_pages + page_off[r] + (size_t)((u * 16 + j) * kHeadDim));
-#pragma unroll
-          for (int s4 = 0; s4 < 4; ++s4)
-            kb[r & 1][u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+        for (int i = 0; i < 4; ++i) {
+          qv[h][i] = x0[i];
+          qv[h][4 + i] = x1[i];
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (r > 0) {
-        const int rp = r - 1;
+      // One page (8 groups of 8 rows) per step, double-buffered: the next
+      // page's 16 loads are issued before the current page's arithmetic.
+      u32x4 kb[2][8][2];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float m = group_max<G>(qk_tile(qf, kb[rp & 1][u]), g4);
-          const int e = wbase + rp * 64 + u * 16 + j;
-          if (g4 == 0 && e < n) {
-            sc[e] = m;
-            atomicAdd(&lh[order_key(m) >> 20], 1u);
+      for (int r = 0; r < 5; ++r) {
+        if (r < 4) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const u32x4* row = reinterpret_cast<const u32x4*>(
+                g.k_pages + page_off[r] + (size_t)((u * 8 + rs) * kHeadDim));
+            kb[r & 1][u][0] = __builtin_nontemporal_load(row + part);
+            kb[r & 1][u][1] = __builtin_nontemporal_load(row + part + 8);
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
+        if (r > 0) {
+          const int rp = r - 1;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const u32x4 k0 = kb[rp & 1][u][0], k1 = kb[rp & 1][u][1];
+            float m = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              float a = 0.f;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][i], k0[i], a);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][4 + i], k1[i], a);
+              m = fmaxf(m, group8_sum(a));
+            }
+            const int e = wbase + rp * 64 + u * 8 + rs;
+            if (part == 0 && e < n) {
+              sc[e] = m;
+              atomicAdd(&lh[order_key(m) >> 20], 1u);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      const int j = lane & 15, g4 = lane >> 4;
+      u32x4 qf[4];
+      load_q_frag<G>(q, g, b, kvh, lane, qf);
+      // One page (4 tiles of 16 tokens) per step, double-buffered: the next page's
+      // 16 loads are issued before the current page's MFMAs (the scheduling
+      // barriers keep the compiler from interleaving them back into a few loads
+      // in flight).  Addresses stay offsets from the kernel-argument base so the
+      // loads remain global loads.
+      u32x4 kb[2][4][4];
+#pragma unroll
+      for (int r = 0; r < 5; ++r) {
+        if (r < 4) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const u32x4* row = reinterpret_cast<const u32x4*>(
+                g.k_pages + page_off[r] + (size_t)((u * 16 + j) * kHeadDim));
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+              kb[r & 1][u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (r > 0) {
+          const int rp = r - 1;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float m = group_max<G>(qk_tile(qf, kb[rp & 1][u]), g4);
+            const int e = wbase + rp * 64 + u * 16 + j;
+            if (g4 == 0 && e < n) {
+              sc[e] = m;
+              atomicAdd(&lh[order_key(m) >> 20], 1u);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   lds_barrier();
@@ -352,7 +432,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
 }
 
 // Refined layer: workgroup w of problem p scores pool entries
-// [w * kPoolEntries, +kPoolEntries) from the pool's row ids; each wave 8 tiles.
+// [w * kPoolEntries, +kPoolEntries) from the pool's row ids, 64 per wave; the
+// key rows are read and combined as in anchor scoring (VALU for groups of up
+// to 8 heads, 8 lanes per row; matrix cores for larger groups).
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, Workspace ws,
                                                                    const uint16_t* __restrict__ q,
@@ -362,33 +444,77 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
   if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int j = lane & 15, g4 = lane >> 4;
   const int wbase = w * kPoolEntries + wave * (kPoolEntries / 4);
   if (wbase >= n) return;
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  u32x4 qf[4];
-  load_q_frag<G>(q, g, b, kvh, lane, qf);
   const uint32_t* prow = ws.pool_row + (size_t)p * g.n_cap;
   float* sc = ws.scores + (size_t)p * g.n_cap;
   const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
-  constexpr int kTiles = kPoolEntries / 4 / 16;  // 8
-  uint32_t rid[kTiles];
+  if constexpr (G <= 8) {
+    const int part = lane & 7, rs = lane >> 3;
+    constexpr int kGroups = kPoolEntries / 4 / 8;  // 8 groups of 8 rows per wave
+    uint32_t rid[kGroups];
 #pragma unroll
-  for (int u = 0; u < kTiles; ++u) rid[u] = prow[min(wbase + u * 16 + j, n - 1)];
-  u32x4 kf[kTiles][4];
+    for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wbase + u * 8 + rs, n - 1)];
+    uint32_t qv[G][8];
 #pragma unroll
-  for (int u = 0; u < kTiles; ++u) {
-    const u32x4* row =
-        reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+    for (int h = 0; h < G; ++h) {
+      const u32x4* qrow =
+          reinterpret_cast<const u32x4*>(q + ((size_t)b * g.hq + kvh * G + h) * kHeadDim);
+      const u32x4 x0 = qrow[part], x1 = qrow[part + 8];
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) kf[u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
-  }
-  __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 4; ++i) {
+        qv[h][i] = x0[i];
+        qv[h][4 + i] = x1[i];
+      }
+    }
+    u32x4 kb[kGroups][2];
 #pragma unroll
-  for (int u = 0; u < kTiles; ++u) {
-    const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
-    const int e = wbase + u * 16 + j;
-    if (g4 == 0 && e < n) sc[e] = m;
+    for (int u = 0; u < kGroups; ++u) {
+      const u32x4* row =
+          reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+      kb[u][0] = __builtin_nontemporal_load(row + part);
+      kb[u][1] = __builtin_nontemporal_load(row + part + 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][i], kb[u][0][i], a);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][4 + i], kb[u][1][i], a);
+        m = fmaxf(m, group8_sum(a));
+      }
+      const int e = wbase + u * 8 + rs;
+      if (part == 0 && e < n) sc[e] = m;
+    }
+  } else {
+    const int j = lane & 15, g4 = lane >> 4;
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    constexpr int kTiles = kPoolEntries / 4 / 16;
+    uint32_t rid[kTiles];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) rid[u] = prow[min(wbase + u * 16 + j, n - 1)];
+    u32x4 kf[kTiles][4];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const u32x4* row =
+          reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) kf[u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
+      const int e = wbase + u * 16 + j;
+      if (g4 == 0 && e < n) sc[e] = m;
+    }
   }
 }
 
