@@ -295,7 +295,7 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // Anchor layer: workgroup w of problem p scores tokens [w * kAnchorEntries, +kAnchorEntries)
-// of the cache; each wave takes 256 consecutive tokens = 4 whole pages.  The
+// of the cache; each wave takes kAnchorEntries / 4 consecutive tokens (whole pages).  The
 // workgroup also counts its scores by coarse bin (top 12 bits of the order
 // key) in LDS and adds the counts to the problem's histogram in the workspace,
 // which the selection uses to find the bin holding the kappa-th score.
@@ -320,16 +320,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
   if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wbase = w * kAnchorEntries + wave * 256;
+  constexpr int kPages = kAnchorEntries / 4 / kPageSize;  // whole pages per wave
+  const int wbase = w * kAnchorEntries + wave * (kAnchorEntries / 4);
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
   lds_barrier();
   if (wbase < n) {
     float* sc = ws.scores + (size_t)p * g.n_cap;
     const int last_page = (n - 1) >> 6;
     const size_t head = (size_t)kvh * kPageSize * kHeadDim;
-    size_t page_off[4];
+    size_t page_off[kPages];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < kPages; ++r)
       page_off[r] = (size_t)phys_page(g, b, min((wbase >> 6) + r, last_page)) * g.page_stride + head;
     if constexpr (G <= 8) {
       const int part = lane & 7, rs = lane >> 3;
@@ -345,26 +346,27 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
           qv[h][4 + i] = x1[i];
         }
       }
-      // One page (8 groups of 8 rows) per step, double-buffered: the next
-      // page's 16 loads are issued before the current page's arithmetic.
-      u32x4 kb[2][8][2];
+      // Half a page (4 groups of 8 rows) per step, three buffers: the loads of
+      // the next two half pages are in flight during the current one's
+      // arithmetic (the scheduling barriers keep the compiler from moving them).
+      u32x4 kb[3][4][2];
 #pragma unroll
-      for (int r = 0; r < 5; ++r) {
-        if (r < 4) {
+      for (int r = 0; r < 2 * kPages + 2; ++r) {
+        if (r < 2 * kPages) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
+          for (int u = 0; u < 4; ++u) {
             const u32x4* row = reinterpret_cast<const u32x4*>(
-                g.k_pages + page_off[r] + (size_t)((u * 8 + rs) * kHeadDim));
-            kb[r & 1][u][0] = __builtin_nontemporal_load(row + part);
-            kb[r & 1][u][1] = __builtin_nontemporal_load(row + part + 8);
+                g.k_pages + page_off[r >> 1] + (size_t)((((r & 1) * 4 + u) * 8 + rs) * kHeadDim));
+            kb[r % 3][u][0] = __builtin_nontemporal_load(row + part);
+            kb[r % 3][u][1] = __builtin_nontemporal_load(row + part + 8);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (r > 0) {
-          const int rp = r - 1;
+        if (r >= 2) {
+          const int rp = r - 2;
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const u32x4 k0 = kb[rp & 1][u][0], k1 = kb[rp & 1][u][1];
+          for (int u = 0; u < 4; ++u) {
+            const u32x4 k0 = kb[rp % 3][u][0], k1 = kb[rp % 3][u][1];
             float m = -INFINITY;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
               for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][4 + i], k1[i], a);
               m = fmaxf(m, group8_sum(a));
             }
-            const int e = wbase + rp * 64 + u * 8 + rs;
+            const int e = wbase + rp * 32 + u * 8 + rs;
             if (part == 0 && e < n) {
               sc[e] = m;
               atomicAdd(&lh[order_key(m) >> 20], 1u);
@@ -395,8 +397,8 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
       // loads remain global loads.
       u32x4 kb[2][4][4];
 #pragma unroll
-      for (int r = 0; r < 5; ++r) {
-        if (r < 4) {
+      for (int r = 0; r < kPages + 1; ++r) {
+        if (r < kPages) {
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const u32x4* row = reinterpret_cast<const u32x4*>(
