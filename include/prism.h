@@ -187,7 +187,7 @@ typedef enum {
   PRISM_KERNEL_SELECT = 2,       /* top-kappa of every (sequence, KV head) list          */
   PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the set + merge of splits  */
   PRISM_KERNEL_POOL_BUILD = 4,   /* pool of an anchor set given to prism_refine_topk     */
-  PRISM_KERNEL_CLASSIFY = 5,     /* anchor layer, contexts > 8192: marks the entries
+  PRISM_KERNEL_CLASSIFY = 5,     /* anchor layer, contexts > 16384: marks the entries
                                     above the kappa-th score's coarse bin, lists the bin */
   PRISM_KERNEL_KINDS = 6
 } prism_kernel_kind;

@@ -48,8 +48,10 @@ struct Geometry {
 struct Workspace {
   uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram; followed by
   uint32_t* cand_cnt;     // [P] threshold-bin entries gathered, and
-  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernels (all three zeroed
-                          //     together at the start of an anchor layer)
+  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernels.  The first two
+                          //     are left at zero by their last reader and checked by the
+                          //     selection; the counter is zeroed by the scoring kernel
+                          //     that precedes each attention launch
   int32_t* sel_meta;      // [P][4] threshold bin, entries above it, entries in it
   uint32_t* cand_key;     // [P][kMaxCand] order keys of the threshold-bin entries
   int32_t* cand_idx;      // [P][kMaxCand] their list indices
