@@ -77,7 +77,7 @@ def launches_per_step(wl):
     # with G <= 8 every layer selects inside its attention kernel
     return {"anchor_score": na, "refine_score": nr,
             "select": wl.num_layers if wl.group > 8 else 0, "attention": wl.num_layers,
-            "classify": na if (L > 16384 and L > wl.kappa) else 0}
+            "classify": na if (L > 16384 and L > wl.kappa) else 0, "merge": wl.num_layers}
 
 
 def kernel_source_hash():

@@ -185,11 +185,13 @@ typedef enum {
   PRISM_KERNEL_ANCHOR_SCORE = 0, /* anchor layer: relevance of every cached token        */
   PRISM_KERNEL_REFINE_SCORE = 1, /* refined layer: relevance of the pool                 */
   PRISM_KERNEL_SELECT = 2,       /* top-kappa of every (sequence, KV head) list          */
-  PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the set + merge of splits  */
+  PRISM_KERNEL_ATTENTION = 3,    /* SparseAttn over splits of the set (and, for a layer,
+                                    the selection that precedes it)                      */
   PRISM_KERNEL_POOL_BUILD = 4,   /* pool of an anchor set given to prism_refine_topk     */
   PRISM_KERNEL_CLASSIFY = 5,     /* anchor layer, contexts > 16384: marks the entries
                                     above the kappa-th score's coarse bin, lists the bin */
-  PRISM_KERNEL_KINDS = 6
+  PRISM_KERNEL_MERGE = 6,        /* merge of the attention splits into out              */
+  PRISM_KERNEL_KINDS = 7
 } prism_kernel_kind;
 
 /*

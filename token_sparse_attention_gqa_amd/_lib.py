@@ -64,7 +64,7 @@ _SIGS = {
 
 # prism_kernel_kind
 KERNEL_KINDS = {"anchor_score": 0, "refine_score": 1, "select": 2, "attention": 3,
-                "pool_build": 4, "classify": 5}
+                "pool_build": 4, "classify": 5, "merge": 6}
 
 _lib = None
 

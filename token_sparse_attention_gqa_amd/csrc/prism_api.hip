@@ -202,7 +202,6 @@ prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_t* q,
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  PRISM_TRY(hip_check(prism::launch_zero_counters(g, w, s), "counter reset launch"));
   return hip_check(prism::launch_attention(g, w, q, idx, false, resolve_scale(params), out, s),
                    "attention launch");
 }

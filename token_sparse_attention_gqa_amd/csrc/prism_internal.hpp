@@ -47,11 +47,8 @@ struct Geometry {
 // row at element offset r * head_dim of a layer's page array.
 struct Workspace {
   uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram; followed by
-  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered, and
-  uint32_t* ticket_attn;  // [P] arrival counters of the attention kernels.  The first two
-                          //     are left at zero by their last reader and checked by the
-                          //     selection; the counter is zeroed by the scoring kernel
-                          //     that precedes each attention launch
+  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered.  Both are left at zero
+                          //     by their last reader and checked by the selection
   int32_t* sel_meta;      // [P][4] threshold bin, entries above it, entries in it
   uint32_t* cand_key;     // [P][kMaxCand] order keys of the threshold-bin entries
   int32_t* cand_idx;      // [P][kMaxCand] their list indices
@@ -74,6 +71,7 @@ enum KernelKind {
   kAttention,
   kPoolBuild,
   kClassify,
+  kMerge,
   kKernelKinds
 };
 
@@ -106,8 +104,6 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
 // layer_idx (nullable) receives the layer's set.
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s);
-// Zeroes the attention arrival counters (before a standalone attention call).
-hipError_t launch_zero_counters(const Geometry& g, const Workspace& w, hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with
 // use_sel_rows, over the row ids the latest selection left in the workspace.
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,

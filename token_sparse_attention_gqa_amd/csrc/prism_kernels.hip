@@ -1,19 +1,24 @@
 // HIP kernels for gfx950 (CDNA4): token-sparse GQA decode attention with
 // proposal-refined cross-layer index sharing ("Prism Attention", arXiv
-// 2610.22985).  Three kernels per layer:
+// 2610.22985).
 //
-//   score_anchor_kernel / score_pool_kernel
-//       relevance (Eq. 9 / Eq. 1) of every cached token at an anchor layer, or
-//       of the refinement pool at a refined layer (Eq. 5), one MFMA per 16
-//       tokens x 32 dimensions;
-//   select_kernel
-//       the exact top-kappa (Eq. 2 / Eq. 6) of each (sequence, KV head) list,
-//       the row ids of the selected tokens, and at an anchor layer the pool
-//       that the following refined layers re-score (the candidate cache that
-//       proposal layers populate in Algorithm 1);
-//   attn_kernel
-//       SparseAttn of Algorithm 1 over one split of the selected set; the last
-//       split of each (sequence, KV head) merges all splits in split order.
+// One decode layer (prism_decode_layer, groups of up to 8 query heads):
+//   anchor layer   score_anchor_kernel  relevance of every cached token (Eq. 9
+//                                       with Eq. 1) and a coarse histogram of
+//                                       the scores;
+//                  classify_kernel      (contexts > kSmall) marks the entries
+//                                       above the bin of the kappa-th score and
+//                                       lists the bin's own entries;
+//                  anchor_attn_kernel   top-kappa (Eq. 2), the refinement pool
+//                                       (the +-w windows of the set), and
+//                                       SparseAttn of Algorithm 1 over one
+//                                       split of the set per workgroup;
+//   refined layer  score_pool_kernel    relevance of the pool's tokens (Eq. 5);
+//                  refine_attn_kernel   top-kappa of the pool (Eq. 6) and
+//                                       SparseAttn over one split;
+//   both           merge_kernel         the splits merged into the output.
+// The single-step entry points and the shapes the fused kernels do not cover
+// use select_kernel, pool_build_kernel and attn_kernel instead.
 #include "prism_internal.hpp"
 
 #include <hip/hip_ext.h>
@@ -89,44 +94,6 @@ __device__ __forceinline__ void map_block(int bid, int P, int W, int* p, int* w)
     *p = bid / W;
     *w = bid % W;
   }
-}
-
-// Attention partials handed from one workgroup to another within a launch are
-// written and read with device-scope accesses (sc1: written through to, and
-// read from, the device coherence point), so no cache-wide L2 writeback or
-// invalidate is needed.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Arrival counter of the workgroups of one problem: zero when the launch
-// starts (zeroed by an earlier kernel of the same call) and reset to zero by
-// the last arrival.  Every wave first waits for its own device-scope stores to
-// complete; one fetch-add per workgroup.  True in every thread of the last one.
-__device__ bool publish_and_arrive(uint32_t* ctr, uint32_t total, int* flag) {
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t old =
-        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = (old + 1u == total) ? 1 : 0;
-  }
-  lds_barrier();
-  return *flag != 0;
-}
-
-__device__ __forceinline__ void ticket_reset(uint32_t* ctr) {
-  __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Orders this workgroup's global stores and L2 atomics before its later
-// cache-bypassing loads (used inside one workgroup only).
-__device__ __forceinline__ void wg_global_sync() {
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
 }
 
 // MFMA A-operand fragment of the group's query heads.  Lane l holds head
@@ -317,7 +284,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
-  if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   constexpr int kPages = kAnchorEntries / 4 / kPageSize;  // whole pages per wave
@@ -443,7 +409,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
                                                                    int wgs) {
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
-  if (w == 0 && threadIdx.x == 0) ws.ticket_attn[p] = 0u;  // for the attention that follows
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wbase = w * kPoolEntries + wave * (kPoolEntries / 4);
@@ -1242,8 +1207,8 @@ __device__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
   for (int i = threadIdx.x; i < np; i += NT) bt[i] = phys_page(g, b, i);
 }
 
-// Top-kappa of one (sequence, KV head) per workgroup; zeroes the problem's
-// attention arrival counter; at an anchor layer also builds the pool.
+// Top-kappa of one (sequence, KV head) per workgroup; at an anchor layer also
+// builds the pool.  Leaves the problem's selection counters at zero.
 template <bool POOL>
 __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
                                                     int32_t* __restrict__ out,
@@ -1252,7 +1217,6 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
   const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
   const int K = g.kappa;
-  if (threadIdx.x == 0) ws.ticket_attn[p] = 0u;
   if (!POOL) {
     load_bt(g, b, L, sm.bt);
     lds_barrier();
@@ -1440,11 +1404,9 @@ __global__ void zero_counters_kernel(uint32_t* c, int n) {
 // scoring (lane j + 16 i4 holds token j for heads 4 i4 .. 4 i4 + 3), softmax
 // statistics over the wave's tokens inside 16-lane rows, the probabilities
 // through the wave's own LDS rows into the V accumulation (two dimensions per
-// lane).  One barrier combines the four waves into the split's statistics
-// (max logit, sum of exponentials) and unnormalised output, which go to the
-// workspace with device-scope stores; the last split to finish merges all
-// splits in split order, loading its share of every split's partials in one
-// batch.
+// lane).  One barrier combines the waves into the split's statistics (max
+// logit, sum of exponentials) and unnormalised output, which go to the
+// workspace; merge_kernel, launched next, merges the splits in split order.
 // ---------------------------------------------------------------------------
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
@@ -1465,7 +1427,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 static_assert(kAttnSplit == 64 && kAttnThreads == 256, "one 16-token tile per wave");
 constexpr int kMergeBatch = 32;  // splits whose partials one merge round loads at once
-static_assert(3 * (kMaxKappa / kAttnSplit) + 1 <= 4 * kHeadDim, "merge tables fit the wave outputs");
+constexpr int kMaxSplits = kMaxKappa / kAttnSplit;  // splits of the smallest split size
 
 template <int G>
 constexpr int prob_stride() { return G < 4 ? 4 : G; }
@@ -1530,21 +1492,15 @@ __device__ __forceinline__ void wave_attend(const Geometry& g, const uint16_t* q
 }
 
 // The block's split of SparseAttn from its NW waves' results (wo, wml, filled
-// and synchronised by the caller): rescaled to a common maximum and stored to
-// the workspace with device-scope stores; then the last split of the problem
-// to arrive merges all splits in split order into out.  Each merging thread
-// owns outputs t + T k; the first batch of their partials is loaded together
-// with the splits' (max, sum) pairs; wave w then finds, for heads w, w + NW,
-// ..., the maximum over splits (one split per lane), every split's weight
-// exp(m - M) and the weighted sum of the splits' sums.
+// and synchronised by the caller), rescaled to a common maximum: the
+// unnormalised output [G][128] and (max, sum) [G][2] of split s of problem p,
+// stored to the workspace for merge_kernel.
 template <int G, int NW, int T>
-__device__ bool finish_split(const Geometry& g, const Workspace& ws, int p, int s, int splits,
-                             int b, int kvh, float (*wo)[G][kHeadDim], float (*wml)[G][2],
-                             int* last, float* out) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+__device__ void store_split(const Workspace& ws, int p, int s, int splits,
+                            float (*wo)[G][kHeadDim], float (*wml)[G][2]) {
   float* po = ws.part_o + ((size_t)p * splits + s) * G * kHeadDim;
   float* pm = ws.part_ml + ((size_t)p * splits + s) * G * 2;
-  for (int o = t; o < G * kHeadDim; o += T) {
+  for (int o = threadIdx.x; o < G * kHeadDim; o += T) {
     const int i = o / kHeadDim, d = o - i * kHeadDim;
     float M = -INFINITY;
 #pragma unroll
@@ -1559,70 +1515,73 @@ __device__ bool finish_split(const Geometry& g, const Workspace& ws, int p, int 
         L += wml[w][i][1] * f;
       }
     }
-    st_dev(po + o, a);
+    po[o] = a;
     if (d == 0) {
-      st_dev(pm + 2 * i, M);
-      st_dev(pm + 2 * i + 1, L);
+      pm[2 * i] = M;
+      pm[2 * i + 1] = L;
     }
   }
+}
 
-  if (!publish_and_arrive(&ws.ticket_attn[p], (uint32_t)splits, last)) return false;
-
-  constexpr int NO = (G * kHeadDim + T - 1) / T;
-  const float* pml = ws.part_ml + (size_t)p * splits * G * 2;
-  const float* pob = ws.part_o + (size_t)p * splits * G * kHeadDim;
-  float* mls = &wo[0][0][0];          // [splits][G][2]
-  float* wgt = mls + 2 * G * splits;  // [G][splits]
-  float* lsum = wgt + G * splits;     // [G]
-  // unconditional loads (indices clamped into the partials; surplus values
-  // get no weight) keep the batch free of branches
-  float pv[NO][kMergeBatch];
+// Merge of the splits of SparseAttn, one workgroup per (problem, query head),
+// one output dimension per thread: the maximum M over the splits' maxima,
+// every split's weight exp(m - M), and out = sum of weighted outputs / sum of
+// weighted sums, accumulated in split order (so the result does not depend on
+// the order in which splits finished).  The partials come from the attention
+// kernel just before it in the stream (the kernel boundary makes them
+// visible; they are read back from L2, not through the device coherence
+// point).  With `reset`, the problem's selection counters are cleared for the
+// next anchor layer (every split has read them by now).
+template <int G>
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(Geometry g, Workspace ws, int splits,
+                                                         float* __restrict__ out, int reset) {
+  __shared__ float sm_m[kMaxSplits], sm_l[kMaxSplits], sm_w[kMaxSplits];
+  __shared__ float sm_sum;
+  int p, i;
+  map_block(blockIdx.x, g.problems(), G, &p, &i);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int d = threadIdx.x, lane = d & 63, wave = d >> 6;
+  const float* pob = ws.part_o + (size_t)p * splits * G * kHeadDim + i * kHeadDim + d;
+  const float* pml = ws.part_ml + (size_t)p * splits * G * 2 + i * 2;
+  constexpr size_t so = (size_t)G * kHeadDim;  // split stride of the outputs
+  // unconditional loads (indices clamped; surplus values get no weight) keep
+  // the first batch free of branches
+  float pv[kMergeBatch];
 #pragma unroll
-  for (int k = 0; k < NO; ++k) {
-    const int o = min(t + T * k, G * kHeadDim - 1);
+  for (int x = 0; x < kMergeBatch; ++x) pv[x] = pob[(size_t)min(x, splits - 1) * so];
+  for (int x = d; x < splits; x += kHeadDim) {
+    sm_m[x] = pml[(size_t)x * G * 2];
+    sm_l[x] = pml[(size_t)x * G * 2 + 1];
+  }
+  lds_barrier();
+  if (wave == 0) {
+    float M = -INFINITY;
+    for (int x = lane; x < splits; x += 64) M = fmaxf(M, sm_m[x]);
+    M = wave_max(M);
+    float l = 0.f;
+    for (int x = lane; x < splits; x += 64) {
+      const float mx = sm_m[x];
+      const float f = (mx == -INFINITY) ? 0.f : __expf(mx - M);
+      sm_w[x] = f;
+      l += sm_l[x] * f;
+    }
+    l = wave_sum(l);
+    if (lane == 0) sm_sum = l;
+  }
+  lds_barrier();
+  float a = 0.f;
+  for (int x0 = 0; x0 < splits; x0 += kMergeBatch) {
+    if (x0 > 0) {
+#pragma unroll
+      for (int x = 0; x < kMergeBatch; ++x) pv[x] = pob[(size_t)min(x0 + x, splits - 1) * so];
+    }
 #pragma unroll
     for (int x = 0; x < kMergeBatch; ++x)
-      pv[k][x] = ld_dev(pob + (size_t)min(x, splits - 1) * G * kHeadDim + o);
+      if (x0 + x < splits) a += pv[x] * sm_w[x0 + x];
   }
-  for (int i = t; i < 2 * G * splits; i += T) mls[i] = ld_dev(pml + i);
-  lds_barrier();
-  for (int i = wave; i < G; i += T / 64) {
-    float M = -INFINITY;
-    for (int x = lane; x < splits; x += 64) M = fmaxf(M, mls[(x * G + i) * 2]);
-    M = wave_max(M);
-    float ls = 0.f;
-    for (int x = lane; x < splits; x += 64) {
-      const float mx = mls[(x * G + i) * 2];
-      const float f = (mx == -INFINITY) ? 0.f : __expf(mx - M);
-      wgt[i * splits + x] = f;
-      ls += mls[(x * G + i) * 2 + 1] * f;
-    }
-    ls = wave_sum(ls);
-    if (lane == 0) lsum[i] = ls;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int k = 0; k < NO; ++k) {
-    const int o = t + T * k;
-    if (o >= G * kHeadDim) break;
-    const int i = o / kHeadDim, d = o - i * kHeadDim;
-    const float* wi = wgt + i * splits;
-    float a = 0.f;
-    for (int x0 = 0; x0 < splits; x0 += kMergeBatch) {
-      if (x0 > 0) {
-#pragma unroll
-        for (int x = 0; x < kMergeBatch; ++x)
-          pv[k][x] = ld_dev(pob + (size_t)min(x0 + x, splits - 1) * G * kHeadDim + o);
-      }
-#pragma unroll
-      for (int x = 0; x < kMergeBatch; ++x)
-        if (x0 + x < splits) a += pv[k][x] * wi[x0 + x];
-    }
-    const float L = lsum[i];
-    out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = L > 0.f ? a / L : 0.f;
-  }
-  if (t == 0) ticket_reset(&ws.ticket_attn[p]);
-  return true;
+  const float L = sm_sum;
+  out[((size_t)b * g.hq + kvh * G + i) * kHeadDim + d] = L > 0.f ? a / L : 0.f;
+  if (reset && i == 0) reset_selection_counters(ws, p);
 }
 
 // SparseAttn over a given set (positions in idx) or over the row ids the
@@ -1632,13 +1591,11 @@ template <int G, bool ROWS>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspace ws,
                                                             const uint16_t* __restrict__ q,
                                                             const int32_t* __restrict__ idx,
-                                                            float scale,
-                                                            float* __restrict__ out) {
+                                                            float scale) {
   constexpr int NW = kAttnThreads / 64;
   __shared__ float wo[NW][G][kHeadDim];
   __shared__ float wml[NW][G][2];
   __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
-  __shared__ int last;
   const int splits = g.splits;
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
@@ -1677,7 +1634,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
     }
   }
   lds_barrier();
-  finish_split<G, NW, kAttnThreads>(g, ws, p, s, splits, b, kvh, wo, wml, &last, out);
+  store_split<G, NW, kAttnThreads>(ws, p, s, splits, wo, wml);
 }
 
 // Refined layer of a decode step: the selection and SparseAttn in one kernel.
@@ -1701,7 +1658,6 @@ struct FusedSmem {
   float wo[kFusedSplit / 16][G][kHeadDim];
   float wml[kFusedSplit / 16][G][2];
   float pw[kFusedSplit / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
-  int last;
 };
 
 // The selection step of refine_attn_kernel: every thread holds R consecutive
@@ -1779,11 +1735,10 @@ __device__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_
 template <int G>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
-                                                         float scale, float* __restrict__ out,
+                                                         float scale,
                                                          int32_t* __restrict__ layer_idx) {
   constexpr int NW = kFusedSplit / 16;  // waves that attend, 16 tokens each
   static_assert(NW >= 1 && NW <= NT / 64, "attending waves fit the workgroup");
-  static_assert(3 * (kMaxKappa / kFusedSplit) + 1 <= NW * kHeadDim, "merge tables fit");
   __shared__ FusedSmem<G> sm;
   const int K = g.kappa;
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
@@ -1844,7 +1799,7 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
     }
   }
   lds_barrier();
-  finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out);
+  store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
 }
 
 // ---------------------------------------------------------------------------
@@ -1854,7 +1809,7 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 // a bitmap over the cache (same inputs, same set), takes the marked entries'
 // ranks, predecessors and run offsets from block scans, writes its rank slice
 // of the anchor set and of the pool, and attends that slice (16 tokens per
-// wave); the last split to finish merges all splits.
+// wave); merge_kernel, launched next, merges the splits.
 // ---------------------------------------------------------------------------
 template <int G>
 struct AnchorSmem {
@@ -1873,7 +1828,6 @@ struct AnchorSmem {
   float wo[kFusedSplit / 16][G][kHeadDim];
   float wml[kFusedSplit / 16][G][2];
   float pw[kFusedSplit / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
-  int last;
 };
 
 // Marks of a list of at most kSmall entries from the keys in registers.
@@ -1896,11 +1850,10 @@ __device__ void small_marks(const float* sc, int n, int K, Sm& sm) {
 template <int G>
 __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
-                                                         float scale, float* __restrict__ out,
+                                                         float scale,
                                                          int32_t* __restrict__ anchor_idx,
                                                          int32_t* __restrict__ layer_idx) {
   constexpr int NW = kFusedSplit / 16;
-  static_assert(3 * (kMaxKappa / kFusedSplit) + 1 <= NW * kHeadDim, "merge tables fit");
   __shared__ AnchorSmem<G> sm;
   const int K = g.kappa;
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
@@ -2073,8 +2026,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
     }
   }
   lds_barrier();
-  if (finish_split<G, NW, NT>(g, ws, p, s, splits, b, kvh, sm.wo, sm.wml, &sm.last, out))
-    reset_selection_counters(ws, p);  // every split has read them
+  store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
 }
 
 // ---------------------------------------------------------------------------
@@ -2119,11 +2071,19 @@ void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* 
          w, q, wgs);
 }
 
+template <int G>
+void launch_merge_g(const Geometry& g, const Workspace& w, int splits, float* out, bool reset,
+                    hipStream_t s) {
+  launch(kMerge, merge_kernel<G>, dim3(g.problems() * G), dim3(kHeadDim), s, g, w, splits, out,
+         reset ? 1 : 0);
+}
+
 template <int G, bool ROWS>
 void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q,
                         const int32_t* idx, float scale, float* out, hipStream_t s) {
   launch(kAttention, attn_kernel<G, ROWS>, dim3(g.problems() * g.splits), dim3(kAttnThreads), s,
-         g, w, q, idx, scale, out);
+         g, w, q, idx, scale);
+  launch_merge_g<G>(g, w, g.splits, out, false, s);
 }
 
 #define PRISM_BY_GROUP(FN, ...)                      \
@@ -2161,7 +2121,7 @@ int64_t profile_launches(int kind) {
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
-  o += align256(P * (kCoarseBins + 2) * 4);                      // ghist, cand_cnt, ticket_attn
+  o += align256(P * (kCoarseBins + 1) * 4);                      // ghist, cand_cnt
   o += align256(P * 4 * 4);                                      // sel_meta
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_key
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx
@@ -2183,8 +2143,7 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   Workspace w;
   w.ghist = reinterpret_cast<uint32_t*>(c);
   w.cand_cnt = w.ghist + P * kCoarseBins;
-  w.ticket_attn = w.cand_cnt + P;
-  c += align256(P * (kCoarseBins + 2) * 4);
+  c += align256(P * (kCoarseBins + 1) * 4);
   w.sel_meta = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4 * 4);
   w.cand_key = reinterpret_cast<uint32_t*>(c);
@@ -2216,7 +2175,7 @@ Workspace carve_workspace(void* base, const Geometry& g) {
 // over many workgroups, then select per problem (and build the pool).
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 2);
+  const int nz = g.problems() * (kCoarseBins + 1);
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -2239,7 +2198,8 @@ void launch_anchor_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
                           float* out, int32_t* anchor_idx, int32_t* layer_idx, hipStream_t s) {
   const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
   launch(kAttention, anchor_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
-         scale, out, anchor_idx, layer_idx);
+         scale, anchor_idx, layer_idx);
+  launch_merge_g<G>(g, w, splits, out, true, s);
 }
 
 hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
@@ -2254,7 +2214,7 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
   }
   // The histogram and candidate counter are zero from the previous anchor
   // layer (the selection checks its own consistency, so a fresh workspace only
-  // takes the exact fallback once); anchor scoring zeroes the arrival counter.
+  // takes the exact fallback once).
   PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -2295,7 +2255,8 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
                           float* out, int32_t* layer_idx, hipStream_t s) {
   const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
   launch(kAttention, refine_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
-         scale, out, layer_idx);
+         scale, layer_idx);
+  launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
@@ -2315,12 +2276,6 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
     case 8: launch_refine_attn_g<8>(g, w, q, scale, out, layer_idx, s); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_zero_counters(const Geometry& g, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(zero_counters_kernel, dim3((g.problems() + 255) / 256), dim3(256), 0, s,
-                     w.ticket_attn, g.problems());
   return hipGetLastError();
 }
 
