@@ -69,14 +69,21 @@ class Hip:
             self.rt.hipEventDestroy(e)
 
 
-def launches_per_step(wl):
+def launches_per_step(wl, cus):
+    """Kernel launches of each kind in one decode step, mirroring the library's
+    choice: layers select inside their attention kernel when G <= 8 and every
+    attention workgroup of the layer fits the device at once (problems x
+    ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
+    196608), else a selection kernel per layer precedes the attention."""
     import synth
     na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     nr = wl.num_layers - na
     L = int(synth.paging(wl).seq_lens.max())
-    # with G <= 8 every layer selects inside its attention kernel
+    fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * -(-wl.kappa // 128) <= cus
+    anchor_fused = fused and L <= 6144 * 32
     return {"anchor_score": na, "refine_score": nr,
-            "select": wl.num_layers if wl.group > 8 else 0, "attention": wl.num_layers,
+            "select": (0 if anchor_fused else na) + (0 if fused else nr),
+            "attention": wl.num_layers,
             "classify": na if (L > 16384 and L > wl.kappa) else 0, "merge": wl.num_layers}
 
 
@@ -139,7 +146,7 @@ def cpu_baseline(wl, host, seconds):
         done += 1
         if time.perf_counter() - t_start > seconds:
             break
-    n_anchor = launches_per_step(wl)["anchor_score"]
+    n_anchor = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     n_ref = wl.num_layers - n_anchor
     P = len(probs)
     step_s = P * (n_anchor * float(np.mean(ta)) + n_ref * float(np.mean(tr)))
@@ -158,6 +165,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3-8b-128k-planted")
+    ap.add_argument("--distinct-layers", type=int, default=0, metavar="N",
+                    help="generate only N layers' inputs and give layer l those of layer l mod N "
+                         "(for workloads whose full KV cache does not fit host memory for "
+                         "generation; every layer still reads its own N-th of the data from HBM)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="budget of the CPU-oracle baseline sample (0 skips it)")
     ap.add_argument("--eager", action="store_true",
@@ -197,7 +208,8 @@ def main():
 
     # ---- inputs, resident in HBM ------------------------------------------------
     t0 = time.perf_counter()
-    log(f"[bench] generating {wl.num_layers} layers of {wl.name} "
+    nd = min(args.distinct_layers, wl.num_layers) if args.distinct_layers > 0 else wl.num_layers
+    log(f"[bench] generating {nd} of {wl.num_layers} layers of {wl.name} "
         f"(B={wl.batch}, L={int(pg.seq_lens.max())}, {wl.num_q_heads}q/{wl.num_kv_heads}kv)")
     bt = torch.from_numpy(pg.block_table).to(dev)
     sl = torch.from_numpy(pg.seq_lens).to(dev)
@@ -206,7 +218,7 @@ def main():
     keep_host = {0, 1} if args.cpu_seconds > 0 else set()
     nthreads = synth.default_threads()
     with ThreadPoolExecutor(nthreads) as ex:
-        futs = {ex.submit(synth.layer_inputs, wl, l, 1): l for l in range(wl.num_layers)}
+        futs = {ex.submit(synth.layer_inputs, wl, l, 1): l for l in range(nd)}
         for n_done, f in enumerate(as_completed(futs), 1):
             l = futs[f]
             li = f.result()
@@ -217,7 +229,7 @@ def main():
             if l in keep_host:
                 host_keep[l] = li
             del li
-            log(f"[bench] layer {l} resident ({n_done}/{wl.num_layers}, "
+            log(f"[bench] layer {l} resident ({n_done}/{nd}, "
                 f"{time.perf_counter() - t0:.1f} s)")
     torch.cuda.synchronize()
 
@@ -230,7 +242,7 @@ def main():
 
     # raw addresses, resolved once: the per-layer call is then one C call
     ws_arg = (ws.data_ptr(), ws.numel())
-    layer_args = [(kv_dev[l], q_dev[l].data_ptr(), outs[l].data_ptr())
+    layer_args = [(kv_dev[l % nd], q_dev[l % nd].data_ptr(), outs[l].data_ptr())
                   for l in range(wl.num_layers)]
     anchor_ptr = anchor.data_ptr()
 
@@ -277,7 +289,7 @@ def main():
 
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
-    per_step = launches_per_step(wl)
+    per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -317,9 +329,10 @@ def main():
     pool_bytes = []
     for l in range(wl.num_layers):
         if wl.is_anchor(l):
-            tsa.prism_score_topk(kv_dev[l], q_dev[l], p, anchor, None, ws)
+            tsa.prism_score_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, None, ws)
         else:
-            tsa.prism_refine_topk(kv_dev[l], q_dev[l], p, anchor, tmp_idx, None, pool_len, None, ws)
+            tsa.prism_refine_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, tmp_idx, None, pool_len,
+                                  None, ws)
             pool_bytes.append(int(pool_len.sum().item()) * D2)
     n_anchor = per_step["anchor_score"]
     step_bytes = n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
@@ -358,7 +371,8 @@ def main():
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "layers": wl.num_layers,
                    "anchor_stride": wl.anchor_stride, "kappa": wl.kappa, "window": wl.window,
-                   "page_size": wl.page_size},
+                   "page_size": wl.page_size,
+                   **({"distinct_layers": nd} if nd < wl.num_layers else {})},
         "roofline": roofline,
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),

@@ -2055,6 +2055,28 @@ void launch(int kind, void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The fused anchor / refined kernels repeat the selection in every attention
+// workgroup of a (sequence, KV head); that costs nothing while all of them run
+// at once (one workgroup of 1024 threads per compute unit), but multiplies
+// when the grid needs several rounds.  Larger grids select once per problem,
+// then attend.
+bool fused_fits(const Geometry& g) {
+  const long long wgs = (long long)g.problems() * ((g.kappa + kFusedSplit - 1) / kFusedSplit);
+  return g.group <= 8 && wgs <= (long long)device_cus();
+}
+
 template <int G>
 void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
                            hipStream_t s) {
@@ -2207,7 +2229,7 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
                                 hipStream_t s) {
   // the fused kernel's LDS holds up to 8 heads and lists up to kFusedAnchorLen
   // nonzero mark words; otherwise select, then attend
-  if (g.group > 8 || g.max_seq_len > kFusedAnchorLen) {
+  if (!fused_fits(g) || g.max_seq_len > kFusedAnchorLen) {
     hipError_t e = launch_anchor(g, w, q, anchor_idx, layer_idx, s);
     if (e != hipSuccess) return e;
     return launch_attention(g, w, q, nullptr, true, scale, out, s);
@@ -2261,7 +2283,7 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
 
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s) {
-  if (g.group > 8) {  // the fused kernel's LDS holds up to 8 heads: select, then attend
+  if (!fused_fits(g)) {  // select once per problem, then attend
     hipError_t e = launch_refine(g, w, q, layer_idx ? layer_idx : w.idx_tmp, s);
     if (e != hipSuccess) return e;
     return launch_attention(g, w, q, nullptr, true, scale, out, s);
