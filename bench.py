@@ -74,17 +74,22 @@ def launches_per_step(wl, cus):
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
-    196608), else a selection kernel per layer precedes the attention."""
+    196608), else a selection kernel per layer precedes the attention, and a
+    refined layer whose pool can exceed 16384 entries is classified first."""
     import synth
     na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
     nr = wl.num_layers - na
     L = int(synth.paging(wl).seq_lens.max())
     fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * -(-wl.kappa // 128) <= cus
     anchor_fused = fused and L <= 6144 * 32
+    n_cap = -(-L // 64) * 64
+    pool_bound = min(n_cap, wl.kappa * (2 * wl.window + 1))
+    pool_classify = not fused and pool_bound > 16384 and pool_bound > wl.kappa
     return {"anchor_score": na, "refine_score": nr,
             "select": (0 if anchor_fused else na) + (0 if fused else nr),
             "attention": wl.num_layers,
-            "classify": na if (L > 16384 and L > wl.kappa) else 0, "merge": wl.num_layers}
+            "classify": (na if (L > 16384 and L > wl.kappa) else 0) + (nr if pool_classify else 0),
+            "merge": wl.num_layers}
 
 
 def kernel_source_hash():

@@ -43,6 +43,7 @@ constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the po
 constexpr int kClsThreads = 256;
 constexpr int kClsEntries = 8192;         // anchor-list entries classified by one workgroup
 constexpr int kFusedSplit = 128;          // selected tokens attended by one fused workgroup
+constexpr int kPoolHistChunks = 4;        // pool chunks per workgroup when pool scoring counts bins
 constexpr int kFusedAnchorLen = 6144 * 32;  // contexts whose nonzero mark words fit sm.hist
 static_assert(kMaxCand <= kCand, "candidates of the threshold bin fit the LDS candidate buffer");
 static_assert(kMaxKappa <= 2 * kCand, "pool-build run offsets fit the LDS candidate buffer");
@@ -400,19 +401,28 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g,
 }
 
 // Refined layer: workgroup w of problem p scores pool entries
-// [w * kPoolEntries, +kPoolEntries) from the pool's row ids, 64 per wave; the
-// key rows are read and combined as in anchor scoring (VALU for groups of up
-// to 8 heads, 8 lanes per row; matrix cores for larger groups).
+// [w * chunks * kPoolEntries, +chunks * kPoolEntries) from the pool's row ids,
+// 64 per wave and chunk; the key rows are read and combined as in anchor
+// scoring (VALU for groups of up to 8 heads, 8 lanes per row; matrix cores for
+// larger groups).  With `hist`, pools longer than kSmall are also counted per
+// coarse bin, as in anchor scoring, for the classification that follows
+// (several chunks per workgroup amortise the LDS histogram).
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, Workspace ws,
                                                                    const uint16_t* __restrict__ q,
-                                                                   int wgs) {
+                                                                   int wgs, int chunks, int hist) {
+  __shared__ uint32_t lh[kCoarseBins];
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+  const int base = w * chunks * kPoolEntries;
+  if (base >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wbase = w * kPoolEntries + wave * (kPoolEntries / 4);
-  if (wbase >= n) return;
+  const bool counted = hist != 0 && n > kSmall;  // uniform over the workgroup
+  if (counted) {
+    for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
+    lds_barrier();
+  }
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const uint32_t* prow = ws.pool_row + (size_t)p * g.n_cap;
   float* sc = ws.scores + (size_t)p * g.n_cap;
@@ -420,9 +430,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
   if constexpr (G <= 8) {
     const int part = lane & 7, rs = lane >> 3;
     constexpr int kGroups = kPoolEntries / 4 / 8;  // 8 groups of 8 rows per wave
-    uint32_t rid[kGroups];
-#pragma unroll
-    for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wbase + u * 8 + rs, n - 1)];
     uint32_t qv[G][8];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -435,52 +442,77 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
         qv[h][4 + i] = x1[i];
       }
     }
-    u32x4 kb[kGroups][2];
+    for (int c = 0; c < chunks; ++c) {
+      const int wbase = base + c * kPoolEntries + wave * (kPoolEntries / 4);
+      if (wbase >= n) break;  // uniform over the wave
+      uint32_t rid[kGroups];
 #pragma unroll
-    for (int u = 0; u < kGroups; ++u) {
-      const u32x4* row =
-          reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
-      kb[u][0] = __builtin_nontemporal_load(row + part);
-      kb[u][1] = __builtin_nontemporal_load(row + part + 8);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wbase + u * 8 + rs, n - 1)];
+      u32x4 kb[kGroups][2];
 #pragma unroll
-    for (int u = 0; u < kGroups; ++u) {
-      float m = -INFINITY;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float a = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][i], kb[u][0][i], a);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][4 + i], kb[u][1][i], a);
-        m = fmaxf(m, group8_sum(a));
+      for (int u = 0; u < kGroups; ++u) {
+        const u32x4* row =
+            reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+        kb[u][0] = __builtin_nontemporal_load(row + part);
+        kb[u][1] = __builtin_nontemporal_load(row + part + 8);
       }
-      const int e = wbase + u * 8 + rs;
-      if (part == 0 && e < n) sc[e] = m;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float a = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][i], kb[u][0][i], a);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a = dot2_bf16(qv[h][4 + i], kb[u][1][i], a);
+          m = fmaxf(m, group8_sum(a));
+        }
+        const int e = wbase + u * 8 + rs;
+        if (part == 0 && e < n) {
+          sc[e] = m;
+          if (counted) atomicAdd(&lh[order_key(m) >> 20], 1u);
+        }
+      }
     }
   } else {
     const int j = lane & 15, g4 = lane >> 4;
     u32x4 qf[4];
     load_q_frag<G>(q, g, b, kvh, lane, qf);
     constexpr int kTiles = kPoolEntries / 4 / 16;
-    uint32_t rid[kTiles];
+    for (int c = 0; c < chunks; ++c) {
+      const int wbase = base + c * kPoolEntries + wave * (kPoolEntries / 4);
+      if (wbase >= n) break;  // uniform over the wave
+      uint32_t rid[kTiles];
 #pragma unroll
-    for (int u = 0; u < kTiles; ++u) rid[u] = prow[min(wbase + u * 16 + j, n - 1)];
-    u32x4 kf[kTiles][4];
+      for (int u = 0; u < kTiles; ++u) rid[u] = prow[min(wbase + u * 16 + j, n - 1)];
+      u32x4 kf[kTiles][4];
 #pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-      const u32x4* row =
-          reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
+      for (int u = 0; u < kTiles; ++u) {
+        const u32x4* row =
+            reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) kf[u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+        for (int s4 = 0; s4 < 4; ++s4) kf[u][s4] = __builtin_nontemporal_load(row + g4 + 4 * s4);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kTiles; ++u) {
+        const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
+        const int e = wbase + u * 16 + j;
+        if (g4 == 0 && e < n) {
+          sc[e] = m;
+          if (counted) atomicAdd(&lh[order_key(m) >> 20], 1u);
+        }
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-      const float m = group_max<G>(qk_tile(qf, kf[u]), g4);
-      const int e = wbase + u * 16 + j;
-      if (g4 == 0 && e < n) sc[e] = m;
+  }
+  if (counted) {
+    lds_barrier();
+    uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
+    for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) {
+      const uint32_t c = lh[i];
+      if (c) atomicAdd(&gh[i], c);
     }
   }
 }
@@ -1241,16 +1273,14 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
     select_small<kSmallPer / 2>(g, c, sm);
   } else if (c.n <= kSmall) {
     select_small<kSmallPer>(g, c, sm);
-  } else if (!POOL) {
+  } else {  // after classify_kernel (with `pool` at a refined layer)
     select_classified(g, ws, p, c, sm);
-  } else {
-    select_large(g, c, sm);
   }
   if (!POOL) {
     lds_barrier();
     build_pool(g, ws, p, kvh, L, sm);
-    reset_selection_counters(ws, p);
   }
+  reset_selection_counters(ws, p);
 }
 
 // Pool of an anchor set given in device memory (one workgroup per problem).
@@ -1266,19 +1296,21 @@ __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws
   build_pool(g, ws, p, kvh, L, sm);
 }
 
-// Anchor lists longer than kSmall: workgroup w of problem p takes list entries
+// Lists longer than kSmall (the cache at an anchor layer, the pool at a refined
+// layer with `pool`): workgroup w of problem p takes list entries
 // [w * kClsEntries, +kClsEntries).  From the problem's coarse histogram it
 // finds the bin holding the kappa-th score (every workgroup finds the same
 // bin; workgroup 0 records it with the count of entries above it and in it),
 // marks its entries above that bin in the workspace bitmap and appends the
 // bin's own entries, with their keys, to the problem's candidate list.
-__global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs) {
+__global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs,
+                                                               int pool) {
   __shared__ int tmp[kClsThreads / 64];
   __shared__ int res[3];
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv;
-  const int n = seq_len_of(g, b);
+  const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : seq_len_of(g, b);
   const int base = w * kClsEntries;
   if (n <= kSmall || n <= g.kappa || base >= n) return;  // uniform over the workgroup
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -2086,11 +2118,13 @@ void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t
 }
 
 template <int G>
-void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* q, bool hist,
                          hipStream_t s) {
-  const int wgs = (g.n_cap + kPoolEntries - 1) / kPoolEntries;
+  const int chunks = hist ? kPoolHistChunks : 1;
+  const int per_wg = chunks * kPoolEntries;
+  const int wgs = (g.n_cap + per_wg - 1) / per_wg;
   launch(kRefineScore, score_pool_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s, g,
-         w, q, wgs);
+         w, q, wgs, chunks, hist ? 1 : 0);
 }
 
 template <int G>
@@ -2207,7 +2241,8 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
   if (e != hipSuccess) return e;
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
-    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs);
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
+           0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2242,7 +2277,8 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
   if (e != hipSuccess) return e;
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
-    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs);
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
+           0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2262,11 +2298,25 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
   return hipGetLastError();
 }
 
+// Refined layer without the fused kernel: score the pool (counting pools longer
+// than kSmall per coarse bin), classify those pools over many workgroups, then
+// select per problem.  The pool's length is known on the device only; its
+// bound min(n_cap, kappa (2w + 1)) decides whether classification can be
+// needed at all.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          hipStream_t s) {
-  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, s);
+  const long long bound = std::min<long long>(g.n_cap, (long long)g.kappa * (2LL * g.window + 1));
+  const bool classify = bound > kSmall && bound > g.kappa;
+  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, classify, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (classify) {
+    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
+           1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w, out,
          static_cast<int32_t*>(nullptr));
   return hipGetLastError();
@@ -2288,7 +2338,7 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
     if (e != hipSuccess) return e;
     return launch_attention(g, w, q, nullptr, true, scale, out, s);
   }
-  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, s);
+  PRISM_BY_GROUP(launch_pool_score_g, g, w, q, false, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (g.group) {
