@@ -36,6 +36,7 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr int NT = kSelThreads;
 constexpr int kSmall = 16384;   // lists up to this length are selected with every key in registers
 constexpr int kSmallPer = kSmall / kSelThreads;  // 16 consecutive entries per thread
+constexpr int kRegMarks = 2 * kSmall;  // fused refined kernel: pools held 32 keys per thread
 constexpr int kSample = 8192;   // most entries of a longer list sampled to bracket the kappa-th key
 constexpr int kCand = 4096;     // bracketed candidates held in LDS
 constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the list pass
@@ -652,7 +653,7 @@ struct Thresh {
 // range), a zero range or a non-finite range falls back to an exact
 // 12/10/10-bit radix over the keys.
 template <int R, typename Sm>
-__device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm& sm) {
+__device__ __forceinline__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm& sm) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
@@ -763,7 +764,7 @@ __device__ Thresh find_threshold(const uint32_t (&key)[R], int nv, int need, Sm&
 // Ties at the threshold go to the lowest list indices (thread order is list
 // order).  Contains barriers: call uniformly.
 template <int R, typename Sm>
-__device__ uint32_t top_k_mask(const uint32_t (&key)[R], int nv, int n, int K, Sm& sm) {
+__device__ __forceinline__ uint32_t top_k_mask(const uint32_t (&key)[R], int nv, int n, int K, Sm& sm) {
   static_assert(R <= 32, "one mask bit per entry");
   if (n <= K) return nv >= 32 ? 0xFFFFFFFFu : ((1u << nv) - 1u);
   const Thresh th = find_threshold<R>(key, nv, K, sm);
@@ -868,7 +869,7 @@ __device__ void emit_bitmap(const Geometry& g, const SelList& c, SelectSmem& sm)
 // radix runs over the whole list instead.  The bitmap, read in order, gives
 // ascending positions; entries equal to T are taken lowest list index first.
 template <typename Sm>
-__device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) {
+__device__ __forceinline__ void select_large_marks(const SelList& c, Sm& sm) {
   const int t = threadIdx.x, lane = t & 63;
   const int n = c.n, K = c.K;
   uint32_t* h1 = sm.hist;
@@ -1035,7 +1036,7 @@ __device__ void select_large_marks(const Geometry& g, const SelList& c, Sm& sm) 
 }
 
 __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
-  select_large_marks(g, c, sm);
+  select_large_marks(c, sm);
   emit_bitmap(g, c, sm);
 }
 
@@ -1674,8 +1675,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
 // workgroup reaches the same set: same keys, same order) and attends its ranks
 // [s * kFusedSplit, +kFusedSplit) of the ascending set, 16 per wave;
 // layer_idx, if given, receives those ranks' positions.  Pools of at most
-// kSmall entries are selected in registers, longer ones by the sampled
-// bracket and one pass over the pool (marks in an LDS bitmap).
+// kSmall entries are selected in registers; up to kRegMarks entries also from
+// registers (32 keys per thread) into marks in an LDS bitmap; longer ones by
+// the sampled bracket and one pass over the pool (marks in the bitmap).
 template <int G>
 struct FusedSmem {
   uint32_t hist[4096 + 1024 + 1024];
@@ -1764,6 +1766,45 @@ __device__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_
   return total;
 }
 
+// The selection step of refine_attn_kernel for pools longer than kSmall, kept
+// out of line (plain pointer and integer arguments) so that the common path
+// stays small: up to kRegMarks entries from 32 keys per thread (each thread's
+// mask is one bitmap word), longer pools by the sampled bracket and one pass.
+// Returns the size of the selected set; sm.srow receives the split's rows.
+template <typename Sm>
+__device__ __attribute__((noinline)) int long_pool_slice(const float* sc, const int32_t* plist,
+                                                        const uint32_t* prow, int n, int n_cap,
+                                                        int K, int p, int r0, int32_t* layer_idx,
+                                                        Sm* smp) {
+  Sm& sm = *smp;
+  const int t = threadIdx.x;
+  SelList c;
+  c.sc = sc;
+  c.plist = plist;
+  c.prow = prow;
+  c.n = n;
+  c.K = K;
+  c.b = 0;
+  c.kvh = 0;
+  c.o1 = c.o2 = nullptr;
+  c.srow = nullptr;
+  if (n <= kRegMarks) {
+    constexpr int R = kRegMarks / NT;
+    static_assert(R == 32, "one bitmap word per thread");
+    const int e0 = R * t;
+    uint32_t key[R];
+    load_run<R>(sc, min(e0, n_cap - R), key);  // n_cap is a multiple of 64
+#pragma unroll
+    for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+    const uint32_t take = top_k_mask<R>(key, clampi(n - e0, 0, R), n, K, sm);
+    if (e0 < n) sm.bitmap[t] = take;
+    lds_barrier();
+  } else {
+    select_large_marks(c, sm);
+  }
+  return slice_from_marks(c, p, r0, layer_idx, sm);
+}
+
 template <int G>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
@@ -1793,18 +1834,9 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   } else {
-    SelList c;
-    c.sc = ws.scores + (size_t)p * g.n_cap;
-    c.plist = ws.pool_pos + (size_t)p * g.n_cap;
-    c.prow = ws.pool_row + (size_t)p * g.n_cap;
-    c.n = n;
-    c.K = K;
-    c.b = b;
-    c.kvh = kvh;
-    c.o1 = c.o2 = nullptr;
-    c.srow = nullptr;
-    select_large_marks(g, c, sm);
-    const int total = slice_from_marks(c, p, r0, layer_idx, sm);
+    const size_t base = (size_t)p * g.n_cap;
+    const int total = long_pool_slice(ws.scores + base, ws.pool_pos + base, ws.pool_row + base, n,
+                                      g.n_cap, K, p, r0, layer_idx, &sm);
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   }
