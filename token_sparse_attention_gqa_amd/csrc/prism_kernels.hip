@@ -1051,8 +1051,9 @@ __device__ void reset_selection_counters(const Workspace& ws, int p) {
 // Anchor lists longer than kSmall, after the classify kernel: the entries
 // above the threshold bin are marked in the workspace bitmap, and the bin's own
 // entries (the candidates) are listed with their keys.  The candidates are
-// ranked here; if the bin held more than kMaxCand of them, an exact radix over
-// the whole list runs instead.
+// ranked here (directly against each other when there are at most kPairMax,
+// else by a threshold search); if the bin held more than kMaxCand of them, an
+// exact radix over the whole list runs instead.
 template <typename Sm>
 __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, const SelList& c,
                                  Sm& sm) {
@@ -1076,7 +1077,36 @@ __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, 
   // the classify pass must agree with itself: as many marks as entries above the
   // threshold bin and as many candidates as entries in it (a histogram left
   // over from an earlier call, e.g. in a fresh workspace, fails this)
-  if (marks == above && ncand == in_bin && need >= 1 && need <= ncand && ncand <= kMaxCand) {
+  if (marks == above && ncand == in_bin && need >= 1 && need <= ncand && ncand <= kPairMax) {
+    // few candidates (the usual case): each one's rank among them, four
+    // threads per candidate: candidates with a larger key, or an equal key and
+    // a lower list index, come first
+    const uint32_t* gk = ws.cand_key + (size_t)p * kMaxCand;
+    const int32_t* gi = ws.cand_idx + (size_t)p * kMaxCand;
+    if (t < ncand) {
+      ckey[t] = gk[t];
+      cidx[t] = gi[t];
+    }
+    lds_barrier();
+    const int x = t >> 2, part = t & 3;
+    uint32_t kx = 0u;
+    int ix = 0, r = 0;
+    if (x < ncand) {
+      kx = ckey[x];
+      ix = cidx[x];
+      for (int y = part; y < ncand; y += 4) {
+        const uint32_t ky = ckey[y];
+        r += (ky > kx || (ky == kx && cidx[y] < ix)) ? 1 : 0;
+      }
+    }
+    r += (int)dpp<kQuadXor1, 0xf>(0u, (uint32_t)r);
+    r += (int)dpp<kQuadXor2, 0xf>(0u, (uint32_t)r);
+    if (x < ncand && part == 0 && r < need) {
+      const int e = clampi(ix, 0, n - 1);
+      atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
+    }
+  } else if (marks == above && ncand == in_bin && need >= 1 && need <= ncand &&
+             ncand <= kMaxCand) {
     constexpr int RC = kMaxCand / NT;
     uint32_t ck[RC];
     int32_t ci[RC];
