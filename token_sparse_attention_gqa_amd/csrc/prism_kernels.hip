@@ -1948,6 +1948,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
                                                          int32_t* __restrict__ anchor_idx,
                                                          int32_t* __restrict__ layer_idx) {
   constexpr int NW = kFusedSplit / 16;
+  static_assert(NW < NT / 64, "waves left over to write the pool during the attention");
   __shared__ AnchorSmem<G> sm;
   const int K = g.kappa;
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
@@ -2067,36 +2068,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
     if (anchor_idx) anchor_idx[(size_t)p * K + r] = a;
     if (layer_idx) layer_idx[(size_t)p * K + r] = a;
   }
-  // 5. this split's part of the pool: 8 consecutive entries per thread, the run
-  //    of the first found by binary search over the slice's offsets
-  int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
-  uint32_t* prw = ws.pool_row + (size_t)p * g.n_cap;
-  if (r0 < kt) {
-    const int re = min(rend, kt);
-    const int ob = lens[r0];
-    const int oe = min(re < kt ? lens[re] : pool_n, g.n_cap);
-    for (int o = ob + 8 * t; o < oe; o += 8 * NT) {
-      int lo = r0, hi = re - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (lens[mid] <= o) lo = mid;
-        else hi = mid - 1;
-      }
-      int k = lo;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int oi = o + i;
-        if (oi < oe) {
-          while (k + 1 < re && lens[k + 1] <= oi) ++k;
-          const int ps = sm.sst[k - r0] + (oi - lens[k]);
-          pp[oi] = ps;
-          prw[oi] = row_id_of_page(g, sm.bt[ps >> 6], kvh, ps);
-        }
-      }
-    }
-  }
-  if (s == 0 && t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
-  lds_barrier();
+  lds_barrier();  // srow, lens and sst are complete
 
   const int myr = r0 + wave * 16 + j;
   bool valid = wave < NW && myr < min(total, K);
@@ -2118,6 +2090,39 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
         }
       }
     }
+  } else {
+    // 5. meanwhile the other waves write this split's part of the pool: 8
+    //    consecutive entries per thread, the run of the first found by binary
+    //    search over the slice's offsets
+    const int tp = t - NW * 64;  // thread index among the pool-writing waves
+    constexpr int TP = NT - NW * 64;
+    int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
+    uint32_t* prw = ws.pool_row + (size_t)p * g.n_cap;
+    if (r0 < kt) {
+      const int re = min(rend, kt);
+      const int ob = lens[r0];
+      const int oe = min(re < kt ? lens[re] : pool_n, g.n_cap);
+      for (int o = ob + 8 * tp; o < oe; o += 8 * TP) {
+        int lo = r0, hi = re - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (lens[mid] <= o) lo = mid;
+          else hi = mid - 1;
+        }
+        int k = lo;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int oi = o + i;
+          if (oi < oe) {
+            while (k + 1 < re && lens[k + 1] <= oi) ++k;
+            const int ps = sm.sst[k - r0] + (oi - lens[k]);
+            pp[oi] = ps;
+            prw[oi] = row_id_of_page(g, sm.bt[ps >> 6], kvh, ps);
+          }
+        }
+      }
+    }
+    if (s == 0 && tp == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
   }
   lds_barrier();
   store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
