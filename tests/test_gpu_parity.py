@@ -304,6 +304,18 @@ def test_decode_from_leftover_workspace(fill):
         _run_chain(st, range(3), probs, f"leftover-ws {fill:#x} step {rep}")
 
 
+def test_decode_chain_per_problem_selection():
+    """A grid the fused kernels do not use (32 problems x 9 splits of 128 > 256
+    compute units): every layer selects once per problem (anchor lists and
+    pools longer than 16384 entries are classified first), then attends.
+    Ragged lengths; unstructured keys, so the pools cover most of the cache."""
+    wl = synth.scaled(synth.BATCHED_16, name="per-problem", wid=193, batch=4, kappa=1100,
+                      window=16, num_layers=3, anchor_stride=3, len_range=(17000, 40000))
+    st = Setup(wl, range(3))
+    probs = [(0, 0), (1, 3), (2, 5), (3, 7)]
+    _run_chain(st, range(3), probs, "per-problem")
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []
