@@ -2,9 +2,10 @@
 decode-step path.  Imported only by the tests, the package smoke check and the
 benchmark's CPU-baseline leg; it shares no code with the HIP library."""
 from .prism_oracle import (bf16_to_f64, cache_rows, relevance, top_kappa, window_pool,
-                           attention_weights, sparse_attention, default_scale, anchor_select,
-                           refined_select, attend, decode_layer, decode_step)
+                           rank_pool, attention_weights, sparse_attention, default_scale,
+                           anchor_select, refine_in_pool, refined_select, attend, decode_layer,
+                           decode_step)
 
-__all__ = ["bf16_to_f64", "cache_rows", "relevance", "top_kappa", "window_pool",
+__all__ = ["bf16_to_f64", "cache_rows", "relevance", "top_kappa", "window_pool", "rank_pool",
            "attention_weights", "sparse_attention", "default_scale", "anchor_select",
-           "refined_select", "attend", "decode_layer", "decode_step"]
+           "refine_in_pool", "refined_select", "attend", "decode_layer", "decode_step"]

@@ -14,9 +14,10 @@ where the paper is silent (all also listed in the design notes):
   * GQA: query head j belongs to KV head j // G (consecutive blocks);
   * TopK ties go to the lower token position; the selected set is returned as
     ascending positions (the paper treats it as a set);
-  * refined layers use a positional window: the candidate pool is the union of
-    [i - w, i + w], clipped to [0, L), over the anchor layer's top-kappa set
-    (the paper's own pool is the anchor's top-(rho*kappa), Eq. 4);
+  * refined layers use a positional window by default: the candidate pool is
+    the union of [i - w, i + w], clipped to [0, L), over the anchor layer's
+    top-kappa set; the paper's own pool, the anchor's top-(rho*kappa) tokens
+    (Eq. 4), is the alternative (pool_rho >= 1);
   * a refined layer always expands the nearest preceding anchor's set;
   * SparseAttn is softmax attention with scale 1/sqrt(D) unless given.
 
@@ -93,6 +94,18 @@ def window_pool(anchor_positions, w: int, length: int) -> np.ndarray:
     return np.flatnonzero(mask).astype(np.int64)
 
 
+def rank_pool(anchor_scores, positions, rho: int, kappa: int) -> np.ndarray:
+    """Eq. 4: the candidate pool a proposal (anchor) layer hands to the layers
+    it serves is its own rho*kappa most relevant tokens, TopK of Eq. 2 with
+    rho*kappa in place of kappa (every candidate when rho*kappa exceeds their
+    number).  anchor_scores are the anchor layer's relevance over `positions`.
+    Returned ascending."""
+    if rho < 1:
+        raise ValueError("rho must be >= 1")
+    positions = np.asarray(positions, dtype=np.int64)
+    return top_kappa(anchor_scores, min(rho * kappa, positions.shape[0]), positions)
+
+
 # ---------------------------------------------------------------------------
 # Algorithm 1, SparseAttn
 # ---------------------------------------------------------------------------
@@ -130,14 +143,22 @@ def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, pag
     return top_kappa(s, kappa, pos), s
 
 
+def refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size):
+    """Refined layer of Algorithm 1 (Eqs. 5-6) over a given candidate pool:
+    re-score only the pool's tokens, keep the top-kappa there.
+    Returns (selected, scores over the pool)."""
+    pool = np.asarray(pool, dtype=np.int64)
+    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pool, page_size))
+    return top_kappa(s, kappa, pool), s
+
+
 def refined_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size,
                    anchor_positions, w):
-    """Refined layer of Algorithm 1 (Eqs. 5-6): re-score only inside the
-    pool built from the anchor's set, keep the top-kappa there.
+    """Refined layer with the window pool built from the anchor's set.
     Returns (selected, pool, scores over the pool)."""
     pool = window_pool(anchor_positions, w, length)
-    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pool, page_size))
-    return top_kappa(s, kappa, pool), pool, s
+    t, s = refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size)
+    return t, pool, s
 
 
 def attend(q_group, k_pages, v_pages, block_table_row, kv_head, selected, page_size, scale):
@@ -148,16 +169,20 @@ def attend(q_group, k_pages, v_pages, block_table_row, kv_head, selected, page_s
 
 def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_kv_heads,
                  kappa, anchor_stride, window, page_size, anchor_state=None, scale=None,
-                 problems=None):
+                 problems=None, pool_rho=0, pool_state=None):
     """One layer of Algorithm 1 for every (sequence, KV head).
 
     q_bits: uint16 [B, Hq, D].  anchor_state: int64 [B, Hkv, kappa], the most
     recent anchor layer's sets (required for a refined layer).
+    pool_rho: 0 for the window pool, rho >= 1 for the anchor's top rho*kappa
+    tokens (Eq. 4); then pool_state, {(b, g): pool} from the most recent
+    anchor layer, is required for a refined layer.
     problems: optional list of (b, g) to restrict the work to (others are left
     as -1 / NaN).
 
     Returns dict(selected [B,Hkv,kappa] int64, out [B,Hq,D] float64,
-    anchor_state, pools {(b,g): pool}, scores {(b,g): scores over the pool}).
+    anchor_state, pool_state, pools {(b,g): pool the layer selected from},
+    scores {(b,g): scores over that pool}).
     """
     B, Hq, D = q_bits.shape
     G = Hq // num_kv_heads
@@ -167,9 +192,12 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
     is_anchor = layer % anchor_stride == 0
     if not is_anchor and anchor_state is None:
         raise ValueError("a refined layer needs the preceding anchor's sets")
+    if not is_anchor and pool_rho >= 1 and pool_state is None:
+        raise ValueError("a refined layer needs the preceding anchor's pools")
     sel = np.full((B, num_kv_heads, kappa), -1, dtype=np.int64)
     out = np.full((B, Hq, D), np.nan)
     pools, scores = {}, {}
+    new_pools = {} if is_anchor else pool_state
     todo = problems if problems is not None else [(b, g) for b in range(B)
                                                   for g in range(num_kv_heads)]
     for b, g in todo:
@@ -178,6 +206,12 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
         if is_anchor:
             t, s = anchor_select(qg, k_pages, block_table[b], g, L, kappa, page_size)
             pools[(b, g)] = np.arange(L, dtype=np.int64)
+            if pool_rho >= 1:
+                new_pools[(b, g)] = rank_pool(s, pools[(b, g)], pool_rho, kappa)
+        elif pool_rho >= 1:
+            pool = pool_state[(b, g)]
+            t, s = refine_in_pool(qg, k_pages, block_table[b], g, pool, kappa, page_size)
+            pools[(b, g)] = pool
         else:
             t, pool, s = refined_select(qg, k_pages, block_table[b], g, L, kappa, page_size,
                                         anchor_state[b, g], window)
@@ -187,19 +221,21 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
         out[b, g * G:(g + 1) * G] = attend(qg, k_pages, v_pages, block_table[b], g, t,
                                            page_size, scale)
     new_state = sel.copy() if is_anchor else anchor_state
-    return dict(selected=sel, out=out, anchor_state=new_state, pools=pools, scores=scores)
+    return dict(selected=sel, out=out, anchor_state=new_state, pool_state=new_pools,
+                pools=pools, scores=scores)
 
 
 def decode_step(layers, block_table, seq_lens, *, num_kv_heads, kappa, anchor_stride, window,
-                page_size, scale=None):
+                page_size, scale=None, pool_rho=0):
     """Algorithm 1 over layers 0..N-1 in order; `layers` yields
     (q_bits, k_pages, v_pages) per layer.  Layer 0 must be an anchor."""
-    state = None
+    state, pstate = None, None
     results = []
     for l, (q_bits, kp, vp) in enumerate(layers):
         r = decode_layer(l, q_bits, kp, vp, block_table, seq_lens, num_kv_heads=num_kv_heads,
                          kappa=kappa, anchor_stride=anchor_stride, window=window,
-                         page_size=page_size, anchor_state=state, scale=scale)
-        state = r["anchor_state"]
+                         page_size=page_size, anchor_state=state, scale=scale,
+                         pool_rho=pool_rho, pool_state=pstate)
+        state, pstate = r["anchor_state"], r["pool_state"]
         results.append(r)
     return results

@@ -192,6 +192,59 @@ def pin_refine_limits(impl, seed=15):
         assert np.array_equal(t0, A) and np.array_equal(pool0, A)
 
 
+# ---------------------------------------------------------------- rank pool
+def pin_rank_pool_exhaustive(impl, seed=19):
+    """Eq. 4: the pool is the rho*kappa best of the anchor's scores (ties to the
+    lower position), every candidate when rho*kappa exceeds their number;
+    against the exhaustive subset search."""
+    rng = np.random.default_rng(seed)
+    for _ in range(60):
+        n = int(rng.integers(1, 9))
+        scores = rng.integers(-2, 3, size=n)            # heavy ties
+        pos = rng.permutation(40)[:n]
+        for kappa in range(1, n + 1):
+            for rho in (1, 2, 3, 9):
+                got = impl.rank_pool(_arr(scores), pos, rho, kappa)
+                want = _brute_topk(list(map(int, scores)), min(rho * kappa, n), pos)
+                assert list(map(int, got)) == want, (scores, pos, rho, kappa, got)
+
+
+def pin_rank_pool_structure(impl, seed=20):
+    """The anchor's own set lies inside its pool, and the pool grows with rho;
+    every pool token outscores every other under the anchor's scores; rho = 1
+    hands over the set itself, so a refined layer reuses it (Eq. 3); a pool
+    covering the cache makes refinement the exact TopK of the refined layer."""
+    rng = np.random.default_rng(seed)
+    for _ in range(25):
+        L, D, G = int(rng.integers(4, 60)), 4, int(rng.integers(1, 4))
+        kappa = int(rng.integers(1, L + 1))
+        ra = np.round(rng.standard_normal((L, D)) * 4) / 4
+        rr = np.round(rng.standard_normal((L, D)) * 4) / 4
+        (pa, pr), bt = _tiny_paged([ra, rr], page_size=4, seed=int(rng.integers(1000)))
+        qa = np.round(rng.standard_normal((G, D)) * 4) / 4
+        qr = np.round(rng.standard_normal((G, D)) * 4) / 4
+        A, s = impl.anchor_select(qa, pa, bt, 0, L, kappa, 4)
+        pos = np.arange(L)
+        prev = None
+        for rho in (1, 2, 3, L):
+            C = np.asarray(impl.rank_pool(s, pos, rho, kappa))
+            assert C.shape == (min(rho * kappa, L),)
+            assert np.all(np.diff(C) > 0)
+            assert np.isin(A, C).all()
+            if prev is not None:
+                assert np.isin(prev, C).all()
+            prev = C
+            rest = np.setdiff1d(pos, C)
+            if rest.size:
+                assert s[C].min() >= s[rest].max()
+            t, _ = impl.refine_in_pool(qr, pr, bt, 0, C, kappa, 4)
+            if rho == 1:
+                assert np.array_equal(t, A)
+            if rho * kappa >= L:
+                exact, _ = impl.anchor_select(qr, pr, bt, 0, L, kappa, 4)
+                assert np.array_equal(t, exact)
+
+
 # ---------------------------------------------------------------- attention
 def pin_attention_dense_library(impl, seed=16):
     """kappa = L: sparse attention over every token equals dense attention, here
@@ -273,5 +326,6 @@ def pin_cache_rows(impl):
 
 ALL_PINS = [pin_bf16_decode, pin_relevance_bruteforce, pin_relevance_hand, pin_topk_exhaustive,
             pin_topk_invariants, pin_topk_hand, pin_pool_bruteforce, pin_pool_hand,
-            pin_refine_hand, pin_refine_limits, pin_attention_dense_library,
+            pin_refine_hand, pin_refine_limits, pin_rank_pool_exhaustive,
+            pin_rank_pool_structure, pin_attention_dense_library,
             pin_attention_closed_forms, pin_attention_hand, pin_cache_rows]

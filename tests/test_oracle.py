@@ -89,3 +89,25 @@ def test_refined_layer_requires_anchor_state():
     with pytest.raises(ValueError):
         oracle.decode_layer(1, *layers[1], bt, lens, num_kv_heads=2, kappa=3, anchor_stride=3,
                             window=1, page_size=2)
+
+
+def test_decode_step_rank_pool():
+    """pool_rho >= 1: the refined layers re-score the anchor layer's top
+    rho*kappa tokens (Eq. 4).  In the hand example the anchor scores
+    [3, 1, 4, -1, 2, 3, 0, 1] give the pool {0, 1, 2, 4, 5, 7} at rho = 2,
+    kappa = 3 (1 and 7 tie at score 1 and both fit); the refined scores
+    [0, 5, 1, 2, 0, 1, 6, 9] over that pool select {1, 2, 7}: position 6, the
+    refined layer's second best, lies outside the pool, and 2 beats 5 on the
+    tie at score 1."""
+    layers, bt, lens = _decode_case()
+    res = oracle.decode_step(layers, bt, lens, num_kv_heads=2, kappa=3, anchor_stride=3,
+                             window=1, page_size=2, pool_rho=2)
+    for h in range(2):
+        assert list(res[0]["selected"][0, h]) == [0, 2, 5]
+        for l in (1, 2):
+            assert list(res[l]["pools"][(0, h)]) == [0, 1, 2, 4, 5, 7]
+            assert list(res[l]["selected"][0, h]) == [1, 2, 7]
+    with pytest.raises(ValueError):   # a refined layer needs the anchor's pools
+        oracle.decode_layer(1, *layers[1], bt, lens, num_kv_heads=2, kappa=3, anchor_stride=3,
+                            window=1, page_size=2, anchor_state=res[0]["anchor_state"],
+                            pool_rho=2)

@@ -11,20 +11,32 @@ from oracle import prism_oracle as po
 from tests import pins
 
 
-def _compose(ns):
-    """anchor/refined selection built from the namespace's own parts, so a
-    mutated part shows through them."""
+def _compose(ns, keep=()):
+    """anchor/refined selection (and the rank pool, unless itself mutated)
+    built from the namespace's own parts, so a mutated part shows through
+    them."""
     def anchor_select(q, kp, bt, g, L, kappa, ps):
         pos = np.arange(L, dtype=np.int64)
         s = ns.relevance(q, ns.cache_rows(kp, bt, g, pos, ps))
         return ns.top_kappa(s, kappa, pos), s
 
+    def refine_in_pool(q, kp, bt, g, pool, kappa, ps):
+        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pool, ps))
+        return ns.top_kappa(s, kappa, pool), s
+
     def refined_select(q, kp, bt, g, L, kappa, ps, A, w):
         pool = ns.window_pool(A, w, L)
-        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pool, ps))
-        return ns.top_kappa(s, kappa, pool), pool, s
+        t, s = ns.refine_in_pool(q, kp, bt, g, pool, kappa, ps)
+        return t, pool, s
+
+    def rank_pool(s, pos, rho, kappa):
+        return ns.top_kappa(s, min(rho * kappa, len(pos)), pos)
 
     ns.anchor_select, ns.refined_select = anchor_select, refined_select
+    if "refine_in_pool" not in keep:
+        ns.refine_in_pool = refine_in_pool
+    if "rank_pool" not in keep:
+        ns.rank_pool = rank_pool
     return ns
 
 
@@ -32,7 +44,7 @@ def _impl(**over):
     ns = types.SimpleNamespace(**{n: getattr(oracle, n) for n in oracle.__all__})
     for k, v in over.items():
         setattr(ns, k, v)
-    return _compose(ns)
+    return _compose(ns, keep=tuple(over))
 
 
 def _topk_with(sort_keys):
@@ -83,6 +95,16 @@ MUTANTS = {
     "kappa-1 kept": dict(top_kappa=lambda s, k, p: oracle.top_kappa(s, k, p)[:-1]),
     "output in score order": dict(
         top_kappa=lambda s, k, p: np.asarray(p)[np.lexsort((np.asarray(p), -np.asarray(s)))[:k]]),
+    "rank pool one short": dict(
+        rank_pool=lambda s, p, r, k: oracle.rank_pool(s, p, r, k)[:-1]),
+    "rank pool ignores rho": dict(rank_pool=lambda s, p, r, k: oracle.top_kappa(s, k, p)),
+    "rank pool of the smallest": dict(
+        rank_pool=lambda s, p, r, k: _topk_with(lambda a, b: (b, a))(s, min(r * k, len(p)), p)),
+    "rank pool ties to the higher position": dict(
+        rank_pool=lambda s, p, r, k: _topk_with(lambda a, b: (-b, -a))(s, min(r * k, len(p)), p)),
+    "refinement keeps the pool's first kappa": dict(
+        refine_in_pool=lambda q, kp, bt, g, pool, k, ps: (
+            np.asarray(pool)[:k], oracle.relevance(q, oracle.cache_rows(kp, bt, g, pool, ps)))),
     "window w-1": dict(window_pool=_pool_with(lambda i, w: i - w + 1, lambda i, w: i + w - 1)),
     "window half open": dict(window_pool=_pool_with(lambda i, w: i - w, lambda i, w: i + w, 0)),
     "window left side only": dict(window_pool=_pool_with(lambda i, w: i - w, lambda i, w: i)),
