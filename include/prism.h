@@ -9,8 +9,9 @@
  *     (computed here on the bf16 keys themselves);
  *   - exact top-kappa selection: Eq. 2 (anchor / proposal layers);
  *   - refinement inside a candidate pool: Eqs. 5-6 (refined layers), where the
- *     pool is the union of [i - w, i + w] (clipped to the sequence) over the
- *     anchor layer's selected positions i;
+ *     pool is either the union of [i - w, i + w] (clipped to the sequence) over
+ *     the anchor layer's selected positions i (window pool), or the anchor
+ *     layer's own rho*kappa most relevant tokens (rank-expanded pool, Eq. 4);
  *   - SparseAttn of Algorithm 1: softmax attention of every query head over
  *     its KV head's selected tokens only.
  *
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 1
+#define PRISM_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -94,8 +95,12 @@ typedef struct {
  * anchor_stride  layer l is an anchor (proposal) layer iff l % anchor_stride == 0;
  *                every other layer is refined against the nearest preceding
  *                anchor (the association f of Section 4.1).  >= 1.
- * window         w >= 0 of the refinement pool [i - w, i + w].
+ * window         w >= 0 of the window pool [i - w, i + w] (unused when pool_rho >= 1).
  * softmax_scale  logit scale of SparseAttn; 0 selects 1/sqrt(head_dim).
+ * pool_rho       0: the refined layers' pool is the window pool.  rho >= 1: it is
+ *                the anchor layer's top min(rho * kappa, L) tokens by relevance
+ *                (Eq. 4, the rank-expanded pool); the anchor attends its own
+ *                top-kappa, which lies inside it.  rho * kappa <= 32768.
  * Query head j belongs to KV head j / G.
  */
 typedef struct {
@@ -104,6 +109,7 @@ typedef struct {
   int32_t anchor_stride;
   int32_t window;
   float softmax_scale;
+  int32_t pool_rho;
 } prism_params;
 
 /* Bytes of device workspace every compute entry point needs for these shapes
@@ -133,7 +139,10 @@ PRISM_API prism_status prism_score_topk(const prism_kv_cache* kv, const uint16_t
  * Refined layer selection (Eqs. 5-6): build the pool from the anchor's set,
  * score only the pool's tokens (Eq. 9), keep the top-kappa.
  *   anchor_idx    int32 [batch][num_kv_heads][kappa]: the anchor layer's sets,
- *                 ascending (as prism_score_topk writes them).
+ *                 ascending (as prism_score_topk writes them).  With pool_rho >= 1
+ *                 the pool cannot be rebuilt from the set: the call re-scores the
+ *                 pool that the latest anchor-layer selection left in the
+ *                 workspace, and anchor_idx may be NULL (it is not read).
  *   idx_out       int32 [batch][num_kv_heads][kappa]: ascending positions.
  *   pool_out      optional int32 [batch][num_kv_heads][max_seq_len]: the pool's
  *                 positions, ascending, first pool_len_out[b][g] entries valid.

@@ -36,7 +36,7 @@ def dev(a: np.ndarray) -> torch.Tensor:
 class Setup:
     """Seeded inputs of some layers of a workload, resident on the device."""
 
-    def __init__(self, wl: synth.Workload, layers):
+    def __init__(self, wl: synth.Workload, layers, pool_rho=0):
         self.wl = wl
         self.pg = synth.paging(wl)
         self.bt = dev(self.pg.block_table)
@@ -50,7 +50,9 @@ class Setup:
             self.kv[l] = tsa.KVCache(dev(li.k_pages), dev(li.v_pages), self.bt, self.sl,
                                      max_seq_len=int(self.pg.seq_lens.max()),
                                      min_seq_len=int(self.pg.seq_lens.min()))
-        self.params = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window)
+        self.pool_rho = pool_rho
+        self.params = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window,
+                                 pool_rho=pool_rho)
         first = next(iter(self.kv.values()))
         self.ws = torch.empty(tsa.prism_workspace_size(first, self.params), dtype=torch.uint8,
                               device="cuda")
@@ -82,6 +84,17 @@ class Setup:
         return oracle.refined_select(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
                                      int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size,
                                      np.asarray(anchor, np.int64), self.wl.window)
+
+    def oracle_rank_pool(self, anchor_scores, b):
+        """Eq. 4 on the anchor layer's oracle scores over the whole cache."""
+        L = int(self.pg.seq_lens[b])
+        return oracle.rank_pool(anchor_scores, np.arange(L), self.pool_rho, self.wl.kappa)
+
+    def oracle_refine_in_pool(self, l, b, g, pool):
+        li = self.host[l]
+        return oracle.refine_in_pool(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
+                                     np.asarray(pool, np.int64), self.wl.kappa,
+                                     self.wl.page_size)
 
     def oracle_attend(self, l, b, g, sel):
         li = self.host[l]

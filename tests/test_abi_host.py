@@ -20,7 +20,8 @@ def _kv(**over):
 
 
 def _params(**over):
-    d = dict(num_q_heads=32, kappa=2048, anchor_stride=8, window=32, softmax_scale=0.0)
+    d = dict(num_q_heads=32, kappa=2048, anchor_stride=8, window=32, softmax_scale=0.0,
+             pool_rho=0)
     d.update(over)
     return L.ParamsStruct(*[d[n] for n, _ in L.ParamsStruct._fields_])
 
@@ -53,7 +54,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 1
+    assert tsa.prism_abi_version() == 2
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -92,6 +93,8 @@ CASES = [
     ("negative window", dict(p=_params(window=-1)), L.PRISM_ERR_INVALID_ARG),
     ("stride 0", dict(p=_params(anchor_stride=0)), L.PRISM_ERR_INVALID_ARG),
     ("nan scale", dict(p=_params(softmax_scale=float("nan"))), L.PRISM_ERR_INVALID_ARG),
+    ("negative pool_rho", dict(p=_params(pool_rho=-1)), L.PRISM_ERR_INVALID_ARG),
+    ("rank pool above 32768", dict(p=_params(pool_rho=17)), L.PRISM_ERR_UNSUPPORTED),
     ("misaligned k", dict(kv=_kv(k_pages=FAKE + 2)), L.PRISM_ERR_INVALID_ARG),
     ("null workspace", dict(ws=None), L.PRISM_ERR_WORKSPACE),
     ("misaligned workspace", dict(ws=FAKE + 16), L.PRISM_ERR_WORKSPACE),
@@ -142,3 +145,20 @@ def test_profile_hook_argument_checks():
     assert lib.prism_profile_launches(0) == 0
     assert lib.prism_profile_launches(42) == -1
     assert lib.prism_profile_launches(3) == 0
+
+
+def test_refine_anchor_idx_needed_for_the_window_pool_only():
+    """With the window pool the pool is built from anchor_idx (NULL rejected);
+    with the rank-expanded pool the call re-scores the pool in the workspace
+    and anchor_idx is not read (NULL accepted; without a GPU the call then
+    fails on the device check)."""
+    import torch
+    lib = tsa.lib()
+    kv = _kv()
+    pw, pr = _params(), _params(pool_rho=4)
+    assert lib.prism_refine_topk(ctypes.byref(kv), FAKE, ctypes.byref(pw), None, FAKE, None, None,
+                                 None, FAKE, 1 << 40, None) == L.PRISM_ERR_INVALID_ARG
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
+    assert lib.prism_refine_topk(ctypes.byref(kv), FAKE, ctypes.byref(pr), None, FAKE, None, None,
+                                 None, FAKE, 1 << 40, None) == L.PRISM_ERR_HIP

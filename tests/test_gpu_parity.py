@@ -316,6 +316,83 @@ def test_decode_chain_per_problem_selection():
     _run_chain(st, range(3), probs, "per-problem")
 
 
+def _gpu_pool(st, l):
+    """The pool the latest anchor selection left in the workspace, read through
+    prism_refine_topk (rank-expanded pool: anchor_idx is not read), which also
+    re-scores it with layer l's query and returns that selection."""
+    wl = st.wl
+    L_max = int(st.pg.seq_lens.max())
+    sel = st.idx_buf()
+    pool = torch.full((wl.batch, wl.num_kv_heads, L_max), -7, dtype=torch.int32, device="cuda")
+    plen = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32, device="cuda")
+    tsa.prism_refine_topk(st.kv[l], st.q[l], st.params, None, sel, pool, plen, None, st.ws)
+    torch.cuda.synchronize()
+    return pool.cpu().numpy(), plen.cpu().numpy(), sel.cpu().numpy()
+
+
+def _run_chain_rank(st, layers, problems, label):
+    """prism_decode_layer with the rank-expanded pool: each anchor layer's set
+    and pool against the oracle (the pool by the same near-tie rule at its
+    rho*kappa boundary), each refined layer against the oracle re-scoring the
+    GPU's own pool, the attention on the GPU's sets."""
+    wl = st.wl
+    anchor, layer_idx, out = st.idx_buf(), st.idx_buf(), st.out_buf()
+    stats = {"exact": 0, "near-tie": 0}
+    pool_gpu = plen_gpu = None
+    for l in layers:
+        say(f"[{label}] layer {l} ({'anchor' if wl.is_anchor(l) else 'refined'})")
+        tsa.prism_decode_layer(l, st.kv[l], st.q[l], st.params, anchor, layer_idx, out, st.ws)
+        torch.cuda.synchronize()
+        sel, o = layer_idx.cpu().numpy(), out.cpu().numpy()
+        if wl.is_anchor(l):
+            assert np.array_equal(anchor.cpu().numpy(), sel)
+            pool_gpu, plen_gpu, _ = _gpu_pool(st, l)
+        for b, g in problems:
+            L = int(st.pg.seq_lens[b])
+            where = f"{label} l{l} b{b} g{g}"
+            if wl.is_anchor(l):
+                want, s = st.oracle_anchor(l, b, g)
+                stats[check_set(sel[b, g], want, s, np.arange(L), wl.kappa, where)] += 1
+                m = min(st.pool_rho * wl.kappa, L)
+                assert plen_gpu[b, g] == m, (where, plen_gpu[b, g], m)
+                gp = pool_gpu[b, g, :m]
+                wp = st.oracle_rank_pool(s, b)
+                stats[check_set(gp, wp, s, np.arange(L), m, where + " pool")] += 1
+                assert np.isin(sel[b, g], gp).all(), where + ": set outside its pool"
+            else:
+                gp = pool_gpu[b, g, :plen_gpu[b, g]]
+                want, s = st.oracle_refine_in_pool(l, b, g, gp)
+                stats[check_set(sel[b, g], want, s, gp, wl.kappa, where)] += 1
+            G = wl.group
+            check_attn(o[b, g * G:(g + 1) * G], st.oracle_attend(l, b, g, sel[b, g]), where)
+    say(f"[{label}] sets: {stats}")
+    return stats
+
+
+@pytest.mark.parametrize("rho", [1, 4, 16])
+def test_decode_chain_rank_pool(rho):
+    """Rank-expanded pool (Eq. 4) through prism_decode_layer on a ragged batch:
+    lists selected in registers and after classification, and a sequence whose
+    pool is its whole cache at rho = 16 (rho * kappa >= L)."""
+    wl = synth.scaled(synth.TINY_4K, name=f"rank-pool-{rho}", wid=194, num_q_heads=32,
+                      num_kv_heads=8, batch=3, context=None, lengths=(6016, 20032, 40000),
+                      kappa=512, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=rho)
+    probs = [(b, g) for b in range(wl.batch) for g in (0, 5)]
+    _run_chain_rank(st, range(3), probs, f"rank-pool rho={rho}")
+
+
+def test_decode_chain_rank_pool_per_problem_selection():
+    """Rank-expanded pool on a grid above the CU count (refined layers select
+    once per problem, pools longer than 16384 entries classified first), G = 8."""
+    wl = synth.scaled(synth.TINY_4K, name="rank-pool-pp", wid=195, num_q_heads=64,
+                      num_kv_heads=8, batch=4, context=None, lengths=(20032, 36032, 24000, 30016),
+                      kappa=1100, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=16)
+    probs = [(0, 1), (1, 4), (2, 6), (3, 7)]
+    _run_chain_rank(st, range(3), probs, "rank-pool per-problem")
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []

@@ -35,7 +35,7 @@ class KVCacheStruct(ctypes.Structure):
 class ParamsStruct(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("kappa", ctypes.c_int32),
                 ("anchor_stride", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("pool_rho", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -151,9 +151,12 @@ class KVCache:
                        min_seq_len=s.min_seq_len, head_dim=s.head_dim, page_size=s.page_size)
 
 
-def params(num_q_heads, kappa, anchor_stride=1, window=0, softmax_scale=0.0) -> ParamsStruct:
+def params(num_q_heads, kappa, anchor_stride=1, window=0, softmax_scale=0.0,
+           pool_rho=0) -> ParamsStruct:
+    """prism_params; pool_rho >= 1 selects the rank-expanded pool (the anchor's
+    top pool_rho * kappa tokens) instead of the window pool."""
     return ParamsStruct(int(num_q_heads), int(kappa), int(anchor_stride), int(window),
-                        float(softmax_scale))
+                        float(softmax_scale), int(pool_rho))
 
 
 def _ws(workspace):
@@ -185,7 +188,8 @@ def prism_refine_topk(kv, q, p, anchor_idx, idx_out, pool_out=None, pool_len_out
     ws, nbytes = _ws(workspace)
     _check(lib().prism_refine_topk(
         ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2), ctypes.byref(p),
-        _ptr(anchor_idx, "anchor_idx", itemsize=4), _ptr(idx_out, "idx_out", itemsize=4),
+        _ptr(anchor_idx, "anchor_idx", itemsize=4, optional=p.pool_rho >= 1),
+        _ptr(idx_out, "idx_out", itemsize=4),
         _ptr(pool_out, "pool_out", itemsize=4, optional=True),
         _ptr(pool_len_out, "pool_len_out", itemsize=4, optional=True),
         _ptr(pool_scores_out, "pool_scores_out", itemsize=4, optional=True),

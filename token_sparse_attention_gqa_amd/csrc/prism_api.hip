@@ -50,6 +50,9 @@ prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* 
     return fail(PRISM_ERR_INVALID_ARG, "need 1 <= kappa <= min_seq_len");
   if (p->kappa > prism::kMaxKappa) return fail(PRISM_ERR_UNSUPPORTED, "kappa above 8192");
   if (p->window < 0) return fail(PRISM_ERR_INVALID_ARG, "window must be >= 0");
+  if (p->pool_rho < 0) return fail(PRISM_ERR_INVALID_ARG, "pool_rho must be >= 0");
+  if ((int64_t)p->pool_rho * p->kappa > prism::kMaxRankPool)
+    return fail(PRISM_ERR_UNSUPPORTED, "pool_rho * kappa above 32768");
   if (p->anchor_stride < 1) return fail(PRISM_ERR_INVALID_ARG, "anchor_stride must be >= 1");
   if (!std::isfinite(p->softmax_scale))
     return fail(PRISM_ERR_INVALID_ARG, "softmax_scale must be finite");
@@ -72,6 +75,7 @@ prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* 
   g->n_cap = (kv->max_seq_len + 63) / 64 * 64;
   g->kappa = p->kappa;
   g->window = p->window;
+  g->pool_rho = p->pool_rho;
   g->splits = (p->kappa + prism::kAttnSplit - 1) / prism::kAttnSplit;
   g->page_stride = (size_t)kv->num_kv_heads * prism::kPageSize * prism::kHeadDim;
   return PRISM_OK;
@@ -155,7 +159,11 @@ prism_status prism_score_topk(const prism_kv_cache* kv, const uint16_t* q,
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  PRISM_TRY(run_anchor(g, w, q, idx_out, nullptr, s));
+  if (g.pool_rho >= 1)
+    PRISM_TRY(hip_check(prism::launch_anchor_rank(g, w, q, idx_out, nullptr, s),
+                        "anchor selection launch"));
+  else
+    PRISM_TRY(run_anchor(g, w, q, idx_out, nullptr, s));
   if (scores_out)
     PRISM_TRY(copy_rows(scores_out, (size_t)g.max_seq_len * 4, w.scores, (size_t)g.n_cap * 4,
                         (size_t)g.max_seq_len * 4, (size_t)g.problems(), s, "scores copy"));
@@ -170,13 +178,15 @@ prism_status prism_refine_topk(const prism_kv_cache* kv, const uint16_t* q,
   Geometry g;
   PRISM_TRY(resolve(kv, params, &g));
   PRISM_TRY(check_q(q));
-  if (!anchor_idx || !idx_out)
-    return fail(PRISM_ERR_INVALID_ARG, "anchor_idx and idx_out must not be NULL");
+  if (!idx_out) return fail(PRISM_ERR_INVALID_ARG, "idx_out must not be NULL");
+  if (!anchor_idx && g.pool_rho < 1)
+    return fail(PRISM_ERR_INVALID_ARG, "anchor_idx must not be NULL for the window pool");
   PRISM_TRY(check_ws(g, workspace, workspace_bytes));
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  PRISM_TRY(hip_check(prism::launch_pool_build(g, w, anchor_idx, s), "pool build launch"));
+  if (g.pool_rho < 1)  // the rank-expanded pool is the one the anchor selection left
+    PRISM_TRY(hip_check(prism::launch_pool_build(g, w, anchor_idx, s), "pool build launch"));
   PRISM_TRY(hip_check(prism::launch_refine(g, w, q, idx_out, s), "refined selection launch"));
   const size_t rowb = (size_t)g.max_seq_len * 4, caprow = (size_t)g.n_cap * 4;
   if (pool_out)
@@ -219,10 +229,18 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   PRISM_TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
-  if (layer % params->anchor_stride == 0)
+  if (layer % params->anchor_stride == 0) {
+    if (g.pool_rho >= 1) {
+      PRISM_TRY(hip_check(prism::launch_anchor_rank(g, w, q, anchor_idx, layer_idx_out, s),
+                          "anchor layer launch"));
+      return hip_check(prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params),
+                                               out, s),
+                       "anchor layer attention launch");
+    }
     return hip_check(prism::launch_anchor_attend(g, w, q, resolve_scale(params), anchor_idx,
                                                  layer_idx_out, out, s),
                      "anchor layer launch");
+  }
   return hip_check(
       prism::launch_refine_attend(g, w, q, resolve_scale(params), layer_idx_out, out, s),
       "refined layer launch");

@@ -13,6 +13,7 @@ constexpr int kPageSize = 64;         // tokens per page
 constexpr int kSelThreads = 1024;     // threads of a selection workgroup
 constexpr int kScoreThreads = 256;    // threads of a relevance workgroup
 constexpr int kAnchorEntries = 1024;  // cached tokens scored by one anchor-layer workgroup
+constexpr int kMaxRankPool = 32768;  // largest rank-expanded pool (rho * kappa)
 constexpr int kPoolEntries = 256;     // pool entries scored by one refined-layer workgroup
 constexpr int kAttnSplit = 64;        // selected tokens attended by one workgroup
 constexpr int kAttnThreads = 256;
@@ -38,6 +39,7 @@ struct Geometry {
   int n_cap;        // per-problem list capacity: max_seq_len rounded up to 64
   int kappa;
   int window;
+  int pool_rho;     // 0: window pool; >= 1: rank-expanded pool of pool_rho * kappa tokens
   int splits;       // attention splits per problem
   size_t page_stride;  // elements per physical page: hkv * page * head_dim
   __host__ __device__ int problems() const { return batch * hkv; }
@@ -102,6 +104,10 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
 // Refined layer of a decode step: pool scoring, then selection and SparseAttn
 // (pools of at most 8192 entries are selected inside the attention kernel).
 // layer_idx (nullable) receives the layer's set.
+// Anchor layer with the rank-expanded pool: scoring, classification of long
+// lists for rho*kappa, the pool and the anchor set (out, out2, row ids).
+hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
+                              int32_t* out, int32_t* out2, hipStream_t s);
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with

@@ -37,6 +37,7 @@ constexpr int NT = kSelThreads;
 constexpr int kSmall = 16384;   // lists up to this length are selected with every key in registers
 constexpr int kSmallPer = kSmall / kSelThreads;  // 16 consecutive entries per thread
 constexpr int kRegMarks = 2 * kSmall;  // fused refined kernel: pools held 32 keys per thread
+static_assert(kMaxRankPool <= kRegMarks, "a rank-expanded pool is selected from registers");
 constexpr int kSample = 8192;   // most entries of a longer list sampled to bracket the kappa-th key
 constexpr int kCand = 4096;     // bracketed candidates held in LDS
 constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the list pass
@@ -1328,14 +1329,15 @@ __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws
 }
 
 // Lists longer than kSmall (the cache at an anchor layer, the pool at a refined
-// layer with `pool`): workgroup w of problem p takes list entries
+// layer with `pool`), of which the need_k largest are wanted (kappa, or the
+// size of a rank-expanded pool): workgroup w of problem p takes list entries
 // [w * kClsEntries, +kClsEntries).  From the problem's coarse histogram it
 // finds the bin holding the kappa-th score (every workgroup finds the same
 // bin; workgroup 0 records it with the count of entries above it and in it),
 // marks its entries above that bin in the workspace bitmap and appends the
 // bin's own entries, with their keys, to the problem's candidate list.
 __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs,
-                                                               int pool) {
+                                                               int pool, int need_k) {
   __shared__ int tmp[kClsThreads / 64];
   __shared__ int res[3];
   int p, w;
@@ -1343,7 +1345,8 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
   const int b = p / g.hkv;
   const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : seq_len_of(g, b);
   const int base = w * kClsEntries;
-  if (n <= kSmall || n <= g.kappa || base >= n) return;  // uniform over the workgroup
+  const int need = min(need_k, n);  // entries to select: kappa, or the rank pool's size
+  if (n <= kSmall || n <= need || base >= n) return;  // uniform over the workgroup
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float* sc = ws.scores + (size_t)p * g.n_cap;
   constexpr int U = kClsEntries / (4 * kClsThreads);
@@ -1370,7 +1373,6 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
   }
   int tot;
   const int above_t = block_excl_scan<kClsThreads>(sum, tmp, &tot);
-  const int need = g.kappa;
   if (above_t < need && need <= above_t + sum) {
     int a = above_t, bin = -1, cnt = 0;
 #pragma unroll
@@ -2131,6 +2133,121 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Anchor layer with the rank-expanded pool (Eq. 4): the pool that the refined
+// layers re-score is the anchor's own top rho*kappa tokens, and the anchor
+// attends its top-kappa, which lies inside that pool.  One workgroup per
+// problem, after scoring (and, for lists longer than kSmall, classification
+// with rho*kappa wanted): the pool's marks over the cache, the pool in
+// position order (positions, row ids, length), then the top-kappa of the
+// pool's scores as the anchor set (positions to out / out2, row ids for the
+// attention).  Leaves the selection counters at zero.
+// ---------------------------------------------------------------------------
+template <int R>
+__device__ void select_in_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int m,
+                               int32_t* out, int32_t* out2, SelectSmem& sm) {
+  const int t = threadIdx.x, K = g.kappa;
+  const size_t base = (size_t)p * g.n_cap;
+  const int e0 = R * t;
+  const int nv = clampi(m - e0, 0, R);
+  uint32_t pos[R], key[R];
+  load_run<R>(ws.pool_pos + base, min(e0, g.n_cap - R), pos);  // n_cap is a multiple of 64
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int e = clampi((int)pos[i], 0, g.n_cap - 1);
+    key[i] = i < nv ? order_key(ws.scores[base + e]) : 0u;
+  }
+  const uint32_t take = top_k_mask<R>(key, nv, m, K, sm);
+  int total;
+  int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
+  int32_t* o1 = out + (size_t)p * K;
+  int32_t* o2 = out2 ? out2 + (size_t)p * K : nullptr;
+  uint32_t* sr = ws.sel_row + (size_t)p * K;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    if (take & (1u << i)) {
+      if (o < K) {
+        const int ps = clampi((int)pos[i], 0, kMaxSeqLen - 1);
+        o1[o] = ps;
+        if (o2) o2[o] = ps;
+        sr[o] = row_id_of_page(g, sm.bt[ps >> 6], kvh, ps);
+      }
+      ++o;
+    }
+  }
+  for (int o3 = total + t; o3 < K; o3 += NT) {
+    o1[o3] = -1;
+    if (o2) o2[o3] = -1;
+    sr[o3] = kNoRow;
+  }
+}
+
+__global__ __launch_bounds__(NT) void rank_pool_kernel(Geometry g, Workspace ws,
+                                                       int32_t* __restrict__ out,
+                                                       int32_t* __restrict__ out2) {
+  __shared__ SelectSmem sm;
+  const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
+  const int t = threadIdx.x;
+  const int L = seq_len_of(g, b);
+  const int m = min(g.pool_rho * g.kappa, L);  // the pool's size
+  const size_t base = (size_t)p * g.n_cap;
+  load_bt(g, b, L, sm.bt);
+  // 1. the pool's marks: the m largest scores of the cache
+  SelList c;
+  c.sc = ws.scores + base;
+  c.plist = nullptr;
+  c.prow = nullptr;
+  c.n = L;
+  c.K = m;
+  c.b = b;
+  c.kvh = kvh;
+  c.o1 = c.o2 = nullptr;
+  c.srow = nullptr;
+  if (m >= L) {
+    for (int i = t; i < ((L + 31) >> 5); i += NT)
+      sm.bitmap[i] = (32 * i + 32 <= L) ? 0xFFFFFFFFu : ((1u << (L & 31)) - 1u);
+    lds_barrier();
+  } else if (L <= kSmall / 2) {
+    small_marks<kSmallPer / 2>(c.sc, L, m, sm);
+  } else if (L <= kSmall) {
+    small_marks<kSmallPer>(c.sc, L, m, sm);
+  } else {
+    classified_marks(g, ws, p, c, sm);  // after classify_kernel with need m
+  }
+  // 2. the pool in position order
+  int pool_n;
+  {
+    const int words = (L + 31) >> 5;
+    const int wpt = (words + NT - 1) / NT;
+    const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+    int cnt = 0;
+    for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
+    int o = block_excl_scan<NT>(cnt, sm.tmp, &pool_n);
+    int32_t* pp = ws.pool_pos + base;
+    uint32_t* pr = ws.pool_row + base;
+    for (int i = w0; i < w1; ++i) {
+      uint32_t mk = sm.bitmap[i];
+      while (mk) {
+        const int e = i * 32 + (__ffs(mk) - 1);
+        mk &= mk - 1u;
+        if (o < g.n_cap) {
+          pp[o] = e;
+          pr[o] = row_id_of_page(g, sm.bt[e >> 6], kvh, e);
+        }
+        ++o;
+      }
+    }
+    if (t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
+  }
+  __syncthreads();  // the pool's global stores are visible to the whole workgroup
+  // 3. the anchor set: the top-kappa of the pool
+  const int mm = min(pool_n, kRegMarks);
+  if (mm <= kSmall / 2) select_in_pool<kSmallPer / 2>(g, ws, p, kvh, mm, out, out2, sm);
+  else if (mm <= kSmall) select_in_pool<kSmallPer>(g, ws, p, kvh, mm, out, out2, sm);
+  else select_in_pool<kRegMarks / NT>(g, ws, p, kvh, mm, out, out2, sm);
+  reset_selection_counters(ws, p);
+}
+
 struct ProfileRing {
   std::vector<hipEvent_t> starts, stops;
   int64_t launches = 0;
@@ -2309,11 +2426,33 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           0);
+           0, g.kappa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
+  return hipGetLastError();
+}
+
+hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
+                              int32_t* out, int32_t* out2, hipStream_t s) {
+  const int nz = g.problems() * (kCoarseBins + 1);
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
+                     w.ghist, nz);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long m = (long long)g.pool_rho * g.kappa;
+  if (g.max_seq_len > kSmall && g.max_seq_len > m) {
+    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
+           0, (int)m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  launch(kSelect, rank_pool_kernel, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
   return hipGetLastError();
 }
 
@@ -2345,7 +2484,7 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           0);
+           0, g.kappa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2368,11 +2507,13 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
 // Refined layer without the fused kernel: score the pool (counting pools longer
 // than kSmall per coarse bin), classify those pools over many workgroups, then
 // select per problem.  The pool's length is known on the device only; its
-// bound min(n_cap, kappa (2w + 1)) decides whether classification can be
-// needed at all.
+// bound (min(n_cap, kappa (2w + 1)) for the window pool, min(n_cap, rho kappa)
+// for the rank-expanded one) decides whether classification can be needed.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          hipStream_t s) {
-  const long long bound = std::min<long long>(g.n_cap, (long long)g.kappa * (2LL * g.window + 1));
+  const long long bound =
+      std::min<long long>(g.n_cap, g.pool_rho >= 1 ? (long long)g.pool_rho * g.kappa
+                                                   : (long long)g.kappa * (2LL * g.window + 1));
   const bool classify = bound > kSmall && bound > g.kappa;
   PRISM_BY_GROUP(launch_pool_score_g, g, w, q, classify, s);
   hipError_t e = hipGetLastError();
@@ -2380,7 +2521,7 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
   if (classify) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           1);
+           1, g.kappa);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
