@@ -69,7 +69,7 @@ class Hip:
             self.rt.hipEventDestroy(e)
 
 
-def launches_per_step(wl, cus):
+def launches_per_step(wl, cus, pool_rho=0):
     """Kernel launches of each kind in one decode step, mirroring the library's
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
@@ -81,14 +81,17 @@ def launches_per_step(wl, cus):
     nr = wl.num_layers - na
     L = int(synth.paging(wl).seq_lens.max())
     fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * -(-wl.kappa // 128) <= cus
-    anchor_fused = fused and L <= 6144 * 32
+    anchor_fused = fused and L <= 6144 * 32 and pool_rho < 1  # rank pools: per problem
     n_cap = -(-L // 64) * 64
-    pool_bound = min(n_cap, wl.kappa * (2 * wl.window + 1))
+    pool_bound = min(n_cap, pool_rho * wl.kappa if pool_rho >= 1
+                     else wl.kappa * (2 * wl.window + 1))
     pool_classify = not fused and pool_bound > 16384 and pool_bound > wl.kappa
+    anchor_need = pool_rho * wl.kappa if pool_rho >= 1 else wl.kappa
     return {"anchor_score": na, "refine_score": nr,
             "select": (0 if anchor_fused else na) + (0 if fused else nr),
             "attention": wl.num_layers,
-            "classify": (na if (L > 16384 and L > wl.kappa) else 0) + (nr if pool_classify else 0),
+            "classify": (na if (L > 16384 and L > anchor_need) else 0)
+                        + (nr if pool_classify else 0),
             "merge": wl.num_layers}
 
 
@@ -113,7 +116,7 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, host, seconds):
+def cpu_baseline(wl, host, seconds, pool_rho=0):
     """The CPU oracle, as it stands, on a bounded sample of the workload: one
     anchor layer and one refined layer for as many (sequence, KV head) problems
     as fit in about `seconds`, extrapolated to a whole decode step."""
@@ -135,14 +138,19 @@ def cpu_baseline(wl, host, seconds):
     for b, g in probs:
         L = int(pg.seq_lens[b])
         t0 = time.perf_counter()
-        A, _ = oracle.anchor_select(qa[b, g * G:(g + 1) * G], host[la].k_pages,
-                                    pg.block_table[b], g, L, wl.kappa, wl.page_size)
+        A, sa = oracle.anchor_select(qa[b, g * G:(g + 1) * G], host[la].k_pages,
+                                     pg.block_table[b], g, L, wl.kappa, wl.page_size)
+        pool = oracle.rank_pool(sa, np.arange(L), pool_rho, wl.kappa) if pool_rho >= 1 else None
         oracle.attend(qa[b, g * G:(g + 1) * G], host[la].k_pages, host[la].v_pages,
                       pg.block_table[b], g, A, wl.page_size, oracle.default_scale(wl.head_dim))
         t1 = time.perf_counter()
-        T, _, _ = oracle.refined_select(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
-                                        pg.block_table[b], g, L, wl.kappa, wl.page_size, A,
-                                        wl.window)
+        if pool is not None:
+            T, _ = oracle.refine_in_pool(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
+                                         pg.block_table[b], g, pool, wl.kappa, wl.page_size)
+        else:
+            T, _, _ = oracle.refined_select(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
+                                            pg.block_table[b], g, L, wl.kappa, wl.page_size, A,
+                                            wl.window)
         oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
                       pg.block_table[b], g, T, wl.page_size, oracle.default_scale(wl.head_dim))
         t2 = time.perf_counter()
@@ -170,6 +178,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama3-8b-128k-planted")
+    ap.add_argument("--pool-rho", type=int, default=0, metavar="RHO",
+                    help="refined layers re-score the anchor's top RHO*kappa tokens (Eq. 4) "
+                         "instead of the +-w window pool (0, the default)")
     ap.add_argument("--distinct-layers", type=int, default=0, metavar="N",
                     help="generate only N layers' inputs and give layer l those of layer l mod N "
                          "(for workloads whose full KV cache does not fit host memory for "
@@ -238,7 +249,8 @@ def main():
                 f"{time.perf_counter() - t0:.1f} s)")
     torch.cuda.synchronize()
 
-    p = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window)
+    p = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window,
+                   pool_rho=args.pool_rho)
     ws = torch.empty(tsa.prism_workspace_size(kv_dev[0], p), dtype=torch.uint8, device=dev)
     anchor = torch.zeros((wl.batch, wl.num_kv_heads, wl.kappa), dtype=torch.int32, device=dev)
     outs = torch.zeros((wl.num_layers, wl.batch, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
@@ -294,7 +306,8 @@ def main():
 
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
-    per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count)
+    per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
+                                 args.pool_rho)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -377,7 +390,9 @@ def main():
                    "head_dim": wl.head_dim, "layers": wl.num_layers,
                    "anchor_stride": wl.anchor_stride, "kappa": wl.kappa, "window": wl.window,
                    "page_size": wl.page_size,
-                   **({"distinct_layers": nd} if nd < wl.num_layers else {})},
+                   **({"distinct_layers": nd} if nd < wl.num_layers else {}),
+                   **({"pool": "rank", "pool_rho": args.pool_rho} if args.pool_rho >= 1
+                      else {"pool": "window"})},
         "roofline": roofline,
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
@@ -392,7 +407,7 @@ def main():
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cb = cpu_baseline(wl, host_keep, args.cpu_seconds)
+        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho)
         result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
     else:
