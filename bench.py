@@ -69,16 +69,24 @@ class Hip:
             self.rt.hipEventDestroy(e)
 
 
-def launches_per_step(wl, cus, pool_rho=0):
+def layer_roles(wl, pattern=None):
+    """One letter per layer: F (proposal / anchor), R (refined), S (shared)."""
+    if pattern:
+        return list(pattern)
+    return ["F" if wl.is_anchor(l) else "R" for l in range(wl.num_layers)]
+
+
+def launches_per_step(wl, cus, pool_rho=0, roles=None):
     """Kernel launches of each kind in one decode step, mirroring the library's
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
     196608), else a selection kernel per layer precedes the attention, and a
-    refined layer whose pool can exceed 16384 entries is classified first."""
+    refined layer whose pool can exceed 16384 entries is classified first.
+    Shared layers launch the attention and its merge only."""
     import synth
-    na = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
-    nr = wl.num_layers - na
+    roles = roles or layer_roles(wl)
+    na, nr = roles.count("F"), roles.count("R")
     L = int(synth.paging(wl).seq_lens.max())
     fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * -(-wl.kappa // 128) <= cus
     anchor_fused = fused and L <= 6144 * 32 and pool_rho < 1  # rank pools: per problem
@@ -116,10 +124,11 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, host, seconds, pool_rho=0):
+def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None):
     """The CPU oracle, as it stands, on a bounded sample of the workload: one
-    anchor layer and one refined layer for as many (sequence, KV head) problems
-    as fit in about `seconds`, extrapolated to a whole decode step."""
+    anchor layer and one refined layer (and the attention alone, for shared
+    layers) for as many (sequence, KV head) problems as fit in about
+    `seconds`, extrapolated to a whole decode step."""
     import numpy as np
     import oracle
     import synth
@@ -133,7 +142,7 @@ def cpu_baseline(wl, host, seconds, pool_rho=0):
     la, lr = 0, 1
     qa, qr = oracle.bf16_to_f64(host[la].q), oracle.bf16_to_f64(host[lr].q)
     probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
-    ta, tr, done = [], [], 0
+    ta, tr, ts, done = [], [], [], 0
     t_start = time.perf_counter()
     for b, g in probs:
         L = int(pg.seq_lens[b])
@@ -154,21 +163,30 @@ def cpu_baseline(wl, host, seconds, pool_rho=0):
         oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
                       pg.block_table[b], g, T, wl.page_size, oracle.default_scale(wl.head_dim))
         t2 = time.perf_counter()
+        if roles is not None and "S" in roles:   # a shared layer: attention over A only
+            oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
+                          pg.block_table[b], g, A, wl.page_size,
+                          oracle.default_scale(wl.head_dim))
+        t3 = time.perf_counter()
         ta.append(t1 - t0)
         tr.append(t2 - t1)
+        ts.append(t3 - t2)
         done += 1
         if time.perf_counter() - t_start > seconds:
             break
-    n_anchor = sum(1 for l in range(wl.num_layers) if wl.is_anchor(l))
-    n_ref = wl.num_layers - n_anchor
+    roles = roles or [("F" if wl.is_anchor(l) else "R") for l in range(wl.num_layers)]
+    n_anchor, n_ref, n_sh = roles.count("F"), roles.count("R"), roles.count("S")
     P = len(probs)
-    step_s = P * (n_anchor * float(np.mean(ta)) + n_ref * float(np.mean(tr)))
+    step_s = P * (n_anchor * float(np.mean(ta)) + n_ref * float(np.mean(tr))
+                  + n_sh * float(np.mean(ts)))
     return {"value": wl.batch / step_s, "unit": "tokens/s", "cores": int(blas_threads),
             "kind": "oracle",
             "sample": (f"oracle (numpy float64) on layer {la} (anchor) and layer {lr} (refined) "
                        f"for {done} of {P} (sequence, KV head) problems "
                        f"({time.perf_counter() - t_start:.1f} s); per-problem times "
-                       f"extrapolated to {n_anchor} anchor + {n_ref} refined layers x {P} problems"),
+                       f"extrapolated to {n_anchor} anchor + {n_ref} refined"
+                       + (f" + {n_sh} shared (attention only)" if n_sh else "")
+                       + f" layers x {P} problems"),
             "ms_per_step": step_s * 1e3}
 
 
@@ -181,6 +199,10 @@ def main():
     ap.add_argument("--pool-rho", type=int, default=0, metavar="RHO",
                     help="refined layers re-score the anchor's top RHO*kappa tokens (Eq. 4) "
                          "instead of the +-w window pool (0, the default)")
+    ap.add_argument("--pattern", default="", metavar="LETTERS",
+                    help="layer roles, one letter per layer: F proposal (anchor), R refined, "
+                         "S shared (reuses the nearest F or R layer's set); default: every "
+                         "anchor_stride-th layer F, the others R")
     ap.add_argument("--distinct-layers", type=int, default=0, metavar="N",
                     help="generate only N layers' inputs and give layer l those of layer l mod N "
                          "(for workloads whose full KV cache does not fit host memory for "
@@ -218,6 +240,13 @@ def main():
 
     wl = synth.BY_NAME[args.workload]
     pg = synth.paging(wl)
+    if args.pattern:
+        bad = [l for l in range(len(args.pattern)) if tsa.prism_pattern_role(args.pattern, l) < 0]
+        if bad or len(args.pattern) != wl.num_layers:
+            print(f"--pattern must be {wl.num_layers} letters F/R/S starting with F",
+                  file=sys.stderr, flush=True)
+            sys.exit(2)
+    roles = layer_roles(wl, args.pattern)
     dev = torch.device("cuda:0")
     tsa.lib()
     hip = Hip()
@@ -263,10 +292,16 @@ def main():
                   for l in range(wl.num_layers)]
     anchor_ptr = anchor.data_ptr()
 
+    role_ids = [tsa.ROLES[c] for c in roles]
+
     def step():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while recording
-        for l, (kv, qp, op) in enumerate(layer_args):
-            tsa.prism_decode_layer(l, kv, qp, p, anchor_ptr, None, op, ws_arg, s)
+        if args.pattern:
+            for (kv, qp, op), r in zip(layer_args, role_ids):
+                tsa.prism_decode_layer_role(r, kv, qp, p, anchor_ptr, op, ws_arg, s)
+        else:
+            for l, (kv, qp, op) in enumerate(layer_args):
+                tsa.prism_decode_layer(l, kv, qp, p, anchor_ptr, None, op, ws_arg, s)
 
     for _ in range(args.warmup):
         step()
@@ -307,7 +342,7 @@ def main():
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
     per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
-                                 args.pool_rho)
+                                 args.pool_rho, roles)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -346,9 +381,9 @@ def main():
     tmp_idx = torch.zeros_like(anchor)
     pool_bytes = []
     for l in range(wl.num_layers):
-        if wl.is_anchor(l):
+        if roles[l] == "F":
             tsa.prism_score_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, None, ws)
-        else:
+        elif roles[l] == "R":
             tsa.prism_refine_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, tmp_idx, None, pool_len,
                                   None, ws)
             pool_bytes.append(int(pool_len.sum().item()) * D2)
@@ -388,7 +423,9 @@ def main():
         "config": {"workload": wl.name, "batch": wl.batch, "context": L_max,
                    "q_heads": wl.num_q_heads, "kv_heads": wl.num_kv_heads,
                    "head_dim": wl.head_dim, "layers": wl.num_layers,
-                   "anchor_stride": wl.anchor_stride, "kappa": wl.kappa, "window": wl.window,
+                   **({"layer_roles": args.pattern} if args.pattern
+                      else {"anchor_stride": wl.anchor_stride}),
+                   "kappa": wl.kappa, "window": wl.window,
                    "page_size": wl.page_size,
                    **({"distinct_layers": nd} if nd < wl.num_layers else {}),
                    **({"pool": "rank", "pool_rho": args.pool_rho} if args.pool_rho >= 1
@@ -407,7 +444,7 @@ def main():
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho)
+        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho, roles)
         result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
     else:

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 2
+#define PRISM_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -186,6 +186,55 @@ PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* k
                                 const prism_params* params, int32_t* anchor_idx,
                                 int32_t* layer_idx_out, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Layer roles of a layer-assignment pattern ("Prism Attention", Algorithm 1's
+ * partition into proposal and refined layers; Appendix E, Table 9, for the
+ * hybrid with shared layers).
+ */
+typedef enum {
+  PRISM_ROLE_PROPOSAL = 0, /* F: scores the whole cache, keeps its top-kappa and
+                              leaves the candidate pool in the workspace          */
+  PRISM_ROLE_REFINED = 1,  /* R: re-scores the pool of the nearest preceding F
+                              layer and keeps its own top-kappa                   */
+  PRISM_ROLE_SHARED = 2    /* S: reuses the set of the nearest preceding F or R
+                              layer as it is; no scoring, no selection            */
+} prism_layer_role;
+
+/*
+ * Role of `layer` in a pattern string of one letter per layer, F, R or S with
+ * Table 9's meanings.  table4 != 0 reads the pattern with Table 4's letters,
+ * where S marks a refined layer (so S maps to PRISM_ROLE_REFINED and R is not
+ * allowed).  Returns the role, or -1 if pattern is NULL, layer lies outside
+ * [0, strlen(pattern)), a letter of the pattern is not allowed, or the first
+ * letter is not F (every other role needs a preceding proposal layer).  Pure
+ * host function; touches no device.
+ */
+PRISM_API int32_t prism_pattern_role(const char* pattern, int32_t table4, int32_t layer);
+
+/*
+ * One layer of a decode step with an explicit role (prism_layer_role):
+ *   PRISM_ROLE_PROPOSAL  as an anchor layer of prism_decode_layer: writes its
+ *                        top-kappa into set_idx and leaves the refinement pool
+ *                        (window or rank-expanded, by params->pool_rho) in the
+ *                        workspace;
+ *   PRISM_ROLE_REFINED   re-scores the pool the nearest preceding proposal
+ *                        layer left in the same workspace, writes its top-kappa
+ *                        into set_idx;
+ *   PRISM_ROLE_SHARED    reads set_idx (the nearest preceding proposal or
+ *                        refined layer's set) and does not change it;
+ * then SparseAttn over the layer's set into out.  params->anchor_stride is not
+ * used.  The layers of one decode step share set_idx and the workspace; a
+ * refined or shared layer before any proposal layer is the caller's error
+ * (the results are then undefined, never out-of-bounds accesses).
+ *   set_idx  int32 [batch][num_kv_heads][kappa], caller-owned state.
+ *   out      float [batch][num_q_heads][head_dim].
+ * Returns PRISM_ERR_INVALID_ARG for an unknown role or a NULL set_idx / out.
+ */
+PRISM_API prism_status prism_decode_layer_role(int32_t role, const prism_kv_cache* kv,
+                                               const uint16_t* q, const prism_params* params,
+                                               int32_t* set_idx, float* out, void* workspace,
+                                               size_t workspace_bytes, void* stream);
 
 /*
  * Optional instrumentation for benchmarks.  Kernel kinds launched by the calls

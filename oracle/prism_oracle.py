@@ -167,9 +167,42 @@ def attend(q_group, k_pages, v_pages, block_table_row, kv_head, selected, page_s
     return sparse_attention(q_group, keys, vals, scale)
 
 
+# ---------------------------------------------------------------------------
+# Layer roles (Algorithm 1's partition into proposal and refined layers; the
+# proposal / refined / shared hybrid of Appendix E, Table 9)
+# ---------------------------------------------------------------------------
+
+ROLES = ("F", "R", "S")
+
+
+def layer_roles(pattern: str, *, table4: bool = False) -> list:
+    """Roles of a layer-assignment pattern, one letter per layer.  F: proposal
+    layer (scores the whole cache and exports the candidate pool); R: refined
+    layer (re-selects within the pool of the nearest preceding F layer); S:
+    shared layer (reuses the set of the nearest preceding F or R layer as it
+    is).  These are Table 9's meanings; Table 4 writes its refined layers as S,
+    which table4=True reads as R.  Layer 0 must be F."""
+    letters = ("F", "S") if table4 else ROLES
+    for c in pattern:
+        if c not in letters:
+            raise ValueError(f"pattern letter {c!r} is not one of {', '.join(letters)}")
+    roles = [("R" if (table4 and c == "S") else c) for c in pattern]
+    if not roles:
+        raise ValueError("empty pattern")
+    if roles[0] != "F":
+        raise ValueError("the first layer of a pattern must be a proposal layer (F)")
+    return roles
+
+
+def stride_role(layer: int, anchor_stride: int) -> str:
+    """Algorithm 1 with a fixed association: every anchor_stride-th layer,
+    starting at layer 0, is a proposal layer; the others are refined."""
+    return "F" if layer % anchor_stride == 0 else "R"
+
+
 def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_kv_heads,
                  kappa, anchor_stride, window, page_size, anchor_state=None, scale=None,
-                 problems=None, pool_rho=0, pool_state=None):
+                 problems=None, pool_rho=0, pool_state=None, role=None, shared_state=None):
     """One layer of Algorithm 1 for every (sequence, KV head).
 
     q_bits: uint16 [B, Hq, D].  anchor_state: int64 [B, Hkv, kappa], the most
@@ -177,23 +210,32 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
     pool_rho: 0 for the window pool, rho >= 1 for the anchor's top rho*kappa
     tokens (Eq. 4); then pool_state, {(b, g): pool} from the most recent
     anchor layer, is required for a refined layer.
+    role: 'F', 'R' or 'S' (see layer_roles); None derives F or R from the
+    stride.  A shared layer attends over shared_state, the most recent F or R
+    layer's sets, and scores nothing.
     problems: optional list of (b, g) to restrict the work to (others are left
     as -1 / NaN).
 
     Returns dict(selected [B,Hkv,kappa] int64, out [B,Hq,D] float64,
-    anchor_state, pool_state, pools {(b,g): pool the layer selected from},
-    scores {(b,g): scores over that pool}).
+    anchor_state, pool_state, shared_state, pools {(b,g): pool the layer
+    selected from}, scores {(b,g): scores over that pool}).
     """
     B, Hq, D = q_bits.shape
     G = Hq // num_kv_heads
     if scale is None or scale == 0:
         scale = default_scale(D)
     q = bf16_to_f64(q_bits)
-    is_anchor = layer % anchor_stride == 0
-    if not is_anchor and anchor_state is None:
+    if role is None:
+        role = stride_role(layer, anchor_stride)
+    if role not in ROLES:
+        raise ValueError(f"unknown role {role!r}")
+    is_anchor = role == "F"
+    if role == "R" and anchor_state is None:
         raise ValueError("a refined layer needs the preceding anchor's sets")
-    if not is_anchor and pool_rho >= 1 and pool_state is None:
+    if role == "R" and pool_rho >= 1 and pool_state is None:
         raise ValueError("a refined layer needs the preceding anchor's pools")
+    if role == "S" and shared_state is None:
+        raise ValueError("a shared layer needs the preceding proposal or refined layer's sets")
     sel = np.full((B, num_kv_heads, kappa), -1, dtype=np.int64)
     out = np.full((B, Hq, D), np.nan)
     pools, scores = {}, {}
@@ -203,7 +245,9 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
     for b, g in todo:
         qg = q[b, g * G:(g + 1) * G]
         L = int(seq_lens[b])
-        if is_anchor:
+        if role == "S":
+            t = np.asarray(shared_state[b, g], dtype=np.int64)
+        elif is_anchor:
             t, s = anchor_select(qg, k_pages, block_table[b], g, L, kappa, page_size)
             pools[(b, g)] = np.arange(L, dtype=np.int64)
             if pool_rho >= 1:
@@ -216,26 +260,32 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
             t, pool, s = refined_select(qg, k_pages, block_table[b], g, L, kappa, page_size,
                                         anchor_state[b, g], window)
             pools[(b, g)] = pool
-        scores[(b, g)] = s
+        if role != "S":
+            scores[(b, g)] = s
         sel[b, g] = t
         out[b, g * G:(g + 1) * G] = attend(qg, k_pages, v_pages, block_table[b], g, t,
                                            page_size, scale)
     new_state = sel.copy() if is_anchor else anchor_state
+    new_shared = sel.copy() if role != "S" else shared_state
     return dict(selected=sel, out=out, anchor_state=new_state, pool_state=new_pools,
-                pools=pools, scores=scores)
+                shared_state=new_shared, pools=pools, scores=scores)
 
 
 def decode_step(layers, block_table, seq_lens, *, num_kv_heads, kappa, anchor_stride, window,
-                page_size, scale=None, pool_rho=0):
+                page_size, scale=None, pool_rho=0, roles=None):
     """Algorithm 1 over layers 0..N-1 in order; `layers` yields
-    (q_bits, k_pages, v_pages) per layer.  Layer 0 must be an anchor."""
-    state, pstate = None, None
+    (q_bits, k_pages, v_pages) per layer.  roles: optional per-layer roles
+    (layer_roles); without them layer l is F iff l mod anchor_stride == 0.
+    Layer 0 must be a proposal layer."""
+    state, pstate, shared = None, None, None
     results = []
     for l, (q_bits, kp, vp) in enumerate(layers):
+        role = roles[l] if roles is not None else None
         r = decode_layer(l, q_bits, kp, vp, block_table, seq_lens, num_kv_heads=num_kv_heads,
                          kappa=kappa, anchor_stride=anchor_stride, window=window,
                          page_size=page_size, anchor_state=state, scale=scale,
-                         pool_rho=pool_rho, pool_state=pstate)
-        state, pstate = r["anchor_state"], r["pool_state"]
+                         pool_rho=pool_rho, pool_state=pstate, role=role,
+                         shared_state=shared)
+        state, pstate, shared = r["anchor_state"], r["pool_state"], r["shared_state"]
         results.append(r)
     return results

@@ -18,6 +18,9 @@ import numpy as np
 _GOLDEN_PATH = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
 with open(_GOLDEN_PATH) as _f:
     GOLDEN = json.load(_f)
+_PATTERNS_PATH = os.path.join(os.path.dirname(__file__), "golden", "layer_patterns.json")
+with open(_PATTERNS_PATH) as _f:
+    PATTERNS = json.load(_f)
 
 
 def _arr(x):
@@ -324,8 +327,113 @@ def pin_cache_rows(impl):
                                                   wl.page_size), want_v)
 
 
+# -------------------------------------------------------------- layer roles
+def pin_layer_patterns(impl):
+    """The pages' printed patterns under their own letters: every Table 4
+    pattern has one proposal layer per 'group' layers (Table 3's caption) and
+    no shared layer once its S is read as refined; Table 9's configuration
+    names give each role's count over GLM-5.2's 78 layers."""
+    for name, e in PATTERNS["table4"]["patterns"].items():
+        roles = impl.layer_roles(e["pattern"], table4=True)
+        assert len(roles) == len(e["pattern"]) and set(roles) <= {"F", "R"}, name
+        assert roles[0] == "F" and roles.count("F") * e["group"] == len(roles), (name, roles)
+    for name, e in PATTERNS["table9"]["patterns"].items():
+        roles = impl.layer_roles(e["pattern"])
+        assert len(roles) == PATTERNS["table9"]["layers"], name
+        assert {c: roles.count(c) for c in "FRS"} == {c: e[c] for c in "FRS"}, name
+    for bad, t4 in (("", False), ("RFS", False), ("SF", False), ("FX", False), ("FR", True)):
+        try:
+            impl.layer_roles(bad, table4=t4)
+        except ValueError:
+            continue
+        raise AssertionError(f"pattern {bad!r} accepted")
+    assert [impl.stride_role(l, 3) for l in range(7)] == list("FRRFRRF")
+
+
+def _bits(x):
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _brute_step(pattern, qs, ks, vs, kappa, w, rho):
+    """Sets and outputs of a layer-role pattern from its definition: F selects
+    its own top-kappa over the whole cache; R re-selects within the pool of
+    the nearest preceding F (the +-w windows of F's set, or F's top rho*kappa
+    when rho >= 1); S reuses the set of the nearest preceding F or R layer.
+    Brute-force scores, TopK and attention in plain Python."""
+    L, D = len(ks[0]), len(ks[0][0])
+    scale = 1.0 / math.sqrt(D)
+    f_set = f_scores = last = None
+    sets, outs = [], []
+    for l, role in enumerate(pattern):
+        q, k, v = qs[l], ks[l], vs[l]
+        s = [max(math.fsum(q[j][d] * k[i][d] for d in range(D)) for j in range(len(q)))
+             for i in range(L)]
+        if role == "F":
+            t = _brute_topk(s, kappa, list(range(L)))
+            f_set, f_scores = t, s
+        elif role == "R":
+            if rho >= 1:
+                pool = _brute_topk(f_scores, min(rho * kappa, L), list(range(L)))
+            else:
+                pool = sorted({p for a in f_set for p in range(max(0, a - w), min(L - 1, a + w) + 1)})
+            t = _brute_topk([s[p] for p in pool], kappa, pool)
+        else:
+            t = list(last)
+        if role != "S":
+            last = t
+        out = []
+        for j in range(len(q)):
+            z = [scale * math.fsum(q[j][d] * k[i][d] for d in range(D)) for i in t]
+            m = max(z)
+            e = [math.exp(x - m) for x in z]
+            tot = math.fsum(e)
+            out.append([math.fsum(e[n] * v[i][d] for n, i in enumerate(t)) / tot
+                        for d in range(D)])
+        sets.append(t)
+        outs.append(out)
+    return sets, outs
+
+
+def pin_pattern_composition(impl, seed=21):
+    """decode_step over random F/R/S patterns (and a stride) equals the
+    brute-force reading of the roles on tiny caches, for the window pool and
+    the rank-expanded pool."""
+    rng = np.random.default_rng(seed)
+    for trial in range(32):
+        L, D, G = int(rng.integers(5, 14)), 4, int(rng.integers(1, 3))
+        kappa = int(rng.integers(1, min(3, L) + 1))
+        w, rho = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+        stride = None
+        if trial % 4 == 3:
+            stride = int(rng.integers(2, 4))
+            pattern = [impl.stride_role(l, stride) for l in range(6)]
+        elif trial % 4 == 2:   # refined layers in a row: each expands the proposal's set
+            w, rho, kappa = 1, 0, 2
+            pattern = list("FRRSRS")
+        else:
+            pattern = ["F"] + list(rng.choice(list("FRS"), size=5, p=[0.2, 0.4, 0.4]))
+        n = len(pattern)
+        ks = [np.round(rng.standard_normal((L, D)) * 3) / 2 for _ in range(n)]
+        vs = [np.round(rng.standard_normal((L, D)) * 4) / 4 for _ in range(n)]
+        qs = [np.round(rng.standard_normal((G, D)) * 3) / 2 for _ in range(n)]
+        pages, bt = _tiny_paged(ks + vs, page_size=2, seed=int(rng.integers(1000)))
+        layers = [(_bits(qs[l])[None], pages[l], pages[n + l]) for l in range(n)]
+        kw = dict(num_kv_heads=1, kappa=kappa, window=w, page_size=2, pool_rho=rho)
+        if stride is None:
+            res = impl.decode_step(layers, bt[None], np.array([L]), anchor_stride=1,
+                                   roles=impl.layer_roles("".join(pattern)), **kw)
+        else:
+            res = impl.decode_step(layers, bt[None], np.array([L]), anchor_stride=stride, **kw)
+        sets, outs = _brute_step(pattern, qs, ks, vs, kappa, w, rho)
+        for l in range(n):
+            got = list(map(int, res[l]["selected"][0, 0]))
+            assert got == sets[l], (trial, "".join(pattern), l, got, sets[l])
+            np.testing.assert_allclose(res[l]["out"][0], outs[l], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [pin_bf16_decode, pin_relevance_bruteforce, pin_relevance_hand, pin_topk_exhaustive,
             pin_topk_invariants, pin_topk_hand, pin_pool_bruteforce, pin_pool_hand,
             pin_refine_hand, pin_refine_limits, pin_rank_pool_exhaustive,
             pin_rank_pool_structure, pin_attention_dense_library,
-            pin_attention_closed_forms, pin_attention_hand, pin_cache_rows]
+            pin_attention_closed_forms, pin_attention_hand, pin_cache_rows,
+            pin_layer_patterns, pin_pattern_composition]

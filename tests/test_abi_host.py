@@ -39,6 +39,9 @@ def _call(fn, kv, p, ws=FAKE, nbytes=1 << 40, **extra):
     if fn == "layer":
         return lib.prism_decode_layer(extra.get("layer", 0), kvp, FAKE, pp, FAKE, None, FAKE, ws,
                                       nbytes, None)
+    if fn == "role":
+        return lib.prism_decode_layer_role(extra.get("role", 0), kvp, FAKE, pp, FAKE, FAKE, ws,
+                                           nbytes, None)
     raise ValueError(fn)
 
 
@@ -47,14 +50,15 @@ def test_library_exports_every_declared_function():
     assert set(declared) == {"prism_workspace_size", "prism_score_topk", "prism_refine_topk",
                              "prism_sparse_attn", "prism_decode_layer", "prism_status_string",
                              "prism_last_error", "prism_abi_version", "prism_profile_events",
-                             "prism_profile_launches"}
+                             "prism_profile_launches", "prism_pattern_role",
+                             "prism_decode_layer_role"}
     lib = tsa.lib()
     for name in declared:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 2
+    assert tsa.prism_abi_version() == 3
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -102,7 +106,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["score", "refine", "attn", "layer"])
+@pytest.mark.parametrize("fn", ["score", "refine", "attn", "layer", "role"])
 @pytest.mark.parametrize("name,args,want", CASES, ids=[c[0] for c in CASES])
 def test_invalid_calls_rejected_on_host(fn, name, args, want):
     kv = args.get("kv", _kv()) if "kv" in args else _kv()
@@ -131,7 +135,7 @@ def test_valid_call_without_gpu_reports_hip_error():
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
-    for fn in ("score", "refine", "attn", "layer"):
+    for fn in ("score", "refine", "attn", "layer", "role"):
         st = _call(fn, _kv(), _params())
         assert st == L.PRISM_ERR_HIP, (fn, st)
         assert "device" in tsa.prism_last_error().lower()
@@ -162,3 +166,42 @@ def test_refine_anchor_idx_needed_for_the_window_pool_only():
         pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
     assert lib.prism_refine_topk(ctypes.byref(kv), FAKE, ctypes.byref(pr), None, FAKE, None, None,
                                  None, FAKE, 1 << 40, None) == L.PRISM_ERR_HIP
+
+
+def test_pattern_roles_of_the_pages_patterns():
+    """prism_pattern_role reads every letter of the pages' patterns (Table 4:
+    F proposal, S refined; Table 9: F, R, S) and rejects malformed ones."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "layer_patterns.json")) as f:
+        pats = json.load(f)
+    for table4, key, letters in ((True, "table4", {"F": 0, "S": 1}),
+                                 (False, "table9", {"F": 0, "R": 1, "S": 2})):
+        for e in pats[key]["patterns"].values():
+            pat = e["pattern"]
+            got = [tsa.prism_pattern_role(pat, l, table4=table4) for l in range(len(pat))]
+            assert got == [letters[c] for c in pat]
+            assert tsa.prism_pattern_role(pat, len(pat), table4=table4) == -1
+    for pat, layer, t4 in (("", 0, False), ("RFS", 1, False), ("SFF", 1, False),
+                           ("FXS", 0, False), ("FRS", 0, True), ("FS", -1, False)):
+        assert tsa.prism_pattern_role(pat, layer, table4=t4) == -1, (pat, layer, t4)
+    assert tsa.lib().prism_pattern_role(None, 0, 0) == -1
+
+
+def test_decode_layer_role_argument_checks():
+    lib = tsa.lib()
+    kv, p = _kv(), _params()
+    for role in (-1, 3, 99):
+        assert _call("role", kv, p, role=role) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_decode_layer_role(2, ctypes.byref(kv), FAKE, ctypes.byref(p), None, FAKE,
+                                       FAKE, 1 << 40, None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_decode_layer_role(0, ctypes.byref(kv), FAKE, ctypes.byref(p), FAKE, None,
+                                       FAKE, 1 << 40, None) == L.PRISM_ERR_INVALID_ARG
+    with pytest.raises(tsa.PrismError):
+        tsa.prism_decode_layer_role("X", _FakeKV(kv), FAKE, p, FAKE, FAKE, workspace=(FAKE, 1 << 40),
+                                    stream=0)
+
+
+class _FakeKV:
+    def __init__(self, struct):
+        self.struct = struct

@@ -393,6 +393,79 @@ def test_decode_chain_rank_pool_per_problem_selection():
     _run_chain_rank(st, range(3), probs, "rank-pool per-problem")
 
 
+def _run_pattern(st, pattern, problems, label, table4=False):
+    """prism_decode_layer_role over a layer-role pattern: proposal layers
+    against the oracle's exact TopK, refined layers against the oracle
+    re-scoring the pool of the GPU's own nearest proposal layer, shared layers
+    reusing the nearest proposal or refined layer's set bit for bit, and the
+    attention of every layer on the GPU's set."""
+    wl = st.wl
+    set_idx, out = st.idx_buf(), st.out_buf()
+    f_set = last = pool_gpu = plen_gpu = None
+    stats = {"exact": 0, "near-tie": 0, "shared": 0}
+    for l, c in enumerate(pattern):
+        role = tsa.prism_pattern_role(pattern, l, table4=table4)
+        kind = "FRS"[role]
+        say(f"[{label}] layer {l} role {kind}")
+        tsa.prism_decode_layer_role(role, st.kv[l], st.q[l], st.params, set_idx, out, st.ws)
+        torch.cuda.synchronize()
+        sel, o = set_idx.cpu().numpy(), out.cpu().numpy()
+        if kind == "F":
+            f_set = sel.copy()
+            if st.pool_rho >= 1:
+                pool_gpu, plen_gpu, _ = _gpu_pool(st, l)
+        if kind == "S":
+            assert np.array_equal(sel, last), f"{label} l{l}: shared layer changed the set"
+            stats["shared"] += 1
+        for b, g in problems:
+            where = f"{label} l{l} b{b} g{g}"
+            L = int(st.pg.seq_lens[b])
+            if kind == "F":
+                want, sc = st.oracle_anchor(l, b, g)
+                stats[check_set(sel[b, g], want, sc, np.arange(L), wl.kappa, where)] += 1
+            elif kind == "R":
+                if st.pool_rho >= 1:
+                    gp = pool_gpu[b, g, :plen_gpu[b, g]]
+                    want, sc = st.oracle_refine_in_pool(l, b, g, gp)
+                else:
+                    want, gp, sc = st.oracle_refine(l, b, g, f_set[b, g])
+                stats[check_set(sel[b, g], want, sc, gp, wl.kappa, where)] += 1
+            G = wl.group
+            check_attn(o[b, g * G:(g + 1) * G], st.oracle_attend(l, b, g, sel[b, g]), where)
+        if kind != "S":
+            last = sel.copy()
+    say(f"[{label}] sets: {stats}")
+    return stats
+
+
+@pytest.mark.parametrize("rho", [0, 4])
+def test_decode_layer_roles_hybrid_pattern(rho):
+    """A proposal / refined / shared hybrid (Appendix E, Table 9's letters):
+    refined layers after shared ones, shared layers after refined ones and a
+    second proposal layer, with the window and the rank-expanded pool, on a
+    ragged batch that spans the register and classified selection paths."""
+    wl = synth.scaled(synth.TINY_4K, name=f"roles-{rho}", wid=196, num_q_heads=32,
+                      num_kv_heads=8, batch=3, context=None, lengths=(6016, 20032, 40000),
+                      kappa=512, num_layers=8, anchor_stride=8)
+    st = Setup(wl, range(8), pool_rho=rho)
+    probs = [(b, g) for b in range(wl.batch) for g in (1, 6)]
+    s = _run_pattern(st, "FSRSRFSR", probs, f"roles rho={rho}")
+    assert s["shared"] == 3
+
+
+def test_decode_layer_roles_table4_pattern_per_problem_selection():
+    """Layers 7-12 of Table 4's Qwen3-4B group-4 pattern (F proposal, S
+    refined) on a grid above the CU count, G = 8: refined layers select once
+    per problem."""
+    wl = synth.scaled(synth.TINY_4K, name="roles-t4", wid=197, num_q_heads=64,
+                      num_kv_heads=8, batch=4, context=None, lengths=(20032, 36032, 24000, 30016),
+                      kappa=1100, num_layers=6, anchor_stride=6)
+    st = Setup(wl, range(6), pool_rho=0)
+    probs = [(0, 2), (1, 5), (2, 0), (3, 7)]
+    s = _run_pattern(st, "FFSSSS", probs, "roles table-4", table4=True)
+    assert s["shared"] == 0
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []

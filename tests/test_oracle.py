@@ -111,3 +111,32 @@ def test_decode_step_rank_pool():
         oracle.decode_layer(1, *layers[1], bt, lens, num_kv_heads=2, kappa=3, anchor_stride=3,
                             window=1, page_size=2, anchor_state=res[0]["anchor_state"],
                             pool_rho=2)
+
+
+def test_decode_step_layer_roles_hand():
+    """Explicit roles on the hand example (anchor scores [3, 1, 4, -1, 2, 3, 0,
+    1], refined scores [0, 5, 1, 2, 0, 1, 6, 9], kappa = 3, w = 1).  FSR: the
+    shared layer 1 attends over layer 0's set {0, 2, 5} with its own keys and
+    values; the refined layer 2 still expands layer 0's set (pool 0..6) and
+    keeps {1, 3, 6}.  FRS: layer 2 reuses layer 1's refined set {1, 3, 6}.
+    FFS: layer 1 is a proposal layer over the whole cache ({1, 6, 7}) and
+    layer 2 reuses that."""
+    layers, bt, lens = _decode_case()
+    kw = dict(num_kv_heads=2, kappa=3, anchor_stride=1, window=1, page_size=2)
+    for pattern, want in (("FSR", [[0, 2, 5], [0, 2, 5], [1, 3, 6]]),
+                          ("FRS", [[0, 2, 5], [1, 3, 6], [1, 3, 6]]),
+                          ("FFS", [[0, 2, 5], [1, 6, 7], [1, 6, 7]])):
+        res = oracle.decode_step(layers, bt, lens, roles=oracle.layer_roles(pattern), **kw)
+        for l, r in enumerate(res):
+            for h in range(2):
+                assert list(r["selected"][0, h]) == want[l], (pattern, l, h)
+        # the shared layer's output is attention over the reused set with its own K, V
+        ls = pattern.index("S")
+        qb, kp, vp = layers[ls]
+        q = oracle.bf16_to_f64(qb)[0]
+        o = oracle.attend(q[0:2], kp, vp, bt[0], 0, res[ls]["selected"][0, 0], 2,
+                          oracle.default_scale(2))
+        np.testing.assert_allclose(res[ls]["out"][0, 0:2], o, rtol=1e-14)
+        assert not res[ls]["scores"]
+    with pytest.raises(ValueError):   # a shared layer needs a preceding set
+        oracle.decode_layer(1, *layers[1], bt, lens, role="S", **kw)

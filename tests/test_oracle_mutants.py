@@ -81,6 +81,24 @@ def _attn_pair(weights):
                 sparse_attention=lambda q, k, v, s: weights(q, k, s) @ v)
 
 
+def _step_with(fix):
+    """decode_step whose per-layer (role, anchor_state, shared_state) pass
+    through fix(role, anchor_state, shared_state) before each layer."""
+    def step(layers, bt, lens, *, roles=None, anchor_stride=1, **kw):
+        st = ps = sh = None
+        out = []
+        for l, (q, kp, vp) in enumerate(layers):
+            role = roles[l] if roles is not None else po.stride_role(l, anchor_stride)
+            role, a_state, s_state = fix(role, st, sh)
+            r = po.decode_layer(l, q, kp, vp, bt, lens, anchor_stride=anchor_stride,
+                                anchor_state=a_state, pool_state=ps, role=role,
+                                shared_state=s_state, **kw)
+            st, ps, sh = r["anchor_state"], r["pool_state"], r["shared_state"]
+            out.append(r)
+        return out
+    return step
+
+
 MUTANTS = {
     "bf16 widened by 15 bits": dict(
         bf16_to_f64=lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15)
@@ -113,6 +131,17 @@ MUTANTS = {
     "attention scale squared": _attn_pair(lambda q, k, s: _softmax_rows(q @ k.T * s * s)),
     "softmax over heads": _attn_pair(lambda q, k, s: _softmax_rows((q @ k.T * s).T).T),
     "logits with a negated key": _attn_pair(lambda q, k, s: _softmax_rows(-(q @ k.T) * s)),
+    "shared layers re-select": dict(
+        layer_roles=lambda p, table4=False: ["R" if c == "S" else c
+                                             for c in po.layer_roles(p, table4=table4)]),
+    "table 4 refined letters read as shared": dict(
+        layer_roles=lambda p, table4=False: po.layer_roles(p.replace("R", "X"), table4=False)),
+    "shared layer takes the proposal layer's set": dict(
+        decode_step=_step_with(lambda role, a, sh: (role, a, a if role == "S" else sh))),
+    "refined layer expands the latest set": dict(
+        decode_step=_step_with(lambda role, a, sh: (role, sh if role == "R" else a, sh))),
+    "every layer a proposal layer": dict(
+        decode_step=_step_with(lambda role, a, sh: ("F", a, sh))),
     "logical page ignores block table": dict(
         cache_rows=lambda pages, bt, g, pos, ps: po.bf16_to_f64(
             pages[np.asarray(pos) // ps, g, np.asarray(pos) % ps, :])),

@@ -7,13 +7,15 @@ this package is its ctypes binding.  Functions carry the C names.
 from ._lib import (PrismError, KVCache, params, lib, declared_functions, prism_workspace_size,
                    prism_score_topk, prism_refine_topk, prism_sparse_attn, prism_decode_layer,
                    prism_status_string, prism_last_error, prism_abi_version, prism_profile_events,
-                   prism_profile_launches, KERNEL_KINDS, PRISM_OK,
+                   prism_profile_launches, prism_pattern_role, prism_decode_layer_role,
+                   KERNEL_KINDS, ROLES, PRISM_OK,
                    PRISM_ERR_INVALID_ARG, PRISM_ERR_UNSUPPORTED, PRISM_ERR_WORKSPACE,
                    PRISM_ERR_HIP, LIB_PATH)
 
 __all__ = ["PrismError", "KVCache", "params", "lib", "declared_functions", "prism_workspace_size",
            "prism_score_topk", "prism_refine_topk", "prism_sparse_attn", "prism_decode_layer",
            "prism_status_string", "prism_last_error", "prism_abi_version",
-           "prism_profile_events", "prism_profile_launches", "KERNEL_KINDS", "PRISM_OK",
+           "prism_profile_events", "prism_profile_launches", "prism_pattern_role",
+           "prism_decode_layer_role", "KERNEL_KINDS", "ROLES", "PRISM_OK",
            "PRISM_ERR_INVALID_ARG", "PRISM_ERR_UNSUPPORTED", "PRISM_ERR_WORKSPACE",
            "PRISM_ERR_HIP", "LIB_PATH"]

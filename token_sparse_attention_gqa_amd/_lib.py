@@ -54,6 +54,10 @@ _SIGS = {
     "prism_decode_layer": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
                                           ctypes.POINTER(ParamsStruct), _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "prism_pattern_role": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_int32, ctypes.c_int32]),
+    "prism_decode_layer_role": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
+                                               ctypes.POINTER(ParamsStruct), _P, _P, _P,
+                                               ctypes.c_size_t, _P]),
     "prism_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "prism_last_error": (ctypes.c_char_p, []),
     "prism_abi_version": (ctypes.c_int32, []),
@@ -61,6 +65,9 @@ _SIGS = {
                                             ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]),
     "prism_profile_launches": (ctypes.c_int64, [ctypes.c_int32]),
 }
+
+# prism_layer_role
+ROLES = {"F": 0, "R": 1, "S": 2}
 
 # prism_kernel_kind
 KERNEL_KINDS = {"anchor_score": 0, "refine_score": 1, "select": 2, "attention": 3,
@@ -213,6 +220,24 @@ def prism_decode_layer(layer, kv, q, p, anchor_idx, layer_idx_out, out, workspac
                                          optional=True),
                                     _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
            "prism_decode_layer")
+
+
+def prism_pattern_role(pattern: str, layer: int, table4: bool = False) -> int:
+    """prism_layer_role of `layer` in a pattern string (-1 if invalid)."""
+    return int(lib().prism_pattern_role(pattern.encode(), int(bool(table4)), int(layer)))
+
+
+def prism_decode_layer_role(role, kv, q, p, set_idx, out, workspace=None, stream=None):
+    """role: a prism_layer_role value, or one of the letters F, R, S."""
+    if isinstance(role, str):
+        role = ROLES.get(role, -1)
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_decode_layer_role(int(role), ctypes.byref(kv.struct),
+                                         _ptr(q, "q", itemsize=2), ctypes.byref(p),
+                                         _ptr(set_idx, "set_idx", itemsize=4),
+                                         _ptr(out, "out", itemsize=4), ws, nbytes,
+                                         _stream(stream)),
+           "prism_decode_layer_role")
 
 
 def prism_status_string(status: int) -> str:

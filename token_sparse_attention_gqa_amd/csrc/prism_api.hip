@@ -246,6 +246,56 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
       "refined layer launch");
 }
 
+int32_t prism_pattern_role(const char* pattern, int32_t table4, int32_t layer) {
+  if (!pattern || layer < 0) return -1;
+  int32_t n = 0, role = -1;
+  for (const char* c = pattern; *c; ++c, ++n) {
+    int32_t r;
+    switch (*c) {
+      case 'F': r = PRISM_ROLE_PROPOSAL; break;
+      case 'R': if (table4) return -1; r = PRISM_ROLE_REFINED; break;
+      case 'S': r = table4 ? PRISM_ROLE_REFINED : PRISM_ROLE_SHARED; break;
+      default: return -1;
+    }
+    if (n == 0 && r != PRISM_ROLE_PROPOSAL) return -1;
+    if (n == layer) role = r;
+  }
+  return role;
+}
+
+prism_status prism_decode_layer_role(int32_t role, const prism_kv_cache* kv, const uint16_t* q,
+                                     const prism_params* params, int32_t* set_idx, float* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (role != PRISM_ROLE_PROPOSAL && role != PRISM_ROLE_REFINED && role != PRISM_ROLE_SHARED)
+    return fail(PRISM_ERR_INVALID_ARG, "role must be PRISM_ROLE_PROPOSAL, _REFINED or _SHARED");
+  if (!set_idx || !out) return fail(PRISM_ERR_INVALID_ARG, "set_idx and out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Workspace w = prism::carve_workspace(workspace, g);
+  const float scale = resolve_scale(params);
+  switch (role) {
+    case PRISM_ROLE_PROPOSAL:
+      if (g.pool_rho >= 1) {
+        PRISM_TRY(hip_check(prism::launch_anchor_rank(g, w, q, set_idx, nullptr, s),
+                            "proposal layer launch"));
+        return hip_check(prism::launch_attention(g, w, q, nullptr, true, scale, out, s),
+                         "proposal layer attention launch");
+      }
+      return hip_check(prism::launch_anchor_attend(g, w, q, scale, set_idx, nullptr, out, s),
+                       "proposal layer launch");
+    case PRISM_ROLE_REFINED:
+      return hip_check(prism::launch_refine_attend(g, w, q, scale, set_idx, out, s),
+                       "refined layer launch");
+    default:
+      return hip_check(prism::launch_attention(g, w, q, set_idx, false, scale, out, s),
+                       "shared layer attention launch");
+  }
+}
+
 prism_status prism_profile_events(int32_t kind, void* const* start_events,
                                   void* const* stop_events, int32_t count) {
   if (!prism::set_profile_events(kind, start_events, stop_events, count))
