@@ -8,9 +8,14 @@ the GPU library.  Only the test suite, the package smoke check and the
 benchmark's CPU-baseline leg may import it.  It shares no code with the HIP
 library and imports nothing from it.
 
-Everything is float64 numpy.  bf16 inputs are widened exactly.  Readings taken
-where the paper is silent (all also listed in the design notes):
-  * scoring uses the bf16 keys themselves, not the paper's INT2 codes;
+Everything is float64 numpy, except the INT2 quantizer, whose integer
+decisions are taken in float32 (the precision the GPU takes them in).  bf16
+inputs are widened exactly.  Readings taken where the paper is silent (all also
+listed in the design notes):
+  * scoring uses the bf16 keys themselves by default; with int2=True it uses
+    the INT2 keys of Section 4.2 (Eqs. 7-9): groups of 32 dimensions, the
+    scale and zero point stored as bf16, and the score taken against the
+    dequantized key alpha * code + beta;
   * GQA: query head j belongs to KV head j // G (consecutive blocks);
   * TopK ties go to the lower token position; the selected set is returned as
     ascending positions (the paper treats it as a set);
@@ -54,6 +59,75 @@ def cache_rows(pages, block_table_row, kv_head: int, positions, page_size: int) 
     pos = np.asarray(positions, dtype=np.int64)
     phys = np.asarray(block_table_row, dtype=np.int64)[pos // page_size]
     return bf16_to_f64(pages[phys, kv_head, pos % page_size, :])
+
+
+def cache_row_bits(pages, block_table_row, kv_head: int, positions, page_size: int):
+    """As cache_rows, the raw bf16 bit patterns: uint16 [n, D]."""
+    pos = np.asarray(positions, dtype=np.int64)
+    phys = np.asarray(block_table_row, dtype=np.int64)[pos // page_size]
+    return np.asarray(pages[phys, kv_head, pos % page_size, :], dtype=np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Section 4.2: INT2 proposal keys (Eqs. 7-8)
+# ---------------------------------------------------------------------------
+
+INT2_BITS = 2
+INT2_GROUP = 32      # dimensions per quantization group (g); the paper leaves it open
+
+
+def _round_to_bf16(x32: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 value (ties to even), returned as float32."""
+    u = np.asarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def quantize_int2(k_bits, group: int = INT2_GROUP):
+    """Group-wise asymmetric b = 2 quantization of keys (Eqs. 7-8).  Each key
+    row is split into D / group consecutive sub-vectors; a sub-vector's zero
+    point beta is its minimum and its scale alpha is (max - min) / (2^b - 1),
+    kept as a bf16 value; each element's code is (k - beta) / alpha rounded to
+    the nearest integer (ties to even) and clipped to [0, 2^b - 1]; a constant
+    sub-vector (alpha = 0) gets code 0.  The subtraction, division and rounding
+    are float32 operations, the precision the GPU decides the codes in.
+
+    k_bits: uint16 bf16 bit patterns [n, D].  Returns (codes uint8 [n, D],
+    alpha float64 [n, D / group], beta float64 [n, D / group]), the scales as
+    the stored bf16 values."""
+    bits = np.asarray(k_bits, dtype=np.uint16)
+    n, D = bits.shape
+    if D % group:
+        raise ValueError("head dimension must be a multiple of the group size")
+    k = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).reshape(n, D // group, group)
+    levels = np.float32(2 ** INT2_BITS - 1)
+    mx, mn = k.max(axis=2), k.min(axis=2)
+    alpha = _round_to_bf16((mx - mn) / levels)
+    beta = mn
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        x = (k - beta[..., None]) / alpha[..., None]
+        c = np.clip(np.rint(x), 0, levels)
+    c = np.where(alpha[..., None] == 0, np.float32(0), c)
+    return (c.astype(np.uint8).reshape(n, D), alpha.astype(np.float64), beta.astype(np.float64))
+
+
+def dequantize_int2(codes, alpha, beta, group: int = INT2_GROUP) -> np.ndarray:
+    """The key an INT2 code row stands for: alpha * code + beta per group
+    (float64 [n, D])."""
+    c = np.asarray(codes, dtype=np.float64)
+    n, D = c.shape
+    c = c.reshape(n, D // group, group)
+    return (np.asarray(alpha)[..., None] * c + np.asarray(beta)[..., None]).reshape(n, D)
+
+
+def proposal_rows(k_pages, block_table_row, kv_head, positions, page_size, int2=False):
+    """The keys relevance is computed from: the cached bf16 rows, or with
+    int2 the dequantized INT2 codes of those rows (Eq. 9 on the quantized
+    keys)."""
+    if not int2:
+        return cache_rows(k_pages, block_table_row, kv_head, positions, page_size)
+    bits = cache_row_bits(k_pages, block_table_row, kv_head, positions, page_size)
+    return dequantize_int2(*quantize_int2(bits))
 
 
 # ---------------------------------------------------------------------------
@@ -135,29 +209,35 @@ def default_scale(head_dim: int) -> float:
 # One layer and one decode step over the paged cache
 # ---------------------------------------------------------------------------
 
-def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size):
-    """Proposal (anchor) layer of Algorithm 1, with bf16 keys: score every
-    cached token, keep the exact top-kappa.  Returns (selected, scores)."""
+def anchor_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size,
+                  int2=False):
+    """Proposal (anchor) layer of Algorithm 1: score every cached token (bf16
+    keys, or INT2 keys with int2), keep the exact top-kappa.
+    Returns (selected, scores)."""
     pos = np.arange(length, dtype=np.int64)
-    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pos, page_size))
+    s = relevance(q_group, proposal_rows(k_pages, block_table_row, kv_head, pos, page_size, int2))
     return top_kappa(s, kappa, pos), s
 
 
-def refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size):
+def refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size,
+                   int2=False):
     """Refined layer of Algorithm 1 (Eqs. 5-6) over a given candidate pool:
-    re-score only the pool's tokens, keep the top-kappa there.
+    re-score only the pool's tokens (with INT2 keys if int2, as Algorithm 1's
+    refined layers do), keep the top-kappa there.
     Returns (selected, scores over the pool)."""
     pool = np.asarray(pool, dtype=np.int64)
-    s = relevance(q_group, cache_rows(k_pages, block_table_row, kv_head, pool, page_size))
+    s = relevance(q_group, proposal_rows(k_pages, block_table_row, kv_head, pool, page_size,
+                                         int2))
     return top_kappa(s, kappa, pool), s
 
 
 def refined_select(q_group, k_pages, block_table_row, kv_head, length, kappa, page_size,
-                   anchor_positions, w):
+                   anchor_positions, w, int2=False):
     """Refined layer with the window pool built from the anchor's set.
     Returns (selected, pool, scores over the pool)."""
     pool = window_pool(anchor_positions, w, length)
-    t, s = refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size)
+    t, s = refine_in_pool(q_group, k_pages, block_table_row, kv_head, pool, kappa, page_size,
+                          int2)
     return t, pool, s
 
 
@@ -202,7 +282,8 @@ def stride_role(layer: int, anchor_stride: int) -> str:
 
 def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_kv_heads,
                  kappa, anchor_stride, window, page_size, anchor_state=None, scale=None,
-                 problems=None, pool_rho=0, pool_state=None, role=None, shared_state=None):
+                 problems=None, pool_rho=0, pool_state=None, role=None, shared_state=None,
+                 int2=False):
     """One layer of Algorithm 1 for every (sequence, KV head).
 
     q_bits: uint16 [B, Hq, D].  anchor_state: int64 [B, Hkv, kappa], the most
@@ -213,6 +294,8 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
     role: 'F', 'R' or 'S' (see layer_roles); None derives F or R from the
     stride.  A shared layer attends over shared_state, the most recent F or R
     layer's sets, and scores nothing.
+    int2: relevance from the INT2 keys (Section 4.2) at proposal and refined
+    layers; attention always reads the bf16 keys and values.
     problems: optional list of (b, g) to restrict the work to (others are left
     as -1 / NaN).
 
@@ -248,17 +331,17 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
         if role == "S":
             t = np.asarray(shared_state[b, g], dtype=np.int64)
         elif is_anchor:
-            t, s = anchor_select(qg, k_pages, block_table[b], g, L, kappa, page_size)
+            t, s = anchor_select(qg, k_pages, block_table[b], g, L, kappa, page_size, int2)
             pools[(b, g)] = np.arange(L, dtype=np.int64)
             if pool_rho >= 1:
                 new_pools[(b, g)] = rank_pool(s, pools[(b, g)], pool_rho, kappa)
         elif pool_rho >= 1:
             pool = pool_state[(b, g)]
-            t, s = refine_in_pool(qg, k_pages, block_table[b], g, pool, kappa, page_size)
+            t, s = refine_in_pool(qg, k_pages, block_table[b], g, pool, kappa, page_size, int2)
             pools[(b, g)] = pool
         else:
             t, pool, s = refined_select(qg, k_pages, block_table[b], g, L, kappa, page_size,
-                                        anchor_state[b, g], window)
+                                        anchor_state[b, g], window, int2)
             pools[(b, g)] = pool
         if role != "S":
             scores[(b, g)] = s
@@ -272,7 +355,7 @@ def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_
 
 
 def decode_step(layers, block_table, seq_lens, *, num_kv_heads, kappa, anchor_stride, window,
-                page_size, scale=None, pool_rho=0, roles=None):
+                page_size, scale=None, pool_rho=0, roles=None, int2=False):
     """Algorithm 1 over layers 0..N-1 in order; `layers` yields
     (q_bits, k_pages, v_pages) per layer.  roles: optional per-layer roles
     (layer_roles); without them layer l is F iff l mod anchor_stride == 0.
@@ -285,7 +368,7 @@ def decode_step(layers, block_table, seq_lens, *, num_kv_heads, kappa, anchor_st
                          kappa=kappa, anchor_stride=anchor_stride, window=window,
                          page_size=page_size, anchor_state=state, scale=scale,
                          pool_rho=pool_rho, pool_state=pstate, role=role,
-                         shared_state=shared)
+                         shared_state=shared, int2=int2)
         state, pstate, shared = r["anchor_state"], r["pool_state"], r["shared_state"]
         results.append(r)
     return results

@@ -327,6 +327,108 @@ def pin_cache_rows(impl):
                                                   wl.page_size), want_v)
 
 
+# ------------------------------------------------------------ INT2 keys
+def _bf16_round(x):
+    """Nearest bf16 value of float64 x (through float32), as float64."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return ((((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32)
+            .view(np.float32).astype(np.float64))
+
+
+def pin_int2_exact_levels(impl, seed=22):
+    """A 32-dimension group whose values lie exactly on beta + alpha * c,
+    c in {0, 1, 2, 3}, with both end levels present and alpha a power of two,
+    quantizes to exactly those codes, scale and zero point (Eq. 8), and
+    dequantizes to itself; a constant group gets scale 0 and codes 0."""
+    rng = np.random.default_rng(seed)
+    for _ in range(40):
+        n, M = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        c = rng.integers(0, 4, size=(n, M, 32))
+        c[:, :, 0], c[:, :, 1] = 0, 3
+        alpha = 2.0 ** rng.integers(-6, 5, size=(n, M))
+        beta = alpha * rng.integers(-60, 61, size=(n, M))   # on alpha's grid: 7 bits suffice
+        k = (alpha[..., None] * c + beta[..., None]).reshape(n, M * 32)
+        assert np.array_equal(_bf16_round(k), k)
+        codes, a, b = impl.quantize_int2(_bits(k))
+        assert np.array_equal(codes, c.reshape(n, M * 32)), "codes"
+        assert np.array_equal(a, alpha) and np.array_equal(b, beta)
+        assert np.array_equal(impl.dequantize_int2(codes, a, b), k)
+    k = np.repeat(np.array([[1.5, -2.0, 0.0, 3.25]]), 32, axis=1)   # four constant groups
+    codes, a, b = impl.quantize_int2(_bits(k))
+    assert not codes.any() and not a.any() and list(b[0]) == [1.5, -2.0, 0.0, 3.25]
+    assert np.array_equal(impl.dequantize_int2(codes, a, b), k)
+
+
+def pin_int2_nearest_level(impl, seed=23):
+    """On random keys: beta is the group minimum; alpha is a bf16 value within
+    half a bf16 step of (max - min) / 3; every code picks a nearest level of
+    beta + alpha * {0, 1, 2, 3} (exact arithmetic, up to float32's decision
+    tolerance); dequantization is within alpha / 2 of the key (plus the top
+    level's shortfall when alpha rounds down); groups are the consecutive
+    32-dimension blocks (a change in one block leaves the others alone)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(30):
+        n = int(rng.integers(1, 6))
+        k = _bf16_round(rng.standard_normal((n, 128)) * float(rng.choice([0.01, 1.0, 30.0])))
+        codes, a, b = impl.quantize_int2(_bits(k))
+        assert codes.shape == (n, 128) and a.shape == b.shape == (n, 4)
+        assert codes.max() <= 3
+        kg = k.reshape(n, 4, 32)
+        mn, mx = kg.min(axis=2), kg.max(axis=2)
+        assert np.array_equal(b, mn)
+        assert np.array_equal(_bf16_round(a), a)
+        third = (mx - mn) / 3.0
+        assert np.all(np.abs(a - third) <= third * 2.0 ** -8 * 1.0001)   # half a bf16 step
+        lev = b[..., None, None] + a[..., None, None] * np.arange(4)        # [n, 4, 1, 4]
+        dist = np.abs(kg[..., None] - lev)                                   # [n, 4, 32, 4]
+        chosen = np.take_along_axis(dist, codes.reshape(n, 4, 32, 1).astype(np.int64), 3)[..., 0]
+        assert np.all(chosen <= dist.min(axis=3) + a[..., None] * 2.0 ** -20)
+        err = np.abs(impl.dequantize_int2(codes, a, b).reshape(n, 4, 32) - kg)
+        bound = a / 2 + 3 * np.maximum(third - a, 0) + a * 2.0 ** -20
+        assert np.all(err <= bound[..., None]), err.max()
+        d = int(rng.integers(0, 128))
+        k2 = k.copy()
+        k2[0, d] = -k2[0, d] * 3 - 1
+        k2 = _bf16_round(k2)
+        c2, a2, b2 = impl.quantize_int2(_bits(k2))
+        keep = [m for m in range(4) if m != d // 32]
+        assert np.array_equal(a2[0, keep], a[0, keep]) and np.array_equal(b2[0, keep], b[0, keep])
+        cols = [i for i in range(128) if i // 32 != d // 32]
+        assert np.array_equal(c2[0, cols], codes[0, cols])
+
+
+def pin_int2_relevance(impl, seed=24):
+    """Relevance on INT2 keys (Eq. 9) is the group maximum of <q_j, k-hat_i>
+    with k-hat = alpha * code + beta: brute-force loops over the quantizer's
+    own output on tiny paged caches, the anchor set by exhaustive TopK, and the
+    refined layer's pool scores likewise; keys already on their levels score
+    exactly as the bf16 keys do."""
+    rng = np.random.default_rng(seed)
+    for trial in range(12):
+        L, G, D = int(rng.integers(3, 8)), int(rng.integers(1, 3)), 64
+        kappa = int(rng.integers(1, min(3, L) + 1))
+        k = _bf16_round(rng.standard_normal((L, D)) * 2)
+        q = _bf16_round(rng.standard_normal((G, D)))
+        (kp,), bt = _tiny_paged([k], page_size=2, seed=trial)
+        codes, a, b = impl.quantize_int2(_bits(k))
+        want = [max(math.fsum(q[j, d] * (a[i, d // 32] * int(codes[i, d]) + b[i, d // 32])
+                              for d in range(D)) for j in range(G)) for i in range(L)]
+        sel, s = impl.anchor_select(q, kp, bt, 0, L, kappa, 2, int2=True)
+        np.testing.assert_allclose(s, want, rtol=1e-12, atol=1e-12)
+        assert list(map(int, sel)) == _brute_topk(want, kappa, list(range(L)))
+        pool = np.sort(rng.choice(L, size=int(rng.integers(kappa, L + 1)), replace=False))
+        t, sp = impl.refine_in_pool(q, kp, bt, 0, pool, kappa, 2, int2=True)
+        np.testing.assert_allclose(sp, [want[i] for i in pool], rtol=1e-12, atol=1e-12)
+        # on-level keys: alpha = 1/2, beta = -1, so quantization loses nothing
+        c = rng.integers(0, 4, size=(L, 2, 32))
+        c[:, :, 0], c[:, :, 1] = 0, 3
+        kl = (0.5 * c - 1.0).reshape(L, D)
+        (kpl,), btl = _tiny_paged([kl], page_size=2, seed=trial)
+        s_int2 = impl.anchor_select(q, kpl, btl, 0, L, kappa, 2, int2=True)[1]
+        s_bf16 = impl.anchor_select(q, kpl, btl, 0, L, kappa, 2)[1]
+        np.testing.assert_allclose(s_int2, s_bf16, rtol=1e-12, atol=1e-12)
+
+
 # -------------------------------------------------------------- layer roles
 def pin_layer_patterns(impl):
     """The pages' printed patterns under their own letters: every Table 4
@@ -436,4 +538,5 @@ ALL_PINS = [pin_bf16_decode, pin_relevance_bruteforce, pin_relevance_hand, pin_t
             pin_refine_hand, pin_refine_limits, pin_rank_pool_exhaustive,
             pin_rank_pool_structure, pin_attention_dense_library,
             pin_attention_closed_forms, pin_attention_hand, pin_cache_rows,
-            pin_layer_patterns, pin_pattern_composition]
+            pin_layer_patterns, pin_pattern_composition, pin_int2_exact_levels,
+            pin_int2_nearest_level, pin_int2_relevance]

@@ -15,18 +15,23 @@ def _compose(ns, keep=()):
     """anchor/refined selection (and the rank pool, unless itself mutated)
     built from the namespace's own parts, so a mutated part shows through
     them."""
-    def anchor_select(q, kp, bt, g, L, kappa, ps):
+    def proposal_rows(kp, bt, g, pos, ps, int2=False):
+        if not int2:
+            return ns.cache_rows(kp, bt, g, pos, ps)
+        return ns.dequantize_int2(*ns.quantize_int2(ns.cache_row_bits(kp, bt, g, pos, ps)))
+
+    def anchor_select(q, kp, bt, g, L, kappa, ps, int2=False):
         pos = np.arange(L, dtype=np.int64)
-        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pos, ps))
+        s = ns.relevance(q, ns.proposal_rows(kp, bt, g, pos, ps, int2))
         return ns.top_kappa(s, kappa, pos), s
 
-    def refine_in_pool(q, kp, bt, g, pool, kappa, ps):
-        s = ns.relevance(q, ns.cache_rows(kp, bt, g, pool, ps))
+    def refine_in_pool(q, kp, bt, g, pool, kappa, ps, int2=False):
+        s = ns.relevance(q, ns.proposal_rows(kp, bt, g, pool, ps, int2))
         return ns.top_kappa(s, kappa, pool), s
 
-    def refined_select(q, kp, bt, g, L, kappa, ps, A, w):
+    def refined_select(q, kp, bt, g, L, kappa, ps, A, w, int2=False):
         pool = ns.window_pool(A, w, L)
-        t, s = ns.refine_in_pool(q, kp, bt, g, pool, kappa, ps)
+        t, s = ns.refine_in_pool(q, kp, bt, g, pool, kappa, ps, int2)
         return t, pool, s
 
     def rank_pool(s, pos, rho, kappa):
@@ -37,6 +42,8 @@ def _compose(ns, keep=()):
         ns.refine_in_pool = refine_in_pool
     if "rank_pool" not in keep:
         ns.rank_pool = rank_pool
+    if "proposal_rows" not in keep:
+        ns.proposal_rows = proposal_rows
     return ns
 
 
@@ -79,6 +86,36 @@ def _softmax_rows(z):
 def _attn_pair(weights):
     return dict(attention_weights=weights,
                 sparse_attention=lambda q, k, v, s: weights(q, k, s) @ v)
+
+
+def _quantize_with(levels=3, group=32, zero=lambda kg: kg.min(axis=2), rnd=np.rint,
+                   bf16_scale=True, order=None):
+    """The INT2 quantizer with one of its choices changed."""
+    def q(bits, g_unused=32):
+        bits = np.asarray(bits, np.uint16)
+        n, D = bits.shape
+        k = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+        perm = order(D) if order is not None else None
+        if perm is not None:
+            k = k[:, perm]
+        kg = k.reshape(n, D // group, group)
+        mn, mx = kg.min(axis=2), kg.max(axis=2)
+        a = (mx - mn) / np.float32(levels)
+        if bf16_scale:
+            a = po._round_to_bf16(a)
+        b = zero(kg)
+        with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+            c = np.clip(rnd((kg - b[..., None]) / a[..., None]), 0, 3)
+        c = np.where(a[..., None] == 0, 0, c).astype(np.uint8).reshape(n, D)
+        if perm is not None:
+            c = c[:, np.argsort(perm)]
+        reps = 32 // group if group < 32 else 1
+        a64, b64 = a.astype(np.float64), b.astype(np.float64)
+        if group != 32:   # report per 32-dim block (first sub-block's values) for the shapes
+            a64 = a64.reshape(n, -1, reps).max(axis=2) if group < 32 else np.repeat(a64, 2, axis=1)
+            b64 = b64.reshape(n, -1, reps).min(axis=2) if group < 32 else np.repeat(b64, 2, axis=1)
+        return c, a64, b64
+    return q
 
 
 def _step_with(fix):
@@ -142,6 +179,20 @@ MUTANTS = {
         decode_step=_step_with(lambda role, a, sh: (role, sh if role == "R" else a, sh))),
     "every layer a proposal layer": dict(
         decode_step=_step_with(lambda role, a, sh: ("F", a, sh))),
+    "int2 scale over four levels": dict(quantize_int2=_quantize_with(levels=4)),
+    "int2 zero point at the maximum": dict(
+        quantize_int2=_quantize_with(zero=lambda kg: kg.max(axis=2))),
+    "int2 codes truncated": dict(quantize_int2=_quantize_with(rnd=np.floor)),
+    "int2 scale kept in float32": dict(quantize_int2=_quantize_with(bf16_scale=False)),
+    "int2 groups of 16": dict(quantize_int2=_quantize_with(group=16)),
+    "int2 groups of 64": dict(quantize_int2=_quantize_with(group=64)),
+    "int2 groups interleaved": dict(
+        quantize_int2=_quantize_with(
+            order=lambda D: np.arange(D).reshape(32, D // 32).T.reshape(-1))),
+    "int2 scores from the bare codes": dict(
+        dequantize_int2=lambda c, a, b, group=32: np.asarray(c, dtype=np.float64)),
+    "int2 dequantized without the zero point": dict(
+        dequantize_int2=lambda c, a, b, group=32: po.dequantize_int2(c, a, np.zeros_like(b))),
     "logical page ignores block table": dict(
         cache_rows=lambda pages, bt, g, pos, ps: po.bf16_to_f64(
             pages[np.asarray(pos) // ps, g, np.asarray(pos) % ps, :])),
