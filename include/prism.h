@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 3
+#define PRISM_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -70,6 +70,20 @@ typedef enum {
  *                      entries are physical page ids in [0, num_pages).
  *   seq_lens         : int32 [batch]; tokens 0 .. seq_lens[b]-1 are attendable
  *                      (the current token is already in the cache).
+ *   k_codes, k_scales: optional INT2 proposal keys ("Prism Attention", Section
+ *                      4.2, Eqs. 7-8), both NULL or both set, 16-byte aligned,
+ *                      paged exactly like k_pages (same page ids and rows):
+ *     k_codes  uint8 [num_pages][num_kv_heads][page_size][32]: the 128 two-bit
+ *              codes of a key row.  The code of dimension d = 32 s + 8 u + j
+ *              (group s, quarter u, element j, all from 0) is in the row's
+ *              little-endian 32-bit word 2 u + s / 2, at bit
+ *              2 (4 (s % 2) + j / 2) + 16 (j % 2).
+ *     k_scales bf16 [num_pages][num_kv_heads][page_size][4][2]: per group of 32
+ *              dimensions, its scale alpha and zero point beta.
+ *              The key the row stands for is alpha_s * code + beta_s.
+ *   When set, relevance (Eq. 9) at anchor and refined layers is computed from
+ *   them instead of k_pages (attention always reads k_pages and v_pages);
+ *   prism_quantize_keys writes them.
  * Host integers: min_seq_len <= seq_lens[b] <= max_seq_len must hold for all b
  * and max_seq_len <= max_pages_per_seq * page_size.  The library cannot check
  * the device arrays; kernels clamp every length and position so that
@@ -88,6 +102,8 @@ typedef struct {
   int32_t max_pages_per_seq;
   int32_t max_seq_len;
   int32_t min_seq_len;
+  const uint8_t* k_codes;     /* optional INT2 codes, see above (NULL: bf16 keys) */
+  const uint16_t* k_scales;   /* optional INT2 (alpha, beta) per group           */
 } prism_kv_cache;
 
 /*
@@ -188,6 +204,23 @@ PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* k
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * INT2 quantization of keys ("Prism Attention", Section 4.2, Eqs. 7-8):
+ * group-wise asymmetric 2-bit codes of the key rows of the last num_new
+ * positions of every sequence (positions [max(0, seq_lens[b] - num_new),
+ * seq_lens[b]), all KV heads; every position when num_new <= 0), read from
+ * kv->k_pages through the block table and written to k_codes / k_scales in
+ * the layout prism_kv_cache documents.  Per group of 32 dimensions: beta =
+ * the minimum, alpha = (max - min) / 3 rounded to the nearest bf16, code = the
+ * integer nearest (ties to even) to (k - beta) / alpha, clipped to [0, 3], and
+ * 0 when alpha = 0; the subtraction and division are IEEE float32; -0 reads
+ * as +0.  Keys must be finite.  A decode step calls it with num_new = 1 for
+ * every layer after the model appended the new token's key; kv->k_codes and
+ * kv->k_scales are not read.  Rows of other positions are left untouched.
+ */
+PRISM_API prism_status prism_quantize_keys(const prism_kv_cache* kv, int32_t num_new,
+                                           uint8_t* k_codes, uint16_t* k_scales, void* stream);
+
+/*
  * Layer roles of a layer-assignment pattern ("Prism Attention", Algorithm 1's
  * partition into proposal and refined layers; Appendix E, Table 9, for the
  * hybrid with shared layers).
@@ -249,7 +282,8 @@ typedef enum {
   PRISM_KERNEL_CLASSIFY = 5,     /* anchor layer, contexts > 16384: marks the entries
                                     above the kappa-th score's coarse bin, lists the bin */
   PRISM_KERNEL_MERGE = 6,        /* merge of the attention splits into out              */
-  PRISM_KERNEL_KINDS = 7
+  PRISM_KERNEL_QUANTIZE = 7,     /* INT2 codes of key rows (prism_quantize_keys)         */
+  PRISM_KERNEL_KINDS = 8
 } prism_kernel_kind;
 
 /*

@@ -90,7 +90,8 @@ def quantize_int2(k_bits, group: int = INT2_GROUP):
     kept as a bf16 value; each element's code is (k - beta) / alpha rounded to
     the nearest integer (ties to even) and clipped to [0, 2^b - 1]; a constant
     sub-vector (alpha = 0) gets code 0.  The subtraction, division and rounding
-    are float32 operations, the precision the GPU decides the codes in.
+    are float32 operations, the precision the GPU decides the codes in; -0 is
+    read as +0.
 
     k_bits: uint16 bf16 bit patterns [n, D].  Returns (codes uint8 [n, D],
     alpha float64 [n, D / group], beta float64 [n, D / group]), the scales as
@@ -100,6 +101,7 @@ def quantize_int2(k_bits, group: int = INT2_GROUP):
     if D % group:
         raise ValueError("head dimension must be a multiple of the group size")
     k = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).reshape(n, D // group, group)
+    k = k + np.float32(0.0)      # -0 reads as +0 (so a zero point is never -0)
     levels = np.float32(2 ** INT2_BITS - 1)
     mx, mn = k.max(axis=2), k.min(axis=2)
     alpha = _round_to_bf16((mx - mn) / levels)

@@ -36,8 +36,12 @@ def dev(a: np.ndarray) -> torch.Tensor:
 class Setup:
     """Seeded inputs of some layers of a workload, resident on the device."""
 
-    def __init__(self, wl: synth.Workload, layers, pool_rho=0):
+    def __init__(self, wl: synth.Workload, layers, pool_rho=0, int2=False):
+        """int2: quantize every layer's keys on the GPU (prism_quantize_keys)
+        and score from the INT2 codes; the oracle then scores its own
+        quantization of the same keys."""
         self.wl = wl
+        self.int2 = int2
         self.pg = synth.paging(wl)
         self.bt = dev(self.pg.block_table)
         self.sl = dev(self.pg.seq_lens)
@@ -50,6 +54,12 @@ class Setup:
             self.kv[l] = tsa.KVCache(dev(li.k_pages), dev(li.v_pages), self.bt, self.sl,
                                      max_seq_len=int(self.pg.seq_lens.max()),
                                      min_seq_len=int(self.pg.seq_lens.min()))
+            if int2:
+                cs, ss = tsa.int2_shapes(li.k_pages.shape[0], wl.num_kv_heads, wl.page_size)
+                codes = torch.zeros(cs, dtype=torch.uint8, device="cuda")
+                scales = torch.zeros(ss, dtype=torch.int16, device="cuda")
+                tsa.prism_quantize_keys(self.kv[l], 0, codes, scales)
+                self.kv[l] = self.kv[l].with_int2(codes, scales)
         self.pool_rho = pool_rho
         self.params = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window,
                                  pool_rho=pool_rho)
@@ -77,13 +87,14 @@ class Setup:
     def oracle_anchor(self, l, b, g):
         li = self.host[l]
         return oracle.anchor_select(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
-                                    int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size)
+                                    int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size,
+                                    int2=self.int2)
 
     def oracle_refine(self, l, b, g, anchor):
         li = self.host[l]
         return oracle.refined_select(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
                                      int(self.pg.seq_lens[b]), self.wl.kappa, self.wl.page_size,
-                                     np.asarray(anchor, np.int64), self.wl.window)
+                                     np.asarray(anchor, np.int64), self.wl.window, int2=self.int2)
 
     def oracle_rank_pool(self, anchor_scores, b):
         """Eq. 4 on the anchor layer's oracle scores over the whole cache."""
@@ -94,13 +105,25 @@ class Setup:
         li = self.host[l]
         return oracle.refine_in_pool(self.q_group(l, b, g), li.k_pages, self.pg.block_table[b], g,
                                      np.asarray(pool, np.int64), self.wl.kappa,
-                                     self.wl.page_size)
+                                     self.wl.page_size, int2=self.int2)
 
     def oracle_attend(self, l, b, g, sel):
         li = self.host[l]
         return oracle.attend(self.q_group(l, b, g), li.k_pages, li.v_pages, self.pg.block_table[b],
                              g, np.asarray(sel, np.int64), self.wl.page_size,
                              oracle.default_scale(self.wl.head_dim))
+
+
+def unpack_int2_codes(codes) -> np.ndarray:
+    """uint8 [..., 32] rows of INT2 codes -> uint8 [..., 128] codes per
+    dimension, by the layout include/prism.h documents (dimension d = 32 s +
+    8 u + j: 32-bit word 2u + s/2, bit 2 (4 (s % 2) + j / 2) + 16 (j % 2))."""
+    w = np.ascontiguousarray(codes).view("<u4")
+    d = np.arange(128)
+    s, u, j = d // 32, (d % 32) // 8, d % 8
+    word = 2 * u + s // 2
+    bit = 2 * (4 * (s % 2) + j // 2) + 16 * (j % 2)
+    return ((w[..., word] >> bit.astype(np.uint32)) & 3).astype(np.uint8)
 
 
 def check_set(gpu_sel, want, scores, pool, kappa, where=""):

@@ -353,6 +353,15 @@ def pin_int2_exact_levels(impl, seed=22):
         assert np.array_equal(codes, c.reshape(n, M * 32)), "codes"
         assert np.array_equal(a, alpha) and np.array_equal(b, beta)
         assert np.array_equal(impl.dequantize_int2(codes, a, b), k)
+    k = np.zeros((1, 32))                     # -0 and +0 mixed: the zero point is +0
+    k[0, ::3] = -0.0
+    k[0, 5] = 3.0
+    codes, a, b = impl.quantize_int2(_bits(k))
+    assert b[0, 0] == 0.0 and math.copysign(1.0, b[0, 0]) > 0 and a[0, 0] == 1.0
+    assert codes[0, 5] == 3 and codes[0].sum() == 3
+    k = np.array([[0.0, 3.0, 0.5, 1.5, 2.5] + [0.0] * 27])   # exact midpoints go to even codes
+    codes, a, b = impl.quantize_int2(_bits(k))
+    assert list(codes[0, :5]) == [0, 3, 0, 2, 2] and a[0, 0] == 1.0
     k = np.repeat(np.array([[1.5, -2.0, 0.0, 3.25]]), 32, axis=1)   # four constant groups
     codes, a, b = impl.quantize_int2(_bits(k))
     assert not codes.any() and not a.any() and list(b[0]) == [1.5, -2.0, 0.0, 3.25]

@@ -14,7 +14,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation
 def _kv(**over):
     d = dict(k_pages=FAKE, v_pages=FAKE, block_table=FAKE, seq_lens=FAKE, batch=2,
              num_kv_heads=8, head_dim=128, page_size=64, num_pages=1024, max_pages_per_seq=512,
-             max_seq_len=32768, min_seq_len=4096)
+             max_seq_len=32768, min_seq_len=4096, k_codes=None, k_scales=None)
     d.update(over)
     return L.KVCacheStruct(*[d[n] for n, _ in L.KVCacheStruct._fields_])
 
@@ -51,14 +51,14 @@ def test_library_exports_every_declared_function():
                              "prism_sparse_attn", "prism_decode_layer", "prism_status_string",
                              "prism_last_error", "prism_abi_version", "prism_profile_events",
                              "prism_profile_launches", "prism_pattern_role",
-                             "prism_decode_layer_role"}
+                             "prism_decode_layer_role", "prism_quantize_keys"}
     lib = tsa.lib()
     for name in declared:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 3
+    assert tsa.prism_abi_version() == 4
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -205,3 +205,26 @@ def test_decode_layer_role_argument_checks():
 class _FakeKV:
     def __init__(self, struct):
         self.struct = struct
+
+
+def test_int2_cache_fields_checked_on_host():
+    """k_codes and k_scales go together and are 16-byte aligned, in every call
+    that reads the cache; prism_quantize_keys needs both outputs."""
+    lib = tsa.lib()
+    for fn in ("score", "refine", "attn", "layer", "role"):
+        assert _call(fn, _kv(k_codes=FAKE), _params()) == L.PRISM_ERR_INVALID_ARG, fn
+        assert _call(fn, _kv(k_scales=FAKE), _params()) == L.PRISM_ERR_INVALID_ARG, fn
+        assert _call(fn, _kv(k_codes=FAKE + 8, k_scales=FAKE), _params()) == L.PRISM_ERR_INVALID_ARG
+    kv = _kv()
+    assert lib.prism_quantize_keys(None, 1, FAKE, FAKE, None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_quantize_keys(ctypes.byref(kv), 1, None, FAKE, None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_quantize_keys(ctypes.byref(kv), 1, FAKE, None, None) == L.PRISM_ERR_INVALID_ARG
+    assert lib.prism_quantize_keys(ctypes.byref(kv), 1, FAKE + 4, FAKE, None) == \
+        L.PRISM_ERR_INVALID_ARG
+    bad = _kv(head_dim=64)
+    assert lib.prism_quantize_keys(ctypes.byref(bad), 1, FAKE, FAKE, None) == L.PRISM_ERR_UNSUPPORTED
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
+    assert lib.prism_quantize_keys(ctypes.byref(kv), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP
+    assert _call("score", _kv(k_codes=FAKE, k_scales=FAKE), _params()) == L.PRISM_ERR_HIP

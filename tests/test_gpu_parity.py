@@ -12,7 +12,7 @@ import torch
 import oracle
 import synth
 import token_sparse_attention_gqa_amd as tsa
-from tests.parity import Setup, check_attn, check_set, dev
+from tests.parity import Setup, check_attn, check_set, dev, unpack_int2_codes
 
 pytestmark = pytest.mark.gpu
 
@@ -464,6 +464,125 @@ def test_decode_layer_roles_table4_pattern_per_problem_selection():
     probs = [(0, 2), (1, 5), (2, 0), (3, 7)]
     s = _run_pattern(st, "FFSSSS", probs, "roles table-4", table4=True)
     assert s["shared"] == 0
+
+
+# --------------------------------------------------------------------------- INT2 keys
+def _plant_special_groups(kp, bt, L):
+    """Key rows with edge cases, written into the cache of sequence 0, KV head 0:
+    a constant group, -0 and +0 mixed, exact midpoints between levels, values
+    near 1e30 and near 1e-30."""
+    rows = {}
+    vals = np.zeros((4, 128), np.float32)
+    vals[0, :32] = 1.5                                    # constant group
+    vals[0, 32:64] = np.where(np.arange(32) % 3 == 0, -0.0, 0.0)
+    vals[0, 37] = 3.0                                     # -0 / +0 with one level above
+    vals[1, :5] = [0.0, 3.0, 0.5, 1.5, 2.5]               # midpoints: ties to even
+    vals[2, :32] = np.linspace(-1e30, 1e30, 32)
+    vals[2, 32:64] = np.linspace(-3e-30, 5e-30, 32)
+    vals[3] = np.random.default_rng(4).standard_normal(128)
+    for i, pos in enumerate((5, 64, 65, L - 1)):
+        bits = (vals[i].view(np.uint32) >> 16).astype(np.uint16)
+        kp[bt[pos // 64], 0, pos % 64] = bits
+        rows[pos] = bits
+    return rows
+
+
+def test_int2_quantize_bit_exact():
+    """prism_quantize_keys against the oracle's quantizer, code for code and bit
+    for bit in the scales, on a ragged batch with edge-case rows; rows of other
+    positions stay untouched; num_new = 5 rewrites exactly the last 5
+    positions of every sequence."""
+    wl = synth.scaled(synth.TINY_4K, name="int2-quant", wid=198, num_q_heads=16,
+                      num_kv_heads=4, batch=3, context=None, lengths=(6016, 777, 12000),
+                      num_layers=1)
+    pg = synth.paging(wl)
+    li = synth.layer_inputs(wl, 0)
+    kp = li.k_pages.copy()
+    _plant_special_groups(kp, pg.block_table[0], int(pg.seq_lens[0]))
+    bt, sl = dev(pg.block_table), dev(pg.seq_lens)
+    kv = tsa.KVCache(dev(kp), dev(li.v_pages), bt, sl, max_seq_len=int(pg.seq_lens.max()),
+                     min_seq_len=int(pg.seq_lens.min()))
+    cs, ss = tsa.int2_shapes(kp.shape[0], wl.num_kv_heads)
+    for num_new in (0, 5):
+        codes = torch.full(cs, 0xCD, dtype=torch.uint8, device="cuda")
+        scales = torch.full(ss, 0x7BCD, dtype=torch.int16, device="cuda")
+        say(f"[int2-quant] num_new={num_new}")
+        tsa.prism_quantize_keys(kv, num_new, codes, scales)
+        torch.cuda.synchronize()
+        c = codes.cpu().numpy()
+        sc = scales.cpu().numpy().view(np.uint16)
+        touched = np.zeros(cs[:3], bool)
+        for b in range(wl.batch):
+            L = int(pg.seq_lens[b])
+            pos = np.arange(L if num_new == 0 else min(num_new, L))
+            if num_new:
+                pos = L - 1 - pos[::-1]
+            phys = pg.block_table[b][pos // 64]
+            for g in range(wl.num_kv_heads):
+                bits = kp[phys, g, pos % 64]
+                wc, wa, wb = oracle.quantize_int2(bits)
+                got_c = unpack_int2_codes(c[phys, g, pos % 64])
+                assert np.array_equal(got_c, wc), f"codes b{b} g{g}"
+                wa16 = (wa.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+                wb16 = (wb.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+                got_s = sc[phys, g, pos % 64]
+                assert np.array_equal(got_s[..., 0], wa16), f"alpha b{b} g{g}"
+                assert np.array_equal(got_s[..., 1], wb16), f"beta b{b} g{g}"
+                touched[phys, g, pos % 64] = True
+        assert np.all(c[~touched] == 0xCD) and np.all(sc[~touched] == 0x7BCD), "untouched rows"
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_int2_anchor_scores_and_sets(G):
+    """INT2 relevance and anchor selection for every group size, ragged lengths
+    on both sides of the register-selection limit: scores within fp32 rounding
+    of the oracle's (dequantized keys in float64), sets by the index rule."""
+    wl = _small(G, (3000, 17000, 700), kappa=130, wid=300 + G, layers=1, stride=1)
+    st = Setup(wl, [0], int2=True)
+    idx, sc = _anchor_gpu(st, 0, scores=True)
+    stats = {"exact": 0, "near-tie": 0}
+    for b in range(wl.batch):
+        L = int(st.pg.seq_lens[b])
+        for g in range(wl.num_kv_heads):
+            want, s = st.oracle_anchor(0, b, g)
+            np.testing.assert_allclose(sc[b, g, :L], s, rtol=1e-5, atol=1e-5 * np.abs(s).max())
+            stats[check_set(idx[b, g], want, s, np.arange(L), wl.kappa, f"int2 G{G} b{b} g{g}")] += 1
+    say(f"[int2 G={G}] sets: {stats}")
+
+
+@pytest.mark.parametrize("rho", [0, 4])
+def test_int2_decode_chain(rho):
+    """INT2 scoring at anchor and refined layers through prism_decode_layer,
+    window and rank-expanded pools, on a ragged batch (fused kernels)."""
+    wl = synth.scaled(synth.TINY_4K, name=f"int2-chain-{rho}", wid=199, num_q_heads=32,
+                      num_kv_heads=8, batch=3, context=None, lengths=(6016, 20032, 40000),
+                      kappa=512, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=rho, int2=True)
+    probs = [(b, g) for b in range(wl.batch) for g in (2, 7)]
+    if rho:
+        _run_chain_rank(st, range(3), probs, f"int2 rank rho={rho}")
+    else:
+        _run_chain(st, range(3), probs, "int2 window")
+
+
+@pytest.mark.parametrize("G", [1, 16])
+def test_int2_decode_chain_groups(G):
+    """INT2 through the per-problem selection kernels (G = 16) and the
+    smallest group, pools on both sides of 16384 entries."""
+    wl = synth.scaled(synth.TINY_4K, name=f"int2-g{G}", wid=310 + G, num_q_heads=2 * G,
+                      num_kv_heads=2, batch=3, context=None, lengths=(4096, 1500, 20000),
+                      kappa=300, window=100, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), int2=True)
+    _run_chain(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"int2-g{G}")
+
+
+def test_int2_full_size_planted_128k():
+    """The 128K planted workload with INT2 keys in the benchmark's launch
+    configuration: layers 0 (anchor), 1 and 7 (refined), every problem."""
+    wl = synth.LLAMA_128K_PLANTED
+    say(f"[int2 full] {wl.name}")
+    st = Setup(wl, [0, 1, 7], int2=True)
+    _run_chain(st, [0, 1, 7], [(0, g) for g in range(wl.num_kv_heads)], f"int2 {wl.name}")
 
 
 def test_determinism():

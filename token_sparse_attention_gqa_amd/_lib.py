@@ -29,7 +29,8 @@ class KVCacheStruct(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
-                ("max_seq_len", ctypes.c_int32), ("min_seq_len", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("min_seq_len", ctypes.c_int32),
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p)]
 
 
 class ParamsStruct(ctypes.Structure):
@@ -54,6 +55,8 @@ _SIGS = {
     "prism_decode_layer": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
                                           ctypes.POINTER(ParamsStruct), _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "prism_quantize_keys": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), ctypes.c_int32, _P, _P,
+                                           _P]),
     "prism_pattern_role": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_int32, ctypes.c_int32]),
     "prism_decode_layer_role": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
                                                ctypes.POINTER(ParamsStruct), _P, _P, _P,
@@ -71,7 +74,7 @@ ROLES = {"F": 0, "R": 1, "S": 2}
 
 # prism_kernel_kind
 KERNEL_KINDS = {"anchor_score": 0, "refine_score": 1, "select": 2, "attention": 3,
-                "pool_build": 4, "classify": 5, "merge": 6}
+                "pool_build": 4, "classify": 5, "merge": 6, "quantize": 7}
 
 _lib = None
 
@@ -137,8 +140,10 @@ class KVCache:
     """One layer's paged cache: keeps the tensors alive and the C struct."""
 
     def __init__(self, k_pages, v_pages, block_table, seq_lens, *, max_seq_len, min_seq_len,
-                 head_dim=None, page_size=None):
-        self.tensors = (k_pages, v_pages, block_table, seq_lens)
+                 head_dim=None, page_size=None, k_codes=None, k_scales=None):
+        """k_codes / k_scales (optional, together): the INT2 proposal keys,
+        uint8 [num_pages, Hkv, page, 32] and bf16 bits [num_pages, Hkv, page, 4, 2]."""
+        self.tensors = (k_pages, v_pages, block_table, seq_lens, k_codes, k_scales)
         num_pages, hkv, ps, d = k_pages.shape
         if tuple(v_pages.shape) != tuple(k_pages.shape):
             raise ValueError("k_pages and v_pages must have the same shape")
@@ -148,14 +153,20 @@ class KVCache:
             _ptr(block_table, "block_table", itemsize=4), _ptr(seq_lens, "seq_lens", itemsize=4),
             batch, hkv, head_dim if head_dim is not None else d,
             page_size if page_size is not None else ps, num_pages, max_pages, int(max_seq_len),
-            int(min_seq_len))
+            int(min_seq_len), _ptr(k_codes, "k_codes", itemsize=1, optional=True),
+            _ptr(k_scales, "k_scales", itemsize=2, optional=True))
 
-    def with_layer(self, k_pages, v_pages) -> "KVCache":
-        """Same sequences and block table, another layer's K/V arrays."""
+    def with_layer(self, k_pages, v_pages, k_codes=None, k_scales=None) -> "KVCache":
+        """Same sequences and block table, another layer's K/V (and INT2) arrays."""
         bt, sl = self.tensors[2], self.tensors[3]
         s = self.struct
         return KVCache(k_pages, v_pages, bt, sl, max_seq_len=s.max_seq_len,
-                       min_seq_len=s.min_seq_len, head_dim=s.head_dim, page_size=s.page_size)
+                       min_seq_len=s.min_seq_len, head_dim=s.head_dim, page_size=s.page_size,
+                       k_codes=k_codes, k_scales=k_scales)
+
+    def with_int2(self, k_codes, k_scales) -> "KVCache":
+        """The same cache with INT2 proposal keys (or without, given None)."""
+        return self.with_layer(self.tensors[0], self.tensors[1], k_codes, k_scales)
 
 
 def params(num_q_heads, kappa, anchor_stride=1, window=0, softmax_scale=0.0,
@@ -220,6 +231,19 @@ def prism_decode_layer(layer, kv, q, p, anchor_idx, layer_idx_out, out, workspac
                                          optional=True),
                                     _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
            "prism_decode_layer")
+
+
+def prism_quantize_keys(kv, num_new, k_codes, k_scales, stream=None):
+    """INT2 codes and scales of the last num_new positions' keys (all if <= 0)."""
+    _check(lib().prism_quantize_keys(ctypes.byref(kv.struct), int(num_new),
+                                     _ptr(k_codes, "k_codes", itemsize=1),
+                                     _ptr(k_scales, "k_scales", itemsize=2), _stream(stream)),
+           "prism_quantize_keys")
+
+
+def int2_shapes(num_pages, num_kv_heads, page_size=64):
+    """Shapes of the INT2 code and scale arrays for a cache of these pages."""
+    return (num_pages, num_kv_heads, page_size, 32), (num_pages, num_kv_heads, page_size, 4, 2)
 
 
 def prism_pattern_role(pattern: str, layer: int, table4: bool = False) -> int:

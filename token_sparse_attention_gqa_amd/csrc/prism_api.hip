@@ -21,18 +21,19 @@ prism_status fail(prism_status s, const std::string& msg) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Validates the cache description and parameters and fills the geometry.
-prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* g) {
-  if (!kv || !p) return fail(PRISM_ERR_INVALID_ARG, "kv cache and params must not be NULL");
+#define PRISM_TRY(expr)                 \
+  do {                                  \
+    const prism_status _s = (expr);     \
+    if (_s != PRISM_OK) return _s;      \
+  } while (0)
+
+// Validates the cache description alone (the fields every call reads).
+prism_status resolve_cache(const prism_kv_cache* kv) {
+  if (!kv) return fail(PRISM_ERR_INVALID_ARG, "kv cache must not be NULL");
   if (!kv->k_pages || !kv->v_pages || !kv->block_table || !kv->seq_lens)
     return fail(PRISM_ERR_INVALID_ARG, "k_pages, v_pages, block_table and seq_lens must not be NULL");
-  if (kv->batch < 1 || kv->num_kv_heads < 1 || p->num_q_heads < 1)
-    return fail(PRISM_ERR_INVALID_ARG, "batch, num_kv_heads and num_q_heads must be >= 1");
-  if (p->num_q_heads % kv->num_kv_heads != 0)
-    return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
-  const int G = p->num_q_heads / kv->num_kv_heads;
-  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
-    return fail(PRISM_ERR_UNSUPPORTED, "group size num_q_heads/num_kv_heads must be 1, 2, 4, 8 or 16");
+  if (kv->batch < 1 || kv->num_kv_heads < 1)
+    return fail(PRISM_ERR_INVALID_ARG, "batch and num_kv_heads must be >= 1");
   if (kv->head_dim != prism::kHeadDim) return fail(PRISM_ERR_UNSUPPORTED, "head_dim must be 128");
   if (kv->page_size != prism::kPageSize) return fail(PRISM_ERR_UNSUPPORTED, "page_size must be 64");
   if (kv->num_pages < 1 || kv->max_pages_per_seq < 1)
@@ -43,8 +44,48 @@ prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* 
     return fail(PRISM_ERR_INVALID_ARG, "max_seq_len exceeds max_pages_per_seq * page_size");
   if (kv->max_seq_len > prism::kMaxSeqLen)
     return fail(PRISM_ERR_UNSUPPORTED, "max_seq_len above 262144");
-  if ((int64_t)kv->batch * kv->num_kv_heads > (1 << 22) ||
-      (int64_t)kv->batch * p->num_q_heads > (1 << 24))
+  if ((int64_t)kv->batch * kv->num_kv_heads > (1 << 22))
+    return fail(PRISM_ERR_UNSUPPORTED, "batch * heads too large");
+  if ((int64_t)kv->num_pages * kv->num_kv_heads * kv->page_size > (int64_t)UINT32_MAX)
+    return fail(PRISM_ERR_UNSUPPORTED, "num_pages * num_kv_heads * page_size above 2^32 rows");
+  if (!aligned(kv->k_pages, 16) || !aligned(kv->v_pages, 16))
+    return fail(PRISM_ERR_INVALID_ARG, "k_pages and v_pages must be 16-byte aligned");
+  if (!aligned(kv->block_table, 4) || !aligned(kv->seq_lens, 4))
+    return fail(PRISM_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
+  if ((kv->k_codes == nullptr) != (kv->k_scales == nullptr))
+    return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must both be set or both be NULL");
+  if (!aligned(kv->k_codes, 16) || !aligned(kv->k_scales, 16))
+    return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must be 16-byte aligned");
+  return PRISM_OK;
+}
+
+void fill_cache(const prism_kv_cache* kv, Geometry* g) {
+  g->k_pages = kv->k_pages;
+  g->v_pages = kv->v_pages;
+  g->block_table = kv->block_table;
+  g->seq_lens = kv->seq_lens;
+  g->k_codes = kv->k_codes;
+  g->k_scales = kv->k_scales;
+  g->batch = kv->batch;
+  g->hkv = kv->num_kv_heads;
+  g->num_pages = kv->num_pages;
+  g->max_pages = kv->max_pages_per_seq;
+  g->max_seq_len = kv->max_seq_len;
+  g->n_cap = (kv->max_seq_len + 63) / 64 * 64;
+  g->page_stride = (size_t)kv->num_kv_heads * prism::kPageSize * prism::kHeadDim;
+}
+
+// Validates the cache description and parameters and fills the geometry.
+prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* g) {
+  if (!kv || !p) return fail(PRISM_ERR_INVALID_ARG, "kv cache and params must not be NULL");
+  PRISM_TRY(resolve_cache(kv));
+  if (p->num_q_heads < 1) return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be >= 1");
+  if (p->num_q_heads % kv->num_kv_heads != 0)
+    return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
+  const int G = p->num_q_heads / kv->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PRISM_ERR_UNSUPPORTED, "group size num_q_heads/num_kv_heads must be 1, 2, 4, 8 or 16");
+  if ((int64_t)kv->batch * p->num_q_heads > (1 << 24))
     return fail(PRISM_ERR_UNSUPPORTED, "batch * heads too large");
   if (p->kappa < 1 || p->kappa > kv->min_seq_len)
     return fail(PRISM_ERR_INVALID_ARG, "need 1 <= kappa <= min_seq_len");
@@ -56,28 +97,14 @@ prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* 
   if (p->anchor_stride < 1) return fail(PRISM_ERR_INVALID_ARG, "anchor_stride must be >= 1");
   if (!std::isfinite(p->softmax_scale))
     return fail(PRISM_ERR_INVALID_ARG, "softmax_scale must be finite");
-  if (!aligned(kv->k_pages, 16) || !aligned(kv->v_pages, 16))
-    return fail(PRISM_ERR_INVALID_ARG, "k_pages and v_pages must be 16-byte aligned");
-  if (!aligned(kv->block_table, 4) || !aligned(kv->seq_lens, 4))
-    return fail(PRISM_ERR_INVALID_ARG, "block_table and seq_lens must be 4-byte aligned");
 
-  g->k_pages = kv->k_pages;
-  g->v_pages = kv->v_pages;
-  g->block_table = kv->block_table;
-  g->seq_lens = kv->seq_lens;
-  g->batch = kv->batch;
-  g->hkv = kv->num_kv_heads;
+  fill_cache(kv, g);
   g->hq = p->num_q_heads;
   g->group = G;
-  g->num_pages = kv->num_pages;
-  g->max_pages = kv->max_pages_per_seq;
-  g->max_seq_len = kv->max_seq_len;
-  g->n_cap = (kv->max_seq_len + 63) / 64 * 64;
   g->kappa = p->kappa;
   g->window = p->window;
   g->pool_rho = p->pool_rho;
   g->splits = (p->kappa + prism::kAttnSplit - 1) / prism::kAttnSplit;
-  g->page_stride = (size_t)kv->num_kv_heads * prism::kPageSize * prism::kHeadDim;
   return PRISM_OK;
 }
 
@@ -120,11 +147,6 @@ float resolve_scale(const prism_params* p) {
   return p->softmax_scale != 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)prism::kHeadDim);
 }
 
-#define PRISM_TRY(expr)                 \
-  do {                                  \
-    const prism_status _s = (expr);     \
-    if (_s != PRISM_OK) return _s;      \
-  } while (0)
 
 prism_status run_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                         int32_t* out2, hipStream_t s) {
@@ -244,6 +266,21 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   return hip_check(
       prism::launch_refine_attend(g, w, q, resolve_scale(params), layer_idx_out, out, s),
       "refined layer launch");
+}
+
+prism_status prism_quantize_keys(const prism_kv_cache* kv, int32_t num_new, uint8_t* k_codes,
+                                 uint16_t* k_scales, void* stream) {
+  PRISM_TRY(resolve_cache(kv));
+  if (!k_codes || !k_scales)
+    return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must not be NULL");
+  if (!aligned(k_codes, 16) || !aligned(k_scales, 16))
+    return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must be 16-byte aligned");
+  PRISM_TRY(check_device());
+  Geometry g{};
+  fill_cache(kv, &g);
+  return hip_check(prism::launch_quantize(g, num_new, k_codes, k_scales,
+                                          static_cast<hipStream_t>(stream)),
+                   "quantize launch");
 }
 
 int32_t prism_pattern_role(const char* pattern, int32_t table4, int32_t layer) {

@@ -29,6 +29,8 @@ struct Geometry {
   const uint16_t* v_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
+  const uint8_t* k_codes;    // INT2 proposal keys (null: relevance from k_pages)
+  const uint16_t* k_scales;  // their per-group (alpha, beta), bf16
   int batch;
   int hkv;          // KV heads
   int hq;           // query heads
@@ -74,6 +76,7 @@ enum KernelKind {
   kPoolBuild,
   kClassify,
   kMerge,
+  kQuantize,
   kKernelKinds
 };
 
@@ -110,6 +113,10 @@ hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint1
                               int32_t* out, int32_t* out2, hipStream_t s);
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s);
+// INT2 codes and scales of the keys of the last num_new positions of every
+// sequence (every position if num_new <= 0), from k_pages.
+hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint16_t* scales,
+                           hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with
 // use_sel_rows, over the row ids the latest selection left in the workspace.
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,

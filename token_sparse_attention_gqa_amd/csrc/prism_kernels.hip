@@ -32,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NT = kSelThreads;
 constexpr int kSmall = 16384;   // lists up to this length are selected with every key in registers
@@ -506,6 +507,285 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
           sc[e] = m;
           if (counted) atomicAdd(&lh[order_key(m) >> 20], 1u);
         }
+      }
+    }
+  }
+  if (counted) {
+    lds_barrier();
+    uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
+    for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) {
+      const uint32_t c = lh[i];
+      if (c) atomicAdd(&gh[i], c);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// INT2 proposal keys ("Prism Attention", Section 4.2, Eqs. 7-9)
+// ---------------------------------------------------------------------------
+// A token's key is stored as 128 two-bit codes (32 bytes) and, per group of 32
+// dimensions, a bf16 scale alpha and zero point beta (16 bytes), in arrays
+// paged exactly like K, so a row id addresses both.  Code of dimension d =
+// 32 s + 8 u + j (group s, lane quarter u, element j): 32-bit word 2u + s/2 of
+// the token's eight, bit 2 t + 16 (j % 2) with t = 4 (s % 2) + j / 2.  The
+// MFMA B-operand fragment of lane quarter u for group s is then word 2u + s/2,
+// whose element pairs (j, j + 1) sit 16 bits apart: one shift and one mask put
+// a pair into both halves of a bf16x2 register.
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // nearest, ties to even
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Eq. 8 on the keys of positions [max(0, L - num_new), L) of every (sequence,
+// KV head), one thread per token (num_new <= 0: every position).  Per group:
+// beta = min, alpha = (max - min) / 3 rounded to bf16, code = the nearest
+// integer (ties to even) to (k - beta) / alpha clipped to [0, 3], 0 when
+// alpha = 0; the subtraction and division are IEEE float32 (the oracle takes
+// the same decisions in the same precision).  -0 is read as +0.
+__global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales) {
+  const int p = blockIdx.x / chunks, c = blockIdx.x - p * chunks;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int n = seq_len_of(g, b);
+  const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
+  const int pos = first + c * 256 + (int)threadIdx.x;
+  if (pos >= n) return;
+  const size_t row = (size_t)row_id(g, b, kvh, pos);
+  const u32x4* src = reinterpret_cast<const u32x4*>(g.k_pages + row * kHeadDim);
+  uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  u32x4 sc;
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 x = src[4 * s4 + i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * i + 2 * e] = __uint_as_float(x[e] << 16) + 0.0f;
+        v[8 * i + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u) + 0.0f;
+      }
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int d = 1; d < 32; ++d) {
+      mn = fminf(mn, v[d]);
+      mx = fmaxf(mx, v[d]);
+    }
+    const uint32_t ab = f32_to_bf16_bits(__fdiv_rn(mx - mn, 3.0f));
+    const float alpha = __uint_as_float(ab << 16);
+#pragma unroll
+    for (int d = 0; d < 32; ++d) {
+      float code = 0.f;
+      if (alpha != 0.f) code = fminf(fmaxf(rintf(__fdiv_rn(v[d] - mn, alpha)), 0.f), 3.f);
+      const int j = d & 7, u = d >> 3;
+      words[2 * u + (s4 >> 1)] |= (uint32_t)code << (2 * (4 * (s4 & 1) + (j >> 1)) + 16 * (j & 1));
+    }
+    sc[s4] = ab | (__float_as_uint(mn) & 0xFFFF0000u);  // alpha low half, beta high half
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(codes + row * (kHeadDim / 4));
+  dst[0] = u32x4{words[0], words[1], words[2], words[3]};
+  dst[1] = u32x4{words[4], words[5], words[6], words[7]};
+  reinterpret_cast<u32x4*>(scales)[row] = sc;
+}
+
+// The group's query heads as MFMA A operands against INT2 keys.  A tile is 16
+// rows (head h, quantization group m) = row 4 (h mod 4) + m, block diagonal
+// over the four group steps: at step s, row (h, m) holds q_h's dimensions of
+// group s when m = s and zeros otherwise.  The B operand of step s is the
+// token's group-s codes c widened to the bf16 value 2 + c / 2 (exact), so the
+// accumulator of row (h, m) is 2 Q_hm + D_hm / 2 with D_hm = sum over group m
+// of q c and Q_hm = the sum of q over group m, and
+//   <q_h, k-hat> = sum_m alpha_m D_hm + beta_m Q_hm
+//               = sum_m alpha_m (2 acc_hm - 4 Q_hm) + beta_m Q_hm.
+// Output lane (token j, quarter g4) holds rows 4 g4 + m: head 4t + g4 of tile t.
+template <int G>
+struct Int2Query {
+  static constexpr int kTiles = (4 * G + 15) / 16;
+  u32x4 a[kTiles][4];
+  float qs[kTiles][4];   // Q of the output lane's head, per group
+  float nq4[kTiles][4];  // -4 Q
+
+  __device__ __forceinline__ void load(const uint16_t* q, const Geometry& g, int b, int kvh,
+                                       int lane) {
+    const int r = lane & 15, g4 = lane >> 4;
+    const uint16_t* qb = q + ((size_t)b * g.hq + (size_t)kvh * G) * kHeadDim;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      const int h = 4 * t + r / 4, m = r % 4;
+      u32x4 x = u32x4{0u, 0u, 0u, 0u};
+      if (h < G) x = reinterpret_cast<const u32x4*>(qb + (size_t)h * kHeadDim)[4 * m + g4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) a[t][s4] = (m == s4) ? x : u32x4{0u, 0u, 0u, 0u};
+      const int ho = 4 * t + g4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sum = 0.f;
+        if (ho < G) {
+          const u32x4* row = reinterpret_cast<const u32x4*>(qb + (size_t)ho * kHeadDim);
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const u32x4 y = row[4 * i + cc];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sum += __uint_as_float(y[e] << 16) + __uint_as_float(y[e] & 0xFFFF0000u);
+          }
+        }
+        qs[t][i] = sum;
+        nq4[t][i] = -4.f * sum;
+      }
+    }
+  }
+
+  // Relevance of the lane's token (max over the group's heads), valid in every
+  // lane of the token's column.  codes: the lane quarter's two code words;
+  // scl: the token's (alpha, beta) pairs.
+  __device__ __forceinline__ float score(u32x2 codes, u32x4 scl, int g4) const {
+    u32x4 bf[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const uint32_t wd = codes[s4 >> 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 4 * (s4 & 1) + i;
+        const uint32_t sh = t <= 2 ? (wd << (5 - 2 * t)) : (wd >> (2 * t - 5));
+        bf[s4][i] = (sh & 0x00600060u) | 0x40004000u;
+      }
+    }
+    float best = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kTiles; ++t) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t][s4]),
+                                                      __builtin_bit_cast(bf16x8, bf[s4]), acc, 0,
+                                                      0, 0);
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float alpha = __uint_as_float(scl[i] << 16);
+        const float beta = __uint_as_float(scl[i] & 0xFFFF0000u);
+        v = fmaf(alpha, fmaf(2.f, acc[i], nq4[t][i]), fmaf(beta, qs[t][i], v));
+      }
+      if (4 * t + g4 < G) best = fmaxf(best, v);
+    }
+    if (G > 1) best = fmaxf(best, __shfl_xor(best, 16));
+    if (G > 2) best = fmaxf(best, __shfl_xor(best, 32));
+    return best;
+  }
+};
+
+// Anchor-layer relevance from INT2 keys: the work split, the score list and the
+// coarse histogram are those of score_anchor_kernel.  Each wave loads the codes
+// and scales of its four pages at once (16 tiles of 16 tokens; a lane reads its
+// quarter's 8 bytes of codes and the token's 16 bytes of scales per tile), then
+// runs four MFMAs per tile and 16-row tile of (head, group) rows.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
+    Geometry g, Workspace ws, const uint16_t* __restrict__ q, int wgs) {
+  __shared__ uint32_t lh[kCoarseBins];
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int n = seq_len_of(g, b);
+  if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int kPages = kAnchorEntries / 4 / kPageSize;
+  const int wbase = w * kAnchorEntries + wave * (kAnchorEntries / 4);
+  for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
+  lds_barrier();
+  if (wbase < n) {
+    float* sc = ws.scores + (size_t)p * g.n_cap;
+    const int last_page = (n - 1) >> 6;
+    const int j = lane & 15, g4 = lane >> 4;
+    Int2Query<G> qq;
+    qq.load(q, g, b, kvh, lane);
+    const u32x2* cbase = reinterpret_cast<const u32x2*>(g.k_codes);
+    const u32x4* sbase = reinterpret_cast<const u32x4*>(g.k_scales);
+    u32x2 cb[kPages][4];
+    u32x4 sb[kPages][4];
+#pragma unroll
+    for (int r = 0; r < kPages; ++r) {
+      const size_t row0 = (size_t)row_id_of_page(g, phys_page(g, b, min((wbase >> 6) + r, last_page)),
+                                                 kvh, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const size_t row = row0 + u * 16 + j;
+        cb[r][u] = __builtin_nontemporal_load(cbase + row * 4 + g4);
+        sb[r][u] = __builtin_nontemporal_load(sbase + row);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < kPages; ++r) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float m = qq.score(cb[r][u], sb[r][u], g4);
+        const int e = wbase + r * 64 + u * 16 + j;
+        if (g4 == 0 && e < n) {
+          sc[e] = m;
+          atomicAdd(&lh[order_key(m) >> 20], 1u);
+        }
+      }
+    }
+  }
+  lds_barrier();
+  uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
+  for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) {
+    const uint32_t c = lh[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// Refined-layer relevance from INT2 keys over the pool's row ids; work split,
+// scores and optional histogram as in score_pool_kernel.
+template <int G>
+__global__ __launch_bounds__(kScoreThreads) void score_pool_int2_kernel(
+    Geometry g, Workspace ws, const uint16_t* __restrict__ q, int wgs, int chunks, int hist) {
+  __shared__ uint32_t lh[kCoarseBins];
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+  const int base = w * chunks * kPoolEntries;
+  if (base >= n) return;  // uniform over the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool counted = hist != 0 && n > kSmall;  // uniform over the workgroup
+  if (counted) {
+    for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
+    lds_barrier();
+  }
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const uint32_t* prow = ws.pool_row + (size_t)p * g.n_cap;
+  float* sc = ws.scores + (size_t)p * g.n_cap;
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  const int j = lane & 15, g4 = lane >> 4;
+  Int2Query<G> qq;
+  qq.load(q, g, b, kvh, lane);
+  const u32x2* cbase = reinterpret_cast<const u32x2*>(g.k_codes);
+  const u32x4* sbase = reinterpret_cast<const u32x4*>(g.k_scales);
+  constexpr int kTiles = kPoolEntries / 4 / 16;
+  for (int c = 0; c < chunks; ++c) {
+    const int wbase = base + c * kPoolEntries + wave * (kPoolEntries / 4);
+    if (wbase >= n) break;  // uniform over the wave
+    u32x2 cb[kTiles];
+    u32x4 sb[kTiles];
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const size_t row = min(prow[min(wbase + u * 16 + j, n - 1)], max_row);
+      cb[u] = __builtin_nontemporal_load(cbase + row * 4 + g4);
+      sb[u] = __builtin_nontemporal_load(sbase + row);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      const float m = qq.score(cb[u], sb[u], g4);
+      const int e = wbase + u * 16 + j;
+      if (g4 == 0 && e < n) {
+        sc[e] = m;
+        if (counted) atomicAdd(&lh[order_key(m) >> 20], 1u);
       }
     }
   }
@@ -2297,8 +2577,12 @@ template <int G>
 void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
                            hipStream_t s) {
   const int wgs = (g.n_cap + kAnchorEntries - 1) / kAnchorEntries;
-  launch(kAnchorScore, score_anchor_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
-         g, w, q, wgs);
+  if (g.k_codes)
+    launch(kAnchorScore, score_anchor_int2_kernel<G>, dim3(g.problems() * wgs),
+           dim3(kScoreThreads), s, g, w, q, wgs);
+  else
+    launch(kAnchorScore, score_anchor_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
+           g, w, q, wgs);
 }
 
 template <int G>
@@ -2307,8 +2591,12 @@ void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* 
   const int chunks = hist ? kPoolHistChunks : 1;
   const int per_wg = chunks * kPoolEntries;
   const int wgs = (g.n_cap + per_wg - 1) / per_wg;
-  launch(kRefineScore, score_pool_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s, g,
-         w, q, wgs, chunks, hist ? 1 : 0);
+  if (g.k_codes)
+    launch(kRefineScore, score_pool_int2_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads),
+           s, g, w, q, wgs, chunks, hist ? 1 : 0);
+  else
+    launch(kRefineScore, score_pool_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
+           g, w, q, wgs, chunks, hist ? 1 : 0);
 }
 
 template <int G>
@@ -2556,6 +2844,15 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
     case 8: launch_refine_attn_g<8>(g, w, q, scale, out, layer_idx, s); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint16_t* scales,
+                           hipStream_t s) {
+  const int range = (num_new > 0 && num_new < g.max_seq_len) ? num_new : g.max_seq_len;
+  const int chunks = (range + 255) / 256;
+  launch(kQuantize, quantize_kernel, dim3(g.problems() * chunks), dim3(256), s, g, num_new, chunks,
+         codes, scales);
   return hipGetLastError();
 }
 
