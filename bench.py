@@ -76,14 +76,15 @@ def layer_roles(wl, pattern=None):
     return ["F" if wl.is_anchor(l) else "R" for l in range(wl.num_layers)]
 
 
-def launches_per_step(wl, cus, pool_rho=0, roles=None):
+def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False):
     """Kernel launches of each kind in one decode step, mirroring the library's
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
     196608), else a selection kernel per layer precedes the attention, and a
     refined layer whose pool can exceed 16384 entries is classified first.
-    Shared layers launch the attention and its merge only."""
+    Shared layers launch the attention and its merge only; with INT2 keys
+    every layer first quantizes its newest key."""
     import synth
     roles = roles or layer_roles(wl)
     na, nr = roles.count("F"), roles.count("R")
@@ -100,7 +101,7 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None):
             "attention": wl.num_layers,
             "classify": (na if (L > 16384 and L > anchor_need) else 0)
                         + (nr if pool_classify else 0),
-            "merge": wl.num_layers}
+            "merge": wl.num_layers, "quantize": wl.num_layers if int2 else 0}
 
 
 def kernel_source_hash():
@@ -124,7 +125,7 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None):
+def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None, int2=False):
     """The CPU oracle, as it stands, on a bounded sample of the workload: one
     anchor layer and one refined layer (and the attention alone, for shared
     layers) for as many (sequence, KV head) problems as fit in about
@@ -148,18 +149,19 @@ def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None):
         L = int(pg.seq_lens[b])
         t0 = time.perf_counter()
         A, sa = oracle.anchor_select(qa[b, g * G:(g + 1) * G], host[la].k_pages,
-                                     pg.block_table[b], g, L, wl.kappa, wl.page_size)
+                                     pg.block_table[b], g, L, wl.kappa, wl.page_size, int2=int2)
         pool = oracle.rank_pool(sa, np.arange(L), pool_rho, wl.kappa) if pool_rho >= 1 else None
         oracle.attend(qa[b, g * G:(g + 1) * G], host[la].k_pages, host[la].v_pages,
                       pg.block_table[b], g, A, wl.page_size, oracle.default_scale(wl.head_dim))
         t1 = time.perf_counter()
         if pool is not None:
             T, _ = oracle.refine_in_pool(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
-                                         pg.block_table[b], g, pool, wl.kappa, wl.page_size)
+                                         pg.block_table[b], g, pool, wl.kappa, wl.page_size,
+                                         int2=int2)
         else:
             T, _, _ = oracle.refined_select(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
                                             pg.block_table[b], g, L, wl.kappa, wl.page_size, A,
-                                            wl.window)
+                                            wl.window, int2=int2)
         oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
                       pg.block_table[b], g, T, wl.page_size, oracle.default_scale(wl.head_dim))
         t2 = time.perf_counter()
@@ -181,7 +183,9 @@ def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None):
                   + n_sh * float(np.mean(ts)))
     return {"value": wl.batch / step_s, "unit": "tokens/s", "cores": int(blas_threads),
             "kind": "oracle",
-            "sample": (f"oracle (numpy float64) on layer {la} (anchor) and layer {lr} (refined) "
+            "sample": (f"oracle (numpy float64"
+                       + (", INT2 keys quantized from bf16 on the fly" if int2 else "")
+                       + f") on layer {la} (anchor) and layer {lr} (refined) "
                        f"for {done} of {P} (sequence, KV head) problems "
                        f"({time.perf_counter() - t_start:.1f} s); per-problem times "
                        f"extrapolated to {n_anchor} anchor + {n_ref} refined"
@@ -203,6 +207,9 @@ def main():
                     help="layer roles, one letter per layer: F proposal (anchor), R refined, "
                          "S shared (reuses the nearest F or R layer's set); default: every "
                          "anchor_stride-th layer F, the others R")
+    ap.add_argument("--int2", action="store_true",
+                    help="score from INT2 proposal keys (Section 4.2): every layer's keys are "
+                         "quantized before timing, and each timed layer quantizes its newest key")
     ap.add_argument("--distinct-layers", type=int, default=0, metavar="N",
                     help="generate only N layers' inputs and give layer l those of layer l mod N "
                          "(for workloads whose full KV cache does not fit host memory for "
@@ -271,6 +278,12 @@ def main():
             k = torch.from_numpy(li.k_pages.view(np.int16)).to(dev)
             v = torch.from_numpy(li.v_pages.view(np.int16)).to(dev)
             kv_dev[l] = tsa.KVCache(k, v, bt, sl, max_seq_len=L_max, min_seq_len=L_min)
+            if args.int2:   # the prefill's quantization, before timing
+                cs, ss = tsa.int2_shapes(k.shape[0], wl.num_kv_heads, wl.page_size)
+                codes = torch.zeros(cs, dtype=torch.uint8, device=dev)
+                scales = torch.zeros(ss, dtype=torch.int16, device=dev)
+                tsa.prism_quantize_keys(kv_dev[l], 0, codes, scales)
+                kv_dev[l] = kv_dev[l].with_int2(codes, scales)
             if l in keep_host:
                 host_keep[l] = li
             del li
@@ -293,14 +306,17 @@ def main():
     anchor_ptr = anchor.data_ptr()
 
     role_ids = [tsa.ROLES[c] for c in roles]
+    int2_args = [(kv.tensors[4].data_ptr(), kv.tensors[5].data_ptr()) if args.int2 else None
+                 for kv, _, _ in layer_args]
 
     def step():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while recording
-        if args.pattern:
-            for (kv, qp, op), r in zip(layer_args, role_ids):
-                tsa.prism_decode_layer_role(r, kv, qp, p, anchor_ptr, op, ws_arg, s)
-        else:
-            for l, (kv, qp, op) in enumerate(layer_args):
+        for l, (kv, qp, op) in enumerate(layer_args):
+            if args.int2:   # the newest token's key, as a decode step appends one per layer
+                tsa.prism_quantize_keys(kv, 1, int2_args[l][0], int2_args[l][1], s)
+            if args.pattern:
+                tsa.prism_decode_layer_role(role_ids[l], kv, qp, p, anchor_ptr, op, ws_arg, s)
+            else:
                 tsa.prism_decode_layer(l, kv, qp, p, anchor_ptr, None, op, ws_arg, s)
 
     for _ in range(args.warmup):
@@ -342,7 +358,7 @@ def main():
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
     per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
-                                 args.pool_rho, roles)
+                                 args.pool_rho, roles, args.int2)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -374,7 +390,8 @@ def main():
 
     # ---- algorithmic bytes ----------------------------------------------------------
     D2 = wl.head_dim * 2
-    anchor_bytes = int(pg.seq_lens.astype(np.int64).sum()) * wl.num_kv_heads * D2
+    KB = 48 if args.int2 else D2   # key bytes scored per token: INT2 codes + scales, or bf16
+    anchor_bytes = int(pg.seq_lens.astype(np.int64).sum()) * wl.num_kv_heads * KB
     attn_bytes = wl.batch * wl.num_kv_heads * wl.kappa * 2 * D2
     # pool sizes of the refined layers of this step (untimed pass, same inputs)
     pool_len = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=dev)
@@ -386,9 +403,11 @@ def main():
         elif roles[l] == "R":
             tsa.prism_refine_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, tmp_idx, None, pool_len,
                                   None, ws)
-            pool_bytes.append(int(pool_len.sum().item()) * D2)
+            pool_bytes.append(int(pool_len.sum().item()) * KB)
     n_anchor = per_step["anchor_score"]
-    step_bytes = n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
+    quant_bytes = wl.batch * wl.num_kv_heads * (D2 + 48) if args.int2 else 0
+    step_bytes = (n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
+                  + per_step["quantize"] * quant_bytes)
     algo = {"anchor_score": anchor_bytes,
             "refine_score": (sum(pool_bytes) / len(pool_bytes)) if pool_bytes else 0,
             "attention": attn_bytes}
@@ -429,7 +448,8 @@ def main():
                    "page_size": wl.page_size,
                    **({"distinct_layers": nd} if nd < wl.num_layers else {}),
                    **({"pool": "rank", "pool_rho": args.pool_rho} if args.pool_rho >= 1
-                      else {"pool": "window"})},
+                      else {"pool": "window"}),
+                   "keys": "int2" if args.int2 else "bf16"},
         "roofline": roofline,
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
@@ -444,7 +464,7 @@ def main():
 
     if args.cpu_seconds > 0:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho, roles)
+        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho, roles, args.int2)
         result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
     else:

@@ -156,6 +156,7 @@ constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;             // lane 7 - i of each 8-lane half row
+constexpr int kRowMirror = 0x140;                 // lane 15 - i of each 16-lane row
 
 // Inclusive scan of an associative op over the wave (ident: its identity);
 // lane 63 ends with the result over all 64 lanes.
@@ -538,57 +539,56 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // nearest, tie
 }
 
 // Eq. 8 on the keys of positions [max(0, L - num_new), L) of every (sequence,
-// KV head), one thread per token (num_new <= 0: every position).  Per group:
-// beta = min, alpha = (max - min) / 3 rounded to bf16, code = the nearest
-// integer (ties to even) to (k - beta) / alpha clipped to [0, 3], 0 when
-// alpha = 0; the subtraction and division are IEEE float32 (the oracle takes
-// the same decisions in the same precision).  -0 is read as +0.
+// KV head) (num_new <= 0: every position), one wave per token row and four
+// rows per workgroup.  Lane l holds dimensions 2l and 2l + 1, so a group of 32
+// dimensions is one 16-lane row of the wave.  Per group: beta = min, alpha =
+// (max - min) / 3 rounded to bf16, code = the nearest integer (ties to even)
+// to (k - beta) / alpha clipped to [0, 3], 0 when alpha = 0; the subtraction
+// and division are IEEE float32 (the oracle takes the same decisions in the
+// same precision).  -0 is read as +0.
 __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
                                                        uint8_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int p = blockIdx.x / chunks, c = blockIdx.x - p * chunks;
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
   const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
-  const int pos = first + c * 256 + (int)threadIdx.x;
-  if (pos >= n) return;
+  const int pos = first + c * 4 + wv;
+  if (pos >= n) return;  // uniform over the wave
   const size_t row = (size_t)row_id(g, b, kvh, pos);
-  const u32x4* src = reinterpret_cast<const u32x4*>(g.k_pages + row * kHeadDim);
-  uint32_t words[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-  u32x4 sc;
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 x = src[4 * s4 + i];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[8 * i + 2 * e] = __uint_as_float(x[e] << 16) + 0.0f;
-        v[8 * i + 2 * e + 1] = __uint_as_float(x[e] & 0xFFFF0000u) + 0.0f;
-      }
-    }
-    float mn = v[0], mx = v[0];
-#pragma unroll
-    for (int d = 1; d < 32; ++d) {
-      mn = fminf(mn, v[d]);
-      mx = fmaxf(mx, v[d]);
-    }
-    const uint32_t ab = f32_to_bf16_bits(__fdiv_rn(mx - mn, 3.0f));
-    const float alpha = __uint_as_float(ab << 16);
-#pragma unroll
-    for (int d = 0; d < 32; ++d) {
-      float code = 0.f;
-      if (alpha != 0.f) code = fminf(fmaxf(rintf(__fdiv_rn(v[d] - mn, alpha)), 0.f), 3.f);
-      const int j = d & 7, u = d >> 3;
-      words[2 * u + (s4 >> 1)] |= (uint32_t)code << (2 * (4 * (s4 & 1) + (j >> 1)) + 16 * (j & 1));
-    }
-    sc[s4] = ab | (__float_as_uint(mn) & 0xFFFF0000u);  // alpha low half, beta high half
+  const uint32_t x = reinterpret_cast<const uint32_t*>(g.k_pages + row * kHeadDim)[lane];
+  const float v0 = __uint_as_float(x << 16) + 0.0f;
+  const float v1 = __uint_as_float(x & 0xFFFF0000u) + 0.0f;
+  float mn = fminf(v0, v1), mx = fmaxf(v0, v1);
+  // min and max over the 16-lane row: quad, half row, row (every lane gets both)
+  mn = fminf(mn, __uint_as_float(dpp<kQuadXor1, 0xf>(0u, __float_as_uint(mn))));
+  mx = fmaxf(mx, __uint_as_float(dpp<kQuadXor1, 0xf>(0u, __float_as_uint(mx))));
+  mn = fminf(mn, __uint_as_float(dpp<kQuadXor2, 0xf>(0u, __float_as_uint(mn))));
+  mx = fmaxf(mx, __uint_as_float(dpp<kQuadXor2, 0xf>(0u, __float_as_uint(mx))));
+  mn = fminf(mn, __uint_as_float(dpp<kRowHalfMirror, 0xf>(0u, __float_as_uint(mn))));
+  mx = fmaxf(mx, __uint_as_float(dpp<kRowHalfMirror, 0xf>(0u, __float_as_uint(mx))));
+  mn = fminf(mn, __uint_as_float(dpp<kRowMirror, 0xf>(0u, __float_as_uint(mn))));
+  mx = fmaxf(mx, __uint_as_float(dpp<kRowMirror, 0xf>(0u, __float_as_uint(mx))));
+  const uint32_t ab = f32_to_bf16_bits(__fdiv_rn(mx - mn, 3.0f));
+  const float alpha = __uint_as_float(ab << 16);
+  uint32_t c0 = 0u, c1 = 0u;
+  if (alpha != 0.f) {
+    c0 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v0 - mn, alpha)), 0.f), 3.f);
+    c1 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v1 - mn, alpha)), 0.f), 3.f);
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(codes + row * (kHeadDim / 4));
-  dst[0] = u32x4{words[0], words[1], words[2], words[3]};
-  dst[1] = u32x4{words[4], words[5], words[6], words[7]};
-  reinterpret_cast<u32x4*>(scales)[row] = sc;
+  // dimensions 2l, 2l + 1: group s = l / 16, quarter u = (l % 16) / 4, elements
+  // j = 2 (l % 4) and j + 1 -> word 2u + s/2, bits 2 (4 (s % 2) + l % 4) (+ 16)
+  const int s4 = lane >> 4;
+  uint32_t wd = (c0 | (c1 << 16)) << (2 * (4 * (s4 & 1) + (lane & 3)));
+  wd |= dpp<kQuadXor1, 0xf>(0u, wd);
+  wd |= dpp<kQuadXor2, 0xf>(0u, wd);
+  wd |= (uint32_t)__shfl_xor((int)wd, 16);  // groups 2m and 2m + 1 share a word
+  if ((lane & 3) == 0 && (s4 & 1) == 0)
+    reinterpret_cast<uint32_t*>(codes + row * (kHeadDim / 4))[2 * ((lane & 15) >> 2) + (s4 >> 1)] =
+        wd;
+  if ((lane & 15) == 0)  // alpha in the low half, beta in the high half
+    reinterpret_cast<uint32_t*>(scales)[row * 4 + s4] = ab | (__float_as_uint(mn) & 0xFFFF0000u);
 }
 
 // The group's query heads as MFMA A operands against INT2 keys.  A tile is 16
@@ -612,6 +612,7 @@ struct Int2Query {
                                        int lane) {
     const int r = lane & 15, g4 = lane >> 4;
     const uint16_t* qb = q + ((size_t)b * g.hq + (size_t)kvh * G) * kHeadDim;
+    const u32x4 twos = {0x40004000u, 0x40004000u, 0x40004000u, 0x40004000u};  // bf16 2.0
 #pragma unroll
     for (int t = 0; t < kTiles; ++t) {
       const int h = 4 * t + r / 4, m = r % 4;
@@ -619,22 +620,18 @@ struct Int2Query {
       if (h < G) x = reinterpret_cast<const u32x4*>(qb + (size_t)h * kHeadDim)[4 * m + g4];
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) a[t][s4] = (m == s4) ? x : u32x4{0u, 0u, 0u, 0u};
-      const int ho = 4 * t + g4;
+      // the same contraction against code 0 (every B element 2.0) gives 2 Q_hm
+      // in the accumulator layout the scores use
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[t][s4]),
+                                                      __builtin_bit_cast(bf16x8, twos), acc, 0, 0,
+                                                      0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float sum = 0.f;
-        if (ho < G) {
-          const u32x4* row = reinterpret_cast<const u32x4*>(qb + (size_t)ho * kHeadDim);
-#pragma unroll
-          for (int cc = 0; cc < 4; ++cc) {
-            const u32x4 y = row[4 * i + cc];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              sum += __uint_as_float(y[e] << 16) + __uint_as_float(y[e] & 0xFFFF0000u);
-          }
-        }
-        qs[t][i] = sum;
-        nq4[t][i] = -4.f * sum;
+        qs[t][i] = 0.5f * acc[i];
+        nq4[t][i] = -2.f * acc[i];
       }
     }
   }
@@ -678,11 +675,18 @@ struct Int2Query {
   }
 };
 
-// Anchor-layer relevance from INT2 keys: the work split, the score list and the
-// coarse histogram are those of score_anchor_kernel.  Each wave loads the codes
-// and scales of its four pages at once (16 tiles of 16 tokens; a lane reads its
-// quarter's 8 bytes of codes and the token's 16 bytes of scales per tile), then
-// runs four MFMAs per tile and 16-row tile of (head, group) rows.
+// Anchor-layer relevance from INT2 keys: the score list and the coarse
+// histogram are those of score_anchor_kernel.  A workgroup scores
+// kInt2Entries tokens (a key row is 48 bytes here, so a workgroup takes four
+// times the tokens of the bf16 kernel to amortise its histogram and query
+// set-up); each wave takes a quarter of them in rounds of two pages, loading
+// the next round's codes and scales while it scores the current one (per
+// 16-token tile a lane reads its quarter's 8 bytes of codes and the token's 16
+// bytes of scales), four MFMAs per tile and 16-row tile of (head, group) rows.
+constexpr int kInt2Entries = 2048;
+constexpr int kInt2RoundPages = 2;
+constexpr int kInt2Rounds = kInt2Entries / 4 / kPageSize / kInt2RoundPages;
+
 template <int G>
 __global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
     Geometry g, Workspace ws, const uint16_t* __restrict__ q, int wgs) {
@@ -691,45 +695,55 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
-  if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
+  if (w * kInt2Entries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kPages = kAnchorEntries / 4 / kPageSize;
-  const int wbase = w * kAnchorEntries + wave * (kAnchorEntries / 4);
+  constexpr int kRoundTokens = kInt2RoundPages * kPageSize;
+  const int wbase = w * kInt2Entries + wave * (kInt2Entries / 4);
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
   lds_barrier();
   if (wbase < n) {
     float* sc = ws.scores + (size_t)p * g.n_cap;
     const int last_page = (n - 1) >> 6;
+    const int rounds = min(kInt2Rounds, (n - wbase + kRoundTokens - 1) / kRoundTokens);
     const int j = lane & 15, g4 = lane >> 4;
     Int2Query<G> qq;
     qq.load(q, g, b, kvh, lane);
     const u32x2* cbase = reinterpret_cast<const u32x2*>(g.k_codes);
     const u32x4* sbase = reinterpret_cast<const u32x4*>(g.k_scales);
-    u32x2 cb[kPages][4];
-    u32x4 sb[kPages][4];
+    u32x2 cb[2][kInt2RoundPages][4];
+    u32x4 sb[2][kInt2RoundPages][4];
+    auto fetch = [&](int r, u32x2 (&cr)[kInt2RoundPages][4], u32x4 (&sr)[kInt2RoundPages][4]) {
 #pragma unroll
-    for (int r = 0; r < kPages; ++r) {
-      const size_t row0 = (size_t)row_id_of_page(g, phys_page(g, b, min((wbase >> 6) + r, last_page)),
-                                                 kvh, 0);
+      for (int pg = 0; pg < kInt2RoundPages; ++pg) {
+        const int lp = min((wbase >> 6) + r * kInt2RoundPages + pg, last_page);
+        const size_t row0 = (size_t)row_id_of_page(g, phys_page(g, b, lp), kvh, 0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const size_t row = row0 + u * 16 + j;
-        cb[r][u] = __builtin_nontemporal_load(cbase + row * 4 + g4);
-        sb[r][u] = __builtin_nontemporal_load(sbase + row);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 0; r < kPages; ++r) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float m = qq.score(cb[r][u], sb[r][u], g4);
-        const int e = wbase + r * 64 + u * 16 + j;
-        if (g4 == 0 && e < n) {
-          sc[e] = m;
-          atomicAdd(&lh[order_key(m) >> 20], 1u);
+        for (int u = 0; u < 4; ++u) {
+          const size_t row = row0 + u * 16 + j;
+          cr[pg][u] = __builtin_nontemporal_load(cbase + row * 4 + g4);
+          sr[pg][u] = __builtin_nontemporal_load(sbase + row);
         }
       }
+    };
+    fetch(0, cb[0], sb[0]);
+#pragma unroll
+    for (int r = 0; r < kInt2Rounds; ++r) {
+      if (r >= rounds) break;  // uniform over the wave
+      if (r + 1 < rounds) fetch(r + 1, cb[(r + 1) & 1], sb[(r + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pg = 0; pg < kInt2RoundPages; ++pg) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float m = qq.score(cb[r & 1][pg][u], sb[r & 1][pg][u], g4);
+          const int e = wbase + r * kRoundTokens + pg * 64 + u * 16 + j;
+          if (g4 == 0 && e < n) {
+            sc[e] = m;
+            atomicAdd(&lh[order_key(m) >> 20], 1u);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   lds_barrier();
@@ -2576,13 +2590,15 @@ bool fused_fits(const Geometry& g) {
 template <int G>
 void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
                            hipStream_t s) {
-  const int wgs = (g.n_cap + kAnchorEntries - 1) / kAnchorEntries;
-  if (g.k_codes)
+  if (g.k_codes) {
+    const int wgs = (g.n_cap + kInt2Entries - 1) / kInt2Entries;
     launch(kAnchorScore, score_anchor_int2_kernel<G>, dim3(g.problems() * wgs),
            dim3(kScoreThreads), s, g, w, q, wgs);
-  else
+  } else {
+    const int wgs = (g.n_cap + kAnchorEntries - 1) / kAnchorEntries;
     launch(kAnchorScore, score_anchor_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
            g, w, q, wgs);
+  }
 }
 
 template <int G>
@@ -2850,7 +2866,7 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
 hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint16_t* scales,
                            hipStream_t s) {
   const int range = (num_new > 0 && num_new < g.max_seq_len) ? num_new : g.max_seq_len;
-  const int chunks = (range + 255) / 256;
+  const int chunks = (range + 3) / 4;  // four token rows per workgroup
   launch(kQuantize, quantize_kernel, dim3(g.problems() * chunks), dim3(256), s, g, num_new, chunks,
          codes, scales);
   return hipGetLastError();
