@@ -76,7 +76,7 @@ def layer_roles(wl, pattern=None):
     return ["F" if wl.is_anchor(l) else "R" for l in range(wl.num_layers)]
 
 
-def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False):
+def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False, dense=False):
     """Kernel launches of each kind in one decode step, mirroring the library's
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
@@ -86,6 +86,9 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False):
     Shared layers launch the attention and its merge only; with INT2 keys
     every layer first quantizes its newest key."""
     import synth
+    if dense:   # every layer: the dense chunks and their merge
+        return {"anchor_score": 0, "refine_score": 0, "select": 0, "attention": 0, "classify": 0,
+                "merge": wl.num_layers, "quantize": 0, "dense": wl.num_layers}
     roles = roles or layer_roles(wl)
     na, nr = roles.count("F"), roles.count("R")
     L = int(synth.paging(wl).seq_lens.max())
@@ -101,7 +104,7 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False):
             "attention": wl.num_layers,
             "classify": (na if (L > 16384 and L > anchor_need) else 0)
                         + (nr if pool_classify else 0),
-            "merge": wl.num_layers, "quantize": wl.num_layers if int2 else 0}
+            "merge": wl.num_layers, "quantize": wl.num_layers if int2 else 0, "dense": 0}
 
 
 def kernel_source_hash():
@@ -210,6 +213,9 @@ def main():
     ap.add_argument("--int2", action="store_true",
                     help="score from INT2 proposal keys (Section 4.2): every layer's keys are "
                          "quantized before timing, and each timed layer quantizes its newest key")
+    ap.add_argument("--dense", action="store_true",
+                    help="dense decode attention over every cached token at every layer (the "
+                         "full-attention baseline of the sparse path); --cpu-seconds is ignored")
     ap.add_argument("--distinct-layers", type=int, default=0, metavar="N",
                     help="generate only N layers' inputs and give layer l those of layer l mod N "
                          "(for workloads whose full KV cache does not fit host memory for "
@@ -311,6 +317,10 @@ def main():
 
     def step():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while recording
+        if args.dense:
+            for kv, qp, op in layer_args:
+                tsa.prism_dense_attn(kv, qp, p, op, ws_arg, s)
+            return
         for l, (kv, qp, op) in enumerate(layer_args):
             if args.int2:   # the newest token's key, as a decode step appends one per layer
                 tsa.prism_quantize_keys(kv, 1, int2_args[l][0], int2_args[l][1], s)
@@ -358,7 +368,7 @@ def main():
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
     per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
-                                 args.pool_rho, roles, args.int2)
+                                 args.pool_rho, roles, args.int2, args.dense)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -397,7 +407,7 @@ def main():
     pool_len = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=dev)
     tmp_idx = torch.zeros_like(anchor)
     pool_bytes = []
-    for l in range(wl.num_layers):
+    for l in range(0 if args.dense else wl.num_layers):
         if roles[l] == "F":
             tsa.prism_score_topk(kv_dev[l % nd], q_dev[l % nd], p, anchor, None, ws)
         elif roles[l] == "R":
@@ -408,9 +418,12 @@ def main():
     quant_bytes = wl.batch * wl.num_kv_heads * (D2 + 48) if args.int2 else 0
     step_bytes = (n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
                   + per_step["quantize"] * quant_bytes)
+    dense_bytes = int(pg.seq_lens.astype(np.int64).sum()) * wl.num_kv_heads * 2 * D2
+    if args.dense:
+        step_bytes = wl.num_layers * dense_bytes
     algo = {"anchor_score": anchor_bytes,
             "refine_score": (sum(pool_bytes) / len(pool_bytes)) if pool_bytes else 0,
-            "attention": attn_bytes}
+            "attention": attn_bytes, "dense": dense_bytes}
     for kind, k in kernels.items():
         if kind in algo and k["avg_us"] > 0:
             k["algorithmic_bytes_per_launch"] = algo[kind]
@@ -449,7 +462,8 @@ def main():
                    **({"distinct_layers": nd} if nd < wl.num_layers else {}),
                    **({"pool": "rank", "pool_rho": args.pool_rho} if args.pool_rho >= 1
                       else {"pool": "window"}),
-                   "keys": "int2" if args.int2 else "bf16"},
+                   "keys": "int2" if args.int2 else "bf16",
+                   **({"attention": "dense"} if args.dense else {})},
         "roofline": roofline,
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_algorithmic_bytes": int(step_bytes),
@@ -462,7 +476,7 @@ def main():
     if graph_err:
         result["graph_error"] = graph_err
 
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and not args.dense:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
         cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho, roles, args.int2)
         result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)

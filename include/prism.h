@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 4
+#define PRISM_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -204,6 +204,22 @@ PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* k
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * Dense decode attention over every cached token (the FlashAttention-style
+ * baseline "Prism Attention" measures against, Tables 6-8): for every query
+ * head j of KV head g,
+ *   out[b][j] = sum_{i < seq_lens[b]} softmax_i(scale * <q_j, k_i>) * v_i,
+ * in fp32 with an online softmax over chunks of the context (at most 128
+ * chunks of at least 1024 tokens), merged in chunk order.  params->kappa,
+ * window, anchor_stride and pool_rho are validated but not used; the
+ * workspace of prism_workspace_size holds the chunk partials (apart from the
+ * state the sparse calls carry, which a dense call leaves intact).
+ *   out  float [batch][num_q_heads][head_dim].
+ */
+PRISM_API prism_status prism_dense_attn(const prism_kv_cache* kv, const uint16_t* q,
+                                        const prism_params* params, float* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
+/*
  * INT2 quantization of keys ("Prism Attention", Section 4.2, Eqs. 7-8):
  * group-wise asymmetric 2-bit codes of the key rows of the last num_new
  * positions of every sequence (positions [max(0, seq_lens[b] - num_new),
@@ -283,7 +299,8 @@ typedef enum {
                                     above the kappa-th score's coarse bin, lists the bin */
   PRISM_KERNEL_MERGE = 6,        /* merge of the attention splits into out              */
   PRISM_KERNEL_QUANTIZE = 7,     /* INT2 codes of key rows (prism_quantize_keys)         */
-  PRISM_KERNEL_KINDS = 8
+  PRISM_KERNEL_DENSE = 8,        /* dense decode attention chunks (prism_dense_attn)     */
+  PRISM_KERNEL_KINDS = 9
 } prism_kernel_kind;
 
 /*

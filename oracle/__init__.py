@@ -5,10 +5,11 @@ from .prism_oracle import (bf16_to_f64, cache_rows, relevance, top_kappa, window
                            rank_pool, attention_weights, sparse_attention, default_scale,
                            anchor_select, refine_in_pool, refined_select, attend, decode_layer,
                            decode_step, layer_roles, stride_role, cache_row_bits,
-                           quantize_int2, dequantize_int2, proposal_rows, INT2_GROUP)
+                           quantize_int2, dequantize_int2, proposal_rows, INT2_GROUP,
+                           dense_attend)
 
 __all__ = ["bf16_to_f64", "cache_rows", "relevance", "top_kappa", "window_pool", "rank_pool",
            "attention_weights", "sparse_attention", "default_scale", "anchor_select",
            "refine_in_pool", "refined_select", "attend", "decode_layer", "decode_step",
            "layer_roles", "stride_role", "cache_row_bits", "quantize_int2", "dequantize_int2",
-           "proposal_rows", "INT2_GROUP"]
+           "proposal_rows", "INT2_GROUP", "dense_attend"]

@@ -282,6 +282,14 @@ def stride_role(layer: int, anchor_stride: int) -> str:
     return "F" if layer % anchor_stride == 0 else "R"
 
 
+def dense_attend(q_group, k_pages, v_pages, block_table_row, kv_head, length, page_size, scale):
+    """Dense decode attention: SparseAttn with every cached token [0, length)
+    as the set (the full-attention baseline the paper's Tables 6-8 compare
+    the sparse path against).  [G, D]."""
+    return attend(q_group, k_pages, v_pages, block_table_row, kv_head,
+                  np.arange(length, dtype=np.int64), page_size, scale)
+
+
 def decode_layer(layer, q_bits, k_pages, v_pages, block_table, seq_lens, *, num_kv_heads,
                  kappa, anchor_stride, window, page_size, anchor_state=None, scale=None,
                  problems=None, pool_rho=0, pool_state=None, role=None, shared_state=None,

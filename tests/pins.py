@@ -438,6 +438,26 @@ def pin_int2_relevance(impl, seed=24):
         np.testing.assert_allclose(s_int2, s_bf16, rtol=1e-12, atol=1e-12)
 
 
+def pin_dense_attend_library(impl, seed=25):
+    """Dense decode over a paged cache equals torch's scaled_dot_product_attention
+    in float64 on the CPU over the sequence's rows in position order."""
+    import torch
+    rng = np.random.default_rng(seed)
+    for trial in range(8):
+        L, G, D = int(rng.integers(1, 40)), int(rng.integers(1, 4)), 8
+        k = _bf16_round(rng.standard_normal((L, D)))
+        v = _bf16_round(rng.standard_normal((L, D)))
+        q = _bf16_round(rng.standard_normal((G, D)))
+        (kp, vp), bt = _tiny_paged([k, v], page_size=4, seed=trial)
+        scale = 1.0 / math.sqrt(D)
+        got = impl.dense_attend(q, kp, vp, bt, 0, L, 4, scale)
+        qt = torch.from_numpy(q)[:, None, :].double()                       # [G, 1, D]
+        kt = torch.from_numpy(k)[None].double().expand(G, L, D)
+        vt = torch.from_numpy(v)[None].double().expand(G, L, D)
+        want = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, 0]
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)
+
+
 # -------------------------------------------------------------- layer roles
 def pin_layer_patterns(impl):
     """The pages' printed patterns under their own letters: every Table 4
@@ -548,4 +568,4 @@ ALL_PINS = [pin_bf16_decode, pin_relevance_bruteforce, pin_relevance_hand, pin_t
             pin_rank_pool_structure, pin_attention_dense_library,
             pin_attention_closed_forms, pin_attention_hand, pin_cache_rows,
             pin_layer_patterns, pin_pattern_composition, pin_int2_exact_levels,
-            pin_int2_nearest_level, pin_int2_relevance]
+            pin_int2_nearest_level, pin_int2_relevance, pin_dense_attend_library]

@@ -39,6 +39,8 @@ def _call(fn, kv, p, ws=FAKE, nbytes=1 << 40, **extra):
     if fn == "layer":
         return lib.prism_decode_layer(extra.get("layer", 0), kvp, FAKE, pp, FAKE, None, FAKE, ws,
                                       nbytes, None)
+    if fn == "dense":
+        return lib.prism_dense_attn(kvp, FAKE, pp, FAKE, ws, nbytes, None)
     if fn == "role":
         return lib.prism_decode_layer_role(extra.get("role", 0), kvp, FAKE, pp, FAKE, FAKE, ws,
                                            nbytes, None)
@@ -51,14 +53,15 @@ def test_library_exports_every_declared_function():
                              "prism_sparse_attn", "prism_decode_layer", "prism_status_string",
                              "prism_last_error", "prism_abi_version", "prism_profile_events",
                              "prism_profile_launches", "prism_pattern_role",
-                             "prism_decode_layer_role", "prism_quantize_keys"}
+                             "prism_decode_layer_role", "prism_quantize_keys",
+                             "prism_dense_attn"}
     lib = tsa.lib()
     for name in declared:
         assert hasattr(lib, name), name
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 4
+    assert tsa.prism_abi_version() == 5
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -106,7 +109,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["score", "refine", "attn", "layer", "role"])
+@pytest.mark.parametrize("fn", ["score", "refine", "attn", "layer", "role", "dense"])
 @pytest.mark.parametrize("name,args,want", CASES, ids=[c[0] for c in CASES])
 def test_invalid_calls_rejected_on_host(fn, name, args, want):
     kv = args.get("kv", _kv()) if "kv" in args else _kv()
@@ -135,7 +138,7 @@ def test_valid_call_without_gpu_reports_hip_error():
     import torch
     if torch.cuda.device_count() > 0:
         pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
-    for fn in ("score", "refine", "attn", "layer", "role"):
+    for fn in ("score", "refine", "attn", "layer", "role", "dense"):
         st = _call(fn, _kv(), _params())
         assert st == L.PRISM_ERR_HIP, (fn, st)
         assert "device" in tsa.prism_last_error().lower()

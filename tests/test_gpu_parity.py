@@ -585,6 +585,58 @@ def test_int2_full_size_planted_128k():
     _run_chain(st, [0, 1, 7], [(0, g) for g in range(wl.num_kv_heads)], f"int2 {wl.name}")
 
 
+# --------------------------------------------------------------------------- dense decode
+def _dense_check(st, l, problems, label):
+    out = st.out_buf()
+    say(f"[{label}] dense layer {l}")
+    tsa.prism_dense_attn(st.kv[l], st.q[l], st.params, out, st.ws)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    G, li = st.wl.group, st.host[l]
+    for b, g in problems:
+        want = oracle.dense_attend(st.q_group(l, b, g), li.k_pages, li.v_pages,
+                                   st.pg.block_table[b], g, int(st.pg.seq_lens[b]),
+                                   st.wl.page_size, oracle.default_scale(st.wl.head_dim))
+        check_attn(o[b, g * G:(g + 1) * G], want, f"{label} l{l} b{b} g{g}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_dense_decode(G):
+    """Dense decode against the oracle over ragged lengths (a sequence shorter
+    than one chunk, one with a ragged last chunk, one of many chunks)."""
+    wl = _small(G, (6016, 777, 40000), kappa=64, wid=400 + G, layers=1, stride=1)
+    st = Setup(wl, [0])
+    _dense_check(st, 0, [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)],
+                 f"dense G={G}")
+
+
+def test_dense_decode_full_size_planted_128k():
+    """Dense decode at 128K (128 chunks of 1024 tokens), every problem."""
+    wl = synth.LLAMA_128K_PLANTED
+    st = Setup(wl, [0])
+    _dense_check(st, 0, [(0, g) for g in range(wl.num_kv_heads)], "dense 128k")
+
+
+def test_dense_call_keeps_the_sparse_pool():
+    """A dense call between an anchor layer and its refined layer leaves the
+    pool in the workspace: the refined layer's set and output are the same as
+    without it."""
+    wl = synth.scaled(synth.TINY_4K, name="dense-between", wid=410, num_q_heads=32,
+                      num_kv_heads=8, batch=2, context=None, lengths=(6016, 20032), kappa=256,
+                      num_layers=2, anchor_stride=2)
+    st = Setup(wl, [0, 1])
+    res = []
+    for dense_between in (False, True):
+        anchor, sel, out = st.idx_buf(), st.idx_buf(), st.out_buf()
+        tsa.prism_decode_layer(0, st.kv[0], st.q[0], st.params, anchor, None, out, st.ws)
+        if dense_between:
+            tsa.prism_dense_attn(st.kv[0], st.q[0], st.params, st.out_buf(), st.ws)
+        tsa.prism_decode_layer(1, st.kv[1], st.q[1], st.params, anchor, sel, out, st.ws)
+        torch.cuda.synchronize()
+        res.append((sel.cpu().numpy(), out.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []

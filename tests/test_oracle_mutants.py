@@ -193,6 +193,12 @@ MUTANTS = {
         dequantize_int2=lambda c, a, b, group=32: np.asarray(c, dtype=np.float64)),
     "int2 dequantized without the zero point": dict(
         dequantize_int2=lambda c, a, b, group=32: po.dequantize_int2(c, a, np.zeros_like(b))),
+    "dense decode drops the newest token": dict(
+        dense_attend=lambda q, kp, vp, bt, g, L, ps, sc: po.attend(
+            q, kp, vp, bt, g, np.arange(max(L - 1, 1)), ps, sc)),
+    "dense decode without the scale": dict(
+        dense_attend=lambda q, kp, vp, bt, g, L, ps, sc: po.attend(
+            q, kp, vp, bt, g, np.arange(L), ps, 1.0)),
     "logical page ignores block table": dict(
         cache_rows=lambda pages, bt, g, pos, ps: po.bf16_to_f64(
             pages[np.asarray(pos) // ps, g, np.asarray(pos) % ps, :])),

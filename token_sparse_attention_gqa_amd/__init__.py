@@ -8,7 +8,7 @@ from ._lib import (PrismError, KVCache, params, lib, declared_functions, prism_w
                    prism_score_topk, prism_refine_topk, prism_sparse_attn, prism_decode_layer,
                    prism_status_string, prism_last_error, prism_abi_version, prism_profile_events,
                    prism_profile_launches, prism_pattern_role, prism_decode_layer_role,
-                   prism_quantize_keys, int2_shapes,
+                   prism_quantize_keys, int2_shapes, prism_dense_attn,
                    KERNEL_KINDS, ROLES, PRISM_OK,
                    PRISM_ERR_INVALID_ARG, PRISM_ERR_UNSUPPORTED, PRISM_ERR_WORKSPACE,
                    PRISM_ERR_HIP, LIB_PATH)
@@ -17,7 +17,8 @@ __all__ = ["PrismError", "KVCache", "params", "lib", "declared_functions", "pris
            "prism_score_topk", "prism_refine_topk", "prism_sparse_attn", "prism_decode_layer",
            "prism_status_string", "prism_last_error", "prism_abi_version",
            "prism_profile_events", "prism_profile_launches", "prism_pattern_role",
-           "prism_decode_layer_role", "prism_quantize_keys", "int2_shapes", "KERNEL_KINDS",
+           "prism_decode_layer_role", "prism_quantize_keys", "int2_shapes", "prism_dense_attn",
+           "KERNEL_KINDS",
            "ROLES", "PRISM_OK",
            "PRISM_ERR_INVALID_ARG", "PRISM_ERR_UNSUPPORTED", "PRISM_ERR_WORKSPACE",
            "PRISM_ERR_HIP", "LIB_PATH"]

@@ -55,6 +55,8 @@ _SIGS = {
     "prism_decode_layer": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
                                           ctypes.POINTER(ParamsStruct), _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "prism_dense_attn": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), _P,
+                                        ctypes.POINTER(ParamsStruct), _P, _P, ctypes.c_size_t, _P]),
     "prism_quantize_keys": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), ctypes.c_int32, _P, _P,
                                            _P]),
     "prism_pattern_role": (ctypes.c_int32, [ctypes.c_char_p, ctypes.c_int32, ctypes.c_int32]),
@@ -74,7 +76,7 @@ ROLES = {"F": 0, "R": 1, "S": 2}
 
 # prism_kernel_kind
 KERNEL_KINDS = {"anchor_score": 0, "refine_score": 1, "select": 2, "attention": 3,
-                "pool_build": 4, "classify": 5, "merge": 6, "quantize": 7}
+                "pool_build": 4, "classify": 5, "merge": 6, "quantize": 7, "dense": 8}
 
 _lib = None
 
@@ -231,6 +233,15 @@ def prism_decode_layer(layer, kv, q, p, anchor_idx, layer_idx_out, out, workspac
                                          optional=True),
                                     _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
            "prism_decode_layer")
+
+
+def prism_dense_attn(kv, q, p, out, workspace=None, stream=None):
+    """Dense decode attention over every cached token into out [B, Hq, D]."""
+    ws, nbytes = _ws(workspace)
+    _check(lib().prism_dense_attn(ctypes.byref(kv.struct), _ptr(q, "q", itemsize=2),
+                                  ctypes.byref(p), _ptr(out, "out", itemsize=4), ws, nbytes,
+                                  _stream(stream)),
+           "prism_dense_attn")
 
 
 def prism_quantize_keys(kv, num_new, k_codes, k_scales, stream=None):

@@ -268,6 +268,21 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
       "refined layer launch");
 }
 
+prism_status prism_dense_attn(const prism_kv_cache* kv, const uint16_t* q,
+                              const prism_params* params, float* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (!out) return fail(PRISM_ERR_INVALID_ARG, "out must not be NULL");
+  PRISM_TRY(check_ws(g, workspace, workspace_bytes));
+  PRISM_TRY(check_device());
+  const Workspace w = prism::carve_workspace(workspace, g);
+  return hip_check(prism::launch_dense(g, w, q, resolve_scale(params), out,
+                                       static_cast<hipStream_t>(stream)),
+                   "dense attention launch");
+}
+
 prism_status prism_quantize_keys(const prism_kv_cache* kv, int32_t num_new, uint8_t* k_codes,
                                  uint16_t* k_scales, void* stream) {
   PRISM_TRY(resolve_cache(kv));

@@ -65,6 +65,8 @@ struct Workspace {
   int32_t* idx_tmp;       // [P][kappa]
   float* part_o;          // [P][splits][G][head_dim]
   float* part_ml;         // [P][splits][G][2]  (max logit, sum of exponentials)
+  float* dense_o;         // [P][dense splits][G][head_dim]: dense decode partials
+  float* dense_ml;        // [P][dense splits][G][2]
 };
 
 // Kernel kinds, numbered as prism_kernel_kind in prism.h.
@@ -77,6 +79,7 @@ enum KernelKind {
   kClassify,
   kMerge,
   kQuantize,
+  kDense,
   kKernelKinds
 };
 
@@ -117,6 +120,9 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
 // sequence (every position if num_new <= 0), from k_pages.
 hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint16_t* scales,
                            hipStream_t s);
+// Dense decode attention over every cached token into out [B][Hq][D].
+hipError_t launch_dense(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
+                        float* out, hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with
 // use_sel_rows, over the row ids the latest selection left in the workspace.
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,

@@ -1787,6 +1787,18 @@ __device__ __forceinline__ float row16_sum(float v) {
 static_assert(kAttnSplit == 64 && kAttnThreads == 256, "one 16-token tile per wave");
 constexpr int kMergeBatch = 32;  // splits whose partials one merge round loads at once
 constexpr int kMaxSplits = kMaxKappa / kAttnSplit;  // splits of the smallest split size
+constexpr int kDenseMinChunk = 1024;  // dense decode: tokens per workgroup (more above 128K)
+
+// Dense decode splits a context into at most kMaxSplits chunks of whole
+// 64-token multiples (16 tokens per wave step, four waves).
+__host__ __device__ inline int dense_splits(const Geometry& g) {
+  const int sp = (g.n_cap + kDenseMinChunk - 1) / kDenseMinChunk;
+  return sp < 1 ? 1 : (sp > kMaxSplits ? kMaxSplits : sp);
+}
+__host__ __device__ inline int dense_chunk(const Geometry& g) {
+  const int sp = dense_splits(g);
+  return ((g.n_cap + sp - 1) / sp + 63) / 64 * 64;
+}
 
 template <int G>
 constexpr int prob_stride() { return G < 4 ? 4 : G; }
@@ -1796,26 +1808,51 @@ constexpr int prob_stride() { return G < 4 ? 4 : G; }
 // l[r] (lanes 16 g4 .. 16 g4 + 15 agree) and the unnormalised output of every
 // head for dimensions 2 lane, 2 lane + 1 in o0, o1.  pw: the wave's own
 // [16][prob_stride<G>] rows of LDS.
+// The K and V of a wave's 16 tokens: the K fragments of the lane's token
+// (lane % 16) and, per token jj, the V dimensions 2 lane, 2 lane + 1.
+struct KvTile {
+  u32x4 kf[4];
+  uint32_t vv[16];
+};
+
+__device__ __forceinline__ void load_kv_tile(const Geometry& g, uint32_t row, int lane,
+                                             KvTile& t) {
+  const int g4 = lane >> 4;
+  const u32x4* krow = reinterpret_cast<const u32x4*>(g.k_pages + (size_t)row * kHeadDim);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) t.kf[s4] = krow[g4 + 4 * s4];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)row, jj);
+    t.vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
+  }
+}
+
+template <int G>
+__device__ __forceinline__ void attend_tile(const KvTile& t, const u32x4 (&qf)[4], bool valid,
+                                            float scale, float* pw, float (&m)[4],
+                                            float (&l)[4], float (&o0)[G], float (&o1)[G]);
+
 template <int G>
 __device__ __forceinline__ void wave_attend(const Geometry& g, const uint16_t* q, int b, int kvh,
                                             uint32_t row, bool valid, float scale, float* pw,
                                             float (&m)[4], float (&l)[4], float (&o0)[G],
                                             float (&o1)[G]) {
-  constexpr int GP = prob_stride<G>();
-  const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
-  u32x4 kf[4];
-  const u32x4* krow = reinterpret_cast<const u32x4*>(g.k_pages + (size_t)row * kHeadDim);
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) kf[s4] = krow[g4 + 4 * s4];
-  uint32_t vv[16];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)row, jj);
-    vv[jj] = reinterpret_cast<const uint32_t*>(g.v_pages + (size_t)rj * kHeadDim)[lane];
-  }
+  const int lane = threadIdx.x & 63;
+  KvTile t;
+  load_kv_tile(g, row, lane, t);
   u32x4 qf[4];
   load_q_frag<G>(q, g, b, kvh, lane, qf);
-  const f32x4 acc = qk_tile(qf, kf);
+  attend_tile<G>(t, qf, valid, scale, pw, m, l, o0, o1);
+}
+
+template <int G>
+__device__ __forceinline__ void attend_tile(const KvTile& t, const u32x4 (&qf)[4], bool valid,
+                                            float scale, float* pw, float (&m)[4],
+                                            float (&l)[4], float (&o0)[G], float (&o1)[G]) {
+  constexpr int GP = prob_stride<G>();
+  const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+  const f32x4 acc = qk_tile(qf, t.kf);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float z = valid ? acc[r] * scale : -INFINITY;
@@ -1833,8 +1870,8 @@ __device__ __forceinline__ void wave_attend(const Geometry& g, const uint16_t* q
   for (int i = 0; i < G; ++i) o0[i] = o1[i] = 0.f;
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    const float v0 = __uint_as_float(vv[jj] << 16);
-    const float v1 = __uint_as_float(vv[jj] & 0xffff0000u);
+    const float v0 = __uint_as_float(t.vv[jj] << 16);
+    const float v1 = __uint_as_float(t.vv[jj] & 0xffff0000u);
 #pragma unroll
     for (int i4 = 0; i4 < GP / 4; ++i4) {
       const float4 w4 = *reinterpret_cast<const float4*>(&pw[jj * GP + 4 * i4]);
@@ -1990,6 +2027,92 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
         wml[wave][4 * g4 + r][0] = m[r];
         wml[wave][4 * g4 + r][1] = l[r];
       }
+    }
+  }
+  lds_barrier();
+  store_split<G, NW, kAttnThreads>(ws, p, s, splits, wo, wml);
+}
+
+// Dense decode attention (every cached token; the FlashAttention-style
+// baseline of the paper's Tables 6-8): workgroup s of problem p takes tokens
+// [s * chunk, (s + 1) * chunk), each wave a quarter of them in 16-token
+// steps with the next step's K and V in flight; a wave keeps running softmax
+// statistics per head (the step's maximum and sum from the same code as
+// SparseAttn, rescaled to the running maximum) and its unnormalised output,
+// and the workgroup stores one split for merge_kernel.  ws carries the dense
+// partials (dense_o, dense_ml) in place of the sparse ones.
+template <int G>
+__global__ __launch_bounds__(kAttnThreads) void dense_attn_kernel(Geometry g, Workspace ws,
+                                                                  const uint16_t* __restrict__ q,
+                                                                  int splits, int chunk,
+                                                                  float scale) {
+  constexpr int NW = kAttnThreads / 64;
+  __shared__ float wo[NW][G][kHeadDim];
+  __shared__ float wml[NW][G][2];
+  __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15;
+  const int L = seq_len_of(g, b);
+  const int per_wave = chunk / NW;  // a multiple of 16
+  const int start = s * chunk + wave * per_wave;
+  const int steps = clampi((min(L, start + per_wave) - start + 15) / 16, 0, per_wave / 16);
+  float Mr[G], Lr[G], O0[G], O1[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    Mr[i] = -INFINITY;
+    Lr[i] = 0.f;
+    O0[i] = O1[i] = 0.f;
+  }
+  if (steps > 0) {  // uniform over the wave
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    auto row_of = [&](int k) {
+      const int pos = min(start + 16 * k + j, L - 1);
+      return row_id(g, b, kvh, pos);
+    };
+    auto step = [&](const KvTile& t, int k) {
+      float m[4], l[4], o0[G], o1[G];
+      attend_tile<G>(t, qf, start + 16 * k + j < L, scale, pw[wave], m, l, o0, o1);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[i & 3]), 16 * (i >> 2)));
+        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i & 3]), 16 * (i >> 2)));
+        const float Mn = fmaxf(Mr[i], mh);
+        const float fa = (Mr[i] == -INFINITY) ? 0.f : __expf(Mr[i] - Mn);
+        const float fb = (mh == -INFINITY) ? 0.f : __expf(mh - Mn);
+        Lr[i] = Lr[i] * fa + lh * fb;
+        O0[i] = O0[i] * fa + o0[i] * fb;
+        O1[i] = O1[i] * fa + o1[i] * fb;
+        Mr[i] = Mn;
+      }
+    };
+    KvTile t0, t1;
+    load_kv_tile(g, row_of(0), lane, t0);
+    for (int k = 0; k < steps; k += 2) {
+      if (k + 1 < steps) load_kv_tile(g, row_of(k + 1), lane, t1);
+      __builtin_amdgcn_sched_barrier(0);
+      step(t0, k);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 1 < steps) {
+        if (k + 2 < steps) load_kv_tile(g, row_of(k + 2), lane, t0);
+        __builtin_amdgcn_sched_barrier(0);
+        step(t1, k + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    wo[wave][i][2 * lane] = O0[i];
+    wo[wave][i][2 * lane + 1] = O1[i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      wml[wave][i][0] = Mr[i];
+      wml[wave][i][1] = Lr[i];
     }
   }
   lds_barrier();
@@ -2678,6 +2801,8 @@ size_t workspace_bytes(const Geometry& g) {
   o += align256(P * (size_t)g.kappa * 4);                        // idx_tmp
   o += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);  // part_o
   o += align256(P * (size_t)g.splits * g.group * 2 * 4);         // part_ml
+  o += align256(P * (size_t)dense_splits(g) * g.group * kHeadDim * 4);  // dense_o
+  o += align256(P * (size_t)dense_splits(g) * g.group * 2 * 4);         // dense_ml
   return o;
 }
 
@@ -2711,6 +2836,10 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   w.part_o = reinterpret_cast<float*>(c);
   c += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);
   w.part_ml = reinterpret_cast<float*>(c);
+  c += align256(P * (size_t)g.splits * g.group * 2 * 4);
+  w.dense_o = reinterpret_cast<float*>(c);
+  c += align256(P * (size_t)dense_splits(g) * g.group * kHeadDim * 4);
+  w.dense_ml = reinterpret_cast<float*>(c);
   return w;
 }
 
@@ -2860,6 +2989,29 @@ hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uin
     case 8: launch_refine_attn_g<8>(g, w, q, scale, out, layer_idx, s); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dense(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
+                        float* out, hipStream_t s) {
+  const int splits = dense_splits(g), chunk = dense_chunk(g);
+  Workspace wd = w;
+  wd.part_o = w.dense_o;
+  wd.part_ml = w.dense_ml;
+#define PRISM_DENSE(G)                                                                          \
+  launch(kDense, dense_attn_kernel<G>, dim3(g.problems() * splits), dim3(kAttnThreads), s, g, wd, \
+         q, splits, chunk, scale);                                                              \
+  launch_merge_g<G>(g, wd, splits, out, false, s);                                              \
+  break;
+  switch (g.group) {
+    case 1: PRISM_DENSE(1)
+    case 2: PRISM_DENSE(2)
+    case 4: PRISM_DENSE(4)
+    case 8: PRISM_DENSE(8)
+    case 16: PRISM_DENSE(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef PRISM_DENSE
   return hipGetLastError();
 }
 
