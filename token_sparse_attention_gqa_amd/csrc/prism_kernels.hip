@@ -2562,13 +2562,18 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
 // ---------------------------------------------------------------------------
 template <int R>
 __device__ void select_in_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int m,
-                               int32_t* out, int32_t* out2, SelectSmem& sm) {
+                               int32_t* out, int32_t* out2, SelectSmem& sm, bool pos_in_lds) {
   const int t = threadIdx.x, K = g.kappa;
   const size_t base = (size_t)p * g.n_cap;
   const int e0 = R * t;
   const int nv = clampi(m - e0, 0, R);
   uint32_t pos[R], key[R];
-  load_run<R>(ws.pool_pos + base, min(e0, g.n_cap - R), pos);  // n_cap is a multiple of 64
+  if (pos_in_lds) {  // the pool's positions in rank order are in sm.apos
+#pragma unroll
+    for (int i = 0; i < R; ++i) pos[i] = i < nv ? (uint32_t)sm.apos[e0 + i] : 0u;
+  } else {
+    load_run<R>(ws.pool_pos + base, min(e0, g.n_cap - R), pos);  // n_cap is a multiple of 64
+  }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int e = clampi((int)pos[i], 0, g.n_cap - 1);
@@ -2633,6 +2638,7 @@ __global__ __launch_bounds__(NT) void rank_pool_kernel(Geometry g, Workspace ws,
   }
   // 2. the pool in position order
   int pool_n;
+  bool in_lds = false;
   {
     const int words = (L + 31) >> 5;
     const int wpt = (words + NT - 1) / NT;
@@ -2642,26 +2648,64 @@ __global__ __launch_bounds__(NT) void rank_pool_kernel(Geometry g, Workspace ws,
     int o = block_excl_scan<NT>(cnt, sm.tmp, &pool_n);
     int32_t* pp = ws.pool_pos + base;
     uint32_t* pr = ws.pool_row + base;
-    for (int i = w0; i < w1; ++i) {
-      uint32_t mk = sm.bitmap[i];
-      while (mk) {
-        const int e = i * 32 + (__ffs(mk) - 1);
-        mk &= mk - 1u;
-        if (o < g.n_cap) {
-          pp[o] = e;
-          pr[o] = row_id_of_page(g, sm.bt[e >> 6], kvh, e);
+    constexpr int kListWords = 4096 + 1024 + 1024;  // sm.hist, free until the selection below
+    in_lds = pool_n <= kMaxKappa;  // the positions also go to sm.apos (uniform)
+    if (in_lds && words > 2 * NT && words <= kListWords) {
+      // long lists: every word's first rank in sm.hist; then thread t places ranks
+      // [R t, R t + R): a binary search finds the word of its first rank,
+      // and it walks forward through the marks, so every thread does the
+      // same small amount of work whatever the clustering of the marks
+      uint32_t* const wb = sm.hist;
+      for (int i = w0; i < w1; ++i) {
+        wb[i] = (uint32_t)o;
+        o += __popc(sm.bitmap[i]);
+      }
+      lds_barrier();
+      constexpr int R = kMaxKappa / NT;
+      const int r0 = R * t;
+      if (r0 < pool_n) {
+        int lo = 0, hi = words;  // first word whose base exceeds r0, minus one
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int)wb[mid] <= r0) lo = mid + 1;
+          else hi = mid;
         }
-        ++o;
+        int wi = lo - 1;
+        uint32_t mk = sm.bitmap[wi];
+        for (int k = r0 - (int)wb[wi]; k > 0; --k) mk &= mk - 1u;
+        for (int i = 0; i < R && r0 + i < pool_n; ++i) {
+          while (mk == 0u) mk = sm.bitmap[++wi];
+          const int a = wi * 32 + (__ffs(mk) - 1);
+          mk &= mk - 1u;
+          sm.apos[r0 + i] = a;
+          pp[r0 + i] = a;
+          pr[r0 + i] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
+        }
+      }
+    } else {  // a few words per thread: each thread emits its own words' marks
+      for (int i = w0; i < w1; ++i) {
+        uint32_t mk = sm.bitmap[i];
+        while (mk) {
+          const int e = i * 32 + (__ffs(mk) - 1);
+          mk &= mk - 1u;
+          if (o < g.n_cap) {
+            pp[o] = e;
+            pr[o] = row_id_of_page(g, sm.bt[e >> 6], kvh, e);
+            if (in_lds) sm.apos[o] = e;
+          }
+          ++o;
+        }
       }
     }
+    if (in_lds) lds_barrier();  // sm.apos complete; sm.hist free again
     if (t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
   }
-  __syncthreads();  // the pool's global stores are visible to the whole workgroup
+  if (!in_lds) __syncthreads();  // the pool's global stores are visible to the whole workgroup
   // 3. the anchor set: the top-kappa of the pool
   const int mm = min(pool_n, kRegMarks);
-  if (mm <= kSmall / 2) select_in_pool<kSmallPer / 2>(g, ws, p, kvh, mm, out, out2, sm);
-  else if (mm <= kSmall) select_in_pool<kSmallPer>(g, ws, p, kvh, mm, out, out2, sm);
-  else select_in_pool<kRegMarks / NT>(g, ws, p, kvh, mm, out, out2, sm);
+  if (mm <= kSmall / 2) select_in_pool<kSmallPer / 2>(g, ws, p, kvh, mm, out, out2, sm, in_lds);
+  else if (mm <= kSmall) select_in_pool<kSmallPer>(g, ws, p, kvh, mm, out, out2, sm, in_lds);
+  else select_in_pool<kRegMarks / NT>(g, ws, p, kvh, mm, out, out2, sm, in_lds);
   reset_selection_counters(ws, p);
 }
 
