@@ -231,7 +231,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested)", file=sys.stderr, flush=True)
         sys.exit(2)
 

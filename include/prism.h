@@ -6,19 +6,23 @@
  * Mechanism for Efficient LLMs Inference" (arXiv 2610.22985):
  *   - relevance of a cached token to the step's query: Eq. 1 with phi given by
  *     Eq. 9, the maximum over the KV head's group of query heads of <q_j, k_i>
- *     (computed here on the bf16 keys themselves);
+ *     (on the bf16 keys, or on the INT2 keys when the cache carries them);
  *   - exact top-kappa selection: Eq. 2 (anchor / proposal layers);
  *   - refinement inside a candidate pool: Eqs. 5-6 (refined layers), where the
  *     pool is either the union of [i - w, i + w] (clipped to the sequence) over
  *     the anchor layer's selected positions i (window pool), or the anchor
  *     layer's own rho*kappa most relevant tokens (rank-expanded pool, Eq. 4);
  *   - SparseAttn of Algorithm 1: softmax attention of every query head over
- *     its KV head's selected tokens only.
+ *     its KV head's selected tokens only;
+ *   - optional INT2 proposal keys (Section 4.2, Eqs. 7-9), layer roles
+ *     (Algorithm 1's proposal / refined partition, the shared layers of
+ *     Appendix E) and dense decode over the whole cache.
  *
  * Conventions shared by every entry point
  *   - Every array argument is a DEVICE pointer unless marked host.  The
- *     caller owns every buffer; the library allocates nothing and keeps no
- *     state between calls.
+ *     caller owns every buffer; the library allocates no device memory and
+ *     keeps no state between calls (besides the optional benchmark event
+ *     rings and a per-device cache of the compute-unit count).
  *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream)
  *     and return without synchronising.  Arguments are validated on the host
  *     before anything is enqueued; an invalid call enqueues nothing.

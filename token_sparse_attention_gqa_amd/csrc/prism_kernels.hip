@@ -18,7 +18,12 @@
 //                                       SparseAttn over one split;
 //   both           merge_kernel         the splits merged into the output.
 // The single-step entry points and the shapes the fused kernels do not cover
-// use select_kernel, pool_build_kernel and attn_kernel instead.
+// use select_kernel, pool_build_kernel and attn_kernel instead.  Options:
+//   rank-expanded pool (Eq. 4)  rank_pool_kernel: the anchor's top rho*kappa
+//                               as the pool, its top-kappa as the anchor set;
+//   INT2 proposal keys (Eqs. 7-9) quantize_kernel, score_anchor_int2_kernel,
+//                               score_pool_int2_kernel;
+//   dense decode                dense_attn_kernel over every cached token.
 #include "prism_internal.hpp"
 
 #include <hip/hip_ext.h>
