@@ -637,6 +637,32 @@ def test_dense_call_keeps_the_sparse_pool():
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
 
 
+# --------------------------------------------------------------------------- maximum sizes
+def _max_wl():
+    return synth.scaled(synth.TINY_4K, name="max-size", wid=420, num_q_heads=8, num_kv_heads=2,
+                        batch=1, context=262144, lengths=None, kappa=8192, window=2,
+                        num_layers=2, anchor_stride=2)
+
+
+@pytest.mark.parametrize("mode", ["window", "rank", "int2", "dense"])
+def test_maximum_sizes(mode):
+    """The largest supported shapes: a 262144-token context (the anchor layer
+    selects in its own kernel), kappa = 8192, a window pool of about 40K
+    entries (the refined layer's long-pool selection), a rank-expanded pool of
+    rho * kappa = 32768 entries, INT2 keys over the whole context, and dense
+    decode in 128 chunks of 2048 tokens."""
+    wl = _max_wl()
+    rho = 4 if mode == "rank" else 0
+    st = Setup(wl, range(2), pool_rho=rho, int2=(mode == "int2"))
+    probs = [(0, 0), (0, 1)]
+    if mode == "dense":
+        _dense_check(st, 0, probs, "max-size dense")
+    elif mode == "rank":
+        _run_chain_rank(st, range(2), probs, "max-size rank")
+    else:
+        _run_chain(st, range(2), probs, f"max-size {mode}")
+
+
 def test_determinism():
     st = Setup(synth.TINY_4K, [0, 1])
     res = []
