@@ -105,6 +105,22 @@ __device__ __forceinline__ void map_block(int bid, int P, int W, int* p, int* w)
   }
 }
 
+// max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) for every lane l, by the
+// VALU row swaps (v_permlane16_swap / v_permlane32_swap with the value as both
+// operands: each lane receives its partner's value in one of the two results).
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ uint32_t xor16_or(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] | r[1];
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // MFMA A-operand fragment of the group's query heads.  Lane l holds head
 // (l % 16) (zero when >= G) and, for step s, the 16-byte chunk g4 + 4s of the
 // head dimension, g4 = l / 16.  Key fragments use the same chunk order, so the
@@ -143,8 +159,8 @@ __device__ __forceinline__ float group_max(const f32x4& acc, int g4) {
 #pragma unroll
   for (int r = 0; r < 4; ++r)
     if (4 * g4 + r < G) m = fmaxf(m, acc[r]);
-  if (G > 4) m = fmaxf(m, __shfl_xor(m, 16));
-  if (G > 8) m = fmaxf(m, __shfl_xor(m, 32));
+  if (G > 4) m = xor16_max(m);
+  if (G > 8) m = xor32_max(m);
   return m;
 }
 
@@ -588,7 +604,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, 
   uint32_t wd = (c0 | (c1 << 16)) << (2 * (4 * (s4 & 1) + (lane & 3)));
   wd |= dpp<kQuadXor1, 0xf>(0u, wd);
   wd |= dpp<kQuadXor2, 0xf>(0u, wd);
-  wd |= (uint32_t)__shfl_xor((int)wd, 16);  // groups 2m and 2m + 1 share a word
+  wd = xor16_or(wd);  // groups 2m and 2m + 1 share a word
   if ((lane & 3) == 0 && (s4 & 1) == 0)
     reinterpret_cast<uint32_t*>(codes + row * (kHeadDim / 4))[2 * ((lane & 15) >> 2) + (s4 >> 1)] =
         wd;
@@ -674,8 +690,8 @@ struct Int2Query {
       }
       if (4 * t + g4 < G) best = fmaxf(best, v);
     }
-    if (G > 1) best = fmaxf(best, __shfl_xor(best, 16));
-    if (G > 2) best = fmaxf(best, __shfl_xor(best, 32));
+    if (G > 1) best = xor16_max(best);
+    if (G > 2) best = xor32_max(best);
     return best;
   }
 };
