@@ -92,13 +92,19 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False, dense=False):
     roles = roles or layer_roles(wl)
     na, nr = roles.count("F"), roles.count("R")
     L = int(synth.paging(wl).seq_lens.max())
-    fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * -(-wl.kappa // 128) <= cus
-    anchor_fused = fused and L <= 6144 * 32 and pool_rho < 1  # rank pools: per problem
+    splits = -(-wl.kappa // 128)
+    fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * splits <= cus
+    if pool_rho >= 1:   # rank pools: one more workgroup per problem writes the pool
+        anchor_fused = (wl.group <= 8 and L <= 6144 * 32
+                        and wl.batch * wl.num_kv_heads * (splits + 1) <= cus)
+    else:
+        anchor_fused = fused and L <= 6144 * 32
     n_cap = -(-L // 64) * 64
     pool_bound = min(n_cap, pool_rho * wl.kappa if pool_rho >= 1
                      else wl.kappa * (2 * wl.window + 1))
     pool_classify = not fused and pool_bound > 16384 and pool_bound > wl.kappa
-    anchor_need = pool_rho * wl.kappa if pool_rho >= 1 else wl.kappa
+    # the fused rank path classifies for kappa (and rho*kappa in the same pass)
+    anchor_need = pool_rho * wl.kappa if (pool_rho >= 1 and not anchor_fused) else wl.kappa
     return {"anchor_score": na, "refine_score": nr,
             "select": (0 if anchor_fused else na) + (0 if fused else nr),
             "attention": wl.num_layers,

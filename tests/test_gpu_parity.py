@@ -304,6 +304,20 @@ def test_decode_from_leftover_workspace(fill):
         _run_chain(st, range(3), probs, f"leftover-ws {fill:#x} step {rep}")
 
 
+@pytest.mark.parametrize("fill", [0x00, 0xAB, 0xFF])
+def test_rank_pool_from_leftover_workspace(fill):
+    """The rank-expanded pool from a workspace holding arbitrary bytes: both
+    classifications (the anchor set's and the pool's) check their own counters,
+    and two decode steps on the same workspace match the oracle."""
+    wl = synth.scaled(synth.LLAMA_128K_PLANTED, name="leftover-rank", wid=191, context=40960,
+                      kappa=512, n_clusters=16, num_layers=3, anchor_stride=2)
+    st = Setup(wl, range(3), pool_rho=4)
+    st.ws.fill_(fill)
+    probs = [(0, g) for g in range(wl.num_kv_heads)]
+    for rep in range(2):
+        _run_chain_rank(st, range(3), probs, f"leftover-rank {fill:#x} step {rep}")
+
+
 def test_decode_chain_per_problem_selection():
     """A grid the fused kernels do not use (32 problems x 9 splits of 128 > 256
     compute units): every layer selects once per problem (anchor lists and

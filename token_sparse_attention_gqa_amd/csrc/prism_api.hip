@@ -252,13 +252,10 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Workspace w = prism::carve_workspace(workspace, g);
   if (layer % params->anchor_stride == 0) {
-    if (g.pool_rho >= 1) {
-      PRISM_TRY(hip_check(prism::launch_anchor_rank(g, w, q, anchor_idx, layer_idx_out, s),
-                          "anchor layer launch"));
-      return hip_check(prism::launch_attention(g, w, q, nullptr, true, resolve_scale(params),
-                                               out, s),
-                       "anchor layer attention launch");
-    }
+    if (g.pool_rho >= 1)
+      return hip_check(prism::launch_anchor_rank_attend(g, w, q, resolve_scale(params),
+                                                        anchor_idx, layer_idx_out, out, s),
+                       "anchor layer launch");
     return hip_check(prism::launch_anchor_attend(g, w, q, resolve_scale(params), anchor_idx,
                                                  layer_idx_out, out, s),
                      "anchor layer launch");
@@ -331,12 +328,9 @@ prism_status prism_decode_layer_role(int32_t role, const prism_kv_cache* kv, con
   const float scale = resolve_scale(params);
   switch (role) {
     case PRISM_ROLE_PROPOSAL:
-      if (g.pool_rho >= 1) {
-        PRISM_TRY(hip_check(prism::launch_anchor_rank(g, w, q, set_idx, nullptr, s),
-                            "proposal layer launch"));
-        return hip_check(prism::launch_attention(g, w, q, nullptr, true, scale, out, s),
-                         "proposal layer attention launch");
-      }
+      if (g.pool_rho >= 1)
+        return hip_check(prism::launch_anchor_rank_attend(g, w, q, scale, set_idx, nullptr, out, s),
+                         "proposal layer launch");
       return hip_check(prism::launch_anchor_attend(g, w, q, scale, set_idx, nullptr, out, s),
                        "proposal layer launch");
     case PRISM_ROLE_REFINED:

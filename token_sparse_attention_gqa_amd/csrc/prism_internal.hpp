@@ -67,6 +67,13 @@ struct Workspace {
   float* part_ml;         // [P][splits][G][2]  (max logit, sum of exponentials)
   float* dense_o;         // [P][dense splits][G][head_dim]: dense decode partials
   float* dense_ml;        // [P][dense splits][G][2]
+  // a second classification of the anchor list, made in the same pass as the
+  // first (the rank-expanded pool's, beside the anchor set's): as above
+  uint32_t* cand_cnt2;    // [P], right after cand_cnt
+  int32_t* sel_meta2;     // [P][4]
+  uint32_t* cand_key2;    // [P][kMaxCand]
+  int32_t* cand_idx2;     // [P][kMaxCand]
+  uint32_t* gbits2;       // [P][n_cap / 32]
 };
 
 // Kernel kinds, numbered as prism_kernel_kind in prism.h.
@@ -114,6 +121,12 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
 // lists for rho*kappa, the pool and the anchor set (out, out2, row ids).
 hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
                               int32_t* out, int32_t* out2, hipStream_t s);
+// Anchor layer of a decode step with the rank-expanded pool: the anchor set
+// (into anchor_idx and layer_idx, if not null), the pool in the workspace, and
+// SparseAttn over the set into out.
+hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                     float scale, int32_t* anchor_idx, int32_t* layer_idx,
+                                     float* out, hipStream_t s);
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s);
 // INT2 codes and scales of the keys of the last num_new positions of every

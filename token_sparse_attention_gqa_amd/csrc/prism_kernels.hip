@@ -1361,7 +1361,22 @@ __device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm
 __device__ void reset_selection_counters(const Workspace& ws, int p) {
   uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
   for (int i = threadIdx.x; i < kCoarseBins; i += blockDim.x) gh[i] = 0u;
-  if (threadIdx.x == 0) ws.cand_cnt[p] = 0u;
+  if (threadIdx.x == 0) {
+    ws.cand_cnt[p] = 0u;
+    ws.cand_cnt2[p] = 0u;
+  }
+}
+
+// The second classification (the rank-expanded pool's, made in the same
+// classify pass as the anchor set's) as the workspace view classified_marks reads.
+__device__ __forceinline__ Workspace second_class(const Workspace& ws) {
+  Workspace w = ws;
+  w.gbits = ws.gbits2;
+  w.cand_key = ws.cand_key2;
+  w.cand_idx = ws.cand_idx2;
+  w.sel_meta = ws.sel_meta2;
+  w.cand_cnt = ws.cand_cnt2;
+  return w;
 }
 
 // Anchor lists longer than kSmall, after the classify kernel: the entries
@@ -1643,41 +1658,21 @@ __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws
   build_pool(g, ws, p, kvh, L, sm);
 }
 
-// Lists longer than kSmall (the cache at an anchor layer, the pool at a refined
-// layer with `pool`), of which the need_k largest are wanted (kappa, or the
-// size of a rank-expanded pool): workgroup w of problem p takes list entries
-// [w * kClsEntries, +kClsEntries).  From the problem's coarse histogram it
-// finds the bin holding the kappa-th score (every workgroup finds the same
-// bin; workgroup 0 records it with the count of entries above it and in it),
-// marks its entries above that bin in the workspace bitmap and appends the
-// bin's own entries, with their keys, to the problem's candidate list.
-__global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs,
-                                                               int pool, int need_k) {
-  __shared__ int tmp[kClsThreads / 64];
-  __shared__ int res[3];
-  int p, w;
-  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
-  const int b = p / g.hkv;
-  const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : seq_len_of(g, b);
-  const int base = w * kClsEntries;
-  const int need = min(need_k, n);  // entries to select: kappa, or the rank pool's size
-  if (n <= kSmall || n <= need || base >= n) return;  // uniform over the workgroup
+// One classification of workgroup w's list entries (raw, from base) for the
+// `need` largest, into the workspace view wv: the bin holding the need-th score
+// (found from the problem's coarse histogram, h: this thread's 16 bins; every
+// workgroup finds the same bin and workgroup 0 records it with the counts of
+// entries above it and in it), marks of the entries above that bin in wv.gbits
+// and the bin's own entries, with their keys, appended to wv's candidate list.
+// Contains barriers: call uniformly.
+constexpr int kClsU = kClsEntries / (4 * kClsThreads);
+constexpr int kClsBPT = kCoarseBins / kClsThreads;  // 16 bins per thread
+__device__ void classify_into(const Geometry& g, const Workspace& wv, int p, int w, int base,
+                              int n, int need, const u32x4 (&raw)[kClsU],
+                              const u32x4 (&h)[kClsBPT / 4], int* tmp, int* res) {
+  constexpr int U = kClsU, BPT = kClsBPT;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float* sc = ws.scores + (size_t)p * g.n_cap;
-  constexpr int U = kClsEntries / (4 * kClsThreads);
-  u32x4 raw[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int e0 = base + u * 4 * kClsThreads + 4 * t;
-    raw[u] = *reinterpret_cast<const u32x4*>(sc + (e0 < n ? e0 : 0));
-  }
-  // thread t holds bins 4080 - 16t .. 4095 - 16t; scanned in thread order the
-  // counts run down from the top bin
-  constexpr int BPT = kCoarseBins / kClsThreads;  // 16
-  const uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins + kCoarseBins - BPT * (t + 1);
-  u32x4 h[BPT / 4];
-#pragma unroll
-  for (int k = 0; k < BPT / 4; ++k) h[k] = reinterpret_cast<const u32x4*>(gh)[k];
+  lds_barrier();  // readers of res from an earlier call are done
   int sum = 0;
 #pragma unroll
   for (int k = 0; k < BPT / 4; ++k) sum += (int)(h[k][0] + h[k][1] + h[k][2] + h[k][3]);
@@ -1712,13 +1707,13 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
   lds_barrier();
   const int bstar = res[0];
   if (w == 0 && t == 0) {
-    ws.sel_meta[4 * p] = bstar;
-    ws.sel_meta[4 * p + 1] = res[1];
-    ws.sel_meta[4 * p + 2] = res[2];
+    wv.sel_meta[4 * p] = bstar;
+    wv.sel_meta[4 * p + 1] = res[1];
+    wv.sel_meta[4 * p + 2] = res[2];
   }
   if (bstar < 0) return;  // the histogram disagrees with the list: the selection falls back
 
-  uint32_t* gb = ws.gbits + (size_t)p * (g.n_cap >> 5);
+  uint32_t* gb = wv.gbits + (size_t)p * (g.n_cap >> 5);
   uint32_t cand = 0u;  // bit 4u + q4: entry in the threshold bin
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -1752,12 +1747,12 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
   const int wtot = (int)lane63((uint32_t)inc);
   if (wtot) {
     uint32_t off = 0u;
-    if (lane == 0) off = atomicAdd(&ws.cand_cnt[p], (uint32_t)wtot);
+    if (lane == 0) off = atomicAdd(&wv.cand_cnt[p], (uint32_t)wtot);
     // unsigned: a counter left over in the workspace gives slots past the end
     // (nothing is written; the selection's consistency check rejects the pass)
     uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)off) + (uint32_t)(inc - cnt);
-    uint32_t* ck = ws.cand_key + (size_t)p * kMaxCand;
-    int32_t* ci = ws.cand_idx + (size_t)p * kMaxCand;
+    uint32_t* ck = wv.cand_key + (size_t)p * kMaxCand;
+    int32_t* ci = wv.cand_idx + (size_t)p * kMaxCand;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
@@ -1772,6 +1767,42 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
       }
     }
   }
+}
+
+// Lists longer than kSmall (the cache at an anchor layer, the pool at a refined
+// layer with `pool`), of which the need_k largest are wanted (kappa, or the
+// size of a rank-expanded pool): workgroup w of problem p takes list entries
+// [w * kClsEntries, +kClsEntries) and classifies them for need_k into the
+// workspace (classify_into); with need2 > need_k (an anchor list whose rank
+// pool is also wanted) a second time for need2 into the second classification.
+__global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Workspace ws, int wgs,
+                                                               int pool, int need_k, int need2) {
+  __shared__ int tmp[kClsThreads / 64];
+  __shared__ int res[3];
+  int p, w;
+  map_block(blockIdx.x, g.problems(), wgs, &p, &w);
+  const int b = p / g.hkv;
+  const int n = pool ? clampi(ws.pool_len[p], 0, g.n_cap) : seq_len_of(g, b);
+  const int base = w * kClsEntries;
+  const int need = min(need_k, n);  // entries to select: kappa, or the rank pool's size
+  if (n <= kSmall || n <= need || base >= n) return;  // uniform over the workgroup
+  const int t = threadIdx.x;
+  const float* sc = ws.scores + (size_t)p * g.n_cap;
+  u32x4 raw[kClsU];
+#pragma unroll
+  for (int u = 0; u < kClsU; ++u) {
+    const int e0 = base + u * 4 * kClsThreads + 4 * t;
+    raw[u] = *reinterpret_cast<const u32x4*>(sc + (e0 < n ? e0 : 0));
+  }
+  // thread t holds bins 4080 - 16t .. 4095 - 16t; scanned in thread order the
+  // counts run down from the top bin
+  const uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins + kCoarseBins - kClsBPT * (t + 1);
+  u32x4 h[kClsBPT / 4];
+#pragma unroll
+  for (int k = 0; k < kClsBPT / 4; ++k) h[k] = reinterpret_cast<const u32x4*>(gh)[k];
+  classify_into(g, ws, p, w, base, n, need, raw, h, tmp, res);
+  if (need2 > need_k && n > need2)  // uniform over the workgroup
+    classify_into(g, second_class(ws), p, w, base, n, need2, raw, h, tmp, res);
 }
 
 __global__ void zero_counters_kernel(uint32_t* c, int n) {
@@ -2345,6 +2376,83 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 // of the anchor set and of the pool, and attends that slice (16 tokens per
 // wave); merge_kernel, launched next, merges the splits.
 // ---------------------------------------------------------------------------
+// The pool in position order from the marks in sm.bitmap over a list of L
+// entries: positions and row ids to the workspace and its length; with kStage
+// also the positions in rank order to sm.apos when the pool has at most
+// kMaxKappa entries (returns whether they went there).  Long lists emit by
+// rank: every word's first rank in sm.hist, then thread t places ranks
+// [R t, R t + R), a binary search finding the word of its first rank and a walk
+// forward through the marks, so every thread does the same small amount of
+// work whatever the clustering of the marks (a thread owning full mark words
+// would otherwise emit 128 entries while most emit none).  Contains barriers.
+template <bool kStage, typename Sm>
+__device__ bool emit_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L, Sm& sm,
+                          int* pool_n_out) {
+  const int t = threadIdx.x;
+  const size_t base = (size_t)p * g.n_cap;
+  const int words = (L + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0;
+  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
+  int pool_n;
+  int o = block_excl_scan<NT>(cnt, sm.tmp, &pool_n);
+  int32_t* pp = ws.pool_pos + base;
+  uint32_t* pr = ws.pool_row + base;
+  constexpr int kListWords = 4096 + 1024 + 1024;  // sm.hist, free until the caller's next phase
+  const bool staged = kStage && pool_n <= kMaxKappa;  // uniform over the workgroup
+  const bool balanced = pool_n <= kMaxKappa && words > 2 * NT && words <= kListWords;
+  if (balanced) {
+    uint32_t* const wb = sm.hist;
+    for (int i = w0; i < w1; ++i) {
+      wb[i] = (uint32_t)o;
+      o += __popc(sm.bitmap[i]);
+    }
+    lds_barrier();
+    constexpr int R = kMaxKappa / NT;
+    const int r0 = R * t;
+    if (r0 < pool_n) {
+      int lo = 0, hi = words;  // first word whose base exceeds r0, minus one
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if ((int)wb[mid] <= r0) lo = mid + 1;
+        else hi = mid;
+      }
+      int wi = lo - 1;
+      uint32_t mk = sm.bitmap[wi];
+      for (int k = r0 - (int)wb[wi]; k > 0; --k) mk &= mk - 1u;
+      for (int i = 0; i < R && r0 + i < pool_n; ++i) {
+        while (mk == 0u) mk = sm.bitmap[++wi];
+        const int a = wi * 32 + (__ffs(mk) - 1);
+        mk &= mk - 1u;
+        if constexpr (kStage) sm.apos[r0 + i] = a;
+        pp[r0 + i] = a;
+        pr[r0 + i] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
+      }
+    }
+  } else {  // a few words per thread: each thread emits its own words' marks
+    for (int i = w0; i < w1; ++i) {
+      uint32_t mk = sm.bitmap[i];
+      while (mk) {
+        const int e = i * 32 + (__ffs(mk) - 1);
+        mk &= mk - 1u;
+        if (o < g.n_cap) {
+          pp[o] = e;
+          pr[o] = row_id_of_page(g, sm.bt[e >> 6], kvh, e);
+          if constexpr (kStage) {
+            if (staged) sm.apos[o] = e;
+          }
+        }
+        ++o;
+      }
+    }
+  }
+  if (t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
+  if (staged || balanced) lds_barrier();  // sm.apos complete; sm.hist free again
+  *pool_n_out = pool_n;
+  return staged;
+}
+
 template <int G>
 struct AnchorSmem {
   int32_t bt[kMaxPages];
@@ -2381,7 +2489,44 @@ __device__ void small_marks(const float* sc, int n, int K, Sm& sm) {
   lds_barrier();
 }
 
+// Rank-expanded pool (Eq. 4) beside the fused anchor kernel's attention: one
+// extra workgroup per problem marks the cache's top rho*kappa (from the second
+// classification) and writes the pool in position order (only in the kernel's
+// rank-pool instantiation, so the window-pool one is left as it is).
 template <int G>
+__device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Workspace& ws, int pe,
+                                                 AnchorSmem<G>& sm) {
+  const int be = pe / g.hkv, kvhe = pe - be * g.hkv;
+  const int ne = seq_len_of(g, be);
+  const int m = min(g.pool_rho * g.kappa, ne);
+  load_bt(g, be, ne, sm.bt);
+  const float* sce = ws.scores + (size_t)pe * g.n_cap;
+  if (m >= ne) {
+    for (int i = threadIdx.x; i < ((ne + 31) >> 5); i += NT)
+      sm.bitmap[i] = (32 * i + 32 <= ne) ? 0xFFFFFFFFu : ((1u << (ne & 31)) - 1u);
+    lds_barrier();
+  } else if (ne <= kSmall / 2) {
+    small_marks<kSmallPer / 2>(sce, ne, m, sm);
+  } else if (ne <= kSmall) {
+    small_marks<kSmallPer>(sce, ne, m, sm);
+  } else {
+    SelList c;
+    c.sc = sce;
+    c.plist = nullptr;
+    c.prow = nullptr;
+    c.n = ne;
+    c.K = m;
+    c.b = be;
+    c.kvh = kvhe;
+    c.o1 = c.o2 = nullptr;
+    c.srow = nullptr;
+    classified_marks(g, second_class(ws), pe, c, sm);
+  }
+  int pool_n;
+  emit_pool<false>(g, ws, pe, kvhe, ne, sm, &pool_n);
+}
+
+template <int G, bool RANK>
 __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
                                                          float scale,
@@ -2392,6 +2537,12 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
   __shared__ AnchorSmem<G> sm;
   const int K = g.kappa;
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
+  if constexpr (RANK) {
+    if ((int)blockIdx.x >= g.problems() * splits) {  // uniform over the workgroup
+      anchor_rank_emit<G>(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
+      return;
+    }
+  }
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
@@ -2454,7 +2605,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
   const int kt = min(total, K);  // anchors
   const int rend = min(K, r0 + kFusedSplit);
   int32_t* const lens = reinterpret_cast<int32_t*>(sm.cbuf);  // [K]: run lengths, then offsets
-  const int win = min(g.window, n);
+  const int win = RANK ? 0 : min(g.window, n);  // rank pool: written by the extra workgroups
   for (int x = 2 * wave; x < nz_total; x += 2 * (NT / 64)) {
     const int idx = x + (lane >> 5), bit = lane & 31;
     if (idx < nz_total) {
@@ -2530,7 +2681,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
         }
       }
     }
-  } else {
+  } else if (!RANK) {
     // 5. meanwhile the other waves write this split's part of the pool: 8
     //    consecutive entries per thread, the run of the first found by binary
     //    search over the slice's offsets
@@ -2657,70 +2808,9 @@ __global__ __launch_bounds__(NT) void rank_pool_kernel(Geometry g, Workspace ws,
   } else {
     classified_marks(g, ws, p, c, sm);  // after classify_kernel with need m
   }
-  // 2. the pool in position order
+  // 2. the pool in position order (positions also in sm.apos when it fits)
   int pool_n;
-  bool in_lds = false;
-  {
-    const int words = (L + 31) >> 5;
-    const int wpt = (words + NT - 1) / NT;
-    const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
-    int cnt = 0;
-    for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
-    int o = block_excl_scan<NT>(cnt, sm.tmp, &pool_n);
-    int32_t* pp = ws.pool_pos + base;
-    uint32_t* pr = ws.pool_row + base;
-    constexpr int kListWords = 4096 + 1024 + 1024;  // sm.hist, free until the selection below
-    in_lds = pool_n <= kMaxKappa;  // the positions also go to sm.apos (uniform)
-    if (in_lds && words > 2 * NT && words <= kListWords) {
-      // long lists: every word's first rank in sm.hist; then thread t places ranks
-      // [R t, R t + R): a binary search finds the word of its first rank,
-      // and it walks forward through the marks, so every thread does the
-      // same small amount of work whatever the clustering of the marks
-      uint32_t* const wb = sm.hist;
-      for (int i = w0; i < w1; ++i) {
-        wb[i] = (uint32_t)o;
-        o += __popc(sm.bitmap[i]);
-      }
-      lds_barrier();
-      constexpr int R = kMaxKappa / NT;
-      const int r0 = R * t;
-      if (r0 < pool_n) {
-        int lo = 0, hi = words;  // first word whose base exceeds r0, minus one
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((int)wb[mid] <= r0) lo = mid + 1;
-          else hi = mid;
-        }
-        int wi = lo - 1;
-        uint32_t mk = sm.bitmap[wi];
-        for (int k = r0 - (int)wb[wi]; k > 0; --k) mk &= mk - 1u;
-        for (int i = 0; i < R && r0 + i < pool_n; ++i) {
-          while (mk == 0u) mk = sm.bitmap[++wi];
-          const int a = wi * 32 + (__ffs(mk) - 1);
-          mk &= mk - 1u;
-          sm.apos[r0 + i] = a;
-          pp[r0 + i] = a;
-          pr[r0 + i] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
-        }
-      }
-    } else {  // a few words per thread: each thread emits its own words' marks
-      for (int i = w0; i < w1; ++i) {
-        uint32_t mk = sm.bitmap[i];
-        while (mk) {
-          const int e = i * 32 + (__ffs(mk) - 1);
-          mk &= mk - 1u;
-          if (o < g.n_cap) {
-            pp[o] = e;
-            pr[o] = row_id_of_page(g, sm.bt[e >> 6], kvh, e);
-            if (in_lds) sm.apos[o] = e;
-          }
-          ++o;
-        }
-      }
-    }
-    if (in_lds) lds_barrier();  // sm.apos complete; sm.hist free again
-    if (t == 0) ws.pool_len[p] = min(pool_n, g.n_cap);
-  }
+  const bool in_lds = emit_pool<true>(g, ws, p, kvh, L, sm, &pool_n);
   if (!in_lds) __syncthreads();  // the pool's global stores are visible to the whole workgroup
   // 3. the anchor set: the top-kappa of the pool
   const int mm = min(pool_n, kRegMarks);
@@ -2853,7 +2943,7 @@ int64_t profile_launches(int kind) {
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
-  o += align256(P * (kCoarseBins + 1) * 4);                      // ghist, cand_cnt
+  o += align256(P * (kCoarseBins + 2) * 4);                      // ghist, cand_cnt, cand_cnt2
   o += align256(P * 4 * 4);                                      // sel_meta
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_key
   o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx
@@ -2868,6 +2958,10 @@ size_t workspace_bytes(const Geometry& g) {
   o += align256(P * (size_t)g.splits * g.group * 2 * 4);         // part_ml
   o += align256(P * (size_t)dense_splits(g) * g.group * kHeadDim * 4);  // dense_o
   o += align256(P * (size_t)dense_splits(g) * g.group * 2 * 4);         // dense_ml
+  o += align256(P * 4 * 4);                                      // sel_meta2
+  o += align256(P * (size_t)kMaxCand * 4);                       // cand_key2
+  o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx2
+  o += align256(P * (size_t)(g.n_cap / 32) * 4);                 // gbits2
   return o;
 }
 
@@ -2877,7 +2971,8 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   Workspace w;
   w.ghist = reinterpret_cast<uint32_t*>(c);
   w.cand_cnt = w.ghist + P * kCoarseBins;
-  c += align256(P * (kCoarseBins + 1) * 4);
+  w.cand_cnt2 = w.cand_cnt + P;
+  c += align256(P * (kCoarseBins + 2) * 4);
   w.sel_meta = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4 * 4);
   w.cand_key = reinterpret_cast<uint32_t*>(c);
@@ -2905,6 +3000,14 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   w.dense_o = reinterpret_cast<float*>(c);
   c += align256(P * (size_t)dense_splits(g) * g.group * kHeadDim * 4);
   w.dense_ml = reinterpret_cast<float*>(c);
+  c += align256(P * (size_t)dense_splits(g) * g.group * 2 * 4);
+  w.sel_meta2 = reinterpret_cast<int32_t*>(c);
+  c += align256(P * 4 * 4);
+  w.cand_key2 = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * (size_t)kMaxCand * 4);
+  w.cand_idx2 = reinterpret_cast<int32_t*>(c);
+  c += align256(P * (size_t)kMaxCand * 4);
+  w.gbits2 = reinterpret_cast<uint32_t*>(c);
   return w;
 }
 
@@ -2913,7 +3016,7 @@ Workspace carve_workspace(void* base, const Geometry& g) {
 // over many workgroups, then select per problem (and build the pool).
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 1);
+  const int nz = g.problems() * (kCoarseBins + 2);
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -2924,7 +3027,7 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           0, g.kappa);
+           0, g.kappa, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2934,7 +3037,7 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
 
 hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
                               int32_t* out, int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 1);
+  const int nz = g.problems() * (kCoarseBins + 2);
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -2946,7 +3049,7 @@ hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint1
   if (g.max_seq_len > kSmall && g.max_seq_len > m) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           0, (int)m);
+           0, (int)m, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2956,10 +3059,15 @@ hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint1
 
 template <int G>
 void launch_anchor_attn_g(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
-                          float* out, int32_t* anchor_idx, int32_t* layer_idx, hipStream_t s) {
+                          float* out, int32_t* anchor_idx, int32_t* layer_idx, bool rank,
+                          hipStream_t s) {
   const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
-  launch(kAttention, anchor_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
-         scale, anchor_idx, layer_idx);
+  if (rank)
+    launch(kAttention, anchor_attn_kernel<G, true>, dim3(g.problems() * (splits + 1)), dim3(NT), s,
+           g, w, q, scale, anchor_idx, layer_idx);
+  else
+    launch(kAttention, anchor_attn_kernel<G, false>, dim3(g.problems() * splits), dim3(NT), s, g,
+           w, q, scale, anchor_idx, layer_idx);
   launch_merge_g<G>(g, w, splits, out, true, s);
 }
 
@@ -2982,15 +3090,53 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           0, g.kappa);
+           0, g.kappa, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   switch (g.group) {
-    case 1: launch_anchor_attn_g<1>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
-    case 2: launch_anchor_attn_g<2>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
-    case 4: launch_anchor_attn_g<4>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
-    case 8: launch_anchor_attn_g<8>(g, w, q, scale, out, anchor_idx, layer_idx, s); break;
+    case 1: launch_anchor_attn_g<1>(g, w, q, scale, out, anchor_idx, layer_idx, false, s); break;
+    case 2: launch_anchor_attn_g<2>(g, w, q, scale, out, anchor_idx, layer_idx, false, s); break;
+    case 4: launch_anchor_attn_g<4>(g, w, q, scale, out, anchor_idx, layer_idx, false, s); break;
+    case 8: launch_anchor_attn_g<8>(g, w, q, scale, out, anchor_idx, layer_idx, false, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// Anchor layer with the rank-expanded pool.  When the fused anchor kernel's
+// grid, with one more workgroup per problem, fits the device: scoring, one
+// classify pass for both kappa (the anchor set) and rho*kappa (the pool), the
+// fused kernel (its attention workgroups select and attend the anchor set as
+// for the window pool; the extra workgroups write the pool meanwhile), the
+// merge.  Otherwise the per-problem rank kernel, then the attention.
+hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                     float scale, int32_t* anchor_idx, int32_t* layer_idx,
+                                     float* out, hipStream_t s) {
+  const long long splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
+  const bool fits = g.group <= 8 && g.max_seq_len <= kFusedAnchorLen &&
+                    (long long)g.problems() * (splits + 1) <= (long long)device_cus();
+  if (!fits) {
+    hipError_t e = launch_anchor_rank(g, w, q, anchor_idx, layer_idx, s);
+    if (e != hipSuccess) return e;
+    return launch_attention(g, w, q, nullptr, true, scale, out, s);
+  }
+  PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long m = (long long)g.pool_rho * g.kappa;
+  if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
+    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
+           0, g.kappa, g.max_seq_len > m ? (int)m : 0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  switch (g.group) {
+    case 1: launch_anchor_attn_g<1>(g, w, q, scale, out, anchor_idx, layer_idx, true, s); break;
+    case 2: launch_anchor_attn_g<2>(g, w, q, scale, out, anchor_idx, layer_idx, true, s); break;
+    case 4: launch_anchor_attn_g<4>(g, w, q, scale, out, anchor_idx, layer_idx, true, s); break;
+    case 8: launch_anchor_attn_g<8>(g, w, q, scale, out, anchor_idx, layer_idx, true, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -3019,7 +3165,7 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
   if (classify) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
-           1, g.kappa);
+           1, g.kappa, 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
