@@ -210,7 +210,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ int wave_incl_scan(int v) {
   return (int)wave_scan((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
 }
-__device__ __forceinline__ int wave_sum_i(int v) { return (int)lane63((uint32_t)wave_incl_scan(v)); }
 __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
   return lane63(wave_scan(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); }));
 }
@@ -1351,12 +1350,7 @@ __device__ __forceinline__ void select_large_marks(const SelList& c, Sm& sm) {
   lds_barrier();
 }
 
-__device__ void select_large(const Geometry& g, const SelList& c, SelectSmem& sm) {
-  select_large_marks(c, sm);
-  emit_bitmap(g, c, sm);
-}
-
-// Leaves the problem's coarse histogram and candidate counter zero for the
+// Leaves the problem's coarse histogram and candidate counters zero for the
 // next anchor layer (called by one workgroup once nothing reads them).
 __device__ void reset_selection_counters(const Workspace& ws, int p) {
   uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
@@ -2373,9 +2367,12 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 // kSmall, classification).  Every split's workgroup rebuilds the selection as
 // a bitmap over the cache (same inputs, same set), takes the marked entries'
 // ranks, predecessors and run offsets from block scans, writes its rank slice
-// of the anchor set and of the pool, and attends that slice (16 tokens per
-// wave); merge_kernel, launched next, merges the splits.
+// of the anchor set and of the window pool, and attends that slice (16 tokens
+// per wave); merge_kernel, launched next, merges the splits.  The rank-pool
+// instantiation (RANK) writes no window pool: one extra workgroup per problem
+// writes the rank-expanded pool instead (anchor_rank_emit).
 // ---------------------------------------------------------------------------
+
 // The pool in position order from the marks in sm.bitmap over a list of L
 // entries: positions and row ids to the workspace and its length; with kStage
 // also the positions in rank order to sm.apos when the pool has at most
