@@ -396,6 +396,18 @@ def test_decode_chain_rank_pool(rho):
     _run_chain_rank(st, range(3), probs, f"rank-pool rho={rho}")
 
 
+@pytest.mark.parametrize("G", [1, 2, 8, 16])
+def test_decode_chain_rank_pool_groups(G):
+    """The rank-expanded pool for every group size: the fused anchor kernel's
+    rank instantiation (G <= 8, pool written by its extra workgroups) and the
+    per-problem rank kernel (G = 16), lengths on both sides of 16384."""
+    wl = synth.scaled(synth.TINY_4K, name=f"rank-g{G}", wid=430 + G, num_q_heads=2 * G,
+                      num_kv_heads=2, batch=3, context=None, lengths=(4096, 1500, 20000),
+                      kappa=300, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=4)
+    _run_chain_rank(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"rank-g{G}")
+
+
 def test_decode_chain_rank_pool_per_problem_selection():
     """Rank-expanded pool on a grid above the CU count (refined layers select
     once per problem, pools longer than 16384 entries classified first), G = 8."""
