@@ -701,6 +701,82 @@ def test_determinism():
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
 
 
+# ---------------------------------------------------------------------- graph replay
+@pytest.mark.parametrize("mode", ["window", "rank", "int2", "roles", "dense"])
+def test_graph_replay_matches_eager(mode):
+    """The decode step captured once as a HIP graph (the launch the benchmark
+    times) and replayed three times, with eager work and synchronisations
+    between the replays: after an eager step, after the workspace was
+    overwritten with 0xAB bytes, and after a standalone call into another
+    output.  Outputs and sets are cleared before every replay, and each
+    replay's must equal the eager step's bit for bit."""
+    nl, pattern = 4, "FRSR"
+    wl = synth.scaled(synth.LLAMA_128K_PLANTED, name=f"graph-{mode}", wid=450, context=20480,
+                      kappa=512, n_clusters=16, num_layers=nl, anchor_stride=2)
+    st = Setup(wl, range(nl), pool_rho=4 if mode == "rank" else 0, int2=(mode == "int2"))
+    anchor = st.idx_buf()
+    sels = [st.idx_buf() for _ in range(nl)]
+    outs = [st.out_buf() for _ in range(nl)]
+
+    def step():
+        for l in range(nl):
+            kv, q = st.kv[l], st.q[l]
+            if mode == "dense":
+                tsa.prism_dense_attn(kv, q, st.params, outs[l], st.ws)
+            elif mode == "roles":
+                tsa.prism_decode_layer_role(pattern[l], kv, q, st.params, anchor, outs[l], st.ws)
+            else:
+                if mode == "int2":   # the newest position's key, as a decode step appends it
+                    tsa.prism_quantize_keys(kv, 1, kv.tensors[4], kv.tensors[5])
+                tsa.prism_decode_layer(l, kv, q, st.params, anchor, sels[l], outs[l], st.ws)
+
+    def clear():
+        for t in sels + [anchor]:
+            t.fill_(-7)
+        for t in outs:
+            t.fill_(float("nan"))
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return ([t.cpu().numpy().copy() for t in sels + [anchor]],
+                [t.cpu().numpy().view(np.uint32).copy() for t in outs])
+
+    clear()
+    step()
+    want_sets, want_outs = snapshot()
+    assert all(np.all(np.isfinite(o.view(np.float32))) for o in want_outs)
+    if mode not in ("dense", "roles"):
+        assert all((s >= 0).all() for s in want_sets)
+
+    gr = torch.cuda.CUDAGraph()
+    clear()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(gr):
+        step()
+    torch.cuda.synchronize()
+
+    spare = st.out_buf()
+    between = [
+        lambda: step(),
+        lambda: st.ws.fill_(0xAB),
+        lambda: tsa.prism_decode_layer(0, st.kv[0], st.q[0], st.params, st.idx_buf(), None,
+                                       spare, st.ws) if mode != "dense"
+        else tsa.prism_dense_attn(st.kv[0], st.q[0], st.params, spare, st.ws),
+    ]
+    for r, eager_work in enumerate(between):
+        eager_work()
+        torch.cuda.synchronize()
+        clear()
+        say(f"[graph-{mode}] replay {r}")
+        gr.replay()
+        got_sets, got_outs = snapshot()
+        for l in range(nl):
+            assert np.array_equal(got_outs[l], want_outs[l]), f"replay {r}: layer {l} output"
+        for i, (g_s, w_s) in enumerate(zip(got_sets, want_sets)):
+            assert np.array_equal(g_s, w_s), f"replay {r}: index buffer {i}"
+    del gr
+
+
 # ---------------------------------------------------------------------- full sizes
 FULL = [
     (synth.LLAMA_32K, [0, 1, 7], None),
