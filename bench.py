@@ -76,15 +76,17 @@ def layer_roles(wl, pattern=None):
     return ["F" if wl.is_anchor(l) else "R" for l in range(wl.num_layers)]
 
 
-def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False, dense=False):
+def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     """Kernel launches of each kind in one decode step, mirroring the library's
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
     196608), else a selection kernel per layer precedes the attention, and a
     refined layer whose pool can exceed 16384 entries is classified first.
-    Shared layers launch the attention and its merge only; with INT2 keys
-    every layer first quantizes its newest key."""
+    Shared layers launch the attention and its merge only.  With INT2 keys
+    the newest key of every layer is quantized inside the layer's scoring
+    kernel (a shared layer's, which scores nothing, inside its attention
+    launch)."""
     import synth
     if dense:   # every layer: the dense chunks and their merge
         return {"anchor_score": 0, "refine_score": 0, "select": 0, "attention": 0, "classify": 0,
@@ -110,7 +112,7 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, int2=False, dense=False):
             "attention": wl.num_layers,
             "classify": (na if (L > 16384 and L > anchor_need) else 0)
                         + (nr if pool_classify else 0),
-            "merge": wl.num_layers, "quantize": wl.num_layers if int2 else 0, "dense": 0}
+            "merge": wl.num_layers, "quantize": 0, "dense": 0}
 
 
 def kernel_source_hash():
@@ -218,7 +220,8 @@ def main():
                          "anchor_stride-th layer F, the others R")
     ap.add_argument("--int2", action="store_true",
                     help="score from INT2 proposal keys (Section 4.2): every layer's keys are "
-                         "quantized before timing, and each timed layer quantizes its newest key")
+                         "quantized before timing, and each timed layer quantizes its newest key "
+                         "(inside its scoring kernel; a shared layer inside its attention launch)")
     ap.add_argument("--dense", action="store_true",
                     help="dense decode attention over every cached token at every layer (the "
                          "full-attention baseline of the sparse path); --cpu-seconds is ignored")
@@ -295,7 +298,9 @@ def main():
                 codes = torch.zeros(cs, dtype=torch.uint8, device=dev)
                 scales = torch.zeros(ss, dtype=torch.int16, device=dev)
                 tsa.prism_quantize_keys(kv_dev[l], 0, codes, scales)
-                kv_dev[l] = kv_dev[l].with_int2(codes, scales)
+                # every step appends one key per layer: the layer's own call
+                # quantizes it before scoring (new_keys = 1)
+                kv_dev[l] = kv_dev[l].with_int2(codes, scales, new_keys=1)
             if l in keep_host:
                 host_keep[l] = li
             del li
@@ -318,8 +323,6 @@ def main():
     anchor_ptr = anchor.data_ptr()
 
     role_ids = [tsa.ROLES[c] for c in roles]
-    int2_args = [(kv.tensors[4].data_ptr(), kv.tensors[5].data_ptr()) if args.int2 else None
-                 for kv, _, _ in layer_args]
 
     def step():
         s = torch.cuda.current_stream().cuda_stream  # the capture stream while recording
@@ -328,8 +331,6 @@ def main():
                 tsa.prism_dense_attn(kv, qp, p, op, ws_arg, s)
             return
         for l, (kv, qp, op) in enumerate(layer_args):
-            if args.int2:   # the newest token's key, as a decode step appends one per layer
-                tsa.prism_quantize_keys(kv, 1, int2_args[l][0], int2_args[l][1], s)
             if args.pattern:
                 tsa.prism_decode_layer_role(role_ids[l], kv, qp, p, anchor_ptr, op, ws_arg, s)
             else:
@@ -374,7 +375,7 @@ def main():
     # ---- timed region 2: eager launches, every kernel's start and end recorded
     #      by its dispatch (per-kernel durations and the roofline) -------------------
     per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
-                                 args.pool_rho, roles, args.int2, args.dense)
+                                 args.pool_rho, roles, args.dense)
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
@@ -423,7 +424,7 @@ def main():
     n_anchor = per_step["anchor_score"]
     quant_bytes = wl.batch * wl.num_kv_heads * (D2 + 48) if args.int2 else 0
     step_bytes = (n_anchor * anchor_bytes + sum(pool_bytes) + wl.num_layers * attn_bytes
-                  + per_step["quantize"] * quant_bytes)
+                  + wl.num_layers * quant_bytes)
     dense_bytes = int(pg.seq_lens.astype(np.int64).sum()) * wl.num_kv_heads * 2 * D2
     if args.dense:
         step_bytes = wl.num_layers * dense_bytes

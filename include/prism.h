@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 5
+#define PRISM_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -88,6 +88,18 @@ typedef enum {
  *   When set, relevance (Eq. 9) at anchor and refined layers is computed from
  *   them instead of k_pages (attention always reads k_pages and v_pages);
  *   prism_quantize_keys writes them.
+ *   new_keys     0 <= new_keys <= 64, used only with k_codes: the key rows of
+ *                positions [max(0, seq_lens[b] - new_keys), seq_lens[b]) of
+ *                every sequence and KV head were just appended (a decode step
+ *                appends one) and have no codes yet.  prism_score_topk,
+ *                prism_refine_topk, prism_decode_layer and
+ *                prism_decode_layer_role then write their codes and scales,
+ *                exactly as prism_quantize_keys(kv, new_keys, ...) would,
+ *                before they score them: inside the scoring kernel, or, for a
+ *                shared layer (which scores nothing), in extra workgroups of
+ *                its attention launch.  A refined layer writes them whether
+ *                or not they are in its pool.  prism_sparse_attn and
+ *                prism_dense_attn never read the codes and ignore it.
  * Host integers: min_seq_len <= seq_lens[b] <= max_seq_len must hold for all b
  * and max_seq_len <= max_pages_per_seq * page_size.  The library cannot check
  * the device arrays; kernels clamp every length and position so that
@@ -106,8 +118,9 @@ typedef struct {
   int32_t max_pages_per_seq;
   int32_t max_seq_len;
   int32_t min_seq_len;
-  const uint8_t* k_codes;     /* optional INT2 codes, see above (NULL: bf16 keys) */
-  const uint16_t* k_scales;   /* optional INT2 (alpha, beta) per group           */
+  uint8_t* k_codes;           /* optional INT2 codes, see above (NULL: bf16 keys) */
+  uint16_t* k_scales;         /* optional INT2 (alpha, beta) per group           */
+  int32_t new_keys;           /* trailing positions still without codes          */
 } prism_kv_cache;
 
 /*
@@ -233,9 +246,11 @@ PRISM_API prism_status prism_dense_attn(const prism_kv_cache* kv, const uint16_t
  * the minimum, alpha = (max - min) / 3 rounded to the nearest bf16, code = the
  * integer nearest (ties to even) to (k - beta) / alpha, clipped to [0, 3], and
  * 0 when alpha = 0; the subtraction and division are IEEE float32; -0 reads
- * as +0.  Keys must be finite.  A decode step calls it with num_new = 1 for
- * every layer after the model appended the new token's key; kv->k_codes and
- * kv->k_scales are not read.  Rows of other positions are left untouched.
+ * as +0.  Keys must be finite.  It quantizes a prefill's keys (num_new <= 0);
+ * a decode step's new keys can instead be left to the layer's own call
+ * (prism_kv_cache.new_keys), which saves this launch.  kv->k_codes,
+ * kv->k_scales and kv->new_keys are not read.  Rows of other positions are
+ * left untouched.
  */
 PRISM_API prism_status prism_quantize_keys(const prism_kv_cache* kv, int32_t num_new,
                                            uint8_t* k_codes, uint16_t* k_scales, void* stream);

@@ -14,7 +14,7 @@ FAKE = 0x10000  # aligned, never dereferenced: every case below fails validation
 def _kv(**over):
     d = dict(k_pages=FAKE, v_pages=FAKE, block_table=FAKE, seq_lens=FAKE, batch=2,
              num_kv_heads=8, head_dim=128, page_size=64, num_pages=1024, max_pages_per_seq=512,
-             max_seq_len=32768, min_seq_len=4096, k_codes=None, k_scales=None)
+             max_seq_len=32768, min_seq_len=4096, k_codes=None, k_scales=None, new_keys=0)
     d.update(over)
     return L.KVCacheStruct(*[d[n] for n, _ in L.KVCacheStruct._fields_])
 
@@ -61,7 +61,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 5
+    assert tsa.prism_abi_version() == 6
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -103,6 +103,9 @@ CASES = [
     ("negative pool_rho", dict(p=_params(pool_rho=-1)), L.PRISM_ERR_INVALID_ARG),
     ("rank pool above 32768", dict(p=_params(pool_rho=17)), L.PRISM_ERR_UNSUPPORTED),
     ("misaligned k", dict(kv=_kv(k_pages=FAKE + 2)), L.PRISM_ERR_INVALID_ARG),
+    ("negative new_keys", dict(kv=_kv(new_keys=-1)), L.PRISM_ERR_INVALID_ARG),
+    ("new_keys above 64", dict(kv=_kv(k_codes=FAKE, k_scales=FAKE, new_keys=65)),
+     L.PRISM_ERR_UNSUPPORTED),
     ("null workspace", dict(ws=None), L.PRISM_ERR_WORKSPACE),
     ("misaligned workspace", dict(ws=FAKE + 16), L.PRISM_ERR_WORKSPACE),
     ("small workspace", dict(nbytes=1024), L.PRISM_ERR_WORKSPACE),
@@ -231,3 +234,10 @@ def test_int2_cache_fields_checked_on_host():
         pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
     assert lib.prism_quantize_keys(ctypes.byref(kv), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP
     assert _call("score", _kv(k_codes=FAKE, k_scales=FAKE), _params()) == L.PRISM_ERR_HIP
+    # new_keys: up to 64 accepted (ignored without codes); prism_quantize_keys does not read it
+    for fn in ("score", "refine", "attn", "layer", "role", "dense"):
+        assert _call(fn, _kv(k_codes=FAKE, k_scales=FAKE, new_keys=64), _params()) == \
+            L.PRISM_ERR_HIP, fn
+        assert _call(fn, _kv(new_keys=7), _params()) == L.PRISM_ERR_HIP, fn
+    odd = _kv(new_keys=1000)
+    assert lib.prism_quantize_keys(ctypes.byref(odd), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP

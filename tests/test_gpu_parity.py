@@ -611,6 +611,87 @@ def test_int2_full_size_planted_128k():
     _run_chain(st, [0, 1, 7], [(0, g) for g in range(wl.num_kv_heads)], f"int2 {wl.name}")
 
 
+def _new_key_slots(st, nk):
+    """(page, slot) of the last nk positions of every sequence."""
+    pages, slots = [], []
+    for b, L in enumerate(st.pg.seq_lens.tolist()):
+        for pos in range(max(0, L - nk), L):
+            pages.append(int(st.pg.block_table[b, pos // st.wl.page_size]))
+            slots.append(pos % st.wl.page_size)
+    return torch.tensor(pages, device="cuda"), torch.tensor(slots, device="cuda")
+
+
+@pytest.mark.parametrize("mode", ["window", "rank", "roles", "standalone"])
+@pytest.mark.parametrize("nk", [1, 5, 64])
+def test_int2_new_keys_quantized_inside_the_call(mode, nk):
+    """prism_kv_cache.new_keys: the codes and scales of every sequence's last
+    nk positions hold garbage (0xFF codes, alpha and beta near 1.7e38), and
+    the calls given new_keys = nk must write them exactly as
+    prism_quantize_keys did before scoring them: every layer's sets, pool
+    scores and outputs bit-identical to a step on correct codes, and afterwards
+    every layer's codes and scales bit-identical to the standalone
+    quantization.  Lengths 2050 (the new keys straddle the anchor kernel's
+    2048-token workgroups), 5000 and 4097; rho = 16 makes the first sequence's
+    pool its whole cache, so its new keys are the pool's last entries and
+    straddle a pool workgroup's 256 entries; the window pool may or may not
+    hold them (the last pool workgroup writes those outside it); FRS puts a
+    shared layer, which scores nothing, last."""
+    nl = 3
+    wl = synth.scaled(synth.TINY_4K, name=f"new-keys-{mode}", wid=460, num_q_heads=8,
+                      num_kv_heads=2, batch=3, context=None, lengths=(2050, 5000, 4097),
+                      kappa=300, window=16, num_layers=nl, anchor_stride=nl)
+    st = Setup(wl, range(nl), pool_rho=16 if mode == "rank" else 0, int2=True)
+    want_codes = [st.kv[l].tensors[4].clone() for l in range(nl)]
+    want_scales = [st.kv[l].tensors[5].clone() for l in range(nl)]
+
+    lens = st.pg.seq_lens.astype(np.int64)
+
+    def step(kvs):
+        anchor = st.idx_buf()
+        res = []
+        for l in range(nl):
+            sel, out = st.idx_buf(), st.out_buf()
+            sc = torch.full((wl.batch, wl.num_kv_heads, int(lens.max())), float("nan"),
+                            device="cuda")
+            valid = np.repeat(lens[:, None], wl.num_kv_heads, 1)  # scores rows' valid prefix
+            if mode == "roles":
+                tsa.prism_decode_layer_role("FRS"[l], kvs[l], st.q[l], st.params, anchor, out,
+                                            st.ws)
+                sel.copy_(anchor)
+            elif mode == "standalone":
+                if l == 0:
+                    tsa.prism_score_topk(kvs[l], st.q[l], st.params, anchor, sc, st.ws)
+                    sel.copy_(anchor)
+                else:
+                    plen = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32,
+                                       device="cuda")
+                    tsa.prism_refine_topk(kvs[l], st.q[l], st.params, anchor, sel,
+                                          pool_len_out=plen, pool_scores_out=sc, workspace=st.ws)
+                    valid = plen.cpu().numpy()
+            else:
+                tsa.prism_decode_layer(l, kvs[l], st.q[l], st.params, anchor, sel, out, st.ws)
+            torch.cuda.synchronize()
+            scores = sc.cpu().numpy().view(np.uint32)
+            scores = np.concatenate([scores[b, g, :valid[b, g]] for b in range(wl.batch)
+                                     for g in range(wl.num_kv_heads)])
+            res.append((sel.cpu().numpy(), out.cpu().numpy().view(np.uint32), scores))
+        return res
+
+    want = step([st.kv[l] for l in range(nl)])
+    pages, slots = _new_key_slots(st, nk)
+    for l in range(nl):
+        st.kv[l].tensors[4][pages, :, slots] = 0xFF
+        st.kv[l].tensors[5][pages, :, slots] = 0x7F00
+        assert not torch.equal(st.kv[l].tensors[4], want_codes[l])
+    say(f"[new-keys {mode} nk={nk}] fused step")
+    got = step([st.kv[l].with_new_keys(nk) for l in range(nl)])
+    for l in range(nl):
+        for name, g_a, w_a in zip(("set", "output", "scores"), got[l], want[l]):
+            assert np.array_equal(g_a, w_a), f"layer {l}: {name} differs"
+        assert torch.equal(st.kv[l].tensors[4], want_codes[l]), f"layer {l}: codes"
+        assert torch.equal(st.kv[l].tensors[5], want_scales[l]), f"layer {l}: scales"
+
+
 # --------------------------------------------------------------------------- dense decode
 def _dense_check(st, l, problems, label):
     out = st.out_buf()

@@ -30,7 +30,8 @@ class KVCacheStruct(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("num_pages", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("min_seq_len", ctypes.c_int32),
-                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p)]
+                ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("new_keys", ctypes.c_int32)]
 
 
 class ParamsStruct(ctypes.Structure):
@@ -142,9 +143,11 @@ class KVCache:
     """One layer's paged cache: keeps the tensors alive and the C struct."""
 
     def __init__(self, k_pages, v_pages, block_table, seq_lens, *, max_seq_len, min_seq_len,
-                 head_dim=None, page_size=None, k_codes=None, k_scales=None):
+                 head_dim=None, page_size=None, k_codes=None, k_scales=None, new_keys=0):
         """k_codes / k_scales (optional, together): the INT2 proposal keys,
-        uint8 [num_pages, Hkv, page, 32] and bf16 bits [num_pages, Hkv, page, 4, 2]."""
+        uint8 [num_pages, Hkv, page, 32] and bf16 bits [num_pages, Hkv, page, 4, 2].
+        new_keys: trailing positions of every sequence whose codes the scoring
+        calls write before scoring them (a decode step's appended keys)."""
         self.tensors = (k_pages, v_pages, block_table, seq_lens, k_codes, k_scales)
         num_pages, hkv, ps, d = k_pages.shape
         if tuple(v_pages.shape) != tuple(k_pages.shape):
@@ -156,19 +159,25 @@ class KVCache:
             batch, hkv, head_dim if head_dim is not None else d,
             page_size if page_size is not None else ps, num_pages, max_pages, int(max_seq_len),
             int(min_seq_len), _ptr(k_codes, "k_codes", itemsize=1, optional=True),
-            _ptr(k_scales, "k_scales", itemsize=2, optional=True))
+            _ptr(k_scales, "k_scales", itemsize=2, optional=True), int(new_keys))
 
-    def with_layer(self, k_pages, v_pages, k_codes=None, k_scales=None) -> "KVCache":
+    def with_layer(self, k_pages, v_pages, k_codes=None, k_scales=None,
+                   new_keys=0) -> "KVCache":
         """Same sequences and block table, another layer's K/V (and INT2) arrays."""
         bt, sl = self.tensors[2], self.tensors[3]
         s = self.struct
         return KVCache(k_pages, v_pages, bt, sl, max_seq_len=s.max_seq_len,
                        min_seq_len=s.min_seq_len, head_dim=s.head_dim, page_size=s.page_size,
-                       k_codes=k_codes, k_scales=k_scales)
+                       k_codes=k_codes, k_scales=k_scales, new_keys=new_keys)
 
-    def with_int2(self, k_codes, k_scales) -> "KVCache":
+    def with_int2(self, k_codes, k_scales, new_keys=0) -> "KVCache":
         """The same cache with INT2 proposal keys (or without, given None)."""
-        return self.with_layer(self.tensors[0], self.tensors[1], k_codes, k_scales)
+        return self.with_layer(self.tensors[0], self.tensors[1], k_codes, k_scales, new_keys)
+
+    def with_new_keys(self, new_keys) -> "KVCache":
+        """The same cache whose last new_keys positions still lack INT2 codes."""
+        t = self.tensors
+        return self.with_layer(t[0], t[1], t[4], t[5], new_keys)
 
 
 def params(num_q_heads, kappa, anchor_stride=1, window=0, softmax_scale=0.0,

@@ -66,6 +66,7 @@ void fill_cache(const prism_kv_cache* kv, Geometry* g) {
   g->seq_lens = kv->seq_lens;
   g->k_codes = kv->k_codes;
   g->k_scales = kv->k_scales;
+  g->new_keys = kv->k_codes ? kv->new_keys : 0;
   g->batch = kv->batch;
   g->hkv = kv->num_kv_heads;
   g->num_pages = kv->num_pages;
@@ -79,6 +80,9 @@ void fill_cache(const prism_kv_cache* kv, Geometry* g) {
 prism_status resolve(const prism_kv_cache* kv, const prism_params* p, Geometry* g) {
   if (!kv || !p) return fail(PRISM_ERR_INVALID_ARG, "kv cache and params must not be NULL");
   PRISM_TRY(resolve_cache(kv));
+  if (kv->new_keys < 0) return fail(PRISM_ERR_INVALID_ARG, "new_keys must be >= 0");
+  if (kv->new_keys > prism::kMaxNewKeys)
+    return fail(PRISM_ERR_UNSUPPORTED, "new_keys above 64 (quantize with prism_quantize_keys)");
   if (p->num_q_heads < 1) return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be >= 1");
   if (p->num_q_heads % kv->num_kv_heads != 0)
     return fail(PRISM_ERR_INVALID_ARG, "num_q_heads must be a multiple of num_kv_heads");
@@ -336,8 +340,8 @@ prism_status prism_decode_layer_role(int32_t role, const prism_kv_cache* kv, con
     case PRISM_ROLE_REFINED:
       return hip_check(prism::launch_refine_attend(g, w, q, scale, set_idx, out, s),
                        "refined layer launch");
-    default:
-      return hip_check(prism::launch_attention(g, w, q, set_idx, false, scale, out, s),
+    default:  // nothing here scores the new keys: the attention launch writes their codes
+      return hip_check(prism::launch_attention(g, w, q, set_idx, false, scale, out, s, true),
                        "shared layer attention launch");
   }
 }

@@ -13,7 +13,8 @@ constexpr int kPageSize = 64;         // tokens per page
 constexpr int kSelThreads = 1024;     // threads of a selection workgroup
 constexpr int kScoreThreads = 256;    // threads of a relevance workgroup
 constexpr int kAnchorEntries = 1024;  // cached tokens scored by one anchor-layer workgroup
-constexpr int kMaxRankPool = 32768;  // largest rank-expanded pool (rho * kappa)
+constexpr int kMaxRankPool = 32768;   // largest rank-expanded pool (rho * kappa)
+constexpr int kMaxNewKeys = 64;       // most new keys a call quantizes in its scoring kernel
 constexpr int kPoolEntries = 256;     // pool entries scored by one refined-layer workgroup
 constexpr int kAttnSplit = 64;        // selected tokens attended by one workgroup
 constexpr int kAttnThreads = 256;
@@ -29,8 +30,9 @@ struct Geometry {
   const uint16_t* v_pages;
   const int32_t* block_table;
   const int32_t* seq_lens;
-  const uint8_t* k_codes;    // INT2 proposal keys (null: relevance from k_pages)
-  const uint16_t* k_scales;  // their per-group (alpha, beta), bf16
+  uint8_t* k_codes;    // INT2 proposal keys (null: relevance from k_pages)
+  uint16_t* k_scales;  // their per-group (alpha, beta), bf16
+  int new_keys;        // trailing positions whose codes the scoring kernels write first
   int batch;
   int hkv;          // KV heads
   int hq;           // query heads
@@ -138,8 +140,10 @@ hipError_t launch_dense(const Geometry& g, const Workspace& w, const uint16_t* q
                         float* out, hipStream_t s);
 // SparseAttn into out [B][Hq][D] over the set `idx` (positions), or, with
 // use_sel_rows, over the row ids the latest selection left in the workspace.
+// quantize_new: the same launch also writes the codes of g.new_keys new keys
+// (for a layer that scores nothing).
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
                             const int32_t* idx, bool use_sel_rows, float scale, float* out,
-                            hipStream_t s);
+                            hipStream_t s, bool quantize_new = false);
 
 }  // namespace prism

@@ -558,25 +558,19 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // nearest, tie
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Eq. 8 on the keys of positions [max(0, L - num_new), L) of every (sequence,
-// KV head) (num_new <= 0: every position), one wave per token row and four
-// rows per workgroup.  Lane l holds dimensions 2l and 2l + 1, so a group of 32
-// dimensions is one 16-lane row of the wave.  Per group: beta = min, alpha =
-// (max - min) / 3 rounded to bf16, code = the nearest integer (ties to even)
-// to (k - beta) / alpha clipped to [0, 3], 0 when alpha = 0; the subtraction
-// and division are IEEE float32 (the oracle takes the same decisions in the
-// same precision).  -0 is read as +0.
-__global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
-                                                       uint8_t* __restrict__ codes,
-                                                       uint16_t* __restrict__ scales) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int p = blockIdx.x / chunks, c = blockIdx.x - p * chunks;
-  const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int n = seq_len_of(g, b);
-  const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
-  const int pos = first + c * 4 + wv;
-  if (pos >= n) return;  // uniform over the wave
-  const size_t row = (size_t)row_id(g, b, kvh, pos);
+// Eq. 8 on one key row, by one whole wave (every lane active).  Lane l holds
+// dimensions 2l and 2l + 1, so a group of 32 dimensions is one 16-lane row of
+// the wave.  Per group: beta = min, alpha = (max - min) / 3 rounded to bf16,
+// code = the nearest integer (ties to even) to (k - beta) / alpha clipped to
+// [0, 3], 0 when alpha = 0; the subtraction and division are IEEE float32 (the
+// oracle takes the same decisions in the same precision).  -0 is read as +0.
+// quantize_kernel applies it to the keys of positions [max(0, L - num_new), L)
+// of every (sequence, KV head) (num_new <= 0: every position), four rows per
+// workgroup; the scoring kernels apply it to a decode step's new keys before
+// they score them (Geometry::new_keys).
+__device__ __forceinline__ void quantize_row(const Geometry& g, size_t row, int lane,
+                                             uint8_t* __restrict__ codes,
+                                             uint16_t* __restrict__ scales) {
   const uint32_t x = reinterpret_cast<const uint32_t*>(g.k_pages + row * kHeadDim)[lane];
   const float v0 = __uint_as_float(x << 16) + 0.0f;
   const float v1 = __uint_as_float(x & 0xFFFF0000u) + 0.0f;
@@ -609,6 +603,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, 
         wd;
   if ((lane & 15) == 0)  // alpha in the low half, beta in the high half
     reinterpret_cast<uint32_t*>(scales)[row * 4 + s4] = ab | (__float_as_uint(mn) & 0xFFFF0000u);
+}
+
+// Positions [lo, hi) of sequence b, KV head kvh, one wave per position.  Every
+// wave of the workgroup calls it (the loop bound is uniform over a wave).
+__device__ __forceinline__ void quantize_positions(const Geometry& g, int b, int kvh, int lo,
+                                                   int hi, int lane, int wave, int waves) {
+  for (int pos = lo + wave; pos < hi; pos += waves)
+    quantize_row(g, (size_t)row_id(g, b, kvh, pos), lane, g.k_codes, g.k_scales);
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int p = blockIdx.x / chunks, c = blockIdx.x - p * chunks;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int n = seq_len_of(g, b);
+  const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
+  const int pos = first + c * 4 + wv;
+  if (pos >= n) return;  // uniform over the wave
+  quantize_row(g, (size_t)row_id(g, b, kvh, pos), lane, codes, scales);
 }
 
 // The group's query heads as MFMA A operands against INT2 keys.  A tile is 16
@@ -720,7 +735,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
   constexpr int kRoundTokens = kInt2RoundPages * kPageSize;
   const int wbase = w * kInt2Entries + wave * (kInt2Entries / 4);
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
-  lds_barrier();
+  // the step's new keys inside this workgroup's range get their codes first
+  const int qlo = max(max(n - g.new_keys, 0), w * kInt2Entries);
+  const int qhi = min(n, (w + 1) * kInt2Entries);
+  if (g.new_keys > 0 && qlo < qhi) {  // uniform over the workgroup
+    quantize_positions(g, b, kvh, qlo, qhi, lane, wave, kScoreThreads / 64);
+    __syncthreads();  // the rows' stores before any wave loads them
+  } else {
+    lds_barrier();
+  }
   if (wbase < n) {
     float* sc = ws.scores + (size_t)p * g.n_cap;
     const int last_page = (n - 1) >> 6;
@@ -784,14 +807,36 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_int2_kernel(
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
   const int base = w * chunks * kPoolEntries;
-  if (base >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  if (g.new_keys > 0) {  // uniform over the workgroup
+    // The step's new keys that can be among this workgroup's entries (pool
+    // positions ascend) get their codes before it loads any; the workgroup
+    // holding the pool's last entry (workgroup 0 if the pool is empty) takes
+    // every new key, so those outside the pool are written as well.
+    const int L = seq_len_of(g, b);
+    int lo = max(L - g.new_keys, 0), hi = L;
+    if (base < n) {
+      const int last = min(base + chunks * kPoolEntries, n) - 1;
+      if (last < n - 1) {
+        const int32_t* ppos = ws.pool_pos + (size_t)p * g.n_cap;
+        lo = max(lo, ppos[base]);
+        hi = min(hi, clampi(ppos[last], -1, L - 1) + 1);
+      }
+    } else if (w != 0 || n != 0) {
+      hi = lo;
+    }
+    if (lo < hi) {
+      quantize_positions(g, b, kvh, lo, hi, lane, wave, kScoreThreads / 64);
+      __syncthreads();  // the rows' stores before any wave loads them
+    }
+  }
+  if (base >= n) return;  // uniform over the workgroup
   const bool counted = hist != 0 && n > kSmall;  // uniform over the workgroup
   if (counted) {
     for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
     lds_barrier();
   }
-  const int b = p / g.hkv, kvh = p - b * g.hkv;
   const uint32_t* prow = ws.pool_row + (size_t)p * g.n_cap;
   float* sc = ws.scores + (size_t)p * g.n_cap;
   const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
@@ -2039,10 +2084,19 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
   __shared__ float wml[NW][G][2];
   __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
   const int splits = g.splits;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  if (blockIdx.x >= (unsigned)(g.problems() * splits)) {  // uniform over the workgroup
+    // one workgroup per problem past the attention's grid (a shared layer's
+    // launch): the step's new keys get their codes, as no kernel of the layer
+    // scores them
+    const int pq = blockIdx.x - g.problems() * splits;
+    const int bq = pq / g.hkv, L = seq_len_of(g, bq);
+    quantize_positions(g, bq, pq - bq * g.hkv, max(L - g.new_keys, 0), L, lane, wave, NW);
+    return;
+  }
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane & 15, g4 = lane >> 4;
 
   const int ti = s * kAttnSplit + wave * 16 + j;
@@ -2899,9 +2953,11 @@ void launch_merge_g(const Geometry& g, const Workspace& w, int splits, float* ou
 
 template <int G, bool ROWS>
 void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q,
-                        const int32_t* idx, float scale, float* out, hipStream_t s) {
-  launch(kAttention, attn_kernel<G, ROWS>, dim3(g.problems() * g.splits), dim3(kAttnThreads), s,
-         g, w, q, idx, scale);
+                        const int32_t* idx, float scale, float* out, bool quantize_new,
+                        hipStream_t s) {
+  const int extra = quantize_new && g.k_codes && g.new_keys > 0 ? g.problems() : 0;
+  launch(kAttention, attn_kernel<G, ROWS>, dim3(g.problems() * g.splits + extra),
+         dim3(kAttnThreads), s, g, w, q, idx, scale);
   launch_merge_g<G>(g, w, g.splits, out, false, s);
 }
 
@@ -3234,23 +3290,23 @@ hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint1
 
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
                             const int32_t* idx, bool use_sel_rows, float scale, float* out,
-                            hipStream_t s) {
+                            hipStream_t s, bool quantize_new) {
   if (use_sel_rows) {
     switch (g.group) {
-      case 1: launch_attention_g<1, true>(g, w, q, idx, scale, out, s); break;
-      case 2: launch_attention_g<2, true>(g, w, q, idx, scale, out, s); break;
-      case 4: launch_attention_g<4, true>(g, w, q, idx, scale, out, s); break;
-      case 8: launch_attention_g<8, true>(g, w, q, idx, scale, out, s); break;
-      case 16: launch_attention_g<16, true>(g, w, q, idx, scale, out, s); break;
+      case 1: launch_attention_g<1, true>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 2: launch_attention_g<2, true>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 4: launch_attention_g<4, true>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 8: launch_attention_g<8, true>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 16: launch_attention_g<16, true>(g, w, q, idx, scale, out, quantize_new, s); break;
       default: return hipErrorInvalidValue;
     }
   } else {
     switch (g.group) {
-      case 1: launch_attention_g<1, false>(g, w, q, idx, scale, out, s); break;
-      case 2: launch_attention_g<2, false>(g, w, q, idx, scale, out, s); break;
-      case 4: launch_attention_g<4, false>(g, w, q, idx, scale, out, s); break;
-      case 8: launch_attention_g<8, false>(g, w, q, idx, scale, out, s); break;
-      case 16: launch_attention_g<16, false>(g, w, q, idx, scale, out, s); break;
+      case 1: launch_attention_g<1, false>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 2: launch_attention_g<2, false>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 4: launch_attention_g<4, false>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 8: launch_attention_g<8, false>(g, w, q, idx, scale, out, quantize_new, s); break;
+      case 16: launch_attention_g<16, false>(g, w, q, idx, scale, out, quantize_new, s); break;
       default: return hipErrorInvalidValue;
     }
   }
