@@ -206,9 +206,10 @@ PRISM_API prism_status prism_sparse_attn(const prism_kv_cache* kv, const uint16_
  * refinement pool in the workspace.  Otherwise the layer is refined as
  * prism_refine_topk would refine it against anchor_idx, re-scoring the pool
  * the nearest preceding anchor layer left in the same workspace: the layers
- * of one decode step share anchor_idx and the workspace, and calling a refined
- * layer before any anchor layer is the caller's error.  Then SparseAttn over
- * the layer's set into out.
+ * of one decode step share anchor_idx, the workspace and the params (kappa,
+ * window and pool_rho bound the pool's size), and calling a refined layer
+ * before any anchor layer is the caller's error.  Then SparseAttn over the
+ * layer's set into out.
  *   anchor_idx     int32 [batch][num_kv_heads][kappa], state carried between
  *                  the layers of one decode step (written by anchors, read by
  *                  refined layers).
@@ -292,9 +293,9 @@ PRISM_API int32_t prism_pattern_role(const char* pattern, int32_t table4, int32_
  *   PRISM_ROLE_SHARED    reads set_idx (the nearest preceding proposal or
  *                        refined layer's set) and does not change it;
  * then SparseAttn over the layer's set into out.  params->anchor_stride is not
- * used.  The layers of one decode step share set_idx and the workspace; a
- * refined or shared layer before any proposal layer is the caller's error
- * (the results are then undefined, never out-of-bounds accesses).
+ * used.  The layers of one decode step share set_idx, the workspace and the
+ * params; a refined or shared layer before any proposal layer is the caller's
+ * error (the results are then undefined, never out-of-bounds accesses).
  *   set_idx  int32 [batch][num_kv_heads][kappa], caller-owned state.
  *   out      float [batch][num_q_heads][head_dim].
  * Returns PRISM_ERR_INVALID_ARG for an unknown role or a NULL set_idx / out.

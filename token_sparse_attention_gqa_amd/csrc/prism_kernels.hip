@@ -809,22 +809,23 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_int2_kernel(
   const int base = w * chunks * kPoolEntries;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  if (g.new_keys > 0) {  // uniform over the workgroup
-    // The step's new keys that can be among this workgroup's entries (pool
-    // positions ascend) get their codes before it loads any; the workgroup
-    // holding the pool's last entry (workgroup 0 if the pool is empty) takes
-    // every new key, so those outside the pool are written as well.
+  if (g.new_keys > 0 && (base < n || (w == 0 && n == 0))) {  // uniform over the workgroup
+    // The step's new keys that can be among this workgroup's entries get
+    // their codes before it loads any.  Pool positions ascend, so new keys
+    // can only be the pool's last new_keys entries; the workgroup holding the
+    // last entry (workgroup 0 if the pool is empty) takes every new key, so
+    // those outside the pool are written as well.
     const int L = seq_len_of(g, b);
     int lo = max(L - g.new_keys, 0), hi = L;
     if (base < n) {
       const int last = min(base + chunks * kPoolEntries, n) - 1;
-      if (last < n - 1) {
+      if (last < n - g.new_keys) {
+        hi = lo;  // every entry here precedes the new keys
+      } else if (last < n - 1) {
         const int32_t* ppos = ws.pool_pos + (size_t)p * g.n_cap;
         lo = max(lo, ppos[base]);
         hi = min(hi, clampi(ppos[last], -1, L - 1) + 1);
       }
-    } else if (w != 0 || n != 0) {
-      hi = lo;
     }
     if (lo < hi) {
       quantize_positions(g, b, kvh, lo, hi, lane, wave, kScoreThreads / 64);
@@ -2930,12 +2931,20 @@ void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t
   }
 }
 
+// Bound of a refinement pool's length: min(n_cap, kappa (2w + 1)) for the
+// window pool, min(n_cap, rho kappa) for the rank-expanded one.
+int pool_cap(const Geometry& g) {
+  return (int)std::min<long long>(g.n_cap, g.pool_rho >= 1
+                                               ? (long long)g.pool_rho * g.kappa
+                                               : (long long)g.kappa * (2LL * g.window + 1));
+}
+
 template <int G>
 void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* q, bool hist,
                          hipStream_t s) {
   const int chunks = hist ? kPoolHistChunks : 1;
   const int per_wg = chunks * kPoolEntries;
-  const int wgs = (g.n_cap + per_wg - 1) / per_wg;
+  const int wgs = (pool_cap(g) + per_wg - 1) / per_wg;
   if (g.k_codes)
     launch(kRefineScore, score_pool_int2_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads),
            s, g, w, q, wgs, chunks, hist ? 1 : 0);
@@ -3204,19 +3213,16 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
 // Refined layer without the fused kernel: score the pool (counting pools longer
 // than kSmall per coarse bin), classify those pools over many workgroups, then
 // select per problem.  The pool's length is known on the device only; its
-// bound (min(n_cap, kappa (2w + 1)) for the window pool, min(n_cap, rho kappa)
-// for the rank-expanded one) decides whether classification can be needed.
+// bound decides whether classification can be needed, and sizes the grids.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          hipStream_t s) {
-  const long long bound =
-      std::min<long long>(g.n_cap, g.pool_rho >= 1 ? (long long)g.pool_rho * g.kappa
-                                                   : (long long)g.kappa * (2LL * g.window + 1));
+  const int bound = pool_cap(g);
   const bool classify = bound > kSmall && bound > g.kappa;
   PRISM_BY_GROUP(launch_pool_score_g, g, w, q, classify, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (classify) {
-    const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
+    const int wgs = (bound + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
            1, g.kappa, 0);
     e = hipGetLastError();
