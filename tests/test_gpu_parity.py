@@ -783,18 +783,23 @@ def test_determinism():
 
 
 # ---------------------------------------------------------------------- graph replay
-@pytest.mark.parametrize("mode", ["window", "rank", "int2", "roles", "dense"])
+@pytest.mark.parametrize("mode", ["window", "rank", "int2", "int2-new-keys", "roles", "dense"])
 def test_graph_replay_matches_eager(mode):
     """The decode step captured once as a HIP graph (the launch the benchmark
     times) and replayed three times, with eager work and synchronisations
     between the replays: after an eager step, after the workspace was
     overwritten with 0xAB bytes, and after a standalone call into another
     output.  Outputs and sets are cleared before every replay, and each
-    replay's must equal the eager step's bit for bit."""
+    replay's must equal the eager step's bit for bit.  The INT2 cases quantize
+    the newest key in a launch of its own or inside the layer's calls
+    (new_keys = 1)."""
     nl, pattern = 4, "FRSR"
     wl = synth.scaled(synth.LLAMA_128K_PLANTED, name=f"graph-{mode}", wid=450, context=20480,
                       kappa=512, n_clusters=16, num_layers=nl, anchor_stride=2)
-    st = Setup(wl, range(nl), pool_rho=4 if mode == "rank" else 0, int2=(mode == "int2"))
+    st = Setup(wl, range(nl), pool_rho=4 if mode == "rank" else 0, int2=mode.startswith("int2"))
+    if mode == "int2-new-keys":   # each layer's call quantizes the newest key itself
+        for l in range(nl):
+            st.kv[l] = st.kv[l].with_new_keys(1)
     anchor = st.idx_buf()
     sels = [st.idx_buf() for _ in range(nl)]
     outs = [st.out_buf() for _ in range(nl)]
