@@ -61,7 +61,11 @@ def test_library_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert tsa.prism_abi_version() == 6
+    """The library, the header and the binding's structs agree on the ABI version."""
+    import re
+    with open(L.HEADER) as f:
+        header = int(re.search(r"#define PRISM_ABI_VERSION (\d+)", f.read()).group(1))
+    assert tsa.prism_abi_version() == header == L.ABI_VERSION == 6
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"

@@ -23,6 +23,9 @@ class PrismError(RuntimeError):
         self.status = status
 
 
+ABI_VERSION = 6   # PRISM_ABI_VERSION of include/prism.h that the structs below follow
+
+
 class KVCacheStruct(ctypes.Structure):
     _fields_ = [("k_pages", ctypes.c_void_p), ("v_pages", ctypes.c_void_p),
                 ("block_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
@@ -93,6 +96,10 @@ def lib() -> ctypes.CDLL:
         for name, (res, args) in _SIGS.items():
             fn = getattr(handle, name)
             fn.restype, fn.argtypes = res, args
+        version = int(handle.prism_abi_version())
+        if version != ABI_VERSION:   # the structs above follow one layout only
+            raise RuntimeError(f"{LIB_PATH} has ABI version {version}, this binding expects "
+                               f"{ABI_VERSION}: rebuild the HIP library")
         _lib = handle
     return _lib
 
