@@ -630,10 +630,10 @@ def test_int2_new_keys_quantized_inside_the_call(mode, nk):
     prism_quantize_keys did before scoring them: every layer's sets, pool
     scores and outputs bit-identical to a step on correct codes, and afterwards
     every layer's codes and scales bit-identical to the standalone
-    quantization.  Lengths 2050 (the new keys straddle the anchor kernel's
-    2048-token workgroups), 5000 and 4097; rho = 16 makes the first sequence's
-    pool its whole cache, so its new keys are the pool's last entries and
-    straddle a pool workgroup's 256 entries; the window pool may or may not
+    quantization.  Lengths 2050 (the new keys straddle two of the anchor
+    kernel's 1024-token workgroups), 5000 and 4097; rho = 16 makes the first
+    sequence's pool its whole cache, so its new keys are the pool's last
+    entries and straddle a pool workgroup's 256 entries; the window pool may or may not
     hold them (the last pool workgroup writes those outside it); FRS puts a
     shared layer, which scores nothing, last."""
     nl = 3

@@ -712,13 +712,14 @@ struct Int2Query {
 
 // Anchor-layer relevance from INT2 keys: the score list and the coarse
 // histogram are those of score_anchor_kernel.  A workgroup scores
-// kInt2Entries tokens (a key row is 48 bytes here, so a workgroup takes four
-// times the tokens of the bf16 kernel to amortise its histogram and query
-// set-up); each wave takes a quarter of them in rounds of two pages, loading
-// the next round's codes and scales while it scores the current one (per
-// 16-token tile a lane reads its quarter's 8 bytes of codes and the token's 16
-// bytes of scales), four MFMAs per tile and 16-row tile of (head, group) rows.
-constexpr int kInt2Entries = 2048;
+// kInt2Entries tokens; each wave takes a quarter of them in rounds of two
+// pages (per 16-token tile a lane reads its quarter's 8 bytes of codes and the
+// token's 16 bytes of scales), four MFMAs per tile and 16-row tile of (head,
+// group) rows.  A round's loads are not prefetched during the previous round:
+// at 104 registers four waves share a SIMD, and the waves' interleaving hides
+// the loads better than a second buffer at two waves per SIMD did (21 against
+// 23.6 us at 128K).
+constexpr int kInt2Entries = 1024;
 constexpr int kInt2RoundPages = 2;
 constexpr int kInt2Rounds = kInt2Entries / 4 / kPageSize / kInt2RoundPages;
 
@@ -753,8 +754,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
     qq.load(q, g, b, kvh, lane);
     const u32x2* cbase = reinterpret_cast<const u32x2*>(g.k_codes);
     const u32x4* sbase = reinterpret_cast<const u32x4*>(g.k_scales);
-    u32x2 cb[2][kInt2RoundPages][4];
-    u32x4 sb[2][kInt2RoundPages][4];
     auto fetch = [&](int r, u32x2 (&cr)[kInt2RoundPages][4], u32x4 (&sr)[kInt2RoundPages][4]) {
 #pragma unroll
       for (int pg = 0; pg < kInt2RoundPages; ++pg) {
@@ -768,17 +767,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_anchor_int2_kernel(
         }
       }
     };
-    fetch(0, cb[0], sb[0]);
 #pragma unroll
     for (int r = 0; r < kInt2Rounds; ++r) {
       if (r >= rounds) break;  // uniform over the wave
-      if (r + 1 < rounds) fetch(r + 1, cb[(r + 1) & 1], sb[(r + 1) & 1]);
+      u32x2 cb[kInt2RoundPages][4];
+      u32x4 sb[kInt2RoundPages][4];
+      fetch(r, cb, sb);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int pg = 0; pg < kInt2RoundPages; ++pg) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float m = qq.score(cb[r & 1][pg][u], sb[r & 1][pg][u], g4);
+          const float m = qq.score(cb[pg][u], sb[pg][u], g4);
           const int e = wbase + r * kRoundTokens + pg * 64 + u * 16 + j;
           if (g4 == 0 && e < n) {
             sc[e] = m;
