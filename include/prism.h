@@ -88,7 +88,8 @@ typedef enum {
  *   When set, relevance (Eq. 9) at anchor and refined layers is computed from
  *   them instead of k_pages (attention always reads k_pages and v_pages);
  *   prism_quantize_keys writes them.
- *   new_keys     0 <= new_keys <= 64, used only with k_codes: the key rows of
+ *   new_keys     0 <= new_keys <= 64 (every call but prism_quantize_keys
+ *                rejects other values), used only with k_codes: the key rows of
  *                positions [max(0, seq_lens[b] - new_keys), seq_lens[b]) of
  *                every sequence and KV head were just appended (a decode step
  *                appends one) and have no codes yet.  prism_score_topk,
@@ -99,7 +100,7 @@ typedef enum {
  *                shared layer (which scores nothing), in extra workgroups of
  *                its attention launch.  A refined layer writes them whether
  *                or not they are in its pool.  prism_sparse_attn and
- *                prism_dense_attn never read the codes and ignore it.
+ *                prism_dense_attn never read the codes and write none.
  * Host integers: min_seq_len <= seq_lens[b] <= max_seq_len must hold for all b
  * and max_seq_len <= max_pages_per_seq * page_size.  The library cannot check
  * the device arrays; kernels clamp every length and position so that
