@@ -621,9 +621,10 @@ def _new_key_slots(st, nk):
     return torch.tensor(pages, device="cuda"), torch.tensor(slots, device="cuda")
 
 
-@pytest.mark.parametrize("mode", ["window", "rank", "roles", "standalone"])
+@pytest.mark.parametrize("mode,G", [("window", 4), ("rank", 4), ("roles", 4), ("standalone", 4),
+                                    ("window", 1), ("window", 16), ("rank", 16)])
 @pytest.mark.parametrize("nk", [1, 5, 64])
-def test_int2_new_keys_quantized_inside_the_call(mode, nk):
+def test_int2_new_keys_quantized_inside_the_call(mode, G, nk):
     """prism_kv_cache.new_keys: the codes and scales of every sequence's last
     nk positions hold garbage (0xFF codes, alpha and beta near 1.7e38), and
     the calls given new_keys = nk must write them exactly as
@@ -635,9 +636,10 @@ def test_int2_new_keys_quantized_inside_the_call(mode, nk):
     sequence's pool its whole cache, so its new keys are the pool's last
     entries and straddle a pool workgroup's 256 entries; the window pool may or may not
     hold them (the last pool workgroup writes those outside it); FRS puts a
-    shared layer, which scores nothing, last."""
+    shared layer, which scores nothing, last.  G = 16 takes the per-problem
+    selection and rank-pool kernels instead of the fused ones."""
     nl = 3
-    wl = synth.scaled(synth.TINY_4K, name=f"new-keys-{mode}", wid=460, num_q_heads=8,
+    wl = synth.scaled(synth.TINY_4K, name=f"new-keys-{mode}", wid=460, num_q_heads=2 * G,
                       num_kv_heads=2, batch=3, context=None, lengths=(2050, 5000, 4097),
                       kappa=300, window=16, num_layers=nl, anchor_stride=nl)
     st = Setup(wl, range(nl), pool_rho=16 if mode == "rank" else 0, int2=True)
@@ -683,7 +685,7 @@ def test_int2_new_keys_quantized_inside_the_call(mode, nk):
         st.kv[l].tensors[4][pages, :, slots] = 0xFF
         st.kv[l].tensors[5][pages, :, slots] = 0x7F00
         assert not torch.equal(st.kv[l].tensors[4], want_codes[l])
-    say(f"[new-keys {mode} nk={nk}] fused step")
+    say(f"[new-keys {mode} G={G} nk={nk}] fused step")
     got = step([st.kv[l].with_new_keys(nk) for l in range(nl)])
     for l in range(nl):
         for name, g_a, w_a in zip(("set", "output", "scores"), got[l], want[l]):
