@@ -9,11 +9,18 @@ top-kappa, SparseAttn).  Inputs are seeded synthetic tensors of the workload's
 shapes, resident in HBM before timing starts.
 
 Two timed regions of K steps each, after W warm-up steps:
-  1. the step captured once as a HIP graph and replayed K times: `value` and
-     `ms_per_step` (with --eager, or if capture fails, region 2 is reported);
-  2. the same steps launched eagerly from the host, each kernel's start and end
-     recorded by its own dispatch (prism_profile_events): the per-kernel
+  1. the step captured once as a HIP graph and replayed K times between two
+     events (`ms_per_step`, `value`), each replay also bracketed by events of
+     its own (`step_ms_median`); with --eager, or if capture fails, region 2
+     is reported instead;
+  2. the same K steps launched eagerly from the host, each kernel's start and
+     end recorded by its own dispatch (prism_profile_events; the AQL packet's
+     timestamps, the ones rocprofv3's kernel trace reports): the per-kernel
      durations, the roofline of the dominant kernel and `eager_ms_per_step`.
+     Event-record nodes inside a captured graph were tried for per-kernel
+     times in graph replay: each pair added 2.5-3 us to the kernel it
+     brackets, against the kernel trace of the replays, while the dispatch
+     timestamps of eager launches agree with it.
 Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -136,73 +143,126 @@ def traffic_for(kernel, workload):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, host, seconds, pool_rho=0, roles=None, int2=False):
-    """The CPU oracle, as it stands, on a bounded sample of the workload: one
-    anchor layer and one refined layer (and the attention alone, for shared
-    layers) for as many (sequence, KV head) problems as fit in about
-    `seconds`, extrapolated to a whole decode step."""
+def sample_layers(wl, roles):
+    """The layers of the CPU-oracle sample: the first anchor group (layer 0,
+    a proposal layer, up to the next proposal layer)."""
+    nxt = [l for l in range(1, len(roles)) if roles[l] == "F"]
+    return list(range(nxt[0] if nxt else len(roles)))
+
+
+def host_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return len(os.sched_getaffinity(0)), int(blas), model
+
+
+def cpu_baseline(wl, host, roles, seconds, pool_rho=0, int2=False):
+    """The CPU oracle, as it stands, on a bounded sample of the workload: every
+    layer of the first anchor group (`host` holds their inputs), one (sequence,
+    KV head) problem at a time, the problems in order and again from the first
+    until about `seconds` have passed; the mean time of a layer of each role
+    per problem, extrapolated to every problem and layer of a decode step."""
     import numpy as np
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        blas_threads = 1
+    cores, blas, model = host_info()
     pg = synth.paging(wl)
-    G = wl.group
-    la, lr = 0, 1
-    qa, qr = oracle.bf16_to_f64(host[la].q), oracle.bf16_to_f64(host[lr].q)
+    layers = sorted(host)
     probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
-    ta, tr, ts, done = [], [], [], 0
-    t_start = time.perf_counter()
-    for b, g in probs:
-        L = int(pg.seq_lens[b])
-        t0 = time.perf_counter()
-        A, sa = oracle.anchor_select(qa[b, g * G:(g + 1) * G], host[la].k_pages,
-                                     pg.block_table[b], g, L, wl.kappa, wl.page_size, int2=int2)
-        pool = oracle.rank_pool(sa, np.arange(L), pool_rho, wl.kappa) if pool_rho >= 1 else None
-        oracle.attend(qa[b, g * G:(g + 1) * G], host[la].k_pages, host[la].v_pages,
-                      pg.block_table[b], g, A, wl.page_size, oracle.default_scale(wl.head_dim))
-        t1 = time.perf_counter()
-        if pool is not None:
-            T, _ = oracle.refine_in_pool(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
-                                         pg.block_table[b], g, pool, wl.kappa, wl.page_size,
-                                         int2=int2)
-        else:
-            T, _, _ = oracle.refined_select(qr[b, g * G:(g + 1) * G], host[lr].k_pages,
-                                            pg.block_table[b], g, L, wl.kappa, wl.page_size, A,
-                                            wl.window, int2=int2)
-        oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
-                      pg.block_table[b], g, T, wl.page_size, oracle.default_scale(wl.head_dim))
-        t2 = time.perf_counter()
-        if roles is not None and "S" in roles:   # a shared layer: attention over A only
-            oracle.attend(qr[b, g * G:(g + 1) * G], host[lr].k_pages, host[lr].v_pages,
-                          pg.block_table[b], g, A, wl.page_size,
-                          oracle.default_scale(wl.head_dim))
-        t3 = time.perf_counter()
-        ta.append(t1 - t0)
-        tr.append(t2 - t1)
-        ts.append(t3 - t2)
+    times = {"F": [], "R": [], "S": []}
+    done, t_start = 0, time.perf_counter()
+    while done == 0 or time.perf_counter() - t_start < seconds:
+        b, g = probs[done % len(probs)]
+        state = pstate = shared = None
+        for l in layers:
+            li = host[l]
+            t0 = time.perf_counter()
+            r = oracle.decode_layer(l, li.q, li.k_pages, li.v_pages, pg.block_table, pg.seq_lens,
+                                    num_kv_heads=wl.num_kv_heads, kappa=wl.kappa,
+                                    anchor_stride=wl.anchor_stride, window=wl.window,
+                                    page_size=wl.page_size, anchor_state=state,
+                                    pool_rho=pool_rho, pool_state=pstate, role=roles[l],
+                                    shared_state=shared, int2=int2, problems=[(b, g)])
+            times[roles[l]].append(time.perf_counter() - t0)
+            state, pstate, shared = r["anchor_state"], r["pool_state"], r["shared_state"]
         done += 1
-        if time.perf_counter() - t_start > seconds:
-            break
-    roles = roles or [("F" if wl.is_anchor(l) else "R") for l in range(wl.num_layers)]
-    n_anchor, n_ref, n_sh = roles.count("F"), roles.count("R"), roles.count("S")
+    elapsed = time.perf_counter() - t_start
     P = len(probs)
-    step_s = P * (n_anchor * float(np.mean(ta)) + n_ref * float(np.mean(tr))
-                  + n_sh * float(np.mean(ts)))
-    return {"value": wl.batch / step_s, "unit": "tokens/s", "cores": int(blas_threads),
+    step_s = P * sum(roles.count(c) * float(np.mean(times[c])) for c in "FRS" if times[c])
+    counts = {c: roles.count(c) for c in "FRS" if roles.count(c)}
+    return {"value": wl.batch / step_s, "unit": "tokens/s", "cores": cores,
             "kind": "oracle",
             "sample": (f"oracle (numpy float64"
                        + (", INT2 keys quantized from bf16 on the fly" if int2 else "")
-                       + f") on layer {la} (anchor) and layer {lr} (refined) "
-                       f"for {done} of {P} (sequence, KV head) problems "
-                       f"({time.perf_counter() - t_start:.1f} s); per-problem times "
-                       f"extrapolated to {n_anchor} anchor + {n_ref} refined"
-                       + (f" + {n_sh} shared (attention only)" if n_sh else "")
-                       + f" layers x {P} problems"),
-            "ms_per_step": step_s * 1e3}
+                       + f") over layers {layers[0]}-{layers[-1]} (one anchor group) for "
+                       f"{done} (sequence, KV head) problem runs ({min(done, P)} distinct of {P}) "
+                       f"in {elapsed:.1f} s; mean per-problem time of each layer role "
+                       f"extrapolated to {P} problems x " + " + ".join(
+                           f"{n} {c}" for c, n in counts.items()) + " layers"),
+            "ms_per_step": step_s * 1e3, "affinity_cores": cores, "blas_threads": blas,
+            "cpu_model": model}
+
+
+def trace_summary(args):
+    """Per-kernel durations of the graph-replayed and eager timed regions of a
+    rocprofv3 kernel trace of this script (run with the same options).  The
+    library's kernels are cut into decode steps of launches_per_step kernels:
+    W eager warm-up steps, max(1, W) graph warm-up replays, K timed replays
+    (region 1), K eager steps (region 2), then the untimed byte-count pass."""
+    import csv
+    import numpy as np
+    import synth
+    wl = synth.BY_NAME[args.workload]
+    roles = layer_roles(wl, args.pattern)
+    per_step = launches_per_step(wl, args.cus, args.pool_rho, roles, args.dense)
+    n = sum(per_step.values())
+    with open(args.trace_summary) as f:
+        rows = [r for r in csv.DictReader(f) if "prism::" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+
+    def name(r):
+        k = r["Kernel_Name"].replace("void ", "").replace("prism::(anonymous namespace)::", "")
+        return k.split("(")[0]
+
+    W, K = args.warmup, args.steps
+    g0 = (W + max(1, W)) * n
+    regions = {"graph replay": rows[g0:g0 + K * n], "eager": rows[g0 + K * n:g0 + 2 * K * n]}
+    first = [name(r) for r in rows[:n]]
+    for label, rs in regions.items():
+        if len(rs) != K * n or any([name(r) for r in rs[i * n:(i + 1) * n]] != first
+                                   for i in range(K)):
+            sys.exit(f"trace does not hold {K} whole steps of {n} kernels in the {label} region")
+    print(f"{K} steps of {n} kernels per region; durations End - Start of each dispatch (us)")
+    print("| kernel | per step | graph replay avg | median | eager avg | median | "
+          "graph step span (ms) |")
+    print("|---|---|---|---|---|---|---|")
+    stats = {}
+    for label, rs in regions.items():
+        d = {}
+        for r in rs:
+            d.setdefault(name(r), []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        stats[label] = d
+    rs = regions["graph replay"]
+    spans = [(int(rs[(i + 1) * n - 1]["End_Timestamp"]) - int(rs[i * n]["Start_Timestamp"])) / 1e6
+             for i in range(K)]
+    for k in dict.fromkeys(first):
+        gd, ed = stats["graph replay"][k], stats["eager"][k]
+        print(f"| `{k}` | {len(gd) // K} | {np.mean(gd):.2f} | {np.median(gd):.2f} | "
+              f"{np.mean(ed):.2f} | {np.median(ed):.2f} | |")
+    print(f"| step (first start to last end) | | | | | | {np.mean(spans):.4f} mean, "
+          f"{np.median(spans):.4f} median |")
 
 
 def main():
@@ -237,7 +297,15 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and "
                          "exit: the known-size reference for hardware byte counters")
+    ap.add_argument("--trace-summary", default="", metavar="CSV",
+                    help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
+                         "of this script with the same workload options, --steps and --warmup, and "
+                         "print per-kernel durations in its graph-replayed and eager regions")
+    ap.add_argument("--cus", type=int, default=256, help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -282,7 +350,7 @@ def main():
     sl = torch.from_numpy(pg.seq_lens).to(dev)
     L_max, L_min = int(pg.seq_lens.max()), int(pg.seq_lens.min())
     q_dev, kv_dev, host_keep = {}, {}, {}
-    keep_host = {0, 1} if args.cpu_seconds > 0 else set()
+    keep_host = set(sample_layers(wl, roles)) if args.cpu_seconds > 0 else set()
     nthreads = synth.default_threads()
     with ThreadPoolExecutor(nthreads) as ex:
         futs = {ex.submit(synth.layer_inputs, wl, l, 1): l for l in range(nd)}
@@ -343,57 +411,62 @@ def main():
     rt = hip.rt
     rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     e_start, e_stop = hip.events(1)[0], hip.events(1)[0]
+    per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
+                                 args.pool_rho, roles, args.dense)
+
+    def capture():
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step()
+        torch.cuda.synchronize()
+        return gr
+
+    def timed(run, k):
+        """k runs between two events; each run also between events of its own.
+        Returns (mean ms per run over the whole bracket, median ms of the runs)."""
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        marks = hip.events(k + 1)
+        torch.cuda.synchronize()
+        rt.hipEventRecord(e_start, s)
+        for i in range(k):
+            rt.hipEventRecord(marks[i], s)
+            run()
+        rt.hipEventRecord(marks[k], s)
+        rt.hipEventRecord(e_stop, s)
+        torch.cuda.synchronize()
+        each = [hip.elapsed_ms(marks[i], marks[i + 1]) for i in range(k)]
+        hip.destroy(marks)
+        return hip.elapsed_ms(e_start, e_stop) / k, float(np.median(each))
 
     # ---- timed region 1 (the reported value): the step captured once as a HIP
     #      graph, replayed K times ----------------------------------------------------
-    graph_ms, graph_err = None, None
+    graph_ms = graph_med = None
+    graph_err = None
     if not args.eager:
         try:
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                step()
+            gr = capture()
             for _ in range(max(1, args.warmup)):
                 gr.replay()
-            torch.cuda.synchronize()
-            gs = torch.cuda.current_stream()
-            wall0 = time.perf_counter()
-            rt.hipEventRecord(e_start, ctypes.c_void_p(gs.cuda_stream))
-            for _ in range(args.steps):
-                gr.replay()
-            rt.hipEventRecord(e_stop, ctypes.c_void_p(gs.cuda_stream))
-            torch.cuda.synchronize()
-            wall1 = time.perf_counter()
-            graph_ms = hip.elapsed_ms(e_start, e_stop) / args.steps
+            graph_ms, graph_med = timed(gr.replay, args.steps)
             log(f"[bench] graph replay, {args.steps} steps: {graph_ms:.4f} ms/step "
-                f"(wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
+                f"(median {graph_med:.4f})")
             del gr
         except Exception as exc:  # report it and fall back to eager launches
             graph_err = str(exc)[:200]
             log(f"[bench] graph capture failed ({graph_err}); reporting eager launches")
             torch.cuda.synchronize()
 
-    # ---- timed region 2: eager launches, every kernel's start and end recorded
-    #      by its dispatch (per-kernel durations and the roofline) -------------------
-    per_step = launches_per_step(wl, torch.cuda.get_device_properties(dev).multi_processor_count,
-                                 args.pool_rho, roles, args.dense)
+    # ---- timed region 2: the same K steps launched eagerly, every kernel's start
+    #      and end recorded by its own dispatch (the AQL packet's timestamps, as
+    #      rocprofv3 takes them): per-kernel durations and the roofline ----------------
     rings = {}
     for kind, n in per_step.items():
         cnt = n * args.steps
         rings[kind] = (hip.events(cnt), hip.events(cnt))
         tsa.prism_profile_events(kind, rings[kind][0], rings[kind][1])
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    rt.hipEventRecord(e_start, ctypes.c_void_p(stream.cuda_stream))
-    for _ in range(args.steps):
-        step()
-    rt.hipEventRecord(e_stop, ctypes.c_void_p(stream.cuda_stream))
-    torch.cuda.synchronize()
-    wall1 = time.perf_counter()
-    eager_ms = hip.elapsed_ms(e_start, e_stop) / args.steps
+    eager_ms, eager_med = timed(step, args.steps)
     log(f"[bench] eager launches with per-kernel events, {args.steps} steps: {eager_ms:.4f} "
-        f"ms/step (wall {1e3 * (wall1 - wall0) / args.steps:.4f} ms/step)")
-    ms_per_step = graph_ms if graph_ms is not None else eager_ms
-
+        f"ms/step (median {eager_med:.4f})")
     kernels = {}
     for kind, (starts, stops) in rings.items():
         n = tsa.prism_profile_launches(kind)
@@ -401,9 +474,15 @@ def main():
         durs = [hip.elapsed_ms(a, b) for a, b in zip(starts, stops)]
         kernels[kind] = {"launches_per_step": per_step[kind],
                          "avg_us": 1e3 * float(np.mean(durs)) if durs else 0.0,
+                         "median_us": 1e3 * float(np.median(durs)) if durs else 0.0,
                          "us_per_step": 1e3 * float(np.sum(durs)) / args.steps}
         tsa.prism_profile_events(kind, [], [])
         hip.destroy(starts + stops)
+    log("[bench] per-kernel durations: " + ", ".join(
+        f"{k} {v['avg_us']:.2f} us x {v['launches_per_step']}"
+        for k, v in kernels.items() if v["launches_per_step"]))
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    step_med = graph_med if graph_ms is not None else eager_med
 
     # ---- algorithmic bytes ----------------------------------------------------------
     D2 = wl.head_dim * 2
@@ -443,7 +522,8 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic_for(dominant, wl.name),
                 "algorithmic_bytes_per_launch": int(algo[dominant]),
-                "avg_launch_us": round(dk["avg_us"], 3)}
+                "avg_launch_us": round(dk["avg_us"], 3),
+                "timed_in": "eager launches, dispatch timestamps"}
 
     result = {
         "metric": "sparse decode-attn tokens/sec + % HBM roofline at 128K, kappa=2048 (1 GPU)",
@@ -453,6 +533,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_ms_median": round(step_med, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -485,7 +566,7 @@ def main():
 
     if args.cpu_seconds > 0 and not args.dense:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        cb = cpu_baseline(wl, host_keep, args.cpu_seconds, args.pool_rho, roles, args.int2)
+        cb = cpu_baseline(wl, host_keep, roles, args.cpu_seconds, args.pool_rho, args.int2)
         result["cpu_baseline"] = {k: (round(v, 4) if isinstance(v, float) else v)
                                   for k, v in cb.items()}
     else:

@@ -8,3 +8,18 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+_SUMMARY = []
+
+
+def record_summary(line: str) -> None:
+    """A line for the end-of-run summary (parity counts of the full-size cases)."""
+    _SUMMARY.append(line)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if _SUMMARY:
+        terminalreporter.section("parity summary")
+        for line in _SUMMARY:
+            terminalreporter.write_line(line)

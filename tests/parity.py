@@ -36,10 +36,11 @@ def dev(a: np.ndarray) -> torch.Tensor:
 class Setup:
     """Seeded inputs of some layers of a workload, resident on the device."""
 
-    def __init__(self, wl: synth.Workload, layers, pool_rho=0, int2=False):
+    def __init__(self, wl: synth.Workload, layers, pool_rho=0, int2=False, host=None):
         """int2: quantize every layer's keys on the GPU (prism_quantize_keys)
         and score from the INT2 codes; the oracle then scores its own
-        quantization of the same keys."""
+        quantization of the same keys.  host: already generated layer inputs
+        ({layer: synth.layer_inputs(wl, layer)}) to use instead of generating."""
         self.wl = wl
         self.int2 = int2
         self.pg = synth.paging(wl)
@@ -48,7 +49,7 @@ class Setup:
         self.host = {}
         self.q, self.kv = {}, {}
         for l in layers:
-            li = synth.layer_inputs(wl, l)
+            li = host[l] if host is not None else synth.layer_inputs(wl, l)
             self.host[l] = li
             self.q[l] = dev(li.q)
             self.kv[l] = tsa.KVCache(dev(li.k_pages), dev(li.v_pages), self.bt, self.sl,

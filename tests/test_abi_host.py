@@ -245,3 +245,7 @@ def test_int2_cache_fields_checked_on_host():
         assert _call(fn, _kv(new_keys=7), _params()) == L.PRISM_ERR_HIP, fn
     odd = _kv(new_keys=1000)
     assert lib.prism_quantize_keys(ctypes.byref(odd), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP
+    # prism_quantize_keys reads neither kv->k_codes nor kv->k_scales: a half-set
+    # or misaligned pair there is not an error for it
+    for kvx in (_kv(k_codes=FAKE), _kv(k_scales=FAKE), _kv(k_codes=FAKE + 8, k_scales=FAKE)):
+        assert lib.prism_quantize_keys(ctypes.byref(kvx), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP

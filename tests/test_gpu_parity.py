@@ -2,8 +2,11 @@
 
 Small cases span several workgroup tiles and ragged tails; the full-size cases
 run every workload at its real shape through prism_decode_layer (the launch
-path the benchmark times) and check sampled (sequence, KV head) problems."""
+path the benchmark times) and check every (sequence, KV head) problem over a
+whole anchor group."""
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import pytest
@@ -12,9 +15,11 @@ import torch
 import oracle
 import synth
 import token_sparse_attention_gqa_amd as tsa
+from tests.conftest import record_summary
 from tests.parity import Setup, check_attn, check_set, dev, unpack_int2_codes
 
 pytestmark = pytest.mark.gpu
+PAR_WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 def say(*a):
@@ -232,9 +237,19 @@ def test_attention_dense_and_ignored_entries():
 
 
 # ---------------------------------------------------------------------- decode chain
+def _par(fn, items):
+    """fn over items on a thread pool (the oracle's numpy work releases the
+    GIL), results in order; the first exception is raised."""
+    items = list(items)
+    if len(items) <= 2:
+        return [fn(x) for x in items]
+    with ThreadPoolExecutor(min(len(items), PAR_WORKERS)) as ex:
+        return list(ex.map(fn, items))
+
+
 def _run_chain(st, layers, problems, label):
     """prism_decode_layer over `layers` in order; each layer checked against the
-    oracle applied to the GPU's own anchor sets (chained) for the sampled problems."""
+    oracle applied to the GPU's own anchor sets (chained) for the listed problems."""
     wl = st.wl
     anchor = st.idx_buf()
     layer_idx = st.idx_buf()
@@ -250,16 +265,22 @@ def _run_chain(st, layers, problems, label):
         if wl.is_anchor(l):
             A_gpu = anchor.cpu().numpy()
             assert np.array_equal(A_gpu, sel)
-        for b, g in problems:
+
+        def check(bg, l=l, sel=sel, o=o, A_gpu=A_gpu):
+            b, g = bg
             if wl.is_anchor(l):
                 want, s = st.oracle_anchor(l, b, g)
                 pool = np.arange(int(st.pg.seq_lens[b]))
             else:
                 want, pool, s = st.oracle_refine(l, b, g, A_gpu[b, g])
-            stats[check_set(sel[b, g], want, s, pool, wl.kappa, f"{label} l{l} b{b} g{g}")] += 1
+            r = check_set(sel[b, g], want, s, pool, wl.kappa, f"{label} l{l} b{b} g{g}")
             G = wl.group
             check_attn(o[b, g * G:(g + 1) * G], st.oracle_attend(l, b, g, sel[b, g]),
                        f"{label} l{l} b{b} g{g}")
+            return r
+
+        for r in _par(check, problems):
+            stats[r] += 1
     say(f"[{label}] sets: {stats}")
     return stats
 
@@ -361,24 +382,32 @@ def _run_chain_rank(st, layers, problems, label):
         if wl.is_anchor(l):
             assert np.array_equal(anchor.cpu().numpy(), sel)
             pool_gpu, plen_gpu, _ = _gpu_pool(st, l)
-        for b, g in problems:
+
+        def check(bg, l=l, sel=sel, o=o, pool_gpu=pool_gpu, plen_gpu=plen_gpu):
+            b, g = bg
+            res = []
             L = int(st.pg.seq_lens[b])
             where = f"{label} l{l} b{b} g{g}"
             if wl.is_anchor(l):
                 want, s = st.oracle_anchor(l, b, g)
-                stats[check_set(sel[b, g], want, s, np.arange(L), wl.kappa, where)] += 1
+                res.append(check_set(sel[b, g], want, s, np.arange(L), wl.kappa, where))
                 m = min(st.pool_rho * wl.kappa, L)
                 assert plen_gpu[b, g] == m, (where, plen_gpu[b, g], m)
                 gp = pool_gpu[b, g, :m]
                 wp = st.oracle_rank_pool(s, b)
-                stats[check_set(gp, wp, s, np.arange(L), m, where + " pool")] += 1
+                res.append(check_set(gp, wp, s, np.arange(L), m, where + " pool"))
                 assert np.isin(sel[b, g], gp).all(), where + ": set outside its pool"
             else:
                 gp = pool_gpu[b, g, :plen_gpu[b, g]]
                 want, s = st.oracle_refine_in_pool(l, b, g, gp)
-                stats[check_set(sel[b, g], want, s, gp, wl.kappa, where)] += 1
+                res.append(check_set(sel[b, g], want, s, gp, wl.kappa, where))
             G = wl.group
             check_attn(o[b, g * G:(g + 1) * G], st.oracle_attend(l, b, g, sel[b, g]), where)
+            return res
+
+        for res in _par(check, problems):
+            for r in res:
+                stats[r] += 1
     say(f"[{label}] sets: {stats}")
     return stats
 
@@ -600,15 +629,6 @@ def test_int2_decode_chain_groups(G):
                       kappa=300, window=100, num_layers=3, anchor_stride=3)
     st = Setup(wl, range(3), int2=True)
     _run_chain(st, range(3), [(b, g) for b in range(3) for g in range(2)], f"int2-g{G}")
-
-
-def test_int2_full_size_planted_128k():
-    """The 128K planted workload with INT2 keys in the benchmark's launch
-    configuration: layers 0 (anchor), 1 and 7 (refined), every problem."""
-    wl = synth.LLAMA_128K_PLANTED
-    say(f"[int2 full] {wl.name}")
-    st = Setup(wl, [0, 1, 7], int2=True)
-    _run_chain(st, [0, 1, 7], [(0, g) for g in range(wl.num_kv_heads)], f"int2 {wl.name}")
 
 
 def _new_key_slots(st, nk):
@@ -866,20 +886,51 @@ def test_graph_replay_matches_eager(mode):
 
 
 # ---------------------------------------------------------------------- full sizes
-FULL = [
-    (synth.LLAMA_32K, [0, 1, 7], None),
-    (synth.LLAMA_128K_PLANTED, [0, 1, 7], None),
-    (synth.BATCHED_16, [0, 1, 3], 6),
-    (synth.LONG_4x128K, [0, 1, 7], 5),
+# Every workload at its real shape, in the launch configuration the benchmark
+# times (prism_decode_layer), over a whole anchor group (the anchor layer and
+# every refined layer that re-selects from its set), every (sequence, KV head)
+# problem against the oracle.  Variants: the window pool, the rank-expanded
+# pool (rho = 4) and INT2 proposal keys with either pool.  A workload's host
+# inputs are generated once (layer by layer, in parallel) and shared by its
+# variants.
+FULL_CASES = [
+    (synth.LLAMA_32K, "window"), (synth.LLAMA_32K, "rank4"), (synth.LLAMA_32K, "int2-rank4"),
+    (synth.LLAMA_128K_PLANTED, "window"), (synth.LLAMA_128K_PLANTED, "rank4"),
+    (synth.LLAMA_128K_PLANTED, "int2-window"),
+    (synth.BATCHED_16, "window"), (synth.BATCHED_16, "rank4"), (synth.BATCHED_16, "int2-rank4"),
+    (synth.LONG_4x128K, "window"), (synth.LONG_4x128K, "rank4"),
+    (synth.LONG_4x128K, "int2-rank4"),
 ]
+_HOST_CACHE = {}
 
 
-@pytest.mark.parametrize("wl,layers,nsample", FULL, ids=[f[0].name for f in FULL])
-def test_full_size_sampled(wl, layers, nsample):
-    say(f"[full] {wl.name}: generating layers {layers}")
-    st = Setup(wl, layers)
+def _group_layers(wl):
+    return list(range(min(wl.anchor_stride, wl.num_layers)))
+
+
+def _host_layers(wl, layers):
+    """Host inputs of `layers`, generated in parallel; only the latest
+    workload's are kept."""
+    if wl.name not in _HOST_CACHE:
+        _HOST_CACHE.clear()
+        with ThreadPoolExecutor(min(len(layers), PAR_WORKERS)) as ex:
+            got = list(ex.map(lambda l: synth.layer_inputs(wl, l, 1), layers))
+        _HOST_CACHE[wl.name] = dict(zip(layers, got))
+    return _HOST_CACHE[wl.name]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("wl,variant", FULL_CASES, ids=[f"{w.name}-{v}" for w, v in FULL_CASES])
+def test_full_size_every_problem(wl, variant):
+    layers = _group_layers(wl)
+    say(f"[full] {wl.name} {variant}: layers {layers[0]}-{layers[-1]}, "
+        f"{wl.batch * wl.num_kv_heads} problems")
+    host = _host_layers(wl, layers)
+    rho = 4 if variant.endswith("rank4") else 0
+    st = Setup(wl, layers, pool_rho=rho, int2=variant.startswith("int2"), host=host)
     probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
-    if nsample is not None:
-        rng = np.random.default_rng(wl.wid)
-        probs = [probs[i] for i in sorted(rng.choice(len(probs), nsample, replace=False))]
-    _run_chain(st, layers, probs, wl.name)
+    label = f"{wl.name} {variant}"
+    stats = (_run_chain_rank if rho else _run_chain)(st, layers, probs, label)
+    record_summary(f"full size {label}: layers {layers[0]}-{layers[-1]} x {len(probs)} problems, "
+                   f"sets exact {stats['exact']}, near-tie {stats['near-tie']}")
+    del st

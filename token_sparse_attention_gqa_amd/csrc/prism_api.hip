@@ -286,14 +286,20 @@ prism_status prism_dense_attn(const prism_kv_cache* kv, const uint16_t* q,
 
 prism_status prism_quantize_keys(const prism_kv_cache* kv, int32_t num_new, uint8_t* k_codes,
                                  uint16_t* k_scales, void* stream) {
-  PRISM_TRY(resolve_cache(kv));
+  if (!kv) return fail(PRISM_ERR_INVALID_ARG, "kv cache must not be NULL");
+  // kv->k_codes, kv->k_scales and kv->new_keys are not read here: validate the
+  // rest of the description without them
+  prism_kv_cache c = *kv;
+  c.k_codes = nullptr;
+  c.k_scales = nullptr;
+  PRISM_TRY(resolve_cache(&c));
   if (!k_codes || !k_scales)
     return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must not be NULL");
   if (!aligned(k_codes, 16) || !aligned(k_scales, 16))
     return fail(PRISM_ERR_INVALID_ARG, "k_codes and k_scales must be 16-byte aligned");
   PRISM_TRY(check_device());
   Geometry g{};
-  fill_cache(kv, &g);
+  fill_cache(&c, &g);
   return hip_check(prism::launch_quantize(g, num_new, k_codes, k_scales,
                                           static_cast<hipStream_t>(stream)),
                    "quantize launch");
