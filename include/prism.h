@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PRISM_ABI_VERSION 6
+#define PRISM_ABI_VERSION 7
 
 #if defined(__GNUC__) || defined(__clang__)
 #define PRISM_API __attribute__((visibility("default")))
@@ -221,6 +221,32 @@ PRISM_API prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* k
                                 const prism_params* params, int32_t* anchor_idx,
                                 int32_t* layer_idx_out, float* out, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * prism_decode_layer with the library's own static workspace instead of a
+ * caller-owned one, same arguments otherwise.  Allocates nothing: the
+ * workspace is a file-scope __device__ array of PRISM_STATIC_WORKSPACE_BYTES
+ * (64 MiB) in the library's device code, which every GPU the library runs on
+ * holds until the process ends.  The first call on a device resolves the
+ * array's device address (hipGetSymbolAddress, which may load the library's
+ * code object onto that device): make it outside graph capture.
+ *   Returns PRISM_ERR_WORKSPACE, enqueueing nothing, when the shapes need more
+ *   workspace than that (prism_workspace_size(kv, params) > 64 MiB), and the
+ *   statuses of prism_decode_layer otherwise.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: the layers of a decode step run in order with the same shapes
+ * (the anchor layer leaves its pool there for the refined layers), and calls
+ * that overlap on one GPU (other streams or threads) race with each other.
+ * Nothing in it needs clearing first: the kernels check every counter they
+ * read from the workspace and take an exact pass when one is stale.
+ */
+#define PRISM_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+PRISM_API prism_status prism_decode_layer_noalloc(int32_t layer, const prism_kv_cache* kv,
+                                                  const uint16_t* q, const prism_params* params,
+                                                  int32_t* anchor_idx, int32_t* layer_idx_out,
+                                                  float* out, void* stream);
 
 /*
  * Dense decode attention over every cached token (the FlashAttention-style

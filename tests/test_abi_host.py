@@ -54,7 +54,7 @@ def test_library_exports_every_declared_function():
                              "prism_last_error", "prism_abi_version", "prism_profile_events",
                              "prism_profile_launches", "prism_pattern_role",
                              "prism_decode_layer_role", "prism_quantize_keys",
-                             "prism_dense_attn"}
+                             "prism_dense_attn", "prism_decode_layer_noalloc"}
     lib = tsa.lib()
     for name in declared:
         assert hasattr(lib, name), name
@@ -65,7 +65,7 @@ def test_version_and_status_strings():
     import re
     with open(L.HEADER) as f:
         header = int(re.search(r"#define PRISM_ABI_VERSION (\d+)", f.read()).group(1))
-    assert tsa.prism_abi_version() == header == L.ABI_VERSION == 6
+    assert tsa.prism_abi_version() == header == L.ABI_VERSION == 7
     for s in (0, -1, -2, -3, -4):
         assert tsa.prism_status_string(s) and tsa.prism_status_string(s) != "unknown status"
     assert tsa.prism_status_string(-99) == "unknown status"
@@ -249,3 +249,37 @@ def test_int2_cache_fields_checked_on_host():
     # or misaligned pair there is not an error for it
     for kvx in (_kv(k_codes=FAKE), _kv(k_scales=FAKE), _kv(k_codes=FAKE + 8, k_scales=FAKE)):
         assert lib.prism_quantize_keys(ctypes.byref(kvx), 1, FAKE, FAKE, None) == L.PRISM_ERR_HIP
+
+
+def test_noalloc_entry_point_checks_on_host():
+    """prism_decode_layer_noalloc validates like prism_decode_layer, rejects
+    shapes whose workspace exceeds the static 64 MiB with PRISM_ERR_WORKSPACE
+    before touching a device, and reports a missing GPU as PRISM_ERR_HIP."""
+    lib = tsa.lib()
+    assert tsa.PRISM_STATIC_WORKSPACE_BYTES == 64 << 20
+
+    def call(kv, p, layer=0, anchor=FAKE, out=FAKE):
+        return lib.prism_decode_layer_noalloc(layer, ctypes.byref(kv) if kv is not None else None,
+                                              FAKE, ctypes.byref(p) if p is not None else None,
+                                              anchor, None, out, None)
+    assert call(None, _params()) == L.PRISM_ERR_INVALID_ARG
+    assert call(_kv(), None) == L.PRISM_ERR_INVALID_ARG
+    assert call(_kv(head_dim=64), _params()) == L.PRISM_ERR_UNSUPPORTED
+    assert call(_kv(), _params(kappa=0)) == L.PRISM_ERR_INVALID_ARG
+    assert call(_kv(), _params(), layer=-1) == L.PRISM_ERR_INVALID_ARG
+    assert call(_kv(), _params(), anchor=None) == L.PRISM_ERR_INVALID_ARG
+    assert call(_kv(), _params(), out=None) == L.PRISM_ERR_INVALID_ARG
+    # 16 x 8 problems over 262144-token lists need far more than 64 MiB
+    big = _kv(batch=16, num_pages=65536, max_pages_per_seq=4096, max_seq_len=262144,
+              min_seq_len=8192)
+    need = lib.prism_workspace_size(ctypes.byref(big), ctypes.byref(_params()))
+    assert need > tsa.PRISM_STATIC_WORKSPACE_BYTES
+    assert call(big, _params()) == L.PRISM_ERR_WORKSPACE
+    assert b"static workspace" in lib.prism_last_error()
+    small = _kv()
+    assert lib.prism_workspace_size(ctypes.byref(small), ctypes.byref(_params())) <= \
+        tsa.PRISM_STATIC_WORKSPACE_BYTES
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: the fake addresses must not reach a kernel")
+    assert call(small, _params()) == L.PRISM_ERR_HIP

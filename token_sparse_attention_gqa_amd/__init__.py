@@ -6,6 +6,7 @@ this package is its ctypes binding.  Functions carry the C names.
 """
 from ._lib import (PrismError, KVCache, params, lib, declared_functions, prism_workspace_size,
                    prism_score_topk, prism_refine_topk, prism_sparse_attn, prism_decode_layer,
+                   prism_decode_layer_noalloc, PRISM_STATIC_WORKSPACE_BYTES,
                    prism_status_string, prism_last_error, prism_abi_version, prism_profile_events,
                    prism_profile_launches, prism_pattern_role, prism_decode_layer_role,
                    prism_quantize_keys, int2_shapes, prism_dense_attn,
@@ -15,6 +16,7 @@ from ._lib import (PrismError, KVCache, params, lib, declared_functions, prism_w
 
 __all__ = ["PrismError", "KVCache", "params", "lib", "declared_functions", "prism_workspace_size",
            "prism_score_topk", "prism_refine_topk", "prism_sparse_attn", "prism_decode_layer",
+           "prism_decode_layer_noalloc", "PRISM_STATIC_WORKSPACE_BYTES",
            "prism_status_string", "prism_last_error", "prism_abi_version",
            "prism_profile_events", "prism_profile_launches", "prism_pattern_role",
            "prism_decode_layer_role", "prism_quantize_keys", "int2_shapes", "prism_dense_attn",

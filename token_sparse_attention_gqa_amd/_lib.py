@@ -13,6 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libprism.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "prism.h")
 
+PRISM_STATIC_WORKSPACE_BYTES = 64 << 20   # include/prism.h: the no-allocation call's workspace
 PRISM_OK, PRISM_ERR_INVALID_ARG, PRISM_ERR_UNSUPPORTED, PRISM_ERR_WORKSPACE, PRISM_ERR_HIP = \
     0, -1, -2, -3, -4
 
@@ -23,7 +24,7 @@ class PrismError(RuntimeError):
         self.status = status
 
 
-ABI_VERSION = 6   # PRISM_ABI_VERSION of include/prism.h that the structs below follow
+ABI_VERSION = 7   # PRISM_ABI_VERSION of include/prism.h that the structs below follow
 
 
 class KVCacheStruct(ctypes.Structure):
@@ -59,6 +60,9 @@ _SIGS = {
     "prism_decode_layer": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct), _P,
                                           ctypes.POINTER(ParamsStruct), _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]),
+    "prism_decode_layer_noalloc": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(KVCacheStruct),
+                                                  _P, ctypes.POINTER(ParamsStruct), _P, _P, _P,
+                                                  _P]),
     "prism_dense_attn": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), _P,
                                         ctypes.POINTER(ParamsStruct), _P, _P, ctypes.c_size_t, _P]),
     "prism_quantize_keys": (ctypes.c_int, [ctypes.POINTER(KVCacheStruct), ctypes.c_int32, _P, _P,
@@ -249,6 +253,18 @@ def prism_decode_layer(layer, kv, q, p, anchor_idx, layer_idx_out, out, workspac
                                          optional=True),
                                     _ptr(out, "out", itemsize=4), ws, nbytes, _stream(stream)),
            "prism_decode_layer")
+
+
+def prism_decode_layer_noalloc(layer, kv, q, p, anchor_idx, layer_idx_out, out, stream=None):
+    """prism_decode_layer on the library's static per-GPU workspace (no
+    allocation; shapes needing more than PRISM_STATIC_WORKSPACE_BYTES fail)."""
+    _check(lib().prism_decode_layer_noalloc(int(layer), ctypes.byref(kv.struct),
+                                            _ptr(q, "q", itemsize=2), ctypes.byref(p),
+                                            _ptr(anchor_idx, "anchor_idx", itemsize=4),
+                                            _ptr(layer_idx_out, "layer_idx_out", itemsize=4,
+                                                 optional=True),
+                                            _ptr(out, "out", itemsize=4), _stream(stream)),
+           "prism_decode_layer_noalloc")
 
 
 def prism_dense_attn(kv, q, p, out, workspace=None, stream=None):

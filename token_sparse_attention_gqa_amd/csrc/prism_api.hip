@@ -5,7 +5,14 @@
 
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 #include <string>
+
+// Workspace of prism_decode_layer_noalloc: one copy per GPU, in this file's
+// device code, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (on the host it names a stand-in, not device memory):
+// scratch_address() gives the current device's copy.
+static __device__ __align__(256) uint8_t scratch[PRISM_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -157,6 +164,31 @@ prism_status run_anchor(const Geometry& g, const Workspace& w, const uint16_t* q
   return hip_check(prism::launch_anchor(g, w, q, out, out2, s), "anchor selection launch");
 }
 
+// Device address of the current device's `scratch`, resolved once per device
+// (with that device current) by hipGetSymbolAddress and kept.
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+prism_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PRISM_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PRISM_ERR_UNSUPPORTED, "static workspace: device ordinal above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || !p)
+      return fail(PRISM_ERR_HIP, std::string("static workspace address: ") +
+                                     (es != hipSuccess ? hipGetErrorString(es) : "null"));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return PRISM_OK;
+}
+
 prism_status copy_rows(void* dst, size_t dst_row, const void* src, size_t src_row, size_t row,
                        size_t rows, hipStream_t s, const char* what) {
   return hip_check(hipMemcpy2DAsync(dst, dst_row, src, src_row, row, rows,
@@ -267,6 +299,29 @@ prism_status prism_decode_layer(int32_t layer, const prism_kv_cache* kv, const u
   return hip_check(
       prism::launch_refine_attend(g, w, q, resolve_scale(params), layer_idx_out, out, s),
       "refined layer launch");
+}
+
+prism_status prism_decode_layer_noalloc(int32_t layer, const prism_kv_cache* kv,
+                                        const uint16_t* q, const prism_params* params,
+                                        int32_t* anchor_idx, int32_t* layer_idx_out, float* out,
+                                        void* stream) {
+  Geometry g;
+  PRISM_TRY(resolve(kv, params, &g));
+  PRISM_TRY(check_q(q));
+  if (layer < 0) return fail(PRISM_ERR_INVALID_ARG, "layer must be >= 0");
+  if (!anchor_idx || !out) return fail(PRISM_ERR_INVALID_ARG, "anchor_idx and out must not be NULL");
+  const size_t need = prism::workspace_bytes(g);
+  if (need > PRISM_STATIC_WORKSPACE_BYTES)
+    return fail(PRISM_ERR_WORKSPACE,
+                "these shapes need " + std::to_string(need) +
+                    " bytes of workspace; the static workspace holds " +
+                    std::to_string(PRISM_STATIC_WORKSPACE_BYTES) +
+                    " (use prism_decode_layer with a caller-owned workspace)");
+  PRISM_TRY(check_device());
+  void* ws = nullptr;
+  PRISM_TRY(scratch_address(&ws));
+  return prism_decode_layer(layer, kv, q, params, anchor_idx, layer_idx_out, out, ws,
+                            PRISM_STATIC_WORKSPACE_BYTES, stream);
 }
 
 prism_status prism_dense_attn(const prism_kv_cache* kv, const uint16_t* q,
