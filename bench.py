@@ -89,15 +89,17 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
     196608), else a selection kernel per layer precedes the attention, and a
-    refined layer whose pool can exceed 16384 entries is classified first.
+    refined layer whose pool can exceed 16384 entries is classified first, and an
+    anchor layer that selects in its own kernel builds the window pool in
+    another.
     Shared layers launch the attention and its merge only.  With INT2 keys
     the newest key of every layer is quantized inside the layer's scoring
     kernel (a shared layer's, which scores nothing, inside its attention
     launch)."""
     import synth
     if dense:   # every layer: the dense chunks and their merge
-        return {"anchor_score": 0, "refine_score": 0, "select": 0, "attention": 0, "classify": 0,
-                "merge": wl.num_layers, "quantize": 0, "dense": wl.num_layers}
+        return {"anchor_score": 0, "refine_score": 0, "select": 0, "pool_build": 0, "attention": 0,
+                "classify": 0, "merge": wl.num_layers, "quantize": 0, "dense": wl.num_layers}
     roles = roles or layer_roles(wl)
     na, nr = roles.count("F"), roles.count("R")
     L = int(synth.paging(wl).seq_lens.max())
@@ -116,6 +118,7 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     anchor_need = pool_rho * wl.kappa if (pool_rho >= 1 and not anchor_fused) else wl.kappa
     return {"anchor_score": na, "refine_score": nr,
             "select": (0 if anchor_fused else na) + (0 if fused else nr),
+            "pool_build": 0 if (anchor_fused or pool_rho >= 1) else na,
             "attention": wl.num_layers,
             "classify": (na if (L > 16384 and L > anchor_need) else 0)
                         + (nr if pool_classify else 0),
@@ -297,6 +300,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times and "
                          "exit: the known-size reference for hardware byte counters")
+    ap.add_argument("--copy-rate", type=int, nargs="*", default=None, metavar="MIB",
+                    help="only time device-to-device copies of these sizes in MiB and exit: the "
+                         "rate a plain streaming kernel reaches at a kernel's working-set size")
     ap.add_argument("--trace-summary", default="", metavar="CSV",
                     help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
                          "of this script with the same workload options, --steps and --warmup, and "
@@ -323,6 +329,29 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.copy_rate:
+        # what a plain streaming kernel (the runtime's device copy) reaches at a
+        # kernel's working-set size: read + write bytes per copy over its time
+        res = {}
+        for mib in args.copy_rate:
+            src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(20)]
+            for e0, e1 in evs:
+                e0.record()
+                dst.copy_(src)
+                e1.record()
+            torch.cuda.synchronize()
+            us = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs])) * 1e3
+            res[f"{mib} MiB"] = {"median_us": round(us, 2),
+                                 "GBps": round(2 * (mib << 20) / (us * 1e-6) / 1e9, 1)}
+            del src, dst
+        print(json.dumps({"copy_rate": res}), flush=True)
         return
 
     import synth

@@ -1,6 +1,10 @@
 """Helpers of the GPU parity tests: upload seeded inputs, call the HIP library
 through its C ABI binding, and compare with the CPU oracle.
 
+Every buffer a test hands to the library through Setup (index sets, outputs,
+the workspace) sits between guard regions that check_guards() verifies after
+each GPU test.
+
 Comparison rules:
   * index sets: valid (kappa ascending distinct positions inside the pool) and
     identical to the oracle's whenever the oracle's kappa-th and (kappa+1)-th
@@ -24,6 +28,40 @@ OVERLAP_MIN = 0.999
 ATTN_MAX_ABS = 2e-3
 ATTN_REL_L2 = 1e-3
 NEAR_TIE = 1e-4
+
+
+# Output and workspace buffers handed to the library carry guard regions of a
+# known byte pattern before and after them; check_guards() (run after every
+# GPU test) asserts that no call wrote into them.
+GUARD_BYTES = 4096
+GUARD_BYTE = 0xA5
+_GUARDED = []
+
+
+def guarded_empty(shape, dtype, label=""):
+    """An uninitialised device tensor inside a larger allocation whose
+    GUARD_BYTES before and after it hold GUARD_BYTE."""
+    itemsize = torch.empty((), dtype=dtype).element_size()
+    n = int(np.prod(shape))
+    base = torch.empty(n * itemsize + 2 * GUARD_BYTES, dtype=torch.uint8, device="cuda")
+    base.fill_(GUARD_BYTE)
+    body = base[GUARD_BYTES:GUARD_BYTES + n * itemsize].view(dtype).view(*shape)
+    _GUARDED.append((base, label or f"{tuple(shape)} {dtype}"))
+    return body
+
+
+def check_guards():
+    """Asserts that every guard region allocated since the last check still
+    holds its pattern, then forgets them."""
+    torch.cuda.synchronize()
+    bad = []
+    for base, label in _GUARDED:
+        head = base[:GUARD_BYTES]
+        tail = base[base.numel() - GUARD_BYTES:]
+        if not (bool((head == GUARD_BYTE).all()) and bool((tail == GUARD_BYTE).all())):
+            bad.append(label)
+    _GUARDED.clear()
+    assert not bad, f"a library call wrote outside its buffer: {bad}"
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
@@ -65,20 +103,22 @@ class Setup:
         self.params = tsa.params(wl.num_q_heads, wl.kappa, wl.anchor_stride, wl.window,
                                  pool_rho=pool_rho)
         first = next(iter(self.kv.values()))
-        self.ws = torch.empty(tsa.prism_workspace_size(first, self.params), dtype=torch.uint8,
-                              device="cuda")
+        self.ws = guarded_empty((tsa.prism_workspace_size(first, self.params),), torch.uint8,
+                                "workspace")
 
     @property
     def P(self):
         return self.wl.batch * self.wl.num_kv_heads
 
     def idx_buf(self):
-        return torch.full((self.wl.batch, self.wl.num_kv_heads, self.wl.kappa), -7,
-                          dtype=torch.int32, device="cuda")
+        t = guarded_empty((self.wl.batch, self.wl.num_kv_heads, self.wl.kappa), torch.int32,
+                          "index set")
+        return t.fill_(-7)
 
     def out_buf(self):
-        return torch.full((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim), float("nan"),
-                          dtype=torch.float32, device="cuda")
+        t = guarded_empty((self.wl.batch, self.wl.num_q_heads, self.wl.head_dim), torch.float32,
+                          "attention output")
+        return t.fill_(float("nan"))
 
     # --- oracle views -------------------------------------------------------
     def q_group(self, l, b, g):

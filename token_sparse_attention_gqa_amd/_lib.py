@@ -10,7 +10,8 @@ import os
 import re
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libprism.so")
+# PRISM_LIBRARY: another build of the same library (the host-sanitizer test loads one)
+LIB_PATH = os.environ.get("PRISM_LIBRARY") or os.path.join(PKG_DIR, "libprism.so")
 HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "prism.h")
 
 PRISM_STATIC_WORKSPACE_BYTES = 64 << 20   # include/prism.h: the no-allocation call's workspace

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 
@@ -417,7 +418,11 @@ prism_status prism_profile_events(int32_t kind, void* const* start_events,
 int64_t prism_profile_launches(int32_t kind) { return prism::profile_launches(kind); }
 
 const char* prism_status_string(prism_status status) {
-  switch (status) {
+  // read as an integer: a C caller may pass any int, and a value outside the
+  // enumeration must not be loaded as the enum type
+  int32_t v;
+  std::memcpy(&v, &status, sizeof v);
+  switch (v) {
     case PRISM_OK: return "ok";
     case PRISM_ERR_INVALID_ARG: return "invalid argument";
     case PRISM_ERR_UNSUPPORTED: return "unsupported shape or parameter";

@@ -12,7 +12,6 @@ constexpr int kHeadDim = 128;         // elements per K/V row
 constexpr int kPageSize = 64;         // tokens per page
 constexpr int kSelThreads = 1024;     // threads of a selection workgroup
 constexpr int kScoreThreads = 256;    // threads of a relevance workgroup
-constexpr int kAnchorEntries = 1024;  // cached tokens scored by one anchor-layer workgroup
 constexpr int kMaxRankPool = 32768;   // largest rank-expanded pool (rho * kappa)
 constexpr int kMaxNewKeys = 64;       // most new keys a call quantizes in its scoring kernel
 constexpr int kPoolEntries = 256;     // pool entries scored by one refined-layer workgroup
@@ -52,12 +51,13 @@ struct Geometry {
 // Carved workspace regions (device pointers).  A row id r addresses the K/V
 // row at element offset r * head_dim of a layer's page array.
 struct Workspace {
-  uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram; followed by
-  uint32_t* cand_cnt;     // [P] threshold-bin entries gathered.  Both are left at zero
-                          //     by their last reader and checked by the selection
+  uint32_t* ghist;        // [P][kCoarseBins] anchor-layer score histogram, left at zero
+                          //     by its last reader and checked by the selection
+  uint32_t* cand_cnt;     // [P][W] threshold-bin entries found by classify workgroup w
+                          //     (W = workgroups per problem), written by every pass
   int32_t* sel_meta;      // [P][4] threshold bin, entries above it, entries in it
-  uint32_t* cand_key;     // [P][kMaxCand] order keys of the threshold-bin entries
-  int32_t* cand_idx;      // [P][kMaxCand] their list indices
+  uint32_t* cand_key;     // [P][W][2048] order keys of the threshold-bin entries, per
+  int32_t* cand_idx;      // [P][W][2048] classify workgroup; their list indices
   uint32_t* gbits;        // [P][n_cap / 32] marks of the entries above the threshold bin
   float* scores;          // [P][n_cap] relevance in list order
   int32_t* pool_pos;      // [P][n_cap] refinement pool: positions, ascending
@@ -65,16 +65,17 @@ struct Workspace {
   int32_t* pool_len;      // [P]
   uint32_t* sel_row;      // [P][kappa] row ids of the latest selection
   int32_t* idx_tmp;       // [P][kappa]
+  int32_t* sel_ent;       // [P][kappa] pool indices of a deferred selection (rank order)
   float* part_o;          // [P][splits][G][head_dim]
   float* part_ml;         // [P][splits][G][2]  (max logit, sum of exponentials)
   float* dense_o;         // [P][dense splits][G][head_dim]: dense decode partials
   float* dense_ml;        // [P][dense splits][G][2]
   // a second classification of the anchor list, made in the same pass as the
   // first (the rank-expanded pool's, beside the anchor set's): as above
-  uint32_t* cand_cnt2;    // [P], right after cand_cnt
+  uint32_t* cand_cnt2;    // [P][W]
   int32_t* sel_meta2;     // [P][4]
-  uint32_t* cand_key2;    // [P][kMaxCand]
-  int32_t* cand_idx2;     // [P][kMaxCand]
+  uint32_t* cand_key2;    // [P][W][2048]
+  int32_t* cand_idx2;     // [P][W][2048]
   uint32_t* gbits2;       // [P][n_cap / 32]
 };
 
@@ -108,9 +109,10 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
 hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
                              hipStream_t s);
 // Refined layer over the workspace's pool: relevance of the pool, top-kappa
-// into out, and the selection's row ids.
+// into out, and the selection's row ids; with `defer`, only the set's pool
+// indices (Workspace::sel_ent) and out is not written.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
-                         hipStream_t s);
+                         hipStream_t s, bool defer = false);
 // Anchor layer of a decode step: scoring, selection, the refinement pool and
 // SparseAttn.  anchor_idx receives the set (and layer_idx, if not null).
 hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
@@ -145,5 +147,9 @@ hipError_t launch_dense(const Geometry& g, const Workspace& w, const uint16_t* q
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
                             const int32_t* idx, bool use_sel_rows, float scale, float* out,
                             hipStream_t s, bool quantize_new = false);
+// SparseAttn over the pool indices a deferred refined selection left in the
+// workspace; pos_out (nullable) receives the set's positions.
+hipError_t launch_attention_entries(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                    int32_t* pos_out, float scale, float* out, hipStream_t s);
 
 }  // namespace prism

@@ -50,6 +50,13 @@ constexpr int kPassUnroll = 4;  // 16-byte loads in flight per thread in the lis
 constexpr int kPoolPer = kMaxKappa / NT;  // anchor entries per thread in the pool build
 constexpr int kClsThreads = 256;
 constexpr int kClsEntries = 8192;         // anchor-list entries classified by one workgroup
+constexpr int kClsCap = 2048;             // threshold-bin entries one classify workgroup keeps
+constexpr int kClsSlots = kMaxSeqLen / kClsEntries;  // classify workgroups of the longest list
+static_assert(kClsSlots <= 32, "candidate region starts fit sm.ured");
+// classify workgroups (candidate regions) per problem
+__host__ __device__ inline int cls_regions(const Geometry& g) {
+  return (g.n_cap + kClsEntries - 1) / kClsEntries;
+}
 constexpr int kFusedSplit = 128;          // selected tokens attended by one fused workgroup
 constexpr int kPoolHistChunks = 4;        // pool chunks per workgroup when pool scoring counts bins
 constexpr int kFusedAnchorLen = 6144 * 32;  // contexts whose nonzero mark words fit sm.hist
@@ -220,7 +227,7 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
 // Exclusive prefix sum over the T threads of the block; *total gets the sum.
 // tmp: at least T/64 ints of LDS.  Contains barriers: call uniformly.
 template <int T>
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   constexpr int NW = T / 64;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -286,8 +293,9 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// Anchor layer: workgroup w of problem p scores tokens [w * kAnchorEntries, +kAnchorEntries)
-// of the cache; each wave takes kAnchorEntries / 4 consecutive tokens (whole pages).  The
+// Anchor layer: workgroup w of problem p scores tokens [w * E, +E) of the cache,
+// E = 256 kPages tokens (kPages whole pages per wave; fewer for caches too short
+// to give every compute unit four workgroups of 1024 tokens).  The
 // workgroup also counts its scores by coarse bin (top 12 bits of the order
 // key) in LDS and adds the counts to the problem's histogram in the workspace,
 // which the selection uses to find the bin holding the kappa-th score.
@@ -300,19 +308,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // bf16 pair products with the group's query chunks (v_dot2), the 8 lanes of a
 // row sum their partials, and the maximum over the heads is the relevance.
 // Larger groups use the matrix cores (four MFMAs per 16 tokens).
-template <int G>
+template <int G, int kPages>
 __global__ __launch_bounds__(kScoreThreads) void score_anchor_kernel(Geometry g, Workspace ws,
                                                                      const uint16_t* __restrict__ q,
                                                                      int wgs) {
+  constexpr int kEntries = 4 * kPages * kPageSize;  // tokens of one workgroup, whole pages per wave
   __shared__ uint32_t lh[kCoarseBins];
   int p, w;
   map_block(blockIdx.x, g.problems(), wgs, &p, &w);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
-  if (w * kAnchorEntries >= n) return;  // uniform over the workgroup
+  if (w * kEntries >= n) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int kPages = kAnchorEntries / 4 / kPageSize;  // whole pages per wave
-  const int wbase = w * kAnchorEntries + wave * (kAnchorEntries / 4);
+  const int wbase = w * kEntries + wave * (kEntries / 4);
   for (int i = threadIdx.x; i < kCoarseBins; i += kScoreThreads) lh[i] = 0u;
   lds_barrier();
   if (wbase < n) {
@@ -565,13 +573,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // nearest, tie
 // [0, 3], 0 when alpha = 0; the subtraction and division are IEEE float32 (the
 // oracle takes the same decisions in the same precision).  -0 is read as +0.
 // quantize_kernel applies it to the keys of positions [max(0, L - num_new), L)
-// of every (sequence, KV head) (num_new <= 0: every position), four rows per
-// workgroup; the scoring kernels apply it to a decode step's new keys before
-// they score them (Geometry::new_keys).
-__device__ __forceinline__ void quantize_row(const Geometry& g, size_t row, int lane,
-                                             uint8_t* __restrict__ codes,
-                                             uint16_t* __restrict__ scales) {
-  const uint32_t x = reinterpret_cast<const uint32_t*>(g.k_pages + row * kHeadDim)[lane];
+// of every (sequence, KV head) (num_new <= 0: every position), 16 rows per
+// wave; the scoring kernels apply it to a decode step's new keys before they
+// score them (Geometry::new_keys).  x: the row's 32-bit word `lane`.
+__device__ __forceinline__ void quantize_value(uint32_t x, size_t row, int lane,
+                                               uint8_t* __restrict__ codes,
+                                               uint16_t* __restrict__ scales) {
   const float v0 = __uint_as_float(x << 16) + 0.0f;
   const float v1 = __uint_as_float(x & 0xFFFF0000u) + 0.0f;
   float mn = fminf(v0, v1), mx = fmaxf(v0, v1);
@@ -605,6 +612,14 @@ __device__ __forceinline__ void quantize_row(const Geometry& g, size_t row, int 
     reinterpret_cast<uint32_t*>(scales)[row * 4 + s4] = ab | (__float_as_uint(mn) & 0xFFFF0000u);
 }
 
+// The same for a row read here (lane l: dimensions 2l, 2l + 1).
+__device__ __forceinline__ void quantize_row(const Geometry& g, size_t row, int lane,
+                                             uint8_t* __restrict__ codes,
+                                             uint16_t* __restrict__ scales) {
+  quantize_value(reinterpret_cast<const uint32_t*>(g.k_pages + row * kHeadDim)[lane], row, lane,
+                 codes, scales);
+}
+
 // Positions [lo, hi) of sequence b, KV head kvh, one wave per position.  Every
 // wave of the workgroup calls it (the loop bound is uniform over a wave).
 __device__ __forceinline__ void quantize_positions(const Geometry& g, int b, int kvh, int lo,
@@ -613,6 +628,10 @@ __device__ __forceinline__ void quantize_positions(const Geometry& g, int b, int
     quantize_row(g, (size_t)row_id(g, b, kvh, pos), lane, g.k_codes, g.k_scales);
 }
 
+// A wave quantizes kQuantRows consecutive positions, all their key rows
+// loaded before the first is quantized (one row per wave and launch slot
+// would leave the prefill's million rows to wave launch rates).
+constexpr int kQuantRows = 16;
 __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
                                                        uint8_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales) {
@@ -621,9 +640,18 @@ __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, 
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int n = seq_len_of(g, b);
   const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
-  const int pos = first + c * 4 + wv;
-  if (pos >= n) return;  // uniform over the wave
-  quantize_row(g, (size_t)row_id(g, b, kvh, pos), lane, codes, scales);
+  const int pos0 = first + (c * 4 + wv) * kQuantRows;
+  if (pos0 >= n) return;  // uniform over the wave
+  size_t rows[kQuantRows];
+  uint32_t x[kQuantRows];
+#pragma unroll
+  for (int i = 0; i < kQuantRows; ++i) {
+    rows[i] = (size_t)row_id(g, b, kvh, min(pos0 + i, n - 1));
+    x[i] = reinterpret_cast<const uint32_t*>(g.k_pages + rows[i] * kHeadDim)[lane];
+  }
+#pragma unroll
+  for (int i = 0; i < kQuantRows; ++i)
+    if (pos0 + i < n) quantize_value(x[i], rows[i], lane, codes, scales);
 }
 
 // The group's query heads as MFMA A operands against INT2 keys.  A tile is 16
@@ -888,7 +916,7 @@ constexpr int kPairMax = 256;  // bucket entries ranked against each other direc
 
 struct SelectSmem {
   int32_t bt[kMaxPages];              // the sequence's block table row (physical pages)
-  uint32_t bitmap[kMaxSeqLen / 32];   // selection marks in list order
+  alignas(16) uint32_t bitmap[kMaxSeqLen / 32];  // selection marks in list order
   uint32_t hist[4096 + 1024 + 1024];  // bucket histogram / three radix levels
   uint32_t cbuf[2 * kCand];           // list keys / sample keys / candidate keys and indices
   int32_t apos[kMaxKappa];            // the emitted set, for the pool build
@@ -907,10 +935,15 @@ struct SelList {
   int32_t* o1;
   int32_t* o2;
   uint32_t* srow;
+  int32_t* ent;          // if set: the set's list indices only (rank order), nothing else
 };
 
-__device__ __forceinline__ void emit_at(const Geometry& g, const SelList& c, int pos, uint32_t row,
-                                        int o, SelectSmem& sm) {
+__device__ __forceinline__ void emit_at(const Geometry& g, const SelList& c, int e, int pos,
+                                        uint32_t row, int o, SelectSmem& sm) {
+  if (c.ent) {
+    c.ent[o] = e;
+    return;
+  }
   c.o1[o] = pos;
   if (c.o2) c.o2[o] = pos;
   c.srow[o] = row;
@@ -919,12 +952,20 @@ __device__ __forceinline__ void emit_at(const Geometry& g, const SelList& c, int
 
 __device__ __forceinline__ void emit_entry(const Geometry& g, const SelList& c, int e, int o,
                                            SelectSmem& sm) {
+  if (c.ent) {
+    c.ent[o] = e;
+    return;
+  }
   const int pos = c.plist ? c.plist[e] : e;
   const uint32_t row = c.prow ? c.prow[e] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
-  emit_at(g, c, pos, row, o, sm);
+  emit_at(g, c, e, pos, row, o, sm);
 }
 
 __device__ __forceinline__ void emit_empty(const SelList& c, int o, SelectSmem& sm) {
+  if (c.ent) {
+    c.ent[o] = -1;
+    return;
+  }
   c.o1[o] = -1;
   if (c.o2) c.o2[o] = -1;
   c.srow[o] = kNoRow;
@@ -1169,7 +1210,7 @@ __device__ __forceinline__ void load_run(const T* base, int e0, uint32_t (&v)[R]
 // (keys, and for a pool their positions and row ids, all loaded up front), so
 // counts scanned in thread order give ascending output positions directly.
 template <int R>
-__device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
+__device__ __forceinline__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm) {
   const int t = threadIdx.x;
   const int e0 = R * t;
   const int nv = clampi(c.n - e0, 0, R);  // valid entries of this thread
@@ -1191,7 +1232,7 @@ __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm
       if (o < c.K) {
         const int pos = c.plist ? (int)pl[i] : e0 + i;
         const uint32_t row = c.prow ? pr[i] : row_id_of_page(g, sm.bt[pos >> 6], c.kvh, pos);
-        emit_at(g, c, pos, row, o, sm);
+        emit_at(g, c, e0 + i, pos, row, o, sm);
       }
       ++o;
     }
@@ -1200,26 +1241,78 @@ __device__ void select_small(const Geometry& g, const SelList& c, SelectSmem& sm
 }
 
 // Emission of the entries marked in the LDS bitmap, in list order (ascending
-// positions): per-thread runs of words, counts scanned in thread order.
-__device__ void emit_bitmap(const Geometry& g, const SelList& c, SelectSmem& sm) {
-  const int t = threadIdx.x;
+// positions), in two steps.  Compaction into an LDS list in rank order
+// (sm.cbuf, free once the marks are final): wave v owns a contiguous range of
+// bitmap words, 64 per step, one word per lane; a wave scan of the words'
+// bit counts gives each word its first rank, and each lane writes its word's
+// marks one after another (a step costs its densest word's count, so runs of
+// dense words share steps and the cost stays near the number of marks).  Then
+// thread t emits ranks t, t + NT, ... from the list, so the outputs leave as
+// coalesced stores and the loads of a pool's positions and row ids (when not
+// deferred) are all in flight together.
+__device__ __forceinline__ void emit_bitmap(const Geometry& g, const SelList& c, SelectSmem& sm) {
+  static_assert(2 * kCand >= kMaxKappa, "the compacted set fits sm.cbuf");
+  constexpr int NW = NT / 64;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int words = (c.n + 31) >> 5;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  const int wpw = ((words + NW - 1) / NW + 63) & ~63;  // words per wave, whole steps
+  const int wlo = min(words, wave * wpw), whi = min(words, wlo + wpw);
   int cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
-  int total;
-  int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
-  for (int i = w0; i < w1; ++i) {
-    uint32_t m = sm.bitmap[i];
-    while (m) {
-      const int e = i * 32 + (__ffs(m) - 1);
+  for (int i = wlo + lane; i < whi; i += 64) cnt += __popc(sm.bitmap[i]);
+  cnt = (int)lane63((uint32_t)wave_incl_scan(cnt));
+  lds_barrier();  // earlier readers of sm.tmp are done
+  if (lane == 0) sm.tmp[wave] = cnt;
+  lds_barrier();
+  int o = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < NW; ++x) {
+    o += x < wave ? sm.tmp[x] : 0;
+    total += sm.tmp[x];
+  }
+  int32_t* const lst = reinterpret_cast<int32_t*>(sm.cbuf);
+  for (int base = wlo; base < whi && o < c.K; base += 64) {  // uniform over the wave
+    const int wi = base + lane;
+    uint32_t m = wi < whi ? sm.bitmap[wi] : 0u;
+    const int n1 = __popc(m);
+    const int inc = wave_incl_scan(n1);
+    int r = o + inc - n1;
+    o += (int)lane63((uint32_t)inc);
+    const int stop = min(c.K, r + n1);
+    for (; r < stop; ++r) {
+      lst[r] = wi * 32 + (__ffs(m) - 1);
       m &= m - 1u;
-      if (o < c.K) emit_entry(g, c, e, o, sm);
-      ++o;
     }
   }
-  for (int o2 = total + t; o2 < c.K; o2 += NT) emit_empty(c, o2, sm);
+  const int lim = min(total, c.K);
+  lds_barrier();
+  constexpr int PER = kMaxKappa / NT;
+  if (c.ent) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int r = t + k * NT;
+      if (r < c.K) c.ent[r] = r < lim ? lst[r] : -1;
+    }
+    return;
+  }
+  int pos[PER];
+  uint32_t row[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {  // every load first
+    const int r = t + k * NT;
+    const int e = r < lim ? lst[r] : 0;
+    pos[k] = c.plist ? c.plist[e] : e;
+    row[k] = c.prow ? c.prow[e] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int r = t + k * NT;
+    if (r < lim) {
+      const uint32_t rw = c.prow ? row[k] : row_id_of_page(g, sm.bt[pos[k] >> 6], c.kvh, pos[k]);
+      emit_at(g, c, lst[r], pos[k], rw, r, sm);
+    } else if (r < c.K) {
+      emit_empty(c, r, sm);
+    }
+  }
 }
 
 // Longer lists.  A strided sample of at most kSample keys brackets the K-th
@@ -1396,15 +1489,12 @@ __device__ __forceinline__ void select_large_marks(const SelList& c, Sm& sm) {
   lds_barrier();
 }
 
-// Leaves the problem's coarse histogram and candidate counters zero for the
-// next anchor layer (called by one workgroup once nothing reads them).
-__device__ void reset_selection_counters(const Workspace& ws, int p) {
+// Leaves the problem's coarse histogram zero for the next anchor layer (called
+// by one workgroup once nothing reads it).  The classify workgroups' candidate
+// counts need no reset: every pass writes each count it uses.
+__device__ __forceinline__ void reset_selection_counters(const Workspace& ws, int p) {
   uint32_t* gh = ws.ghist + (size_t)p * kCoarseBins;
   for (int i = threadIdx.x; i < kCoarseBins; i += blockDim.x) gh[i] = 0u;
-  if (threadIdx.x == 0) {
-    ws.cand_cnt[p] = 0u;
-    ws.cand_cnt2[p] = 0u;
-  }
 }
 
 // The second classification (the rank-expanded pool's, made in the same
@@ -1426,25 +1516,91 @@ __device__ __forceinline__ Workspace second_class(const Workspace& ws) {
 // else by a threshold search); if the bin held more than kMaxCand of them, an
 // exact radix over the whole list runs instead.
 template <typename Sm>
-__device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, const SelList& c,
+__device__ __forceinline__ void classified_marks(const Geometry& g, const Workspace& ws, int p, const SelList& c,
                                  Sm& sm) {
   const int t = threadIdx.x, lane = t & 63;
   const int n = c.n, K = c.K;
   const int words = (n + 31) >> 5;
   const uint32_t* gb = ws.gbits + (size_t)p * (g.n_cap >> 5);
   int marks = 0;
-  for (int i = t; i < words; i += NT) {
-    const uint32_t m = gb[i];
-    sm.bitmap[i] = m;
-    marks += __popc(m);
+  {
+    constexpr int PER = kMaxSeqLen / 32 / NT;  // all of a thread's words loaded at once
+    uint32_t m[PER];
+    const int last = (g.n_cap >> 5) - 1;  // inside the problem's row: loads need no branch
+#pragma unroll
+    for (int k = 0; k < PER; ++k) m[k] = gb[min(t + k * NT, last)];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) m[k] = t + k * NT < words ? m[k] : 0u;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      if (t + k * NT < words) sm.bitmap[t + k * NT] = m[k];
+      marks += __popc(m[k]);
+    }
   }
   block_excl_scan<NT>(marks, sm.tmp, &marks);
   const int above = ws.sel_meta[4 * p + 1];
   const int in_bin = ws.sel_meta[4 * p + 2];
-  const int ncand = (int)ws.cand_cnt[p];
   const int need = K - above;
   uint32_t* const ckey = sm.cbuf;
   int32_t* const cidx = reinterpret_cast<int32_t*>(sm.cbuf + kCand);
+  // the classify workgroups' candidate regions, gathered into LDS in region
+  // order: the counts (at most kClsSlots) are loaded at once and scanned by
+  // wave 0 into region starts (sm.ured, free here), then every thread copies
+  // up to kMaxCand / NT candidates, all loads issued before any store.  A
+  // region that overflowed makes the pass inconsistent (ncand = -1).
+  const int regions = (n + kClsEntries - 1) / kClsEntries;
+  const int W = cls_regions(g);
+  const uint32_t* gk = ws.cand_key + (size_t)p * W * kClsCap;
+  const int32_t* gi = ws.cand_idx + (size_t)p * W * kClsCap;
+  if (t < 64) {
+    // counts are read unsigned and clamped: a classification this call did not
+    // make (the rank pool's at rho = 1) leaves arbitrary workspace bytes, and
+    // the region starts must stay monotone and each within its region
+    const uint32_t cu = t < regions ? ws.cand_cnt[(size_t)p * W + t] : 0u;
+    const int c = (int)min(cu, (uint32_t)kClsCap + 1u);
+    const int cs = min(c, kClsCap);
+    const int inc = wave_incl_scan(cs);
+    if (t < regions) sm.ured[t] = (uint32_t)(inc - cs);
+    const bool ovf = __ballot(c > kClsCap) != 0ull;
+    if (t == 63) {
+      sm.res[0] = inc;
+      sm.res[1] = ovf ? 1 : 0;
+    }
+  }
+  lds_barrier();
+  const int stored = sm.res[0];
+  const int ncand = sm.res[1] ? -1 : stored;
+  {
+    constexpr int CU = kMaxCand / NT;
+    uint32_t kk[CU];
+    int32_t ii[CU];
+    int dst[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      const int i = t + NT * u;
+      dst[u] = -1;
+      if (i < min(stored, kMaxCand)) {
+        int lo = 0, hi = regions - 1;  // the last region starting at or before i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int)sm.ured[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t src = (size_t)lo * kClsCap + (size_t)(i - (int)sm.ured[lo]);
+        kk[u] = gk[src];
+        ii[u] = gi[src];
+        dst[u] = i;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < CU; ++u) {
+      if (dst[u] >= 0) {
+        ckey[dst[u]] = kk[u];
+        cidx[dst[u]] = ii[u];
+      }
+    }
+  }
+  lds_barrier();
   // the classify pass must agree with itself: as many marks as entries above the
   // threshold bin and as many candidates as entries in it (a histogram left
   // over from an earlier call, e.g. in a fresh workspace, fails this)
@@ -1452,13 +1608,6 @@ __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, 
     // few candidates (the usual case): each one's rank among them, four
     // threads per candidate: candidates with a larger key, or an equal key and
     // a lower list index, come first
-    const uint32_t* gk = ws.cand_key + (size_t)p * kMaxCand;
-    const int32_t* gi = ws.cand_idx + (size_t)p * kMaxCand;
-    if (t < ncand) {
-      ckey[t] = gk[t];
-      cidx[t] = gi[t];
-    }
-    lds_barrier();
     const int x = t >> 2, part = t & 3;
     uint32_t kx = 0u;
     int ix = 0, r = 0;
@@ -1481,15 +1630,11 @@ __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, 
     constexpr int RC = kMaxCand / NT;
     uint32_t ck[RC];
     int32_t ci[RC];
-    const uint32_t* gk = ws.cand_key + (size_t)p * kMaxCand;
-    const int32_t* gi = ws.cand_idx + (size_t)p * kMaxCand;
 #pragma unroll
     for (int u = 0; u < RC; ++u) {
       const int i = u * NT + t;
-      ck[u] = gk[i];
-      ci[u] = gi[i];
-      ckey[i] = ck[u];
-      cidx[i] = ci[u];
+      ck[u] = ckey[i];
+      ci[u] = cidx[i];
     }
     const int nvc = clampi((ncand - t + NT - 1) / NT, 0, RC);
     const Thresh th = find_threshold<RC>(ck, nvc, need, sm);  // its barriers order the LDS writes
@@ -1553,7 +1698,7 @@ __device__ void classified_marks(const Geometry& g, const Workspace& ws, int p, 
   lds_barrier();
 }
 
-__device__ void select_classified(const Geometry& g, const Workspace& ws, int p, const SelList& c,
+__device__ __forceinline__ void select_classified(const Geometry& g, const Workspace& ws, int p, const SelList& c,
                                   SelectSmem& sm) {
   classified_marks(g, ws, p, c, sm);
   emit_bitmap(g, c, sm);
@@ -1567,8 +1712,9 @@ __device__ void select_classified(const Geometry& g, const Workspace& ws, int p,
 // entries per round: a binary search over the offsets finds the run of the
 // first one, and positions and row ids leave as 32-byte stores.  sm.apos holds
 // the anchor set, sm.bt the sequence's block table.
-__device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L,
-                           SelectSmem& sm) {
+template <typename Sm>
+__device__ __forceinline__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kvh,
+                                           int L, Sm& sm, int slice = 0, int slices = 1) {
   const int K = g.kappa, t = threadIdx.x;
   const int win = min(g.window, L);
   int32_t* const off = reinterpret_cast<int32_t*>(sm.cbuf);  // [K] run offsets
@@ -1600,11 +1746,14 @@ __device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kv
     e += lens[i];
   }
   const int n = min(total, g.n_cap);
-  if (t == 0) ws.pool_len[p] = n;
+  if (t == 0 && slice == 0) ws.pool_len[p] = n;
   lds_barrier();
   int32_t* pp = ws.pool_pos + (size_t)p * g.n_cap;
   uint32_t* pr = ws.pool_row + (size_t)p * g.n_cap;
-  for (int o0 = 8 * t; o0 < n; o0 += 8 * NT) {
+  // this call's share of the entries: [s_lo, s_hi), ends at multiples of 8 (or n)
+  const int per8 = ((n + slices - 1) / slices + 7) & ~7;
+  const int s_lo = min(n, slice * per8), s_hi = min(n, s_lo + per8);
+  for (int o0 = s_lo + 8 * t; o0 < s_hi; o0 += 8 * NT) {
     int lo = 0, hi = K - 1;  // the last run k with off[k] <= o0 (it is not empty)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -1618,7 +1767,7 @@ __device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kv
     for (int i = 0; i < 8; ++i) {
       const int o = o0 + i;
       uint32_t ps = 0u, rw = 0u;
-      if (o < n) {
+      if (o < s_hi) {
         while (k + 1 < K && off[k + 1] <= o) run_of(++k, &st);
         ps = (uint32_t)(st + (o - off[k]));
         rw = row_id_of_page(g, sm.bt[ps >> 6], kvh, (int)ps);
@@ -1636,17 +1785,29 @@ __device__ void build_pool(const Geometry& g, const Workspace& ws, int p, int kv
 
 // Loads the block table row of sequence b (its first ceil(L/64) entries,
 // clamped to physical pages) into LDS.
-__device__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
+__device__ __forceinline__ void load_bt(const Geometry& g, int b, int L, int32_t* bt) {
+  constexpr int PER = kMaxPages / NT;  // every thread's loads go out before its stores
   const int np = (L + kPageSize - 1) / kPageSize;
-  for (int i = threadIdx.x; i < np; i += NT) bt[i] = phys_page(g, b, i);
+  int v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + k * NT;
+    v[k] = i < np ? phys_page(g, b, i) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + k * NT;
+    if (i < np) bt[i] = v[k];
+  }
 }
 
-// Top-kappa of one (sequence, KV head) per workgroup; at an anchor layer also
-// builds the pool.  Leaves the problem's selection counters at zero.
+// Top-kappa of one (sequence, KV head) per workgroup (an anchor layer's pool is
+// built by pool_build_kernel next).  Leaves the problem's coarse histogram at
+// zero.
 template <bool POOL>
 __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
                                                     int32_t* __restrict__ out,
-                                                    int32_t* __restrict__ out2) {
+                                                    int32_t* __restrict__ out2, int defer) {
   __shared__ SelectSmem sm;
   const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
@@ -1663,9 +1824,13 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
   c.K = K;
   c.b = b;
   c.kvh = kvh;
-  c.o1 = out + (size_t)p * K;
+  c.o1 = out ? out + (size_t)p * K : nullptr;
   c.o2 = out2 ? out2 + (size_t)p * K : nullptr;
   c.srow = ws.sel_row + (size_t)p * K;
+  // deferred (a pool, for attn_kernel's entry mode): only the set's pool
+  // indices leave this kernel; the attention's many workgroups look up the
+  // positions and row ids, instead of this one workgroup gathering them
+  c.ent = (POOL && defer) ? ws.sel_ent + (size_t)p * K : nullptr;
   if (c.n <= K) {
     for (int e = threadIdx.x; e < K; e += NT) {
       if (e < c.n) emit_entry(g, c, e, e, sm);
@@ -1678,24 +1843,45 @@ __global__ __launch_bounds__(NT) void select_kernel(Geometry g, Workspace ws,
   } else {  // after classify_kernel (with `pool` at a refined layer)
     select_classified(g, ws, p, c, sm);
   }
-  if (!POOL) {
-    lds_barrier();
-    build_pool(g, ws, p, kvh, L, sm);
-  }
   reset_selection_counters(ws, p);
 }
 
-// Pool of an anchor set given in device memory (one workgroup per problem).
+// Pool of an anchor set given in device memory: workgroup w of a problem
+// writes slice w of the pool's entries (every workgroup scans the same run
+// lengths).  One workgroup per problem would write the pool of a long context
+// (over 100K entries at 128K tokens with w = 64) alone.
+struct PoolSmem {
+  int32_t bt[kMaxPages];
+  int32_t apos[kMaxKappa];
+  uint32_t cbuf[kMaxKappa];  // run offsets
+  int tmp[NT / 64 + 1];
+};
+
 __global__ __launch_bounds__(NT) void pool_build_kernel(Geometry g, Workspace ws,
-                                                        const int32_t* __restrict__ anchor) {
-  __shared__ SelectSmem sm;
-  const int p = blockIdx.x, b = p / g.hkv, kvh = p - b * g.hkv;
+                                                        const int32_t* __restrict__ anchor,
+                                                        int slices) {
+  __shared__ PoolSmem sm;
+  const int p = blockIdx.x / slices, w = blockIdx.x - p * slices;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int L = seq_len_of(g, b);
   const int32_t* a = anchor + (size_t)p * g.kappa;
   load_bt(g, b, L, sm.bt);
-  for (int k = threadIdx.x; k < g.kappa; k += NT) sm.apos[k] = a[k];
+  {
+    constexpr int PER = kMaxKappa / NT;
+    int32_t v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * NT;
+      v[k] = i < g.kappa ? a[i] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = threadIdx.x + k * NT;
+      if (i < g.kappa) sm.apos[i] = v[k];
+    }
+  }
   lds_barrier();
-  build_pool(g, ws, p, kvh, L, sm);
+  build_pool(g, ws, p, kvh, L, sm, w, slices);
 }
 
 // One classification of workgroup w's list entries (raw, from base) for the
@@ -1751,7 +1937,10 @@ __device__ void classify_into(const Geometry& g, const Workspace& wv, int p, int
     wv.sel_meta[4 * p + 1] = res[1];
     wv.sel_meta[4 * p + 2] = res[2];
   }
-  if (bstar < 0) return;  // the histogram disagrees with the list: the selection falls back
+  if (bstar < 0) {  // the histogram disagrees with the list: the selection falls back
+    if (t == 0) wv.cand_cnt[(size_t)p * cls_regions(g) + w] = 0u;
+    return;
+  }
 
   uint32_t* gb = wv.gbits + (size_t)p * (g.n_cap >> 5);
   uint32_t cand = 0u;  // bit 4u + q4: entry in the threshold bin
@@ -1782,23 +1971,31 @@ __device__ void classify_into(const Geometry& g, const Workspace& wv, int p, int
       gb[first >> 5] = word;
     }
   }
+  // the bin's entries go to this workgroup's own candidate region, in thread
+  // order (no counter shared between workgroups); its count goes beside it
   const int cnt = __popc(cand);
   const int inc = wave_incl_scan(cnt);
-  const int wtot = (int)lane63((uint32_t)inc);
-  if (wtot) {
-    uint32_t off = 0u;
-    if (lane == 0) off = atomicAdd(&wv.cand_cnt[p], (uint32_t)wtot);
-    // unsigned: a counter left over in the workspace gives slots past the end
-    // (nothing is written; the selection's consistency check rejects the pass)
-    uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)off) + (uint32_t)(inc - cnt);
-    uint32_t* ck = wv.cand_key + (size_t)p * kMaxCand;
-    int32_t* ci = wv.cand_idx + (size_t)p * kMaxCand;
+  if (lane == 63) tmp[wave] = inc;
+  lds_barrier();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int x = 0; x < kClsThreads / 64; ++x) {
+    const int c = tmp[x];
+    before += x < wave ? c : 0;
+    total += c;
+  }
+  const int W = cls_regions(g);
+  if (t == 0) wv.cand_cnt[(size_t)p * W + w] = (uint32_t)total;
+  if (cnt) {
+    int slot = before + inc - cnt;
+    uint32_t* ck = wv.cand_key + ((size_t)p * W + w) * kClsCap;
+    int32_t* ci = wv.cand_idx + ((size_t)p * W + w) * kClsCap;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         if (cand & (1u << (4 * u + q4))) {
-          if (slot < (uint32_t)kMaxCand) {
+          if (slot < kClsCap) {
             ck[slot] = order_key(__uint_as_float(raw[u][q4]));
             ci[slot] = base + u * 4 * kClsThreads + 4 * t + q4;
           }
@@ -1876,7 +2073,7 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-static_assert(kAttnSplit == 64 && kAttnThreads == 256, "one 16-token tile per wave");
+static_assert(kAttnSplit == 64 && kAttnThreads == 256, "the smallest split: one 16-token tile per wave");
 constexpr int kMergeBatch = 32;  // splits whose partials one merge round loads at once
 constexpr int kMaxSplits = kMaxKappa / kAttnSplit;  // splits of the smallest split size
 constexpr int kDenseMinChunk = 1024;  // dense decode: tokens per workgroup (more above 128K)
@@ -1984,7 +2181,7 @@ __device__ __forceinline__ void attend_tile(const KvTile& t, const u32x4 (&qf)[4
 // unnormalised output [G][128] and (max, sum) [G][2] of split s of problem p,
 // stored to the workspace for merge_kernel.
 template <int G, int NW, int T>
-__device__ void store_split(const Workspace& ws, int p, int s, int splits,
+__device__ __forceinline__ void store_split(const Workspace& ws, int p, int s, int splits,
                             float (*wo)[G][kHeadDim], float (*wml)[G][2]) {
   float* po = ws.part_o + ((size_t)p * splits + s) * G * kHeadDim;
   float* pm = ws.part_ml + ((size_t)p * splits + s) * G * 2;
@@ -2073,18 +2270,27 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geometry g, Workspace w
 }
 
 // SparseAttn over a given set (positions in idx) or over the row ids the
-// latest selection left in the workspace (ROWS): kAttnSplit tokens per
-// workgroup, 16 per wave.
-template <int G, bool ROWS>
+// latest selection left in the workspace (ROWS): workgroup s of a problem
+// takes set entries [s * 64 T, (s + 1) * 64 T), each wave T consecutive
+// 16-token tiles with the next tile's K and V in flight while the current one
+// is combined (running softmax statistics per head, rescaled to the running
+// maximum as in dense decode), and the workgroup stores one split.  T grows
+// with the set (fewer, larger splits: less partial traffic for the merge)
+// while the grid still fills the device.
+constexpr int kSetPositions = 0;  // attn_kernel's set: positions in idx
+constexpr int kSetRows = 1;       // row ids the latest selection left (Workspace::sel_row)
+constexpr int kSetEntries = 2;    // pool indices of a deferred selection (Workspace::sel_ent)
+
+template <int G, int MODE, int T>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspace ws,
                                                             const uint16_t* __restrict__ q,
                                                             const int32_t* __restrict__ idx,
-                                                            float scale) {
+                                                            int32_t* __restrict__ pos_out,
+                                                            float scale, int splits) {
   constexpr int NW = kAttnThreads / 64;
   __shared__ float wo[NW][G][kHeadDim];
   __shared__ float wml[NW][G][2];
   __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
-  const int splits = g.splits;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (blockIdx.x >= (unsigned)(g.problems() * splits)) {  // uniform over the workgroup
     // one workgroup per problem past the attention's grid (a shared layer's
@@ -2098,36 +2304,91 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int j = lane & 15, g4 = lane >> 4;
-
-  const int ti = s * kAttnSplit + wave * 16 + j;
-  bool valid;
-  uint32_t row;
-  if (ROWS) {
-    row = ti < g.kappa ? ws.sel_row[(size_t)p * g.kappa + ti] : kNoRow;
-    const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
-    valid = row <= max_row;
-    if (!valid) row = 0u;
-  } else {
-    const int L = seq_len_of(g, b);
-    const int pos = ti < g.kappa ? idx[(size_t)p * g.kappa + ti] : -1;
-    valid = pos >= 0 && pos < L;
-    row = row_id(g, b, kvh, valid ? pos : 0);
+  const int j = lane & 15;
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  const int L = seq_len_of(g, b);
+  const int first = s * (64 * T) + wave * (16 * T);  // this wave's first set entry
+  uint32_t row[T];
+  bool valid[T];
+#pragma unroll
+  for (int k = 0; k < T; ++k) {
+    const int ti = first + 16 * k + j;
+    if (MODE == kSetRows) {
+      uint32_t r = ti < g.kappa ? ws.sel_row[(size_t)p * g.kappa + ti] : kNoRow;
+      valid[k] = r <= max_row;
+      row[k] = valid[k] ? r : 0u;
+    } else if (MODE == kSetEntries) {
+      // pool index -> row id and position; the set's positions go to pos_out
+      const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+      const int e = ti < g.kappa ? ws.sel_ent[(size_t)p * g.kappa + ti] : -1;
+      const bool ok = e >= 0 && e < n;
+      const size_t pe = (size_t)p * g.n_cap + (ok ? e : 0);
+      const uint32_t r = ws.pool_row[pe];
+      valid[k] = ok && r <= max_row;
+      row[k] = valid[k] ? r : 0u;
+      if (pos_out && lane < 16 && ti < g.kappa)
+        pos_out[(size_t)p * g.kappa + ti] = valid[k] ? ws.pool_pos[pe] : -1;
+    } else {
+      const int pos = ti < g.kappa ? idx[(size_t)p * g.kappa + ti] : -1;
+      valid[k] = pos >= 0 && pos < L;
+      row[k] = row_id(g, b, kvh, valid[k] ? pos : 0);
+    }
   }
-  float m[4], l[4], o0[G], o1[G];
-  wave_attend<G>(g, q, b, kvh, row, valid, scale, pw[wave], m, l, o0, o1);
+  float Mr[G], Lr[G], O0[G], O1[G];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    wo[wave][i][2 * lane] = o0[i];
-    wo[wave][i][2 * lane + 1] = o1[i];
+    Mr[i] = -INFINITY;
+    Lr[i] = 0.f;
+    O0[i] = O1[i] = 0.f;
   }
-  if (j == 0) {
+  const int ntiles = clampi((g.kappa - first + 15) / 16, 0, T);  // uniform over the wave
+  if (ntiles > 0) {
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    auto step = [&](const KvTile& kt, int k) {
+      float m[4], l[4], o0[G], o1[G];
+      attend_tile<G>(kt, qf, valid[k], scale, pw[wave], m, l, o0, o1);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * g4 + r < G) {
-        wml[wave][4 * g4 + r][0] = m[r];
-        wml[wave][4 * g4 + r][1] = l[r];
+      for (int i = 0; i < G; ++i) {
+        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[i & 3]), 16 * (i >> 2)));
+        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i & 3]), 16 * (i >> 2)));
+        const float Mn = fmaxf(Mr[i], mh);
+        const float fa = (Mr[i] == -INFINITY) ? 0.f : __expf(Mr[i] - Mn);
+        const float fb = (mh == -INFINITY) ? 0.f : __expf(mh - Mn);
+        Lr[i] = Lr[i] * fa + lh * fb;
+        O0[i] = O0[i] * fa + o0[i] * fb;
+        O1[i] = O1[i] * fa + o1[i] * fb;
+        Mr[i] = Mn;
       }
+    };
+    KvTile t0, t1;
+    load_kv_tile(g, row[0], lane, t0);
+#pragma unroll
+    for (int k = 0; k < T; k += 2) {
+      if (k < ntiles) {
+        if (k + 1 < ntiles) load_kv_tile(g, row[k + 1], lane, t1);
+        __builtin_amdgcn_sched_barrier(0);
+        step(t0, k);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < ntiles) {
+          if (k + 2 < ntiles) load_kv_tile(g, row[k + 2], lane, t0);
+          __builtin_amdgcn_sched_barrier(0);
+          step(t1, k + 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    wo[wave][i][2 * lane] = O0[i];
+    wo[wave][i][2 * lane + 1] = O1[i];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      wml[wave][i][0] = Mr[i];
+      wml[wave][i][1] = Lr[i];
     }
   }
   lds_barrier();
@@ -2286,7 +2547,7 @@ __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p,
 // list order, so ranks are ascending positions): their row ids go to sm.srow
 // and their positions to layer_idx.  Returns the number of marked entries.
 template <typename Sm>
-__device__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_idx, Sm& sm) {
+__device__ __forceinline__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_idx, Sm& sm) {
   const int t = threadIdx.x, K = c.K;
   const int words = (c.n + 31) >> 5;
   const int wpt = (words + NT - 1) / NT;
@@ -2338,6 +2599,7 @@ __device__ __attribute__((noinline)) int long_pool_slice(const float* sc, const 
   c.kvh = 0;
   c.o1 = c.o2 = nullptr;
   c.srow = nullptr;
+  c.ent = nullptr;
   if (n <= kRegMarks) {
     constexpr int R = kRegMarks / NT;
     static_assert(R == 32, "one bitmap word per thread");
@@ -2438,7 +2700,7 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 // work whatever the clustering of the marks (a thread owning full mark words
 // would otherwise emit 128 entries while most emit none).  Contains barriers.
 template <bool kStage, typename Sm>
-__device__ bool emit_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L, Sm& sm,
+__device__ __forceinline__ bool emit_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int L, Sm& sm,
                           int* pool_n_out) {
   const int t = threadIdx.x;
   const size_t base = (size_t)p * g.n_cap;
@@ -2526,7 +2788,7 @@ struct AnchorSmem {
 
 // Marks of a list of at most kSmall entries from the keys in registers.
 template <int R, typename Sm>
-__device__ void small_marks(const float* sc, int n, int K, Sm& sm) {
+__device__ __forceinline__ void small_marks(const float* sc, int n, int K, Sm& sm) {
   const int t = threadIdx.x;
   const int words = (n + 31) >> 5;
   for (int i = t; i < words; i += NT) sm.bitmap[i] = 0u;
@@ -2572,6 +2834,7 @@ __device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Worksp
     c.kvh = kvhe;
     c.o1 = c.o2 = nullptr;
     c.srow = nullptr;
+    c.ent = nullptr;
     classified_marks(g, second_class(ws), pe, c, sm);
   }
   int pool_n;
@@ -2624,6 +2887,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
     c.kvh = kvh;
     c.o1 = c.o2 = nullptr;
     c.srow = nullptr;
+    c.ent = nullptr;
     classified_marks(g, ws, p, c, sm);
   }
 
@@ -2785,7 +3049,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
 // attention).  Leaves the selection counters at zero.
 // ---------------------------------------------------------------------------
 template <int R>
-__device__ void select_in_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int m,
+__device__ __forceinline__ void select_in_pool(const Geometry& g, const Workspace& ws, int p, int kvh, int m,
                                int32_t* out, int32_t* out2, SelectSmem& sm, bool pos_in_lds) {
   const int t = threadIdx.x, K = g.kappa;
   const size_t base = (size_t)p * g.n_cap;
@@ -2849,6 +3113,7 @@ __global__ __launch_bounds__(NT) void rank_pool_kernel(Geometry g, Workspace ws,
   c.kvh = kvh;
   c.o1 = c.o2 = nullptr;
   c.srow = nullptr;
+  c.ent = nullptr;
   if (m >= L) {
     for (int i = t; i < ((L + 31) >> 5); i += NT)
       sm.bitmap[i] = (32 * i + 32 <= L) ? 0xFFFFFFFFu : ((1u << (L & 31)) - 1u);
@@ -2925,9 +3190,21 @@ void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t
     launch(kAnchorScore, score_anchor_int2_kernel<G>, dim3(g.problems() * wgs),
            dim3(kScoreThreads), s, g, w, q, wgs);
   } else {
-    const int wgs = (g.n_cap + kAnchorEntries - 1) / kAnchorEntries;
-    launch(kAnchorScore, score_anchor_kernel<G>, dim3(g.problems() * wgs), dim3(kScoreThreads), s,
-           g, w, q, wgs);
+    // pages per wave: the largest of 4, 2, 1 that still gives every compute
+    // unit four workgroups
+    const long long four_per_cu = 4LL * std::max(device_cus(), 1);
+    int pages = 4;
+    while (pages > 1 && (long long)g.problems() * ((g.n_cap + 256 * pages - 1) / (256 * pages)) <
+                            four_per_cu)
+      pages >>= 1;
+    const int wgs = (g.n_cap + 256 * pages - 1) / (256 * pages);
+    const dim3 grid(g.problems() * wgs), block(kScoreThreads);
+    if (pages == 4)
+      launch(kAnchorScore, score_anchor_kernel<G, 4>, grid, block, s, g, w, q, wgs);
+    else if (pages == 2)
+      launch(kAnchorScore, score_anchor_kernel<G, 2>, grid, block, s, g, w, q, wgs);
+    else
+      launch(kAnchorScore, score_anchor_kernel<G, 1>, grid, block, s, g, w, q, wgs);
   }
 }
 
@@ -2960,14 +3237,15 @@ void launch_merge_g(const Geometry& g, const Workspace& w, int splits, float* ou
          reset ? 1 : 0);
 }
 
-template <int G, bool ROWS>
+template <int G, int MODE>
 void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q,
-                        const int32_t* idx, float scale, float* out, bool quantize_new,
-                        hipStream_t s) {
+                        const int32_t* idx, int32_t* pos_out, float scale, float* out,
+                        bool quantize_new, hipStream_t s) {
   const int extra = quantize_new && g.k_codes && g.new_keys > 0 ? g.problems() : 0;
-  launch(kAttention, attn_kernel<G, ROWS>, dim3(g.problems() * g.splits + extra),
-         dim3(kAttnThreads), s, g, w, q, idx, scale);
-  launch_merge_g<G>(g, w, g.splits, out, false, s);
+  const int splits = (g.kappa + kAttnSplit - 1) / kAttnSplit;
+  launch(kAttention, attn_kernel<G, MODE, 1>, dim3(g.problems() * splits + extra),
+         dim3(kAttnThreads), s, g, w, q, idx, pos_out, scale, splits);
+  launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
 #define PRISM_BY_GROUP(FN, ...)                      \
@@ -3005,10 +3283,13 @@ int64_t profile_launches(int kind) {
 size_t workspace_bytes(const Geometry& g) {
   const size_t P = (size_t)g.problems();
   size_t o = 0;
-  o += align256(P * (kCoarseBins + 2) * 4);                      // ghist, cand_cnt, cand_cnt2
+  const size_t W = (size_t)cls_regions(g);
+  o += align256(P * kCoarseBins * 4);                            // ghist
+  o += align256(P * W * 4);                                      // cand_cnt
+  o += align256(P * W * 4);                                      // cand_cnt2
   o += align256(P * 4 * 4);                                      // sel_meta
-  o += align256(P * (size_t)kMaxCand * 4);                       // cand_key
-  o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx
+  o += align256(P * W * kClsCap * 4);                            // cand_key
+  o += align256(P * W * kClsCap * 4);                            // cand_idx
   o += align256(P * (size_t)(g.n_cap / 32) * 4);                 // gbits
   o += align256(P * (size_t)g.n_cap * 4);                        // scores
   o += align256(P * (size_t)g.n_cap * 4);                        // pool_pos
@@ -3016,13 +3297,14 @@ size_t workspace_bytes(const Geometry& g) {
   o += align256(P * 4);                                          // pool_len
   o += align256(P * (size_t)g.kappa * 4);                        // sel_row
   o += align256(P * (size_t)g.kappa * 4);                        // idx_tmp
+  o += align256(P * (size_t)g.kappa * 4);                        // sel_ent
   o += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);  // part_o
   o += align256(P * (size_t)g.splits * g.group * 2 * 4);         // part_ml
   o += align256(P * (size_t)dense_splits(g) * g.group * kHeadDim * 4);  // dense_o
   o += align256(P * (size_t)dense_splits(g) * g.group * 2 * 4);         // dense_ml
   o += align256(P * 4 * 4);                                      // sel_meta2
-  o += align256(P * (size_t)kMaxCand * 4);                       // cand_key2
-  o += align256(P * (size_t)kMaxCand * 4);                       // cand_idx2
+  o += align256(P * W * kClsCap * 4);                            // cand_key2
+  o += align256(P * W * kClsCap * 4);                            // cand_idx2
   o += align256(P * (size_t)(g.n_cap / 32) * 4);                 // gbits2
   return o;
 }
@@ -3031,16 +3313,19 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   const size_t P = (size_t)g.problems();
   char* c = static_cast<char*>(base);
   Workspace w;
+  const size_t W = (size_t)cls_regions(g);
   w.ghist = reinterpret_cast<uint32_t*>(c);
-  w.cand_cnt = w.ghist + P * kCoarseBins;
-  w.cand_cnt2 = w.cand_cnt + P;
-  c += align256(P * (kCoarseBins + 2) * 4);
+  c += align256(P * kCoarseBins * 4);
+  w.cand_cnt = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * W * 4);
+  w.cand_cnt2 = reinterpret_cast<uint32_t*>(c);
+  c += align256(P * W * 4);
   w.sel_meta = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4 * 4);
   w.cand_key = reinterpret_cast<uint32_t*>(c);
-  c += align256(P * (size_t)kMaxCand * 4);
+  c += align256(P * W * kClsCap * 4);
   w.cand_idx = reinterpret_cast<int32_t*>(c);
-  c += align256(P * (size_t)kMaxCand * 4);
+  c += align256(P * W * kClsCap * 4);
   w.gbits = reinterpret_cast<uint32_t*>(c);
   c += align256(P * (size_t)(g.n_cap / 32) * 4);
   w.scores = reinterpret_cast<float*>(c);
@@ -3055,6 +3340,8 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   c += align256(P * (size_t)g.kappa * 4);
   w.idx_tmp = reinterpret_cast<int32_t*>(c);
   c += align256(P * (size_t)g.kappa * 4);
+  w.sel_ent = reinterpret_cast<int32_t*>(c);
+  c += align256(P * (size_t)g.kappa * 4);
   w.part_o = reinterpret_cast<float*>(c);
   c += align256(P * (size_t)g.splits * g.group * kHeadDim * 4);
   w.part_ml = reinterpret_cast<float*>(c);
@@ -3066,9 +3353,9 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   w.sel_meta2 = reinterpret_cast<int32_t*>(c);
   c += align256(P * 4 * 4);
   w.cand_key2 = reinterpret_cast<uint32_t*>(c);
-  c += align256(P * (size_t)kMaxCand * 4);
+  c += align256(P * W * kClsCap * 4);
   w.cand_idx2 = reinterpret_cast<int32_t*>(c);
-  c += align256(P * (size_t)kMaxCand * 4);
+  c += align256(P * W * kClsCap * 4);
   w.gbits2 = reinterpret_cast<uint32_t*>(c);
   return w;
 }
@@ -3078,7 +3365,7 @@ Workspace carve_workspace(void* base, const Geometry& g) {
 // over many workgroups, then select per problem (and build the pool).
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 2);
+  const int nz = g.problems() * kCoarseBins;
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -3093,13 +3380,15 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2);
-  return hipGetLastError();
+  launch(kSelect, select_kernel<false>, dim3(g.problems()), dim3(NT), s, g, w, out, out2, 0);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_pool_build(g, w, out, s);  // the pool of the set just written to out
 }
 
 hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
                               int32_t* out, int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * (kCoarseBins + 2);
+  const int nz = g.problems() * kCoarseBins;
   hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
                      w.ghist, nz);
   hipError_t e = hipGetLastError();
@@ -3206,7 +3495,9 @@ hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, cons
 
 hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_t* anchor_idx,
                              hipStream_t s) {
-  launch(kPoolBuild, pool_build_kernel, dim3(g.problems()), dim3(NT), s, g, w, anchor_idx);
+  const int slices = std::max(1, (pool_cap(g) + 8 * NT - 1) / (8 * NT));  // 8 entries per thread
+  launch(kPoolBuild, pool_build_kernel, dim3(g.problems() * slices), dim3(NT), s, g, w,
+         anchor_idx, slices);
   return hipGetLastError();
 }
 
@@ -3215,7 +3506,7 @@ hipError_t launch_pool_build(const Geometry& g, const Workspace& w, const int32_
 // select per problem.  The pool's length is known on the device only; its
 // bound decides whether classification can be needed, and sizes the grids.
 hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
-                         hipStream_t s) {
+                         hipStream_t s, bool defer) {
   const int bound = pool_cap(g);
   const bool classify = bound > kSmall && bound > g.kappa;
   PRISM_BY_GROUP(launch_pool_score_g, g, w, q, classify, s);
@@ -3229,7 +3520,7 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
     if (e != hipSuccess) return e;
   }
   launch(kSelect, select_kernel<true>, dim3(g.problems()), dim3(NT), s, g, w, out,
-         static_cast<int32_t*>(nullptr));
+         static_cast<int32_t*>(nullptr), defer ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -3244,10 +3535,10 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
 
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s) {
-  if (!fused_fits(g)) {  // select once per problem, then attend
-    hipError_t e = launch_refine(g, w, q, layer_idx ? layer_idx : w.idx_tmp, s);
+  if (!fused_fits(g)) {  // select once per problem (pool indices only), then attend
+    hipError_t e = launch_refine(g, w, q, nullptr, s, true);
     if (e != hipSuccess) return e;
-    return launch_attention(g, w, q, nullptr, true, scale, out, s);
+    return launch_attention_entries(g, w, q, layer_idx, scale, out, s);
   }
   PRISM_BY_GROUP(launch_pool_score_g, g, w, q, false, s);
   hipError_t e = hipGetLastError();
@@ -3288,7 +3579,7 @@ hipError_t launch_dense(const Geometry& g, const Workspace& w, const uint16_t* q
 hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint16_t* scales,
                            hipStream_t s) {
   const int range = (num_new > 0 && num_new < g.max_seq_len) ? num_new : g.max_seq_len;
-  const int chunks = (range + 3) / 4;  // four token rows per workgroup
+  const int chunks = (range + 4 * kQuantRows - 1) / (4 * kQuantRows);  // four waves per workgroup
   launch(kQuantize, quantize_kernel, dim3(g.problems() * chunks), dim3(256), s, g, num_new, chunks,
          codes, scales);
   return hipGetLastError();
@@ -3297,24 +3588,33 @@ hipError_t launch_quantize(const Geometry& g, int num_new, uint8_t* codes, uint1
 hipError_t launch_attention(const Geometry& g, const Workspace& w, const uint16_t* q,
                             const int32_t* idx, bool use_sel_rows, float scale, float* out,
                             hipStream_t s, bool quantize_new) {
+#define PRISM_ATTN(MODE)                                                                    \
+  switch (g.group) {                                                                        \
+    case 1: launch_attention_g<1, MODE>(g, w, q, idx, nullptr, scale, out, quantize_new, s); break; \
+    case 2: launch_attention_g<2, MODE>(g, w, q, idx, nullptr, scale, out, quantize_new, s); break; \
+    case 4: launch_attention_g<4, MODE>(g, w, q, idx, nullptr, scale, out, quantize_new, s); break; \
+    case 8: launch_attention_g<8, MODE>(g, w, q, idx, nullptr, scale, out, quantize_new, s); break; \
+    case 16: launch_attention_g<16, MODE>(g, w, q, idx, nullptr, scale, out, quantize_new, s); break; \
+    default: return hipErrorInvalidValue;                                                    \
+  }
   if (use_sel_rows) {
-    switch (g.group) {
-      case 1: launch_attention_g<1, true>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 2: launch_attention_g<2, true>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 4: launch_attention_g<4, true>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 8: launch_attention_g<8, true>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 16: launch_attention_g<16, true>(g, w, q, idx, scale, out, quantize_new, s); break;
-      default: return hipErrorInvalidValue;
-    }
+    PRISM_ATTN(kSetRows)
   } else {
-    switch (g.group) {
-      case 1: launch_attention_g<1, false>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 2: launch_attention_g<2, false>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 4: launch_attention_g<4, false>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 8: launch_attention_g<8, false>(g, w, q, idx, scale, out, quantize_new, s); break;
-      case 16: launch_attention_g<16, false>(g, w, q, idx, scale, out, quantize_new, s); break;
-      default: return hipErrorInvalidValue;
-    }
+    PRISM_ATTN(kSetPositions)
+  }
+#undef PRISM_ATTN
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_entries(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                    int32_t* pos_out, float scale, float* out, hipStream_t s) {
+  switch (g.group) {
+    case 1: launch_attention_g<1, kSetEntries>(g, w, q, nullptr, pos_out, scale, out, false, s); break;
+    case 2: launch_attention_g<2, kSetEntries>(g, w, q, nullptr, pos_out, scale, out, false, s); break;
+    case 4: launch_attention_g<4, kSetEntries>(g, w, q, nullptr, pos_out, scale, out, false, s); break;
+    case 8: launch_attention_g<8, kSetEntries>(g, w, q, nullptr, pos_out, scale, out, false, s); break;
+    case 16: launch_attention_g<16, kSetEntries>(g, w, q, nullptr, pos_out, scale, out, false, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
