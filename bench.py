@@ -140,10 +140,122 @@ def traffic_for(kernel, workload):
         return None
     if t.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    e = t.get("kernels", {}).get(kernel)
-    if not e or e.get("workload") != workload:
-        return None
-    return e.get("hbm_bytes_per_launch")
+    e = t.get("kernels", {}).get(kernel, {}).get(workload)
+    return e.get("hbm_bytes_per_launch") if e else None
+
+
+# library kernel (name up to its template arguments) -> benchmark kind
+KERNEL_KINDS = {
+    "score_anchor_kernel": "anchor_score", "score_anchor_int2_kernel": "anchor_score",
+    "score_pool_kernel": "refine_score", "score_pool_int2_kernel": "refine_score",
+    "anchor_attn_kernel": "attention", "refine_attn_kernel": "attention",
+    "attn_kernel": "attention", "select_kernel": "select", "rank_pool_kernel": "select",
+    "classify_kernel": "classify", "merge_kernel": "merge", "pool_build_kernel": "pool_build",
+    "quantize_kernel": "quantize", "dense_attn_kernel": "dense",
+    "zero_counters_kernel": "counter reset",
+}
+
+
+def _short_kernel(name):
+    k = name.replace("void ", "").replace("prism::(anonymous namespace)::", "")
+    return k.split("(")[0].strip()
+
+
+def _counter_per_dispatch(path, counter):
+    """{dispatch id: (kernel name, value)} of one counter from a rocprofv3 --pmc
+    counter_collection.csv (values of one dispatch summed)."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            name, v = out.get(d, (r["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def counter_summary(args):
+    """HBM traffic per kernel from two rocprofv3 --pmc runs of this script
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch) and the same two counters
+    over --copy-probe, whose known size gives the scale of each counter.
+    Prints a markdown table; with --bench-json (the JSON line of a run with the
+    same workload options) also the ratio to the algorithmic bytes, and records
+    the per-launch HBM bytes of the scored kinds in the committed counter file
+    for this workload and kernel source."""
+    import numpy as np
+    fetch_csv, write_csv, copy_fetch_csv, copy_write_csv = args.counter_summary
+    copy_bytes = args.copy_probe_mib << 20
+
+    def factor(path, counter):
+        vals = [v for _, v in _counter_per_dispatch(path, counter).values()]
+        big = [v for v in vals if v * 1024 > copy_bytes / 4]   # the copy dispatches
+        if not big:
+            sys.exit(f"{path}: no dispatch of the {args.copy_probe_mib} MiB copy")
+        return copy_bytes / (float(np.mean(big)) * 1024), float(np.mean(big))
+
+    ff, fk = factor(copy_fetch_csv, "FETCH_SIZE")
+    wf, wk = factor(copy_write_csv, "WRITE_SIZE")
+    fetch = _counter_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_csv, "WRITE_SIZE")
+    per = {}
+    for src, idx in ((fetch, 0), (write, 1)):
+        for name, v in src.values():
+            if "prism::" not in name:
+                continue
+            per.setdefault(_short_kernel(name), ([], []))[idx].append(v)
+    algo = {}
+    if args.bench_json:
+        with open(args.bench_json) as f:
+            line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
+        for kind, k in json.loads(line)["kernels"].items():
+            if k.get("algorithmic_bytes_per_launch"):
+                algo[kind] = k["algorithmic_bytes_per_launch"]
+    print(f"Calibration: the {args.copy_probe_mib} MiB device copy reads and writes "
+          f"{copy_bytes >> 10} KiB per dispatch; the counters read FETCH_SIZE {fk:.1f} KiB and "
+          f"WRITE_SIZE {wk:.1f} KiB, so fetched bytes are scaled by {ff:.4f} and written bytes "
+          f"by {wf:.4f}.\n")
+    print("| kernel | kind | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) "
+          "| algorithmic bytes | ratio |")
+    print("|---|---|---|---|---|---|---|---|")
+    by_kind = {}
+    rows = []
+    for k, (fv, wv) in per.items():
+        if not fv or not wv:
+            continue
+        kind = KERNEL_KINDS.get(k.split("<")[0], "other")
+        hbm = float(np.mean(fv)) * 1024 * ff + float(np.mean(wv)) * 1024 * wf
+        rows.append((hbm * len(fv), k, kind, len(fv), float(np.mean(fv)), float(np.mean(wv)), hbm))
+        agg = by_kind.setdefault(kind, [0.0, 0.0, 0.0, 0])
+        agg[0] += float(np.sum(fv))
+        agg[1] += float(np.sum(wv))
+        agg[2] += hbm * len(fv)
+        agg[3] += len(fv)
+    for _, k, kind, n, fkib, wkib, hbm in sorted(rows, reverse=True):
+        a = algo.get(kind)
+        print(f"| `{k}` | {kind} | {n} | {fkib:.1f} | {wkib:.1f} | {hbm:.4g} | "
+              f"{f'{a:.4g}' if a else '-'} | {f'{hbm / a:.3f}' if a else '-'} |")
+    if not args.bench_json:
+        return
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        t = {}
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        t = {"kernel_source_sha256": kernel_source_hash(), "kernels": {}}
+    for kind in algo:
+        if kind not in by_kind:
+            continue
+        fsum, wsum, hsum, n = by_kind[kind]
+        t["kernels"].setdefault(kind, {})[args.workload] = {
+            "fetch_kib": round(fsum / n, 1), "write_kib": round(wsum / n, 1),
+            "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
+            "hbm_bytes_per_launch": int(round(hsum / n)), "dispatches_averaged": n}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+        f.write("\n")
 
 
 def sample_layers(wl, roles):
@@ -231,13 +343,16 @@ def trace_summary(args):
     roles = layer_roles(wl, args.pattern)
     per_step = launches_per_step(wl, args.cus, args.pool_rho, roles, args.dense)
     n = sum(per_step.values())
+    def name(r):
+        return _short_kernel(r["Kernel_Name"])
+
+    # the counter reset before a per-problem anchor selection is launched
+    # outside the library's per-kind profiling: reported apart, not counted
     with open(args.trace_summary) as f:
         rows = [r for r in csv.DictReader(f) if "prism::" in r["Kernel_Name"]]
+    resets = [r for r in rows if name(r) == "zero_counters_kernel"]
+    rows = [r for r in rows if name(r) != "zero_counters_kernel"]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
-
-    def name(r):
-        k = r["Kernel_Name"].replace("void ", "").replace("prism::(anonymous namespace)::", "")
-        return k.split("(")[0]
 
     W, K = args.warmup, args.steps
     g0 = (W + max(1, W)) * n
@@ -266,6 +381,10 @@ def trace_summary(args):
               f"{np.mean(ed):.2f} | {np.median(ed):.2f} | |")
     print(f"| step (first start to last end) | | | | | | {np.mean(spans):.4f} mean, "
           f"{np.median(spans):.4f} median |")
+    if resets:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in resets]
+        print(f"\n`zero_counters_kernel` (the counter reset before a per-problem anchor "
+              f"selection): {len(d)} dispatches in the trace, {np.mean(d):.2f} us average")
 
 
 def main():
@@ -307,10 +426,23 @@ def main():
                     help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
                          "of this script with the same workload options, --steps and --warmup, and "
                          "print per-kernel durations in its graph-replayed and eager regions")
+    ap.add_argument("--counter-summary", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="no GPU work: HBM traffic per kernel from the counter_collection.csv of "
+                         "rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE runs of this script and "
+                         "of --copy-probe (size --copy-probe-mib)")
+    ap.add_argument("--copy-probe-mib", type=int, default=1024, metavar="MIB",
+                    help="size of the --copy-probe run the counter summary calibrates against")
+    ap.add_argument("--bench-json", default="", metavar="FILE",
+                    help="with --counter-summary: output of a run with the same options, for the "
+                         "algorithmic bytes; the traffic is then recorded for this workload")
     ap.add_argument("--cus", type=int, default=256, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
 
     if args.gpus != 1:

@@ -1,0 +1,112 @@
+"""Host-side checks of the benchmark's profile summaries (no GPU): the counter
+summary's calibration against the known-size copy and the record it keeps per
+workload, and the kernel-trace summary's split of a trace into decode steps."""
+import argparse
+import csv
+import json
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+COLS = ["Correlation_Id", "Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _pmc(path, counter, dispatches):
+    """dispatches: (kernel name, [values summed per dispatch])."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COLS)
+        w.writeheader()
+        for d, (name, vals) in enumerate(dispatches):
+            for v in vals:   # a derived counter may come as several rows
+                w.writerow({"Correlation_Id": d, "Dispatch_Id": d, "Kernel_Name": name,
+                            "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_counter_summary_calibrates_and_records(tmp_path, monkeypatch, capsys):
+    traffic = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
+    score = "void prism::(anonymous namespace)::score_anchor_kernel<4, 4>(prism::Geometry, int)"
+    merge = "void prism::(anonymous namespace)::merge_kernel<4>(prism::Geometry, int)"
+    other = "void at::native::fill_kernel(int)"
+    # the copy: 1 MiB read and written; FETCH_SIZE reports half the bytes read
+    _pmc(tmp_path / "cf.csv", "FETCH_SIZE", [("copy", [256.0, 256.0]), (other, [0.1])])
+    _pmc(tmp_path / "cw.csv", "WRITE_SIZE", [("copy", [1024.0]), (other, [0.1])])
+    _pmc(tmp_path / "f.csv", "FETCH_SIZE",
+         [(score, [100.0, 28.0]), (score, [120.0, 8.0]), (merge, [2.0]), (other, [5.0])])
+    _pmc(tmp_path / "w.csv", "WRITE_SIZE", [(score, [4.0]), (score, [4.0]), (merge, [1.0]),
+                                            (other, [5.0])])
+    bj = tmp_path / "bench.json"
+    bj.write_text("[bench] log line\n" + json.dumps(
+        {"kernels": {"anchor_score": {"algorithmic_bytes_per_launch": 262144},
+                     "merge": {"avg_us": 1.0}}}) + "\n")
+    args = argparse.Namespace(counter_summary=[str(tmp_path / n) for n in
+                                               ("f.csv", "w.csv", "cf.csv", "cw.csv")],
+                              copy_probe_mib=1, bench_json=str(bj), workload="tiny-4k-gqa4")
+    bench.counter_summary(args)
+    out = capsys.readouterr().out
+    assert "scaled by 2.0000" in out and "by 1.0000" in out
+    # 128 KiB fetched x 2 + 4 KiB written = 266240 bytes per dispatch
+    row = [l for l in out.splitlines() if "score_anchor_kernel<4, 4>" in l][0]
+    assert "| anchor_score | 2 | 128.0 | 4.0 | 2.662e+05 | 2.621e+05 | 1.016 |" in row
+    assert not [l for l in out.splitlines() if "at::native" in l]
+    rec = json.loads(traffic.read_text())
+    assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
+    e = rec["kernels"]["anchor_score"]["tiny-4k-gqa4"]
+    assert e["hbm_bytes_per_launch"] == 266240 and e["dispatches_averaged"] == 2
+    assert "merge" not in rec["kernels"]   # no algorithmic bytes: not recorded
+    assert bench.traffic_for("anchor_score", "tiny-4k-gqa4") == 266240
+    assert bench.traffic_for("anchor_score", "llama3-8b-32k") is None
+    # a second workload is added beside the first
+    args.workload = "llama3-8b-32k"
+    bench.counter_summary(args)
+    rec = json.loads(traffic.read_text())
+    assert set(rec["kernels"]["anchor_score"]) == {"tiny-4k-gqa4", "llama3-8b-32k"}
+
+
+def test_counter_summary_needs_the_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    _pmc(tmp_path / "cf.csv", "FETCH_SIZE", [("copy", [10.0])])   # far below 1 GiB
+    _pmc(tmp_path / "x.csv", "FETCH_SIZE", [])
+    args = argparse.Namespace(counter_summary=[str(tmp_path / n) for n in
+                                               ("x.csv", "x.csv", "cf.csv", "cf.csv")],
+                              copy_probe_mib=1024, bench_json="", workload="tiny-4k-gqa4")
+    with pytest.raises(SystemExit):
+        bench.counter_summary(args)
+
+
+def test_trace_summary_splits_steps(tmp_path, capsys):
+    import synth
+    wl = synth.BY_NAME["tiny-4k-gqa4"]
+    per_step = bench.launches_per_step(wl, 256, 0, bench.layer_roles(wl))
+    n = sum(per_step.values())
+    W, K = 1, 3
+    total = (W + max(1, W)) * n + 2 * K * n + n   # warm-ups, two regions, byte pass
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 0
+        for i in range(total):
+            k = i % n
+            dur = 1000 * (k + 1) if i < (W + max(1, W)) * n + K * n else 2000 * (k + 1)
+            w.writerow({"Kernel_Name": f"void prism::(anonymous namespace)::kern{k}<4>(int)",
+                        "Start_Timestamp": t, "End_Timestamp": t + dur})
+            t += dur + 500
+    args = argparse.Namespace(workload=wl.name, pattern="", cus=256, pool_rho=0, dense=False,
+                              steps=K, warmup=W, trace_summary=str(path))
+    bench.trace_summary(args)
+    out = capsys.readouterr().out
+    row = [l for l in out.splitlines() if "`kern0<4>`" in l][0]
+    # graph replay region: 1 us per dispatch; eager region: 2 us
+    assert row.startswith("| `kern0<4>` | 1 | 1.00 | 1.00 | 2.00 | 2.00 |")
+    # a trace cut short is refused
+    with open(path) as f:
+        lines = f.read().splitlines()
+    path.write_text("\n".join(lines[:-(n + 2)]) + "\n")
+    with pytest.raises(SystemExit):
+        bench.trace_summary(args)

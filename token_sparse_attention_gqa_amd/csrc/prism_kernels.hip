@@ -474,12 +474,17 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
         qv[h][4 + i] = x1[i];
       }
     }
+    // row ids one chunk ahead: the next chunk's are loaded behind the current
+    // chunk's keys, so only the first chunk waits for its row ids
+    uint32_t rid[kGroups];
+    {
+      const int wb0 = base + wave * (kPoolEntries / 4);
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wb0 + u * 8 + rs, n - 1)];
+    }
     for (int c = 0; c < chunks; ++c) {
       const int wbase = base + c * kPoolEntries + wave * (kPoolEntries / 4);
       if (wbase >= n) break;  // uniform over the wave
-      uint32_t rid[kGroups];
-#pragma unroll
-      for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wbase + u * 8 + rs, n - 1)];
       u32x4 kb[kGroups][2];
 #pragma unroll
       for (int u = 0; u < kGroups; ++u) {
@@ -487,6 +492,11 @@ __global__ __launch_bounds__(kScoreThreads) void score_pool_kernel(Geometry g, W
             reinterpret_cast<const u32x4*>(g.k_pages + (size_t)min(rid[u], max_row) * kHeadDim);
         kb[u][0] = __builtin_nontemporal_load(row + part);
         kb[u][1] = __builtin_nontemporal_load(row + part + 8);
+      }
+      {
+        const int wn = wbase + kPoolEntries;  // clamped into the pool: in bounds
+#pragma unroll
+        for (int u = 0; u < kGroups; ++u) rid[u] = prow[min(wn + u * 8 + rs, n - 1)];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
