@@ -2052,10 +2052,6 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
     classify_into(g, second_class(ws), p, w, base, n, need2, raw, h, tmp, res);
 }
 
-__global__ void zero_counters_kernel(uint32_t* c, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) c[i] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // SparseAttn over one split of kAttnSplit selected tokens of one (sequence, KV
 // head), all G query heads.  Each wave takes 16 tokens: logits by MFMA as in
@@ -3370,18 +3366,16 @@ Workspace carve_workspace(void* base, const Geometry& g) {
   return w;
 }
 
-// Anchor layer: zero the coarse histogram and candidate counters, score every
-// cached token (filling the histogram), classify lists longer than kSmall
-// over many workgroups, then select per problem (and build the pool).
+// Anchor layer: score every cached token (filling the coarse histogram),
+// classify lists longer than kSmall over many workgroups, then select per
+// problem (and build the pool).  The histogram is zero from its last reader
+// (each selection clears it); in a fresh or reused workspace it holds other
+// bytes, and then the classification disagrees with itself and the selection
+// runs its exact fallback once.
 hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* q, int32_t* out,
                          int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * kCoarseBins;
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
-                     w.ghist, nz);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
@@ -3398,13 +3392,8 @@ hipError_t launch_anchor(const Geometry& g, const Workspace& w, const uint16_t* 
 
 hipError_t launch_anchor_rank(const Geometry& g, const Workspace& w, const uint16_t* q,
                               int32_t* out, int32_t* out2, hipStream_t s) {
-  const int nz = g.problems() * kCoarseBins;
-  hipLaunchKernelGGL(zero_counters_kernel, dim3(min((nz + 255) / 256, 1024)), dim3(256), 0, s,
-                     w.ghist, nz);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long m = (long long)g.pool_rho * g.kappa;
   if (g.max_seq_len > kSmall && g.max_seq_len > m) {
