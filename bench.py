@@ -152,7 +152,6 @@ KERNEL_KINDS = {
     "attn_kernel": "attention", "select_kernel": "select", "rank_pool_kernel": "select",
     "classify_kernel": "classify", "merge_kernel": "merge", "pool_build_kernel": "pool_build",
     "quantize_kernel": "quantize", "dense_attn_kernel": "dense",
-    "zero_counters_kernel": "counter reset",
 }
 
 
@@ -346,12 +345,8 @@ def trace_summary(args):
     def name(r):
         return _short_kernel(r["Kernel_Name"])
 
-    # the counter reset before a per-problem anchor selection is launched
-    # outside the library's per-kind profiling: reported apart, not counted
     with open(args.trace_summary) as f:
         rows = [r for r in csv.DictReader(f) if "prism::" in r["Kernel_Name"]]
-    resets = [r for r in rows if name(r) == "zero_counters_kernel"]
-    rows = [r for r in rows if name(r) != "zero_counters_kernel"]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
 
     W, K = args.warmup, args.steps
@@ -381,10 +376,6 @@ def trace_summary(args):
               f"{np.mean(ed):.2f} | {np.median(ed):.2f} | |")
     print(f"| step (first start to last end) | | | | | | {np.mean(spans):.4f} mean, "
           f"{np.median(spans):.4f} median |")
-    if resets:
-        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in resets]
-        print(f"\n`zero_counters_kernel` (the counter reset before a per-problem anchor "
-              f"selection): {len(d)} dispatches in the trace, {np.mean(d):.2f} us average")
 
 
 def main():

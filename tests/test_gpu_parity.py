@@ -549,7 +549,8 @@ def test_int2_quantize_bit_exact():
     """prism_quantize_keys against the oracle's quantizer, code for code and bit
     for bit in the scales, on a ragged batch with edge-case rows; rows of other
     positions stay untouched; num_new = 5 rewrites exactly the last 5
-    positions of every sequence."""
+    positions of every sequence, num_new = 37 the last 37 (a kernel wave's 16
+    positions then start unaligned and can span two pages)."""
     wl = synth.scaled(synth.TINY_4K, name="int2-quant", wid=198, num_q_heads=16,
                       num_kv_heads=4, batch=3, context=None, lengths=(6016, 777, 12000),
                       num_layers=1)
@@ -561,7 +562,7 @@ def test_int2_quantize_bit_exact():
     kv = tsa.KVCache(dev(kp), dev(li.v_pages), bt, sl, max_seq_len=int(pg.seq_lens.max()),
                      min_seq_len=int(pg.seq_lens.min()))
     cs, ss = tsa.int2_shapes(kp.shape[0], wl.num_kv_heads)
-    for num_new in (0, 5):
+    for num_new in (0, 5, 37):
         codes = torch.full(cs, 0xCD, dtype=torch.uint8, device="cuda")
         scales = torch.full(ss, 0x7BCD, dtype=torch.int16, device="cuda")
         say(f"[int2-quant] num_new={num_new}")

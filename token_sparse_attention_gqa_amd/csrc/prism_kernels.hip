@@ -70,6 +70,11 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float whose order_key is k (-0 comes back as +0).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Workgroup barrier for LDS communication only: waits for the workgroup's LDS
@@ -185,6 +190,7 @@ constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E;  // quad_perm [1,0,3,2] and [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;             // lane 7 - i of each 8-lane half row
 constexpr int kRowMirror = 0x140;                 // lane 15 - i of each 16-lane row
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;  // rotate right in a row
 
 // Inclusive scan of an associative op over the wave (ident: its identity);
 // lane 63 ends with the result over all 64 lanes.
@@ -586,34 +592,57 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {  // nearest, tie
 // of every (sequence, KV head) (num_new <= 0: every position), 16 rows per
 // wave; the scoring kernels apply it to a decode step's new keys before they
 // score them (Geometry::new_keys).  x: the row's 32-bit word `lane`.
+// Code of one element: rint(fl(d / alpha)) clipped to [0, 3], ties to even
+// (d = v - min >= 0, alpha > 0).  The quotient from the approximate reciprocal
+// ra (int2_recip) is within a few ulp of fl(d / alpha), so it rounds the same
+// way unless it lies within 1e-5 of a half-integer; only then, or when ra is
+// NaN, is the IEEE quotient taken.
+__device__ __forceinline__ float int2_recip(float alpha) {
+  // far from 1 the reciprocal could leave the normal range: every element then
+  // takes the IEEE quotient
+  return (alpha >= 0x1p-100f && alpha <= 0x1p100f) ? __builtin_amdgcn_rcpf(alpha)
+                                                   : __builtin_nanf("");
+}
+__device__ __forceinline__ uint32_t int2_code(float d, float alpha, float ra) {
+  const float q = d * ra;
+  float r = rintf(q);
+  if (!(fabsf(q - r) <= 0.49999f)) r = rintf(__fdiv_rn(d, alpha));
+  return (uint32_t)__builtin_amdgcn_fmed3f(r, 0.f, 3.f);
+}
+
 __device__ __forceinline__ void quantize_value(uint32_t x, size_t row, int lane,
                                                uint8_t* __restrict__ codes,
                                                uint16_t* __restrict__ scales) {
   const float v0 = __uint_as_float(x << 16) + 0.0f;
   const float v1 = __uint_as_float(x & 0xFFFF0000u) + 0.0f;
-  float mn = fminf(v0, v1), mx = fmaxf(v0, v1);
-  // min and max over the 16-lane row: quad, half row, row (every lane gets both)
-  mn = fminf(mn, __uint_as_float(dpp<kQuadXor1, 0xf>(0u, __float_as_uint(mn))));
-  mx = fmaxf(mx, __uint_as_float(dpp<kQuadXor1, 0xf>(0u, __float_as_uint(mx))));
-  mn = fminf(mn, __uint_as_float(dpp<kQuadXor2, 0xf>(0u, __float_as_uint(mn))));
-  mx = fmaxf(mx, __uint_as_float(dpp<kQuadXor2, 0xf>(0u, __float_as_uint(mx))));
-  mn = fminf(mn, __uint_as_float(dpp<kRowHalfMirror, 0xf>(0u, __float_as_uint(mn))));
-  mx = fmaxf(mx, __uint_as_float(dpp<kRowHalfMirror, 0xf>(0u, __float_as_uint(mx))));
-  mn = fminf(mn, __uint_as_float(dpp<kRowMirror, 0xf>(0u, __float_as_uint(mn))));
-  mx = fmaxf(mx, __uint_as_float(dpp<kRowMirror, 0xf>(0u, __float_as_uint(mx))));
+  // min and max over the 16-lane row (quad, half row, row; every lane gets
+  // both), on order-preserving integer keys: integer min and max take their
+  // DPP operand directly, with no float canonicalisation in between
+  const uint32_t k0 = order_key(v0), k1 = order_key(v1);
+  uint32_t kn = min(k0, k1), kx = max(k0, k1);
+  kn = min(kn, dpp<kQuadXor1, 0xf>(0xFFFFFFFFu, kn));  // old = the identity: one DPP op each
+  kx = max(kx, dpp<kQuadXor1, 0xf>(0u, kx));
+  kn = min(kn, dpp<kQuadXor2, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kQuadXor2, 0xf>(0u, kx));
+  kn = min(kn, dpp<kRowHalfMirror, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kRowHalfMirror, 0xf>(0u, kx));
+  kn = min(kn, dpp<kRowMirror, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kRowMirror, 0xf>(0u, kx));
+  const float mn = key_value(kn), mx = key_value(kx);
   const uint32_t ab = f32_to_bf16_bits(__fdiv_rn(mx - mn, 3.0f));
   const float alpha = __uint_as_float(ab << 16);
   uint32_t c0 = 0u, c1 = 0u;
   if (alpha != 0.f) {
-    c0 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v0 - mn, alpha)), 0.f), 3.f);
-    c1 = (uint32_t)fminf(fmaxf(rintf(__fdiv_rn(v1 - mn, alpha)), 0.f), 3.f);
+    const float ra = int2_recip(alpha);
+    c0 = int2_code(v0 - mn, alpha, ra);
+    c1 = int2_code(v1 - mn, alpha, ra);
   }
   // dimensions 2l, 2l + 1: group s = l / 16, quarter u = (l % 16) / 4, elements
   // j = 2 (l % 4) and j + 1 -> word 2u + s/2, bits 2 (4 (s % 2) + l % 4) (+ 16)
   const int s4 = lane >> 4;
   uint32_t wd = (c0 | (c1 << 16)) << (2 * (4 * (s4 & 1) + (lane & 3)));
-  wd |= dpp<kQuadXor1, 0xf>(0u, wd);
-  wd |= dpp<kQuadXor2, 0xf>(0u, wd);
+  wd |= dpp<kQuadXor1, 0xf>(wd, wd);
+  wd |= dpp<kQuadXor2, 0xf>(wd, wd);
   wd = xor16_or(wd);  // groups 2m and 2m + 1 share a word
   if ((lane & 3) == 0 && (s4 & 1) == 0)
     reinterpret_cast<uint32_t*>(codes + row * (kHeadDim / 4))[2 * ((lane & 15) >> 2) + (s4 >> 1)] =
@@ -638,10 +667,52 @@ __device__ __forceinline__ void quantize_positions(const Geometry& g, int b, int
     quantize_row(g, (size_t)row_id(g, b, kvh, pos), lane, g.k_codes, g.k_scales);
 }
 
-// A wave quantizes kQuantRows consecutive positions, all their key rows
-// loaded before the first is quantized (one row per wave and launch slot
-// would leave the prefill's million rows to wave launch rates).
+// Prefill: a wave quantizes kQuantRows consecutive positions, two rows per
+// pass (lanes 0-31 the first, 32-63 the second, four dimensions per lane, so
+// a 32-dimension group is 8 lanes), all rows loaded before the first pass.
+// Per pass: the group's min and max over its 8 lanes (integer keys, DPP), then
+// alpha, the codes, and the code bits OR-combined across the 4 lanes that
+// share a 32-bit code word; the same codes and scales quantize_value writes.
 constexpr int kQuantRows = 16;
+__device__ __forceinline__ void quantize_pair(uint32_t w0, uint32_t w1, size_t row, int lq,
+                                              bool live, uint8_t* __restrict__ codes,
+                                              uint16_t* __restrict__ scales) {
+  // dimensions 4 lq .. 4 lq + 3: group s = lq / 8; quarter u = (lq % 8) / 2;
+  // elements j = 4 (lq % 2) + e -> word 2u + s/2, bits 2t (+ 2), (+ 16), t =
+  // 4 (s % 2) + 2 (lq % 2)
+  const float v0 = __uint_as_float(w0 << 16) + 0.0f;
+  const float v1 = __uint_as_float(w0 & 0xFFFF0000u) + 0.0f;
+  const float v2 = __uint_as_float(w1 << 16) + 0.0f;
+  const float v3 = __uint_as_float(w1 & 0xFFFF0000u) + 0.0f;
+  uint32_t kn = order_key(fminf(fminf(v0, v1), fminf(v2, v3)));
+  uint32_t kx = order_key(fmaxf(fmaxf(v0, v1), fmaxf(v2, v3)));
+  kn = min(kn, dpp<kQuadXor1, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kQuadXor1, 0xf>(0u, kx));
+  kn = min(kn, dpp<kQuadXor2, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kQuadXor2, 0xf>(0u, kx));
+  kn = min(kn, dpp<kRowHalfMirror, 0xf>(0xFFFFFFFFu, kn));
+  kx = max(kx, dpp<kRowHalfMirror, 0xf>(0u, kx));
+  const float mn = key_value(kn), mx = key_value(kx);
+  const uint32_t ab = f32_to_bf16_bits(__fdiv_rn(mx - mn, 3.0f));
+  const float alpha = __uint_as_float(ab << 16);
+  uint32_t c0 = 0u, c1 = 0u, c2 = 0u, c3 = 0u;
+  if (alpha != 0.f) {
+    const float ra = int2_recip(alpha);
+    c0 = int2_code(v0 - mn, alpha, ra);
+    c1 = int2_code(v1 - mn, alpha, ra);
+    c2 = int2_code(v2 - mn, alpha, ra);
+    c3 = int2_code(v3 - mn, alpha, ra);
+  }
+  const int s = lq >> 3;
+  uint32_t wd = (c0 | (c1 << 16) | (c2 << 2) | (c3 << 18)) << (2 * (4 * (s & 1) + 2 * (lq & 1)));
+  wd |= dpp<kQuadXor1, 0xf>(0u, wd);
+  wd |= dpp<kRowRor8, 0xf>(0u, wd);  // groups 2m and 2m + 1 share a word
+  if (live && (lq & 1) == 0 && (s & 1) == 0)
+    reinterpret_cast<uint32_t*>(codes + row * (kHeadDim / 4))[2 * ((lq & 7) >> 1) + (s >> 1)] = wd;
+  if (live && (lq & 7) == 0)  // alpha in the low half, beta in the high half
+    reinterpret_cast<uint32_t*>(scales)[row * 4 + s] = ab | (__float_as_uint(mn) & 0xFFFF0000u);
+}
+
 __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, int chunks,
                                                        uint8_t* __restrict__ codes,
                                                        uint16_t* __restrict__ scales) {
@@ -652,16 +723,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, 
   const int first = (num_new > 0 && num_new < n) ? n - num_new : 0;
   const int pos0 = first + (c * 4 + wv) * kQuantRows;
   if (pos0 >= n) return;  // uniform over the wave
-  size_t rows[kQuantRows];
-  uint32_t x[kQuantRows];
+  const int h = lane >> 5, lq = lane & 31;
+  // the wave's positions lie in one page unless its range starts unaligned
+  const int plast = min(pos0 + kQuantRows - 1, n - 1);
+  const bool one_page = (pos0 >> 6) == (plast >> 6);
+  const uint32_t row0 = row_id(g, b, kvh, pos0);
+  constexpr int kPairs = kQuantRows / 2;
+  uint32_t rows[kPairs];
+  u32x2 x[kPairs];
 #pragma unroll
-  for (int i = 0; i < kQuantRows; ++i) {
-    rows[i] = (size_t)row_id(g, b, kvh, min(pos0 + i, n - 1));
-    x[i] = reinterpret_cast<const uint32_t*>(g.k_pages + rows[i] * kHeadDim)[lane];
+  for (int i = 0; i < kPairs; ++i) {
+    const int pos = min(pos0 + 2 * i + h, n - 1);
+    rows[i] = one_page ? row0 + (uint32_t)(pos - pos0) : row_id(g, b, kvh, pos);
+    x[i] = reinterpret_cast<const u32x2*>(g.k_pages + (size_t)rows[i] * kHeadDim)[lq];
   }
 #pragma unroll
-  for (int i = 0; i < kQuantRows; ++i)
-    if (pos0 + i < n) quantize_value(x[i], rows[i], lane, codes, scales);
+  for (int i = 0; i < kPairs; ++i) {
+    // both halves run every pass (a DPP row lies inside one half); a half
+    // past the sequence's end stores nothing
+    quantize_pair(x[i][0], x[i][1], rows[i], lq, pos0 + 2 * i + h < n, codes, scales);
+  }
 }
 
 // The group's query heads as MFMA A operands against INT2 keys.  A tile is 16
@@ -1039,11 +1120,6 @@ __device__ Bin block_find_top(const uint32_t* h, int need, Sm& sm) {
   }
   lds_barrier();
   return Bin{sm.res[3], sm.res[4], sm.res[5]};
-}
-
-// The float whose order_key is k (-0 comes back as +0).
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
 
 // Threshold of a selection: T is the need-th largest key; need_eq entries
@@ -2062,7 +2138,6 @@ __global__ __launch_bounds__(kClsThreads) void classify_kernel(Geometry g, Works
 // logit, sum of exponentials) and unnormalised output, which go to the
 // workspace; merge_kernel, launched next, merges the splits in split order.
 // ---------------------------------------------------------------------------
-constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
 
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, __uint_as_float(dpp<kRowRor8, 0xf>(0u, __float_as_uint(v))));
@@ -2275,25 +2350,28 @@ __global__ __launch_bounds__(kHeadDim) void merge_kernel(Geometry g, Workspace w
   if (reset && i == 0) reset_selection_counters(ws, p);
 }
 
-// SparseAttn over a given set (positions in idx) or over the row ids the
-// latest selection left in the workspace (ROWS): workgroup s of a problem
-// takes set entries [s * 64 T, (s + 1) * 64 T), each wave T consecutive
-// 16-token tiles with the next tile's K and V in flight while the current one
-// is combined (running softmax statistics per head, rescaled to the running
-// maximum as in dense decode), and the workgroup stores one split.  T grows
-// with the set (fewer, larger splits: less partial traffic for the merge)
-// while the grid still fills the device.
+// SparseAttn over a given set (positions in idx), over the row ids the latest
+// selection left in the workspace, or over a deferred selection's pool
+// indices: workgroup s of a problem takes set entries [s * kSetSplit,
+// (s + 1) * kSetSplit), one 16-token tile per wave, and stores one split for
+// merge_kernel.  Eight waves per workgroup: a 128-token split halves the
+// partials the merge reads against 64-token splits, and the loads of each
+// wave's tile are still all in flight at once (1.1% of the 4 x 128K GQA-8
+// step).
 constexpr int kSetPositions = 0;  // attn_kernel's set: positions in idx
 constexpr int kSetRows = 1;       // row ids the latest selection left (Workspace::sel_row)
 constexpr int kSetEntries = 2;    // pool indices of a deferred selection (Workspace::sel_ent)
+constexpr int kSetWaves = 8;
+constexpr int kSetSplit = 16 * kSetWaves;  // set entries of one workgroup
+static_assert(kSetSplit >= kAttnSplit, "the workspace holds partials of kAttnSplit-token splits");
 
-template <int G, int MODE, int T>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspace ws,
-                                                            const uint16_t* __restrict__ q,
-                                                            const int32_t* __restrict__ idx,
-                                                            int32_t* __restrict__ pos_out,
-                                                            float scale, int splits) {
-  constexpr int NW = kAttnThreads / 64;
+template <int G, int MODE>
+__global__ __launch_bounds__(64 * kSetWaves) void attn_kernel(Geometry g, Workspace ws,
+                                                              const uint16_t* __restrict__ q,
+                                                              const int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ pos_out,
+                                                              float scale, int splits) {
+  constexpr int NW = kSetWaves;
   __shared__ float wo[NW][G][kHeadDim];
   __shared__ float wml[NW][G][2];
   __shared__ __attribute__((aligned(16))) float pw[NW][16 * prob_stride<G>()];
@@ -2313,32 +2391,29 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
   const int j = lane & 15;
   const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
   const int L = seq_len_of(g, b);
-  const int first = s * (64 * T) + wave * (16 * T);  // this wave's first set entry
-  uint32_t row[T];
-  bool valid[T];
-#pragma unroll
-  for (int k = 0; k < T; ++k) {
-    const int ti = first + 16 * k + j;
-    if (MODE == kSetRows) {
-      uint32_t r = ti < g.kappa ? ws.sel_row[(size_t)p * g.kappa + ti] : kNoRow;
-      valid[k] = r <= max_row;
-      row[k] = valid[k] ? r : 0u;
-    } else if (MODE == kSetEntries) {
-      // pool index -> row id and position; the set's positions go to pos_out
-      const int n = clampi(ws.pool_len[p], 0, g.n_cap);
-      const int e = ti < g.kappa ? ws.sel_ent[(size_t)p * g.kappa + ti] : -1;
-      const bool ok = e >= 0 && e < n;
-      const size_t pe = (size_t)p * g.n_cap + (ok ? e : 0);
-      const uint32_t r = ws.pool_row[pe];
-      valid[k] = ok && r <= max_row;
-      row[k] = valid[k] ? r : 0u;
-      if (pos_out && lane < 16 && ti < g.kappa)
-        pos_out[(size_t)p * g.kappa + ti] = valid[k] ? ws.pool_pos[pe] : -1;
-    } else {
-      const int pos = ti < g.kappa ? idx[(size_t)p * g.kappa + ti] : -1;
-      valid[k] = pos >= 0 && pos < L;
-      row[k] = row_id(g, b, kvh, valid[k] ? pos : 0);
-    }
+  const int first = s * kSetSplit + wave * 16;  // this wave's first set entry
+  const int ti = first + j;
+  uint32_t row;
+  bool valid;
+  if (MODE == kSetRows) {
+    const uint32_t r = ti < g.kappa ? ws.sel_row[(size_t)p * g.kappa + ti] : kNoRow;
+    valid = r <= max_row;
+    row = valid ? r : 0u;
+  } else if (MODE == kSetEntries) {
+    // pool index -> row id and position; the set's positions go to pos_out
+    const int n = clampi(ws.pool_len[p], 0, g.n_cap);
+    const int e = ti < g.kappa ? ws.sel_ent[(size_t)p * g.kappa + ti] : -1;
+    const bool ok = e >= 0 && e < n;
+    const size_t pe = (size_t)p * g.n_cap + (ok ? e : 0);
+    const uint32_t r = ws.pool_row[pe];
+    valid = ok && r <= max_row;
+    row = valid ? r : 0u;
+    if (pos_out && lane < 16 && ti < g.kappa)
+      pos_out[(size_t)p * g.kappa + ti] = valid ? ws.pool_pos[pe] : -1;
+  } else {
+    const int pos = ti < g.kappa ? idx[(size_t)p * g.kappa + ti] : -1;
+    valid = pos >= 0 && pos < L;
+    row = row_id(g, b, kvh, valid ? pos : 0);
   }
   float Mr[G], Lr[G], O0[G], O1[G];
 #pragma unroll
@@ -2347,42 +2422,17 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
     Lr[i] = 0.f;
     O0[i] = O1[i] = 0.f;
   }
-  const int ntiles = clampi((g.kappa - first + 15) / 16, 0, T);  // uniform over the wave
-  if (ntiles > 0) {
+  if (first < g.kappa) {  // uniform over the wave
     u32x4 qf[4];
     load_q_frag<G>(q, g, b, kvh, lane, qf);
-    auto step = [&](const KvTile& kt, int k) {
-      float m[4], l[4], o0[G], o1[G];
-      attend_tile<G>(kt, qf, valid[k], scale, pw[wave], m, l, o0, o1);
+    KvTile kt;
+    load_kv_tile(g, row, lane, kt);
+    float m[4], l[4];
+    attend_tile<G>(kt, qf, valid, scale, pw[wave], m, l, O0, O1);
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[i & 3]), 16 * (i >> 2)));
-        const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i & 3]), 16 * (i >> 2)));
-        const float Mn = fmaxf(Mr[i], mh);
-        const float fa = (Mr[i] == -INFINITY) ? 0.f : __expf(Mr[i] - Mn);
-        const float fb = (mh == -INFINITY) ? 0.f : __expf(mh - Mn);
-        Lr[i] = Lr[i] * fa + lh * fb;
-        O0[i] = O0[i] * fa + o0[i] * fb;
-        O1[i] = O1[i] * fa + o1[i] * fb;
-        Mr[i] = Mn;
-      }
-    };
-    KvTile t0, t1;
-    load_kv_tile(g, row[0], lane, t0);
-#pragma unroll
-    for (int k = 0; k < T; k += 2) {
-      if (k < ntiles) {
-        if (k + 1 < ntiles) load_kv_tile(g, row[k + 1], lane, t1);
-        __builtin_amdgcn_sched_barrier(0);
-        step(t0, k);
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 1 < ntiles) {
-          if (k + 2 < ntiles) load_kv_tile(g, row[k + 2], lane, t0);
-          __builtin_amdgcn_sched_barrier(0);
-          step(t1, k + 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+    for (int i = 0; i < G; ++i) {
+      Mr[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m[i & 3]), 16 * (i >> 2)));
+      Lr[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l[i & 3]), 16 * (i >> 2)));
     }
   }
 #pragma unroll
@@ -2398,7 +2448,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(Geometry g, Workspac
     }
   }
   lds_barrier();
-  store_split<G, NW, kAttnThreads>(ws, p, s, splits, wo, wml);
+  store_split<G, NW, 64 * kSetWaves>(ws, p, s, splits, wo, wml);
 }
 
 // Dense decode attention (every cached token; the FlashAttention-style
@@ -3248,9 +3298,9 @@ void launch_attention_g(const Geometry& g, const Workspace& w, const uint16_t* q
                         const int32_t* idx, int32_t* pos_out, float scale, float* out,
                         bool quantize_new, hipStream_t s) {
   const int extra = quantize_new && g.k_codes && g.new_keys > 0 ? g.problems() : 0;
-  const int splits = (g.kappa + kAttnSplit - 1) / kAttnSplit;
-  launch(kAttention, attn_kernel<G, MODE, 1>, dim3(g.problems() * splits + extra),
-         dim3(kAttnThreads), s, g, w, q, idx, pos_out, scale, splits);
+  const int splits = (g.kappa + kSetSplit - 1) / kSetSplit;
+  launch(kAttention, attn_kernel<G, MODE>, dim3(g.problems() * splits + extra),
+         dim3(64 * kSetWaves), s, g, w, q, idx, pos_out, scale, splits);
   launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
