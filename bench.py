@@ -334,7 +334,9 @@ def trace_summary(args):
     rocprofv3 kernel trace of this script (run with the same options).  The
     library's kernels are cut into decode steps of launches_per_step kernels:
     W eager warm-up steps, max(1, W) graph warm-up replays, K timed replays
-    (region 1), K eager steps (region 2), then the untimed byte-count pass."""
+    (region 1), K eager steps (region 2), then the untimed byte-count pass.
+    With --int2, the prefill quantization launches before the steps
+    (quantize_kernel, which no decode step launches) are reported apart."""
     import csv
     import numpy as np
     import synth
@@ -347,6 +349,8 @@ def trace_summary(args):
 
     with open(args.trace_summary) as f:
         rows = [r for r in csv.DictReader(f) if "prism::" in r["Kernel_Name"]]
+    prefill = [r for r in rows if name(r) == "quantize_kernel"]
+    rows = [r for r in rows if name(r) != "quantize_kernel"]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
 
     W, K = args.warmup, args.steps
@@ -376,6 +380,10 @@ def trace_summary(args):
               f"{np.mean(ed):.2f} | {np.median(ed):.2f} | |")
     print(f"| step (first start to last end) | | | | | | {np.mean(spans):.4f} mean, "
           f"{np.median(spans):.4f} median |")
+    if prefill:
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in prefill]
+        print(f"\nPrefill INT2 quantization (`quantize_kernel`, one launch per layer): "
+              f"{len(d)} launches, {np.mean(d):.2f} us average, {np.median(d):.2f} us median")
 
 
 def main():
