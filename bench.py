@@ -130,9 +130,25 @@ def kernel_source_hash():
         return hashlib.sha256(f.read()).hexdigest()
 
 
+def config_key(args):
+    """The workload and the options that change what a kernel moves: the key
+    of a counter record."""
+    key = args.workload
+    if getattr(args, "pool_rho", 0) >= 1:
+        key += f"/rho{args.pool_rho}"
+    if getattr(args, "int2", False):
+        key += "/int2"
+    if getattr(args, "pattern", ""):
+        key += f"/pattern:{args.pattern}"
+    if getattr(args, "dense", False):
+        key += "/dense"
+    return key
+
+
 def traffic_for(kernel, workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source and this workload; else None."""
+    taken on the current kernel source and this configuration (config_key);
+    else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -182,7 +198,7 @@ def counter_summary(args):
     Prints a markdown table; with --bench-json (the JSON line of a run with the
     same workload options) also the ratio to the algorithmic bytes, and records
     the per-launch HBM bytes of the scored kinds in the committed counter file
-    for this workload and kernel source."""
+    for this configuration (config_key) and kernel source."""
     import numpy as np
     fetch_csv, write_csv, copy_fetch_csv, copy_write_csv = args.counter_summary
     copy_bytes = args.copy_probe_mib << 20
@@ -248,7 +264,7 @@ def counter_summary(args):
         if kind not in by_kind:
             continue
         fsum, wsum, hsum, n = by_kind[kind]
-        t["kernels"].setdefault(kind, {})[args.workload] = {
+        t["kernels"].setdefault(kind, {})[config_key(args)] = {
             "fetch_kib": round(fsum / n, 1), "write_kib": round(wsum / n, 1),
             "fetch_factor": round(ff, 5), "write_factor": round(wf, 5),
             "hbm_bytes_per_launch": int(round(hsum / n)), "dispatches_averaged": n}
@@ -434,7 +450,7 @@ def main():
                     help="size of the --copy-probe run the counter summary calibrates against")
     ap.add_argument("--bench-json", default="", metavar="FILE",
                     help="with --counter-summary: output of a run with the same options, for the "
-                         "algorithmic bytes; the traffic is then recorded for this workload")
+                         "algorithmic bytes; the traffic is then recorded for this configuration")
     ap.add_argument("--cus", type=int, default=256, help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.trace_summary:
@@ -680,7 +696,7 @@ def main():
     achieved = dk["GBps"]
     roofline = {"kernel": dominant, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic_for(dominant, wl.name),
+                "traffic": traffic_for(dominant, config_key(args)),
                 "algorithmic_bytes_per_launch": int(algo[dominant]),
                 "avg_launch_us": round(dk["avg_us"], 3),
                 "timed_in": "eager launches, dispatch timestamps"}

@@ -1,6 +1,6 @@
 """Host-side checks of the benchmark's profile summaries (no GPU): the counter
 summary's calibration against the known-size copy and the record it keeps per
-workload, and the kernel-trace summary's split of a trace into decode steps."""
+configuration, and the kernel-trace summary's split of a trace into decode steps."""
 import argparse
 import csv
 import json
@@ -46,7 +46,8 @@ def test_counter_summary_calibrates_and_records(tmp_path, monkeypatch, capsys):
                      "merge": {"avg_us": 1.0}}}) + "\n")
     args = argparse.Namespace(counter_summary=[str(tmp_path / n) for n in
                                                ("f.csv", "w.csv", "cf.csv", "cw.csv")],
-                              copy_probe_mib=1, bench_json=str(bj), workload="tiny-4k-gqa4")
+                              copy_probe_mib=1, bench_json=str(bj), workload="tiny-4k-gqa4",
+                              pool_rho=0, int2=False, pattern="", dense=False)
     bench.counter_summary(args)
     out = capsys.readouterr().out
     assert "scaled by 2.0000" in out and "by 1.0000" in out
@@ -61,11 +62,18 @@ def test_counter_summary_calibrates_and_records(tmp_path, monkeypatch, capsys):
     assert "merge" not in rec["kernels"]   # no algorithmic bytes: not recorded
     assert bench.traffic_for("anchor_score", "tiny-4k-gqa4") == 266240
     assert bench.traffic_for("anchor_score", "llama3-8b-32k") is None
-    # a second workload is added beside the first
+    # a second workload, and an option that changes the traffic, are added
+    # beside the first; a run of that configuration only finds its own record
     args.workload = "llama3-8b-32k"
     bench.counter_summary(args)
+    args.int2, args.pool_rho = True, 4
+    bench.counter_summary(args)
     rec = json.loads(traffic.read_text())
-    assert set(rec["kernels"]["anchor_score"]) == {"tiny-4k-gqa4", "llama3-8b-32k"}
+    assert set(rec["kernels"]["anchor_score"]) == {"tiny-4k-gqa4", "llama3-8b-32k",
+                                                   "llama3-8b-32k/rho4/int2"}
+    assert bench.traffic_for("anchor_score", bench.config_key(args)) == 266240
+    args.int2 = False
+    assert bench.traffic_for("anchor_score", bench.config_key(args)) is None
 
 
 def test_counter_summary_needs_the_copy(tmp_path, monkeypatch):
@@ -74,7 +82,8 @@ def test_counter_summary_needs_the_copy(tmp_path, monkeypatch):
     _pmc(tmp_path / "x.csv", "FETCH_SIZE", [])
     args = argparse.Namespace(counter_summary=[str(tmp_path / n) for n in
                                                ("x.csv", "x.csv", "cf.csv", "cf.csv")],
-                              copy_probe_mib=1024, bench_json="", workload="tiny-4k-gqa4")
+                              copy_probe_mib=1024, bench_json="", workload="tiny-4k-gqa4",
+                              pool_rho=0, int2=False, pattern="", dense=False)
     with pytest.raises(SystemExit):
         bench.counter_summary(args)
 
