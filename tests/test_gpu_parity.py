@@ -144,6 +144,48 @@ def test_concentrated_scores_and_long_ties(L, kappa):
     check_set(got[0, 1], want, s, np.arange(L), kappa, f"outlier L{L}")
 
 
+def test_wide_threshold_bin_with_ties():
+    """A list longer than 16384 whose threshold bin (one coarse score bin)
+    holds more candidates than LDS keeps: about 8000 of 40000 entries, each
+    classify region within its own capacity.  Scores are exact (one query
+    head, q = e_0 + e_1 / 256, keys with only those two dimensions), about 120
+    of them equal at the kappa-th place: the selection ranks the stored
+    candidates by their remaining key bits and gives the tie to the lowest
+    positions, exactly as the oracle."""
+    rng = np.random.default_rng(21)
+    L = 40000
+    k = np.zeros((L, 128), np.float32)
+    u = rng.random(L)
+    above, inbin = u < 0.05, (u >= 0.05) & (u < 0.25)
+    below = ~(above | inbin)
+    k[above, 0], k[above, 1] = 2.5, rng.standard_normal(int(above.sum()))
+    k[inbin, 0], k[inbin, 1] = 1.0, rng.uniform(0.0, 24.0, int(inbin.sum()))  # scores in [1, 1.094)
+    k[below, 0], k[below, 1] = 0.5, rng.standard_normal(int(below.sum()))
+    k[np.sort(rng.choice(np.nonzero(inbin)[0], 100, replace=False)), 1] = 12.0
+    rows = synth.f32_to_bf16_bits(k)
+    q = np.zeros((1, 1, 128), np.float32)
+    q[0, 0, 0], q[0, 0, 1] = 1.0, 1.0 / 256
+    q = synth.f32_to_bf16_bits(q)
+    kp, bt = _hand_cache([rows], [L])
+    # kappa: every score above 1 + 12/256, then about half of those equal to it
+    sc = oracle.relevance(oracle.bf16_to_f64(q[0]), oracle.bf16_to_f64(rows))
+    thr = 1.0 + 12.0 / 256
+    n_above, n_eq = int((sc > thr).sum()), int((sc == thr).sum())
+    assert 4096 < int(((sc >= 1.0) & (sc < 1.125)).sum()) and 100 <= n_eq <= 256
+    kappa = n_above + n_eq // 2
+    kv = tsa.KVCache(dev(kp), dev(kp), dev(bt), dev(np.array([L], np.int32)), max_seq_len=L,
+                     min_seq_len=L)
+    p = tsa.params(1, kappa)
+    ws = torch.empty(tsa.prism_workspace_size(kv, p), dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((1, 1, kappa), dtype=torch.int32, device="cuda")
+    for rep in range(2):  # a fresh workspace takes the exact fallback once
+        say(f"[wide-bin] kappa={kappa} n_eq={n_eq} rep={rep}")
+        tsa.prism_score_topk(kv, dev(q), p, idx, None, ws)
+        got = idx.cpu().numpy()[0, 0]
+        want, _ = oracle.anchor_select(oracle.bf16_to_f64(q[0]), kp, bt[0], 0, L, kappa, 64)
+        assert np.array_equal(np.sort(got), np.sort(want)), f"rep {rep}"
+
+
 # --------------------------------------------------------------------------- refine
 def test_refine_stage_isolated_tiny():
     st = Setup(synth.TINY_4K, [0, 1])

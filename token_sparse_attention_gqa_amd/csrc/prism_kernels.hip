@@ -1742,43 +1742,126 @@ __device__ __forceinline__ void classified_marks(const Geometry& g, const Worksp
       }
     }
   } else {
-    // exact radix over the whole list
-    uint32_t* h1 = sm.hist;
-    uint32_t* h2 = sm.hist + 4096;
-    uint32_t* h3 = sm.hist + 5120;
-    for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
-    lds_barrier();
-    for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
-    lds_barrier();
-    const Bin a = find_publish<4096>(h1, K, sm, 0);
-    for (int e = t; e < n; e += NT) {
-      const uint32_t key = order_key(c.sc[e]);
-      if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
+    // More candidates than LDS holds (a wide threshold bin, as when ranking
+    // rho * kappa of a long list), but every one stored in its region: a
+    // radix select over the candidates' next 10 and last 10 key bits, read
+    // from the regions.  Equal keys at the threshold beyond those needed are
+    // ranked by list index in LDS; more than kPairMax of them fall back to
+    // the exact radix over the whole list below, as does an inconsistent or
+    // overflowing classification.
+    bool whole_list = true;
+    if (marks == above && ncand == in_bin && need >= 1 && need <= ncand) {
+      auto cand = [&](int i, uint32_t* key, int32_t* idx) {
+        int lo = 0, hi = regions - 1;  // the last region starting at or before i
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int)sm.ured[mid] <= i) lo = mid;
+          else hi = mid - 1;
+        }
+        const size_t src = (size_t)lo * kClsCap + (size_t)(i - (int)sm.ured[lo]);
+        *key = gk[src];
+        *idx = gi[src];
+      };
+      uint32_t* h2 = sm.hist;
+      uint32_t* h3 = sm.hist + 1024;
+      for (int i = t; i < 2048; i += NT) sm.hist[i] = 0u;
+      if (t == 0) sm.cnt[0] = 0;
+      lds_barrier();
+      for (int i = t; i < ncand; i += NT) {
+        uint32_t k;
+        int32_t x;
+        cand(i, &k, &x);
+        atomicAdd(&h2[(k >> 10) & 1023u], 1u);
+      }
+      lds_barrier();
+      const Bin bb = find_publish<1024>(h2, need, sm, 3);
+      for (int i = t; i < ncand; i += NT) {
+        uint32_t k;
+        int32_t x;
+        cand(i, &k, &x);
+        if ((int)((k >> 10) & 1023u) == bb.bin) atomicAdd(&h3[k & 1023u], 1u);
+      }
+      lds_barrier();
+      const Bin cc = find_publish<1024>(h3, need - bb.above, sm, 6);
+      const uint32_t T = ((uint32_t)ws.sel_meta[4 * p] << 20) | ((uint32_t)bb.bin << 10) |
+                         (uint32_t)cc.bin;
+      const int need_eq = need - bb.above - cc.above;
+      if (bb.bin >= 0 && cc.bin >= 0 && need_eq >= 1 &&
+          (need_eq == cc.count || cc.count <= kPairMax)) {  // uniform over the workgroup
+        whole_list = false;
+        if (need_eq != cc.count) {  // the equal keys' list indices, for their ranks
+          for (int i = t; i < ncand; i += NT) {
+            uint32_t k;
+            int32_t x;
+            cand(i, &k, &x);
+            if (k == T) {
+              const int slot = atomicAdd(&sm.cnt[0], 1);
+              if (slot < kPairMax) sm.pair[slot] = (uint32_t)x;
+            }
+          }
+          lds_barrier();
+        }
+        const int ne = min(cc.count, kPairMax);
+        for (int i = t; i < ncand; i += NT) {
+          uint32_t k;
+          int32_t x;
+          cand(i, &k, &x);
+          bool take = k > T;
+          if (k == T) {
+            if (need_eq == cc.count) {
+              take = true;
+            } else {
+              int rank = 0;
+              for (int y = 0; y < ne; ++y) rank += (int)sm.pair[y] < x ? 1 : 0;
+              take = rank < need_eq;
+            }
+          }
+          if (take) {
+            const int e = clampi(x, 0, n - 1);
+            atomicOr(&sm.bitmap[e >> 5], 1u << (e & 31));
+          }
+        }
+      }
     }
-    lds_barrier();
-    const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
-    const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
-    for (int e = t; e < n; e += NT) {
-      const uint32_t key = order_key(c.sc[e]);
-      if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
-    }
-    lds_barrier();
-    const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
-    const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
-    const int need_eq = K - a.above - bb.above - cc.above;
-    int run = 0;  // equal keys in earlier chunks
-    for (int base = 0; base < n; base += NT) {
-      const int e = base + t;
-      const bool valid = e < n;
-      const uint32_t key = valid ? order_key(c.sc[e]) : 0u;
-      const bool eq = valid && key == T;
-      int tot;
-      const int r = block_excl_scan<NT>(eq ? 1 : 0, sm.tmp, &tot);
-      const bool take = valid && (key > T || (eq && run + r < need_eq));
-      const unsigned long long m = __ballot(take);
-      if (lane == 0 && e < n) sm.bitmap[e >> 5] = (uint32_t)m;
-      if (lane == 32 && e < n) sm.bitmap[e >> 5] = (uint32_t)(m >> 32);
-      run += tot;
+    if (whole_list) {  // exact radix over the whole list
+      uint32_t* h1 = sm.hist;
+      uint32_t* h2 = sm.hist + 4096;
+      uint32_t* h3 = sm.hist + 5120;
+      lds_barrier();  // earlier readers of sm.hist are done
+      for (int i = t; i < 6144; i += NT) sm.hist[i] = 0u;
+      lds_barrier();
+      for (int e = t; e < n; e += NT) atomicAdd(&h1[order_key(c.sc[e]) >> 20], 1u);
+      lds_barrier();
+      const Bin a = find_publish<4096>(h1, K, sm, 0);
+      for (int e = t; e < n; e += NT) {
+        const uint32_t key = order_key(c.sc[e]);
+        if ((int)(key >> 20) == a.bin) atomicAdd(&h2[(key >> 10) & 1023u], 1u);
+      }
+      lds_barrier();
+      const Bin bb = find_publish<1024>(h2, K - a.above, sm, 3);
+      const uint32_t pre = ((uint32_t)a.bin << 10) | (uint32_t)bb.bin;
+      for (int e = t; e < n; e += NT) {
+        const uint32_t key = order_key(c.sc[e]);
+        if ((key >> 10) == pre) atomicAdd(&h3[key & 1023u], 1u);
+      }
+      lds_barrier();
+      const Bin cc = find_publish<1024>(h3, K - a.above - bb.above, sm, 6);
+      const uint32_t T = (pre << 10) | (uint32_t)cc.bin;
+      const int need_eq = K - a.above - bb.above - cc.above;
+      int run = 0;  // equal keys in earlier chunks
+      for (int base = 0; base < n; base += NT) {
+        const int e = base + t;
+        const bool valid = e < n;
+        const uint32_t key = valid ? order_key(c.sc[e]) : 0u;
+        const bool eq = valid && key == T;
+        int tot;
+        const int r = block_excl_scan<NT>(eq ? 1 : 0, sm.tmp, &tot);
+        const bool take = valid && (key > T || (eq && run + r < need_eq));
+        const unsigned long long m = __ballot(take);
+        if (lane == 0 && e < n) sm.bitmap[e >> 5] = (uint32_t)m;
+        if (lane == 32 && e < n) sm.bitmap[e >> 5] = (uint32_t)(m >> 32);
+        run += tot;
+      }
     }
   }
   lds_barrier();
