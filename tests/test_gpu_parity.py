@@ -340,6 +340,18 @@ def test_decode_chain_planted_small():
     _run_chain(st, range(8), [(0, g) for g in range(8)], "planted-16k")
 
 
+def test_decode_chain_fused_128_token_splits():
+    """16 (sequence, KV head) problems at kappa = 2048: 64-token splits of the
+    fused refined kernel would need 512 workgroups, more than the device holds
+    at once, so its refined layers take 128-token splits (256 workgroups);
+    smaller grids take 64.  Both split sizes give the oracle's sets."""
+    wl = synth.scaled(synth.TINY_4K, name="fused-128", wid=177, num_q_heads=32, num_kv_heads=8,
+                      batch=2, context=None, lengths=(12000, 9000), kappa=2048, window=16,
+                      num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3))
+    _run_chain(st, range(3), [(b, g) for b in range(2) for g in (0, 3, 7)], "fused-128")
+
+
 @pytest.mark.parametrize("G", [1, 2, 8, 16])
 def test_decode_chain_groups_mixed_pools(G):
     """Ragged batch whose refined pools fall on both sides of 16384 entries

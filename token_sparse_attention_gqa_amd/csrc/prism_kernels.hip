@@ -2623,12 +2623,13 @@ __global__ __launch_bounds__(kAttnThreads) void dense_attn_kernel(Geometry g, Wo
 // Refined layer of a decode step: the selection and SparseAttn in one kernel.
 // Workgroup s of problem p selects the pool's top-kappa itself (every split's
 // workgroup reaches the same set: same keys, same order) and attends its ranks
-// [s * kFusedSplit, +kFusedSplit) of the ascending set, 16 per wave;
+// [s * SP, (s + 1) * SP) of the ascending set, 16 per wave (SP = 64 when the
+// grid of 64-token splits still fits the device at once, else 128);
 // layer_idx, if given, receives those ranks' positions.  Pools of at most
 // kSmall entries are selected in registers; up to kRegMarks entries also from
 // registers (32 keys per thread) into marks in an LDS bitmap; longer ones by
 // the sampled bracket and one pass over the pool (marks in the bitmap).
-template <int G>
+template <int G, int SP>
 struct FusedSmem {
   uint32_t hist[4096 + 1024 + 1024];
   uint32_t pair[kPairMax];
@@ -2638,19 +2639,19 @@ struct FusedSmem {
   int cnt[2];
   uint32_t bitmap[kMaxSeqLen / 32];  // pools longer than kSmall: selection marks
   uint32_t cbuf[2 * kCand];
-  uint32_t srow[kFusedSplit];
-  float wo[kFusedSplit / 16][G][kHeadDim];
-  float wml[kFusedSplit / 16][G][2];
-  float pw[kFusedSplit / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
+  uint32_t srow[SP];
+  float wo[SP / 16][G][kHeadDim];
+  float wml[SP / 16][G][2];
+  float pw[SP / 16][16 * prob_stride<G>()] __attribute__((aligned(16)));
 };
 
 // The selection step of refine_attn_kernel: every thread holds R consecutive
 // pool entries (R n_threads >= n); the block finds the pool's top-kappa and
-// keeps the row ids of ranks [r0, r0 + kFusedSplit) in sm.srow (and writes
-// their positions to layer_idx).  Returns the size of the selected set.
+// keeps the row ids of ranks [r0, r0 + span) in sm.srow (and writes their
+// positions to layer_idx).  Returns the size of the selected set.
 template <int R, typename Sm>
 __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p, int n, int r0,
-                                  int32_t* layer_idx, Sm& sm) {
+                                  int span, int32_t* layer_idx, Sm& sm) {
   const int t = threadIdx.x, K = g.kappa;
   const int e0 = R * t;
   const int nv = clampi(n - e0, 0, R);
@@ -2665,7 +2666,7 @@ __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p,
   const uint32_t take = top_k_mask<R>(key, nv, n, K, sm);
   int total;
   int o = block_excl_scan<NT>(__popc(take), sm.tmp, &total);
-  const int rend = min(K, r0 + kFusedSplit);
+  const int rend = min(K, r0 + span);
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     if (take & (1u << i)) {
@@ -2682,11 +2683,12 @@ __device__ int fused_select_slice(const Geometry& g, const Workspace& ws, int p,
   return total;
 }
 
-// Ranks [r0, r0 + kFusedSplit) of the entries marked in sm.bitmap (marks in
-// list order, so ranks are ascending positions): their row ids go to sm.srow
-// and their positions to layer_idx.  Returns the number of marked entries.
+// Ranks [r0, r0 + span) of the entries marked in sm.bitmap (marks in list
+// order, so ranks are ascending positions): their row ids go to sm.srow and
+// their positions to layer_idx.  Returns the number of marked entries.
 template <typename Sm>
-__device__ __forceinline__ int slice_from_marks(const SelList& c, int p, int r0, int32_t* layer_idx, Sm& sm) {
+__device__ __forceinline__ int slice_from_marks(const SelList& c, int p, int r0, int span,
+                                                int32_t* layer_idx, Sm& sm) {
   const int t = threadIdx.x, K = c.K;
   const int words = (c.n + 31) >> 5;
   const int wpt = (words + NT - 1) / NT;
@@ -2695,7 +2697,7 @@ __device__ __forceinline__ int slice_from_marks(const SelList& c, int p, int r0,
   for (int i = w0; i < w1; ++i) cnt += __popc(sm.bitmap[i]);
   int total;
   int o = block_excl_scan<NT>(cnt, sm.tmp, &total);
-  const int rend = min(K, r0 + kFusedSplit);
+  const int rend = min(K, r0 + span);
   if (o < rend && o + cnt > r0) {
     for (int i = w0; i < w1 && o < rend; ++i) {
       uint32_t m = sm.bitmap[i];
@@ -2724,8 +2726,8 @@ __device__ __forceinline__ int slice_from_marks(const SelList& c, int p, int r0,
 template <typename Sm>
 __device__ __attribute__((noinline)) int long_pool_slice(const float* sc, const int32_t* plist,
                                                         const uint32_t* prow, int n, int n_cap,
-                                                        int K, int p, int r0, int32_t* layer_idx,
-                                                        Sm* smp) {
+                                                        int K, int p, int r0, int span,
+                                                        int32_t* layer_idx, Sm* smp) {
   Sm& sm = *smp;
   const int t = threadIdx.x;
   SelList c;
@@ -2753,41 +2755,41 @@ __device__ __attribute__((noinline)) int long_pool_slice(const float* sc, const 
   } else {
     select_large_marks(c, sm);
   }
-  return slice_from_marks(c, p, r0, layer_idx, sm);
+  return slice_from_marks(c, p, r0, span, layer_idx, sm);
 }
 
-template <int G>
+template <int G, int SP>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
                                                          float scale,
                                                          int32_t* __restrict__ layer_idx) {
-  constexpr int NW = kFusedSplit / 16;  // waves that attend, 16 tokens each
+  constexpr int NW = SP / 16;  // waves that attend, 16 tokens each
   static_assert(NW >= 1 && NW <= NT / 64, "attending waves fit the workgroup");
-  __shared__ FusedSmem<G> sm;
+  __shared__ FusedSmem<G, SP> sm;
   const int K = g.kappa;
-  const int splits = (K + kFusedSplit - 1) / kFusedSplit;
+  const int splits = (K + SP - 1) / SP;
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane & 15, g4 = lane >> 4;
   const int n = clampi(ws.pool_len[p], 0, g.n_cap);
-  const int r0 = s * kFusedSplit;  // first rank of this split
+  const int r0 = s * SP;  // first rank of this split
   const int myr = r0 + wave * 16 + j;
   uint32_t row = 0u;
   bool valid = false;
   if (n <= kSmall) {  // uniform over the workgroup
     int total;
     if (n <= kSmall / 2)
-      total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, layer_idx, sm);
+      total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, SP, layer_idx, sm);
     else
-      total = fused_select_slice<kSmallPer>(g, ws, p, n, r0, layer_idx, sm);
+      total = fused_select_slice<kSmallPer>(g, ws, p, n, r0, SP, layer_idx, sm);
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   } else {
     const size_t base = (size_t)p * g.n_cap;
     const int total = long_pool_slice(ws.scores + base, ws.pool_pos + base, ws.pool_row + base, n,
-                                      g.n_cap, K, p, r0, layer_idx, &sm);
+                                      g.n_cap, K, p, r0, SP, layer_idx, &sm);
     valid = myr < min(total, K);
     row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
   }
@@ -3321,6 +3323,15 @@ bool fused_fits(const Geometry& g) {
   return g.group <= 8 && wgs <= (long long)device_cus();
 }
 
+// Tokens per workgroup of the fused refined kernel: 64 when that grid still
+// fits the device at once (each workgroup then gathers half the rows, and the
+// repeated selection runs on compute units that would idle; 128K planted
+// workload: 0.828 against 0.859 ms per step), else kFusedSplit.
+int refine_split(const Geometry& g) {
+  return (long long)g.problems() * ((g.kappa + 63) / 64) <= (long long)device_cus() ? 64
+                                                                                    : kFusedSplit;
+}
+
 template <int G>
 void launch_anchor_score_g(const Geometry& g, const Workspace& w, const uint16_t* q,
                            hipStream_t s) {
@@ -3659,9 +3670,14 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
 template <int G>
 void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
                           float* out, int32_t* layer_idx, hipStream_t s) {
-  const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
-  launch(kAttention, refine_attn_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g, w, q,
-         scale, layer_idx);
+  const int sp = refine_split(g);
+  const int splits = (g.kappa + sp - 1) / sp;
+  if (sp == 64)
+    launch(kAttention, refine_attn_kernel<G, 64>, dim3(g.problems() * splits), dim3(NT), s, g, w,
+           q, scale, layer_idx);
+  else
+    launch(kAttention, refine_attn_kernel<G, kFusedSplit>, dim3(g.problems() * splits), dim3(NT),
+           s, g, w, q, scale, layer_idx);
   launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
