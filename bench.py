@@ -402,6 +402,75 @@ def trace_summary(args):
               f"{len(d)} launches, {np.mean(d):.2f} us average, {np.median(d):.2f} us median")
 
 
+def attn_sweep(args):
+    """SparseAttn alone (prism_sparse_attn: the attention kernel over a given
+    set, then the merge) on layer 0 of the workload, for set sizes 512 ..
+    8192 and two set shapes: uniform random positions and the most recent
+    tokens of each sequence (contiguous within each page).  The attention
+    kernel's duration comes from its own dispatch timestamps (median of 20);
+    a least-squares line over the sizes splits it into a fixed cost and a
+    streaming rate for the K and V bytes."""
+    import numpy as np
+    import torch
+    import synth
+    import token_sparse_attention_gqa_amd as tsa
+
+    wl = synth.BY_NAME[args.workload]
+    pg = synth.paging(wl)
+    dev = torch.device("cuda:0")
+    li = synth.layer_inputs(wl, 0, synth.default_threads())
+    q = torch.from_numpy(li.q.view(np.int16)).to(dev)
+    kv = tsa.KVCache(torch.from_numpy(li.k_pages.view(np.int16)).to(dev),
+                     torch.from_numpy(li.v_pages.view(np.int16)).to(dev),
+                     torch.from_numpy(pg.block_table).to(dev),
+                     torch.from_numpy(pg.seq_lens).to(dev),
+                     max_seq_len=int(pg.seq_lens.max()), min_seq_len=int(pg.seq_lens.min()))
+    del li
+    B, H = wl.batch, wl.num_kv_heads
+    lens = pg.seq_lens.astype(np.int64)
+    sizes = [k for k in (512, 1024, 2048, 4096, 8192) if k <= int(lens.min())]
+    pmax = tsa.params(wl.num_q_heads, max(sizes), wl.anchor_stride, wl.window)
+    ws = torch.empty(tsa.prism_workspace_size(kv, pmax), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(1)
+    res, n = {}, 20
+    for shape in ("uniform random", "most recent"):
+        rows = []
+        for k in sizes:
+            idx = np.zeros((B, H, k), np.int32)
+            for b in range(B):
+                for h in range(H):
+                    L = int(lens[b])
+                    idx[b, h] = (np.sort(rng.choice(L, k, replace=False)) if shape[0] == "u"
+                                 else np.arange(L - k, L))
+            idx_d = torch.from_numpy(idx).to(dev)
+            p = tsa.params(wl.num_q_heads, k, wl.anchor_stride, wl.window)
+            for _ in range(3):
+                tsa.prism_sparse_attn(kv, q, p, idx_d, out, ws)
+            st = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            en = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            tsa.prism_profile_events("attention", st, en)
+            for _ in range(n):
+                tsa.prism_sparse_attn(kv, q, p, idx_d, out, ws)
+            torch.cuda.synchronize()
+            tsa.prism_profile_events("attention", [], [])
+            us = float(np.median([a.elapsed_time(b) for a, b in zip(st, en)])) * 1e3
+            byts = B * H * k * 2 * wl.head_dim * 2
+            rows.append((k, byts, us))
+        x = np.array([r[1] for r in rows], np.float64)
+        y = np.array([r[2] for r in rows], np.float64)
+        slope, icpt = np.polyfit(x, y, 1)
+        res[shape] = {"sizes": [{"kappa": k, "bytes": b, "attention_us": round(u, 2),
+                                 "TBps": round(b / u / 1e6, 3)} for k, b, u in rows],
+                      "fixed_us": round(float(icpt), 2),
+                      "streaming_TBps": round(float(1e-6 / slope), 3)}
+        log(f"[bench] {wl.name} {shape}: " + ", ".join(
+            f"kappa {k}: {u:.2f} us ({b / u / 1e6:.2f} TB/s)" for k, b, u in rows)
+            + f"; fit {icpt:.2f} us + bytes / {1e-6 / slope:.2f} TB/s")
+    print(json.dumps({"attn_sweep": {"workload": wl.name, "group": wl.group, "sets": res}}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -437,6 +506,11 @@ def main():
     ap.add_argument("--copy-rate", type=int, nargs="*", default=None, metavar="MIB",
                     help="only time device-to-device copies of these sizes in MiB and exit: the "
                          "rate a plain streaming kernel reaches at a kernel's working-set size")
+    ap.add_argument("--attn-sweep", action="store_true",
+                    help="only time prism_sparse_attn's attention kernel on layer 0 of --workload "
+                         "for sets of 512 to 8192 positions per (sequence, KV head), uniform "
+                         "random and the most recent tokens, then exit: its fixed cost and "
+                         "streaming rate (least squares over the set sizes)")
     ap.add_argument("--trace-summary", default="", metavar="CSV",
                     help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
                          "of this script with the same workload options, --steps and --warmup, and "
@@ -503,6 +577,10 @@ def main():
 
     import synth
     import token_sparse_attention_gqa_amd as tsa
+
+    if args.attn_sweep:
+        attn_sweep(args)
+        return
 
     wl = synth.BY_NAME[args.workload]
     pg = synth.paging(wl)
