@@ -405,8 +405,9 @@ def trace_summary(args):
 def attn_sweep(args):
     """SparseAttn alone (prism_sparse_attn: the attention kernel over a given
     set, then the merge) on layer 0 of the workload, for set sizes 512 ..
-    8192 and two set shapes: uniform random positions and the most recent
-    tokens of each sequence (contiguous within each page).  The attention
+    8192 and four set shapes: uniform random positions, the most recent
+    tokens of each sequence (contiguous within each page), and aligned runs of
+    64 (whole pages) or 16 tokens at random places.  The attention
     kernel's duration comes from its own dispatch timestamps (median of 20);
     a least-squares line over the sizes splits it into a fixed cost and a
     streaming rate for the K and V bytes."""
@@ -434,15 +435,23 @@ def attn_sweep(args):
     out = torch.empty((B, wl.num_q_heads, wl.head_dim), dtype=torch.float32, device=dev)
     rng = np.random.default_rng(1)
     res, n = {}, 20
-    for shape in ("uniform random", "most recent"):
+    def positions(shape, L, k):
+        if shape == "uniform random":
+            return np.sort(rng.choice(L, k, replace=False))
+        if shape == "most recent":
+            return np.arange(L - k, L)
+        run = 64 if shape == "random 64-token runs" else 16   # aligned runs of that length
+        starts = np.sort(rng.choice(L // run, k // run, replace=False)) * run
+        return (starts[:, None] + np.arange(run)).ravel()
+
+    for shape in ("uniform random", "most recent", "random 64-token runs",
+                  "random 16-token runs"):
         rows = []
         for k in sizes:
             idx = np.zeros((B, H, k), np.int32)
             for b in range(B):
                 for h in range(H):
-                    L = int(lens[b])
-                    idx[b, h] = (np.sort(rng.choice(L, k, replace=False)) if shape[0] == "u"
-                                 else np.arange(L - k, L))
+                    idx[b, h] = positions(shape, int(lens[b]), k)
             idx_d = torch.from_numpy(idx).to(dev)
             p = tsa.params(wl.num_q_heads, k, wl.anchor_stride, wl.window)
             for _ in range(3):
@@ -508,8 +517,9 @@ def main():
                          "rate a plain streaming kernel reaches at a kernel's working-set size")
     ap.add_argument("--attn-sweep", action="store_true",
                     help="only time prism_sparse_attn's attention kernel on layer 0 of --workload "
-                         "for sets of 512 to 8192 positions per (sequence, KV head), uniform "
-                         "random and the most recent tokens, then exit: its fixed cost and "
+                         "for sets of 512 to 8192 positions per (sequence, KV head) of four "
+                         "shapes (uniform random, the most recent tokens, random 64- and "
+                         "16-token runs), then exit: its fixed cost and "
                          "streaming rate (least squares over the set sizes)")
     ap.add_argument("--trace-summary", default="", metavar="CSV",
                     help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
