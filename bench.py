@@ -88,7 +88,9 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
-    196608), else a selection kernel per layer precedes the attention, and a
+    196608; refined layers whose pools stay within 16384 entries also when
+    problems x ceil(kappa / (256 t)) fits for some t <= 8, the multi-tile
+    kernel), else a selection kernel per layer precedes the attention, and a
     refined layer whose pool can exceed 16384 entries is classified first, and an
     anchor layer that selects in its own kernel builds the window pool in
     another.
@@ -113,11 +115,17 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     n_cap = -(-L // 64) * 64
     pool_bound = min(n_cap, pool_rho * wl.kappa if pool_rho >= 1
                      else wl.kappa * (2 * wl.window + 1))
-    pool_classify = not fused and pool_bound > 16384 and pool_bound > wl.kappa
+    # refined layers beyond the fused grid, with pools of at most 16384 entries:
+    # the multi-tile kernel (selection inside, 256 * tiles ranks per workgroup)
+    problems = wl.batch * wl.num_kv_heads
+    multi = (not fused and wl.group <= 8 and pool_bound <= 16384
+             and any(problems * -(-wl.kappa // (256 * t)) <= cus for t in range(1, 9)))
+    refined_own_select = fused or multi
+    pool_classify = not refined_own_select and pool_bound > 16384 and pool_bound > wl.kappa
     # the fused rank path classifies for kappa (and rho*kappa in the same pass)
     anchor_need = pool_rho * wl.kappa if (pool_rho >= 1 and not anchor_fused) else wl.kappa
     return {"anchor_score": na, "refine_score": nr,
-            "select": (0 if anchor_fused else na) + (0 if fused else nr),
+            "select": (0 if anchor_fused else na) + (0 if refined_own_select else nr),
             "pool_build": 0 if (anchor_fused or pool_rho >= 1) else na,
             "attention": wl.num_layers,
             "classify": (na if (L > 16384 and L > anchor_need) else 0)

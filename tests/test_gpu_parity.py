@@ -505,6 +505,38 @@ def test_decode_chain_rank_pool_per_problem_selection():
     _run_chain_rank(st, range(3), probs, "rank-pool per-problem")
 
 
+# (G, kappa, pool): grids of 48 problems that the fused refined kernel's
+# 128-token splits do not fit on 256 compute units, so refined layers take the
+# multi-tile kernel: 256 ranks per workgroup at kappa = 700 (3 splits, the last
+# ragged), 512 at kappa = 1500 (two tiles per wave, a ragged last split whose
+# waves hold one or two tiles); the window pools stay within 16384 entries.
+MULTI_CASES = [(1, 1500, "rank4"), (2, 700, "window5"), (4, 1500, "window3"), (8, 1500, "rank4"),
+               (8, 700, "window5")]
+
+
+@pytest.mark.parametrize("G,kappa,pool", MULTI_CASES,
+                         ids=[f"G{G}-k{k}-{pl}" for G, k, pl in MULTI_CASES])
+def test_decode_chain_multi_tile_refined(G, kappa, pool):
+    """Refined layers of grids above the device (48 problems) with pools of at
+    most 16384 entries: every split's workgroup selects the pool's top-kappa
+    itself and attends 256 or 512 of its ranks in 16-token tiles per wave.  A
+    ragged batch with a sequence of 1500 tokens (at kappa = 1500 its pool is
+    its whole cache and every token is selected), every problem checked on
+    the anchor layer and both refined layers."""
+    rho = 4 if pool == "rank4" else 0
+    window = 5 if pool == "rank4" else int(pool[len("window"):])
+    wl = synth.scaled(synth.TINY_4K, name=f"multi-{G}-{kappa}-{pool}", wid=520 + G + kappa % 7,
+                      num_q_heads=8 * G, num_kv_heads=8, batch=6, context=None,
+                      lengths=(9024, 1500, 12000, 4096, 16384, 7001), kappa=kappa,
+                      window=window, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=rho)
+    probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    if rho:
+        _run_chain_rank(st, range(3), probs, f"multi G={G} kappa={kappa} {pool}")
+    else:
+        _run_chain(st, range(3), probs, f"multi G={G} kappa={kappa} {pool}")
+
+
 def _run_pattern(st, pattern, problems, label, table4=False):
     """prism_decode_layer_role over a layer-role pattern: proposal layers
     against the oracle's exact TopK, refined layers against the oracle

@@ -2339,6 +2339,59 @@ __device__ __forceinline__ void attend_tile(const KvTile& t, const u32x4 (&qf)[4
   }
 }
 
+// One 16-token tile folded into a wave's running softmax state (online
+// softmax): Mrow[r], Lrow[r] the running maximum logit and sum of exponentials
+// of head 4 g4 + r (the 16 lanes of row g4 agree), O0[i], O1[i] head i's
+// unnormalised output for dimensions 2 lane, 2 lane + 1.  The tile's
+// probabilities are taken against the updated maximum and the output is
+// rescaled once per tile, so no per-tile partial is kept.
+template <int G>
+__device__ __forceinline__ void attend_tile_online(const KvTile& t, const u32x4 (&qf)[4],
+                                                   bool valid, float scale, float* pw,
+                                                   float (&Mrow)[4], float (&Lrow)[4],
+                                                   float (&O0)[G], float (&O1)[G]) {
+  constexpr int GP = prob_stride<G>();
+  const int lane = threadIdx.x & 63, j = lane & 15, g4 = lane >> 4;
+  const f32x4 acc = qk_tile(qf, t.kf);
+  float fr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float z = valid ? acc[r] * scale : -INFINITY;
+    const float Mn = fmaxf(Mrow[r], row16_max(z));
+    fr[r] = (Mrow[r] == -INFINITY) ? 0.f : __expf(Mrow[r] - Mn);
+    const float e = (z == -INFINITY) ? 0.f : __expf(z - Mn);
+    Lrow[r] = Lrow[r] * fr[r] + row16_sum(e);
+    Mrow[r] = Mn;
+    if (4 * g4 + r < G) pw[j * GP + 4 * g4 + r] = e;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float f = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fr[i & 3]), 16 * (i >> 2)));
+    O0[i] *= f;
+    O1[i] *= f;
+  }
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const float v0 = __uint_as_float(t.vv[jj] << 16);
+    const float v1 = __uint_as_float(t.vv[jj] & 0xffff0000u);
+#pragma unroll
+    for (int i4 = 0; i4 < GP / 4; ++i4) {
+      const float4 w4 = *reinterpret_cast<const float4*>(&pw[jj * GP + 4 * i4]);
+      const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (4 * i4 + r < G) {
+          O0[4 * i4 + r] += wv[r] * v0;
+          O1[4 * i4 + r] += wv[r] * v1;
+        }
+      }
+    }
+  }
+}
+
 // The block's split of SparseAttn from its NW waves' results (wo, wml, filled
 // and synchronised by the caller), rescaled to a common maximum: the
 // unnormalised output [G][128] and (max, sum) [G][2] of split s of problem p,
@@ -2811,6 +2864,117 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
           sm.wml[wave][4 * g4 + r][0] = m[r];
           sm.wml[wave][4 * g4 + r][1] = l[r];
         }
+      }
+    }
+  }
+  lds_barrier();
+  store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
+}
+
+// Refined layer of grids that the fused kernel's one workgroup per 64 or 128
+// selected tokens would not fit at once (many (sequence, KV head) problems,
+// or a large kappa), for pools of at most kSmall entries: `splits` workgroups
+// per problem, each selecting the pool's top-kappa from keys in registers as
+// refine_attn_kernel does (every split reaches the same set), then attending
+// its 256 * tiles consecutive ranks of the set with all sixteen waves, each
+// wave a strided run of 16-token tiles with the next tile's K and V in flight
+// while one is attended and running softmax statistics per head (the pattern
+// of dense_attn_kernel).  The waves' results are combined in the workgroup and
+// stored as one split for merge_kernel.  The selection's LDS is reused for the
+// waves' results once the set's rows are in sm.srow.
+constexpr int kMultiMaxTiles = 8;                 // 16-token tiles per wave at most
+constexpr int kMultiMaxSpan = 16 * NT / 64 * kMultiMaxTiles;  // ranks per workgroup at most
+
+template <int G>
+struct MultiSmem {
+  union {
+    struct {
+      uint32_t hist[4096 + 1024 + 1024];
+      uint32_t pair[kPairMax];
+      uint32_t ured[32];
+      int tmp[NT / 64 + 1];
+      int res[9];
+      int cnt[2];
+    };
+    struct {
+      float wo[NT / 64][G][kHeadDim];
+      float wml[NT / 64][G][2];
+    };
+  };
+  uint32_t srow[kMultiMaxSpan];
+  float pw[NT / 64][16 * prob_stride<G>()] __attribute__((aligned(16)));
+};
+
+template <int G>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 4))) void refine_attn_multi_kernel(Geometry g, Workspace ws,
+                                                               const uint16_t* __restrict__ q,
+                                                               float scale,
+                                                               int32_t* __restrict__ layer_idx,
+                                                               int tiles) {
+  constexpr int NW = NT / 64;
+  __shared__ MultiSmem<G> sm;
+  const int K = g.kappa;
+  tiles = clampi(tiles, 1, kMultiMaxTiles);
+  const int span = 16 * NW * tiles;  // ranks of one workgroup
+  const int splits = (K + span - 1) / span;
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15;
+  // the launch takes this kernel only for pools of at most kSmall entries;
+  // a longer length in the workspace is clamped (a wrong set, never an access
+  // beyond the pool)
+  const int n = min(clampi(ws.pool_len[p], 0, g.n_cap), kSmall);
+  const int r0 = s * span;
+  int total;
+  if (n <= kSmall / 2)
+    total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, span, layer_idx, sm);
+  else
+    total = fused_select_slice<kSmallPer>(g, ws, p, n, r0, span, layer_idx, sm);
+  const int lim = min(min(total, K) - r0, span);  // ranks of this split that hold a token
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  // wave w attends tiles w, w + NW, w + 2 NW, ... of the split
+  const int steps = clampi((lim - 16 * wave + 16 * NW - 1) / (16 * NW), 0, tiles);
+  float Mrow[4], Lrow[4], O0[G], O1[G];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Mrow[r] = -INFINITY;
+    Lrow[r] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) O0[i] = O1[i] = 0.f;
+  if (steps > 0) {  // uniform over the wave
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    auto rank_of = [&](int k) { return 16 * (k * NW + wave) + j; };
+    auto row_of = [&](int k) {
+      const int r = rank_of(k);
+      const uint32_t row = r < lim ? sm.srow[r] : 0u;
+      return row <= max_row ? row : 0u;
+    };
+    auto step = [&](const KvTile& t, int k) {
+      const int r = rank_of(k);
+      const bool valid = r < lim && sm.srow[r] <= max_row;
+      attend_tile_online<G>(t, qf, valid, scale, sm.pw[wave], Mrow, Lrow, O0, O1);
+    };
+    for (int k = 0; k < steps; ++k) {
+      KvTile t0;
+      load_kv_tile(g, row_of(k), lane, t0);
+      step(t0, k);
+    }
+  }
+  // every thread has passed the selection's last barrier, so its LDS is free
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    sm.wo[wave][i][2 * lane] = O0[i];
+    sm.wo[wave][i][2 * lane + 1] = O1[i];
+  }
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * (lane >> 4) + r < G) {
+        sm.wml[wave][4 * (lane >> 4) + r][0] = Mrow[r];
+        sm.wml[wave][4 * (lane >> 4) + r][1] = Lrow[r];
       }
     }
   }
@@ -3365,6 +3529,21 @@ int pool_cap(const Geometry& g) {
                                                : (long long)g.kappa * (2LL * g.window + 1));
 }
 
+// Tiles per wave of refine_attn_multi_kernel at a refined layer whose grid
+// the fused kernel does not fit: the fewest (up to kMultiMaxTiles) whose grid
+// of problems x ceil(kappa / (256 tiles)) workgroups fits the device at once;
+// 0 (the per-problem path) when none does, for groups above 8, and when the
+// pool can hold more than kSmall entries.
+int multi_tiles(const Geometry& g) {
+  if (g.group > 8 || pool_cap(g) > kSmall) return 0;
+  for (int tl = 1; tl <= kMultiMaxTiles; ++tl) {
+    const int span = 16 * (NT / 64) * tl;
+    if ((long long)g.problems() * ((g.kappa + span - 1) / span) <= (long long)device_cus())
+      return tl;
+  }
+  return 0;
+}
+
 template <int G>
 void launch_pool_score_g(const Geometry& g, const Workspace& w, const uint16_t* q, bool hist,
                          hipStream_t s) {
@@ -3669,6 +3848,15 @@ hipError_t launch_refine(const Geometry& g, const Workspace& w, const uint16_t* 
 template <int G>
 void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t* q, float scale,
                           float* out, int32_t* layer_idx, hipStream_t s) {
+  if (!fused_fits(g)) {  // the caller checked multi_tiles(g) > 0
+    const int tiles = multi_tiles(g);
+    const int span = 16 * (NT / 64) * tiles;
+    const int splits = (g.kappa + span - 1) / span;
+    launch(kAttention, refine_attn_multi_kernel<G>, dim3(g.problems() * splits), dim3(NT), s, g,
+           w, q, scale, layer_idx, tiles);
+    launch_merge_g<G>(g, w, splits, out, false, s);
+    return;
+  }
   const int sp = refine_split(g);
   const int splits = (g.kappa + sp - 1) / sp;
   if (sp == 64)
@@ -3682,7 +3870,8 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
 
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s) {
-  if (!fused_fits(g)) {  // select once per problem (pool indices only), then attend
+  if (!fused_fits(g) && multi_tiles(g) == 0) {
+    // select once per problem (pool indices only), then attend
     hipError_t e = launch_refine(g, w, q, nullptr, s, true);
     if (e != hipSuccess) return e;
     return launch_attention_entries(g, w, q, layer_idx, scale, out, s);
