@@ -88,9 +88,10 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     choice: layers select inside their attention kernel when G <= 8 and every
     attention workgroup of the layer fits the device at once (problems x
     ceil(kappa / 128) <= compute units; anchor layers also need contexts up to
-    196608; refined layers whose pools stay within 16384 entries also when
-    problems x ceil(kappa / (256 t)) fits for some t <= 8, the multi-tile
-    kernel), else a selection kernel per layer precedes the attention, and a
+    196608; refined layers whose pools stay within 16384 entries, and anchor
+    layers with the rank-expanded pool, also when problems x ceil(kappa /
+    (256 t)) workgroups (plus one per problem for the rank pool) fit for some
+    t <= 8: the multi-tile kernels), else a selection kernel per layer precedes the attention, and a
     refined layer whose pool can exceed 16384 entries is classified first, and an
     anchor layer that selects in its own kernel builds the window pool in
     another.
@@ -107,9 +108,14 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     L = int(synth.paging(wl).seq_lens.max())
     splits = -(-wl.kappa // 128)
     fused = wl.group <= 8 and wl.batch * wl.num_kv_heads * splits <= cus
+    problems = wl.batch * wl.num_kv_heads
     if pool_rho >= 1:   # rank pools: one more workgroup per problem writes the pool
+        # (with 128-token splits, or 256 t ranks per workgroup for the fewest
+        # t <= 8 that fits, if that leaves two or more splits)
+        fit_t = [t for t in range(1, 9) if problems * (-(-wl.kappa // (256 * t)) + 1) <= cus]
         anchor_fused = (wl.group <= 8 and L <= 6144 * 32
-                        and wl.batch * wl.num_kv_heads * (splits + 1) <= cus)
+                        and (problems * (splits + 1) <= cus
+                             or (fit_t != [] and -(-wl.kappa // (256 * fit_t[0])) >= 2)))
     else:
         anchor_fused = fused and L <= 6144 * 32
     n_cap = -(-L // 64) * 64
@@ -117,7 +123,6 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
                      else wl.kappa * (2 * wl.window + 1))
     # refined layers beyond the fused grid, with pools of at most 16384 entries:
     # the multi-tile kernel (selection inside, 256 * tiles ranks per workgroup)
-    problems = wl.batch * wl.num_kv_heads
     multi = (not fused and wl.group <= 8 and pool_bound <= 16384
              and any(problems * -(-wl.kappa // (256 * t)) <= cus for t in range(1, 9)))
     refined_own_select = fused or multi

@@ -124,17 +124,20 @@ def test_trace_summary_splits_steps(tmp_path, capsys):
 def test_launch_model_per_workload():
     """The launch counts the benchmark checks its profile rings against, for
     the paths the library takes on 256 compute units: fused kernels at 128K
-    planted; refined layers of the batched and 4 x 128K GQA-8 workloads in the
-    multi-tile kernel with the rank pool (pools of 4096 and 16384 entries), and
-    selected per problem after classification with the window pool (pools up
-    to the whole cache)."""
+    planted; anchor and refined layers of the batched and 4 x 128K GQA-8
+    workloads in the multi-tile kernels with the rank pool (pools of 4096 and
+    16384 entries), and selected per problem after classification with the
+    window pool (pools up to the whole cache)."""
     import synth
     m = bench.launches_per_step
     p = m(synth.BY_NAME["llama3-8b-128k-planted"], 256)
     assert (p["select"], p["classify"], p["pool_build"], p["attention"]) == (0, 4, 0, 32)
-    for name, na, nr in (("batched-16x8k-64k", 8, 24), ("long-4x128k-gqa8", 10, 70)):
+    # rank pool: the anchor layer in the multi-tile kernel on 4 x 128K (six
+    # splits per problem), selected per problem on the batched workload (one
+    # split per problem would fit)
+    for name, na, nr, sel in (("batched-16x8k-64k", 8, 24, 8), ("long-4x128k-gqa8", 10, 70, 0)):
         wl = synth.BY_NAME[name]
         r = m(wl, 256, pool_rho=4)
-        assert (r["select"], r["classify"], r["pool_build"]) == (na, na, 0), (name, r)
+        assert (r["select"], r["classify"], r["pool_build"]) == (sel, na, 0), (name, r)
         w = m(wl, 256)
         assert (w["select"], w["classify"], w["pool_build"]) == (na + nr, na + nr, na), (name, w)

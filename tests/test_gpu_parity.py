@@ -521,13 +521,16 @@ def test_decode_chain_multi_tile_refined(G, kappa, pool):
     most 16384 entries: every split's workgroup selects the pool's top-kappa
     itself and attends 256 or 512 of its ranks in 16-token tiles per wave.  A
     ragged batch with a sequence of 1500 tokens (at kappa = 1500 its pool is
-    its whole cache and every token is selected), every problem checked on
-    the anchor layer and both refined layers."""
+    its whole cache and every token is selected) and one of 40000 (selected
+    after classification), every problem checked on the anchor layer and both
+    refined layers.  With the rank pool the anchor layer takes the multi-tile
+    kernel too (two tiles per wave, and one more workgroup per problem that
+    writes the pool)."""
     rho = 4 if pool == "rank4" else 0
     window = 5 if pool == "rank4" else int(pool[len("window"):])
     wl = synth.scaled(synth.TINY_4K, name=f"multi-{G}-{kappa}-{pool}", wid=520 + G + kappa % 7,
                       num_q_heads=8 * G, num_kv_heads=8, batch=6, context=None,
-                      lengths=(9024, 1500, 12000, 4096, 16384, 7001), kappa=kappa,
+                      lengths=(9024, 1500, 12000, 4096, 40000, 7001), kappa=kappa,
                       window=window, num_layers=3, anchor_stride=3)
     st = Setup(wl, range(3), pool_rho=rho)
     probs = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]

@@ -2871,6 +2871,58 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
   store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
 }
 
+// The attention phase shared by the multi-tile kernels: wave w attends tiles
+// w, w + 16, w + 32, ... of the workgroup's `lim` ranks (row ids in srow),
+// then the waves' results are combined and stored as split s.  Contains
+// barriers; the caller's LDS behind wo / wml must be free.
+template <int G, typename Sm>
+__device__ __forceinline__ void multi_attend_store(const Geometry& g, const Workspace& ws,
+                                                   const uint16_t* q, float scale, int p, int s,
+                                                   int splits, int lim, int tiles, Sm& sm) {
+  constexpr int NW = NT / 64;
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15;
+  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
+  const int steps = clampi((lim - 16 * wave + 16 * NW - 1) / (16 * NW), 0, tiles);
+  float Mrow[4], Lrow[4], O0[G], O1[G];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Mrow[r] = -INFINITY;
+    Lrow[r] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < G; ++i) O0[i] = O1[i] = 0.f;
+  if (steps > 0) {  // uniform over the wave
+    u32x4 qf[4];
+    load_q_frag<G>(q, g, b, kvh, lane, qf);
+    for (int k = 0; k < steps; ++k) {
+      const int r = 16 * (k * NW + wave) + j;
+      const uint32_t row = r < lim ? sm.srow[r] : 0u;
+      const bool valid = r < lim && row <= max_row;
+      KvTile t0;
+      load_kv_tile(g, valid ? row : 0u, lane, t0);
+      attend_tile_online<G>(t0, qf, valid, scale, sm.pw[wave], Mrow, Lrow, O0, O1);
+    }
+  }
+  lds_barrier();  // every wave is past its last read of the selection's LDS
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    sm.wo[wave][i][2 * lane] = O0[i];
+    sm.wo[wave][i][2 * lane + 1] = O1[i];
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (4 * (lane >> 4) + r < G) {
+        sm.wml[wave][4 * (lane >> 4) + r][0] = Mrow[r];
+        sm.wml[wave][4 * (lane >> 4) + r][1] = Lrow[r];
+      }
+    }
+  }
+  lds_barrier();
+  store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
+}
+
 // Refined layer of grids that the fused kernel's one workgroup per 64 or 128
 // selected tokens would not fit at once (many (sequence, KV head) problems,
 // or a large kappa), for pools of at most kSmall entries: `splits` workgroups
@@ -2906,7 +2958,7 @@ struct MultiSmem {
 };
 
 template <int G>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 4))) void refine_attn_multi_kernel(Geometry g, Workspace ws,
+__global__ __launch_bounds__(NT) void refine_attn_multi_kernel(Geometry g, Workspace ws,
                                                                const uint16_t* __restrict__ q,
                                                                float scale,
                                                                int32_t* __restrict__ layer_idx,
@@ -2919,8 +2971,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 4))) void
   const int splits = (K + span - 1) / span;
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
-  const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, j = lane & 15;
   // the launch takes this kernel only for pools of at most kSmall entries;
   // a longer length in the workspace is clamped (a wrong set, never an access
   // beyond the pool)
@@ -2931,55 +2981,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 4))) void
     total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, span, layer_idx, sm);
   else
     total = fused_select_slice<kSmallPer>(g, ws, p, n, r0, span, layer_idx, sm);
-  const int lim = min(min(total, K) - r0, span);  // ranks of this split that hold a token
-  const uint32_t max_row = (uint32_t)g.num_pages * (uint32_t)(g.hkv * kPageSize) - 1u;
-  // wave w attends tiles w, w + NW, w + 2 NW, ... of the split
-  const int steps = clampi((lim - 16 * wave + 16 * NW - 1) / (16 * NW), 0, tiles);
-  float Mrow[4], Lrow[4], O0[G], O1[G];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    Mrow[r] = -INFINITY;
-    Lrow[r] = 0.f;
-  }
-#pragma unroll
-  for (int i = 0; i < G; ++i) O0[i] = O1[i] = 0.f;
-  if (steps > 0) {  // uniform over the wave
-    u32x4 qf[4];
-    load_q_frag<G>(q, g, b, kvh, lane, qf);
-    auto rank_of = [&](int k) { return 16 * (k * NW + wave) + j; };
-    auto row_of = [&](int k) {
-      const int r = rank_of(k);
-      const uint32_t row = r < lim ? sm.srow[r] : 0u;
-      return row <= max_row ? row : 0u;
-    };
-    auto step = [&](const KvTile& t, int k) {
-      const int r = rank_of(k);
-      const bool valid = r < lim && sm.srow[r] <= max_row;
-      attend_tile_online<G>(t, qf, valid, scale, sm.pw[wave], Mrow, Lrow, O0, O1);
-    };
-    for (int k = 0; k < steps; ++k) {
-      KvTile t0;
-      load_kv_tile(g, row_of(k), lane, t0);
-      step(t0, k);
-    }
-  }
-  // every thread has passed the selection's last barrier, so its LDS is free
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-    sm.wo[wave][i][2 * lane] = O0[i];
-    sm.wo[wave][i][2 * lane + 1] = O1[i];
-  }
-  if ((lane & 15) == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (4 * (lane >> 4) + r < G) {
-        sm.wml[wave][4 * (lane >> 4) + r][0] = Mrow[r];
-        sm.wml[wave][4 * (lane >> 4) + r][1] = Lrow[r];
-      }
-    }
-  }
-  lds_barrier();
-  store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
+  // ranks of this split that hold a token
+  multi_attend_store<G>(g, ws, q, scale, p, s, splits, min(min(total, K) - r0, span), tiles, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -3111,9 +3114,9 @@ __device__ __forceinline__ void small_marks(const float* sc, int n, int K, Sm& s
 // extra workgroup per problem marks the cache's top rho*kappa (from the second
 // classification) and writes the pool in position order (only in the kernel's
 // rank-pool instantiation, so the window-pool one is left as it is).
-template <int G>
+template <typename Sm>
 __device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Workspace& ws, int pe,
-                                                 AnchorSmem<G>& sm) {
+                                                 Sm& sm) {
   const int be = pe / g.hkv, kvhe = pe - be * g.hkv;
   const int ne = seq_len_of(g, be);
   const int m = min(g.pool_rho * g.kappa, ne);
@@ -3158,7 +3161,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
   if constexpr (RANK) {
     if ((int)blockIdx.x >= g.problems() * splits) {  // uniform over the workgroup
-      anchor_rank_emit<G>(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
+      anchor_rank_emit(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
       return;
     }
   }
@@ -3337,6 +3340,142 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
   }
   lds_barrier();
   store_split<G, NW, NT>(ws, p, s, splits, sm.wo, sm.wml);
+}
+
+// Anchor layer with the rank-expanded pool on grids that the fused anchor
+// kernel's one workgroup per 128 selected tokens would not fit (many
+// problems, a large kappa): every split's workgroup marks the top-kappa over
+// the cache as anchor_attn_kernel does (same inputs, same set), takes the
+// positions of its 256 * tiles ranks of the set from the marks, and attends
+// them with all sixteen waves in 16-token tiles with running softmax
+// statistics (as refine_attn_multi_kernel); one extra workgroup per problem
+// writes the rank-expanded pool meanwhile (anchor_rank_emit).  merge_kernel,
+// launched next, merges the splits and clears the selection counters.
+template <int G>
+struct AnchorMultiSmem {
+  int32_t bt[kMaxPages];
+  uint32_t bitmap[kMaxSeqLen / 32];
+  union {
+    struct {  // the selection
+      uint32_t cbuf[2 * kCand];
+      uint32_t hist[4096 + 1024 + 1024];
+      uint32_t pair[kPairMax];
+      uint32_t ured[32];
+      int tmp[NT / 64 + 1];
+      int res[9];
+      int cnt[2];
+    };
+    struct {  // the waves' results, after the selection
+      float wo[NT / 64][G][kHeadDim];
+      float wml[NT / 64][G][2];
+    };
+  };
+  uint32_t srow[kMultiMaxSpan];
+  int32_t spos[kMultiMaxSpan];
+  float pw[NT / 64][16 * prob_stride<G>()] __attribute__((aligned(16)));
+};
+
+template <int G>
+__global__ __launch_bounds__(NT) void anchor_rank_multi_kernel(Geometry g, Workspace ws,
+                                                               const uint16_t* __restrict__ q,
+                                                               float scale,
+                                                               int32_t* __restrict__ anchor_idx,
+                                                               int32_t* __restrict__ layer_idx,
+                                                               int tiles) {
+  __shared__ AnchorMultiSmem<G> sm;
+  const int K = g.kappa;
+  tiles = clampi(tiles, 1, kMultiMaxTiles);
+  const int span = 16 * (NT / 64) * tiles;
+  const int splits = (K + span - 1) / span;
+  if ((int)blockIdx.x >= g.problems() * splits) {  // uniform over the workgroup
+    anchor_rank_emit(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
+    return;
+  }
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = seq_len_of(g, b);
+  const int r0 = s * span;
+  load_bt(g, b, n, sm.bt);
+
+  // the selection as marks over the list
+  if (n <= K) {
+    for (int i = t; i < ((n + 31) >> 5); i += NT)
+      sm.bitmap[i] = (32 * i + 32 <= n) ? 0xFFFFFFFFu : ((1u << (n & 31)) - 1u);
+    lds_barrier();
+  } else if (n <= kSmall / 2) {
+    small_marks<kSmallPer / 2>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
+  } else if (n <= kSmall) {
+    small_marks<kSmallPer>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
+  } else {
+    SelList c;
+    c.sc = ws.scores + (size_t)p * g.n_cap;
+    c.plist = nullptr;
+    c.prow = nullptr;
+    c.n = n;
+    c.K = K;
+    c.b = b;
+    c.kvh = kvh;
+    c.o1 = c.o2 = nullptr;
+    c.srow = nullptr;
+    c.ent = nullptr;
+    classified_marks(g, ws, p, c, sm);
+  }
+
+  // the nonzero mark words in order, each with the rank of its first mark
+  // (word index << 14 | rank) in sm.hist
+  const int words = (n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0, nz = 0;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    cnt += __popc(m);
+    nz += m ? 1 : 0;
+  }
+  int total, nz_total;
+  int rank = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  int slot = block_excl_scan<NT>(nz, sm.tmp, &nz_total);
+  uint32_t* const wl = sm.hist;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    if (m) {
+      wl[slot++] = ((uint32_t)i << 14) | (uint32_t)min(rank, 16383);
+      rank += __popc(m);
+    }
+  }
+  lds_barrier();
+  // one lane per bit of two listed words at a time: the positions of this
+  // split's ranks
+  const int rend = min(K, r0 + span);
+  for (int x = 2 * wave; x < nz_total; x += 2 * (NT / 64)) {
+    const int idx = x + (lane >> 5), bit = lane & 31;
+    if (idx < nz_total) {
+      const uint32_t e = wl[idx];
+      const int wi = (int)(e >> 14), base = (int)(e & 16383u);
+      const uint32_t m = sm.bitmap[wi];
+      if ((m >> bit) & 1u) {
+        const int r = base + __popc(m & ((1u << bit) - 1u));
+        if (r >= r0 && r < rend) sm.spos[r - r0] = wi * 32 + bit;
+      }
+    }
+  }
+  lds_barrier();
+  // this split's ranks: row ids for the attention, the anchor set
+  const int kt = min(total, K);
+  for (int k = t; k < rend - r0; k += NT) {
+    const int r = r0 + k;
+    int a = -1;
+    if (r < kt) {
+      a = clampi(sm.spos[k], 0, n - 1);
+      sm.srow[k] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
+    }
+    if (anchor_idx) anchor_idx[(size_t)p * K + r] = a;
+    if (layer_idx) layer_idx[(size_t)p * K + r] = a;
+  }
+  lds_barrier();
+  multi_attend_store<G>(g, ws, q, scale, p, s, splits, min(kt - r0, span), tiles, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -3743,6 +3882,37 @@ void launch_anchor_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
   launch_merge_g<G>(g, w, splits, out, true, s);
 }
 
+// Tiles per wave of anchor_rank_multi_kernel at a rank-pool anchor layer
+// whose grid the fused anchor kernel does not fit: the fewest (up to
+// kMultiMaxTiles) whose grid of problems x (ceil(kappa / (256 tiles)) + 1)
+// workgroups fits the device at once, if that still gives every problem two
+// or more attention workgroups; else 0 (the per-problem rank kernel, then
+// the attention over many workgroups), also for groups above 8 and for
+// contexts whose nonzero mark words exceed the word list.  With one split a
+// single compute unit would gather all kappa rows of its problem (batched
+// 16 x 8K-64K workload, kappa = 1024: 3.26 against 3.23 ms per step).
+int anchor_multi_tiles(const Geometry& g) {
+  if (g.group > 8 || g.max_seq_len > kFusedAnchorLen) return 0;
+  for (int tl = 1; tl <= kMultiMaxTiles; ++tl) {
+    const int span = 16 * (NT / 64) * tl;
+    const int splits = (g.kappa + span - 1) / span;
+    if ((long long)g.problems() * (splits + 1) <= (long long)device_cus())
+      return splits >= 2 ? tl : 0;
+  }
+  return 0;
+}
+
+template <int G>
+void launch_anchor_rank_multi_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, float* out, int32_t* anchor_idx, int32_t* layer_idx,
+                                int tiles, hipStream_t s) {
+  const int span = 16 * (NT / 64) * tiles;
+  const int splits = (g.kappa + span - 1) / span;
+  launch(kAttention, anchor_rank_multi_kernel<G>, dim3(g.problems() * (splits + 1)), dim3(NT), s,
+         g, w, q, scale, anchor_idx, layer_idx, tiles);
+  launch_merge_g<G>(g, w, splits, out, true, s);
+}
+
 hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* anchor_idx, int32_t* layer_idx, float* out,
                                 hipStream_t s) {
@@ -3788,7 +3958,8 @@ hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, cons
   const long long splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
   const bool fits = g.group <= 8 && g.max_seq_len <= kFusedAnchorLen &&
                     (long long)g.problems() * (splits + 1) <= (long long)device_cus();
-  if (!fits) {
+  const int tiles = fits ? 0 : anchor_multi_tiles(g);
+  if (!fits && tiles == 0) {
     hipError_t e = launch_anchor_rank(g, w, q, anchor_idx, layer_idx, s);
     if (e != hipSuccess) return e;
     return launch_attention(g, w, q, nullptr, true, scale, out, s);
@@ -3803,6 +3974,19 @@ hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, cons
            0, g.kappa, g.max_seq_len > m ? (int)m : 0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (tiles > 0) {  // groups of at most 8 heads
+#define PRISM_RANK_MULTI(G) \
+  launch_anchor_rank_multi_g<G>(g, w, q, scale, out, anchor_idx, layer_idx, tiles, s); break;
+    switch (g.group) {
+      case 1: PRISM_RANK_MULTI(1)
+      case 2: PRISM_RANK_MULTI(2)
+      case 4: PRISM_RANK_MULTI(4)
+      case 8: PRISM_RANK_MULTI(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef PRISM_RANK_MULTI
+    return hipGetLastError();
   }
   switch (g.group) {
     case 1: launch_anchor_attn_g<1>(g, w, q, scale, out, anchor_idx, layer_idx, true, s); break;
