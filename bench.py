@@ -123,10 +123,14 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
                      else wl.kappa * (2 * wl.window + 1))
     # refined layers beyond the fused grid, with pools of at most 16384 entries:
     # the multi-tile kernel (selection inside, 256 * tiles ranks per workgroup)
-    multi = (not fused and wl.group <= 8 and pool_bound <= 16384
-             and any(problems * -(-wl.kappa // (256 * t)) <= cus for t in range(1, 9)))
-    refined_own_select = fused or multi
-    pool_classify = not refined_own_select and pool_bound > 16384 and pool_bound > wl.kappa
+    fit_r = [t for t in range(1, 9) if problems * -(-wl.kappa // (256 * t)) <= cus]
+    multi = not fused and wl.group <= 8 and pool_bound <= 16384 and fit_r != []
+    # longer pools: classified, then the multi-tile kernel when that leaves
+    # two or more workgroups per problem (else selected once per problem)
+    long_multi = (not fused and wl.group <= 8 and L <= 6144 * 32 and pool_bound > 16384
+                  and fit_r != [] and -(-wl.kappa // (256 * fit_r[0])) >= 2)
+    refined_own_select = fused or multi or long_multi
+    pool_classify = not fused and not multi and pool_bound > 16384 and pool_bound > wl.kappa
     # the fused rank path classifies for kappa (and rho*kappa in the same pass)
     anchor_need = pool_rho * wl.kappa if (pool_rho >= 1 and not anchor_fused) else wl.kappa
     return {"anchor_score": na, "refine_score": nr,

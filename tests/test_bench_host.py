@@ -126,8 +126,9 @@ def test_launch_model_per_workload():
     the paths the library takes on 256 compute units: fused kernels at 128K
     planted; anchor and refined layers of the batched and 4 x 128K GQA-8
     workloads in the multi-tile kernels with the rank pool (pools of 4096 and
-    16384 entries), and selected per problem after classification with the
-    window pool (pools up to the whole cache)."""
+    16384 entries); with the window pool (pools up to the whole cache) the
+    anchor layers select per problem and the refined layers are classified,
+    then selected and attended in the multi-tile kernel."""
     import synth
     m = bench.launches_per_step
     p = m(synth.BY_NAME["llama3-8b-128k-planted"], 256)
@@ -139,5 +140,5 @@ def test_launch_model_per_workload():
         wl = synth.BY_NAME[name]
         r = m(wl, 256, pool_rho=4)
         assert (r["select"], r["classify"], r["pool_build"]) == (sel, na, 0), (name, r)
-        w = m(wl, 256)
-        assert (w["select"], w["classify"], w["pool_build"]) == (na + nr, na + nr, na), (name, w)
+        w = m(wl, 256)   # refined layers: classified, then the multi-tile kernel
+        assert (w["select"], w["classify"], w["pool_build"]) == (na, na + nr, na), (name, w)

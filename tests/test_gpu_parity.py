@@ -507,11 +507,15 @@ def test_decode_chain_rank_pool_per_problem_selection():
 
 # (G, kappa, pool): grids of 48 problems that the fused refined kernel's
 # 128-token splits do not fit on 256 compute units, so refined layers take the
-# multi-tile kernel: 256 ranks per workgroup at kappa = 700 (3 splits, the last
+# multi-tile kernels: 256 ranks per workgroup at kappa = 700 (3 splits, the last
 # ragged), 512 at kappa = 1500 (two tiles per wave, a ragged last split whose
-# waves hold one or two tiles); the window pools stay within 16384 entries.
+# waves hold one or two tiles).  Windows of 3 and 5 keep every pool within
+# 16384 entries (selected from registers); windows of 10 and 16 let the
+# 40000-token sequence's pools exceed it (scored with coarse counts,
+# classified, then selected from the classification).
 MULTI_CASES = [(1, 1500, "rank4"), (2, 700, "window5"), (4, 1500, "window3"), (8, 1500, "rank4"),
-               (8, 700, "window5")]
+               (8, 700, "window5"), (4, 1500, "window10"), (8, 700, "window16"),
+               (1, 700, "window16")]
 
 
 @pytest.mark.parametrize("G,kappa,pool", MULTI_CASES,

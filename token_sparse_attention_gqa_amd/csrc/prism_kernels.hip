@@ -3375,6 +3375,67 @@ struct AnchorMultiSmem {
   float pw[NT / 64][16 * prob_stride<G>()] __attribute__((aligned(16)));
 };
 
+// The selection step of the multi-tile kernels over a list of c.n entries
+// (scores c.sc; lists longer than kSmall after classify_kernel), as the fused
+// anchor kernel makes it: the top-c.K as marks in sm.bitmap, the nonzero mark
+// words in order with the rank of their first mark, then the list indices of
+// ranks [r0, r0 + span) in sm.spos.  Returns the number of marked entries.
+// Contains barriers; lists up to kFusedAnchorLen entries.
+template <typename Sm>
+__device__ __forceinline__ int multi_select_slice(const Geometry& g, const Workspace& ws, int p,
+                                                  const SelList& c, int r0, int span, Sm& sm) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int n = c.n, K = c.K;
+  if (n <= K) {
+    for (int i = t; i < ((n + 31) >> 5); i += NT)
+      sm.bitmap[i] = (32 * i + 32 <= n) ? 0xFFFFFFFFu : ((1u << (n & 31)) - 1u);
+    lds_barrier();
+  } else if (n <= kSmall / 2) {
+    small_marks<kSmallPer / 2>(c.sc, n, K, sm);
+  } else if (n <= kSmall) {
+    small_marks<kSmallPer>(c.sc, n, K, sm);
+  } else {
+    classified_marks(g, ws, p, c, sm);
+  }
+  const int words = (n + 31) >> 5;
+  const int wpt = (words + NT - 1) / NT;
+  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
+  int cnt = 0, nz = 0;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    cnt += __popc(m);
+    nz += m ? 1 : 0;
+  }
+  int total, nz_total;
+  int rank = block_excl_scan<NT>(cnt, sm.tmp, &total);
+  int slot = block_excl_scan<NT>(nz, sm.tmp, &nz_total);
+  uint32_t* const wl = sm.hist;  // word index << 14 | rank of its first mark
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t m = sm.bitmap[i];
+    if (m) {
+      wl[slot++] = ((uint32_t)i << 14) | (uint32_t)min(rank, 16383);
+      rank += __popc(m);
+    }
+  }
+  lds_barrier();
+  // one lane per bit of two listed words at a time
+  const int rend = min(K, r0 + span);
+  for (int x = 2 * wave; x < nz_total; x += 2 * (NT / 64)) {
+    const int idx = x + (lane >> 5), bit = lane & 31;
+    if (idx < nz_total) {
+      const uint32_t e = wl[idx];
+      const int wi = (int)(e >> 14), base = (int)(e & 16383u);
+      const uint32_t m = sm.bitmap[wi];
+      if ((m >> bit) & 1u) {
+        const int r = base + __popc(m & ((1u << bit) - 1u));
+        if (r >= r0 && r < rend) sm.spos[r - r0] = wi * 32 + bit;
+      }
+    }
+  }
+  lds_barrier();
+  return total;
+}
+
 template <int G>
 __global__ __launch_bounds__(NT) void anchor_rank_multi_kernel(Geometry g, Workspace ws,
                                                                const uint16_t* __restrict__ q,
@@ -3394,74 +3455,23 @@ __global__ __launch_bounds__(NT) void anchor_rank_multi_kernel(Geometry g, Works
   int p, s;
   map_block(blockIdx.x, g.problems(), splits, &p, &s);
   const int b = p / g.hkv, kvh = p - b * g.hkv;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int t = threadIdx.x;
   const int n = seq_len_of(g, b);
   const int r0 = s * span;
   load_bt(g, b, n, sm.bt);
-
-  // the selection as marks over the list
-  if (n <= K) {
-    for (int i = t; i < ((n + 31) >> 5); i += NT)
-      sm.bitmap[i] = (32 * i + 32 <= n) ? 0xFFFFFFFFu : ((1u << (n & 31)) - 1u);
-    lds_barrier();
-  } else if (n <= kSmall / 2) {
-    small_marks<kSmallPer / 2>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
-  } else if (n <= kSmall) {
-    small_marks<kSmallPer>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
-  } else {
-    SelList c;
-    c.sc = ws.scores + (size_t)p * g.n_cap;
-    c.plist = nullptr;
-    c.prow = nullptr;
-    c.n = n;
-    c.K = K;
-    c.b = b;
-    c.kvh = kvh;
-    c.o1 = c.o2 = nullptr;
-    c.srow = nullptr;
-    c.ent = nullptr;
-    classified_marks(g, ws, p, c, sm);
-  }
-
-  // the nonzero mark words in order, each with the rank of its first mark
-  // (word index << 14 | rank) in sm.hist
-  const int words = (n + 31) >> 5;
-  const int wpt = (words + NT - 1) / NT;
-  const int w0 = min(words, t * wpt), w1 = min(words, w0 + wpt);
-  int cnt = 0, nz = 0;
-  for (int i = w0; i < w1; ++i) {
-    const uint32_t m = sm.bitmap[i];
-    cnt += __popc(m);
-    nz += m ? 1 : 0;
-  }
-  int total, nz_total;
-  int rank = block_excl_scan<NT>(cnt, sm.tmp, &total);
-  int slot = block_excl_scan<NT>(nz, sm.tmp, &nz_total);
-  uint32_t* const wl = sm.hist;
-  for (int i = w0; i < w1; ++i) {
-    const uint32_t m = sm.bitmap[i];
-    if (m) {
-      wl[slot++] = ((uint32_t)i << 14) | (uint32_t)min(rank, 16383);
-      rank += __popc(m);
-    }
-  }
-  lds_barrier();
-  // one lane per bit of two listed words at a time: the positions of this
-  // split's ranks
+  SelList c;
+  c.sc = ws.scores + (size_t)p * g.n_cap;
+  c.plist = nullptr;
+  c.prow = nullptr;
+  c.n = n;
+  c.K = K;
+  c.b = b;
+  c.kvh = kvh;
+  c.o1 = c.o2 = nullptr;
+  c.srow = nullptr;
+  c.ent = nullptr;
+  const int total = multi_select_slice(g, ws, p, c, r0, span, sm);
   const int rend = min(K, r0 + span);
-  for (int x = 2 * wave; x < nz_total; x += 2 * (NT / 64)) {
-    const int idx = x + (lane >> 5), bit = lane & 31;
-    if (idx < nz_total) {
-      const uint32_t e = wl[idx];
-      const int wi = (int)(e >> 14), base = (int)(e & 16383u);
-      const uint32_t m = sm.bitmap[wi];
-      if ((m >> bit) & 1u) {
-        const int r = base + __popc(m & ((1u << bit) - 1u));
-        if (r >= r0 && r < rend) sm.spos[r - r0] = wi * 32 + bit;
-      }
-    }
-  }
-  lds_barrier();
   // this split's ranks: row ids for the attention, the anchor set
   const int kt = min(total, K);
   for (int k = t; k < rend - r0; k += NT) {
@@ -3472,6 +3482,55 @@ __global__ __launch_bounds__(NT) void anchor_rank_multi_kernel(Geometry g, Works
       sm.srow[k] = row_id_of_page(g, sm.bt[a >> 6], kvh, a);
     }
     if (anchor_idx) anchor_idx[(size_t)p * K + r] = a;
+    if (layer_idx) layer_idx[(size_t)p * K + r] = a;
+  }
+  lds_barrier();
+  multi_attend_store<G>(g, ws, q, scale, p, s, splits, min(kt - r0, span), tiles, sm);
+}
+
+// Refined layer of grids the fused kernel does not fit, for pools that can
+// hold more than kSmall entries (scored with coarse counts and classified
+// first): the multi-tile kernels' selection over the pool's list (its scores
+// in pool order and the pool's classification), this split's ranks resolved
+// to row ids and positions through the pool, then the multi-tile attention.
+// merge_kernel, launched next, clears the counters the classification used.
+template <int G>
+__global__ __launch_bounds__(NT) void refine_attn_multi_long_kernel(
+    Geometry g, Workspace ws, const uint16_t* __restrict__ q, float scale,
+    int32_t* __restrict__ layer_idx, int tiles) {
+  __shared__ AnchorMultiSmem<G> sm;
+  const int K = g.kappa;
+  tiles = clampi(tiles, 1, kMultiMaxTiles);
+  const int span = 16 * (NT / 64) * tiles;
+  const int splits = (K + span - 1) / span;
+  int p, s;
+  map_block(blockIdx.x, g.problems(), splits, &p, &s);
+  const int b = p / g.hkv, kvh = p - b * g.hkv;
+  const int t = threadIdx.x;
+  const size_t base = (size_t)p * g.n_cap;
+  SelList c;
+  c.sc = ws.scores + base;
+  c.plist = ws.pool_pos + base;
+  c.prow = ws.pool_row + base;
+  c.n = min(clampi(ws.pool_len[p], 0, g.n_cap), kFusedAnchorLen);
+  c.K = K;
+  c.b = b;
+  c.kvh = kvh;
+  c.o1 = c.o2 = nullptr;
+  c.srow = nullptr;
+  c.ent = nullptr;
+  const int r0 = s * span;
+  const int total = multi_select_slice(g, ws, p, c, r0, span, sm);
+  const int rend = min(K, r0 + span);
+  const int kt = min(total, K);
+  for (int k = t; k < rend - r0; k += NT) {
+    const int r = r0 + k;
+    int a = -1;
+    if (r < kt) {
+      const int e = clampi(sm.spos[k], 0, c.n - 1);
+      a = c.plist[e];
+      sm.srow[k] = c.prow[e];
+    }
     if (layer_idx) layer_idx[(size_t)p * K + r] = a;
   }
   lds_barrier();
@@ -4052,8 +4111,63 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
   launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
+// Tiles per wave of refine_attn_multi_long_kernel at a refined layer whose
+// grid the fused kernel does not fit and whose pool can exceed kSmall
+// entries: the fewest (up to kMultiMaxTiles) whose grid of problems x
+// ceil(kappa / (256 tiles)) workgroups fits the device, if that leaves two or
+// more workgroups per problem; else 0 (selection once per problem), also for
+// groups above 8 and pools longer than the multi-tile selection's word list.
+int multi_long_tiles(const Geometry& g) {
+  if (g.group > 8 || g.max_seq_len > kFusedAnchorLen || pool_cap(g) <= kSmall) return 0;
+  for (int tl = 1; tl <= kMultiMaxTiles; ++tl) {
+    const int span = 16 * (NT / 64) * tl;
+    const int splits = (g.kappa + span - 1) / span;
+    if ((long long)g.problems() * splits <= (long long)device_cus()) return splits >= 2 ? tl : 0;
+  }
+  return 0;
+}
+
+template <int G>
+void launch_refine_multi_long_g(const Geometry& g, const Workspace& w, const uint16_t* q,
+                                float scale, float* out, int32_t* layer_idx, int tiles,
+                                hipStream_t s) {
+  const int span = 16 * (NT / 64) * tiles;
+  const int splits = (g.kappa + span - 1) / span;
+  launch(kAttention, refine_attn_multi_long_kernel<G>, dim3(g.problems() * splits), dim3(NT), s,
+         g, w, q, scale, layer_idx, tiles);
+  launch_merge_g<G>(g, w, splits, out, true, s);
+}
+
 hipError_t launch_refine_attend(const Geometry& g, const Workspace& w, const uint16_t* q,
                                 float scale, int32_t* layer_idx, float* out, hipStream_t s) {
+  const int long_tiles = fused_fits(g) ? 0 : multi_long_tiles(g);
+  if (long_tiles > 0) {
+    // pools scored with coarse counts and classified over many workgroups,
+    // then selected and attended in the multi-tile kernel
+    const int bound = pool_cap(g);
+    const bool classify = bound > g.kappa;  // bound > kSmall here
+    PRISM_BY_GROUP(launch_pool_score_g, g, w, q, classify, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (classify) {
+      const int wgs = (bound + kClsEntries - 1) / kClsEntries;
+      launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w,
+             wgs, 1, g.kappa, 0);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+#define PRISM_LONG_MULTI(G) \
+  launch_refine_multi_long_g<G>(g, w, q, scale, out, layer_idx, long_tiles, s); break;
+    switch (g.group) {
+      case 1: PRISM_LONG_MULTI(1)
+      case 2: PRISM_LONG_MULTI(2)
+      case 4: PRISM_LONG_MULTI(4)
+      case 8: PRISM_LONG_MULTI(8)
+      default: return hipErrorInvalidValue;
+    }
+#undef PRISM_LONG_MULTI
+    return hipGetLastError();
+  }
   if (!fused_fits(g) && multi_tiles(g) == 0) {
     // select once per problem (pool indices only), then attend
     hipError_t e = launch_refine(g, w, q, nullptr, s, true);
