@@ -183,6 +183,7 @@ KERNEL_KINDS = {
     "score_pool_kernel": "refine_score", "score_pool_int2_kernel": "refine_score",
     "anchor_attn_kernel": "attention", "refine_attn_kernel": "attention",
     "refine_attn_multi_kernel": "attention", "anchor_rank_multi_kernel": "attention",
+    "refine_attn_multi_long_kernel": "attention",
     "attn_kernel": "attention", "select_kernel": "select", "rank_pool_kernel": "select",
     "classify_kernel": "classify", "merge_kernel": "merge", "pool_build_kernel": "pool_build",
     "quantize_kernel": "quantize", "dense_attn_kernel": "dense",
