@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+TIMES_FILE = os.path.join(ROOT, "profiles", "kernel_times.json")
 KERNEL_SRC = os.path.join(ROOT, "token_sparse_attention_gqa_amd", "csrc", "prism_kernels.hip")
 
 
@@ -160,6 +161,21 @@ def config_key(args):
     if getattr(args, "dense", False):
         key += "/dense"
     return key
+
+
+def graph_time_for(kernel, workload):
+    """Average dispatch duration (us) of a kernel kind in the graph-replayed
+    steps of the committed rocprofv3 kernel trace of this configuration, if
+    it was taken on the current kernel source; else None."""
+    try:
+        with open(TIMES_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    e = t.get("kernels", {}).get(kernel, {}).get(workload)
+    return e.get("graph_replay_avg_us") if e else None
 
 
 def traffic_for(kernel, workload):
@@ -415,6 +431,27 @@ def trace_summary(args):
               f"{np.mean(ed):.2f} | {np.median(ed):.2f} | |")
     print(f"| step (first start to last end) | | | | | | {np.mean(spans):.4f} mean, "
           f"{np.median(spans):.4f} median |")
+    if getattr(args, "record_times", False):
+        # per kind: the average dispatch duration in each region, recorded for
+        # this configuration and kernel source (the benchmark reports the
+        # graph-replay figure of its roofline kernel next to its own)
+        try:
+            with open(TIMES_FILE) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            t = {}
+        if t.get("kernel_source_sha256") != kernel_source_hash():
+            t = {"kernel_source_sha256": kernel_source_hash(), "kernels": {}}
+        for kind in dict.fromkeys(KERNEL_KINDS.get(k.split("<")[0], "other") for k in first):
+            ks = [k for k in dict.fromkeys(first) if KERNEL_KINDS.get(k.split("<")[0]) == kind]
+            gd = [x for k in ks for x in stats["graph replay"][k]]
+            ed = [x for k in ks for x in stats["eager"][k]]
+            t["kernels"].setdefault(kind, {})[config_key(args)] = {
+                "graph_replay_avg_us": round(float(np.mean(gd)), 3),
+                "eager_avg_us": round(float(np.mean(ed)), 3), "dispatches_per_region": len(gd)}
+        with open(TIMES_FILE, "w") as f:
+            json.dump(t, f, indent=1, sort_keys=True)
+            f.write("\n")
     if prefill:
         d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in prefill]
         print(f"\nPrefill INT2 quantization (`quantize_kernel`, one launch per layer): "
@@ -540,6 +577,9 @@ def main():
                          "shapes (uniform random, the most recent tokens, random 64- and "
                          "16-token runs), then exit: its fixed cost and "
                          "streaming rate (least squares over the set sizes)")
+    ap.add_argument("--record-times", action="store_true",
+                    help="with --trace-summary: record each kind's average duration in "
+                         "profiles/kernel_times.json for this configuration")
     ap.add_argument("--trace-summary", default="", metavar="CSV",
                     help="no GPU work: read the kernel_trace.csv of a rocprofv3 --kernel-trace run "
                          "of this script with the same workload options, --steps and --warmup, and "
@@ -807,6 +847,10 @@ def main():
                 "algorithmic_bytes_per_launch": int(algo[dominant]),
                 "avg_launch_us": round(dk["avg_us"], 3),
                 "timed_in": "eager launches, dispatch timestamps"}
+    g_us = graph_time_for(dominant, config_key(args))
+    if g_us:   # the same kernel inside the replayed graph (committed trace, same source)
+        roofline["graph_replay_avg_us"] = g_us
+        roofline["graph_replay_frac"] = round(algo[dominant] / (g_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     result = {
         "metric": "sparse decode-attn tokens/sec + % HBM roofline at 128K, kappa=2048 (1 GPU)",

@@ -7,6 +7,7 @@ import json
 import os
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -88,7 +89,7 @@ def test_counter_summary_needs_the_copy(tmp_path, monkeypatch):
         bench.counter_summary(args)
 
 
-def test_trace_summary_splits_steps(tmp_path, capsys):
+def test_trace_summary_splits_steps(tmp_path, capsys, monkeypatch):
     import synth
     wl = synth.BY_NAME["tiny-4k-gqa4"]
     per_step = bench.launches_per_step(wl, 256, 0, bench.layer_roles(wl))
@@ -109,6 +110,23 @@ def test_trace_summary_splits_steps(tmp_path, capsys):
     args = argparse.Namespace(workload=wl.name, pattern="", cus=256, pool_rho=0, dense=False,
                               steps=K, warmup=W, trace_summary=str(path))
     bench.trace_summary(args)
+    # with --record-times the graph-replay and eager averages of every kind go
+    # to the kernel-times record for this configuration and kernel source
+    times = tmp_path / "times.json"
+    monkeypatch.setattr(bench, "TIMES_FILE", str(times))
+    monkeypatch.setattr(bench, "KERNEL_KINDS", {f"kern{k}": f"kind{k % 2}" for k in range(n)})
+    args.record_times = True
+    args.int2 = False
+    bench.trace_summary(args)
+    rec = json.loads(times.read_text())
+    assert rec["kernel_source_sha256"] == bench.kernel_source_hash()
+    e = rec["kernels"]["kind0"][wl.name]
+    assert e["dispatches_per_region"] == K * ((n + 1) // 2)
+    want_g = np.mean([1.0 * (k + 1) for k in range(0, n, 2)])
+    assert abs(e["graph_replay_avg_us"] - want_g) < 1e-3
+    assert abs(e["eager_avg_us"] - 2 * want_g) < 1e-3
+    assert bench.graph_time_for("kind0", wl.name) == e["graph_replay_avg_us"]
+    assert bench.graph_time_for("kind0", "other-workload") is None
     out = capsys.readouterr().out
     row = [l for l in out.splitlines() if "`kern0<4>`" in l][0]
     # graph replay region: 1 us per dispatch; eager region: 2 us
