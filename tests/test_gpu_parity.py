@@ -396,6 +396,27 @@ def test_rank_pool_from_leftover_workspace(fill, rho):
         _run_chain_rank(st, range(3), probs, f"leftover-rank rho={rho} {fill:#x} step {rep}")
 
 
+@pytest.mark.parametrize("pool", ["window16", "rank4"])
+@pytest.mark.parametrize("fill", [0xAB, 0xFF])
+def test_multi_tile_from_leftover_workspace(fill, pool):
+    """The multi-tile kernels from a workspace holding arbitrary bytes (48
+    problems, G = 4, kappa = 1500): with the window pool the refined layers
+    select from the pool's classification, with the rank pool the anchor layer
+    from the list's; the selections check their own counters, and two decode
+    steps on the same workspace match the oracle."""
+    rho = 4 if pool == "rank4" else 0
+    wl = synth.scaled(synth.TINY_4K, name=f"leftover-multi-{pool}", wid=540 + rho,
+                      num_q_heads=32, num_kv_heads=8, batch=6, context=None,
+                      lengths=(9024, 1500, 12000, 4096, 40000, 7001), kappa=1500,
+                      window=16 if rho == 0 else 5, num_layers=3, anchor_stride=3)
+    st = Setup(wl, range(3), pool_rho=rho)
+    st.ws.fill_(fill)
+    probs = [(b, g) for b in range(wl.batch) for g in (0, 3, 7)]
+    run = _run_chain_rank if rho else _run_chain
+    for rep in range(2):
+        run(st, range(3), probs, f"leftover-multi {pool} {fill:#x} step {rep}")
+
+
 def test_decode_chain_per_problem_selection():
     """A grid the fused kernels do not use (32 problems x 9 splits of 128 > 256
     compute units): every layer selects once per problem (anchor lists and

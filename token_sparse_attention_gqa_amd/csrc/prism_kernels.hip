@@ -17,8 +17,13 @@
 //                  refine_attn_kernel   top-kappa of the pool (Eq. 6) and
 //                                       SparseAttn over one split;
 //   both           merge_kernel         the splits merged into the output.
-// The single-step entry points and the shapes the fused kernels do not cover
-// use select_kernel, pool_build_kernel and attn_kernel instead.  Options:
+// Grids the fused kernels do not fit at once (many problems, large kappa)
+// use fewer, wider splits: refine_attn_multi_kernel (pools up to kSmall),
+// refine_attn_multi_long_kernel (longer pools, after classify_kernel) and
+// anchor_rank_multi_kernel (the rank-expanded pool's anchor layer), each
+// selecting in every split and attending 256-2048 ranks with all sixteen
+// waves.  The single-step entry points and the remaining shapes use
+// select_kernel, pool_build_kernel and attn_kernel instead.  Options:
 //   rank-expanded pool (Eq. 4)  rank_pool_kernel: the anchor's top rho*kappa
 //                               as the pool, its top-kappa as the anchor set;
 //   INT2 proposal keys (Eqs. 7-9) quantize_kernel, score_anchor_int2_kernel,
