@@ -767,6 +767,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(Geometry g, int num_new, 
 //   <q_h, k-hat> = sum_m alpha_m D_hm + beta_m Q_hm
 //               = sum_m alpha_m (2 acc_hm - 4 Q_hm) + beta_m Q_hm.
 // Output lane (token j, quarter g4) holds rows 4 g4 + m: head 4t + g4 of tile t.
+// (a & m) | c in one VALU instruction.  The compiler keeps the two constants
+// as literals of a VOP2 AND and a VOP2 OR (VOP3 takes no literal on gfx9);
+// with the mask in a scalar register and c in a vector register the VOP3
+// form does both, one instruction of the INT2 operand build per code dword.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
+
 template <int G>
 struct Int2Query {
   static constexpr int kTiles = (4 * G + 15) / 16;
@@ -814,7 +824,7 @@ struct Int2Query {
       for (int i = 0; i < 4; ++i) {
         const int t = 4 * (s4 & 1) + i;
         const uint32_t sh = t <= 2 ? (wd << (5 - 2 * t)) : (wd >> (2 * t - 5));
-        bf[s4][i] = (sh & 0x00600060u) | 0x40004000u;
+        bf[s4][i] = and_or(sh, 0x00600060u, 0x40004000u);
       }
     }
     float best = -INFINITY;
