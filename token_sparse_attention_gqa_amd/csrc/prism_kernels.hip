@@ -125,9 +125,17 @@ __device__ __forceinline__ void map_block(int bid, int P, int W, int* p, int* w)
 // max(v[l], v[l ^ 16]) and max(v[l], v[l ^ 32]) for every lane l, by the
 // VALU row swaps (v_permlane16_swap / v_permlane32_swap with the value as both
 // operands: each lane receives its partner's value in one of the two results).
+// The larger of two scores in one v_max_f32: fmaxf first canonicalises each
+// operand that comes from a lane swap (two more instructions), which scores
+// (finite, or -inf for masked entries) never need.
+__device__ __forceinline__ float max_score(float a, float b) {
+  float d;
+  asm("v_max_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
 __device__ __forceinline__ float xor16_max(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_score(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ uint32_t xor16_or(uint32_t v) {
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -135,7 +143,7 @@ __device__ __forceinline__ uint32_t xor16_or(uint32_t v) {
 }
 __device__ __forceinline__ float xor32_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_score(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // MFMA A-operand fragment of the group's query heads.  Lane l holds head
