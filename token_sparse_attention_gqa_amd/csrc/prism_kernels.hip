@@ -2833,7 +2833,7 @@ __device__ __attribute__((noinline)) int long_pool_slice(const float* sc, const 
   return slice_from_marks(c, p, r0, span, layer_idx, sm);
 }
 
-template <int G, int SP>
+template <int G, int SP, bool REG32 = false>
 __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
                                                          float scale,
@@ -2853,7 +2853,40 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
   const int myr = r0 + wave * 16 + j;
   uint32_t row = 0u;
   bool valid = false;
-  if (n <= kSmall) {  // uniform over the workgroup
+  if (REG32 && n <= kSmall / 2) {  // uniform over the workgroup
+    const int total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, SP, layer_idx, sm);
+    valid = myr < min(total, K);
+    row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
+  } else if constexpr (REG32) {
+    // caches of at most kRegMarks tokens (the launch's choice): pools above
+    // kSmall / 2 entries are selected from 32 keys per thread, inline, with no
+    // call frame; the split's rows and positions are read from the pool by
+    // rank
+    const size_t base = (size_t)p * g.n_cap;
+    constexpr int R = kRegMarks / NT;
+    const int e0 = R * t, m = min(n, kRegMarks);
+    uint32_t key[R];
+    load_run<R>(ws.scores + base, min(e0, g.n_cap - R), key);  // n_cap is a multiple of 64
+#pragma unroll
+    for (int i = 0; i < R; ++i) key[i] = order_key(__uint_as_float(key[i]));
+    const uint32_t take = top_k_mask<R>(key, clampi(m - e0, 0, R), m, K, sm);
+    if (e0 < m) sm.bitmap[t] = take;
+    lds_barrier();
+    SelList c;
+    c.sc = ws.scores + base;
+    c.plist = ws.pool_pos + base;
+    c.prow = ws.pool_row + base;
+    c.n = m;
+    c.K = K;
+    c.b = b;
+    c.kvh = kvh;
+    c.o1 = c.o2 = nullptr;
+    c.srow = nullptr;
+    c.ent = nullptr;
+    const int total = slice_from_marks(c, p, r0, SP, layer_idx, sm);
+    valid = myr < min(total, K);
+    row = valid && wave < NW ? sm.srow[wave * 16 + j] : 0u;
+  } else if (n <= kSmall) {  // uniform over the workgroup
     int total;
     if (n <= kSmall / 2)
       total = fused_select_slice<kSmallPer / 2>(g, ws, p, n, r0, SP, layer_idx, sm);
@@ -4125,12 +4158,25 @@ void launch_refine_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
   }
   const int sp = refine_split(g);
   const int splits = (g.kappa + sp - 1) / sp;
-  if (sp == 64)
-    launch(kAttention, refine_attn_kernel<G, 64>, dim3(g.problems() * splits), dim3(NT), s, g, w,
-           q, scale, layer_idx);
-  else
-    launch(kAttention, refine_attn_kernel<G, kFusedSplit>, dim3(g.problems() * splits), dim3(NT),
-           s, g, w, q, scale, layer_idx);
+  // caches of at most kRegMarks tokens select every pool from registers in
+  // the kernel itself: the out-of-line path for longer pools, and its call
+  // frame, are then not compiled in (the 32K workload, whose unstructured
+  // pools cover most of the cache, takes it on every refined layer)
+  const bool reg32 = g.n_cap <= kRegMarks;
+  const dim3 grid(g.problems() * splits), block(NT);
+  if (sp == 64) {
+    if (reg32)
+      launch(kAttention, refine_attn_kernel<G, 64, true>, grid, block, s, g, w, q, scale, layer_idx);
+    else
+      launch(kAttention, refine_attn_kernel<G, 64>, grid, block, s, g, w, q, scale, layer_idx);
+  } else {
+    if (reg32)
+      launch(kAttention, refine_attn_kernel<G, kFusedSplit, true>, grid, block, s, g, w, q, scale,
+             layer_idx);
+    else
+      launch(kAttention, refine_attn_kernel<G, kFusedSplit>, grid, block, s, g, w, q, scale,
+             layer_idx);
+  }
   launch_merge_g<G>(g, w, splits, out, false, s);
 }
 
