@@ -92,10 +92,11 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
     196608; refined layers whose pools stay within 16384 entries, and anchor
     layers with the rank-expanded pool, also when problems x ceil(kappa /
     (256 t)) workgroups (plus one per problem for the rank pool) fit for some
-    t <= 8: the multi-tile kernels), else a selection kernel per layer precedes the attention, and a
-    refined layer whose pool can exceed 16384 entries is classified first, and an
-    anchor layer that selects in its own kernel builds the window pool in
-    another.
+    t <= 8: the multi-tile kernels), else a selection kernel per layer
+    precedes the attention, and a refined layer whose pool can exceed 16384
+    entries is classified first, and an anchor layer that selects in its own
+    kernel builds the window pool in another.  The fused anchor kernel
+    selects contexts up to 32768 tokens without a classification.
     Shared layers launch the attention and its merge only.  With INT2 keys
     the newest key of every layer is quantized inside the layer's scoring
     kernel (a shared layer's, which scores nothing, inside its attention
@@ -114,11 +115,14 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
         # (with 128-token splits, or 256 t ranks per workgroup for the fewest
         # t <= 8 that fits, if that leaves two or more splits)
         fit_t = [t for t in range(1, 9) if problems * (-(-wl.kappa // (256 * t)) + 1) <= cus]
-        anchor_fused = (wl.group <= 8 and L <= 6144 * 32
-                        and (problems * (splits + 1) <= cus
-                             or (fit_t != [] and -(-wl.kappa // (256 * fit_t[0])) >= 2)))
+        anchor_fits = wl.group <= 8 and L <= 6144 * 32 and problems * (splits + 1) <= cus
+        anchor_fused = anchor_fits or (wl.group <= 8 and L <= 6144 * 32 and fit_t != []
+                                       and -(-wl.kappa // (256 * fit_t[0])) >= 2)
     else:
-        anchor_fused = fused and L <= 6144 * 32
+        anchor_fused = anchor_fits = fused and L <= 6144 * 32
+    # the fused anchor kernel selects contexts of up to 32768 tokens from keys
+    # in registers; other anchor paths classify lists above 16384 entries
+    anchor_cls_min = 32768 if anchor_fits else 16384
     n_cap = -(-L // 64) * 64
     pool_bound = min(n_cap, pool_rho * wl.kappa if pool_rho >= 1
                      else wl.kappa * (2 * wl.window + 1))
@@ -138,7 +142,7 @@ def launches_per_step(wl, cus, pool_rho=0, roles=None, dense=False):
             "select": (0 if anchor_fused else na) + (0 if refined_own_select else nr),
             "pool_build": 0 if (anchor_fused or pool_rho >= 1) else na,
             "attention": wl.num_layers,
-            "classify": (na if (L > 16384 and L > anchor_need) else 0)
+            "classify": (na if (L > anchor_cls_min and L > anchor_need) else 0)
                         + (nr if pool_classify else 0),
             "merge": wl.num_layers, "quantize": 0, "dense": 0}
 

@@ -117,11 +117,14 @@ def test_exact_ties_go_to_lowest_position():
     assert list(got[0, 1]) == list(dup_pos[:kappa])
 
 
-@pytest.mark.parametrize("L,kappa", [(3000, 100), (20000, 1000)])
+@pytest.mark.parametrize("L,kappa", [(3000, 100), (20000, 1000), (30000, 2000)])
 def test_concentrated_scores_and_long_ties(L, kappa):
     """Head 0: every row equal (one score repeated L times).  Head 1: one key
     row scaled by 2^16, so every other score sits inside one 1/4096 slice of
-    the score range.  Lists below and above 16384 entries."""
+    the score range.  Lists below and above 16384 entries, through the
+    per-problem selection (prism_score_topk) and the fused anchor kernel
+    (prism_decode_layer, which selects these contexts from keys in
+    registers)."""
     rng = np.random.default_rng(8)
     G = 4
     base = rng.standard_normal((L, 128)).astype(np.float32)
@@ -142,6 +145,11 @@ def test_concentrated_scores_and_long_ties(L, kappa):
     qf = oracle.bf16_to_f64(q[0, G:2 * G])
     want, s = oracle.anchor_select(qf, kp, bt[0], 1, L, kappa, 64)
     check_set(got[0, 1], want, s, np.arange(L), kappa, f"outlier L{L}")
+    anchor, sel = torch.zeros_like(idx), torch.zeros_like(idx)
+    out = torch.zeros((1, 2 * G, 128), dtype=torch.float32, device="cuda")
+    tsa.prism_decode_layer(0, kv, dev(q), p, anchor, sel, out, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(sel.cpu().numpy(), got), f"fused anchor kernel L{L}"
 
 
 def test_wide_threshold_bin_with_ties():

@@ -3170,7 +3170,7 @@ __device__ __forceinline__ void small_marks(const float* sc, int n, int K, Sm& s
 // extra workgroup per problem marks the cache's top rho*kappa (from the second
 // classification) and writes the pool in position order (only in the kernel's
 // rank-pool instantiation, so the window-pool one is left as it is).
-template <typename Sm>
+template <bool REG32 = false, typename Sm>
 __device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Workspace& ws, int pe,
                                                  Sm& sm) {
   const int be = pe / g.hkv, kvhe = pe - be * g.hkv;
@@ -3186,6 +3186,8 @@ __device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Worksp
     small_marks<kSmallPer / 2>(sce, ne, m, sm);
   } else if (ne <= kSmall) {
     small_marks<kSmallPer>(sce, ne, m, sm);
+  } else if (REG32) {  // caches of at most kRegMarks tokens: no classification
+    small_marks<kRegMarks / NT>(sce, ne, m, sm);
   } else {
     SelList c;
     c.sc = sce;
@@ -3204,7 +3206,7 @@ __device__ __forceinline__ void anchor_rank_emit(const Geometry& g, const Worksp
   emit_pool<false>(g, ws, pe, kvhe, ne, sm, &pool_n);
 }
 
-template <int G, bool RANK>
+template <int G, bool RANK, bool REG32 = false>
 __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace ws,
                                                          const uint16_t* __restrict__ q,
                                                          float scale,
@@ -3217,7 +3219,7 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
   const int splits = (K + kFusedSplit - 1) / kFusedSplit;
   if constexpr (RANK) {
     if ((int)blockIdx.x >= g.problems() * splits) {  // uniform over the workgroup
-      anchor_rank_emit(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
+      anchor_rank_emit<REG32>(g, ws, (int)blockIdx.x - g.problems() * splits, sm);
       return;
     }
   }
@@ -3239,6 +3241,8 @@ __global__ __launch_bounds__(NT) void anchor_attn_kernel(Geometry g, Workspace w
     small_marks<kSmallPer / 2>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
   } else if (n <= kSmall) {
     small_marks<kSmallPer>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
+  } else if (REG32) {  // caches of at most kRegMarks tokens: no classification
+    small_marks<kRegMarks / NT>(ws.scores + (size_t)p * g.n_cap, n, K, sm);
   } else {
     SelList c;
     c.sc = ws.scores + (size_t)p * g.n_cap;
@@ -3988,12 +3992,27 @@ void launch_anchor_attn_g(const Geometry& g, const Workspace& w, const uint16_t*
                           float* out, int32_t* anchor_idx, int32_t* layer_idx, bool rank,
                           hipStream_t s) {
   const int splits = (g.kappa + kFusedSplit - 1) / kFusedSplit;
-  if (rank)
-    launch(kAttention, anchor_attn_kernel<G, true>, dim3(g.problems() * (splits + 1)), dim3(NT), s,
-           g, w, q, scale, anchor_idx, layer_idx);
-  else
-    launch(kAttention, anchor_attn_kernel<G, false>, dim3(g.problems() * splits), dim3(NT), s, g,
-           w, q, scale, anchor_idx, layer_idx);
+  const dim3 block(NT);
+  // contexts of at most kRegMarks tokens are selected from keys in registers
+  // (no classification launched before)
+  const bool reg32 = g.max_seq_len <= kRegMarks;
+  if (rank) {
+    const dim3 grid(g.problems() * (splits + 1));
+    if (reg32)
+      launch(kAttention, anchor_attn_kernel<G, true, true>, grid, block, s, g, w, q, scale,
+             anchor_idx, layer_idx);
+    else
+      launch(kAttention, anchor_attn_kernel<G, true>, grid, block, s, g, w, q, scale, anchor_idx,
+             layer_idx);
+  } else {
+    const dim3 grid(g.problems() * splits);
+    if (reg32)
+      launch(kAttention, anchor_attn_kernel<G, false, true>, grid, block, s, g, w, q, scale,
+             anchor_idx, layer_idx);
+    else
+      launch(kAttention, anchor_attn_kernel<G, false>, grid, block, s, g, w, q, scale, anchor_idx,
+             layer_idx);
+  }
   launch_merge_g<G>(g, w, splits, out, true, s);
 }
 
@@ -4044,7 +4063,7 @@ hipError_t launch_anchor_attend(const Geometry& g, const Workspace& w, const uin
   PRISM_BY_GROUP(launch_anchor_score_g, g, w, q, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
+  if (g.max_seq_len > kRegMarks && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
            0, g.kappa, 0);
@@ -4083,7 +4102,9 @@ hipError_t launch_anchor_rank_attend(const Geometry& g, const Workspace& w, cons
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long long m = (long long)g.pool_rho * g.kappa;
-  if (g.max_seq_len > kSmall && g.max_seq_len > g.kappa) {
+  // the fused kernel selects contexts of at most kRegMarks tokens from keys in
+  // registers; the multi-tile kernel selects from the classification
+  if (g.max_seq_len > (tiles > 0 ? kSmall : kRegMarks) && g.max_seq_len > g.kappa) {
     const int wgs = (g.n_cap + kClsEntries - 1) / kClsEntries;
     launch(kClassify, classify_kernel, dim3(g.problems() * wgs), dim3(kClsThreads), s, g, w, wgs,
            0, g.kappa, g.max_seq_len > m ? (int)m : 0);
