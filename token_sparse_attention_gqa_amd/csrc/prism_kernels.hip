@@ -2703,7 +2703,10 @@ __global__ __launch_bounds__(kAttnThreads) void dense_attn_kernel(Geometry g, Wo
 // layer_idx, if given, receives those ranks' positions.  Pools of at most
 // kSmall entries are selected in registers; up to kRegMarks entries also from
 // registers (32 keys per thread) into marks in an LDS bitmap; longer ones by
-// the sampled bracket and one pass over the pool (marks in the bitmap).
+// the sampled bracket and one pass over the pool (marks in the bitmap), both
+// in an out-of-line function.  The REG32 instantiation (caches of at most
+// kRegMarks tokens) selects pools above kSmall / 2 entries from 32 keys per
+// thread inline and has no out-of-line path.
 template <int G, int SP>
 struct FusedSmem {
   uint32_t hist[4096 + 1024 + 1024];
@@ -2930,7 +2933,8 @@ __global__ __launch_bounds__(NT) void refine_attn_kernel(Geometry g, Workspace w
 // The attention phase shared by the multi-tile kernels: wave w attends tiles
 // w, w + 16, w + 32, ... of the workgroup's `lim` ranks (row ids in srow),
 // then the waves' results are combined and stored as split s.  Contains
-// barriers; the caller's LDS behind wo / wml must be free.
+// barriers; after the first one the helper overwrites the LDS behind wo / wml,
+// so the caller must no longer need it.
 template <int G, typename Sm>
 __device__ __forceinline__ void multi_attend_store(const Geometry& g, const Workspace& ws,
                                                    const uint16_t* q, float scale, int p, int s,
@@ -2985,11 +2989,13 @@ __device__ __forceinline__ void multi_attend_store(const Geometry& g, const Work
 // per problem, each selecting the pool's top-kappa from keys in registers as
 // refine_attn_kernel does (every split reaches the same set), then attending
 // its 256 * tiles consecutive ranks of the set with all sixteen waves, each
-// wave a strided run of 16-token tiles with the next tile's K and V in flight
-// while one is attended and running softmax statistics per head (the pattern
-// of dense_attn_kernel).  The waves' results are combined in the workgroup and
-// stored as one split for merge_kernel.  The selection's LDS is reused for the
-// waves' results once the set's rows are in sm.srow.
+// wave a strided run of 16-token tiles, one tile's K and V in flight at a time
+// (sixteen waves per compute unit keep enough loads outstanding; a second
+// buffer would not fit 128 registers at G = 8), each folded into running
+// softmax statistics per head (attend_tile_online).  The waves' results are
+// combined in the workgroup and stored as one split for merge_kernel.  The
+// selection's LDS is reused for the waves' results once the set's rows are in
+// sm.srow.
 constexpr int kMultiMaxTiles = 8;                 // 16-token tiles per wave at most
 constexpr int kMultiMaxSpan = 16 * NT / 64 * kMultiMaxTiles;  // ranks per workgroup at most
 
