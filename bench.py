@@ -411,9 +411,13 @@ def trace_summary(args):
     W, K = args.warmup, args.steps
     g0 = (W + max(1, W)) * n
     regions = {"graph replay": rows[g0:g0 + K * n], "eager": rows[g0 + K * n:g0 + 2 * K * n]}
-    first = [name(r) for r in rows[:n]]
+    # every timed step launches the same kernels; two dispatches with equal
+    # start stamps may sort either way, so steps are compared as multisets
+    from collections import Counter
+    first = [name(r) for r in rows[g0:g0 + n]]
+    want = Counter(first)
     for label, rs in regions.items():
-        if len(rs) != K * n or any([name(r) for r in rs[i * n:(i + 1) * n]] != first
+        if len(rs) != K * n or any(Counter(name(r) for r in rs[i * n:(i + 1) * n]) != want
                                    for i in range(K)):
             sys.exit(f"trace does not hold {K} whole steps of {n} kernels in the {label} region")
     print(f"{K} steps of {n} kernels per region; durations End - Start of each dispatch (us)")
