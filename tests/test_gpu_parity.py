@@ -768,7 +768,8 @@ def _new_key_slots(st, nk):
 
 
 @pytest.mark.parametrize("mode,G", [("window", 4), ("rank", 4), ("roles", 4), ("standalone", 4),
-                                    ("window", 1), ("window", 16), ("rank", 16)])
+                                    ("window", 1), ("window", 16), ("rank", 16),
+                                    ("multi-window", 4), ("multi-rank", 4)])
 @pytest.mark.parametrize("nk", [1, 5, 64])
 def test_int2_new_keys_quantized_inside_the_call(mode, G, nk):
     """prism_kv_cache.new_keys: the codes and scales of every sequence's last
@@ -783,12 +784,20 @@ def test_int2_new_keys_quantized_inside_the_call(mode, G, nk):
     entries and straddle a pool workgroup's 256 entries; the window pool may or may not
     hold them (the last pool workgroup writes those outside it); FRS puts a
     shared layer, which scores nothing, last.  G = 16 takes the per-problem
-    selection and rank-pool kernels instead of the fused ones."""
+    selection and rank-pool kernels instead of the fused ones; the multi
+    modes (16 KV heads, 48 problems, kappa = 700, the 5000-token sequence
+    made 20000) the multi-tile kernels: refined layers classified first
+    (window pools up to 20032 entries), or the rank pool's anchor kernel
+    (selecting the 20000-token list from its classification) and refined
+    kernel."""
     nl = 3
-    wl = synth.scaled(synth.TINY_4K, name=f"new-keys-{mode}", wid=460, num_q_heads=2 * G,
-                      num_kv_heads=2, batch=3, context=None, lengths=(2050, 5000, 4097),
-                      kappa=300, window=16, num_layers=nl, anchor_stride=nl)
-    st = Setup(wl, range(nl), pool_rho=16 if mode == "rank" else 0, int2=True)
+    multi = mode.startswith("multi")
+    hkv = 16 if multi else 2
+    wl = synth.scaled(synth.TINY_4K, name=f"new-keys-{mode}", wid=460, num_q_heads=hkv * G,
+                      num_kv_heads=hkv, batch=3, context=None,
+                      lengths=(2050, 20000 if multi else 5000, 4097),
+                      kappa=700 if multi else 300, window=16, num_layers=nl, anchor_stride=nl)
+    st = Setup(wl, range(nl), pool_rho=16 if mode.endswith("rank") else 0, int2=True)
     want_codes = [st.kv[l].tensors[4].clone() for l in range(nl)]
     want_scales = [st.kv[l].tensors[5].clone() for l in range(nl)]
 
