@@ -940,7 +940,8 @@ def test_determinism():
 
 
 # ---------------------------------------------------------------------- graph replay
-@pytest.mark.parametrize("mode", ["window", "rank", "int2", "int2-new-keys", "roles", "dense"])
+@pytest.mark.parametrize("mode", ["window", "rank", "int2", "int2-new-keys", "roles", "dense",
+                                  "multi-window", "multi-rank-int2"])
 def test_graph_replay_matches_eager(mode):
     """The decode step captured once as a HIP graph (the launch the benchmark
     times) and replayed three times, with eager work and synchronisations
@@ -951,10 +952,16 @@ def test_graph_replay_matches_eager(mode):
     the newest key in a launch of its own or inside the layer's calls
     (new_keys = 1)."""
     nl, pattern = 4, "FRSR"
+    # the multi modes: 48 problems at kappa = 1500, beyond the fused kernels'
+    # grid (window pools classified per refined layer; the rank pool's
+    # multi-tile anchor and refined kernels, with INT2 keys and new_keys = 1)
+    multi = mode.startswith("multi")
     wl = synth.scaled(synth.LLAMA_128K_PLANTED, name=f"graph-{mode}", wid=450, context=20480,
-                      kappa=512, n_clusters=16, num_layers=nl, anchor_stride=2)
-    st = Setup(wl, range(nl), pool_rho=4 if mode == "rank" else 0, int2=mode.startswith("int2"))
-    if mode == "int2-new-keys":   # each layer's call quantizes the newest key itself
+                      batch=6 if multi else 1, kappa=1500 if multi else 512, n_clusters=16,
+                      num_layers=nl, anchor_stride=2)
+    st = Setup(wl, range(nl), pool_rho=4 if mode in ("rank", "multi-rank-int2") else 0,
+               int2=mode.startswith("int2") or mode.endswith("int2"))
+    if mode in ("int2-new-keys", "multi-rank-int2"):   # each layer's call quantizes its newest key
         for l in range(nl):
             st.kv[l] = st.kv[l].with_new_keys(1)
     anchor = st.idx_buf()
